@@ -1,0 +1,286 @@
+/*
+ * la_oracle.c -- plain fp64 CPU oracle for kernelized linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file.  Its only users are the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark.  It shares no code, header, table or
+ * helper with the HIP library; the two meet only in the seeded input arrays.
+ *
+ * Sources (web pages on Katharopoulos et al., "Transformers are RNNs: Fast
+ * Autoregressive Transformers with Linear Attention", ICML 2020):
+ *   [review]  nubint.ai, "[Paper Review] Transformers are RNNs: ...",
+ *             section "Proposed method".
+ *   [summary] paperlayer.ai, "Transformers are RNNs: ..." (arXiv 2006.16236v3
+ *             summary), sections 3.2, 3.2.1, 3.3, 3.3.1, 3.3.2, 3.4 and
+ *             appendix "A. Gradient Derivation".
+ *   [deck]    zhengyuhong.cn, "Transformers are RNNs: ... 解读", slide 3
+ *             (associativity, feature map) and slide 4 (causal prefix states).
+ *
+ * Every routine below follows the per-token recurrence literally, in double
+ * precision, with no chunking, blocking or reordering.  Arrays are dense and
+ * row-major: q,k are [B][H][N][D], v,out are [B][H][N][M].  The (b,h) slices
+ * are independent recurrences, so they are spread over OpenMP threads; the
+ * order of operations inside one slice is the plain sequential order.
+ *
+ * Readings where the pages are silent (each one is also listed in the design doc):
+ *   - feature map phi(x) = elu(x) + 1 with alpha = 1, i.e. x + 1 for x > 0
+ *     and exp(x) otherwise ([deck] slide 3; [summary] 3.2.1).  Both branches
+ *     give value 1 and slope 1 at x = 0, so the branch choice at 0 is moot.
+ *   - causal prefix states include token i itself (j <= i) ([deck] slide 4).
+ *   - no 1/sqrt(D) scaling and no epsilon in the denominator; phi > 0 makes
+ *     every denominator positive.
+ *   - the decode step updates the state first and then reads it out, so it
+ *     reproduces the inclusive causal forward ([review] "Proposed method",
+ *     two-step update; [deck] slide 4).
+ *   - the backward pass differentiates with respect to the raw Q, K, V,
+ *     through phi and through the denominator.  The pages only sketch the
+ *     numerator part ([summary] appendix A) and leave the rest to autograd;
+ *     the formulas used here are derived in the comments of
+ *     orc_backward_causal and pinned by finite differences in the tests.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* phi(x) = elu(x) + 1 ([deck] slide 3; [summary] 3.2.1). */
+static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* d phi / dx: 1 for x > 0, exp(x) otherwise. */
+static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Elementwise phi and phi' over n values (used to pin phi itself). */
+void orc_feature_map(const double *x, double *y, double *dy, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        y[i] = phi(x[i]);
+        if (dy) dy[i] = dphi(x[i]);
+    }
+}
+
+/*
+ * Causal forward ([deck] slide 4; [review] "Proposed method"; [summary] 3.3):
+ *   S_i = S_{i-1} + phi(K_i) V_i^T        (D x M)
+ *   Z_i = Z_{i-1} + phi(K_i)              (D)
+ *   out_i = S_i^T phi(Q_i) / (phi(Q_i) . Z_i)
+ * S_io / Z_io (nullable, [B][H][D][M] and [B][H][D]) hold the starting state
+ * on entry and the final state S_N, Z_N on return; when null the state starts
+ * at zero.  den (nullable, [B][H][N]) receives each denominator.
+ */
+void orc_forward_causal(const double *q, const double *k, const double *v,
+                        double *out, double *S_io, double *Z_io, double *den,
+                        int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M;
+        double *O = out + bh * N * M;
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)D, sizeof(double));
+        double *qh = (double *)malloc((size_t)D * sizeof(double));
+        double *kh = (double *)malloc((size_t)D * sizeof(double));
+        if (S_io) memcpy(S, S_io + bh * D * M, (size_t)(D * M) * sizeof(double));
+        if (Z_io) memcpy(Z, Z_io + bh * D, (size_t)D * sizeof(double));
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t d = 0; d < D; ++d) {
+                kh[d] = phi(K[i * D + d]);
+                qh[d] = phi(Q[i * D + d]);
+            }
+            /* state update, token i included */
+            for (int64_t d = 0; d < D; ++d) {
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += kh[d] * V[i * M + m];
+                Z[d] += kh[d];
+            }
+            /* readout */
+            double dd = 0.0;
+            for (int64_t d = 0; d < D; ++d) dd += qh[d] * Z[d];
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t d = 0; d < D; ++d) n += qh[d] * S[d * M + m];
+                O[i * M + m] = n / dd;
+            }
+            if (den) den[bh * N + i] = dd;
+        }
+        if (S_io) memcpy(S_io + bh * D * M, S, (size_t)(D * M) * sizeof(double));
+        if (Z_io) memcpy(Z_io + bh * D, Z, (size_t)D * sizeof(double));
+        free(S); free(Z); free(qh); free(kh);
+    }
+}
+
+/*
+ * Non-causal forward ([review] "Proposed method"; [summary] 3.2; [deck]
+ * slide 3): S = sum_j phi(K_j) V_j^T and Z = sum_j phi(K_j) over all N
+ * tokens, then out_i = S^T phi(Q_i) / (phi(Q_i) . Z).
+ */
+void orc_forward_noncausal(const double *q, const double *k, const double *v,
+                           double *out, int64_t B, int64_t H, int64_t N,
+                           int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M;
+        double *O = out + bh * N * M;
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)D, sizeof(double));
+        double *qh = (double *)malloc((size_t)D * sizeof(double));
+        for (int64_t j = 0; j < N; ++j) {
+            for (int64_t d = 0; d < D; ++d) {
+                double kd = phi(K[j * D + d]);
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += kd * V[j * M + m];
+                Z[d] += kd;
+            }
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            double dd = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                qh[d] = phi(Q[i * D + d]);
+                dd += qh[d] * Z[d];
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t d = 0; d < D; ++d) n += qh[d] * S[d * M + m];
+                O[i * M + m] = n / dd;
+            }
+        }
+        free(S); free(Z); free(qh);
+    }
+}
+
+/*
+ * Causal backward.  With loss L = sum_i G_i . out_i (G = dout), write
+ * qh_i = phi(Q_i), kh_j = phi(K_j), a_ij = qh_i . kh_j for j <= i,
+ * d_i = sum_{j<=i} a_ij and out_i = sum_{j<=i} a_ij V_j / d_i.  Then
+ *   dL/da_ij = G_i . (V_j - out_i) / d_i = g_i . V_j + h_i,
+ *   with g_i = G_i / d_i and h_i = -(G_i . out_i) / d_i.
+ * Summing over the indices each a_ij touches:
+ *   dL/dqh_i = sum_{j<=i} (g_i . V_j + h_i) kh_j = S_i g_i + h_i Z_i
+ *              (no sum over later tokens: [summary] appendix A, eq. 13),
+ *   dL/dkh_j = sum_{i>=j} (g_i . V_j + h_i) qh_i = R_j V_j + u_j,
+ *   dL/dV_j  = sum_{i>=j} a_ij g_i = R_j^T kh_j,
+ *   with the reverse prefix sums R_j = sum_{i>=j} qh_i g_i^T (D x M) and
+ *   u_j = sum_{i>=j} h_i qh_i (D) ([summary] appendix A, eqs. 14-15: key j
+ *   affects every output i >= j, and this sum runs in the opposite direction
+ *   to the forward one).  Finally dQ = dL/dqh * phi'(Q), dK = dL/dkh * phi'(K).
+ * Pass 1 runs i = 1..N and rebuilds S_i, Z_i, d_i, out_i as the forward does;
+ * it keeps only g (N x M) and h (N), never the N states S_i.  Pass 2 runs
+ * j = N..1 carrying R and u.
+ */
+void orc_backward_causal(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk, double *dv,
+                         int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M, *G = dout + bh * N * M;
+        double *dQ = dq + bh * N * D, *dK = dk + bh * N * D, *dV = dv + bh * N * M;
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)D, sizeof(double));
+        double *g = (double *)malloc((size_t)(N * M) * sizeof(double));
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+        double *qh = (double *)malloc((size_t)D * sizeof(double));
+        double *kh = (double *)malloc((size_t)D * sizeof(double));
+        double *o = (double *)malloc((size_t)M * sizeof(double));
+
+        /* pass 1: forward direction */
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t d = 0; d < D; ++d) {
+                kh[d] = phi(K[i * D + d]);
+                qh[d] = phi(Q[i * D + d]);
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += kh[d] * V[i * M + m];
+                Z[d] += kh[d];
+            }
+            double dd = 0.0;
+            for (int64_t d = 0; d < D; ++d) dd += qh[d] * Z[d];
+            double go = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t d = 0; d < D; ++d) n += qh[d] * S[d * M + m];
+                o[m] = n / dd;
+                go += G[i * M + m] * o[m];
+            }
+            for (int64_t m = 0; m < M; ++m) g[i * M + m] = G[i * M + m] / dd;
+            h[i] = -go / dd;
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = h[i] * Z[d];
+                for (int64_t m = 0; m < M; ++m) acc += S[d * M + m] * g[i * M + m];
+                dQ[i * D + d] = acc * dphi(Q[i * D + d]);
+            }
+        }
+
+        /* pass 2: reverse direction; S is reused as R, Z as u */
+        memset(S, 0, (size_t)(D * M) * sizeof(double));
+        memset(Z, 0, (size_t)D * sizeof(double));
+        for (int64_t j = N - 1; j >= 0; --j) {
+            for (int64_t d = 0; d < D; ++d) {
+                qh[d] = phi(Q[j * D + d]);
+                kh[d] = phi(K[j * D + d]);
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += qh[d] * g[j * M + m];
+                Z[d] += h[j] * qh[d];
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = Z[d];
+                for (int64_t m = 0; m < M; ++m) acc += S[d * M + m] * V[j * M + m];
+                dK[j * D + d] = acc * dphi(K[j * D + d]);
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc += S[d * M + m] * kh[d];
+                dV[j * M + m] = acc;
+            }
+        }
+        free(S); free(Z); free(g); free(h); free(qh); free(kh); free(o);
+    }
+}
+
+/*
+ * One RNN-style decode step for B*H independent streams ([review] "Proposed
+ * method", attention memory s and normalizer memory z; [summary] 3.3.2, 3.4;
+ * [deck] slide 4): S += phi(k) v^T, Z += phi(k), then
+ * out = S^T phi(q) / (phi(q) . Z).  q,k: [B][H][D]; v,out: [B][H][M];
+ * S: [B][H][D][M]; Z: [B][H][D]; S and Z are updated in place.
+ */
+void orc_decode_step(const double *q, const double *k, const double *v,
+                     double *S, double *Z, double *out,
+                     int64_t B, int64_t H, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *qq = q + bh * D, *kk = k + bh * D, *vv = v + bh * M;
+        double *SS = S + bh * D * M, *ZZ = Z + bh * D, *oo = out + bh * M;
+        double dd = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            double kd = phi(kk[d]);
+            for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m];
+            ZZ[d] += kd;
+            dd += phi(qq[d]) * ZZ[d];
+        }
+        for (int64_t m = 0; m < M; ++m) {
+            double n = 0.0;
+            for (int64_t d = 0; d < D; ++d) n += phi(qq[d]) * SS[d * M + m];
+            oo[m] = n / dd;
+        }
+    }
+}

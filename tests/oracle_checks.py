@@ -1,0 +1,224 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each ``check_*`` takes an oracle library handle and raises AssertionError on a
+mismatch.  ``tests/test_oracle_pins.py`` runs them on the real oracle; the
+mutation tests run them on copies of the oracle source with a planted mistake
+and require that at least one check fails.
+
+What pins what:
+  * phi against numpy's exp and the closed form x + 1;
+  * causal and non-causal forward against the quadratic brute force (an
+    independent definition) and against exact rational arithmetic;
+  * closed forms: N = 1 gives V; identical keys give the running mean of V;
+    constant V gives V; D = 1 makes the output independent of Q;
+  * invariants: last causal row equals the non-causal row, Z_N = sum phi(K),
+    S_N = sum phi(K_j) V_j^T, positive denominators, convex-hull bounds,
+    carrying (S, Z) across a split equals one pass;
+  * decode: stacked decode steps equal the causal forward, and the state after
+    t steps equals the sum of outer products;
+  * backward: central finite differences, the independent quadratic gradient,
+    torch fp64 autograd of the brute force, and homogeneity/shift identities.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from tests import brute_force as bf
+
+
+def _rel(x, y):
+    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
+    return float(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300))
+
+
+def _rand(seed, *shape, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def check_phi(lib):
+    x = np.concatenate([np.linspace(-30, 30, 2001), [0.0, -0.0, 1e-300, -1e-300, -700.0, 5e-324]])
+    y, dy = oracle.feature_map(x, lib=lib)
+    pos = x > 0
+    assert np.array_equal(y[pos], x[pos] + 1.0)
+    assert np.allclose(y[~pos], np.exp(x[~pos]), rtol=4e-16, atol=0)
+    assert np.array_equal(dy[pos], np.ones(pos.sum()))
+    assert np.allclose(dy[~pos], np.exp(x[~pos]), rtol=4e-16, atol=0)
+    y0, dy0 = oracle.feature_map(np.array([0.0, -0.0]), lib=lib)
+    assert y0.tolist() == [1.0, 1.0] and dy0.tolist() == [1.0, 1.0]
+    assert (y > 0).all()
+
+
+def check_forward_vs_brute(lib):
+    shapes = [(1, 2, 256, 32, 32), (2, 3, 37, 5, 7), (1, 1, 1, 4, 3), (1, 2, 50, 1, 2), (2, 1, 65, 16, 1),
+              (1, 1, 200, 64, 64)]
+    for s, (B, H, N, D, M) in enumerate(shapes):
+        q = _rand(10 + s, B, H, N, D)
+        k = _rand(20 + s, B, H, N, D)
+        v = _rand(30 + s, B, H, N, M)
+        o = oracle.forward_causal(q, k, v, lib=lib)
+        assert _rel(o, bf.forward(q, k, v, True)) < 1e-12, (B, H, N, D, M)
+        onc = oracle.forward_noncausal(q, k, v, lib=lib)
+        assert _rel(onc, bf.forward(q, k, v, False)) < 1e-12, (B, H, N, D, M)
+
+
+def check_forward_exact(lib):
+    rng = np.random.default_rng(7)
+    N, D, M = 6, 3, 2
+    # dyadic positive entries: phi = x + 1 is exact and the rational result is exact
+    q = rng.integers(1, 9, (N, D)) / 8.0
+    k = rng.integers(1, 9, (N, D)) / 4.0
+    v = rng.integers(-8, 9, (N, M)) / 2.0
+    exact = bf.forward_causal_exact(bf.to_fractions(q), bf.to_fractions(k), bf.to_fractions(v))
+    o = oracle.forward_causal(q[None, None], k[None, None], v[None, None], lib=lib)[0, 0]
+    for i in range(N):
+        for m in range(M):
+            e = float(exact[i][m])
+            assert abs(o[i, m] - e) <= 4e-16 * max(1.0, abs(e)), (i, m, o[i, m], e)
+
+
+def check_closed_forms(lib):
+    # N = 1: out_1 = V_1
+    q, k, v = _rand(1, 2, 2, 1, 8), _rand(2, 2, 2, 1, 8), _rand(3, 2, 2, 1, 5)
+    assert np.allclose(oracle.forward_causal(q, k, v, lib=lib), v, rtol=1e-15, atol=1e-15)
+    # identical keys: out_i is the running mean of V, whatever Q is
+    N = 40
+    q = _rand(4, 1, 1, N, 6)
+    k = np.repeat(_rand(5, 1, 1, 1, 6), N, axis=2)
+    v = _rand(6, 1, 1, N, 3)
+    mean = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert _rel(oracle.forward_causal(q, k, v, lib=lib), mean) < 1e-13
+    # constant V: out = V
+    v = np.full((1, 1, N, 3), 2.5)
+    assert np.allclose(oracle.forward_causal(q, _rand(7, 1, 1, N, 6), v, lib=lib), 2.5, rtol=1e-14, atol=0)
+    # D = 1: phi(q) cancels in the ratio, so out does not depend on Q
+    k1, v1 = _rand(8, 1, 2, N, 1), _rand(9, 1, 2, N, 4)
+    o1 = oracle.forward_causal(_rand(10, 1, 2, N, 1), k1, v1, lib=lib)
+    o2 = oracle.forward_causal(_rand(11, 1, 2, N, 1) * 3.0, k1, v1, lib=lib)
+    assert _rel(o1, o2) < 1e-13
+    # ... but with D > 1 it does (guards against a readout that ignores Q)
+    o3 = oracle.forward_causal(_rand(10, 1, 2, N, 3), _rand(8, 1, 2, N, 3), v1, lib=lib)
+    o4 = oracle.forward_causal(_rand(11, 1, 2, N, 3) * 3.0, _rand(8, 1, 2, N, 3), v1, lib=lib)
+    assert _rel(o3, o4) > 1e-3
+
+
+def check_invariants(lib):
+    B, H, N, D, M = 2, 3, 97, 8, 5
+    q, k, v = _rand(40, B, H, N, D), _rand(41, B, H, N, D), _rand(42, B, H, N, M)
+    o, S, Z, den = oracle.forward_causal(q, k, v, return_state=True, return_den=True, lib=lib)
+    onc = oracle.forward_noncausal(q, k, v, lib=lib)
+    assert _rel(o[:, :, -1], onc[:, :, -1]) < 1e-13
+    kh = bf.phi(k)
+    assert _rel(Z, kh.sum(2)) < 1e-14
+    assert _rel(S, np.einsum("bhnd,bhnm->bhdm", kh, v)) < 1e-13
+    assert (den > 0).all()
+    assert _rel(den, (bf.phi(q) * np.cumsum(kh, axis=2)).sum(-1)) < 1e-13
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    assert (o >= lo - 1e-12).all() and (o <= hi + 1e-12).all()
+    # first row is exactly V_1 up to rounding
+    assert np.allclose(o[:, :, 0], v[:, :, 0], rtol=1e-14, atol=1e-14)
+    # carrying the state across a split equals one pass
+    c = 41
+    o_a, S_a, Z_a = oracle.forward_causal(q[:, :, :c], k[:, :, :c], v[:, :, :c], return_state=True, lib=lib)
+    o_b, S_b, Z_b = oracle.forward_causal(q[:, :, c:], k[:, :, c:], v[:, :, c:], S0=S_a, Z0=Z_a,
+                                          return_state=True, lib=lib)
+    assert _rel(np.concatenate([o_a, o_b], axis=2), o) < 1e-14
+    assert _rel(S_b, S) < 1e-14 and _rel(Z_b, Z) < 1e-14
+
+
+def check_decode(lib):
+    B, H, T, D, M = 3, 2, 60, 6, 4
+    qs, ks, vs = _rand(50, T, B, H, D), _rand(51, T, B, H, D), _rand(52, T, B, H, M)
+    S = np.zeros((B, H, D, M))
+    Z = np.zeros((B, H, D))
+    outs = []
+    for t in range(T):
+        if t == 25:   # save and resume: continue from copies of the state
+            S, Z = S.copy(), Z.copy()
+        outs.append(oracle.decode_step(qs[t], ks[t], vs[t], S, Z, lib=lib))
+    dec = np.stack(outs, axis=2)                   # [B,H,T,M]
+    tr = lambda x: np.ascontiguousarray(np.moveaxis(x, 0, 2))
+    fwd = bf.forward(tr(qs), tr(ks), tr(vs), True)
+    assert _rel(dec, fwd) < 1e-13
+    kh = bf.phi(tr(ks))
+    assert _rel(S, np.einsum("bhnd,bhnm->bhdm", kh, tr(vs))) < 1e-13
+    assert _rel(Z, kh.sum(2)) < 1e-14
+
+
+def check_backward_vs_quadratic(lib):
+    for s, (B, H, N, D, M) in enumerate([(1, 2, 64, 8, 6), (2, 1, 33, 3, 9), (1, 1, 1, 4, 4), (1, 1, 120, 32, 32)]):
+        q, k, v, g = (_rand(60 + 4 * s + i, B, H, N, x) for i, x in enumerate((D, D, M, M)))
+        dq, dk, dv = oracle.backward_causal(q, k, v, g, lib=lib)
+        rq, rk, rv = bf.backward_causal(q, k, v, g)
+        if N == 1:
+            # out_1 = V_1 whatever Q, K are: dQ = dK = 0 and dV = G
+            assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14 and _rel(dv, g) < 1e-15
+            continue
+        assert _rel(dq, rq) < 1e-11 and _rel(dk, rk) < 1e-11 and _rel(dv, rv) < 1e-11, (B, H, N, D, M)
+
+
+def check_backward_fd(lib):
+    B, H, N, D, M = 1, 1, 7, 3, 2
+    q, k, v, g = _rand(70, B, H, N, D), _rand(71, B, H, N, D), _rand(72, B, H, N, M), _rand(73, B, H, N, M)
+    dq, dk, dv = oracle.backward_causal(q, k, v, g, lib=lib)
+
+    def loss(q_, k_, v_):
+        return float((oracle.forward_causal(q_, k_, v_, lib=lib) * g).sum())
+
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        base = [q, k, v]
+        num = np.zeros_like(base[which])
+        it = np.nditer(num, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            p = [x.copy() for x in base]
+            m_ = [x.copy() for x in base]
+            p[which][idx] += eps
+            m_[which][idx] -= eps
+            num[idx] = (loss(*p) - loss(*m_)) / (2 * eps)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-8), (which, np.abs(grad - num).max())
+
+
+def check_backward_autograd(lib):
+    import torch
+
+    B, H, N, D, M = 2, 2, 45, 6, 5
+    arrs = [_rand(80 + i, B, H, N, x) for i, x in enumerate((D, D, M, M))]
+    q, k, v, g = (torch.tensor(a, dtype=torch.float64) for a in arrs)
+    q.requires_grad_(True); k.requires_grad_(True); v.requires_grad_(True)
+    qh = torch.nn.functional.elu(q) + 1.0
+    kh = torch.nn.functional.elu(k) + 1.0
+    a = torch.tril(qh @ kh.transpose(-1, -2).contiguous())
+    o = (a @ v) / a.sum(-1, keepdim=True)
+    (o * g).sum().backward()
+    dq, dk, dv = oracle.backward_causal(*arrs, lib=lib)
+    assert _rel(dq, q.grad.numpy()) < 1e-11
+    assert _rel(dk, k.grad.numpy()) < 1e-11
+    assert _rel(dv, v.grad.numpy()) < 1e-11
+
+
+def check_backward_identities(lib):
+    B, H, N, D, M = 1, 2, 300, 16, 12
+    q, k, v, g = _rand(90, B, H, N, D), _rand(91, B, H, N, D), _rand(92, B, H, N, M), _rand(93, B, H, N, M)
+    dq, dk, dv = oracle.backward_causal(q, k, v, g, lib=lib)
+    o = oracle.forward_causal(q, k, v, lib=lib)
+    # shifting V[:, m] by t shifts out[:, m] by t, so sum_j dV_j = sum_i G_i
+    assert _rel(dv.sum(2), g.sum(2)) < 1e-12
+    # out is linear in V: sum_j V_j . dV_j = sum_i G_i . out_i
+    assert abs((v * dv).sum() - (g * o).sum()) < 1e-10 * max(1.0, abs((g * o).sum()))
+    # out_i is 0-homogeneous in phi(Q_i): sum_d dQ_id * phi(Q_id)/phi'(Q_id) = 0 per token
+    w = 1.0 + np.maximum(q, 0.0)
+    assert np.abs((dq * w).sum(-1)).max() < 1e-11 * np.abs(dq * w).max() * D
+    # ... and 0-homogeneous in all phi(K) together: the sum vanishes per (b, h)
+    wk = 1.0 + np.maximum(k, 0.0)
+    per_bh = (dk * wk).sum(axis=(2, 3))
+    assert np.abs(per_bh).max() < 1e-10 * np.abs(dk * wk).sum()
+    # the gradient is not trivially zero
+    assert np.abs(dq).max() > 1e-3 and np.abs(dk).max() > 1e-3
+
+
+ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,
+              check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
+              check_backward_identities]
