@@ -1,0 +1,136 @@
+/*
+ * la.h -- C ABI of the MI355X (gfx950) kernelized linear-attention library.
+ *
+ * The method (Katharopoulos et al., "Transformers are RNNs: Fast
+ * Autoregressive Transformers with Linear Attention", ICML 2020), as stated
+ * on the pages this library is built from:
+ *   [review]  nubint.ai, "[Paper Review] Transformers are RNNs: ...",
+ *             section "Proposed method".
+ *   [summary] paperlayer.ai, "Transformers are RNNs: ..." summary of arXiv
+ *             2006.16236v3, sections 3.2, 3.2.1, 3.3, 3.3.1, 3.3.2, 3.4 and
+ *             appendix "A. Gradient Derivation".
+ *   [deck]    zhengyuhong.cn, "Transformers are RNNs: ... 解读", slides 3-4.
+ *
+ * Feature map phi(x) = elu(x) + 1 ([deck] slide 3; [summary] 3.2.1): x + 1
+ * for x > 0, exp(x) otherwise.  No 1/sqrt(D) scale and no epsilon: phi > 0
+ * keeps every denominator positive.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major, in device memory owned by the caller:
+ *     q, k are [B][H][N][D]; v, out, dout are [B][H][N][M] (decode: no N).
+ *     dt gives the element type of q, k, v, out, dout, dq, dk, dv (fp32 or
+ *     bf16).  All state and accumulation is fp32 inside the kernels.
+ *   - Supported head sizes: D, M in {32, 64}.  B, H, N >= 1.
+ *   - Every tensor pointer must be 16-byte aligned; outputs must not overlap
+ *     any input or each other.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  The library
+ *     never allocates, frees or synchronizes; scratch memory is the caller's
+ *     `workspace`, at least la_workspace_size(...) bytes, 256-byte aligned.
+ *     Workspace contents need no initialization and are clobbered.
+ *   - Argument errors are reported before anything is launched and leave all
+ *     buffers untouched.  LA_ERR_HIP reports a failed launch.  Non-finite
+ *     inputs are not errors; they propagate to the outputs.
+ *   - The library keeps no global state; calls on different streams are
+ *     independent as long as their buffers (workspace included) are
+ *     disjoint.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, overlap */
+    LA_ERR_UNSUPPORTED = 2,      /* D or M outside the supported set, unknown dtype */
+    LA_ERR_WORKSPACE = 3,        /* workspace missing, misaligned or too small */
+    LA_ERR_HIP = 4               /* a kernel launch failed */
+} la_status_t;
+
+typedef enum { LA_OP_FWD_CAUSAL = 0, LA_OP_FWD_NONCAUSAL = 1, LA_OP_BWD_CAUSAL = 2 } la_op_t;
+
+/*
+ * Causal forward ([deck] slide 4; [review] "Proposed method"; [summary] 3.3,
+ * 3.3.2 parallel training-time form):
+ *   S_i = S_{i-1} + phi(K_i) V_i^T,  Z_i = Z_{i-1} + phi(K_i),
+ *   out_i = phi(Q_i)^T S_i / (phi(Q_i)^T Z_i),   S_0 = 0, Z_0 = 0,
+ * independently for each (b, h).  Token i sees itself (j <= i).
+ * q, k: [B][H][N][D]; v: [B][H][N][M] (inputs, read only).
+ * out: [B][H][N][M] (output, fully written).
+ */
+la_status_t la_forward_causal(const void *q, const void *k, const void *v, void *out,
+                              int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                              la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * Non-causal forward through associativity ([review] "Proposed method";
+ * [summary] 3.2; [deck] slide 3): S = sum_j phi(K_j) V_j^T and
+ * Z = sum_j phi(K_j) over all N tokens of each (b, h), then
+ * out_i = phi(Q_i)^T S / (phi(Q_i)^T Z).  Same arguments as the causal call.
+ */
+la_status_t la_forward_noncausal(const void *q, const void *k, const void *v, void *out,
+                                 int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                 la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Causal backward ([summary] 3.3.1 and appendix A: gradients through
+ * cumulative sums, in linear time, never storing every S_i).  Given
+ * dout = dL/dout for out = la_forward_causal(q, k, v), writes the gradients
+ * with respect to the raw inputs (through phi and the denominator):
+ *   dq, dk: [B][H][N][D];  dv: [B][H][N][M]  (outputs, fully written).
+ * The forward quantities (denominators, out) are recomputed; out is not an
+ * argument.  With g_i = dout_i / d_i and h_i = -(dout_i . out_i) / d_i:
+ *   dL/dphi(Q_i) = S_i g_i + h_i Z_i,
+ *   dL/dphi(K_j) = R_j V_j + u_j,  dv_j = R_j^T phi(K_j),
+ *   R_j = sum_{i>=j} phi(Q_i) g_i^T,  u_j = sum_{i>=j} h_i phi(Q_i),
+ * and dq = dL/dphi(Q) * phi'(Q), dk = dL/dphi(K) * phi'(K).
+ */
+la_status_t la_backward_causal(const void *q, const void *k, const void *v, const void *dout,
+                               void *dq, void *dk, void *dv,
+                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                               la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * One RNN-style decode step for B*H independent streams ([review] "Proposed
+ * method": attention memory s and normalizer memory z with a two-step update;
+ * [summary] 3.3.2 and 3.4; [deck] slide 4):
+ *   S += phi(k) v^T;  Z += phi(k);  out = S^T phi(q) / (phi(q)^T Z).
+ * The update comes first, so a sequence of steps reproduces the causal
+ * forward.  q, k: [B][H][D]; v, out: [B][H][M] in dtype dt.
+ * S: [B][H][D][M] fp32 and Z: [B][H][D] fp32 are read and updated in place;
+ * the caller zeroes them before the first token and may save/restore them
+ * between calls (they are the whole recurrent state).  No workspace.
+ */
+la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S, float *Z,
+                           void *out, int64_t B, int64_t H, int64_t D, int64_t M,
+                           la_dtype_t dt, hipStream_t stream);
+
+/* Bytes of workspace `op` needs for this shape (0 if the shape is invalid). */
+size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                         la_dtype_t dt);
+
+/* Static, human-readable name of a status code. */
+const char *la_status_string(la_status_t s);
+
+/* LA_ABI_VERSION of the loaded library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

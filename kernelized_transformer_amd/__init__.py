@@ -1,0 +1,169 @@
+"""Python binding of the gfx950 kernelized linear-attention library (libla.so).
+
+Thin ctypes wrapper over the C ABI in ``include/la.h``: it only checks that
+arguments are device tensors of the right dtype and layout, allocates outputs
+and workspace with torch (device memory plumbing), and passes raw pointers and
+the current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no CPU or PyTorch fallback.  If ``libla.so`` has not been
+built, every call raises.
+
+Functions carry the C names:
+  la_forward_causal(q, k, v, out=None, workspace=None)
+  la_forward_noncausal(q, k, v, out=None, workspace=None)
+  la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
+  la_decode_step(q, k, v, S, Z, out=None)
+  la_workspace_size(op, B, H, N, D, M, dtype)
+  la_status_string(status), la_abi_version()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["la_forward_causal", "la_forward_noncausal", "la_backward_causal", "la_decode_step",
+           "la_workspace_size", "la_status_string", "la_abi_version", "LAError", "lib_path", "load",
+           "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
+
+LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
+LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL = 0, 1, 2
+_DT = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libla.so")
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {la_status_string(status)} ({status})")
+
+
+def load():
+    """Load libla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"HIP library not built: {lib_path} is missing "
+                           "(run `python -m kernelized_transformer_amd.build`)")
+    lib = ctypes.CDLL(lib_path)
+    vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    fwd = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_forward_causal.argtypes = fwd
+    lib.la_forward_noncausal.argtypes = fwd
+    lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    for f in ("la_forward_causal", "la_forward_noncausal", "la_backward_causal", "la_decode_step"):
+        getattr(lib, f).restype = i32
+    lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
+    lib.la_workspace_size.restype = sz
+    lib.la_status_string.argtypes = [i32]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_abi_version.argtypes = []
+    lib.la_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def la_status_string(status: int) -> str:
+    return load().la_status_string(int(status)).decode()
+
+
+def la_abi_version() -> int:
+    return int(load().la_abi_version())
+
+
+def la_workspace_size(op: int, B: int, H: int, N: int, D: int, M: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load().la_workspace_size(int(op), B, H, N, D, M, dt))
+
+
+def _dev(*ts: torch.Tensor):
+    dev = ts[0].device
+    for t in ts:
+        if not (t.is_cuda and t.device == dev and t.is_contiguous()):
+            raise ValueError("expected contiguous tensors on the same GPU")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ws(op, B, H, N, D, M, dtype, workspace, dev):
+    need = la_workspace_size(op, B, H, N, D, M, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _check(func: str, status: int):
+    if status != 0:
+        raise LAError(func, status)
+
+
+def _forward(func: str, op: int, q, k, v, out, workspace):
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k: [B,H,N,D]; v: [B,H,N,M]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    _dev(q, out)
+    ws, wsb = _ws(op, B, H, N, D, M, q.dtype, workspace, dev)
+    st = getattr(load(), func)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
+                               _DT[q.dtype], ws.data_ptr(), wsb, _stream(dev))
+    _check(func, st)
+    return out
+
+
+def la_forward_causal(q, k, v, out=None, workspace=None):
+    """Causal linear attention forward; returns out [B,H,N,M]."""
+    return _forward("la_forward_causal", LA_OP_FWD_CAUSAL, q, k, v, out, workspace)
+
+
+def la_forward_noncausal(q, k, v, out=None, workspace=None):
+    """Non-causal linear attention forward; returns out [B,H,N,M]."""
+    return _forward("la_forward_noncausal", LA_OP_FWD_NONCAUSAL, q, k, v, out, workspace)
+
+
+def la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of sum(dout * la_forward_causal(q, k, v)); returns (dq, dk, dv)."""
+    dev = _dev(q, k, v, dout)
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v, dout must share dtype float32 or bfloat16")
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _dev(q, dq, dk, dv)
+    ws, wsb = _ws(LA_OP_BWD_CAUSAL, B, H, N, D, M, q.dtype, workspace, dev)
+    st = load().la_backward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), B, H, N, D, M, _DT[q.dtype], ws.data_ptr(), wsb,
+                                   _stream(dev))
+    _check("la_backward_causal", st)
+    return dq, dk, dv
+
+
+def la_decode_step(q, k, v, S, Z, out=None):
+    """One decode step; q,k: [B,H,D], v: [B,H,M]; S [B,H,D,M] and Z [B,H,D] fp32 are updated in place."""
+    dev = _dev(q, k, v, S, Z)
+    if S.dtype != torch.float32 or Z.dtype != torch.float32:
+        raise ValueError("S and Z must be float32")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, D = q.shape
+    M = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, M), dtype=q.dtype, device=dev)
+    st = load().la_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), S.data_ptr(), Z.data_ptr(),
+                               out.data_ptr(), B, H, D, M, _DT[q.dtype], _stream(dev))
+    _check("la_decode_step", st)
+    return out

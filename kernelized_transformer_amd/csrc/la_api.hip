@@ -1,0 +1,158 @@
+// la_api.hip -- the C ABI declared in include/la.h: argument validation,
+// workspace sizing and dispatch to the kernel launchers.  Stateless.
+#include "la.h"
+#include "la_internal.h"
+
+namespace {
+
+using la::align256;
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+};
+
+Span span(const void *p, size_t bytes) {
+    Span s;
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+    return s;
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t esize(la_dtype_t dt) { return dt == LA_DTYPE_F32 ? 4 : 2; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+la_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt) {
+    if (B < 1 || H < 1 || N < 1 || D < 1 || M < 1) return LA_ERR_INVALID_ARGUMENT;
+    if (B > kMaxElems || H > kMaxElems || N > kMaxElems) return LA_ERR_INVALID_ARGUMENT;
+    if (B * H > kMaxElems / N) return LA_ERR_INVALID_ARGUMENT;
+    if (dt != LA_DTYPE_F32 && dt != LA_DTYPE_BF16) return LA_ERR_UNSUPPORTED;
+    if ((D != 32 && D != 64) || (M != 32 && M != 64)) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+// Pointers: all non-null and 16-byte aligned; no output overlaps any other
+// buffer (inputs may alias each other).
+la_status_t check_buffers(const Span *in, int nin, const Span *outs, int nout) {
+    for (int i = 0; i < nin; ++i)
+        if (in[i].lo == 0 || (in[i].lo & 15)) return LA_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < nout; ++i) {
+        if (outs[i].lo == 0 || (outs[i].lo & 15)) return LA_ERR_INVALID_ARGUMENT;
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i], in[j])) return LA_ERR_INVALID_ARGUMENT;
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return LA_ERR_INVALID_ARGUMENT;
+    }
+    return LA_OK;
+}
+
+la_status_t check_workspace(void *ws, size_t have, size_t need, const Span *bufs, int nb) {
+    if (need == 0) return LA_OK;
+    if (ws == nullptr || !aligned(ws, 256) || have < need) return LA_ERR_WORKSPACE;
+    const Span w = span(ws, need);
+    for (int i = 0; i < nb; ++i)
+        if (overlap(w, bufs[i])) return LA_ERR_WORKSPACE;
+    return LA_OK;
+}
+
+la_status_t forward_common(bool causal, const void *q, const void *k, const void *v, void *out, int64_t B,
+                           int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, D, M, dt);
+    if (st != LA_OK) return st;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[3] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
+                        span(v, size_t(BH * N * M) * es)};
+    const Span o[1] = {span(out, size_t(BH * N * M) * es)};
+    if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
+    const Span all[4] = {in[0], in[1], in[2], o[0]};
+    if ((st = check_workspace(workspace, workspace_bytes, la::forward_workspace_bytes(BH, N, D, M), all, 4)) !=
+        LA_OK)
+        return st;
+    const hipError_t e = la::launch_forward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+                                            static_cast<float *>(workspace), stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+la_status_t la_forward_causal(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
+                              int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    return forward_common(true, q, k, v, out, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
+}
+
+la_status_t la_forward_noncausal(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
+                                 int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return forward_common(false, q, k, v, out, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
+}
+
+la_status_t la_backward_causal(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                               void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, D, M, dt);
+    if (st != LA_OK) return st;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[4] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
+                        span(v, size_t(BH * N * M) * es), span(dout, size_t(BH * N * M) * es)};
+    const Span o[3] = {span(dq, size_t(BH * N * D) * es), span(dk, size_t(BH * N * D) * es),
+                       span(dv, size_t(BH * N * M) * es)};
+    if ((st = check_buffers(in, 4, o, 3)) != LA_OK) return st;
+    const Span all[7] = {in[0], in[1], in[2], in[3], o[0], o[1], o[2]};
+    if ((st = check_workspace(workspace, workspace_bytes, la::backward_workspace_bytes(BH, N, D, M, es), all, 7)) !=
+        LA_OK)
+        return st;
+    const hipError_t e = la::launch_backward(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, dout, dq, dk, dv, BH, N, D, M,
+                                             static_cast<float *>(workspace), stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S, float *Z, void *out, int64_t B,
+                           int64_t H, int64_t D, int64_t M, la_dtype_t dt, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, 1, D, M, dt);
+    if (st != LA_OK) return st;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[3] = {span(q, size_t(BH * D) * es), span(k, size_t(BH * D) * es), span(v, size_t(BH * M) * es)};
+    const Span o[3] = {span(S, size_t(BH * D * M) * 4), span(Z, size_t(BH * D) * 4), span(out, size_t(BH * M) * es)};
+    if ((st = check_buffers(in, 3, o, 3)) != LA_OK) return st;
+    const hipError_t e =
+        la::launch_decode(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, S, Z, out, BH, D, M, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt) {
+    if (check_shape(B, H, N, D, M, dt) != LA_OK) return 0;
+    switch (op) {
+    case LA_OP_FWD_CAUSAL:
+    case LA_OP_FWD_NONCAUSAL:
+        return la::forward_workspace_bytes(B * H, N, D, M);
+    case LA_OP_BWD_CAUSAL:
+        return la::backward_workspace_bytes(B * H, N, D, M, esize(dt));
+    }
+    return 0;
+}
+
+const char *la_status_string(la_status_t s) {
+    switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARGUMENT: return "LA_ERR_INVALID_ARGUMENT";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+    }
+    return "LA_ERR_UNKNOWN";
+}
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+} // extern "C"

@@ -1,0 +1,341 @@
+// la_backward.hip -- causal backward through cumulative sums on gfx950.
+//
+// Method ([summary] = paperlayer.ai summary of "Transformers are RNNs",
+// section 3.3.1 and appendix "A. Gradient Derivation"): the gradient is
+// evaluated in linear time with running sums, never storing every S_i; the
+// query gradient uses the forward-direction sum and the key/value gradients
+// a sum of the same size running in the opposite direction.  The pages give
+// the numerator part for feature-mapped inputs; the denominator and phi'
+// terms are written out here.  With qh = phi(Q), kh = phi(K),
+// a_ij = qh_i . kh_j (j <= i), d_i = sum_{j<=i} a_ij, out_i = num_i / d_i,
+// and dout = G:
+//   g_i = G_i / d_i,  h_i = -(G_i . out_i) / d_i,  gh_i = [g_i, h_i],
+//   vh_j = [V_j, 1],  dA_ij = dL/da_ij = gh_i . vh_j,
+//   dL/dqh_i = sum_{j<=i} dA_ij kh_j = S_aug_{i} gh_i          (forward sum)
+//   dL/dkh_j = sum_{i>=j} dA_ij qh_i = R_aug_{j} vh_j          (reverse sum)
+//   dV_j     = sum_{i>=j} a_ij g_i   = R_j^T kh_j
+//   with S_aug = [S | Z] and R_aug = sum_{i>=j} qh_i gh_i^T = [R | u];
+//   dQ = dL/dqh * phi'(Q), dK = dL/dkh * phi'(K).
+// Chunked exactly like the forward (16-token chunks here, so that the three
+// fp32 states of a wavefront fit in registers):
+//   1. k_segment_state + scan  -> S_aug at the start of every segment;
+//   2. k_bwd_dq    (forward direction, one wavefront per segment): recompute
+//      out and d for the chunk, form gh, write dQ, store g and h for pass 4,
+//      and accumulate the segment's sum_i qh_i gh_i^T;
+//   3. reverse scan            -> R_aug after the end of every segment;
+//   4. k_bwd_dkdv  (reverse direction): walk the chunks backwards carrying
+//      R_aug, write dK and dV.
+#include "la_chunk.h"
+#include "la_internal.h"
+
+namespace la {
+
+constexpr int BTT = 1;  // token tiles per chunk in the backward kernels
+constexpr int BCH = 16 * BTT;
+
+// ---- pass 2: forward direction --------------------------------------------
+template <typename T, int D, int M>
+__global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
+                                               const T *__restrict__ v, const T *__restrict__ dout,
+                                               T *__restrict__ dq, const float *__restrict__ wsS,
+                                               float *__restrict__ wsR, T *__restrict__ gbuf,
+                                               float *__restrict__ hbuf, int64_t N, int64_t nseg,
+                                               int64_t seg_tokens, int64_t rec) {
+    typedef typename IO<T>::frag Fr;
+    typedef typename IO<T>::vec4 V4;
+    constexpr int DT = D / 16, MT = M / 16;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    const T *Q = q + bh * N * D;
+    const T *K = k + bh * N * D;
+    const T *V = v + bh * N * M;
+    const T *G = dout + bh * N * M;
+    T *DQ = dq + bh * N * D;
+    T *GB = gbuf + bh * N * M;
+    float *HB = hbuf + bh * N;
+
+    const float *srec = wsS + (bh * nseg + seg) * rec;
+    f32x4 St[DT][MT + 1];      // S_aug, rows d
+    f32x4 StT[MT + 1][DT];     // S_aug^T, rows m'
+    f32x4 Ra[DT][MT + 1];      // this segment's sum_i qh_i gh_i^T, rows d
+    state_load<D, M>(St, srec);
+    stateT_load<D, M>(StT, srec);
+    state_zero<D, M>(Ra);
+
+    const Fr ones = frag_row0_ones<Fr>();
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
+    load_chunk<T, D, BTT>(rq, Q, t_begin, t_end);
+    load_chunk<T, D, BTT>(rk, K, t_begin, t_end);
+    load_chunk<T, M, BTT>(rv, V, t_begin, t_end);
+    load_chunk<T, M, BTT>(rg, G, t_begin, t_end);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += BCH) {
+        Fr Qn[BTT][DT], Kn[BTT][DT], Vn[BTT][MT];
+        phi_frags<T, D, BTT>(Qn, rq, t0, t_end);
+        phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
+        raw_frags<T, M, BTT>(Vn, rv);
+        f32x4 qraw[DT], graw[MT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) qraw[dt] = IO<T>::to_f32(rq[0][dt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) graw[mt] = IO<T>::to_f32(rg[0][mt]);
+        if (t0 + BCH < t_end) {
+            load_chunk<T, D, BTT>(rq, Q, t0 + BCH, t_end);
+            load_chunk<T, D, BTT>(rk, K, t0 + BCH, t_end);
+            load_chunk<T, M, BTT>(rv, V, t0 + BCH, t_end);
+            load_chunk<T, M, BTT>(rg, G, t0 + BCH, t_end);
+        }
+        const int64_t t = t0 + c;   // this lane's query token
+        const bool valid = t < t_end;
+
+        Fr KT[BTT][DT], VT[BTT][MT];
+        transpose_frags<Fr, DT, BTT>(KT, Kn);
+        transpose_frags<Fr, MT, BTT>(VT, Vn);
+
+        // recompute out^T (and den in the normalizer block) as the forward does
+        f32x4 Ot[MT + 1];
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[0][dt], Kn[0][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+        const Fr PT = IO<T>::to_frag(p);
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) {
+            Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dt = 0; dt < DT; dt += 2)
+                mma2(Ot[mt], IO<T>::to_frag(St[dt][mt]), IO<T>::to_frag(St[dt + 1][mt]), Qn[0][dt], Qn[0][dt + 1]);
+            mma1(Ot[mt], mt < MT ? VT[0][mt] : ones, PT);
+        }
+        const float den = __shfl(Ot[MT][0], c);
+        const float inv = valid ? __builtin_amdgcn_rcpf(den) : 0.f;
+
+        // gh = [G / d, -(G . out) / d]; lane (c, g) holds m = 16 mt + 4g + r of token c
+        float go = 0.f;
+        f32x4 gv[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 o = Ot[mt] * inv;
+            go += graw[mt][0] * o[0] + graw[mt][1] * o[1] + graw[mt][2] * o[2] + graw[mt][3] * o[3];
+            gv[mt] = graw[mt] * inv;
+        }
+        go += __shfl_xor(go, 16);
+        go += __shfl_xor(go, 32);
+        const float h = -go * inv;
+        Fr Gn[BTT][MT + 1];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<T>::to_frag(gv[mt]);
+        Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
+        if (valid) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) store4<T>(GB + t * M + 16 * mt + 4 * g, IO<T>::from_f32(gv[mt]));
+            if (g == 0) HB[t] = h;
+        }
+
+        // dA^T[j][i] = vh_j . gh_i, masked to j <= i
+        f32x4 da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt + 1 <= MT; mt += 2) {
+            const Fr a1 = (mt + 1 < MT) ? Vn[0][mt + 1] : k0ones;
+            mma2(da, Vn[0][mt], a1, Gn[0][mt], Gn[0][mt + 1]);
+        }
+        if ((MT & 1) == 0) mma1(da, k0ones, Gn[0][MT]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
+        const Fr dAT = IO<T>::to_frag(da);
+
+        // dL/dqh^T[d][i] = sum_j kh[j][d] dA^T[j][i] + sum_m' S_aug[d][m'] gh[i][m']
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma1(acc, KT[0][dt], dAT);
+#pragma unroll
+            for (int mt = 0; mt + 1 <= MT; mt += 2)
+                mma2(acc, IO<T>::to_frag(StT[mt][dt]), IO<T>::to_frag(StT[mt + 1][dt]), Gn[0][mt], Gn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, IO<T>::to_frag(StT[MT][dt]), Gn[0][MT]);
+            if (valid) store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(acc * dphi4(qraw[dt])));
+        }
+
+        // this segment's reverse-sum contribution: Ra += sum_i qh_i gh_i^T
+        Fr QT[BTT][DT], GT[BTT][MT + 1];
+        transpose_frags<Fr, DT, BTT>(QT, Qn);
+        transpose_frags<Fr, MT + 1, BTT>(GT, Gn);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt) mma1(Ra[dt][mt], QT[0][dt], GT[0][mt]);
+
+        // carry S_aug (both layouts) past this chunk
+        state_accumulate<Fr, D, M, BTT>(St, KT, VT);
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) mma1(StT[mt][dt], mt < MT ? VT[0][mt] : ones, KT[0][dt]);
+    }
+    state_store<D, M>(wsR + (bh * nseg + seg) * rec, Ra);
+}
+
+// ---- pass 4: reverse direction --------------------------------------------
+template <typename T, int D, int M>
+__global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const T *__restrict__ k,
+                                                 const T *__restrict__ v, const T *__restrict__ gbuf,
+                                                 const float *__restrict__ hbuf, T *__restrict__ dk,
+                                                 T *__restrict__ dv, const float *__restrict__ wsR, int64_t N,
+                                                 int64_t nseg, int64_t seg_tokens, int64_t rec) {
+    typedef typename IO<T>::frag Fr;
+    typedef typename IO<T>::vec4 V4;
+    constexpr int DT = D / 16, MT = M / 16;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    const T *Q = q + bh * N * D;
+    const T *K = k + bh * N * D;
+    const T *V = v + bh * N * M;
+    const T *GB = gbuf + bh * N * M;
+    const float *HB = hbuf + bh * N;
+    T *DK = dk + bh * N * D;
+    T *DV = dv + bh * N * M;
+
+    const float *rrec = wsR + (bh * nseg + seg) * rec;
+    f32x4 Rr[DT][MT + 1];      // R_aug, rows d (the u block is not used)
+    f32x4 RT[MT + 1][DT];      // R_aug^T, rows m'
+    state_load<D, M>(Rr, rrec);
+    stateT_load<D, M>(RT, rrec);
+
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
+    V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
+    float rh;
+    auto load_all = [&](int64_t t0) {
+        load_chunk<T, D, BTT>(rq, Q, t0, t_end);
+        load_chunk<T, D, BTT>(rk, K, t0, t_end);
+        load_chunk<T, M, BTT>(rv, V, t0, t_end);
+        load_chunk<T, M, BTT>(rg, GB, t0, t_end);
+        rh = (t0 + c < t_end) ? HB[t0 + c] : 0.f;
+    };
+    load_all(t_begin + (nch - 1) * BCH);
+    for (int64_t ci = nch - 1; ci >= 0; --ci) {
+        const int64_t t0 = t_begin + ci * BCH;
+        Fr Qn[BTT][DT], Kn[BTT][DT], Vn[BTT][MT + 1], Gn[BTT][MT + 1];
+        phi_frags<T, D, BTT>(Qn, rq, t0, t_end);
+        phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
+        {
+            Fr tmp[BTT][MT];
+            raw_frags<T, M, BTT>(tmp, rv);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) Vn[0][mt] = tmp[0][mt];
+            Vn[0][MT] = k0ones;
+            raw_frags<T, M, BTT>(tmp, rg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = tmp[0][mt];
+            Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
+        }
+        f32x4 kraw[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) kraw[dt] = IO<T>::to_f32(rk[0][dt]);
+        if (ci > 0) load_all(t0 - BCH);
+
+        const int64_t t = t0 + c;   // this lane's key token
+        const bool valid = t < t_end;
+
+        Fr QT[BTT][DT], GT[BTT][MT + 1];
+        transpose_frags<Fr, DT, BTT>(QT, Qn);
+        transpose_frags<Fr, MT + 1, BTT>(GT, Gn);
+
+        // P[i][j] = qh_i . kh_j and dA[i][j] = gh_i . vh_j, masked to i >= j
+        f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; dt += 2) mma2(p, Qn[0][dt], Qn[0][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
+#pragma unroll
+        for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(da, Gn[0][mt], Gn[0][mt + 1], Vn[0][mt], Vn[0][mt + 1]);
+        if ((MT & 1) == 0) mma1(da, Gn[0][MT], Vn[0][MT]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool keep = 4 * g + r >= c;
+            p[r] = keep ? p[r] : 0.f;
+            da[r] = keep ? da[r] : 0.f;
+        }
+        const Fr Pf = IO<T>::to_frag(p), dAf = IO<T>::to_frag(da);
+
+        // dL/dkh^T[d][j] = sum_i qh[i][d] dA[i][j] + sum_m' R_aug[d][m'] vh[j][m']
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma1(acc, QT[0][dt], dAf);
+#pragma unroll
+            for (int mt = 0; mt + 1 <= MT; mt += 2)
+                mma2(acc, IO<T>::to_frag(RT[mt][dt]), IO<T>::to_frag(RT[mt + 1][dt]), Vn[0][mt], Vn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, IO<T>::to_frag(RT[MT][dt]), Vn[0][MT]);
+            if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(acc * dphi4(kraw[dt])));
+        }
+        // dV^T[m][j] = sum_i g[i][m] P[i][j] + sum_d R[d][m] kh[j][d]
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma1(acc, GT[0][mt], Pf);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt += 2)
+                mma2(acc, IO<T>::to_frag(Rr[dt][mt]), IO<T>::to_frag(Rr[dt + 1][mt]), Kn[0][dt], Kn[0][dt + 1]);
+            if (valid) store4<T>(DV + t * M + 16 * mt + 4 * g, IO<T>::from_f32(acc));
+        }
+
+        // carry R_aug (both layouts) past this chunk, towards earlier tokens
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) mma1(RT[mt][dt], GT[0][mt], QT[0][dt]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) mma1(Rr[dt][mt], QT[0][dt], GT[0][mt]);
+    }
+}
+
+template <typename T, int D, int M>
+static hipError_t run_backward(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                               void *dv, int64_t BH, int64_t N, float *ws, hipStream_t s) {
+    const SegPlan p = make_plan(BH, N, D, M);
+    const BwdLayout L = backward_layout(BH, N, D, M, sizeof(T));
+    float *wsS = ws;
+    float *wsR = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.states);
+    T *gbuf = reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + L.g_off);
+    float *hbuf = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.h_off);
+    const dim3 grid(unsigned(BH * p.nseg));
+    const int dt = sizeof(T) == 4 ? 0 : 1;
+    hipError_t e = launch_segment_state(dt, k, v, wsS, BH, N, D, M, s);
+    if (e != hipSuccess) return e;
+    if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_dq<T, D, M>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                       (const T *)dout, (T *)dq, (const float *)wsS, wsR, gbuf, hbuf, N, p.nseg, p.seg_tokens, p.rec);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_dkdv<T, D, M>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                       (const T *)gbuf, (const float *)hbuf, (T *)dk, (T *)dv, (const float *)wsR, N, p.nseg,
+                       p.seg_tokens, p.rec);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t run_backward_t(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                                 void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s) {
+    if (D == 32 && M == 32) return run_backward<T, 32, 32>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 32 && M == 64) return run_backward<T, 32, 64>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 32) return run_backward<T, 64, 32>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 64) return run_backward<T, 64, 64>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq,
+                           void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+                           hipStream_t s) {
+    if (dt == 0) return run_backward_t<float>(q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+    return run_backward_t<bf16>(q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+}
+
+} // namespace la

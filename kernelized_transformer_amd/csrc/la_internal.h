@@ -1,0 +1,88 @@
+// la_internal.h -- host-side plan and launcher declarations (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+// Tokens per chunk: the unit of the intra-chunk masked product on the
+// matrix cores (two 16-token tiles).
+constexpr int64_t kChunk = 32;
+// Largest number of segments per (b, h) the segment scan handles.
+constexpr int64_t kMaxSegPerHead = 256;
+// Aim for about this many independent segments (one wavefront each) so that
+// every SIMD of the 256 CUs has work.
+constexpr int64_t kTargetSegments = 1024;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// How a (B*H, N) problem is cut into segments of whole chunks.  Each
+// segment is processed by one wavefront, chunk after chunk, carrying the
+// fp32 state; segment states are combined by a scan across segments.
+struct SegPlan {
+    int64_t seg_tokens = 0;  // tokens per segment (multiple of kChunk)
+    int64_t nseg = 0;        // segments per (b, h)
+    int64_t rec = 0;         // floats per state record: D*M + D (S then Z)
+};
+
+inline SegPlan make_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
+    SegPlan p;
+    const int64_t nch = ceil_div(N, kChunk);
+    int64_t cps = ceil_div(BH * nch, kTargetSegments);       // chunks per segment
+    cps = cps < 1 ? 1 : cps;
+    const int64_t min_cps = ceil_div(nch, kMaxSegPerHead);
+    if (cps < min_cps) cps = min_cps;
+    p.seg_tokens = cps * kChunk;
+    p.nseg = ceil_div(N, p.seg_tokens);
+    p.rec = D * M + D;
+    return p;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace: one fp32 state record per segment.
+inline size_t forward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
+    const SegPlan p = make_plan(BH, N, D, M);
+    return align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
+}
+
+// Backward workspace, in order: forward state records, reverse state records
+// (same size), the per-token normalized output gradient g_i = dout_i / d_i
+// ([BH][N][M] in the I/O type) and h_i = -(dout_i . out_i) / d_i ([BH][N]
+// fp32).
+struct BwdLayout {
+    size_t states = 0, g_off = 0, h_off = 0, total = 0;
+};
+
+inline BwdLayout backward_layout(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+    const SegPlan p = make_plan(BH, N, D, M);
+    BwdLayout L;
+    L.states = align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
+    L.g_off = 2 * L.states;
+    L.h_off = L.g_off + align256(size_t(BH * N * M) * esize);
+    L.total = L.h_off + align256(size_t(BH * N) * sizeof(float));
+    return L;
+}
+
+inline size_t backward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+    return backward_layout(BH, N, D, M, esize).total;
+}
+
+// Launchers (hipError_t of the last launch).  dt: 0 = fp32, 1 = bf16.
+hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
+                          int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s);
+hipError_t launch_segment_state(int dt, const void *k, const void *v, float *ws, int64_t BH, int64_t N, int64_t D,
+                                int64_t M, hipStream_t s);
+// mode 0: exclusive prefix over segments; 1: total into record 0;
+// 2: exclusive suffix (sum of the later segments).
+hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, const float *init, float *fin,
+                       hipStream_t s);
+hipError_t launch_backward(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq,
+                           void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+                           hipStream_t s);
+hipError_t launch_decode(int dt, const void *q, const void *k, const void *v, float *S, float *Z, void *out,
+                         int64_t BH, int64_t D, int64_t M, hipStream_t s);
+
+} // namespace la

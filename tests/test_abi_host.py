@@ -1,0 +1,118 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function ``include/la.h`` declares, and
+reject bad arguments with the documented status codes before touching any
+pointer.  Only argument combinations that fail validation are passed here, so
+no call reaches a kernel launch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kernelized_transformer_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for f in ("la_forward_causal", "la_forward_noncausal", "la_backward_causal", "la_decode_step",
+              "la_workspace_size", "la_status_string", "la_abi_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.load()
+    for f in declared_functions():
+        assert hasattr(lib, f), f"libla.so does not export {f}"
+
+
+def test_abi_version_and_status_strings():
+    assert la.la_abi_version() == 1
+    names = [la.la_status_string(s) for s in range(5)]
+    assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
+    assert la.la_status_string(99) == "LA_ERR_UNKNOWN"
+
+
+def test_workspace_size():
+    import torch
+    f = la.la_workspace_size
+    # one fp32 record (D*M + D floats) per segment, 256-byte aligned
+    n = f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
+    assert n > 0 and n % 256 == 0 and n >= 2 * (32 * 32 + 32) * 4
+    assert f(la.LA_OP_FWD_NONCAUSAL, 1, 2, 256, 32, 32, torch.float32) == n
+    assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32) > 2 * n
+    assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
+    assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) == 0     # unsupported D
+    # grows linearly in N at fixed segment count ceiling
+    a = f(la.LA_OP_FWD_CAUSAL, 1, 8, 65536, 64, 64, torch.bfloat16)
+    assert a <= 8 * 256 * (64 * 64 + 64) * 4 + 256
+
+
+FAKE = 1 << 32   # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, fn, q=FAKE, k=FAKE + (1 << 24), v=FAKE + (2 << 24), out=FAKE + (3 << 24), B=1, H=1, N=8, D=32, M=32,
+         dt=0, ws=FAKE + (4 << 24), wsb=0):
+    return getattr(lib, fn)(q, k, v, out, B, H, N, D, M, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["la_forward_causal", "la_forward_noncausal"])
+def test_forward_argument_errors(fn):
+    lib = la.load()
+    assert _fwd(lib, fn, q=0) == 1                      # null input
+    assert _fwd(lib, fn, out=0) == 1                    # null output
+    assert _fwd(lib, fn, q=FAKE + 8) == 1               # misaligned
+    assert _fwd(lib, fn, N=0) == 1                      # empty
+    assert _fwd(lib, fn, B=-1) == 1
+    assert _fwd(lib, fn, D=48) == 2                     # unsupported head size
+    assert _fwd(lib, fn, M=16) == 2
+    assert _fwd(lib, fn, dt=7) == 2                     # unknown dtype
+    assert _fwd(lib, fn, out=FAKE + 64) == 1            # output overlaps q
+    assert _fwd(lib, fn, ws=0, wsb=1 << 20) == 3        # missing workspace
+    assert _fwd(lib, fn, wsb=16) == 3                   # too small
+    assert _fwd(lib, fn, ws=FAKE + (4 << 24) + 16, wsb=1 << 20) == 3   # misaligned workspace
+    assert _fwd(lib, fn, ws=FAKE, wsb=1 << 20) == 3     # workspace overlaps an input
+
+
+def test_backward_and_decode_argument_errors():
+    lib = la.load()
+    base = [FAKE + (i << 24) for i in range(8)]
+    ok = dict(B=1, H=1, N=8, D=32, M=32, dt=1)
+
+    def bwd(ptrs, B=1, H=1, N=8, D=32, M=32, dt=1, ws=base[7], wsb=0):
+        return lib.la_backward_causal(*ptrs, B, H, N, D, M, dt, ws, wsb, None)
+
+    assert bwd(base[:7]) == 3                                   # no workspace bytes
+    assert bwd([0] + base[1:7]) == 1
+    assert bwd(base[:4] + [base[0], base[5], base[6]]) == 1     # dq aliases q
+    assert bwd(base[:4] + [base[4], base[4], base[6]]) == 1     # dq aliases dk
+    assert bwd(base[:7], D=128) == 2
+    assert ok
+
+    def dec(q=base[0], k=base[1], v=base[2], S=base[3], Z=base[4], out=base[5], B=2, H=2, D=64, M=64, dt=1):
+        return lib.la_decode_step(q, k, v, S, Z, out, B, H, D, M, dt, None)
+
+    assert dec(S=0) == 1
+    assert dec(Z=base[3] + 16) == 1                             # Z overlaps S
+    assert dec(out=base[0]) == 1                                # out aliases q
+    assert dec(D=100) == 2
+    assert dec(B=0) == 1
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(la, "lib_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(la, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        la.load()

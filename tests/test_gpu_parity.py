@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs from ``workloads``, runs the library on the GPU
+and compares, per (b, h) slice and per output tensor, the normwise relative
+error ||gpu - oracle|| / ||oracle|| against 1e-4 (fp32 I/O) or 2e-2 (bf16 I/O).
+The five workloads run at their full sizes; extra cases cover ragged tails,
+single tokens, mixed head sizes, many segments and stressed inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.gpu_util import TOL, check, dev, host
+
+pytestmark = pytest.mark.gpu
+
+la = pytest.importorskip("kernelized_transformer_amd")
+
+
+def _wl(seed, B, H, N, D, M, dtype, scale=1.0):
+    return wl.Workload(seed, f"edge seed {seed}", B, H, N, D, M, dtype, scale)
+
+
+def _say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+FWD_CASES = [
+    ("w1", wl.WORKLOADS[1]),
+    ("w2", wl.WORKLOADS[2]),
+    ("w3", wl.WORKLOADS[3]),
+    ("w4_n4096", wl.WORKLOADS[4].with_n(4096)),
+    ("w4_full", wl.WORKLOADS[4]),
+    ("n1_f32", _wl(101, 1, 1, 1, 32, 32, "f32")),
+    ("n1_bf16", _wl(102, 2, 1, 1, 64, 64, "bf16")),
+    ("n17_d32m64", _wl(103, 2, 3, 17, 32, 64, "f32")),
+    ("n33_d64m32", _wl(104, 1, 2, 33, 64, 32, "bf16")),
+    ("n100_d64m64_f32", _wl(105, 3, 1, 100, 64, 64, "f32")),
+    ("n1000_bf16", _wl(106, 1, 1, 1000, 32, 32, "bf16")),
+    ("n4097_ragged", _wl(107, 2, 2, 4097, 64, 64, "bf16")),
+    ("n200000_many_segments", _wl(108, 1, 1, 200000, 32, 32, "bf16")),
+    ("stress_sigma3_f32", _wl(109, 1, 2, 700, 32, 32, "f32", 3.0)),
+    ("stress_sigma3_bf16", _wl(110, 1, 2, 700, 64, 64, "bf16", 3.0)),
+]
+
+
+@pytest.mark.parametrize("name,w", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_causal(name, w):
+    q, k, v = wl.forward_inputs(w)
+    _say(f"forward causal {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    out = la.la_forward_causal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    ref = oracle.forward_causal(q, k, v)
+    check(f"out[{name}]", host(out), ref, w.dtype)
+
+
+NC_CASES = [("w1", wl.WORKLOADS[1]), ("w3_noncausal", wl.WORKLOADS[3]),
+            ("n1", _wl(111, 1, 1, 1, 32, 32, "f32")), ("n77_d64m32", _wl(112, 2, 2, 77, 64, 32, "bf16")),
+            ("n5000_f32", _wl(113, 1, 3, 5000, 64, 64, "f32"))]
+
+
+@pytest.mark.parametrize("name,w", NC_CASES, ids=[c[0] for c in NC_CASES])
+def test_forward_noncausal(name, w):
+    q, k, v = wl.forward_inputs(w)
+    _say(f"forward non-causal {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    out = la.la_forward_noncausal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    ref = oracle.forward_noncausal(q, k, v)
+    check(f"out[{name}]", host(out), ref, w.dtype)
+
+
+def test_causal_last_row_equals_noncausal():
+    w = _wl(114, 2, 2, 999, 64, 64, "f32")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("causal last row == non-causal last row")
+    oc = host(la.la_forward_causal(q, k, v))
+    onc = host(la.la_forward_noncausal(q, k, v))
+    assert np.abs(oc[:, :, -1] - onc[:, :, -1]).max() <= 1e-5 * np.abs(onc[:, :, -1]).max()
+
+
+BWD_CASES = [
+    ("w1_shape", wl.WORKLOADS[1]),
+    ("w2_shape", wl.WORKLOADS[2]),
+    ("w3_shape_b2h2", wl.WORKLOADS[3].with_shape(B=2, H=2)),
+    ("w4_n4096", wl.WORKLOADS[4].with_n(4096)),
+    ("w4_full", wl.WORKLOADS[4]),
+    ("n1", _wl(121, 1, 2, 1, 32, 32, "f32")),
+    ("n17_d32m64", _wl(122, 2, 1, 17, 32, 64, "f32")),
+    ("n50_d64m32_bf16", _wl(123, 1, 3, 50, 64, 32, "bf16")),
+    ("n3001_ragged_f32", _wl(124, 1, 2, 3001, 64, 64, "f32")),
+    ("n100000_many_segments", _wl(125, 1, 1, 100000, 32, 32, "bf16")),
+]
+
+
+@pytest.mark.parametrize("name,w", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_causal(name, w):
+    q, k, v, g = wl.forward_inputs(w, with_dout=True)
+    _say(f"backward causal {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    dq, dk, dv = la.la_backward_causal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), dev(g, w.dtype))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_causal(q, k, v, g)
+    if w.N == 1:   # out_1 = V_1: dQ = dK = 0, dV = dout
+        assert np.abs(host(dq)).max() < 1e-6 and np.abs(host(dk)).max() < 1e-6
+        check(f"dv[{name}]", host(dv), rv, w.dtype)
+        return
+    check(f"dq[{name}]", host(dq), rq, w.dtype)
+    check(f"dk[{name}]", host(dk), rk, w.dtype)
+    check(f"dv[{name}]", host(dv), rv, w.dtype)
+
+
+def _decode_run(w, steps, sample=None):
+    stream = wl.DecodeStream(w)
+    qs, ks, vs = stream.take(steps)
+    S = torch.zeros((w.B, w.H, w.D, w.M), dtype=torch.float32, device="cuda")
+    Z = torch.zeros((w.B, w.H, w.D), dtype=torch.float32, device="cuda")
+    dq_, dk_, dv_ = dev(qs, w.dtype), dev(ks, w.dtype), dev(vs, w.dtype)
+    outs = torch.empty((steps, w.B, w.H, w.M), dtype=dq_.dtype, device="cuda")
+    for t in range(steps):
+        la.la_decode_step(dq_[t], dk_[t], dv_[t], S, Z, out=outs[t])
+    torch.cuda.synchronize()
+    return qs, ks, vs, host(outs), host(S), host(Z)
+
+
+def test_decode_small_f32():
+    w = _wl(131, 2, 3, 1, 32, 64, "f32")
+    _say("decode small f32: B2 H3 D32 M64, 80 steps")
+    qs, ks, vs, outs, S, Z = _decode_run(w, 80)
+    So = np.zeros((w.B, w.H, w.D, w.M))
+    Zo = np.zeros((w.B, w.H, w.D))
+    ref = np.stack([oracle.decode_step(qs[t], ks[t], vs[t], So, Zo) for t in range(80)])
+    check("decode out", outs, ref, "f32", lead=3)
+    check("decode S", S, So, "f32")
+    check("decode Z", Z, Zo, "f32")
+
+
+def test_decode_full_workload_sampled_streams():
+    w = wl.WORKLOADS[5]
+    _say(f"decode full workload: B{w.B} H{w.H} D{w.D} M{w.M} {w.dtype}, {w.steps} steps")
+    qs, ks, vs, outs, S, Z = _decode_run(w, w.steps)
+    rng = np.random.default_rng(5)
+    bs = rng.choice(w.B, 8, replace=False)
+    hs = rng.integers(0, w.H, 8)
+    sq, sk, sv = qs[:, bs, hs][:, None], ks[:, bs, hs][:, None], vs[:, bs, hs][:, None]   # [T,1,8,.]
+    So = np.zeros((1, 8, w.D, w.M))
+    Zo = np.zeros((1, 8, w.D))
+    ref = np.stack([oracle.decode_step(sq[t], sk[t], sv[t], So, Zo) for t in range(w.steps)])   # [T,1,8,M]
+    got = outs[:, bs, hs][:, None]
+    check("decode out (sampled streams, per step)", got, ref, w.dtype, lead=3)
+    check("decode S (sampled streams)", S[bs, hs][None], So, "f32")
+    check("decode Z (sampled streams)", Z[bs, hs][None], Zo, "f32")
+    # every stream: Z_T = sum_t phi(k_t), checked against the oracle's phi
+    phik = oracle.feature_map(ks.astype(np.float64))[0].sum(0)
+    check("decode Z (all streams)", Z, phik, "f32")
+
+
+def test_decode_equals_forward_on_gpu():
+    w = _wl(132, 1, 4, 1, 64, 64, "f32")
+    T = 300
+    _say("decode == causal forward on the stacked sequence")
+    qs, ks, vs, outs, _, _ = _decode_run(w, T)
+    tr = lambda x: np.ascontiguousarray(np.moveaxis(x, 0, 2))
+    fwd = host(la.la_forward_causal(dev(tr(qs), "f32"), dev(tr(ks), "f32"), dev(tr(vs), "f32")))
+    np.testing.assert_allclose(np.moveaxis(outs, 0, 2), fwd, rtol=0, atol=2e-5 * np.abs(fwd).max())
+
+
+def test_forward_deterministic_and_guarded():
+    w = _wl(141, 2, 3, 1500, 64, 64, "bf16")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("determinism + guard bands, forward and backward")
+    n = w.B * w.H * w.N * w.M
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + n].view(w.B, w.H, w.N, w.M)
+    la.la_forward_causal(q, k, v, out=out)
+    a = out.clone()
+    la.la_forward_causal(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(a, out)
+    assert (buf[:pad] == 7.0).all() and (buf[pad + n:] == 7.0).all()
+    g = dev(wl.forward_inputs(w, with_dout=True)[3], w.dtype)
+    r1 = la.la_backward_causal(q, k, v, g)
+    r2 = la.la_backward_causal(q, k, v, g)
+    torch.cuda.synchronize()
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+
+
+def test_segment_plan_independence():
+    """A head computed alone and inside a large batch (different segment cuts)
+    gives the same result up to fp32 rounding."""
+    w = _wl(151, 8, 8, 2048, 32, 32, "f32")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("segment plan independence")
+    full = host(la.la_forward_causal(q, k, v))
+    one = host(la.la_forward_causal(q[3:4, 5:6].contiguous(), k[3:4, 5:6].contiguous(), v[3:4, 5:6].contiguous()))
+    assert np.abs(full[3:4, 5:6] - one).max() <= 1e-5 * np.abs(one).max()
+
+
+def test_invalid_arguments_leave_outputs_untouched():
+    w = _wl(161, 1, 2, 64, 32, 32, "f32")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("error paths on the GPU")
+    out = torch.full((1, 2, 64, 32), 3.0, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(la.LAError) as e:
+        la.la_forward_causal(q, k, v, out=out, workspace=small)
+    assert e.value.status == 3
+    with pytest.raises(la.LAError) as e:
+        la.la_forward_causal(q, k, v, out=q)   # output aliases an input
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert (out == 3.0).all()
