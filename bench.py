@@ -1,0 +1,286 @@
+"""Benchmark of the kernelized linear-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
+
+Headline (``value``): causal forward throughput in tokens*heads/s on the long
+sequence workload B=1, H=8, N=65536, D=M=64, bf16 I/O, fp32 state.  One step
+is one la_forward_causal call over the whole batch, inputs already resident
+in HBM; two input sets alternate so that consecutive steps do not re-read the
+same 268 MB from the 256 MB Infinity Cache.
+
+In the same run, each timed with HIP events on the stream the library launches
+on, and reported next to the headline:
+  * decode: 3072 sequential la_decode_step calls for B=256 streams x H=8 heads,
+    D=M=64 (steps/s), eager launches and a replayed HIP graph of the same calls;
+  * backward: la_backward_causal on the long-sequence workload;
+  * non-causal forward on the long-sequence workload;
+  * the causal forward of the three smaller workloads;
+  * optionally (--sweep) the causal forward for N = 512 .. 65536.
+``roofline`` relates the forward's algorithmic HBM bytes (Q, K, V read once,
+out written once: 512 B per token*head) to its measured time against the
+MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` times the fp64 oracle on the host
+cores over the full long-sequence workload, as a reference point only.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-passes", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward"], default="all",
+                    help="restrict the timed work (for profiling runs)")
+    return ap.parse_args()
+
+
+def main():
+    a = _args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build targets one GPU; the path shards by (batch, head) with no communication, "
+              "but only --gpus 1 is measured.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kernelized_transformer_amd as la
+    import workloads as wl
+
+    lib = la.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def to_dev(x, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+        return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).contiguous()
+
+    def log(*m):
+        print("[bench]", *m, file=sys.stderr, flush=True)
+
+    def time_events(fn, iters):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(iters):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    # ---- forward on the long-sequence workload ----------------------------------
+    w4 = wl.WORKLOADS[4]
+    BH = w4.B * w4.H
+    tok_heads = BH * w4.N
+    fwd_bytes = tok_heads * (2 * w4.D + w4.M) * 2 + tok_heads * w4.M * 2      # 512 B / token*head
+    fwd_flops = tok_heads * (4 * w4.D * w4.M + 4 * w4.D)                      # recurrence form
+    results = {}
+    log("generating long-sequence inputs")
+    sets = []
+    for seed in (4, 40):
+        q, k, v, g = wl.forward_inputs(w4, with_dout=True, seed=seed)
+        sets.append(tuple(to_dev(x, "bf16") for x in (q, k, v, g)))
+    out = torch.empty((w4.B, w4.H, w4.N, w4.M), dtype=torch.bfloat16, device=dev)
+    ws_f = torch.empty(la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w4.B, w4.H, w4.N, w4.D, w4.M, torch.bfloat16),
+                       dtype=torch.uint8, device=dev)
+
+    def fwd(i, causal=True):
+        q, k, v, _ = sets[i % 2]
+        f = lib.la_forward_causal if causal else lib.la_forward_noncausal
+        st = f(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), w4.B, w4.H, w4.N, w4.D, w4.M,
+               la.LA_DTYPE_BF16, ws_f.data_ptr(), ws_f.numel(), sptr)
+        if st != 0:
+            raise la.LAError("forward", st)
+
+    if a.only in ("all", "forward"):
+        for i in range(a.warmup):
+            fwd(i)
+        t = time_events(fwd, a.steps)
+        ms = t / a.steps * 1e3
+        results["forward"] = dict(seconds=t, ms_per_step=ms, tok_heads_per_s=tok_heads * a.steps / t)
+        log(f"causal forward: {ms:.4f} ms/step, {tok_heads * a.steps / t:.4e} tokens*heads/s")
+        # same input every step (Infinity Cache may hold part of it): reported, not the headline
+        t_same = time_events(lambda i: fwd(0), a.steps)
+        results["forward_same_input"] = dict(ms_per_step=t_same / a.steps * 1e3,
+                                             tok_heads_per_s=tok_heads * a.steps / t_same)
+
+    # ---- backward / non-causal on the long-sequence workload --------------------------
+    if a.only in ("all", "backward"):
+        dq, dk, dv = (torch.empty_like(sets[0][0]), torch.empty_like(sets[0][1]), torch.empty_like(sets[0][2]))
+        ws_b = torch.empty(la.la_workspace_size(la.LA_OP_BWD_CAUSAL, w4.B, w4.H, w4.N, w4.D, w4.M, torch.bfloat16),
+                           dtype=torch.uint8, device=dev)
+
+        def bwd(i):
+            q, k, v, g = sets[i % 2]
+            st = lib.la_backward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), w4.B, w4.H, w4.N, w4.D, w4.M, la.LA_DTYPE_BF16,
+                                        ws_b.data_ptr(), ws_b.numel(), sptr)
+            if st != 0:
+                raise la.LAError("backward", st)
+
+        for i in range(2):
+            bwd(i)
+        nb = max(5, a.steps // 4)
+        t = time_events(bwd, nb)
+        bwd_bytes = tok_heads * (2 * w4.D + 2 * w4.M) * 2 + tok_heads * (2 * w4.D + w4.M) * 2   # 896 B
+        results["backward"] = dict(ms_per_call=t / nb * 1e3, tok_heads_per_s=tok_heads * nb / t,
+                                   algorithmic_bytes=bwd_bytes,
+                                   hbm_frac=bwd_bytes / (t / nb) / 1e9 / HBM_PEAK_GBS)
+        log(f"causal backward: {t / nb * 1e3:.4f} ms/call")
+    if a.only in ("all",):
+        for i in range(2):
+            fwd(i, causal=False)
+        t = time_events(lambda i: fwd(i, causal=False), a.steps)
+        results["noncausal"] = dict(ms_per_call=t / a.steps * 1e3, tok_heads_per_s=tok_heads * a.steps / t)
+        log(f"non-causal forward: {t / a.steps * 1e3:.4f} ms/call")
+
+    # ---- smaller forward workloads and the N sweep --------------------------------------
+    def fwd_rate(w, seed=None, iters=20):
+        q, k, v = (to_dev(x, w.dtype) for x in wl.forward_inputs(w, seed=seed))
+        o = torch.empty((w.B, w.H, w.N, w.M), dtype=q.dtype, device=dev)
+        dtc = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+        ws = torch.empty(max(1, la.la_workspace_size(0, w.B, w.H, w.N, w.D, w.M, dtc)), dtype=torch.uint8, device=dev)
+
+        def f(i):
+            st = lib.la_forward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.H, w.N, w.D,
+                                       w.M, dtc, ws.data_ptr(), ws.numel(), sptr)
+            if st != 0:
+                raise la.LAError("forward", st)
+
+        for i in range(3):
+            f(i)
+        t = time_events(f, iters)
+        th = w.B * w.H * w.N
+        by = th * ((2 * w.D + w.M) + w.M) * (2 if w.dtype == "bf16" else 4)
+        return dict(us_per_call=t / iters * 1e6, tok_heads_per_s=th * iters / t,
+                    hbm_frac=by / (t / iters) / 1e9 / HBM_PEAK_GBS)
+
+    if a.only == "all":
+        results["small_workloads"] = {wl.WORKLOADS[i].name: fwd_rate(wl.WORKLOADS[i]) for i in (1, 2, 3)}
+        if a.sweep:
+            results["sweep"] = {str(n): fwd_rate(w4.with_n(n)) for n in wl.SWEEP_N}
+
+    # ---- decode ------------------------------------------------------------------------------
+    if a.only in ("all", "decode"):
+        w5 = wl.WORKLOADS[5]
+        log("generating decode inputs")
+        qs, ks, vs = wl.DecodeStream(w5).take(w5.steps)
+        dq5, dk5, dv5 = to_dev(qs, "bf16"), to_dev(ks, "bf16"), to_dev(vs, "bf16")
+        del qs, ks, vs
+        S = torch.zeros((w5.B, w5.H, w5.D, w5.M), dtype=torch.float32, device=dev)
+        Z = torch.zeros((w5.B, w5.H, w5.D), dtype=torch.float32, device=dev)
+        o5 = torch.empty((w5.steps, w5.B, w5.H, w5.M), dtype=torch.bfloat16, device=dev)
+        BH5 = w5.B * w5.H
+        qb, kb, vb, ob = dq5.data_ptr(), dk5.data_ptr(), dv5.data_ptr(), o5.data_ptr()
+        sq, so = BH5 * w5.D * 2, BH5 * w5.M * 2
+        dec = lib.la_decode_step
+        Sp, Zp = S.data_ptr(), Z.data_ptr()
+
+        def one_pass(_):
+            for t in range(w5.steps):
+                dec(qb + t * sq, kb + t * sq, vb + t * so, Sp, Zp, ob + t * so, w5.B, w5.H, w5.D, w5.M,
+                    la.LA_DTYPE_BF16, sptr)
+
+        S.zero_(); Z.zero_()
+        one_pass(0)
+        passes = []
+        for p in range(a.decode_passes):
+            S.zero_(); Z.zero_()
+            passes.append(time_events(one_pass, 1))
+        t_eager = min(passes)
+        # the same 3072 calls captured once into a HIP graph and replayed
+        g = torch.cuda.CUDAGraph()
+        S.zero_(); Z.zero_()
+        cap = torch.cuda.Stream(dev)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            for t in range(w5.steps):
+                dec(qb + t * sq, kb + t * sq, vb + t * so, Sp, Zp, ob + t * so, w5.B, w5.H, w5.D, w5.M,
+                    la.LA_DTYPE_BF16, cs)
+        gpasses = []
+        for p in range(a.decode_passes):
+            S.zero_(); Z.zero_()
+            torch.cuda.synchronize()
+            gpasses.append(time_events(lambda i: g.replay(), 1))
+        t_graph = min(gpasses)
+        bytes_call = BH5 * (2 * w5.D * w5.M * 4 + 2 * w5.D * 4) + BH5 * (2 * w5.D + 2 * w5.M) * 2
+        results["decode"] = dict(
+            steps_per_s_eager=w5.steps / t_eager, steps_per_s_graph=w5.steps / t_graph,
+            us_per_call_eager=t_eager / w5.steps * 1e6, us_per_call_graph=t_graph / w5.steps * 1e6,
+            algorithmic_bytes_per_call=bytes_call,
+            effective_gbs_graph=bytes_call * w5.steps / t_graph / 1e9,
+            effective_gbs_eager=bytes_call * w5.steps / t_eager / 1e9)
+        log(f"decode: eager {w5.steps / t_eager:.4e} steps/s, graph {w5.steps / t_graph:.4e} steps/s")
+        del g
+
+    # ---- CPU baseline: the fp64 oracle on the host cores ---------------------------------------
+    cpu = None
+    if not a.no_cpu_baseline and a.only == "all":
+        import oracle
+        lo = oracle.load()
+        q, k, v, _ = wl.forward_inputs(w4, with_dout=True)
+        threads = min(oracle.num_threads(lo), BH)
+        t0 = time.time()
+        reps = 0
+        while True:
+            oracle.forward_causal(q, k, v, lib=lo)
+            reps += 1
+            if time.time() - t0 >= 10.0:
+                break
+        dt = time.time() - t0
+        cpu = {"value": tok_heads * reps / dt, "unit": "tokens*heads/s", "cores": threads, "kind": "oracle",
+               "sample": f"full long-sequence workload (B1 H8 N65536 D=M=64, bf16 values in fp64), "
+                         f"{reps} causal forward pass(es) in {dt:.1f} s, OpenMP over the 8 (b,h) recurrences"}
+        log(f"oracle: {cpu['value']:.4e} tokens*heads/s on {threads} threads")
+
+    f = results.get("forward")
+    roof = None
+    if f:
+        ach = fwd_bytes / (f["ms_per_step"] / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "la_forward_causal (k_segment_state + k_state_scan + k_segment_output)",
+                "algorithmic_bytes_per_launch": fwd_bytes}
+    line = {
+        "metric": "causal lin-attn fwd tokens·heads/s (N=65536,D=M=64); decode steps/s",
+        "value": f["tok_heads_per_s"] if f else None,
+        "unit": "tokens*heads/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": f["ms_per_step"] if f else None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 I/O, fp32 state/accumulate",
+        "data": "synthetic (seeded N(0,1) Q, K, V; no dataset or weights)",
+        "config": {"workload": "causal forward B1 H8 N65536 D=M=64 bf16", "B": w4.B, "H": w4.H, "N": w4.N,
+                   "D": w4.D, "M": w4.M},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": results.get("decode"),
+        "extra": {k_: v_ for k_, v_ in results.items() if k_ not in ("decode",)},
+        "flops_per_step": fwd_flops,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
