@@ -66,6 +66,8 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 
     const Fr ones = frag_row0_ones<Fr>();
     const Fr k0ones = frag_k0_ones<Fr>();
+    __shared__ bf16 stage_mem[stage_elems<DT, BTT>() + stage_elems<MT + 1, BTT>()];
+    lds_bf16 *stage = (lds_bf16 *)(stage_mem);
 
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
     load_chunk<T, D, BTT>(rq, Q, t_begin, t_end);
@@ -76,24 +78,22 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         Fr Qn[BTT][DT], Kn[BTT][DT], Vn[BTT][MT];
         phi_frags<T, D, BTT>(Qn, rq, t0, t_end);
         phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
-        raw_frags<T, M, BTT>(Vn, rv);
+        raw_frags<T, M, BTT>(Vn, rv, t0, t_end);
         f32x4 qraw[DT], graw[MT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) qraw[dt] = IO<T>::to_f32(rq[0][dt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) graw[mt] = IO<T>::to_f32(rg[0][mt]);
-        if (t0 + BCH < t_end) {
-            load_chunk<T, D, BTT>(rq, Q, t0 + BCH, t_end);
-            load_chunk<T, D, BTT>(rk, K, t0 + BCH, t_end);
-            load_chunk<T, M, BTT>(rv, V, t0 + BCH, t_end);
-            load_chunk<T, M, BTT>(rg, G, t0 + BCH, t_end);
-        }
+        load_chunk<T, D, BTT>(rq, Q, t0 + BCH, t_end);
+        load_chunk<T, D, BTT>(rk, K, t0 + BCH, t_end);
+        load_chunk<T, M, BTT>(rv, V, t0 + BCH, t_end);
+        load_chunk<T, M, BTT>(rg, G, t0 + BCH, t_end);
         const int64_t t = t0 + c;   // this lane's query token
         const bool valid = t < t_end;
 
         Fr KT[BTT][DT], VT[BTT][MT];
-        transpose_frags<Fr, DT, BTT>(KT, Kn);
-        transpose_frags<Fr, MT, BTT>(VT, Vn);
+        transpose_frags<DT, BTT>(KT, Kn, stage);
+        transpose_frags<MT, BTT>(VT, Vn, stage + stage_elems<DT, BTT>());
 
         // recompute out^T (and den in the normalizer block) as the forward does
         f32x4 Ot[MT + 1];
@@ -162,8 +162,8 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 
         // this segment's reverse-sum contribution: Ra += sum_i qh_i gh_i^T
         Fr QT[BTT][DT], GT[BTT][MT + 1];
-        transpose_frags<Fr, DT, BTT>(QT, Qn);
-        transpose_frags<Fr, MT + 1, BTT>(GT, Gn);
+        transpose_frags<DT, BTT>(QT, Qn, stage);
+        transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -208,6 +208,8 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     stateT_load<D, M>(RT, rrec);
 
     const Fr k0ones = frag_k0_ones<Fr>();
+    __shared__ bf16 stage_mem[stage_elems<DT, BTT>() + stage_elems<MT + 1, BTT>()];
+    lds_bf16 *stage = (lds_bf16 *)(stage_mem);
 
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
@@ -227,11 +229,11 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
         phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
         {
             Fr tmp[BTT][MT];
-            raw_frags<T, M, BTT>(tmp, rv);
+            raw_frags<T, M, BTT>(tmp, rv, t0, t_end);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) Vn[0][mt] = tmp[0][mt];
             Vn[0][MT] = k0ones;
-            raw_frags<T, M, BTT>(tmp, rg);
+            raw_frags<T, M, BTT>(tmp, rg, t0, t_end);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = tmp[0][mt];
             Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
         const bool valid = t < t_end;
 
         Fr QT[BTT][DT], GT[BTT][MT + 1];
-        transpose_frags<Fr, DT, BTT>(QT, Qn);
-        transpose_frags<Fr, MT + 1, BTT>(GT, Gn);
+        transpose_frags<DT, BTT>(QT, Qn, stage);
+        transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
 
         // P[i][j] = qh_i . kh_j and dA[i][j] = gh_i . vh_j, masked to i >= j
         f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};

@@ -12,21 +12,22 @@
 
 namespace la {
 
-// Raw load of one chunk of rows [t0, t0 + 16 TT) of a [N][F] slice; rows at
-// or beyond t_end read as zero.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Raw load of one chunk of rows [t0, t0 + 16 TT) of a [N][F] slice.  The
+// load is issued for every lane (rows at or beyond t_end read row t_end - 1,
+// which always exists), so no lane branches around it and the compiler can
+// keep several chunks in flight; the consumers (phi_frags, raw_frags) zero
+// the rows at or beyond t_end.  Requires t_end >= 1.
 template <typename T, int F, int TT>
 __device__ __forceinline__ void load_chunk(typename IO<T>::vec4 (&x)[TT][F / 16], const T *__restrict__ base,
                                            int64_t t0, int64_t t_end) {
     const int c = lane_id() & 15, g = lane_id() >> 4;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-        const int64_t t = t0 + 16 * tt + c;
-        const bool ok = t < t_end;
+        const int64_t t = min(t0 + 16 * tt + c, t_end - 1);
 #pragma unroll
-        for (int ft = 0; ft < F / 16; ++ft) {
-            typename IO<T>::vec4 z = {0, 0, 0, 0};
-            x[tt][ft] = ok ? load4<T>(base + t * F + 16 * ft + 4 * g) : z;
-        }
+        for (int ft = 0; ft < F / 16; ++ft) x[tt][ft] = load4<T>(base + t * F + 16 * ft + 4 * g);
     }
 }
 
@@ -48,24 +49,166 @@ __device__ __forceinline__ void phi_frags(typename IO<T>::frag (&y)[TT][F / 16],
     }
 }
 
+// V rows as fragments for the forward products, unmasked: every product
+// that reads them also multiplies by phi(K) of the same row, which is zero
+// past t_end (and the padded rows are copies of row t_end - 1, so finite
+// whenever the data is).
+__device__ __forceinline__ void value_frags_unmasked(bf16x4 &y, bf16x4 x) { y = x; }
+__device__ __forceinline__ void value_frags_unmasked(f32x4 &y, f32x4 x) { y = x; }
+
+// The loaded values as fragments, rows at or beyond t_end zeroed.
 template <typename T, int F, int TT>
 __device__ __forceinline__ void raw_frags(typename IO<T>::frag (&y)[TT][F / 16],
-                                          const typename IO<T>::vec4 (&x)[TT][F / 16]) {
+                                          const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
+    const int c = lane_id() & 15;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const bool ok = t0 + 16 * tt + c < t_end;
+#pragma unroll
+        for (int ft = 0; ft < F / 16; ++ft) {
+            f32x4 p = IO<T>::to_f32(x[tt][ft]);
+            if (!ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
+            y[tt][ft] = IO<T>::to_frag(p);
+        }
+    }
+}
+
+// ---- LDS staging (bf16) ---------------------------------------------------
+// A wavefront's private staging area for one chunk of one tensor: rows of
+// 16*NF features (bf16), padded to kStagePad extra elements per row.
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+constexpr int kStagePad = 8;
+
+// Token-contiguous copies of bf16 fragments through LDS: the natural
+// fragments are written row-major (one 8-byte store per lane and tile), then
+// read back with the gfx950 transposing LDS read, which hands lane (c, g) of
+// a 16x16 tile the elements [4g + r][c], r = 0..3, when lane (c, g) points at
+// row 4g + c/4, columns 4 (c % 4) .. + 3.  Exact (a copy).
+template <int NF, int TT>
+__device__ __forceinline__ void transpose_frags_lds(bf16x4 (&yt)[TT][NF], const bf16x4 (&y)[TT][NF],
+                                                    lds_bf16 *stage) {
+    constexpr int S = 16 * NF + kStagePad;
+    const int c = lane_id() & 15, g = lane_id() >> 4;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int ft = 0; ft < F / 16; ++ft) y[tt][ft] = IO<T>::to_frag(IO<T>::to_f32(x[tt][ft]));
+        for (int ft = 0; ft < NF; ++ft)
+            *reinterpret_cast<lds_bf16x4 *>(stage + (16 * tt + c) * S + 16 * ft + 4 * g) = y[tt][ft];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < NF; ++ft) {
+            const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<lds_i16x4 *>(stage + (16 * tt + 4 * g + (c >> 2)) * S + 16 * ft + 4 * (c & 3)));
+            yt[tt][ft] = __builtin_bit_cast(bf16x4, r);
+        }
 }
 
+// ---- contiguous chunk loads (bf16) -------------------------------------------
+// A chunk of 16 TT rows x F bf16 features is fetched with 16-byte loads in
+// row-major order (each load instruction of the wavefront covers 1 KB of
+// consecutive memory), which streams HBM far better than per-fragment 8-byte
+// loads.  The rows then go through the wavefront's LDS staging area, from
+// which the MFMA fragments are read in either orientation.
+typedef unsigned int dwordx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dwordx4 lds_dwordx4;
+
+template <int F, int TT> struct Lines {
+    static constexpr int n = TT * F / 32;   // 16-byte loads per lane
+};
+
+// Rows at or beyond t_end read row t_end - 1 (always valid); stage_lines
+// zeroes them where that matters.  Requires t_end >= 1.
+template <int F, int TT>
+__device__ __forceinline__ void load_lines(dwordx4 (&x)[TT * F / 32], const bf16 *__restrict__ base, int64_t t0,
+                                           int64_t t_end) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < Lines<F, TT>::n; ++i) {
+        const int e = (64 * i + l) * 8;          // first element of this lane's 8
+        const int64_t t = min(t0 + e / F, t_end - 1);
+        x[i] = *reinterpret_cast<const dwordx4 *>(base + t * F + e % F);
+    }
+}
+
+// phi of 8 packed bf16 values (two per dword), rounded back to bf16.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ dwordx4 phi8(dwordx4 x) {
+    dwordx4 y;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float lo = __builtin_bit_cast(float, x[w] << 16);
+        const float hi = __builtin_bit_cast(float, x[w] & 0xffff0000u);
+        const bf16x2 p = {(bf16)phi(lo), (bf16)phi(hi)};
+        y[w] = __builtin_bit_cast(unsigned int, p);
+    }
+    return y;
+}
+
+// Writes the loaded rows into the staging area (row stride F + kStagePad);
+// with PHI the feature map is applied and rows at or beyond t_end become 0.
+template <int F, int TT, bool PHI>
+__device__ __forceinline__ void stage_lines(lds_bf16 *stage, const dwordx4 (&x)[TT * F / 32], int64_t t0,
+                                            int64_t t_end) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < Lines<F, TT>::n; ++i) {
+        const int e = (64 * i + l) * 8;
+        const int row = e / F, col = e % F;
+        dwordx4 y = x[i];
+        if (PHI) {
+            y = phi8(y);
+            if (t0 + row >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
+        }
+        *reinterpret_cast<lds_dwordx4 *>(stage + row * (F + kStagePad) + col) = y;
+    }
+}
+
+// Natural fragments (token rows, contraction over features) from staging.
+template <int F, int TT>
+__device__ __forceinline__ void natural_frags_lds(bf16x4 (&y)[TT][F / 16], const lds_bf16 *stage) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < F / 16; ++ft)
+            y[tt][ft] = *reinterpret_cast<const lds_bf16x4 *>(stage + (16 * tt + c) * (F + kStagePad) + 16 * ft + 4 * g);
+}
+
+// Token-contiguous fragments from staging (see transpose_frags_lds).
+template <int F, int TT>
+__device__ __forceinline__ void transposed_frags_lds(bf16x4 (&yt)[TT][F / 16], const lds_bf16 *stage) {
+    constexpr int S = F + kStagePad;
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < F / 16; ++ft) {
+            const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4 *>(
+                const_cast<lds_bf16 *>(stage) + (16 * tt + 4 * g + (c >> 2)) * S + 16 * ft + 4 * (c & 3)));
+            yt[tt][ft] = __builtin_bit_cast(bf16x4, r);
+        }
+}
+
+// Elements of LDS staging one wavefront needs per tensor chunk.
+template <int NF, int TT> constexpr int stage_elems() { return 16 * TT * (16 * NF + kStagePad); }
+
 // Token-contiguous copies: yt[tt][ft] holds, in lane (c, g), the 4 tokens
-// 16*tt + 4g .. + 3 of feature 16*ft + c.
-template <typename Fr, int NF, int TT>
-__device__ __forceinline__ void transpose_frags(Fr (&yt)[TT][NF], const Fr (&y)[TT][NF]) {
-    const Fr ident = frag_identity<Fr>();
+// 16*tt + 4g .. + 3 of feature 16*ft + c.  bf16 goes through LDS; fp32 goes
+// through an identity product on the matrix cores.
+template <int NF, int TT>
+__device__ __forceinline__ void transpose_frags(f32x4 (&yt)[TT][NF], const f32x4 (&y)[TT][NF], lds_bf16 *) {
+    const f32x4 ident = frag_identity<f32x4>();
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int ft = 0; ft < NF; ++ft) yt[tt][ft] = transpose_frag(y[tt][ft], ident);
+}
+template <int NF, int TT>
+__device__ __forceinline__ void transpose_frags(bf16x4 (&yt)[TT][NF], const bf16x4 (&y)[TT][NF], lds_bf16 *stage) {
+    transpose_frags_lds<NF, TT>(yt, y, stage);
 }
 
 // ---- state records --------------------------------------------------------

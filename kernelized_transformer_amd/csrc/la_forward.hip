@@ -15,12 +15,16 @@
 // so that every operand is either a plain row-major load or an accumulator
 // tile reused in place (see la_device.h).
 //
-// Sequence parallelism: each (b, h) is cut into segments of whole chunks,
-// one wavefront per segment.  Three launches:
-//   1. k_segment_state: per segment, sum_t phi(K_t) [V_t, 1]^T  (fp32),
-//   2. k_state_scan:    exclusive prefix of those records over segments,
-//   3. k_segment_output: per segment, start from its prefix and walk the
-//      chunks, writing out and carrying (S, Z) in fp32 registers.
+// Sequence parallelism.  Each wavefront owns a sub-segment of whole chunks
+// and walks it twice: first summing phi(K_t) [V_t, 1]^T into a local fp32
+// state, then (after learning the state of everything before it) producing
+// the outputs chunk by chunk while carrying (S, Z) in registers.
+//   causal (one launch, k_fwd_fused): four wavefronts form a block; their
+//     local states are combined in LDS, and blocks of the same (b, h) hand
+//     their states to each other through the workspace with a decoupled
+//     look-back (see the comment at the kernel);
+//   non-causal (three launches): per-segment states, their sum per (b, h),
+//     then the readout.
 #include "la_chunk.h"
 #include "la_internal.h"
 
@@ -29,43 +33,355 @@ namespace la {
 constexpr int TT = 2;        // token tiles per chunk in the forward kernels
 constexpr int CH = 16 * TT;  // = kChunk
 static_assert(CH == kChunk, "forward chunk");
+constexpr int kPrefetch = 2; // chunks in flight ahead of the one being computed
 
-// ---- 1. per-segment state ------------------------------------------------
+// ---- chunk loops ------------------------------------------------------------
+
+// St += sum over tokens [t_begin, t_end) of phi(K_t) [V_t, 1]^T.
+// PF chunks are kept in flight: the loop is unrolled by PF so that chunk i
+// always lives in buffer i % PF (a register copy between buffers would force
+// a wait on the loads in flight).
+template <typename T, int D, int M, int PF>
+__device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *__restrict__ V, int64_t t_begin,
+                                              int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
+                                              lds_bf16 *stage_v) {
+    typedef typename IO<T>::frag Fr;
+    typedef typename IO<T>::vec4 V4;
+    V4 rk[PF][TT][D / 16], rv[PF][TT][M / 16];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        load_chunk<T, D, TT>(rk[b], K, t_begin + b * CH, t_end);
+        load_chunk<T, M, TT>(rv[b], V, t_begin + b * CH, t_end);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
+#pragma unroll
+        for (int b = 0; b < PF; ++b) {
+            const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
+            Fr Kn[TT][D / 16], Vn[TT][M / 16];
+            phi_frags<T, D, TT>(Kn, rk[b], t0, t_end);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int f = 0; f < M / 16; ++f) value_frags_unmasked(Vn[tt][f], rv[b][tt][f]);
+            load_chunk<T, D, TT>(rk[b], K, t0 + PF * CH, t_end);
+            load_chunk<T, M, TT>(rv[b], V, t0 + PF * CH, t_end);
+            // keep the prefetch where it is: the scheduler would otherwise sink
+            // the loads next to their use two chunks later
+            __builtin_amdgcn_sched_barrier(0);
+            Fr KT[TT][D / 16], VT[TT][M / 16];
+            transpose_frags<D / 16, TT>(KT, Kn, stage_k);
+            transpose_frags<M / 16, TT>(VT, Vn, stage_v);
+            state_accumulate<Fr, D, M, TT>(St, KT, VT);
+        }
+    }
+}
+
+// Outputs for tokens [t_begin, t_end), starting from the state St of all
+// earlier tokens (updated as the walk proceeds when CAUSAL).  Per chunk,
+// with Acc tiles Ot[mt][it] = out^T (rows m plus the normalizer row block,
+// cols = queries):
+//   readout:  Ot[mt][it] += S^T[m][d] phi(Q)[i][d]      (S from St, as is)
+//   intra:    Ot[mt][it] += V^T[m][j] P^T[j][i], P^T[j][i] = phi(K_j).phi(Q_i), j <= i
+//   update:   St += phi(K)^T [V, 1]
+// The normalizer row block of Ot gets den_i in row 0.
+template <typename T, int D, int M, bool CAUSAL, int PF>
+__device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__restrict__ K,
+                                           const T *__restrict__ V, T *__restrict__ O, int64_t t_begin,
+                                           int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
+                                           lds_bf16 *stage_v) {
+    typedef typename IO<T>::frag Fr;
+    typedef typename IO<T>::vec4 V4;
+    constexpr int DT = D / 16, MT = M / 16;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const Fr ones = frag_row0_ones<Fr>();
+    const Fr zero = frag_zero<Fr>();
+
+    V4 rq[PF][TT][DT], rk[PF][TT][DT], rv[PF][TT][MT];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        load_chunk<T, D, TT>(rq[b], Q, t_begin + b * CH, t_end);
+        if (CAUSAL) {
+            load_chunk<T, D, TT>(rk[b], K, t_begin + b * CH, t_end);
+            load_chunk<T, M, TT>(rv[b], V, t_begin + b * CH, t_end);
+        }
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
+        Fr Qn[TT][DT], Kn[TT][DT], Vn[TT][MT];
+        phi_frags<T, D, TT>(Qn, rq[b], t0, t_end);
+        if (CAUSAL) {
+            phi_frags<T, D, TT>(Kn, rk[b], t0, t_end);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int f = 0; f < MT; ++f) value_frags_unmasked(Vn[tt][f], rv[b][tt][f]);
+        }
+        load_chunk<T, D, TT>(rq[b], Q, t0 + PF * CH, t_end);
+        if (CAUSAL) {
+            load_chunk<T, D, TT>(rk[b], K, t0 + PF * CH, t_end);
+            load_chunk<T, M, TT>(rv[b], V, t0 + PF * CH, t_end);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        f32x4 Ot[MT + 1][TT];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int it = 0; it < TT; ++it) Ot[mt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // readout against the state carried in from earlier tokens
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) {
+            Fr SF[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<T>::to_frag(St[dt][mt]);
+#pragma unroll
+            for (int it = 0; it < TT; ++it)
+#pragma unroll
+                for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt][it], SF[dt], SF[dt + 1], Qn[it][dt], Qn[it][dt + 1]);
+        }
+
+        if (CAUSAL) {
+            // P^T tiles (keys x queries), causal mask inside the diagonal tiles
+            Fr PT[TT][TT];
+#pragma unroll
+            for (int it = 0; it < TT; ++it)
+#pragma unroll
+                for (int jt = 0; jt < TT; ++jt) {
+                    if (jt > it) {
+                        PT[jt][it] = zero;
+                        continue;
+                    }
+                    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[jt][dt], Kn[jt][dt + 1], Qn[it][dt], Qn[it][dt + 1]);
+                    if (jt == it) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+                    }
+                    PT[jt][it] = IO<T>::to_frag(p);
+                }
+            Fr KT[TT][DT], VT[TT][MT];
+            transpose_frags<DT, TT>(KT, Kn, stage_k);
+            transpose_frags<MT, TT>(VT, Vn, stage_v);
+            // intra-chunk term; the ones row block sums P^T into den
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+                for (int it = 0; it < TT; ++it) {
+                    const Fr a0 = (mt < MT) ? VT[0][mt] : ones;
+                    const Fr a1 = (mt < MT) ? VT[1][mt] : ones;
+                    mma2(Ot[mt][it], a0, a1, PT[0][it], PT[1][it]);
+                }
+            state_accumulate<Fr, D, M, TT>(St, KT, VT);
+        }
+
+        // normalize and store: den_i sits in row 0 of the normalizer block,
+        // i.e. element 0 of lane c (g = 0)
+#pragma unroll
+        for (int it = 0; it < TT; ++it) {
+            const float den = __shfl(Ot[MT][it][0], c);
+            const float inv = __builtin_amdgcn_rcpf(den);
+            const int64_t t = t0 + 16 * it + c;
+            if (t < t_end) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) store4<T>(O + t * M + 16 * mt + 4 * g, IO<T>::from_f32(Ot[mt][it] * inv));
+            }
+        }
+    }
+    }
+}
+
+// ---- chunk loops, bf16: contiguous loads + LDS staging ---------------------------
+// Same products as above; the chunk's rows are fetched with contiguous
+// 16-byte loads, the feature map is applied in registers, and the rows are
+// staged in the wavefront's LDS area, from which the natural and the
+// token-contiguous fragments are read.
+
+template <int D, int M, int PF>
+__device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+                                                   int64_t t_begin, int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1],
+                                                   lds_bf16 *sk, lds_bf16 *sv) {
+    constexpr int NK = Lines<D, TT>::n, NV = Lines<M, TT>::n;
+    dwordx4 rk[PF][NK], rv[PF][NV];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        load_lines<D, TT>(rk[b], K, t_begin + b * CH, t_end);
+        load_lines<M, TT>(rv[b], V, t_begin + b * CH, t_end);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
+#pragma unroll
+        for (int b = 0; b < PF; ++b) {
+            const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked
+            stage_lines<D, TT, true>(sk, rk[b], t0, t_end);
+            stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
+            load_lines<D, TT>(rk[b], K, t0 + PF * CH, t_end);
+            load_lines<M, TT>(rv[b], V, t0 + PF * CH, t_end);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x4 KT[TT][D / 16], VT[TT][M / 16];
+            transposed_frags_lds<D, TT>(KT, sk);
+            transposed_frags_lds<M, TT>(VT, sv);
+            state_accumulate<bf16x4, D, M, TT>(St, KT, VT);
+        }
+    }
+}
+
+template <int D, int M, bool CAUSAL, int PF>
+__device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+                                                const bf16 *__restrict__ V, bf16 *__restrict__ O, int64_t t_begin,
+                                                int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *sq,
+                                                lds_bf16 *sk, lds_bf16 *sv) {
+    typedef bf16x4 Fr;
+    constexpr int DT = D / 16, MT = M / 16;
+    constexpr int NQ = Lines<D, TT>::n, NV = Lines<M, TT>::n;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const Fr ones = frag_row0_ones<Fr>();
+    const Fr zero = frag_zero<Fr>();
+
+    dwordx4 rq[PF][NQ], rk[PF][NQ], rv[PF][NV];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        load_lines<D, TT>(rq[b], Q, t_begin + b * CH, t_end);
+        if (CAUSAL) {
+            load_lines<D, TT>(rk[b], K, t_begin + b * CH, t_end);
+            load_lines<M, TT>(rv[b], V, t_begin + b * CH, t_end);
+        }
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
+        stage_lines<D, TT, true>(sq, rq[b], t0, t_end);
+        if (CAUSAL) {
+            stage_lines<D, TT, true>(sk, rk[b], t0, t_end);
+            stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
+        }
+        load_lines<D, TT>(rq[b], Q, t0 + PF * CH, t_end);
+        if (CAUSAL) {
+            load_lines<D, TT>(rk[b], K, t0 + PF * CH, t_end);
+            load_lines<M, TT>(rv[b], V, t0 + PF * CH, t_end);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        Fr Qn[TT][DT];
+        natural_frags_lds<D, TT>(Qn, sq);
+
+        f32x4 Ot[MT + 1][TT];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int it = 0; it < TT; ++it) Ot[mt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // readout against the state carried in from earlier tokens
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) {
+            Fr SF[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<bf16>::to_frag(St[dt][mt]);
+#pragma unroll
+            for (int it = 0; it < TT; ++it)
+#pragma unroll
+                for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt][it], SF[dt], SF[dt + 1], Qn[it][dt], Qn[it][dt + 1]);
+        }
+
+        if (CAUSAL) {
+            Fr Kn[TT][DT], KT[TT][DT], VT[TT][MT];
+            natural_frags_lds<D, TT>(Kn, sk);
+            transposed_frags_lds<D, TT>(KT, sk);
+            transposed_frags_lds<M, TT>(VT, sv);
+            // P^T tiles (keys x queries), causal mask inside the diagonal tiles
+            Fr PT[TT][TT];
+#pragma unroll
+            for (int it = 0; it < TT; ++it)
+#pragma unroll
+                for (int jt = 0; jt < TT; ++jt) {
+                    if (jt > it) {
+                        PT[jt][it] = zero;
+                        continue;
+                    }
+                    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[jt][dt], Kn[jt][dt + 1], Qn[it][dt], Qn[it][dt + 1]);
+                    if (jt == it) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+                    }
+                    PT[jt][it] = IO<bf16>::to_frag(p);
+                }
+            // intra-chunk term; the ones row block sums P^T into den
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+                for (int it = 0; it < TT; ++it) {
+                    const Fr a0 = (mt < MT) ? VT[0][mt] : ones;
+                    const Fr a1 = (mt < MT) ? VT[1][mt] : ones;
+                    mma2(Ot[mt][it], a0, a1, PT[0][it], PT[1][it]);
+                }
+            state_accumulate<Fr, D, M, TT>(St, KT, VT);
+        }
+
+        // normalize and store: den_i sits in row 0 of the normalizer block,
+        // i.e. element 0 of lane c (g = 0)
+#pragma unroll
+        for (int it = 0; it < TT; ++it) {
+            const float den = __shfl(Ot[MT][it][0], c);
+            const float inv = __builtin_amdgcn_rcpf(den);
+            const int64_t t = t0 + 16 * it + c;
+            if (t < t_end) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    store4<bf16>(O + t * M + 16 * mt + 4 * g, IO<bf16>::from_f32(Ot[mt][it] * inv));
+            }
+        }
+    }
+    }
+}
+
+// ---- per-segment kernels (non-causal path, and the backward's forward state) ----
 template <typename T, int D, int M>
 __global__ __launch_bounds__(64) void k_segment_state(const T *__restrict__ k, const T *__restrict__ v,
                                                       float *__restrict__ ws, int64_t N, int64_t nseg,
                                                       int64_t seg_tokens, int64_t rec) {
-    typedef typename IO<T>::frag Fr;
-    typedef typename IO<T>::vec4 V4;
     const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t t_begin = seg * seg_tokens;
     const int64_t t_end = min(N, t_begin + seg_tokens);
-    const T *K = k + bh * N * D;
-    const T *V = v + bh * N * M;
-
+    __shared__ bf16 stage[stage_elems<D / 16, TT>() + stage_elems<M / 16, TT>()];
+    lds_bf16 *sk = (lds_bf16 *)(stage);
     f32x4 St[D / 16][M / 16 + 1];
     state_zero<D, M>(St);
-
-    V4 rk[TT][D / 16], rv[TT][M / 16];
-    load_chunk<T, D, TT>(rk, K, t_begin, t_end);
-    load_chunk<T, M, TT>(rv, V, t_begin, t_end);
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += CH) {
-        Fr Kn[TT][D / 16], Vn[TT][M / 16];
-        phi_frags<T, D, TT>(Kn, rk, t0, t_end);
-        raw_frags<T, M, TT>(Vn, rv);
-        if (t0 + CH < t_end) {
-            load_chunk<T, D, TT>(rk, K, t0 + CH, t_end);
-            load_chunk<T, M, TT>(rv, V, t0 + CH, t_end);
-        }
-        Fr KT[TT][D / 16], VT[TT][M / 16];
-        transpose_frags<Fr, D / 16, TT>(KT, Kn);
-        transpose_frags<Fr, M / 16, TT>(VT, Vn);
-        state_accumulate<Fr, D, M, TT>(St, KT, VT);
-    }
+    if constexpr (sizeof(T) == 2)
+        seg_aggregate_bf16<D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk,
+                                            sk + stage_elems<D / 16, TT>());
+    else
+        seg_aggregate<T, D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk,
+                                          sk + stage_elems<D / 16, TT>());
     state_store<D, M>(ws + (bh * nseg + seg) * rec, St);
 }
 
-// ---- 2. scan over segments ----------------------------------------------
+template <typename T, int D, int M, bool CAUSAL>
+__global__ __launch_bounds__(64) void k_segment_output(const T *__restrict__ q, const T *__restrict__ k,
+                                                       const T *__restrict__ v, T *__restrict__ out,
+                                                       const float *__restrict__ ws, int64_t N, int64_t nseg,
+                                                       int64_t seg_tokens, int64_t rec) {
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    __shared__ bf16 stage[2 * stage_elems<D / 16, TT>() + stage_elems<M / 16, TT>()];
+    lds_bf16 *sq = (lds_bf16 *)(stage);
+    lds_bf16 *sk = sq + stage_elems<D / 16, TT>();
+    lds_bf16 *sv = sk + stage_elems<D / 16, TT>();
+    f32x4 St[D / 16][M / 16 + 1];
+    state_load<D, M>(St, ws + (bh * nseg + (CAUSAL ? seg : 0)) * rec);
+    if constexpr (sizeof(T) == 2)
+        seg_output_bf16<D, M, CAUSAL, kPrefetch>(q + bh * N * D, k + bh * N * D, v + bh * N * M, out + bh * N * M,
+                                                 t_begin, t_end, St, sq, sk, sv);
+    else
+        seg_output<T, D, M, CAUSAL, kPrefetch>(q + bh * N * D, k + bh * N * D, v + bh * N * M, out + bh * N * M,
+                                               t_begin, t_end, St, sk, sv);
+}
+
+// ---- scan over segments ---------------------------------------------------
 // Block = 64 record elements x 4 segment quarters (256 threads).  Each thread
 // keeps its quarter's values in registers, the quarters' totals are combined
 // in LDS, then the prefixes are written back.
@@ -128,142 +444,242 @@ hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mod
     return hipGetLastError();
 }
 
-// ---- 3. per-segment output -------------------------------------------------
-// Per chunk (32 tokens = query tiles it, key tiles jt), with Acc tiles
-// Ot[mt][it] = out^T (rows m, plus the normalizer row block), cols = queries:
-//   readout:  Ot[mt][it] += S^T[m][d] phi(Q)[i][d]      (S from St, as is)
-//   intra:    Ot[mt][it] += V^T[m][j] P^T[j][i], P^T[j][i] = phi(K_j).phi(Q_i), j <= i
-//   update:   St += phi(K)^T [V, 1]
-// The normalizer row block of Ot gets den_i in row 0.
-template <typename T, int D, int M, bool CAUSAL>
-__global__ __launch_bounds__(64) void k_segment_output(const T *__restrict__ q, const T *__restrict__ k,
-                                                       const T *__restrict__ v, T *__restrict__ out,
-                                                       const float *__restrict__ ws, int64_t N, int64_t nseg,
-                                                       int64_t seg_tokens, int64_t rec) {
-    typedef typename IO<T>::frag Fr;
-    typedef typename IO<T>::vec4 V4;
-    constexpr int DT = D / 16, MT = M / 16;
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int64_t t_begin = seg * seg_tokens;
-    const int64_t t_end = min(N, t_begin + seg_tokens);
-    const T *Q = q + bh * N * D;
-    const T *K = k + bh * N * D;
-    const T *V = v + bh * N * M;
-    T *O = out + bh * N * M;
+// ---- fused causal forward ---------------------------------------------------
+//
+// Workgroup = kFusedWaves wavefronts = one block of consecutive sub-segments
+// of one (b, h).  Blocks take tickets in launch order from a counter, so a
+// block only ever waits on blocks that are already running.
+//   1. each wavefront sums phi(K) [V, 1]^T over its sub-segment (fp32);
+//   2. the block total A_s = A_w0 + A_w1 + ... is published (flag = 1);
+//      the block then finds, among its predecessors, the nearest one p whose
+//      inclusive prefix I_p is published (flag = 2), waiting only until every
+//      block between p and s has published its total, and forms its
+//      exclusive prefix P_s = I_p + A_{p+1} + ... + A_{s-1}, always summed in
+//      increasing block order.  Since every I_p is itself such a left-to-right
+//      sum, P_s has the same bits whichever p is found: results do not depend
+//      on timing.  I_s = P_s + A_s is published (flag = 2);
+//   3. wavefront w starts from P_s + A_w0 + ... + A_{w-1} and writes its
+//      outputs, re-reading its K, V (mostly from the memory-side cache).
+// Records go through the workspace with plain loads and stores ordered by
+// agent-scope release/acquire fences around the flag accesses (visible
+// across XCDs); only wavefront 0 of a block touches them.  Every wait is bounded: a
+// block that waited too long sets the error word and carries on, so every
+// wavefront always exits.
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kLookbackBatch = 8;
 
-    f32x4 St[DT][MT + 1];
-    state_load<D, M>(St, ws + (bh * nseg + (CAUSAL ? seg : 0)) * rec);
-
-    const Fr ones = frag_row0_ones<Fr>();
-    const Fr zero = frag_zero<Fr>();
-
-    V4 rq[TT][DT], rk[TT][DT], rv[TT][MT];
-    load_chunk<T, D, TT>(rq, Q, t_begin, t_end);
-    if (CAUSAL) {
-        load_chunk<T, D, TT>(rk, K, t_begin, t_end);
-        load_chunk<T, M, TT>(rv, V, t_begin, t_end);
-    }
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += CH) {
-        Fr Qn[TT][DT], Kn[TT][DT], Vn[TT][MT];
-        phi_frags<T, D, TT>(Qn, rq, t0, t_end);
-        if (CAUSAL) {
-            phi_frags<T, D, TT>(Kn, rk, t0, t_end);
-            raw_frags<T, M, TT>(Vn, rv);
-        }
-        if (t0 + CH < t_end) {
-            load_chunk<T, D, TT>(rq, Q, t0 + CH, t_end);
-            if (CAUSAL) {
-                load_chunk<T, D, TT>(rk, K, t0 + CH, t_end);
-                load_chunk<T, M, TT>(rv, V, t0 + CH, t_end);
-            }
-        }
-
-        f32x4 Ot[MT + 1][TT];
-#pragma unroll
-        for (int mt = 0; mt <= MT; ++mt)
-#pragma unroll
-            for (int it = 0; it < TT; ++it) Ot[mt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        // readout against the state carried in from earlier tokens
-#pragma unroll
-        for (int mt = 0; mt <= MT; ++mt) {
-            Fr SF[DT];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<T>::to_frag(St[dt][mt]);
-#pragma unroll
-            for (int it = 0; it < TT; ++it)
-#pragma unroll
-                for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt][it], SF[dt], SF[dt + 1], Qn[it][dt], Qn[it][dt + 1]);
-        }
-
-        if (CAUSAL) {
-            // P^T tiles (keys x queries), causal mask inside the diagonal tiles
-            Fr PT[TT][TT];
-#pragma unroll
-            for (int it = 0; it < TT; ++it)
-#pragma unroll
-                for (int jt = 0; jt < TT; ++jt) {
-                    if (jt > it) {
-                        PT[jt][it] = zero;
-                        continue;
-                    }
-                    f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[jt][dt], Kn[jt][dt + 1], Qn[it][dt], Qn[it][dt + 1]);
-                    if (jt == it) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-                    }
-                    PT[jt][it] = IO<T>::to_frag(p);
-                }
-            Fr KT[TT][DT], VT[TT][MT];
-            transpose_frags<Fr, DT, TT>(KT, Kn);
-            transpose_frags<Fr, MT, TT>(VT, Vn);
-            // intra-chunk term; the ones row block sums P^T into den
-#pragma unroll
-            for (int mt = 0; mt <= MT; ++mt)
-#pragma unroll
-                for (int it = 0; it < TT; ++it) {
-                    const Fr a0 = (mt < MT) ? VT[0][mt] : ones;
-                    const Fr a1 = (mt < MT) ? VT[1][mt] : ones;
-                    mma2(Ot[mt][it], a0, a1, PT[0][it], PT[1][it]);
-                }
-            state_accumulate<Fr, D, M, TT>(St, KT, VT);
-        }
-
-        // normalize and store: den_i sits in row 0 of the normalizer block,
-        // i.e. element 0 of lane c (g = 0)
-#pragma unroll
-        for (int it = 0; it < TT; ++it) {
-            const float den = __shfl(Ot[MT][it][0], c);
-            const float inv = __builtin_amdgcn_rcpf(den);
-            const int64_t t = t0 + 16 * it + c;
-            if (t < t_end) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) store4<T>(O + t * M + 16 * mt + 4 * g, IO<T>::from_f32(Ot[mt][it] * inv));
-            }
-        }
-    }
+__global__ void k_fused_reset(int *__restrict__ words, int64_t n) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) words[i] = 0;
 }
 
 template <typename T, int D, int M>
+__global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd_fused(const T *__restrict__ q, const T *__restrict__ k,
+                                                                const T *__restrict__ v, T *__restrict__ out,
+                                                                int *__restrict__ header, int *__restrict__ flags,
+                                                                float *__restrict__ recs, int64_t N, int64_t nblk,
+                                                                int64_t sub_tokens) {
+    constexpr int REC = D * M + D;
+    __shared__ float lds_a[kFusedWaves][REC];   // per-wavefront totals
+    __shared__ float lds_p[REC];                // the block's exclusive prefix
+    __shared__ float lds_x[REC];                // block total, then inclusive prefix
+    __shared__ int lds_ticket, lds_from;
+    constexpr int SK = stage_elems<D / 16, TT>(), SV = stage_elems<M / 16, TT>();
+    __shared__ bf16 lds_stage[kFusedWaves][2 * SK + SV];   // per-wavefront staging: q, k, v
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
+
+    if (tid == 0) lds_ticket = atomicAdd(&header[0], 1);
+    __syncthreads();
+    const int64_t ticket = __builtin_amdgcn_readfirstlane(lds_ticket);
+    const int64_t bh = ticket / nblk, blk = ticket % nblk;
+    const int64_t t_begin = min(N, (blk * kFusedWaves + wave) * sub_tokens);
+    const int64_t t_end = min(N, t_begin + sub_tokens);
+    const T *Q = q + bh * N * D;
+    const T *K = k + bh * N * D;
+    const T *V = v + bh * N * M;
+    int *fl = flags + bh * nblk;
+    float *agg_rec = recs + (bh * nblk + blk) * 2 * REC;
+    float *inc_rec = agg_rec + REC;
+
+    // 1. local totals
+    f32x4 St[D / 16][M / 16 + 1];
+    state_zero<D, M>(St);
+    lds_bf16 *stage_q = (lds_bf16 *)(&lds_stage[wave][0]);
+    lds_bf16 *stage_k = stage_q + SK;
+    lds_bf16 *stage_v = stage_k + SK;
+    if constexpr (sizeof(T) == 2)
+        seg_aggregate_bf16<D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
+    else
+        seg_aggregate<T, D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
+    state_store<D, M>(&lds_a[wave][0], St);
+    __syncthreads();
+
+    // 2. block total, publish, look-back, exclusive and inclusive prefix.
+    // Wavefront 0 alone stores records and flags, so its own agent-scope
+    // release fences order them; all wavefronts share the summation of the
+    // predecessors' records (loads of kLookbackBatch records kept in flight,
+    // added in increasing block order).
+    const bool last = blk == nblk - 1;
+    constexpr int NT = 64 * kFusedWaves;
+    constexpr int NJ = (REC + NT - 1) / NT;
+    float a[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = tid + NT * j;
+        float x = 0.f;
+        if (e < REC) {
+            x = lds_a[0][e];
+#pragma unroll
+            for (int w = 1; w < kFusedWaves; ++w) x += lds_a[w][e];
+            lds_x[e] = x;
+        }
+        a[j] = x;
+    }
+    __syncthreads();
+    if (wave == 0 && blk > 0) {
+        if (!last) {
+            for (int e = lane; e < REC; e += 64) agg_rec[e] = lds_x[e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (lane == 0) __hip_atomic_store(&fl[blk], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // lane i watches block blk - 1 - i; lane blk stands for "before block 0"
+        int from = -1;
+        for (int iter = 0;; ++iter) {
+            int f = 0;
+            if (lane < blk) f = __hip_atomic_load(&fl[blk - 1 - lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned long long incl = __ballot(lane < blk ? f == 2 : lane == blk);
+            const unsigned long long none = __ballot(lane < blk && f == 0);
+            const int i = __builtin_ctzll(incl);   // nearest inclusive (lane blk always qualifies)
+            const unsigned long long below = (i >= 63) ? ~0ull : ((1ull << i) - 1);
+            if ((none & below) == 0) {
+                from = int(blk) - 1 - i;           // -1: start from block 0's inclusive
+                break;
+            }
+            if (iter >= kSpinLimit) {
+                if (lane == 0) atomicOr(&header[1], 1);
+                from = int(blk) - 1;               // gave up waiting: result is wrong, error word set
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) lds_from = from;
+    }
+    __syncthreads();
+    float p[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) p[j] = 0.f;
+    if (blk > 0) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int64_t from = __builtin_amdgcn_readfirstlane(lds_from);
+        const float *base = recs + (bh * nblk) * 2 * REC;
+        // P_s = I_from + A_{from+1} + ... + A_{blk-1}, left to right; block 0
+        // publishes no separate total (its inclusive is its total)
+        const float *first = (from >= 0) ? base + (from * 2 + 1) * REC : base + REC;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int e = tid + NT * j;
+            if (e < REC) p[j] = first[e];
+        }
+        for (int64_t b0 = (from >= 0 ? from + 1 : 1); b0 < blk; b0 += kLookbackBatch) {
+            float buf[kLookbackBatch][NJ];
+#pragma unroll
+            for (int r = 0; r < kLookbackBatch; ++r) {
+                const float *src = base + (b0 + r) * 2 * REC;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int e = tid + NT * j;
+                    buf[r][j] = (b0 + r < blk && e < REC) ? src[e] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kLookbackBatch; ++r) {
+                if (b0 + r < blk) {
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) p[j] += buf[r][j];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = tid + NT * j;
+        if (e < REC) {
+            lds_p[e] = p[j];
+            lds_x[e] = (blk > 0) ? p[j] + a[j] : a[j];
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && !last) {
+        for (int e = lane; e < REC; e += 64) inc_rec[e] = lds_x[e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) __hip_atomic_store(&fl[blk], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // 3. outputs, starting from P_s + the totals of the earlier wavefronts
+    {
+        const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+            for (int mt = 0; mt <= M / 16; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = 16 * dt + 4 * g + r;
+                    int e;
+                    bool on = true;
+                    if (mt < M / 16) {
+                        e = d * M + 16 * mt + c;
+                    } else {
+                        e = D * M + d;
+                        on = c == 0;
+                    }
+                    float x = 0.f;
+                    if (on) {
+                        x = lds_p[e];
+                        for (int w = 0; w < wave; ++w) x += lds_a[w][e];
+                    }
+                    St[dt][mt][r] = x;
+                }
+            }
+        }
+    }
+    if constexpr (sizeof(T) == 2)
+        seg_output_bf16<D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q, stage_k,
+                                               stage_v);
+    else
+        seg_output<T, D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_k, stage_v);
+}
+
+// ---- host side ---------------------------------------------------------------
+template <typename T, int D, int M>
 static hipError_t run_forward(bool causal, const void *q, const void *k, const void *v, void *out, int64_t BH,
                               int64_t N, float *ws, hipStream_t s) {
+    if (causal) {
+        const FusedPlan p = make_fused_plan(BH, N, D, M);
+        char *base = reinterpret_cast<char *>(ws);
+        int *header = reinterpret_cast<int *>(base);
+        int *flags = reinterpret_cast<int *>(base + p.flags_off);
+        float *recs = reinterpret_cast<float *>(base + p.recs_off);
+        const int64_t nreset = int64_t(p.flags_off / sizeof(int)) + BH * p.nblk;   // header + flags
+        hipLaunchKernelGGL(k_fused_reset, dim3(unsigned((nreset + 255) / 256)), dim3(256), 0, s, header, nreset);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_fwd_fused<T, D, M>), dim3(unsigned(BH * p.nblk)), dim3(64 * kFusedWaves), 0, s,
+                           (const T *)q, (const T *)k, (const T *)v, (T *)out, header, flags, recs, N, p.nblk,
+                           p.sub_tokens);
+        return hipGetLastError();
+    }
     const SegPlan p = make_plan(BH, N, D, M);
     const dim3 grid(unsigned(BH * p.nseg));
     hipLaunchKernelGGL((k_segment_state<T, D, M>), grid, dim3(64), 0, s, (const T *)k, (const T *)v, ws, N, p.nseg,
                        p.seg_tokens, p.rec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_scan(ws, BH, p.nseg, p.rec, causal ? 0 : 1, nullptr, nullptr, s);
+    e = launch_scan(ws, BH, p.nseg, p.rec, 1, nullptr, nullptr, s);
     if (e != hipSuccess) return e;
-    if (causal)
-        hipLaunchKernelGGL((k_segment_output<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, (const float *)ws, N, p.nseg, p.seg_tokens, p.rec);
-    else
-        hipLaunchKernelGGL((k_segment_output<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, (const float *)ws, N, p.nseg, p.seg_tokens, p.rec);
+    hipLaunchKernelGGL((k_segment_output<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
+                       (const T *)v, (T *)out, (const float *)ws, N, p.nseg, p.seg_tokens, p.rec);
     return hipGetLastError();
 }
 

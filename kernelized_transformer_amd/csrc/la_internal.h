@@ -42,10 +42,48 @@ inline SegPlan make_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: one fp32 state record per segment.
+// Workspace of the non-causal forward: one fp32 state record per segment.
 inline size_t forward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
     const SegPlan p = make_plan(BH, N, D, M);
     return align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
+}
+
+// The causal forward runs as one pass: workgroups of kFusedWaves wavefronts,
+// each workgroup owning a block of kFusedWaves consecutive sub-segments (one
+// per wavefront) of one (b, h).  Blocks exchange their fp32 state records
+// through the workspace (decoupled look-back), so no segment scan launch is
+// needed.
+constexpr int kFusedWaves = 4;
+constexpr int64_t kMaxBlkPerHead = 64;   // look-back window = one wavefront of flags
+constexpr int64_t kTargetWaves = 1024;   // one wavefront per SIMD of the 256 CUs
+
+struct FusedPlan {
+    int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
+    int64_t nblk = 0;        // blocks per (b, h)
+    int64_t rec = 0;         // floats per state record
+    size_t flags_off = 0;    // int flags [BH][nblk] (after a 256-byte header: ticket, error word)
+    size_t recs_off = 0;     // float records [BH][nblk][2][rec]: block aggregate, inclusive prefix
+    size_t total = 0;
+};
+
+inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
+    FusedPlan p;
+    const int64_t nch = ceil_div(N, kChunk);
+    int64_t cpw = ceil_div(BH * nch, kTargetWaves);
+    if (cpw < 1) cpw = 1;
+    const int64_t min_cpw = ceil_div(nch, kFusedWaves * kMaxBlkPerHead);
+    if (cpw < min_cpw) cpw = min_cpw;
+    p.sub_tokens = cpw * kChunk;
+    p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
+    p.rec = D * M + D;
+    p.flags_off = 256;
+    p.recs_off = p.flags_off + align256(size_t(BH * p.nblk) * sizeof(int));
+    p.total = p.recs_off + align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float));
+    return p;
+}
+
+inline size_t causal_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
+    return make_fused_plan(BH, N, D, M).total;
 }
 
 // Backward workspace, in order: forward state records, reverse state records

@@ -189,6 +189,20 @@ def test_forward_deterministic_and_guarded():
         assert torch.equal(x, y)
 
 
+def test_fused_forward_error_word_clear():
+    """The causal forward's cross-block hand-off reports a timed-out wait in
+    word 1 of the workspace; it must stay clear."""
+    w = _wl(171, 1, 4, 100000, 64, 64, "bf16")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("fused forward error word")
+    n = la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.D, w.M, torch.bfloat16)
+    ws = torch.full((n,), 0x55, dtype=torch.uint8, device="cuda")   # garbage before the call
+    la.la_forward_causal(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    words = ws[:8].view(torch.int32).cpu().tolist()
+    assert words[1] == 0, words
+
+
 def test_segment_plan_independence():
     """A head computed alone and inside a large batch (different segment cuts)
     gives the same result up to fp32 rounding."""
