@@ -148,8 +148,9 @@ __device__ __forceinline__ dwordx4 phi8(dwordx4 x) {
 }
 
 // Writes the loaded rows into the staging area (row stride F + kStagePad);
-// with PHI the feature map is applied and rows at or beyond t_end become 0.
-template <int F, int TT, bool PHI>
+// with PHI the feature map is applied, with MASK rows at or beyond t_end
+// become 0.
+template <int F, int TT, bool PHI, bool MASK = PHI>
 __device__ __forceinline__ void stage_lines(lds_bf16 *stage, const dwordx4 (&x)[TT * F / 32], int64_t t0,
                                             int64_t t_end) {
     const int l = lane_id();
@@ -158,10 +159,8 @@ __device__ __forceinline__ void stage_lines(lds_bf16 *stage, const dwordx4 (&x)[
         const int e = (64 * i + l) * 8;
         const int row = e / F, col = e % F;
         dwordx4 y = x[i];
-        if (PHI) {
-            y = phi8(y);
-            if (t0 + row >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
-        }
+        if (PHI) y = phi8(y);
+        if (MASK && t0 + row >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
         *reinterpret_cast<lds_dwordx4 *>(stage + row * (F + kStagePad) + col) = y;
     }
 }

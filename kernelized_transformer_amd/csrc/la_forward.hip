@@ -20,9 +20,9 @@
 // state, then (after learning the state of everything before it) producing
 // the outputs chunk by chunk while carrying (S, Z) in registers.
 //   causal (one launch, k_fwd_fused): four wavefronts form a block; their
-//     local states are combined in LDS, and blocks of the same (b, h) hand
-//     their states to each other through the workspace with a decoupled
-//     look-back (see the comment at the kernel);
+//     local states are combined in LDS, and the blocks of one (b, h) form
+//     their prefix states together through the workspace (see the comment
+//     at the kernel);
 //   non-causal (three launches): per-segment states, their sum per (b, h),
 //     then the readout.
 #include "la_chunk.h"
@@ -253,10 +253,13 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
         const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
-        stage_lines<D, TT, true>(sq, rq[b], t0, t_end);
+        // no row masks: rows past t_end hold copies of the last valid row (finite),
+        // their outputs are not stored, the causal mask keeps them out of every
+        // stored output, and the state is not used after the last chunk
+        stage_lines<D, TT, true, false>(sq, rq[b], t0, t_end);
         if (CAUSAL) {
-            stage_lines<D, TT, true>(sk, rk[b], t0, t_end);
-            stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
+            stage_lines<D, TT, true, false>(sk, rk[b], t0, t_end);
+            stage_lines<M, TT, false, false>(sv, rv[b], t0, t_end);
         }
         load_lines<D, TT>(rq[b], Q, t0 + PF * CH, t_end);
         if (CAUSAL) {
@@ -450,27 +453,72 @@ hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mod
 // of one (b, h).  Blocks take tickets in launch order from a counter, so a
 // block only ever waits on blocks that are already running.
 //   1. each wavefront sums phi(K) [V, 1]^T over its sub-segment (fp32);
-//   2. the block total A_s = A_w0 + A_w1 + ... is published (flag = 1);
-//      the block then finds, among its predecessors, the nearest one p whose
-//      inclusive prefix I_p is published (flag = 2), waiting only until every
-//      block between p and s has published its total, and forms its
-//      exclusive prefix P_s = I_p + A_{p+1} + ... + A_{s-1}, always summed in
-//      increasing block order.  Since every I_p is itself such a left-to-right
-//      sum, P_s has the same bits whichever p is found: results do not depend
-//      on timing.  I_s = P_s + A_s is published (flag = 2);
+//   2. hand-off between the nb blocks of a head, through the workspace:
+//      a. block s publishes its total A_s = A_w0 + A_w1 + ... (the last block
+//         of the head publishes none: nobody needs it);
+//      b. the record is cut into nb slices and block s owns slice s: once all
+//         totals are out it forms, for its slice, the exclusive prefixes
+//         P_t = A_0 + A_1 + ... + A_{t-1} of every block t (one running sum in
+//         block order per element) and publishes them;
+//      c. once every slice is out, block s reads its P_s.
+//      Each element of each P_t is summed by one thread in a fixed order, so
+//      results do not depend on timing.  A block moves 3 records and waits
+//      twice, however many blocks precede it;
 //   3. wavefront w starts from P_s + A_w0 + ... + A_{w-1} and writes its
 //      outputs, re-reading its K, V (mostly from the memory-side cache).
-// Records go through the workspace with plain loads and stores ordered by
-// agent-scope release/acquire fences around the flag accesses (visible
-// across XCDs); only wavefront 0 of a block touches them.  Every wait is bounded: a
-// block that waited too long sets the error word and carries on, so every
-// wavefront always exits.
+// Records and flags move with device-coherent (agent-scope, sc1) loads and
+// stores, which bypass the per-XCD caches that are not kept coherent with
+// each other; a flag is stored only after the wavefront's record stores have
+// completed (vmcnt 0), and records are loaded only after the flag has been
+// seen.  No cache-wide write-back or invalidate is needed, so the hand-off
+// does not disturb the other blocks' cached K, V.  Only wavefront 0 of a block
+// stores records.  Every wait is bounded: a block that waited too long sets
+// the error word and carries on, so every wavefront always exits.  All blocks
+// of a head must be able to run at the same time (at most kMaxBlkPerHead
+// blocks of kFusedWaves wavefronts); the chip holds hundreds.
 constexpr int kSpinLimit = 1 << 20;
-constexpr int kLookbackBatch = 8;
+constexpr int kWaitVmcnt0 = 0x0f70;   // s_waitcnt vmcnt(0), other counters untouched
+
+__device__ __forceinline__ void dev_store(f32x4 *p, f32x4 x) {
+    unsigned long long *u = reinterpret_cast<unsigned long long *>(p);
+    __hip_atomic_store(u, __builtin_bit_cast(unsigned long long, f32x2{x[0], x[1]}), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(u + 1, __builtin_bit_cast(unsigned long long, f32x2{x[2], x[3]}), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 dev_load(const f32x4 *p) {
+    const unsigned long long *u = reinterpret_cast<const unsigned long long *>(p);
+    const f32x2 a = __builtin_bit_cast(f32x2, __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const f32x2 b = __builtin_bit_cast(f32x2, __hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return f32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Sets *flag once every earlier store of this wavefront has completed.
+__device__ __forceinline__ void publish_flag(int *flag) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the compiler keeps the stores above
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                  // the hardware completes them
+    if (lane_id() == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __global__ void k_fused_reset(int *__restrict__ words, int64_t n) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < n) words[i] = 0;
+}
+
+// Wavefront-wide wait until flags[0 .. count) are all set (count <= 64).
+__device__ __forceinline__ void wait_flags(const int *flags, int count, int *err) {
+    const int lane = lane_id();
+    for (int iter = 0;; ++iter) {
+        const int f = (lane < count) ? __hip_atomic_load(&flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+        if (__ballot(f == 0) == 0) break;
+        if (iter >= kSpinLimit) {
+            if (lane == 0) atomicOr(err, 1);   // gave up: results are wrong, the error word says so
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // later loads stay below (compiler)
 }
 
 template <typename T, int D, int M>
@@ -479,13 +527,19 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
                                                                 int *__restrict__ header, int *__restrict__ flags,
                                                                 float *__restrict__ recs, int64_t N, int64_t nblk,
                                                                 int64_t sub_tokens) {
-    constexpr int REC = D * M + D;
-    __shared__ float lds_a[kFusedWaves][REC];   // per-wavefront totals
-    __shared__ float lds_p[REC];                // the block's exclusive prefix
-    __shared__ float lds_x[REC];                // block total, then inclusive prefix
-    __shared__ int lds_ticket, lds_from;
+    constexpr int REC = D * M + D, REC4 = REC / 4;
+    static_assert(REC % 4 == 0, "records move as f32x4");
+    constexpr int NT = 64 * kFusedWaves;
+    __shared__ __align__(16) float lds_a[kFusedWaves][REC];   // per-wavefront totals, then partial sums
     constexpr int SK = stage_elems<D / 16, TT>(), SV = stage_elems<M / 16, TT>();
-    __shared__ bf16 lds_stage[kFusedWaves][2 * SK + SV];   // per-wavefront staging: q, k, v
+    __shared__ __align__(16) bf16 lds_stage[kFusedWaves][2 * SK + SV];   // per-wavefront staging: q, k, v
+    // during the hand-off the staging area holds the prefix slice being formed
+    // (at most REC4 + kMaxBlkPerHead f32x4) and then the block's prefix
+    constexpr int SLICE4 = REC4 + int(kMaxBlkPerHead);
+    static_assert(sizeof(lds_stage) >= (SLICE4 + REC4) * sizeof(f32x4), "hand-off scratch fits the staging area");
+    f32x4 *slice = reinterpret_cast<f32x4 *>(&lds_stage[0][0]);
+    float *pbuf = reinterpret_cast<float *>(slice + SLICE4);
+    __shared__ int lds_ticket;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
 
@@ -493,14 +547,15 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     __syncthreads();
     const int64_t ticket = __builtin_amdgcn_readfirstlane(lds_ticket);
     const int64_t bh = ticket / nblk, blk = ticket % nblk;
+    const int nb = int(nblk), sb = int(blk);
     const int64_t t_begin = min(N, (blk * kFusedWaves + wave) * sub_tokens);
     const int64_t t_end = min(N, t_begin + sub_tokens);
     const T *Q = q + bh * N * D;
     const T *K = k + bh * N * D;
     const T *V = v + bh * N * M;
-    int *fl = flags + bh * nblk;
-    float *agg_rec = recs + (bh * nblk + blk) * 2 * REC;
-    float *inc_rec = agg_rec + REC;
+    int *flag_tot = flags + bh * 2 * nblk;   // [nblk]: total published
+    int *flag_pre = flag_tot + nblk;         // [nblk]: prefix slice published
+    float *head_recs = recs + bh * nblk * 2 * REC;   // per block: total, exclusive prefix
 
     // 1. local totals
     f32x4 St[D / 16][M / 16 + 1];
@@ -513,108 +568,99 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     else
         seg_aggregate<T, D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
     state_store<D, M>(&lds_a[wave][0], St);
+    __syncthreads();   // also: every wavefront is done with its staging area
+
+    // 2a. in place: lds_a[w] = A_w0 + ... + A_{w-1} for w >= 1, lds_a[0] = the
+    // block total A_s (wavefront 0's partial sum is zero)
+#pragma unroll
+    for (int j = 0; j < (REC + NT - 1) / NT; ++j) {
+        const int e = tid + NT * j;
+        if (e < REC) {
+            float run = lds_a[0][e];
+#pragma unroll
+            for (int w = 1; w < kFusedWaves; ++w) {
+                const float x = lds_a[w][e];
+                lds_a[w][e] = run;
+                run += x;
+            }
+            lds_a[0][e] = run;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        if (sb < nb - 1) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + blk * 2 * REC);
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(&lds_a[0][0]);
+            for (int i = lane; i < REC4; i += 64) dev_store(dst + i, src[i]);
+            publish_flag(&flag_tot[blk]);
+        }
+        for (int i = lane; i < REC; i += 64) lds_a[0][i] = 0.f;   // wavefront 0 starts from P_s alone
+        if (nb > 1) wait_flags(flag_tot, nb - 1, &header[1]);
+    }
     __syncthreads();
 
-    // 2. block total, publish, look-back, exclusive and inclusive prefix.
-    // Wavefront 0 alone stores records and flags, so its own agent-scope
-    // release fences order them; all wavefronts share the summation of the
-    // predecessors' records (loads of kLookbackBatch records kept in flight,
-    // added in increasing block order).
-    const bool last = blk == nblk - 1;
-    constexpr int NT = 64 * kFusedWaves;
-    constexpr int NJ = (REC + NT - 1) / NT;
-    float a[NJ];
+    if (nb > 1) {
+        // 2b. this block's slice [c0, c0 + ncol) of every prefix P_1 .. P_{nb-1}
+        const int per = (REC4 + nb - 1) / nb;
+        const int c0 = min(REC4, sb * per), ncol = min(REC4, c0 + per) - c0;
+        const int items = (nb - 1) * ncol;   // <= SLICE4
+        {
+            constexpr int NI = (SLICE4 + NT - 1) / NT;
+            f32x4 buf[NI];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = tid + NT * j;
-        float x = 0.f;
-        if (e < REC) {
-            x = lds_a[0][e];
-#pragma unroll
-            for (int w = 1; w < kFusedWaves; ++w) x += lds_a[w][e];
-            lds_x[e] = x;
-        }
-        a[j] = x;
-    }
-    __syncthreads();
-    if (wave == 0 && blk > 0) {
-        if (!last) {
-            for (int e = lane; e < REC; e += 64) agg_rec[e] = lds_x[e];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            if (lane == 0) __hip_atomic_store(&fl[blk], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // lane i watches block blk - 1 - i; lane blk stands for "before block 0"
-        int from = -1;
-        for (int iter = 0;; ++iter) {
-            int f = 0;
-            if (lane < blk) f = __hip_atomic_load(&fl[blk - 1 - lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const unsigned long long incl = __ballot(lane < blk ? f == 2 : lane == blk);
-            const unsigned long long none = __ballot(lane < blk && f == 0);
-            const int i = __builtin_ctzll(incl);   // nearest inclusive (lane blk always qualifies)
-            const unsigned long long below = (i >= 63) ? ~0ull : ((1ull << i) - 1);
-            if ((none & below) == 0) {
-                from = int(blk) - 1 - i;           // -1: start from block 0's inclusive
-                break;
-            }
-            if (iter >= kSpinLimit) {
-                if (lane == 0) atomicOr(&header[1], 1);
-                from = int(blk) - 1;               // gave up waiting: result is wrong, error word set
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (lane == 0) lds_from = from;
-    }
-    __syncthreads();
-    float p[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) p[j] = 0.f;
-    if (blk > 0) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const int64_t from = __builtin_amdgcn_readfirstlane(lds_from);
-        const float *base = recs + (bh * nblk) * 2 * REC;
-        // P_s = I_from + A_{from+1} + ... + A_{blk-1}, left to right; block 0
-        // publishes no separate total (its inclusive is its total)
-        const float *first = (from >= 0) ? base + (from * 2 + 1) * REC : base + REC;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int e = tid + NT * j;
-            if (e < REC) p[j] = first[e];
-        }
-        for (int64_t b0 = (from >= 0 ? from + 1 : 1); b0 < blk; b0 += kLookbackBatch) {
-            float buf[kLookbackBatch][NJ];
-#pragma unroll
-            for (int r = 0; r < kLookbackBatch; ++r) {
-                const float *src = base + (b0 + r) * 2 * REC;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int e = tid + NT * j;
-                    buf[r][j] = (b0 + r < blk && e < REC) ? src[e] : 0.f;
+            for (int j = 0; j < NI; ++j) {   // all loads in flight before the first LDS store
+                const int i = tid + NT * j;
+                if (i < items) {
+                    const int t = i / ncol, cc = i - t * ncol;
+                    buf[j] = dev_load(reinterpret_cast<const f32x4 *>(head_recs + int64_t(t) * 2 * REC) + c0 + cc);
                 }
             }
 #pragma unroll
-            for (int r = 0; r < kLookbackBatch; ++r) {
-                if (b0 + r < blk) {
+            for (int j = 0; j < NI; ++j)
+                if (tid + NT * j < items) slice[tid + NT * j] = buf[j];
+        }
+        __syncthreads();
+        for (int cc = tid; cc < ncol; cc += NT) {   // running sum down each column, in block order
+            f32x4 run = {0.f, 0.f, 0.f, 0.f};
+            for (int t0 = 0; t0 < nb - 1; t0 += 8) {
+                f32x4 x[8];
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) p[j] += buf[r][j];
-                }
+                for (int u = 0; u < 8; ++u)
+                    if (t0 + u < nb - 1) x[u] = slice[(t0 + u) * ncol + cc];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (t0 + u < nb - 1) {
+                        run += x[u];
+                        slice[(t0 + u) * ncol + cc] = run;   // = P_{t0+u+1}
+                    }
             }
         }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = tid + NT * j;
-        if (e < REC) {
-            lds_p[e] = p[j];
-            lds_x[e] = (blk > 0) ? p[j] + a[j] : a[j];
+        __syncthreads();
+        if (wave == 0) {
+            for (int i = lane; i < items; i += 64) {
+                const int t = i / ncol, cc = i - t * ncol;
+                dev_store(reinterpret_cast<f32x4 *>(head_recs + (int64_t(t + 1) * 2 + 1) * REC) + c0 + cc, slice[i]);
+            }
+            publish_flag(&flag_pre[blk]);
+            if (sb > 0) wait_flags(flag_pre, nb, &header[1]);
         }
+        __syncthreads();
+    }
+    // 2c. P_s into LDS (zero for the first block)
+    if (sb > 0) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(head_recs + (blk * 2 + 1) * REC);
+        constexpr int NJ4 = (REC4 + NT - 1) / NT;
+        f32x4 buf[NJ4];
+#pragma unroll
+        for (int j = 0; j < NJ4; ++j)
+            if (tid + NT * j < REC4) buf[j] = dev_load(src + tid + NT * j);
+#pragma unroll
+        for (int j = 0; j < NJ4; ++j)
+            if (tid + NT * j < REC4) reinterpret_cast<f32x4 *>(pbuf)[tid + NT * j] = buf[j];
+    } else {
+        for (int i = tid; i < REC; i += NT) pbuf[i] = 0.f;
     }
     __syncthreads();
-    if (wave == 0 && !last) {
-        for (int e = lane; e < REC; e += 64) inc_rec[e] = lds_x[e];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        if (lane == 0) __hip_atomic_store(&fl[blk], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 
     // 3. outputs, starting from P_s + the totals of the earlier wavefronts
     {
@@ -626,24 +672,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int d = 16 * dt + 4 * g + r;
-                    int e;
-                    bool on = true;
-                    if (mt < M / 16) {
-                        e = d * M + 16 * mt + c;
-                    } else {
-                        e = D * M + d;
-                        on = c == 0;
-                    }
-                    float x = 0.f;
-                    if (on) {
-                        x = lds_p[e];
-                        for (int w = 0; w < wave; ++w) x += lds_a[w][e];
-                    }
-                    St[dt][mt][r] = x;
+                    const bool z = mt == M / 16;
+                    const int e = z ? D * M + d : d * M + 16 * mt + c;
+                    St[dt][mt][r] = (!z || c == 0) ? pbuf[e] + lds_a[wave][e] : 0.f;
                 }
             }
         }
     }
+    __syncthreads();   // the prefix is read: the staging area is free again
     if constexpr (sizeof(T) == 2)
         seg_output_bf16<D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q, stage_k,
                                                stage_v);
@@ -661,7 +697,7 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
         int *header = reinterpret_cast<int *>(base);
         int *flags = reinterpret_cast<int *>(base + p.flags_off);
         float *recs = reinterpret_cast<float *>(base + p.recs_off);
-        const int64_t nreset = int64_t(p.flags_off / sizeof(int)) + BH * p.nblk;   // header + flags
+        const int64_t nreset = int64_t(p.flags_off / sizeof(int)) + 2 * BH * p.nblk;   // header + flags
         hipLaunchKernelGGL(k_fused_reset, dim3(unsigned((nreset + 255) / 256)), dim3(256), 0, s, header, nreset);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -50,19 +50,20 @@ inline size_t forward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t 
 
 // The causal forward runs as one pass: workgroups of kFusedWaves wavefronts,
 // each workgroup owning a block of kFusedWaves consecutive sub-segments (one
-// per wavefront) of one (b, h).  Blocks exchange their fp32 state records
-// through the workspace (decoupled look-back), so no segment scan launch is
-// needed.
+// per wavefront) of one (b, h).  Blocks exchange fp32 state records through
+// the workspace (block totals, then their exclusive prefix sums, computed
+// slice by slice by all blocks of the head), so no scan launch is needed.
 constexpr int kFusedWaves = 4;
-constexpr int64_t kMaxBlkPerHead = 64;   // look-back window = one wavefront of flags
+constexpr int64_t kMaxBlkPerHead = 64;   // flags of a head fit one wavefront
 constexpr int64_t kTargetWaves = 1024;   // one wavefront per SIMD of the 256 CUs
 
 struct FusedPlan {
     int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
     int64_t nblk = 0;        // blocks per (b, h)
     int64_t rec = 0;         // floats per state record
-    size_t flags_off = 0;    // int flags [BH][nblk] (after a 256-byte header: ticket, error word)
-    size_t recs_off = 0;     // float records [BH][nblk][2][rec]: block aggregate, inclusive prefix
+    size_t flags_off = 0;    // int flags [BH][2][nblk]: total published, prefix slice published
+                             // (after a 256-byte header: ticket counter, error word)
+    size_t recs_off = 0;     // float records [BH][nblk][2][rec]: block total, exclusive prefix
     size_t total = 0;
 };
 
@@ -77,7 +78,7 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
     p.rec = D * M + D;
     p.flags_off = 256;
-    p.recs_off = p.flags_off + align256(size_t(BH * p.nblk) * sizeof(int));
+    p.recs_off = p.flags_off + align256(size_t(2 * BH * p.nblk) * sizeof(int));
     p.total = p.recs_off + align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float));
     return p;
 }
