@@ -101,8 +101,8 @@ def main():
         q, k, v, g = wl.forward_inputs(w4, with_dout=True, seed=seed)
         sets.append(tuple(to_dev(x, "bf16") for x in (q, k, v, g)))
     out = torch.empty((w4.B, w4.H, w4.N, w4.M), dtype=torch.bfloat16, device=dev)
-    ws_f = torch.empty(la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w4.B, w4.H, w4.N, w4.D, w4.M, torch.bfloat16),
-                       dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(la.la_workspace_size(op, w4.B, w4.H, w4.N, w4.D, w4.M, torch.bfloat16)
+                           for op in (la.LA_OP_FWD_CAUSAL, la.LA_OP_FWD_NONCAUSAL)), dtype=torch.uint8, device=dev)
 
     def fwd(i, causal=True):
         q, k, v, _ = sets[i % 2]

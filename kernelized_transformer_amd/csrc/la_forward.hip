@@ -6,7 +6,7 @@
 //               prefix states S_i = sum_{j<=i} phi(K_j) V_j^T, Z_i = sum_{j<=i} phi(K_j);
 //   non-causal: the same with S, Z summed over all tokens.
 // The training-time form is evaluated in parallel over the sequence
-// ([summary] 3.3.2): the sequence is cut into chunks of 32 tokens, and a
+// ([summary] 3.3.2): the sequence is cut into chunks of 16 tokens, and a
 // chunk's outputs are
 //   num_c = tril(phi(Q_c) phi(K_c)^T) V_c + phi(Q_c) S_prev,
 //   den_c = tril(phi(Q_c) phi(K_c)^T) 1   + phi(Q_c) Z_prev,
@@ -19,7 +19,7 @@
 // and walks it twice: first summing phi(K_t) [V_t, 1]^T into a local fp32
 // state, then (after learning the state of everything before it) producing
 // the outputs chunk by chunk while carrying (S, Z) in registers.
-//   causal (one launch, k_fwd_fused): four wavefronts form a block; their
+//   causal (one launch, k_fwd_fused): eight wavefronts (two per SIMD) form a block; their
 //     local states are combined in LDS, and the blocks of one (b, h) form
 //     their prefix states together through the workspace (see the comment
 //     at the kernel);
@@ -30,7 +30,7 @@
 
 namespace la {
 
-constexpr int TT = 2;        // token tiles per chunk in the forward kernels
+constexpr int TT = 1;        // token tiles per chunk in the forward kernels
 constexpr int CH = 16 * TT;  // = kChunk
 static_assert(CH == kChunk, "forward chunk");
 constexpr int kPrefetch = 2; // chunks in flight ahead of the one being computed
@@ -171,9 +171,13 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
             for (int mt = 0; mt <= MT; ++mt)
 #pragma unroll
                 for (int it = 0; it < TT; ++it) {
-                    const Fr a0 = (mt < MT) ? VT[0][mt] : ones;
-                    const Fr a1 = (mt < MT) ? VT[1][mt] : ones;
-                    mma2(Ot[mt][it], a0, a1, PT[0][it], PT[1][it]);
+                    Fr a[TT], b[TT];
+#pragma unroll
+                    for (int jt = 0; jt < TT; ++jt) {
+                        a[jt] = (mt < MT) ? VT[jt][mt] : ones;
+                        b[jt] = PT[jt][it];
+                    }
+                    mma_tiles<Fr, TT>(Ot[mt][it], a, b);
                 }
             state_accumulate<Fr, D, M, TT>(St, KT, VT);
         }
@@ -317,9 +321,13 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
             for (int mt = 0; mt <= MT; ++mt)
 #pragma unroll
                 for (int it = 0; it < TT; ++it) {
-                    const Fr a0 = (mt < MT) ? VT[0][mt] : ones;
-                    const Fr a1 = (mt < MT) ? VT[1][mt] : ones;
-                    mma2(Ot[mt][it], a0, a1, PT[0][it], PT[1][it]);
+                    Fr a[TT], b[TT];
+#pragma unroll
+                    for (int jt = 0; jt < TT; ++jt) {
+                        a[jt] = (mt < MT) ? VT[jt][mt] : ones;
+                        b[jt] = PT[jt][it];
+                    }
+                    mma_tiles<Fr, TT>(Ot[mt][it], a, b);
                 }
             state_accumulate<Fr, D, M, TT>(St, KT, VT);
         }
@@ -522,7 +530,7 @@ __device__ __forceinline__ void wait_flags(const int *flags, int count, int *err
 }
 
 template <typename T, int D, int M>
-__global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd_fused(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd_fused(const T *__restrict__ q, const T *__restrict__ k,
                                                                 const T *__restrict__ v, T *__restrict__ out,
                                                                 int *__restrict__ header, int *__restrict__ flags,
                                                                 float *__restrict__ recs, int64_t N, int64_t nblk,
@@ -530,15 +538,21 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     constexpr int REC = D * M + D, REC4 = REC / 4;
     static_assert(REC % 4 == 0, "records move as f32x4");
     constexpr int NT = 64 * kFusedWaves;
-    __shared__ __align__(16) float lds_a[kFusedWaves][REC];   // per-wavefront totals, then partial sums
+    // LDS: per-wavefront staging (q, k, v chunks) during the two passes; during
+    // the hand-off the same bytes hold one slot per wavefront: slot w >= 1 the
+    // partial sum A_w0 + ... + A_{w-1}, slot 0 the block total, then the
+    // prefix slice being formed (at most REC4 + kMaxBlkPerHead float4), then
+    // the block's own prefix P_s.
     constexpr int SK = stage_elems<D / 16, TT>(), SV = stage_elems<M / 16, TT>();
-    __shared__ __align__(16) bf16 lds_stage[kFusedWaves][2 * SK + SV];   // per-wavefront staging: q, k, v
-    // during the hand-off the staging area holds the prefix slice being formed
-    // (at most REC4 + kMaxBlkPerHead f32x4) and then the block's prefix
-    constexpr int SLICE4 = REC4 + int(kMaxBlkPerHead);
-    static_assert(sizeof(lds_stage) >= (SLICE4 + REC4) * sizeof(f32x4), "hand-off scratch fits the staging area");
-    f32x4 *slice = reinterpret_cast<f32x4 *>(&lds_stage[0][0]);
-    float *pbuf = reinterpret_cast<float *>(slice + SLICE4);
+    constexpr int STAGE_BYTES = kFusedWaves * (2 * SK + SV) * int(sizeof(bf16));
+    constexpr int SLOT4 = REC4 + int(kMaxBlkPerHead);
+    constexpr int SLOT_BYTES = kFusedWaves * SLOT4 * int(sizeof(f32x4));
+    __shared__ __align__(16) unsigned char lds_raw[STAGE_BYTES > SLOT_BYTES ? STAGE_BYTES : SLOT_BYTES];
+    bf16 *lds_stage = reinterpret_cast<bf16 *>(lds_raw);
+    f32x4 *slot4 = reinterpret_cast<f32x4 *>(lds_raw);
+    auto slot = [&](int w) { return reinterpret_cast<float *>(slot4 + w * SLOT4); };
+    f32x4 *slice = slot4;               // slot 0
+    float *pbuf = slot(0);              // slot 0, once the slice is out
     __shared__ int lds_ticket;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
@@ -560,41 +574,41 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     // 1. local totals
     f32x4 St[D / 16][M / 16 + 1];
     state_zero<D, M>(St);
-    lds_bf16 *stage_q = (lds_bf16 *)(&lds_stage[wave][0]);
+    lds_bf16 *stage_q = (lds_bf16 *)(lds_stage + wave * (2 * SK + SV));
     lds_bf16 *stage_k = stage_q + SK;
     lds_bf16 *stage_v = stage_k + SK;
     if constexpr (sizeof(T) == 2)
         seg_aggregate_bf16<D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
     else
         seg_aggregate<T, D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
-    state_store<D, M>(&lds_a[wave][0], St);
-    __syncthreads();   // also: every wavefront is done with its staging area
+    __syncthreads();   // every wavefront is done with its staging area
+    state_store<D, M>(slot(wave), St);
+    __syncthreads();
 
-    // 2a. in place: lds_a[w] = A_w0 + ... + A_{w-1} for w >= 1, lds_a[0] = the
+    // 2a. in place: slot w = A_w0 + ... + A_{w-1} for w >= 1, slot 0 = the
     // block total A_s (wavefront 0's partial sum is zero)
 #pragma unroll
     for (int j = 0; j < (REC + NT - 1) / NT; ++j) {
         const int e = tid + NT * j;
         if (e < REC) {
-            float run = lds_a[0][e];
+            float run = slot(0)[e];
 #pragma unroll
             for (int w = 1; w < kFusedWaves; ++w) {
-                const float x = lds_a[w][e];
-                lds_a[w][e] = run;
+                const float x = slot(w)[e];
+                slot(w)[e] = run;
                 run += x;
             }
-            lds_a[0][e] = run;
+            slot(0)[e] = run;
         }
     }
     __syncthreads();
     if (wave == 0) {
         if (sb < nb - 1) {
             f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + blk * 2 * REC);
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(&lds_a[0][0]);
+            const f32x4 *src = slot4;
             for (int i = lane; i < REC4; i += 64) dev_store(dst + i, src[i]);
             publish_flag(&flag_tot[blk]);
         }
-        for (int i = lane; i < REC; i += 64) lds_a[0][i] = 0.f;   // wavefront 0 starts from P_s alone
         if (nb > 1) wait_flags(flag_tot, nb - 1, &header[1]);
     }
     __syncthreads();
@@ -603,9 +617,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         // 2b. this block's slice [c0, c0 + ncol) of every prefix P_1 .. P_{nb-1}
         const int per = (REC4 + nb - 1) / nb;
         const int c0 = min(REC4, sb * per), ncol = min(REC4, c0 + per) - c0;
-        const int items = (nb - 1) * ncol;   // <= SLICE4
+        const int items = (nb - 1) * ncol;   // <= SLOT4
         {
-            constexpr int NI = (SLICE4 + NT - 1) / NT;
+            constexpr int NI = (SLOT4 + NT - 1) / NT;
             f32x4 buf[NI];
 #pragma unroll
             for (int j = 0; j < NI; ++j) {   // all loads in flight before the first LDS store
@@ -674,7 +688,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
                     const int d = 16 * dt + 4 * g + r;
                     const bool z = mt == M / 16;
                     const int e = z ? D * M + d : d * M + 16 * mt + c;
-                    St[dt][mt][r] = (!z || c == 0) ? pbuf[e] + lds_a[wave][e] : 0.f;
+                    St[dt][mt][r] = (!z || c == 0) ? pbuf[e] + (wave > 0 ? slot(wave)[e] : 0.f) : 0.f;
                 }
             }
         }

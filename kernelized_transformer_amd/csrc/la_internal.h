@@ -9,7 +9,7 @@ namespace la {
 
 // Tokens per chunk: the unit of the intra-chunk masked product on the
 // matrix cores (two 16-token tiles).
-constexpr int64_t kChunk = 32;
+constexpr int64_t kChunk = 16;
 // Largest number of segments per (b, h) the segment scan handles.
 constexpr int64_t kMaxSegPerHead = 256;
 // Aim for about this many independent segments (one wavefront each) so that
@@ -53,9 +53,9 @@ inline size_t forward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t 
 // per wavefront) of one (b, h).  Blocks exchange fp32 state records through
 // the workspace (block totals, then their exclusive prefix sums, computed
 // slice by slice by all blocks of the head), so no scan launch is needed.
-constexpr int kFusedWaves = 4;
+constexpr int kFusedWaves = 8;
 constexpr int64_t kMaxBlkPerHead = 64;   // flags of a head fit one wavefront
-constexpr int64_t kTargetWaves = 1024;   // one wavefront per SIMD of the 256 CUs
+constexpr int64_t kTargetWaves = 2048;   // two wavefronts per SIMD of the 256 CUs
 
 struct FusedPlan {
     int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
