@@ -502,11 +502,13 @@ __device__ __forceinline__ f32x4 dev_load(const f32x4 *p) {
     return f32x4{a[0], a[1], b[0], b[1]};
 }
 
-// Sets *flag once every earlier store of this wavefront has completed.
-__device__ __forceinline__ void publish_flag(int *flag) {
+// Whole workgroup: every thread's earlier stores complete, then one thread
+// sets *flag.
+__device__ __forceinline__ void block_publish(int *flag) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the compiler keeps the stores above
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                  // the hardware completes them
-    if (lane_id() == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void k_fused_reset(int *__restrict__ words, int64_t n) {
@@ -541,8 +543,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     // LDS: per-wavefront staging (q, k, v chunks) during the two passes; during
     // the hand-off the same bytes hold one slot per wavefront: slot w >= 1 the
     // partial sum A_w0 + ... + A_{w-1}, slot 0 the block total, then the
-    // prefix slice being formed (at most REC4 + kMaxBlkPerHead float4), then
-    // the block's own prefix P_s.
+    // group sums of the prefix slice being formed, then the block's own
+    // prefix P_s.
     constexpr int SK = stage_elems<D / 16, TT>(), SV = stage_elems<M / 16, TT>();
     constexpr int STAGE_BYTES = kFusedWaves * (2 * SK + SV) * int(sizeof(bf16));
     constexpr int SLOT4 = REC4 + int(kMaxBlkPerHead);
@@ -551,8 +553,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     bf16 *lds_stage = reinterpret_cast<bf16 *>(lds_raw);
     f32x4 *slot4 = reinterpret_cast<f32x4 *>(lds_raw);
     auto slot = [&](int w) { return reinterpret_cast<float *>(slot4 + w * SLOT4); };
-    f32x4 *slice = slot4;               // slot 0
-    float *pbuf = slot(0);              // slot 0, once the slice is out
+    float *pbuf = slot(0);
     __shared__ int lds_ticket;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
@@ -602,62 +603,56 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        if (sb < nb - 1) {
-            f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + blk * 2 * REC);
-            const f32x4 *src = slot4;
-            for (int i = lane; i < REC4; i += 64) dev_store(dst + i, src[i]);
-            publish_flag(&flag_tot[blk]);
-        }
-        if (nb > 1) wait_flags(flag_tot, nb - 1, &header[1]);
+    if (sb < nb - 1) {   // every thread stores a share of the total
+        f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + blk * 2 * REC);
+#pragma unroll
+        for (int j = 0; j < (REC4 + NT - 1) / NT; ++j)
+            if (tid + NT * j < REC4) dev_store(dst + tid + NT * j, slot4[tid + NT * j]);
+        block_publish(&flag_tot[blk]);
     }
+    if (wave == 0 && nb > 1) wait_flags(flag_tot, nb - 1, &header[1]);
     __syncthreads();
 
     if (nb > 1) {
-        // 2b. this block's slice [c0, c0 + ncol) of every prefix P_1 .. P_{nb-1}
+        // 2b. this block's slice [c0, c0 + ncol) of every prefix P_1 .. P_{nb-1}.
+        // Work unit (column cc, row group g): rows g R .. g R + R - 1 of the
+        // nr = nb - 1 totals; a unit sums its rows, the group sums go through
+        // LDS, and each row's prefix is (sum of the earlier groups) + (running
+        // sum within the group) -- a fixed order for every element.
+        const int nr = nb - 1;
         const int per = (REC4 + nb - 1) / nb;
         const int c0 = min(REC4, sb * per), ncol = min(REC4, c0 + per) - c0;
-        const int items = (nb - 1) * ncol;   // <= SLOT4
-        {
-            constexpr int NI = (SLOT4 + NT - 1) / NT;
-            f32x4 buf[NI];
+        const int G = ncol > 0 ? max(1, min(nr, NT / max(ncol, 1))) : 1;
+        const int R = (nr + G - 1) / G;
+        constexpr int RMAX = kFusedSliceRows;   // R <= RMAX (checked on the host)
+        f32x4 *gsum = slot4;      // [G][ncol] group sums, in slot 0
+        f32x4 run[RMAX];
+        for (int u0 = 0; u0 < ncol * G; u0 += NT) {   // one pass unless ncol > NT
+            const int u = u0 + tid;
+            const bool on = u < ncol * G;
+            const int g = on ? u / ncol : 0, cc = on ? u - g * ncol : 0;
+            const int r0 = g * R;
+            const f32x4 *col = reinterpret_cast<const f32x4 *>(head_recs) + c0 + cc;
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {   // all loads in flight before the first LDS store
-                const int i = tid + NT * j;
-                if (i < items) {
-                    const int t = i / ncol, cc = i - t * ncol;
-                    buf[j] = dev_load(reinterpret_cast<const f32x4 *>(head_recs + int64_t(t) * 2 * REC) + c0 + cc);
-                }
+            for (int k = 0; k < RMAX; ++k)   // all loads in flight first
+                run[k] = (on && k < R && r0 + k < nr) ? dev_load(col + int64_t(r0 + k) * 2 * REC4)
+                                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 1; k < RMAX; ++k) run[k] += run[k - 1];
+            if (on) gsum[g * ncol + cc] = run[RMAX - 1];
+            __syncthreads();
+            if (on) {
+                f32x4 off = {0.f, 0.f, 0.f, 0.f};
+                for (int h = 0; h < g; ++h) off += gsum[h * ncol + cc];
+                f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + 3 * REC) + c0 + cc;   // prefix of block r + 1
+#pragma unroll
+                for (int k = 0; k < RMAX; ++k)
+                    if (k < R && r0 + k < nr) dev_store(dst + int64_t(r0 + k) * 2 * REC4, (g > 0 ? off + run[k] : run[k]));
             }
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                if (tid + NT * j < items) slice[tid + NT * j] = buf[j];
+            __syncthreads();
         }
-        __syncthreads();
-        for (int cc = tid; cc < ncol; cc += NT) {   // running sum down each column, in block order
-            f32x4 run = {0.f, 0.f, 0.f, 0.f};
-            for (int t0 = 0; t0 < nb - 1; t0 += 8) {
-                f32x4 x[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (t0 + u < nb - 1) x[u] = slice[(t0 + u) * ncol + cc];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (t0 + u < nb - 1) {
-                        run += x[u];
-                        slice[(t0 + u) * ncol + cc] = run;   // = P_{t0+u+1}
-                    }
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            for (int i = lane; i < items; i += 64) {
-                const int t = i / ncol, cc = i - t * ncol;
-                dev_store(reinterpret_cast<f32x4 *>(head_recs + (int64_t(t + 1) * 2 + 1) * REC) + c0 + cc, slice[i]);
-            }
-            publish_flag(&flag_pre[blk]);
-            if (sb > 0) wait_flags(flag_pre, nb, &header[1]);
-        }
+        block_publish(&flag_pre[blk]);
+        if (wave == 0 && sb > 0) wait_flags(flag_pre, nb, &header[1]);
         __syncthreads();
     }
     // 2c. P_s into LDS (zero for the first block)
@@ -707,6 +702,7 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
                               int64_t N, float *ws, hipStream_t s) {
     if (causal) {
         const FusedPlan p = make_fused_plan(BH, N, D, M);
+        if (fused_slice_rows(p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows) return hipErrorInvalidValue;
         char *base = reinterpret_cast<char *>(ws);
         int *header = reinterpret_cast<int *>(base);
         int *flags = reinterpret_cast<int *>(base + p.flags_off);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace la {
 
 // Tokens per chunk: the unit of the intra-chunk masked product on the
@@ -81,6 +83,23 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     p.recs_off = p.flags_off + align256(size_t(2 * BH * p.nblk) * sizeof(int));
     p.total = p.recs_off + align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float));
     return p;
+}
+
+// Rows of block totals one thread sums while forming its slice of the
+// prefixes (the kernel keeps at most kFusedSliceRows in registers): block sb
+// of nb owns ncol = its share of the rec4 float4 columns; nthreads threads
+// cover ncol columns x G row groups.
+constexpr int kFusedSliceRows = 4;
+inline int64_t fused_slice_rows(int64_t nb, int64_t rec4, int64_t nthreads) {
+    int64_t worst = 0;
+    const int64_t nr = nb - 1, per = ceil_div(rec4, nb);
+    for (int64_t sb = 0; sb < nb && nr > 0; ++sb) {
+        const int64_t c0 = std::min(rec4, sb * per), ncol = std::min(rec4, c0 + per) - c0;
+        if (ncol <= 0) continue;
+        const int64_t G = std::max<int64_t>(1, std::min(nr, nthreads / ncol));
+        worst = std::max(worst, ceil_div(nr, G));
+    }
+    return worst;
 }
 
 inline size_t causal_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
