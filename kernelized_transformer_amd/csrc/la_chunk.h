@@ -214,10 +214,13 @@ __device__ __forceinline__ void transpose_frags(bf16x4 (&yt)[TT][NF], const bf16
 // A state record is D*M floats of S (row-major [d][m]) followed by D floats
 // of Z.  In registers the state is an augmented D x (M + 16) matrix of Acc
 // tiles St[dt][mt], dt < D/16, mt <= M/16: tile mt = M/16 holds Z in its
-// column 0 and zeros elsewhere, so the products that use S also produce the
-// normalizer.  Lane (c, g) element r of St[dt][mt] is row d = 16 dt + 4g + r,
+// column 0 and zeros elsewhere (or Z in every column, see state_load), so
+// the products that use S also produce the normalizer.  Lane (c, g) element r of St[dt][mt] is row d = 16 dt + 4g + r,
 // column m = 16 mt + c.
-template <int D, int M>
+// With REP the normalizer tile holds Z in every column instead of column 0
+// (the layout the forward kernels use: their normalizer rows come out
+// replicated, so each lane holds its tokens' denominators).
+template <int D, int M, bool REP = false>
 __device__ __forceinline__ void state_load(f32x4 (&St)[D / 16][M / 16 + 1], const float *__restrict__ rec) {
     const int c = lane_id() & 15, g = lane_id() >> 4;
 #pragma unroll
@@ -227,7 +230,7 @@ __device__ __forceinline__ void state_load(f32x4 (&St)[D / 16][M / 16 + 1], cons
 #pragma unroll
             for (int r = 0; r < 4; ++r) St[dt][mt][r] = rec[(16 * dt + 4 * g + r) * M + 16 * mt + c];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) St[dt][M / 16][r] = (c == 0) ? rec[D * M + 16 * dt + 4 * g + r] : 0.f;
+        for (int r = 0; r < 4; ++r) St[dt][M / 16][r] = (REP || c == 0) ? rec[D * M + 16 * dt + 4 * g + r] : 0.f;
     }
 }
 
@@ -274,11 +277,11 @@ __device__ __forceinline__ void state_store(float *__restrict__ rec, const f32x4
 // St += sum over the chunk's tokens of A_t B_t^T, where KT/VT are
 // token-contiguous fragments (KT: rows = the D features of A; VT: rows = the
 // M features of B).  The extra column block adds sum_t A_t to the
-// normalizer column.
-template <typename Fr, int D, int M, int TT>
+// normalizer column (to every column of that block with REP).
+template <typename Fr, int D, int M, int TT, bool REP = false>
 __device__ __forceinline__ void state_accumulate(f32x4 (&St)[D / 16][M / 16 + 1], const Fr (&KT)[TT][D / 16],
                                                  const Fr (&VT)[TT][M / 16]) {
-    const Fr ones = frag_row0_ones<Fr>();
+    const Fr ones = REP ? frag_ones<Fr>() : frag_row0_ones<Fr>();
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll

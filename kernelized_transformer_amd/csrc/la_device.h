@@ -42,9 +42,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (positive).
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-// phi'(x): 1 for x > 0, exp(x) otherwise.
-__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
+// Evaluated as max(exp(-|x|), x + 1) -- for x <= 0, exp(x) >= x + 1; for
+// x > 0, exp(-x) < 1 < x + 1 -- which costs one exponential and no select.
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float phi(float x) {
+    return __builtin_fmaxf(__builtin_amdgcn_exp2f(-__builtin_fabsf(x * kLog2e)), x + 1.f);
+}
+// phi'(x): 1 for x > 0, exp(x) otherwise, i.e. min(exp(x), 1).
+__device__ __forceinline__ float dphi(float x) { return __builtin_fminf(__builtin_amdgcn_exp2f(x * kLog2e), 1.f); }
 
 // ---- element type traits ------------------------------------------------
 template <typename T> struct IO;
@@ -109,6 +114,11 @@ template <typename F> __device__ __forceinline__ F frag_row0_ones() {
     const float o = ((lane_id() & 15) == 0) ? 1.f : 0.f;
     return frag_from<F>(f32x4{o, o, o, o});
 }
+
+// Frag of all ones: as an A operand every output row is the sum of the B
+// operand over the contraction; as a B operand every output column is the
+// sum of the A operand (the normalizer replicated across the tile).
+template <typename F> __device__ __forceinline__ F frag_ones() { return frag_from<F>(f32x4{1.f, 1.f, 1.f, 1.f}); }
 
 // 16x16 identity as a Frag: lane (c, g) element r is [4g + r == c].
 template <typename F> __device__ __forceinline__ F frag_identity() {

@@ -71,7 +71,7 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
             Fr KT[TT][D / 16], VT[TT][M / 16];
             transpose_frags<D / 16, TT>(KT, Kn, stage_k);
             transpose_frags<M / 16, TT>(VT, Vn, stage_v);
-            state_accumulate<Fr, D, M, TT>(St, KT, VT);
+            state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
     }
 }
@@ -93,7 +93,7 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
     typedef typename IO<T>::vec4 V4;
     constexpr int DT = D / 16, MT = M / 16;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-    const Fr ones = frag_row0_ones<Fr>();
+    const Fr ones = frag_ones<Fr>();
     const Fr zero = frag_zero<Fr>();
 
     V4 rq[PF][TT][DT], rk[PF][TT][DT], rv[PF][TT][MT];
@@ -166,7 +166,7 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
             Fr KT[TT][DT], VT[TT][MT];
             transpose_frags<DT, TT>(KT, Kn, stage_k);
             transpose_frags<MT, TT>(VT, Vn, stage_v);
-            // intra-chunk term; the ones row block sums P^T into den
+            // intra-chunk term; the ones block sums P^T into den (every row)
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt)
 #pragma unroll
@@ -179,14 +179,14 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
                     }
                     mma_tiles<Fr, TT>(Ot[mt][it], a, b);
                 }
-            state_accumulate<Fr, D, M, TT>(St, KT, VT);
+            state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
 
-        // normalize and store: den_i sits in row 0 of the normalizer block,
-        // i.e. element 0 of lane c (g = 0)
+        // normalize and store: every row of the normalizer block holds den,
+        // so element 0 of lane (c, g) is the denominator of token c
 #pragma unroll
         for (int it = 0; it < TT; ++it) {
-            const float den = __shfl(Ot[MT][it][0], c);
+            const float den = Ot[MT][it][0];
             const float inv = __builtin_amdgcn_rcpf(den);
             const int64_t t = t0 + 16 * it + c;
             if (t < t_end) {
@@ -227,7 +227,7 @@ __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, c
             bf16x4 KT[TT][D / 16], VT[TT][M / 16];
             transposed_frags_lds<D, TT>(KT, sk);
             transposed_frags_lds<M, TT>(VT, sv);
-            state_accumulate<bf16x4, D, M, TT>(St, KT, VT);
+            state_accumulate<bf16x4, D, M, TT, true>(St, KT, VT);
         }
     }
 }
@@ -241,7 +241,7 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
     constexpr int DT = D / 16, MT = M / 16;
     constexpr int NQ = Lines<D, TT>::n, NV = Lines<M, TT>::n;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-    const Fr ones = frag_row0_ones<Fr>();
+    const Fr ones = frag_ones<Fr>();
     const Fr zero = frag_zero<Fr>();
 
     dwordx4 rq[PF][NQ], rk[PF][NQ], rv[PF][NV];
@@ -316,7 +316,7 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
                     }
                     PT[jt][it] = IO<bf16>::to_frag(p);
                 }
-            // intra-chunk term; the ones row block sums P^T into den
+            // intra-chunk term; the ones block sums P^T into den (every row)
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt)
 #pragma unroll
@@ -329,14 +329,14 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
                     }
                     mma_tiles<Fr, TT>(Ot[mt][it], a, b);
                 }
-            state_accumulate<Fr, D, M, TT>(St, KT, VT);
+            state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
 
-        // normalize and store: den_i sits in row 0 of the normalizer block,
-        // i.e. element 0 of lane c (g = 0)
+        // normalize and store: every row of the normalizer block holds den,
+        // so element 0 of lane (c, g) is the denominator of token c
 #pragma unroll
         for (int it = 0; it < TT; ++it) {
-            const float den = __shfl(Ot[MT][it][0], c);
+            const float den = Ot[MT][it][0];
             const float inv = __builtin_amdgcn_rcpf(den);
             const int64_t t = t0 + 16 * it + c;
             if (t < t_end) {
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(64) void k_segment_output(const T *__restrict__ q, 
     lds_bf16 *sk = sq + stage_elems<D / 16, TT>();
     lds_bf16 *sv = sk + stage_elems<D / 16, TT>();
     f32x4 St[D / 16][M / 16 + 1];
-    state_load<D, M>(St, ws + (bh * nseg + (CAUSAL ? seg : 0)) * rec);
+    state_load<D, M, true>(St, ws + (bh * nseg + (CAUSAL ? seg : 0)) * rec);
     if constexpr (sizeof(T) == 2)
         seg_output_bf16<D, M, CAUSAL, kPrefetch>(q + bh * N * D, k + bh * N * D, v + bh * N * M, out + bh * N * M,
                                                  t_begin, t_end, St, sq, sk, sv);
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
                     const int d = 16 * dt + 4 * g + r;
                     const bool z = mt == M / 16;
                     const int e = z ? D * M + d : d * M + 16 * mt + c;
-                    St[dt][mt][r] = (!z || c == 0) ? pbuf[e] + (wave > 0 ? slot(wave)[e] : 0.f) : 0.f;
+                    St[dt][mt][r] = pbuf[e] + (wave > 0 ? slot(wave)[e] : 0.f);
                 }
             }
         }
