@@ -48,11 +48,84 @@ def _args():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--only", choices=["all", "forward", "decode", "backward"], default="all",
                     help="restrict the timed work (for profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device to device three times (a plain copy kernel of known size, "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters of a profiling run)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter CSVs of two profiling runs made with --copy-calibration "
+                         "into per-launch HBM bytes of the causal forward kernel, and print them")
     return ap.parse_args()
+
+
+# Sources of the causal forward kernel: a stored traffic figure is used only
+# while these are unchanged.
+KERNEL_SOURCES = ["kernelized_transformer_amd/csrc/" + f for f in
+                  ("la_forward.hip", "la_chunk.h", "la_device.h", "la_internal.h")]
+TRAFFIC_FILE = "profiles/forward_causal_B1H8N65536_D64M64_bf16.md"
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """Per-launch HBM bytes of k_fwd_fused from the committed counter summary,
+    or None when the kernel sources have changed since it was taken."""
+    try:
+        text = open(os.path.join(ROOT, TRAFFIC_FILE)).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:") or line.startswith("source_sha256:"):
+            k_, v_ = line.split(":", 1)
+            vals[k_.strip()] = v_.strip().strip("`")
+    if vals.get("source_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int = 1024) -> dict:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel, each
+    scaled by bytes / counter of the plain copy kernel in the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    res = {}
+    for name, path, counter in (("read", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = per_kernel(path, counter)
+        copy = [v for k_, vs in rows.items() if "copy" in k_.lower() for v in vs]
+        fused = [v for k_, vs in rows.items() if "k_fwd_fused" in k_ for v in vs]
+        copy_bytes = copy_mib * 2 ** 20
+        big = [v for v in copy if v > 0.25 * copy_bytes]      # the calibration copies, not small copies
+        factor = copy_bytes / (sum(big) / len(big))
+        res[name] = dict(counter_bytes=sum(fused) / len(fused), copy_counter_bytes=sum(big) / len(big),
+                         factor=factor, bytes=sum(fused) / len(fused) * factor)
+    res["traffic_bytes_per_launch"] = int(round(res["read"]["bytes"] + res["write"]["bytes"]))
+    res["source_sha256"] = kernel_sources_sha256()
+    return res
 
 
 def main():
     a = _args()
+    if a.traffic_from:
+        print(json.dumps(traffic_from(*a.traffic_from, copy_mib=a.copy_calibration or 1024), indent=1))
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build targets one GPU; the path shards by (batch, head) with no communication, "
               "but only --gpus 1 is measured.", file=sys.stderr)
@@ -76,6 +149,16 @@ def main():
 
     def log(*m):
         print("[bench]", *m, file=sys.stderr, flush=True)
+
+    if a.copy_calibration:
+        src = torch.empty(a.copy_calibration * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration: copied {a.copy_calibration} MiB three times")
 
     def time_events(fn, iters):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -259,8 +342,9 @@ def main():
     if f:
         ach = fwd_bytes / (f["ms_per_step"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "la_forward_causal (k_segment_state + k_state_scan + k_segment_output)",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
+                "kernel": "k_fwd_fused (one launch per la_forward_causal call; the timed call also launches "
+                          "the small k_fused_reset that clears the hand-off flags)",
                 "algorithmic_bytes_per_launch": fwd_bytes}
     line = {
         "metric": "causal lin-attn fwd tokens·heads/s (N=65536,D=M=64); decode steps/s",
@@ -269,7 +353,8 @@ def main():
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": f["ms_per_step"] if f else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 I/O, fp32 state/accumulate",
+        "dtype": "bf16",
+        "accumulate": "fp32",
         "data": "synthetic (seeded N(0,1) Q, K, V; no dataset or weights)",
         "config": {"workload": "causal forward B1 H8 N65536 D=M=64 bf16", "B": w4.B, "H": w4.H, "N": w4.N,
                    "D": w4.D, "M": w4.M},

@@ -30,7 +30,9 @@
  *   - Argument errors are reported before anything is launched and leave all
  *     buffers untouched.  LA_ERR_HIP reports a failed launch.  Non-finite
  *     inputs are not errors; they propagate to the outputs.
- *   - The library keeps no global state; calls on different streams are
+ *   - The library keeps no global state beyond a process-wide call counter
+ *     (it tags the causal forward's cross-workgroup flags, so the workspace
+ *     needs no clearing between calls); calls on different streams are
  *     independent as long as their buffers (workspace included) are
  *     disjoint.
  */
@@ -68,6 +70,13 @@ typedef enum { LA_OP_FWD_CAUSAL = 0, LA_OP_FWD_NONCAUSAL = 1, LA_OP_BWD_CAUSAL =
  * independently for each (b, h).  Token i sees itself (j <= i).
  * q, k: [B][H][N][D]; v: [B][H][N][M] (inputs, read only).
  * out: [B][H][N][M] (output, fully written).
+ * The workgroups of one (b, h) exchange state through the workspace and
+ * wait for each other (each wait is bounded), so they must be able to run
+ * at the same time: at most 64 workgroups per (b, h), about 256 in all.
+ * Diagnostic: if a wait ever timed out (only possible when other work keeps
+ * most of the GPU busy), the call or-s 1 into the 32-bit word at byte 4 of
+ * the workspace and its output is wrong; the library never clears that
+ * word, so a caller who wants the diagnostic zeroes it first.
  */
 la_status_t la_forward_causal(const void *q, const void *k, const void *v, void *out,
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,

@@ -25,6 +25,9 @@
 //     at the kernel);
 //   non-causal (three launches): per-segment states, their sum per (b, h),
 //     then the readout.
+#include <atomic>
+#include <chrono>
+
 #include "la_chunk.h"
 #include "la_internal.h"
 
@@ -458,8 +461,7 @@ hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mod
 // ---- fused causal forward ---------------------------------------------------
 //
 // Workgroup = kFusedWaves wavefronts = one block of consecutive sub-segments
-// of one (b, h).  Blocks take tickets in launch order from a counter, so a
-// block only ever waits on blocks that are already running.
+// of one (b, h); workgroup i is block i % nb of head i / nb.
 //   1. each wavefront sums phi(K) [V, 1]^T over its sub-segment (fp32);
 //   2. hand-off between the nb blocks of a head, through the workspace:
 //      a. block s publishes its total A_s = A_w0 + A_w1 + ... (the last block
@@ -502,26 +504,28 @@ __device__ __forceinline__ f32x4 dev_load(const f32x4 *p) {
     return f32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Flags are 64-bit words: a flag is set for this call when it holds the
+// call's tag, a value the host draws fresh for every call (never 0), so the
+// flags need no clearing between calls and stale or uninitialized words do
+// not read as set.
+
 // Whole workgroup: every thread's earlier stores complete, then one thread
-// sets *flag.
-__device__ __forceinline__ void block_publish(int *flag) {
+// stores the tag into *flag.
+__device__ __forceinline__ void block_publish(unsigned long long *flag, unsigned long long tag) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the compiler keeps the stores above
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                  // the hardware completes them
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void k_fused_reset(int *__restrict__ words, int64_t n) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < n) words[i] = 0;
-}
-
-// Wavefront-wide wait until flags[0 .. count) are all set (count <= 64).
-__device__ __forceinline__ void wait_flags(const int *flags, int count, int *err) {
+// Wavefront-wide wait until flags[0 .. count) all hold tag (count <= 64).
+__device__ __forceinline__ void wait_flags(const unsigned long long *flags, int count, unsigned long long tag,
+                                           int *err) {
     const int lane = lane_id();
     for (int iter = 0;; ++iter) {
-        const int f = (lane < count) ? __hip_atomic_load(&flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
-        if (__ballot(f == 0) == 0) break;
+        const bool set = (lane >= count) ||
+                         __hip_atomic_load(&flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        if (__ballot(!set) == 0) break;
         if (iter >= kSpinLimit) {
             if (lane == 0) atomicOr(err, 1);   // gave up: results are wrong, the error word says so
             break;
@@ -534,7 +538,9 @@ __device__ __forceinline__ void wait_flags(const int *flags, int count, int *err
 template <typename T, int D, int M>
 __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd_fused(const T *__restrict__ q, const T *__restrict__ k,
                                                                 const T *__restrict__ v, T *__restrict__ out,
-                                                                int *__restrict__ header, int *__restrict__ flags,
+                                                                int *__restrict__ header,
+                                                                unsigned long long *__restrict__ flags,
+                                                                unsigned long long tag,
                                                                 float *__restrict__ recs, int64_t N, int64_t nblk,
                                                                 int64_t sub_tokens) {
     constexpr int REC = D * M + D, REC4 = REC / 4;
@@ -554,22 +560,18 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     f32x4 *slot4 = reinterpret_cast<f32x4 *>(lds_raw);
     auto slot = [&](int w) { return reinterpret_cast<float *>(slot4 + w * SLOT4); };
     float *pbuf = slot(0);
-    __shared__ int lds_ticket;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
 
-    if (tid == 0) lds_ticket = atomicAdd(&header[0], 1);
-    __syncthreads();
-    const int64_t ticket = __builtin_amdgcn_readfirstlane(lds_ticket);
-    const int64_t bh = ticket / nblk, blk = ticket % nblk;
+    const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     const int nb = int(nblk), sb = int(blk);
     const int64_t t_begin = min(N, (blk * kFusedWaves + wave) * sub_tokens);
     const int64_t t_end = min(N, t_begin + sub_tokens);
     const T *Q = q + bh * N * D;
     const T *K = k + bh * N * D;
     const T *V = v + bh * N * M;
-    int *flag_tot = flags + bh * 2 * nblk;   // [nblk]: total published
-    int *flag_pre = flag_tot + nblk;         // [nblk]: prefix slice published
+    unsigned long long *flag_tot = flags + bh * 2 * nblk;   // [nblk]: total published
+    unsigned long long *flag_pre = flag_tot + nblk;         // [nblk]: prefix slice published
     float *head_recs = recs + bh * nblk * 2 * REC;   // per block: total, exclusive prefix
 
     // 1. local totals
@@ -608,9 +610,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int j = 0; j < (REC4 + NT - 1) / NT; ++j)
             if (tid + NT * j < REC4) dev_store(dst + tid + NT * j, slot4[tid + NT * j]);
-        block_publish(&flag_tot[blk]);
+        block_publish(&flag_tot[blk], tag);
     }
-    if (wave == 0 && nb > 1) wait_flags(flag_tot, nb - 1, &header[1]);
+    if (wave == 0 && nb > 1) wait_flags(flag_tot, nb - 1, tag, &header[1]);
     __syncthreads();
 
     if (nb > 1) {
@@ -651,8 +653,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
             }
             __syncthreads();
         }
-        block_publish(&flag_pre[blk]);
-        if (wave == 0 && sb > 0) wait_flags(flag_pre, nb, &header[1]);
+        block_publish(&flag_pre[blk], tag);
+        if (wave == 0 && sb > 0) wait_flags(flag_pre, nb, tag, &header[1]);
         __syncthreads();
     }
     // 2c. P_s into LDS (zero for the first block)
@@ -697,6 +699,17 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
 }
 
 // ---- host side ---------------------------------------------------------------
+uint64_t next_call_tag() {
+    static const uint64_t seed =
+        uint64_t(std::chrono::steady_clock::now().time_since_epoch().count()) ^ uint64_t(uintptr_t(&seed));
+    static std::atomic<uint64_t> count{0};
+    uint64_t z = seed + 0x9E3779B97F4A7C15ull * (count.fetch_add(1, std::memory_order_relaxed) + 1);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;   // splitmix64 finalizer: a bijection
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z ? z : 1;
+}
+
 template <typename T, int D, int M>
 static hipError_t run_forward(bool causal, const void *q, const void *k, const void *v, void *out, int64_t BH,
                               int64_t N, float *ws, hipStream_t s) {
@@ -705,15 +718,11 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
         if (fused_slice_rows(p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows) return hipErrorInvalidValue;
         char *base = reinterpret_cast<char *>(ws);
         int *header = reinterpret_cast<int *>(base);
-        int *flags = reinterpret_cast<int *>(base + p.flags_off);
+        unsigned long long *flags = reinterpret_cast<unsigned long long *>(base + p.flags_off);
         float *recs = reinterpret_cast<float *>(base + p.recs_off);
-        const int64_t nreset = int64_t(p.flags_off / sizeof(int)) + 2 * BH * p.nblk;   // header + flags
-        hipLaunchKernelGGL(k_fused_reset, dim3(unsigned((nreset + 255) / 256)), dim3(256), 0, s, header, nreset);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         hipLaunchKernelGGL((k_fwd_fused<T, D, M>), dim3(unsigned(BH * p.nblk)), dim3(64 * kFusedWaves), 0, s,
-                           (const T *)q, (const T *)k, (const T *)v, (T *)out, header, flags, recs, N, p.nblk,
-                           p.sub_tokens);
+                           (const T *)q, (const T *)k, (const T *)v, (T *)out, header, flags, next_call_tag(), recs,
+                           N, p.nblk, p.sub_tokens);
         return hipGetLastError();
     }
     const SegPlan p = make_plan(BH, N, D, M);

@@ -63,8 +63,8 @@ struct FusedPlan {
     int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
     int64_t nblk = 0;        // blocks per (b, h)
     int64_t rec = 0;         // floats per state record
-    size_t flags_off = 0;    // int flags [BH][2][nblk]: total published, prefix slice published
-                             // (after a 256-byte header: ticket counter, error word)
+    size_t flags_off = 0;    // 64-bit flags [BH][2][nblk]: total published, prefix slice published
+                             // (after a 256-byte header; int word 1 is the error word)
     size_t recs_off = 0;     // float records [BH][nblk][2][rec]: block total, exclusive prefix
     size_t total = 0;
 };
@@ -80,7 +80,7 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
     p.rec = D * M + D;
     p.flags_off = 256;
-    p.recs_off = p.flags_off + align256(size_t(2 * BH * p.nblk) * sizeof(int));
+    p.recs_off = p.flags_off + align256(size_t(2 * BH * p.nblk) * sizeof(unsigned long long));
     p.total = p.recs_off + align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float));
     return p;
 }
@@ -101,6 +101,11 @@ inline int64_t fused_slice_rows(int64_t nb, int64_t rec4, int64_t nthreads) {
     }
     return worst;
 }
+
+// A fresh nonzero 64-bit value per call (process-wide counter through a
+// bijective mixer, seeded once per process): the causal forward's hand-off
+// flags count as set only when they hold the current call's tag.
+uint64_t next_call_tag();
 
 inline size_t causal_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
     return make_fused_plan(BH, N, D, M).total;

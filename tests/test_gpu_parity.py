@@ -190,17 +190,39 @@ def test_forward_deterministic_and_guarded():
 
 
 def test_fused_forward_error_word_clear():
-    """The causal forward's cross-block hand-off reports a timed-out wait in
-    word 1 of the workspace; it must stay clear."""
+    """The causal forward's cross-workgroup waits report a time-out by or-ing
+    1 into word 1 of the workspace; after a normal call it stays clear."""
     w = _wl(171, 1, 4, 100000, 64, 64, "bf16")
     q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
     _say("fused forward error word")
     n = la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.D, w.M, torch.bfloat16)
-    ws = torch.full((n,), 0x55, dtype=torch.uint8, device="cuda")   # garbage before the call
+    ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
     la.la_forward_causal(q, k, v, workspace=ws)
     torch.cuda.synchronize()
     words = ws[:8].view(torch.int32).cpu().tolist()
     assert words[1] == 0, words
+
+
+def test_fused_forward_workspace_needs_no_clearing():
+    """Garbage in the workspace (including words left by an earlier call with
+    another shape, or a backward call) never reads as a published flag:
+    results are bit-identical to those with a fresh zeroed workspace."""
+    w = _wl(172, 1, 8, 20000, 64, 64, "bf16")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("fused forward garbage workspace")
+    n = la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.D, w.M, torch.bfloat16)
+    ref = la.la_forward_causal(q, k, v, workspace=torch.zeros((n,), dtype=torch.uint8, device="cuda"))
+    ws = torch.full((n,), 0x55, dtype=torch.uint8, device="cuda")
+    out1 = la.la_forward_causal(q, k, v, workspace=ws)              # garbage flags
+    out2 = la.la_forward_causal(q, k, v, workspace=ws)              # flags of the previous call
+    w2 = _wl(173, 1, 2, 30000, 64, 64, "bf16")                      # another plan in the same bytes
+    q2, k2, v2 = (dev(x, w2.dtype) for x in wl.forward_inputs(w2))
+    la.la_forward_causal(q2, k2, v2, workspace=ws[:la.la_workspace_size(la.LA_OP_FWD_CAUSAL, 1, 2, 30000, 64, 64,
+                                                                           torch.bfloat16)])
+    out3 = la.la_forward_causal(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    for o in (out1, out2, out3):
+        assert torch.equal(o, ref)
 
 
 def test_segment_plan_independence():
