@@ -32,6 +32,11 @@ namespace la {
 
 constexpr int BTT = 1;  // token tiles per chunk in the backward kernels
 constexpr int BCH = 16 * BTT;
+// LDS per wavefront: the chunk transposes, or the state's (M + 16) x D transpose
+template <int D, int M>
+constexpr int kBwdStage = (stage_elems<D / 16, BTT>() + stage_elems<M / 16 + 1, BTT>() > stage_elems<D / 16, M / 16 + 1>())
+                              ? stage_elems<D / 16, BTT>() + stage_elems<M / 16 + 1, BTT>()
+                              : stage_elems<D / 16, M / 16 + 1>();
 
 // ---- pass 2: forward direction --------------------------------------------
 template <typename T, int D, int M>
@@ -58,15 +63,13 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 
     const float *srec = wsS + (bh * nseg + seg) * rec;
     f32x4 St[DT][MT + 1];      // S_aug, rows d
-    f32x4 StT[MT + 1][DT];     // S_aug^T, rows m'
     f32x4 Ra[DT][MT + 1];      // this segment's sum_i qh_i gh_i^T, rows d
     state_load<D, M>(St, srec);
-    stateT_load<D, M>(StT, srec);
     state_zero<D, M>(Ra);
 
     const Fr ones = frag_row0_ones<Fr>();
     const Fr k0ones = frag_k0_ones<Fr>();
-    __shared__ bf16 stage_mem[stage_elems<DT, BTT>() + stage_elems<MT + 1, BTT>()];
+    __shared__ bf16 stage_mem[kBwdStage<D, M>];
     lds_bf16 *stage = (lds_bf16 *)(stage_mem);
 
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
@@ -91,6 +94,16 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         const int64_t t = t0 + c;   // this lane's query token
         const bool valid = t < t_end;
 
+        // S_aug as operand tiles in both orientations: SF[mt][dt] (rows m',
+        // contraction d) is the accumulator tile itself, SFT[mt][dt] (rows d,
+        // contraction m') its transpose through LDS
+        Fr SF[MT + 1][DT], SFT[MT + 1][DT];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = IO<T>::to_frag(St[dt][mt]);
+        transpose_frags<DT, MT + 1>(SFT, SF, stage);
+
         Fr KT[BTT][DT], VT[BTT][MT];
         transpose_frags<DT, BTT>(KT, Kn, stage);
         transpose_frags<MT, BTT>(VT, Vn, stage + stage_elems<DT, BTT>());
@@ -107,8 +120,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         for (int mt = 0; mt <= MT; ++mt) {
             Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < DT; dt += 2)
-                mma2(Ot[mt], IO<T>::to_frag(St[dt][mt]), IO<T>::to_frag(St[dt + 1][mt]), Qn[0][dt], Qn[0][dt + 1]);
+            for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt], SF[mt][dt], SF[mt][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
             mma1(Ot[mt], mt < MT ? VT[0][mt] : ones, PT);
         }
         const float den = __shfl(Ot[MT][0], c);
@@ -154,9 +166,8 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma1(acc, KT[0][dt], dAT);
 #pragma unroll
-            for (int mt = 0; mt + 1 <= MT; mt += 2)
-                mma2(acc, IO<T>::to_frag(StT[mt][dt]), IO<T>::to_frag(StT[mt + 1][dt]), Gn[0][mt], Gn[0][mt + 1]);
-            if ((MT & 1) == 0) mma1(acc, IO<T>::to_frag(StT[MT][dt]), Gn[0][MT]);
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, SFT[mt][dt], SFT[mt + 1][dt], Gn[0][mt], Gn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, SFT[MT][dt], Gn[0][MT]);
             if (valid) store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(acc * dphi4(qraw[dt])));
         }
 
@@ -169,12 +180,8 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt) mma1(Ra[dt][mt], QT[0][dt], GT[0][mt]);
 
-        // carry S_aug (both layouts) past this chunk
+        // carry S_aug past this chunk
         state_accumulate<Fr, D, M, BTT>(St, KT, VT);
-#pragma unroll
-        for (int mt = 0; mt <= MT; ++mt)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) mma1(StT[mt][dt], mt < MT ? VT[0][mt] : ones, KT[0][dt]);
     }
     state_store<D, M>(wsR + (bh * nseg + seg) * rec, Ra);
 }
@@ -202,13 +209,11 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     T *DV = dv + bh * N * M;
 
     const float *rrec = wsR + (bh * nseg + seg) * rec;
-    f32x4 Rr[DT][MT + 1];      // R_aug, rows d (the u block is not used)
-    f32x4 RT[MT + 1][DT];      // R_aug^T, rows m'
+    f32x4 Rr[DT][MT + 1];      // R_aug = [R | u], rows d
     state_load<D, M>(Rr, rrec);
-    stateT_load<D, M>(RT, rrec);
 
     const Fr k0ones = frag_k0_ones<Fr>();
-    __shared__ bf16 stage_mem[stage_elems<DT, BTT>() + stage_elems<MT + 1, BTT>()];
+    __shared__ bf16 stage_mem[kBwdStage<D, M>];
     lds_bf16 *stage = (lds_bf16 *)(stage_mem);
 
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
@@ -246,6 +251,14 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
         const int64_t t = t0 + c;   // this lane's key token
         const bool valid = t < t_end;
 
+        // R_aug as operand tiles in both orientations (see the forward-direction pass)
+        Fr RF[MT + 1][DT], RFT[MT + 1][DT];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) RF[mt][dt] = IO<T>::to_frag(Rr[dt][mt]);
+        transpose_frags<DT, MT + 1>(RFT, RF, stage);
+
         Fr QT[BTT][DT], GT[BTT][MT + 1];
         transpose_frags<DT, BTT>(QT, Qn, stage);
         transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
@@ -271,9 +284,8 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma1(acc, QT[0][dt], dAf);
 #pragma unroll
-            for (int mt = 0; mt + 1 <= MT; mt += 2)
-                mma2(acc, IO<T>::to_frag(RT[mt][dt]), IO<T>::to_frag(RT[mt + 1][dt]), Vn[0][mt], Vn[0][mt + 1]);
-            if ((MT & 1) == 0) mma1(acc, IO<T>::to_frag(RT[MT][dt]), Vn[0][MT]);
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, RFT[mt][dt], RFT[mt + 1][dt], Vn[0][mt], Vn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, RFT[MT][dt], Vn[0][MT]);
             if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(acc * dphi4(kraw[dt])));
         }
         // dV^T[m][j] = sum_i g[i][m] P[i][j] + sum_d R[d][m] kh[j][d]
@@ -282,20 +294,15 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma1(acc, GT[0][mt], Pf);
 #pragma unroll
-            for (int dt = 0; dt < DT; dt += 2)
-                mma2(acc, IO<T>::to_frag(Rr[dt][mt]), IO<T>::to_frag(Rr[dt + 1][mt]), Kn[0][dt], Kn[0][dt + 1]);
+            for (int dt = 0; dt < DT; dt += 2) mma2(acc, RF[mt][dt], RF[mt][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
             if (valid) store4<T>(DV + t * M + 16 * mt + 4 * g, IO<T>::from_f32(acc));
         }
 
-        // carry R_aug (both layouts) past this chunk, towards earlier tokens
-#pragma unroll
-        for (int mt = 0; mt <= MT; ++mt)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) mma1(RT[mt][dt], GT[0][mt], QT[0][dt]);
+        // carry R_aug past this chunk, towards earlier tokens
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) mma1(Rr[dt][mt], QT[0][dt], GT[0][mt]);
+            for (int mt = 0; mt <= MT; ++mt) mma1(Rr[dt][mt], QT[0][dt], GT[0][mt]);
     }
 }
 
