@@ -396,64 +396,71 @@ __global__ __launch_bounds__(64) void k_segment_output(const T *__restrict__ q, 
 }
 
 // ---- scan over segments ---------------------------------------------------
-// Block = 64 record elements x 4 segment quarters (256 threads).  Each thread
-// keeps its quarter's values in registers, the quarters' totals are combined
-// in LDS, then the prefixes are written back.
-constexpr int kScanQ = 4;
-constexpr int kScanPerQ = int(kMaxSegPerHead / kScanQ);
+// Block = kScanCols float4 columns of the records x kScanG groups of
+// consecutive segments (256 threads).  Each thread loads its group's values
+// (all loads in flight at once: rows past the end read a valid record and are
+// zeroed), sums them, the group sums are combined in LDS in group order, and
+// the prefixes are written back.  The summation order depends only on nseg.
+constexpr int kScanG = 8;
+constexpr int kScanCols = 32;
+constexpr int kScanRows = int(kMaxSegPerHead / kScanG);
 
 __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int64_t nseg, int64_t rec, int mode,
                                                     const float *__restrict__ init, float *__restrict__ fin) {
     // mode 0: exclusive prefix in place; 1: total into record 0 (non-causal);
     // 2: exclusive suffix in place (scan from the last segment backwards).
-    __shared__ float part[kScanQ][64];
-    const int e_local = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int64_t nblk_e = (rec + 63) / 64;
-    const int64_t bh = blockIdx.x / nblk_e;
-    const int64_t e = (blockIdx.x % nblk_e) * 64 + e_local;
-    const bool ok = e < rec;
+    __shared__ f32x4 part[kScanG][kScanCols];
+    const int cl = threadIdx.x % kScanCols, grp = threadIdx.x / kScanCols;
+    const int64_t rec4 = rec / 4;
+    const int64_t nblk_c = (rec4 + kScanCols - 1) / kScanCols;
+    const int64_t bh = blockIdx.x / nblk_c;
+    const int64_t c4 = (blockIdx.x % nblk_c) * kScanCols + cl;
+    const bool ok = c4 < rec4;
     const bool rev = mode == 2;
-    const int64_t per_q = (nseg + kScanQ - 1) / kScanQ;
-    const int64_t s0 = q * per_q;   // position in scan order
-    float *base = ws + bh * nseg * rec + e;
+    const int64_t per = (nseg + kScanG - 1) / kScanG;
+    const int64_t s0 = grp * per;   // position in scan order
+    f32x4 *base = reinterpret_cast<f32x4 *>(ws + bh * nseg * rec) + (ok ? c4 : 0);
 
-    float x[kScanPerQ];
-    float sum = 0.f;
+    f32x4 x[kScanRows];
 #pragma unroll
-    for (int j = 0; j < kScanPerQ; ++j) {
-        const int64_t s = s0 + j;
-        const int64_t seg = rev ? nseg - 1 - s : s;
-        x[j] = (ok && j < per_q && s < nseg) ? base[seg * rec] : 0.f;
+    for (int j = 0; j < kScanRows; ++j) {
+        const int64_t s = min(s0 + j, nseg - 1);
+        x[j] = base[(rev ? nseg - 1 - s : s) * rec4];
+    }
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kScanRows; ++j) {
+        if (!(j < per && s0 + j < nseg)) x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         sum += x[j];
     }
-    part[q][e_local] = sum;
+    part[grp][cl] = sum;
     __syncthreads();
-    float run = (ok && init) ? init[bh * rec + e] : 0.f;
-    float total = run;
-    for (int p = 0; p < kScanQ; ++p) {
-        if (p < q) run += part[p][e_local];
-        total += part[p][e_local];
+    f32x4 run = (ok && init) ? reinterpret_cast<const f32x4 *>(init + bh * rec)[c4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 total = run;
+    for (int p = 0; p < kScanG; ++p) {
+        if (p < grp) run += part[p][cl];
+        total += part[p][cl];
     }
     if (!ok) return;
     if (mode != 1) {
 #pragma unroll
-        for (int j = 0; j < kScanPerQ; ++j) {
+        for (int j = 0; j < kScanRows; ++j) {
             const int64_t s = s0 + j;
-            const int64_t seg = rev ? nseg - 1 - s : s;
-            if (j < per_q && s < nseg) {
-                base[seg * rec] = run;
+            if (j < per && s < nseg) {
+                base[(rev ? nseg - 1 - s : s) * rec4] = run;
                 run += x[j];
             }
         }
-    } else if (q == 0) {
+    } else if (grp == 0) {
         base[0] = total;
     }
-    if (fin && q == 0) fin[bh * rec + e] = total;
+    if (fin && grp == 0) reinterpret_cast<f32x4 *>(fin + bh * rec)[c4] = total;
 }
 
 hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, const float *init, float *fin,
                        hipStream_t s) {
-    const int64_t nblk = BH * ((rec + 63) / 64);
+    if (rec % 4 != 0 || nseg > kMaxSegPerHead) return hipErrorInvalidValue;
+    const int64_t nblk = BH * ((rec / 4 + kScanCols - 1) / kScanCols);
     hipLaunchKernelGGL(k_state_scan, dim3(unsigned(nblk)), dim3(256), 0, s, ws, nseg, rec, mode, init, fin);
     return hipGetLastError();
 }
