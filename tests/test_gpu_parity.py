@@ -58,6 +58,38 @@ def test_forward_causal(name, w):
     check(f"out[{name}]", host(out), ref, w.dtype)
 
 
+# Plans of the single-launch causal forward (workgroups per (b, h), nb) that
+# exercise its cross-workgroup hand-off: nb = 1 (no hand-off, more workgroups
+# than CUs), 2, 3 (ragged last workgroup), 36, 63 (fp32, D = M = 64) and 64
+# (the largest; some workgroups own an empty slice of the state record).
+PLAN_CASES = [
+    ("nb64_empty_slices", _wl(181, 1, 1, 262144, 64, 64, "bf16"), 64),
+    ("nb63_f32_d64m64", _wl(182, 1, 2, 40000, 64, 64, "f32"), 63),
+    ("nb2_128_heads", _wl(183, 8, 16, 4096, 64, 64, "bf16"), 2),
+    ("nb3_ragged_96_heads", _wl(184, 6, 16, 3000, 32, 32, "bf16"), 3),
+    ("nb1_1024_heads", _wl(185, 64, 16, 512, 32, 64, "bf16"), 1),
+    ("nb36_d32m64", _wl(186, 1, 3, 9000, 32, 64, "bf16"), 36),
+]
+
+
+def _fused_nb(BH, N, chunk=16, waves=8, target_waves=2048, max_blk=64):
+    """Workgroups per (b, h) the library plans for the causal forward."""
+    nch = -(-N // chunk)
+    cpw = max(1, -(-BH * nch // target_waves), -(-nch // (waves * max_blk)))
+    return -(-N // (waves * cpw * chunk))
+
+
+@pytest.mark.parametrize("name,w,nb", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_forward_causal_plans(name, w, nb):
+    assert _fused_nb(w.B * w.H, w.N) == nb
+    q, k, v = wl.forward_inputs(w)
+    _say(f"forward causal plan {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}, {nb} workgroups per head")
+    out = la.la_forward_causal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    ref = oracle.forward_causal(q, k, v)
+    check(f"out[{name}]", host(out), ref, w.dtype)
+
+
 NC_CASES = [("w1", wl.WORKLOADS[1]), ("w3_noncausal", wl.WORKLOADS[3]),
             ("n1", _wl(111, 1, 1, 1, 32, 32, "f32")), ("n77_d64m32", _wl(112, 2, 2, 77, 64, 32, "bf16")),
             ("n5000_f32", _wl(113, 1, 3, 5000, 64, 64, "f32"))]
