@@ -202,6 +202,28 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
 }
 
 // ---- chunk loops, bf16: contiguous loads + LDS staging ---------------------------
+
+// Normalizes one 16-token output tile (Ot[mt] = out^T tiles, every row of
+// the normalizer block Ot[M/16] holding the tokens' denominators) and stores
+// it through the wavefront's LDS tile `so` (16 rows of M + kStagePad), so
+// that each store instruction writes 1 KB of whole rows.
+template <int M>
+__device__ __forceinline__ void store_tile_bf16(bf16 *__restrict__ O, int64_t t0, int64_t t_end,
+                                                const f32x4 (&Ot)[M / 16 + 1], lds_bf16 *so) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const float inv = __builtin_amdgcn_rcpf(Ot[M / 16][0]);
+#pragma unroll
+    for (int mt = 0; mt < M / 16; ++mt)
+        *reinterpret_cast<lds_bf16x4 *>(so + c * (M + kStagePad) + 16 * mt + 4 * g) = IO<bf16>::from_f32(Ot[mt] * inv);
+#pragma unroll
+    for (int i = 0; i < M / 32; ++i) {
+        const int e = (64 * i + lane) * 8, row = e / M, col = e % M;
+        const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(so + row * (M + kStagePad) + col);
+        const int64_t t = t0 + row;
+        if (t < t_end) *reinterpret_cast<dwordx4 *>(O + t * M + col) = y;
+    }
+}
+
 // Same products as above; the chunk's rows are fetched with contiguous
 // 16-byte loads, the feature map is applied in registers, and the rows are
 // staged in the wavefront's LDS area, from which the natural and the
@@ -239,7 +261,7 @@ template <int D, int M, bool CAUSAL, int PF>
 __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                 const bf16 *__restrict__ V, bf16 *__restrict__ O, int64_t t_begin,
                                                 int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *sq,
-                                                lds_bf16 *sk, lds_bf16 *sv) {
+                                                lds_bf16 *sk, lds_bf16 *sv, lds_bf16 *so) {
     typedef bf16x4 Fr;
     constexpr int DT = D / 16, MT = M / 16;
     constexpr int NQ = Lines<D, TT>::n, NV = Lines<M, TT>::n;
@@ -335,18 +357,13 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
             state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
 
-        // normalize and store: every row of the normalizer block holds den,
-        // so element 0 of lane (c, g) is the denominator of token c
+        // normalize and store (every row of the normalizer block holds den)
 #pragma unroll
         for (int it = 0; it < TT; ++it) {
-            const float den = Ot[MT][it][0];
-            const float inv = __builtin_amdgcn_rcpf(den);
-            const int64_t t = t0 + 16 * it + c;
-            if (t < t_end) {
+            f32x4 tile[MT + 1];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    store4<bf16>(O + t * M + 16 * mt + 4 * g, IO<bf16>::from_f32(Ot[mt][it] * inv));
-            }
+            for (int mt = 0; mt <= MT; ++mt) tile[mt] = Ot[mt][it];
+            store_tile_bf16<M>(O, t0 + 16 * it, t_end, tile, so);
         }
     }
     }
@@ -373,26 +390,95 @@ __global__ __launch_bounds__(64) void k_segment_state(const T *__restrict__ k, c
     state_store<D, M>(ws + (bh * nseg + seg) * rec, St);
 }
 
-template <typename T, int D, int M, bool CAUSAL>
-__global__ __launch_bounds__(64) void k_segment_output(const T *__restrict__ q, const T *__restrict__ k,
-                                                       const T *__restrict__ v, T *__restrict__ out,
-                                                       const float *__restrict__ ws, int64_t N, int64_t nseg,
-                                                       int64_t seg_tokens, int64_t rec) {
-    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int64_t t_begin = seg * seg_tokens;
-    const int64_t t_end = min(N, t_begin + seg_tokens);
-    __shared__ bf16 stage[2 * stage_elems<D / 16, TT>() + stage_elems<M / 16, TT>()];
-    lds_bf16 *sq = (lds_bf16 *)(stage);
-    lds_bf16 *sk = sq + stage_elems<D / 16, TT>();
-    lds_bf16 *sv = sk + stage_elems<D / 16, TT>();
-    f32x4 St[D / 16][M / 16 + 1];
-    state_load<D, M, true>(St, ws + (bh * nseg + (CAUSAL ? seg : 0)) * rec);
-    if constexpr (sizeof(T) == 2)
-        seg_output_bf16<D, M, CAUSAL, kPrefetch>(q + bh * N * D, k + bh * N * D, v + bh * N * M, out + bh * N * M,
-                                                 t_begin, t_end, St, sq, sk, sv);
-    else
-        seg_output<T, D, M, CAUSAL, kPrefetch>(q + bh * N * D, k + bh * N * D, v + bh * N * M, out + bh * N * M,
-                                               t_begin, t_end, St, sk, sv);
+// Non-causal readout: out_i = phi(Q_i)^T S / phi(Q_i)^T Z with the head's
+// total (S, Z).  The state never changes, so each wavefront converts it to
+// operand tiles once and then only streams its tokens: contiguous loads of
+// Q, the feature map, one LDS staging round trip for the fragments, the
+// products, normalization and stores.  Four wavefronts per workgroup, each
+// with its own token range (kNcWaves per SIMD in flight).
+constexpr int kNcWavesPerBlock = 4;
+constexpr int64_t kNcTargetWaves = 4096;
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__(64 * kNcWavesPerBlock) void k_noncausal_output(
+    const T *__restrict__ q, T *__restrict__ out, const float *__restrict__ ws, int64_t BH, int64_t N, int64_t nsub,
+    int64_t sub_tokens, int64_t nseg_rec, int64_t rec) {
+    constexpr int DT = D / 16, MT = M / 16;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t gw = int64_t(blockIdx.x) * kNcWavesPerBlock + wave;
+    const int64_t bh = gw / nsub, sub = gw % nsub;
+    if (bh >= BH) return;   // whole wavefront; no workgroup barrier below
+    const int64_t t_begin = sub * sub_tokens;
+    const int64_t t_end = min(N, t_begin + sub_tokens);
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const T *Q = q + bh * N * D;
+    T *O = out + bh * N * M;
+    typedef typename IO<T>::frag Fr;
+    Fr SF[MT + 1][DT];
+    {
+        f32x4 St[DT][MT + 1];
+        state_load<D, M, true>(St, ws + bh * nseg_rec * rec);
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = IO<T>::to_frag(St[dt][mt]);
+    }
+    constexpr int SQ = stage_elems<DT, TT>(), SO = 16 * (M + kStagePad);
+    __shared__ bf16 stage_mem[kNcWavesPerBlock][SQ + SO];
+    lds_bf16 *sq = (lds_bf16 *)(&stage_mem[wave][0]);
+    lds_bf16 *so = sq + SQ;   // one 16-token output tile
+
+    auto readout = [&](int64_t t0, const Fr (&Qn)[TT][DT]) {
+#pragma unroll
+        for (int it = 0; it < TT; ++it) {
+            f32x4 Ot[MT + 1];
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt) {
+                Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt], SF[mt][dt], SF[mt][dt + 1], Qn[it][dt], Qn[it][dt + 1]);
+            }
+            if constexpr (sizeof(T) == 2) {
+                store_tile_bf16<M>(O, t0 + 16 * it, t_end, Ot, so);
+            } else {
+                const float inv = __builtin_amdgcn_rcpf(Ot[MT][0]);   // every row of the block holds den
+                const int64_t t = t0 + 16 * it + c;
+                if (t < t_end) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        store4<T>(O + t * M + 16 * mt + 4 * g, IO<T>::from_f32(Ot[mt] * inv));
+                }
+            }
+        }
+    };
+    if constexpr (sizeof(T) == 2) {
+        constexpr int NQ = Lines<D, TT>::n;
+        dwordx4 rq[2][NQ];
+        load_lines<D, TT>(rq[0], Q, t_begin, t_end);
+        load_lines<D, TT>(rq[1], Q, t_begin + CH, t_end);
+        for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * CH) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int64_t t0 = t00 + b * CH;   // may lie past t_end: no stores
+                stage_lines<D, TT, true, false>(sq, rq[b], t0, t_end);
+                load_lines<D, TT>(rq[b], Q, t0 + 2 * CH, t_end);
+                __builtin_amdgcn_sched_barrier(0);
+                Fr Qn[TT][DT];
+                natural_frags_lds<D, TT>(Qn, sq);
+                readout(t0, Qn);
+            }
+        }
+    } else {
+        typedef typename IO<T>::vec4 V4;
+        V4 rq[TT][DT];
+        load_chunk<T, D, TT>(rq, Q, t_begin, t_end);
+        for (int64_t t0 = t_begin; t0 < t_end; t0 += CH) {
+            Fr Qn[TT][DT];
+            phi_frags<T, D, TT>(Qn, rq, t0, t_end);
+            load_chunk<T, D, TT>(rq, Q, t0 + CH, t_end);
+            readout(t0, Qn);
+        }
+    }
 }
 
 // ---- scan over segments ---------------------------------------------------
@@ -558,8 +644,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     // partial sum A_w0 + ... + A_{w-1}, slot 0 the block total, then the
     // group sums of the prefix slice being formed, then the block's own
     // prefix P_s.
-    constexpr int SK = stage_elems<D / 16, TT>(), SV = stage_elems<M / 16, TT>();
-    constexpr int STAGE_BYTES = kFusedWaves * (2 * SK + SV) * int(sizeof(bf16));
+    constexpr int SK = stage_elems<D / 16, TT>(), SV = stage_elems<M / 16, TT>(), SO = 16 * (M + kStagePad);
+    constexpr int SW = 2 * SK + SV + SO;   // per wavefront: q, k, v chunks and one output tile
+    constexpr int STAGE_BYTES = kFusedWaves * SW * int(sizeof(bf16));
     constexpr int SLOT4 = REC4 + int(kMaxBlkPerHead);
     constexpr int SLOT_BYTES = kFusedWaves * SLOT4 * int(sizeof(f32x4));
     __shared__ __align__(16) unsigned char lds_raw[STAGE_BYTES > SLOT_BYTES ? STAGE_BYTES : SLOT_BYTES];
@@ -584,7 +671,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     // 1. local totals
     f32x4 St[D / 16][M / 16 + 1];
     state_zero<D, M>(St);
-    lds_bf16 *stage_q = (lds_bf16 *)(lds_stage + wave * (2 * SK + SV));
+    lds_bf16 *stage_q = (lds_bf16 *)(lds_stage + wave * SW);
     lds_bf16 *stage_k = stage_q + SK;
     lds_bf16 *stage_v = stage_k + SK;
     if constexpr (sizeof(T) == 2)
@@ -700,7 +787,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     __syncthreads();   // the prefix is read: the staging area is free again
     if constexpr (sizeof(T) == 2)
         seg_output_bf16<D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q, stage_k,
-                                               stage_v);
+                                               stage_v, stage_v + SV);
     else
         seg_output<T, D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_k, stage_v);
 }
@@ -740,8 +827,15 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
     if (e != hipSuccess) return e;
     e = launch_scan(ws, BH, p.nseg, p.rec, 1, nullptr, nullptr, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_segment_output<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                       (const T *)v, (T *)out, (const float *)ws, N, p.nseg, p.seg_tokens, p.rec);
+    // readout with its own, finer split: ~kNcTargetWaves wavefronts in all
+    const int64_t nch = ceil_div(N, kChunk);
+    const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(nch, ceil_div(kNcTargetWaves, BH)));
+    const int64_t sub_tokens = ceil_div(nch, per_head) * kChunk;
+    const int64_t nsub = ceil_div(N, sub_tokens);
+    const int64_t nwaves = BH * nsub;
+    hipLaunchKernelGGL((k_noncausal_output<T, D, M>), dim3(unsigned(ceil_div(nwaves, kNcWavesPerBlock))),
+                       dim3(64 * kNcWavesPerBlock), 0, s, (const T *)q, (T *)out, (const float *)ws, BH, N, nsub,
+                       sub_tokens, p.nseg, p.rec);
     return hipGetLastError();
 }
 
