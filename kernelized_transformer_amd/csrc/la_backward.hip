@@ -37,6 +37,8 @@ template <int D, int M>
 constexpr int kBwdStage = (stage_elems<D / 16, BTT>() + stage_elems<M / 16 + 1, BTT>() > stage_elems<D / 16, M / 16 + 1>())
                               ? stage_elems<D / 16, BTT>() + stage_elems<M / 16 + 1, BTT>()
                               : stage_elems<D / 16, M / 16 + 1>();
+template <int D, int M>
+constexpr int kBwdTile = 16 * ((D > M ? D : M) + kStagePad);
 
 // ---- pass 2: forward direction --------------------------------------------
 template <typename T, int D, int M>
@@ -69,8 +71,9 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 
     const Fr ones = frag_row0_ones<Fr>();
     const Fr k0ones = frag_k0_ones<Fr>();
-    __shared__ bf16 stage_mem[kBwdStage<D, M>];
+    __shared__ bf16 stage_mem[kBwdStage<D, M> + kBwdTile<D, M>];
     lds_bf16 *stage = (lds_bf16 *)(stage_mem);
+    lds_bf16 *otile = stage + kBwdStage<D, M>;   // one 16-token output tile (bf16)
 
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
     load_chunk<T, D, BTT>(rq, Q, t_begin, t_end);
@@ -142,11 +145,15 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<T>::to_frag(gv[mt]);
         Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
-        if (valid) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) tile_put_bf16<M>(otile, mt, IO<bf16>::from_f32(gv[mt]));
+            tile_flush_bf16<M>((bf16 *)GB, t0, t_end, otile);
+        } else if (valid) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) store4<T>(GB + t * M + 16 * mt + 4 * g, IO<T>::from_f32(gv[mt]));
-            if (g == 0) HB[t] = h;
         }
+        if (valid && g == 0) HB[t] = h;
 
         // dA^T[j][i] = vh_j . gh_i, masked to j <= i
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
@@ -168,8 +175,13 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 #pragma unroll
             for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, SFT[mt][dt], SFT[mt + 1][dt], Gn[0][mt], Gn[0][mt + 1]);
             if ((MT & 1) == 0) mma1(acc, SFT[MT][dt], Gn[0][MT]);
-            if (valid) store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(acc * dphi4(qraw[dt])));
+            const f32x4 dqv = acc * dphi4(qraw[dt]);
+            if constexpr (sizeof(T) == 2)
+                tile_put_bf16<D>(otile, dt, IO<bf16>::from_f32(dqv));
+            else if (valid)
+                store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dqv));
         }
+        if constexpr (sizeof(T) == 2) tile_flush_bf16<D>((bf16 *)DQ, t0, t_end, otile);
 
         // this segment's reverse-sum contribution: Ra += sum_i qh_i gh_i^T
         Fr QT[BTT][DT], GT[BTT][MT + 1];
@@ -213,8 +225,9 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     state_load<D, M>(Rr, rrec);
 
     const Fr k0ones = frag_k0_ones<Fr>();
-    __shared__ bf16 stage_mem[kBwdStage<D, M>];
+    __shared__ bf16 stage_mem[kBwdStage<D, M> + kBwdTile<D, M>];
     lds_bf16 *stage = (lds_bf16 *)(stage_mem);
+    lds_bf16 *otile = stage + kBwdStage<D, M>;   // one 16-token output tile (bf16)
 
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
@@ -286,8 +299,13 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 #pragma unroll
             for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, RFT[mt][dt], RFT[mt + 1][dt], Vn[0][mt], Vn[0][mt + 1]);
             if ((MT & 1) == 0) mma1(acc, RFT[MT][dt], Vn[0][MT]);
-            if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(acc * dphi4(kraw[dt])));
+            const f32x4 dkv = acc * dphi4(kraw[dt]);
+            if constexpr (sizeof(T) == 2)
+                tile_put_bf16<D>(otile, dt, IO<bf16>::from_f32(dkv));
+            else if (valid)
+                store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dkv));
         }
+        if constexpr (sizeof(T) == 2) tile_flush_bf16<D>((bf16 *)DK, t0, t_end, otile);
         // dV^T[m][j] = sum_i g[i][m] P[i][j] + sum_d R[d][m] kh[j][d]
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -295,8 +313,12 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
             mma1(acc, GT[0][mt], Pf);
 #pragma unroll
             for (int dt = 0; dt < DT; dt += 2) mma2(acc, RF[mt][dt], RF[mt][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
-            if (valid) store4<T>(DV + t * M + 16 * mt + 4 * g, IO<T>::from_f32(acc));
+            if constexpr (sizeof(T) == 2)
+                tile_put_bf16<M>(otile, mt, IO<bf16>::from_f32(acc));
+            else if (valid)
+                store4<T>(DV + t * M + 16 * mt + 4 * g, IO<T>::from_f32(acc));
         }
+        if constexpr (sizeof(T) == 2) tile_flush_bf16<M>((bf16 *)DV, t0, t_end, otile);
 
         // carry R_aug past this chunk, towards earlier tokens
 #pragma unroll

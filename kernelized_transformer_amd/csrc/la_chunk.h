@@ -191,6 +191,27 @@ __device__ __forceinline__ void transposed_frags_lds(bf16x4 (&yt)[TT][F / 16], c
         }
 }
 
+// Output tiles of 16 tokens x F bf16 features go through LDS (row stride
+// F + kStagePad): each lane puts the 4 consecutive features it holds (Acc
+// layout: lane (c, g) has token c, features 16 ft + 4g .. + 3), then every
+// store instruction writes 1 KB of whole rows.
+template <int F>
+__device__ __forceinline__ void tile_put_bf16(lds_bf16 *tile, int ft, bf16x4 x) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+    *reinterpret_cast<lds_bf16x4 *>(tile + c * (F + kStagePad) + 16 * ft + 4 * g) = x;
+}
+template <int F>
+__device__ __forceinline__ void tile_flush_bf16(bf16 *__restrict__ dst, int64_t t0, int64_t t_end,
+                                                const lds_bf16 *tile) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < F / 32; ++i) {
+        const int e = (64 * i + l) * 8, row = e / F, col = e % F;
+        const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(tile + row * (F + kStagePad) + col);
+        if (t0 + row < t_end) *reinterpret_cast<dwordx4 *>(dst + (t0 + row) * F + col) = y;
+    }
+}
+
 // Elements of LDS staging one wavefront needs per tensor chunk.
 template <int NF, int TT> constexpr int stage_elems() { return 16 * TT * (16 * NF + kStagePad); }
 
