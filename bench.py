@@ -6,7 +6,10 @@ Headline (``value``): causal forward throughput in tokens*heads/s on the long
 sequence workload B=1, H=8, N=65536, D=M=64, bf16 I/O, fp32 state.  One step
 is one la_forward_causal call over the whole batch, inputs already resident
 in HBM; two input sets alternate so that consecutive steps do not re-read the
-same 268 MB from the 256 MB Infinity Cache.
+same 268 MB from the 256 MB Infinity Cache.  Per-call medians over at least 20
+calls are reported beside it: alternating inputs, cold (512 MB of scratch
+written before each call, which evicts the Infinity Cache) and warm (the same
+input again).
 
 In the same run, each timed with HIP events on the stream the library launches
 on, and reported next to the headline:
@@ -171,6 +174,33 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) / 1e3
 
+    def time_each(fn, iters, between=None):
+        """Per-call durations (s): one event pair around each call; ``between``
+        runs outside the pairs (e.g. a cache flush)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            if between is not None:
+                between()
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) / 1e3 for e0, e1 in ev]
+
+    def med(xs):
+        xs = sorted(xs)
+        n = len(xs)
+        return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+    # Writing 512 MB of scratch evicts the 256 MB Infinity Cache (and every L2).
+    flush_buf = [None]
+
+    def flush():
+        if flush_buf[0] is None:
+            flush_buf[0] = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        flush_buf[0].fill_(7)
+
     # ---- forward on the long-sequence workload ----------------------------------
     w4 = wl.WORKLOADS[4]
     BH = w4.B * w4.H
@@ -206,6 +236,18 @@ def main():
         t_same = time_events(lambda i: fwd(0), a.steps)
         results["forward_same_input"] = dict(ms_per_step=t_same / a.steps * 1e3,
                                              tok_heads_per_s=tok_heads * a.steps / t_same)
+        # medians over per-call event pairs: alternating inputs, cold (caches
+        # flushed before each call), warm (the same input again)
+        reps = max(20, a.steps)
+        t_alt = med(time_each(fwd, reps))
+        t_cold = med(time_each(fwd, reps, between=flush))
+        t_warm = med(time_each(lambda i: fwd(0), reps))
+        results["forward_median"] = {
+            k_: dict(ms=t_ * 1e3, tok_heads_per_s=tok_heads / t_, hbm_frac=fwd_bytes / t_ / 1e9 / HBM_PEAK_GBS)
+            for k_, t_ in (("alternating", t_alt), ("cold", t_cold), ("warm", t_warm))}
+        results["forward_median"]["reps"] = reps
+        log(f"causal forward medians over {reps}: alternating {t_alt * 1e3:.4f}, cold {t_cold * 1e3:.4f}, "
+            f"warm {t_warm * 1e3:.4f} ms")
 
     # ---- backward / non-causal on the long-sequence workload --------------------------
     if a.only in ("all", "backward"):
@@ -229,7 +271,12 @@ def main():
         results["backward"] = dict(ms_per_call=t / nb * 1e3, tok_heads_per_s=tok_heads * nb / t,
                                    algorithmic_bytes=bwd_bytes,
                                    hbm_frac=bwd_bytes / (t / nb) / 1e9 / HBM_PEAK_GBS)
-        log(f"causal backward: {t / nb * 1e3:.4f} ms/call")
+        reps = max(20, nb)
+        t_alt = med(time_each(bwd, reps))
+        t_cold = med(time_each(bwd, reps, between=flush))
+        results["backward"]["median"] = {"reps": reps, "alternating_ms": t_alt * 1e3, "cold_ms": t_cold * 1e3}
+        log(f"causal backward: {t / nb * 1e3:.4f} ms/call; medians over {reps}: alternating "
+            f"{t_alt * 1e3:.4f}, cold {t_cold * 1e3:.4f} ms")
         del dq, dk, dv, ws_b
     if a.only in ("all",):
         for i in range(2):
@@ -269,6 +316,7 @@ def main():
     # the decode state is a fresh allocation as in a serving process (carved out
     # of the caching allocator's older segments it was measured 25% slower).
     del sets, out, ws_f
+    flush_buf[0] = None
     torch.cuda.empty_cache()
     if a.only in ("all", "decode"):
         w5 = wl.WORKLOADS[5]

@@ -295,6 +295,43 @@ __device__ __forceinline__ void state_store(float *__restrict__ rec, const f32x4
     }
 }
 
+// The same state in fragment order, for records that are only ever summed
+// elementwise (the causal forward's block totals and prefixes): the S part
+// is the Acc tiles one after another, St[dt][mt] (mt < M/16) as 64 lanes x 4
+// consecutive floats, so every lane moves one f32x4 per tile without LDS
+// bank conflicts; Z follows in natural order, D floats.  Same size as the
+// row-major record.
+template <int D, int M>
+__device__ __forceinline__ void state_store_frag(float *__restrict__ rec, const f32x4 (&St)[D / 16][M / 16 + 1]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    f32x4 *r4 = reinterpret_cast<f32x4 *>(rec);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt) r4[(dt * (M / 16) + mt) * 64 + lane] = St[dt][mt];
+        if (c == 0) r4[(D * M) / 4 + 4 * dt + g] = St[dt][M / 16];
+    }
+}
+// St = A + B of two fragment-order records (B may be null), normalizer tile
+// replicated (the REP layout of state_load).
+template <int D, int M>
+__device__ __forceinline__ void state_load_frag2(f32x4 (&St)[D / 16][M / 16 + 1], const float *__restrict__ a,
+                                                 const float *__restrict__ b) {
+    const int lane = lane_id(), g = lane >> 4;
+    const f32x4 *a4 = reinterpret_cast<const f32x4 *>(a);
+    const f32x4 *b4 = reinterpret_cast<const f32x4 *>(b);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt) {
+            const int i = (dt * (M / 16) + mt) * 64 + lane;
+            St[dt][mt] = b4 ? a4[i] + b4[i] : a4[i];
+        }
+        const int i = (D * M) / 4 + 4 * dt + g;
+        St[dt][M / 16] = b4 ? a4[i] + b4[i] : a4[i];
+    }
+}
+
 // St += sum over the chunk's tokens of A_t B_t^T, where KT/VT are
 // token-contiguous fragments (KT: rows = the D features of A; VT: rows = the
 // M features of B).  The extra column block adds sum_t A_t to the

@@ -679,7 +679,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     else
         seg_aggregate<T, D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
     __syncthreads();   // every wavefront is done with its staging area
-    state_store<D, M>(slot(wave), St);
+    state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
 
     // 2a. in place: slot w = A_w0 + ... + A_{w-1} for w >= 1, slot 0 = the
@@ -768,22 +768,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     __syncthreads();
 
     // 3. outputs, starting from P_s + the totals of the earlier wavefronts
-    {
-        const int c = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-#pragma unroll
-            for (int mt = 0; mt <= M / 16; ++mt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int d = 16 * dt + 4 * g + r;
-                    const bool z = mt == M / 16;
-                    const int e = z ? D * M + d : d * M + 16 * mt + c;
-                    St[dt][mt][r] = pbuf[e] + (wave > 0 ? slot(wave)[e] : 0.f);
-                }
-            }
-        }
-    }
+    state_load_frag2<D, M>(St, pbuf, wave > 0 ? slot(wave) : nullptr);
     __syncthreads();   // the prefix is read: the staging area is free again
     if constexpr (sizeof(T) == 2)
         seg_output_bf16<D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q, stage_k,

@@ -66,6 +66,7 @@ struct FusedPlan {
     size_t flags_off = 0;    // 64-bit flags [BH][2][nblk]: total published, prefix slice published
                              // (after a 256-byte header; int word 1 is the error word)
     size_t recs_off = 0;     // float records [BH][nblk][2][rec]: block total, exclusive prefix
+                             // (fragment order: only ever summed elementwise)
     size_t total = 0;
 };
 
