@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
 
@@ -82,6 +82,31 @@ la_status_t la_forward_causal(const void *q, const void *k, const void *v, void 
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                               la_dtype_t dt, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * Causal forward continuing from a given recurrent state, and/or returning
+ * the state after the last token ([summary] 3.3.2 and 3.4: the memory s_i,
+ * z_i is all a step needs; 4.2.1: only s_i and z_i are kept between pixels;
+ * 4.2.2: image completion conditions on a prefix and then generates):
+ *   S_0 = s0, Z_0 = z0 (zero when s0 = z0 = NULL), then the recurrence of
+ *   la_forward_causal for i = 1..N;  s_final = S_N, z_final = Z_N.
+ * s0, s_final: [B][H][D][M] fp32; z0, z_final: [B][H][D] fp32 -- the layout
+ * of la_decode_step's S and Z, so a prompt's forward hands its state to
+ * decode directly, and a sequence split into consecutive pieces gives the
+ * same outputs piece by piece.  s0/z0 are both NULL or both set, and so are
+ * s_final/z_final (NULL: the final state is not written).  s_final == s0
+ * and z_final == z0 update the state in place; any other overlap of a state
+ * tensor with another buffer is LA_ERR_INVALID_ARGUMENT.  A start state
+ * should be one a recurrence can reach (z0 with phi(q) . z0 + ... > 0);
+ * the library does not check it.  Other arguments, workspace and
+ * diagnostic word: as la_forward_causal (whose call equals this one with
+ * all four state pointers NULL).
+ */
+la_status_t la_forward_causal_state(const void *q, const void *k, const void *v, void *out,
+                                    const float *s0, const float *z0, float *s_final,
+                                    float *z_final, int64_t B, int64_t H, int64_t N, int64_t D,
+                                    int64_t M, la_dtype_t dt, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Non-causal forward through associativity ([review] "Proposed method";

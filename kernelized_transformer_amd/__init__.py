@@ -9,6 +9,7 @@ built, every call raises.
 
 Functions carry the C names:
   la_forward_causal(q, k, v, out=None, workspace=None)
+  la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None)
   la_forward_noncausal(q, k, v, out=None, workspace=None)
   la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_decode_step(q, k, v, S, Z, out=None)
@@ -22,7 +23,7 @@ import os
 
 import torch
 
-__all__ = ["la_forward_causal", "la_forward_noncausal", "la_backward_causal", "la_decode_step",
+__all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal", "la_decode_step",
            "la_workspace_size", "la_status_string", "la_abi_version", "LAError", "lib_path", "load",
            "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
 
@@ -56,7 +57,9 @@ def load():
     lib.la_forward_noncausal.argtypes = fwd
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
-    for f in ("la_forward_causal", "la_forward_noncausal", "la_backward_causal", "la_decode_step"):
+    lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal",
+              "la_decode_step"):
         getattr(lib, f).restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
     lib.la_workspace_size.restype = sz
@@ -126,6 +129,41 @@ def _forward(func: str, op: int, q, k, v, out, workspace):
 def la_forward_causal(q, k, v, out=None, workspace=None):
     """Causal linear attention forward; returns out [B,H,N,M]."""
     return _forward("la_forward_causal", LA_OP_FWD_CAUSAL, q, k, v, out, workspace)
+
+
+def la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None):
+    """Causal forward from the fp32 state (s0 [B,H,D,M], z0 [B,H,D]; None: zero);
+    returns (out, s_final, z_final), the state after the last token (allocated
+    unless given; pass s_final=s0, z_final=z0 to update in place)."""
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k: [B,H,N,D]; v: [B,H,N,M]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if (s0 is None) != (z0 is None):
+        raise ValueError("give both s0 and z0, or neither")
+    if s_final is None:
+        s_final = torch.empty((B, H, D, M), dtype=torch.float32, device=dev)
+    if z_final is None:
+        z_final = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    states = [s_final, z_final] + ([s0, z0] if s0 is not None else [])
+    for t, shape in zip(states, [(B, H, D, M), (B, H, D)] * 2):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape:
+            raise ValueError("states: float32 s [B,H,D,M] and z [B,H,D]")
+    _dev(q, *states)
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    _dev(q, out)
+    ws, wsb = _ws(LA_OP_FWD_CAUSAL, B, H, N, D, M, q.dtype, workspace, dev)
+    st = load().la_forward_causal_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        s0.data_ptr() if s0 is not None else None,
+                                        z0.data_ptr() if z0 is not None else None, s_final.data_ptr(),
+                                        z_final.data_ptr(), B, H, N, D, M, _DT[q.dtype], ws.data_ptr(), wsb,
+                                        _stream(dev))
+    _check("la_forward_causal_state", st)
+    return out, s_final, z_final
 
 
 def la_forward_noncausal(q, k, v, out=None, workspace=None):

@@ -88,6 +88,48 @@ la_status_t la_forward_causal(const void *q, const void *k, const void *v, void 
     return forward_common(true, q, k, v, out, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
 }
 
+la_status_t la_forward_causal_state(const void *q, const void *k, const void *v, void *out, const float *s0,
+                                    const float *z0, float *s_final, float *z_final, int64_t B, int64_t H, int64_t N,
+                                    int64_t D, int64_t M, la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, D, M, dt);
+    if (st != LA_OK) return st;
+    if ((s0 == nullptr) != (z0 == nullptr) || (s_final == nullptr) != (z_final == nullptr))
+        return LA_ERR_INVALID_ARGUMENT;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const size_t sbytes = size_t(BH * D * M) * 4, zbytes = size_t(BH * D) * 4;
+    // inputs: q, k, v and the start state unless it is updated in place (a
+    // state tensor passed as both is checked once, as an output)
+    Span in[5] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
+                  span(v, size_t(BH * N * M) * es)};
+    int nin = 3;
+    if (s0 != nullptr && s0 != s_final) in[nin++] = span(s0, sbytes);
+    if (z0 != nullptr && z0 != z_final) in[nin++] = span(z0, zbytes);
+    Span o[3] = {span(out, size_t(BH * N * M) * es)};
+    int nout = 1;
+    if (s_final != nullptr) {
+        o[nout++] = span(s_final, sbytes);
+        o[nout++] = span(z_final, zbytes);
+    }
+    if ((st = check_buffers(in, nin, o, nout)) != LA_OK) return st;
+    Span all[8];
+    int nall = 0;
+    for (int i = 0; i < nin; ++i) all[nall++] = in[i];
+    for (int i = 0; i < nout; ++i) all[nall++] = o[i];
+    if ((st = check_workspace(workspace, workspace_bytes, la::causal_workspace_bytes(BH, N, D, M), all, nall)) !=
+        LA_OK)
+        return st;
+    la::StateIO sio;
+    sio.s0 = s0;
+    sio.z0 = z0;
+    sio.s1 = s_final;
+    sio.z1 = z_final;
+    const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+                                            static_cast<float *>(workspace), stream, sio);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 la_status_t la_forward_noncausal(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
                                  int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {

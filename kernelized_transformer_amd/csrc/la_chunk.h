@@ -332,6 +332,33 @@ __device__ __forceinline__ void state_load_frag2(f32x4 (&St)[D / 16][M / 16 + 1]
     }
 }
 
+// Element i4 (an f32x4) of a fragment-order record, from / to a state kept
+// as separate row-major S [D][M] and Z [D]: an S element holds rows
+// 16 dt + 4g + r (r = 0..3) of column 16 mt + c, where i4 = (dt (M/16) + mt)
+// 64 + 16 g + c; past the S part, 4 consecutive Z entries.
+template <int D, int M>
+__device__ __forceinline__ f32x4 record_frag4_load(const float *S, const float *Z, int i4) {
+    if (i4 < D * M / 4) {
+        const int ln = i4 & 63, tile = i4 >> 6, dt = tile / (M / 16), mt = tile % (M / 16);
+        const float *p = S + (16 * dt + 4 * (ln >> 4)) * M + 16 * mt + (ln & 15);
+        return f32x4{p[0], p[M], p[2 * M], p[3 * M]};
+    }
+    return *reinterpret_cast<const f32x4 *>(Z + 4 * (i4 - D * M / 4));
+}
+template <int D, int M>
+__device__ __forceinline__ void record_frag4_store(float *S, float *Z, int i4, f32x4 x) {
+    if (i4 < D * M / 4) {
+        const int ln = i4 & 63, tile = i4 >> 6, dt = tile / (M / 16), mt = tile % (M / 16);
+        float *p = S + (16 * dt + 4 * (ln >> 4)) * M + 16 * mt + (ln & 15);
+        p[0] = x[0];
+        p[M] = x[1];
+        p[2 * M] = x[2];
+        p[3 * M] = x[3];
+    } else {
+        *reinterpret_cast<f32x4 *>(Z + 4 * (i4 - D * M / 4)) = x;
+    }
+}
+
 // St += sum over the chunk's tokens of A_t B_t^T, where KT/VT are
 // token-contiguous fragments (KT: rows = the D features of A; VT: rows = the
 // M features of B).  The extra column block adds sum_t A_t to the

@@ -635,7 +635,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
                                                                 unsigned long long *__restrict__ flags,
                                                                 unsigned long long tag,
                                                                 float *__restrict__ recs, int64_t N, int64_t nblk,
-                                                                int64_t sub_tokens) {
+                                                                int64_t sub_tokens, StateIO sio) {
     constexpr int REC = D * M + D, REC4 = REC / 4;
     static_assert(REC % 4 == 0, "records move as f32x4");
     constexpr int NT = 64 * kFusedWaves;
@@ -682,6 +682,19 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
 
+    // Initial state (zero unless given), this thread's record elements.  Read
+    // here, before the block publishes anything: the last block of the head
+    // writes the final state only after every block has published, so the
+    // two may share memory.
+    constexpr int NJ4 = (REC4 + NT - 1) / NT;
+    f32x4 init[NJ4];
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j) {
+        const int i4 = tid + NT * j;
+        init[j] = (sio.s0 && i4 < REC4) ? record_frag4_load<D, M>(sio.s0 + bh * D * M, sio.z0 + bh * D, i4)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     // 2a. in place: slot w = A_w0 + ... + A_{w-1} for w >= 1, slot 0 = the
     // block total A_s (wavefront 0's partial sum is zero)
 #pragma unroll
@@ -699,6 +712,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         }
     }
     __syncthreads();
+    // the last block keeps its total for the final state (the slice scan
+    // below reuses slot 0 as scratch)
+    const bool last = sio.s1 != nullptr && sb == nb - 1;
+    f32x4 tot[NJ4];
+#pragma unroll
+    for (int j = 0; j < NJ4; ++j)
+        tot[j] = (last && tid + NT * j < REC4) ? slot4[tid + NT * j] : f32x4{0.f, 0.f, 0.f, 0.f};
     if (sb < nb - 1) {   // every thread stores a share of the total
         f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + blk * 2 * REC);
 #pragma unroll
@@ -751,19 +771,28 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         if (wave == 0 && sb > 0) wait_flags(flag_pre, nb, tag, &header[1]);
         __syncthreads();
     }
-    // 2c. P_s into LDS (zero for the first block)
-    if (sb > 0) {
+    // 2c. P_s = initial state + the earlier blocks' totals into LDS; the last
+    // block also forms the final state P_s + A_s
+    {
         const f32x4 *src = reinterpret_cast<const f32x4 *>(head_recs + (blk * 2 + 1) * REC);
-        constexpr int NJ4 = (REC4 + NT - 1) / NT;
         f32x4 buf[NJ4];
 #pragma unroll
         for (int j = 0; j < NJ4; ++j)
-            if (tid + NT * j < REC4) buf[j] = dev_load(src + tid + NT * j);
+            buf[j] = (sb > 0 && tid + NT * j < REC4) ? dev_load(src + tid + NT * j) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NJ4; ++j)
-            if (tid + NT * j < REC4) reinterpret_cast<f32x4 *>(pbuf)[tid + NT * j] = buf[j];
-    } else {
-        for (int i = tid; i < REC; i += NT) pbuf[i] = 0.f;
+        for (int j = 0; j < NJ4; ++j) {
+            const int i4 = tid + NT * j;
+            if (i4 < REC4) {
+                const f32x4 p = buf[j] + init[j];
+                if (last) buf[j] = p + tot[j];
+                reinterpret_cast<f32x4 *>(pbuf)[i4] = p;
+            }
+        }
+        if (last) {
+#pragma unroll
+            for (int j = 0; j < NJ4; ++j)
+                if (tid + NT * j < REC4) record_frag4_store<D, M>(sio.s1 + bh * D * M, sio.z1 + bh * D, tid + NT * j, buf[j]);
+        }
     }
     __syncthreads();
 
@@ -791,7 +820,7 @@ uint64_t next_call_tag() {
 
 template <typename T, int D, int M>
 static hipError_t run_forward(bool causal, const void *q, const void *k, const void *v, void *out, int64_t BH,
-                              int64_t N, float *ws, hipStream_t s) {
+                              int64_t N, float *ws, StateIO sio, hipStream_t s) {
     if (causal) {
         const FusedPlan p = make_fused_plan(BH, N, D, M);
         if (fused_slice_rows(p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows) return hipErrorInvalidValue;
@@ -801,7 +830,7 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
         float *recs = reinterpret_cast<float *>(base + p.recs_off);
         hipLaunchKernelGGL((k_fwd_fused<T, D, M>), dim3(unsigned(BH * p.nblk)), dim3(64 * kFusedWaves), 0, s,
                            (const T *)q, (const T *)k, (const T *)v, (T *)out, header, flags, next_call_tag(), recs,
-                           N, p.nblk, p.sub_tokens);
+                           N, p.nblk, p.sub_tokens, sio);
         return hipGetLastError();
     }
     const SegPlan p = make_plan(BH, N, D, M);
@@ -826,18 +855,19 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
 
 template <typename T>
 static hipError_t run_forward_t(bool causal, const void *q, const void *k, const void *v, void *out, int64_t BH,
-                                int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s) {
-    if (D == 32 && M == 32) return run_forward<T, 32, 32>(causal, q, k, v, out, BH, N, ws, s);
-    if (D == 32 && M == 64) return run_forward<T, 32, 64>(causal, q, k, v, out, BH, N, ws, s);
-    if (D == 64 && M == 32) return run_forward<T, 64, 32>(causal, q, k, v, out, BH, N, ws, s);
-    if (D == 64 && M == 64) return run_forward<T, 64, 64>(causal, q, k, v, out, BH, N, ws, s);
+                                int64_t N, int64_t D, int64_t M, float *ws, StateIO sio, hipStream_t s) {
+    if (D == 32 && M == 32) return run_forward<T, 32, 32>(causal, q, k, v, out, BH, N, ws, sio, s);
+    if (D == 32 && M == 64) return run_forward<T, 32, 64>(causal, q, k, v, out, BH, N, ws, sio, s);
+    if (D == 64 && M == 32) return run_forward<T, 64, 32>(causal, q, k, v, out, BH, N, ws, sio, s);
+    if (D == 64 && M == 64) return run_forward<T, 64, 64>(causal, q, k, v, out, BH, N, ws, sio, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out, int64_t BH,
-                          int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s) {
-    if (dt == 0) return run_forward_t<float>(causal, q, k, v, out, BH, N, D, M, ws, s);
-    return run_forward_t<bf16>(causal, q, k, v, out, BH, N, D, M, ws, s);
+                          int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s, StateIO sio) {
+    if (!causal && (sio.s0 || sio.s1)) return hipErrorInvalidValue;
+    if (dt == 0) return run_forward_t<float>(causal, q, k, v, out, BH, N, D, M, ws, sio, s);
+    return run_forward_t<bf16>(causal, q, k, v, out, BH, N, D, M, ws, sio, s);
 }
 
 template <typename T>

@@ -134,9 +134,18 @@ inline size_t backward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t
     return backward_layout(BH, N, D, M, esize).total;
 }
 
+// Optional fp32 state of the causal forward, [BH][D][M] and [BH][D] (the
+// decode layout): s0/z0 start the recurrence (null: zero), s1/z1 receive the
+// state after the last token (null: not written); s1 may equal s0.
+struct StateIO {
+    const float *s0 = nullptr, *z0 = nullptr;
+    float *s1 = nullptr, *z1 = nullptr;
+};
+
 // Launchers (hipError_t of the last launch).  dt: 0 = fp32, 1 = bf16.
 hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
-                          int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s);
+                          int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s,
+                          StateIO sio = StateIO());
 hipError_t launch_segment_state(int dt, const void *k, const void *v, float *ws, int64_t BH, int64_t N, int64_t D,
                                 int64_t M, hipStream_t s);
 // mode 0: exclusive prefix over segments; 1: total into record 0;

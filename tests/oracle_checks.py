@@ -127,6 +127,28 @@ def check_invariants(lib):
     assert _rel(S_b, S) < 1e-14 and _rel(Z_b, Z) < 1e-14
 
 
+def check_initial_state(lib):
+    """An arbitrary starting state (S0 of any sign, Z0 > 0, not the state of
+    any prefix) enters every readout as one extra, pre-summed key: written out
+    by brute force, out_i = (phi(q_i) S0 + sum_{j<=i} a_ij v_j) /
+    (phi(q_i) . Z0 + sum_{j<=i} a_ij), and the final state is S0 + sum_j
+    phi(k_j) v_j^T, Z0 + sum_j phi(k_j)."""
+    B, H, N, D, M = 2, 2, 33, 5, 3
+    q, k, v = _rand(60, B, H, N, D), _rand(61, B, H, N, D), _rand(62, B, H, N, M)
+    S0 = _rand(63, B, H, D, M) * 4.0
+    Z0 = np.abs(_rand(64, B, H, D)) * 5.0 + 0.5
+    o, S, Z = oracle.forward_causal(q, k, v, S0=S0, Z0=Z0, return_state=True, lib=lib)
+    qh, kh = bf.phi(q), bf.phi(k)
+    a = bf.similarity(q, k, True)
+    num = np.einsum("bhnd,bhdm->bhnm", qh, S0) + a @ v
+    den = np.einsum("bhnd,bhd->bhn", qh, Z0)[..., None] + a.sum(-1, keepdims=True)
+    assert _rel(o, num / den) < 1e-13
+    assert _rel(S, S0 + np.einsum("bhnd,bhnm->bhdm", kh, v)) < 1e-13
+    assert _rel(Z, Z0 + kh.sum(2)) < 1e-14
+    # the start state matters (guards against a recurrence that drops it)
+    assert _rel(o, bf.forward(q, k, v)) > 1e-2
+
+
 def check_decode(lib):
     B, H, T, D, M = 3, 2, 60, 6, 4
     qs, ks, vs = _rand(50, T, B, H, D), _rand(51, T, B, H, D), _rand(52, T, B, H, M)
@@ -220,5 +242,5 @@ def check_backward_identities(lib):
 
 
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,
-              check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
+              check_initial_state, check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
               check_backward_identities]

@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("la_forward_causal", "la_forward_noncausal", "la_backward_causal", "la_decode_step",
-              "la_workspace_size", "la_status_string", "la_abi_version"):
+    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal",
+              "la_decode_step", "la_workspace_size", "la_status_string", "la_abi_version"):
         assert f in fns
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 1
+    assert la.la_abi_version() == 2
     names = [la.la_status_string(s) for s in range(5)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
     assert la.la_status_string(99) == "LA_ERR_UNKNOWN"
@@ -85,6 +85,29 @@ def test_forward_argument_errors(fn):
     assert _fwd(lib, fn, wsb=16) == 3                   # too small
     assert _fwd(lib, fn, ws=FAKE + (4 << 24) + 16, wsb=1 << 20) == 3   # misaligned workspace
     assert _fwd(lib, fn, ws=FAKE, wsb=1 << 20) == 3     # workspace overlaps an input
+
+
+def test_forward_state_argument_errors():
+    lib = la.load()
+    b = [FAKE + (i << 24) for i in range(10)]   # q k v out s0 z0 s1 z1 ws
+
+    def fs(q=b[0], k=b[1], v=b[2], out=b[3], s0=b[4], z0=b[5], s1=b[6], z1=b[7], B=1, H=2, N=8, D=32, M=32, dt=1,
+           ws=b[8], wsb=0):
+        return lib.la_forward_causal_state(q, k, v, out, s0, z0, s1, z1, B, H, N, D, M, dt, ws, wsb, None)
+
+    assert fs() == 3                                # all buffers valid: only the workspace is missing
+    assert fs(s0=0, z0=0, s1=0, z1=0) == 3          # no state at all is valid too
+    assert fs(s1=b[4], z1=b[5]) == 3                # in place is valid
+    assert fs(s0=0) == 1                            # s0 without z0
+    assert fs(z1=0) == 1                            # s_final without z_final
+    assert fs(s0=b[4] + 4) == 1                     # misaligned start state
+    assert fs(z1=b[7] + 8) == 1                     # misaligned final state
+    assert fs(s1=b[4] + 16, z1=b[7]) == 1           # final state partly overlaps the start state
+    assert fs(s1=b[6], z1=b[6] + 256) == 1          # z_final overlaps s_final
+    assert fs(s1=b[4], z1=b[4] + 16) == 1           # in place S, z_final inside it
+    assert fs(s1=b[0]) == 1                         # final state over q
+    assert fs(D=48) == 2
+    assert fs(ws=b[6], wsb=1 << 20) == 3            # workspace overlaps the final state
 
 
 def test_backward_and_decode_argument_errors():

@@ -199,6 +199,115 @@ def test_decode_equals_forward_on_gpu():
     np.testing.assert_allclose(np.moveaxis(outs, 0, 2), fwd, rtol=0, atol=2e-5 * np.abs(fwd).max())
 
 
+# Causal forward carrying the recurrent state across calls: the sequence is
+# cut into consecutive pieces; the first call starts from zero and returns
+# its final state, each later one continues from it in place.  The joined
+# outputs and the last state must match one oracle pass over the whole
+# sequence.
+STATE_CHAIN_CASES = [
+    ("two_pieces_f32_nb1", _wl(191, 2, 3, 300, 32, 64, "f32"), [0, 97, 300]),
+    ("two_pieces_bf16_many_blocks", _wl(192, 1, 2, 40000, 64, 64, "bf16"), [0, 12345, 40000]),
+    ("four_pieces_bf16_single_token", _wl(193, 4, 4, 5000, 32, 32, "bf16"), [0, 1, 2049, 2050, 5000]),
+    ("three_pieces_f32_d64m32", _wl(194, 2, 2, 9000, 64, 32, "f32"), [0, 4500, 4517, 9000]),
+]
+
+
+@pytest.mark.parametrize("name,w,cuts", STATE_CHAIN_CASES, ids=[c[0] for c in STATE_CHAIN_CASES])
+def test_forward_state_chain(name, w, cuts):
+    q, k, v = wl.forward_inputs(w)
+    _say(f"forward state chain {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}, cuts {cuts}")
+    keep, outs = [], []
+    S = Z = None
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        qd, kd, vd = (dev(np.ascontiguousarray(x[:, :, a:b]), w.dtype) for x in (q, k, v))
+        keep += [qd, kd, vd]
+        if S is None:
+            out, S, Z = la.la_forward_causal_state(qd, kd, vd)
+        else:
+            out, _, _ = la.la_forward_causal_state(qd, kd, vd, s0=S, z0=Z, s_final=S, z_final=Z)
+        outs.append(out)
+    torch.cuda.synchronize()
+    ref, S_ref, Z_ref = oracle.forward_causal(q, k, v, return_state=True)
+    check(f"out[{name}]", np.concatenate([host(o) for o in outs], axis=2), ref, w.dtype)
+    check(f"S_N[{name}]", host(S), S_ref, w.dtype)
+    check(f"Z_N[{name}]", host(Z), Z_ref, w.dtype)
+
+
+@pytest.mark.parametrize("name,w", [("bf16_24_blocks", _wl(195, 2, 2, 3000, 64, 64, "bf16")),
+                                    ("f32_one_block", _wl(196, 1, 3, 100, 32, 32, "f32"))],
+                         ids=["bf16_24_blocks", "f32_one_block"])
+def test_forward_state_arbitrary_start(name, w):
+    """A start state that no prefix produced (S0 of any sign): outputs and
+    final state against the oracle started from the same state; with a null
+    final state the outputs are bit-identical."""
+    q, k, v = wl.forward_inputs(w)
+    S0, Z0 = wl.start_state(w, seed=w.wid + 1000)
+    _say(f"forward from an arbitrary state {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    qd, kd, vd = (dev(x, w.dtype) for x in (q, k, v))
+    s0, z0 = dev(S0, "f32"), dev(Z0, "f32")
+    out, S1, Z1 = la.la_forward_causal_state(qd, kd, vd, s0=s0, z0=z0)
+    out2 = torch.empty_like(out)
+    nws = la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.D, w.M, qd.dtype)
+    ws = torch.empty((nws,), dtype=torch.uint8, device="cuda")
+    st = la.load().la_forward_causal_state(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out2.data_ptr(),
+                                           s0.data_ptr(), z0.data_ptr(), None, None, w.B, w.H, w.N, w.D, w.M,
+                                           1 if w.dtype == "bf16" else 0, ws.data_ptr(), nws,
+                                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    ref, S_ref, Z_ref = oracle.forward_causal(q, k, v, S0=S0, Z0=Z0, return_state=True)
+    check(f"out[{name}]", host(out), ref, w.dtype)
+    check(f"S_N[{name}]", host(S1), S_ref, w.dtype)
+    check(f"Z_N[{name}]", host(Z1), Z_ref, w.dtype)
+    assert torch.equal(out, out2)
+    assert torch.equal(s0, dev(S0, "f32")) and torch.equal(z0, dev(Z0, "f32"))   # inputs untouched
+
+
+def test_forward_state_null_and_zero_start_equal_plain_forward():
+    w = _wl(197, 2, 4, 6000, 64, 64, "bf16")
+    q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
+    _say("state entry point with no / zero start state == la_forward_causal (bitwise)")
+    plain = la.la_forward_causal(q, k, v)
+    a, _, _ = la.la_forward_causal_state(q, k, v)
+    zs = torch.zeros((w.B, w.H, w.D, w.M), device="cuda")
+    zz = torch.zeros((w.B, w.H, w.D), device="cuda")
+    b, _, _ = la.la_forward_causal_state(q, k, v, s0=zs, z0=zz)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, a) and torch.equal(plain, b)
+
+
+def test_forward_state_then_decode():
+    """A prompt's forward hands its final state to decode: the decoded
+    outputs continue the forward over the whole sequence."""
+    w = _wl(198, 2, 4, 1050, 64, 64, "bf16")
+    P = 1000
+    q, k, v = wl.forward_inputs(w)
+    _say(f"prompt forward (N={P}) then {w.N - P} decode steps, bf16")
+    qd, kd, vd = (dev(np.ascontiguousarray(x[:, :, :P]), w.dtype) for x in (q, k, v))
+    out_p, S, Z = la.la_forward_causal_state(qd, kd, vd)
+    steps = []
+    for t in range(P, w.N):
+        qt, kt, vt = (dev(np.ascontiguousarray(x[:, :, t]), w.dtype) for x in (q, k, v))
+        steps.append((qt, kt, vt, la.la_decode_step(qt, kt, vt, S, Z)))
+    torch.cuda.synchronize()
+    ref = oracle.forward_causal(q, k, v)
+    check("prompt out", host(out_p), ref[:, :, :P], w.dtype)
+    check("decoded out", np.stack([host(s[3]) for s in steps], axis=2), ref[:, :, P:], w.dtype)
+
+
+def test_forward_state_full_long_sequence():
+    """Final state of the long-sequence workload (B1 H8 N65536 D=M=64 bf16)."""
+    w = wl.WORKLOADS[4]
+    q, k, v = wl.forward_inputs(w)
+    _say(f"final state, full long-sequence workload B{w.B} H{w.H} N{w.N}")
+    out, S, Z = la.la_forward_causal_state(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    ref, S_ref, Z_ref = oracle.forward_causal(q, k, v, return_state=True)
+    check("out", host(out), ref, w.dtype)
+    check("S_N", host(S), S_ref, w.dtype)
+    check("Z_N", host(Z), Z_ref, w.dtype)
+
+
 def test_forward_deterministic_and_guarded():
     w = _wl(141, 2, 3, 1500, 64, 64, "bf16")
     q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))

@@ -52,6 +52,10 @@ MUTATIONS = [
      [oc.check_backward_vs_quadratic, oc.check_backward_identities]),
     ("decode_normalizer_uses_key", "dd += phi(qq[d]) * ZZ[d];", "dd += phi(kk[d]) * ZZ[d];",
      [oc.check_decode]),
+    ("forward_drops_initial_z",
+     "if (Z_io) memcpy(Z, Z_io + bh * D, (size_t)D * sizeof(double));",
+     "if (Z_io && N < 0) memcpy(Z, Z_io + bh * D, (size_t)D * sizeof(double));",
+     [oc.check_initial_state]),
     ("decode_reads_before_update_of_s",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m];",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m] * (m > 0);",

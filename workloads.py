@@ -104,6 +104,16 @@ def forward_inputs(w: Workload, with_dout: bool = False, seed: int | None = None
     return tuple(out)
 
 
+def start_state(w: Workload, seed: int):
+    """An arbitrary fp32 recurrent state to start a causal forward from:
+    S0 [B, H, D, M] = 4 x standard normal (any sign), Z0 [B, H, D] =
+    5 |standard normal| + 0.5 (positive, so every denominator is positive)."""
+    g = rng(seed)
+    S0 = g.standard_normal((w.B, w.H, w.D, w.M), dtype=np.float32) * np.float32(4.0)
+    Z0 = np.abs(g.standard_normal((w.B, w.H, w.D), dtype=np.float32)) * np.float32(5.0) + np.float32(0.5)
+    return np.ascontiguousarray(S0), np.ascontiguousarray(Z0)
+
+
 class DecodeStream:
     """Per-step decode inputs, drawn in order q_t, k_t, v_t for t = 0, 1, ..."""
 
