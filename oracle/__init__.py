@@ -48,9 +48,10 @@ def _bind(lib):
     lib.orc_forward_causal.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_forward_noncausal.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_backward_causal.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
+    lib.orc_backward_noncausal.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_decode_step.argtypes = [d, d, d, d, d, d, i64, i64, i64, i64]
     for f in ("orc_feature_map", "orc_forward_causal", "orc_forward_noncausal",
-              "orc_backward_causal", "orc_decode_step"):
+              "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step"):
         getattr(lib, f).restype = None
     return lib
 
@@ -140,6 +141,19 @@ def backward_causal(q, k, v, dout, lib=None):
     dk = np.empty_like(k)
     dv = np.empty_like(v)
     lib.orc_backward_causal(_p(q), _p(k), _p(v), _p(g), _p(dq), _p(dk), _p(dv), B, H, N, D, M)
+    return dq, dk, dv
+
+
+def backward_noncausal(q, k, v, dout, lib=None):
+    """Gradients (dQ, dK, dV) of sum(dout * forward_noncausal(q,k,v)) w.r.t. raw q,k,v."""
+    lib = lib or load()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    lib.orc_backward_noncausal(_p(q), _p(k), _p(v), _p(g), _p(dq), _p(dk), _p(dv), B, H, N, D, M)
     return dq, dk, dv
 
 

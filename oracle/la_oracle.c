@@ -255,6 +255,84 @@ void orc_backward_causal(const double *q, const double *k, const double *v,
 }
 
 /*
+ * Non-causal backward.  The derivation of orc_backward_causal with every
+ * token seeing every other (a_ij = qh_i . kh_j for all i, j; [summary] 3.2:
+ * the non-causal form through associativity): S = sum_j kh_j V_j^T and
+ * Z = sum_j kh_j are the full sums, d_i = qh_i . Z, out_i = S^T qh_i / d_i,
+ * g_i = G_i / d_i, h_i = -(G_i . out_i) / d_i, and
+ *   dL/dqh_i = S g_i + h_i Z,
+ *   dL/dkh_j = R V_j + u,   dL/dV_j = R^T kh_j,
+ *   with R = sum_i qh_i g_i^T and u = sum_i h_i qh_i over all i (no prefix:
+ *   every output depends on every key).  dQ = dL/dqh * phi'(Q),
+ *   dK = dL/dkh * phi'(K).
+ */
+void orc_backward_noncausal(const double *q, const double *k, const double *v,
+                            const double *dout, double *dq, double *dk, double *dv,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M, *G = dout + bh * N * M;
+        double *dQ = dq + bh * N * D, *dK = dk + bh * N * D, *dV = dv + bh * N * M;
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)D, sizeof(double));
+        double *R = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *u = (double *)calloc((size_t)D, sizeof(double));
+        double *qh = (double *)malloc((size_t)D * sizeof(double));
+        double *kh = (double *)malloc((size_t)D * sizeof(double));
+        double *g = (double *)malloc((size_t)M * sizeof(double));
+
+        /* the full sums S, Z */
+        for (int64_t j = 0; j < N; ++j)
+            for (int64_t d = 0; d < D; ++d) {
+                const double kj = phi(K[j * D + d]);
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += kj * V[j * M + m];
+                Z[d] += kj;
+            }
+        /* per query: out_i, d_i, g_i, h_i; dQ_i; accumulate R, u */
+        for (int64_t i = 0; i < N; ++i) {
+            double dd = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                qh[d] = phi(Q[i * D + d]);
+                dd += qh[d] * Z[d];
+            }
+            double go = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t d = 0; d < D; ++d) n += qh[d] * S[d * M + m];
+                go += G[i * M + m] * (n / dd);
+                g[m] = G[i * M + m] / dd;
+            }
+            const double h = -go / dd;
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = h * Z[d];
+                for (int64_t m = 0; m < M; ++m) acc += S[d * M + m] * g[m];
+                dQ[i * D + d] = acc * dphi(Q[i * D + d]);
+                for (int64_t m = 0; m < M; ++m) R[d * M + m] += qh[d] * g[m];
+                u[d] += h * qh[d];
+            }
+        }
+        /* per key: dK_j, dV_j */
+        for (int64_t j = 0; j < N; ++j) {
+            for (int64_t d = 0; d < D; ++d) kh[d] = phi(K[j * D + d]);
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = u[d];
+                for (int64_t m = 0; m < M; ++m) acc += R[d * M + m] * V[j * M + m];
+                dK[j * D + d] = acc * dphi(K[j * D + d]);
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc += R[d * M + m] * kh[d];
+                dV[j * M + m] = acc;
+            }
+        }
+        free(S); free(Z); free(R); free(u); free(qh); free(kh); free(g);
+    }
+}
+
+/*
  * One RNN-style decode step for B*H independent streams ([review] "Proposed
  * method", attention memory s and normalizer memory z; [summary] 3.3.2, 3.4;
  * [deck] slide 4): S += phi(k) v^T, Z += phi(k), then

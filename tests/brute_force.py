@@ -50,16 +50,20 @@ def forward(q, k, v, causal: bool = True):
 
 
 def backward_causal(q, k, v, g):
+    return backward(q, k, v, g, causal=True)
+
+
+def backward(q, k, v, g, causal: bool = True):
     q, k, v, g = (np.asarray(x, np.float64) for x in (q, k, v, g))
     qh, kh = phi(q), phi(k)
-    a = similarity(q, k, True)
+    a = similarity(q, k, causal)
     d = a.sum(-1, keepdims=True)
     o = (a @ v) / d
     # dL/da_ij = G_i . (V_j - O_i) / d_i, masked to j <= i
     gv = g @ np.swapaxes(v, -1, -2)                       # G_i . V_j
     go = (g * o).sum(-1, keepdims=True)                   # G_i . O_i
     n = a.shape[-1]
-    mask = np.tril(np.ones((n, n)))
+    mask = np.tril(np.ones((n, n))) if causal else np.ones((n, n))
     da = (gv - go) / d * mask
     dqh = da @ kh
     dkh = np.swapaxes(da, -1, -2) @ qh

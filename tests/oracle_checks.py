@@ -241,6 +241,56 @@ def check_backward_identities(lib):
     assert np.abs(dq).max() > 1e-3 and np.abs(dk).max() > 1e-3
 
 
+def check_backward_noncausal(lib):
+    """Non-causal backward: the quadratic gradient without a mask, central
+    differences of the oracle's own non-causal forward, torch fp64 autograd of
+    the brute-force form, and the identities of the causal case, which hold
+    with the mask removed too."""
+    import torch
+
+    for s, (B, H, N, D, M) in enumerate([(1, 2, 64, 8, 6), (2, 1, 33, 3, 9), (1, 1, 1, 4, 4), (1, 1, 90, 32, 32)]):
+        q, k, v, g = (_rand(300 + 4 * s + i, B, H, N, x) for i, x in enumerate((D, D, M, M)))
+        dq, dk, dv = oracle.backward_noncausal(q, k, v, g, lib=lib)
+        rq, rk, rv = bf.backward(q, k, v, g, causal=False)
+        if N == 1:
+            assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14 and _rel(dv, g) < 1e-15
+            continue
+        assert _rel(dq, rq) < 1e-11 and _rel(dk, rk) < 1e-11 and _rel(dv, rv) < 1e-11, (B, H, N, D, M)
+        o = oracle.forward_noncausal(q, k, v, lib=lib)
+        assert _rel(dv.sum(2), g.sum(2)) < 1e-12                       # shift of V
+        assert _rel((v * dv).sum((2, 3)), (g * o).sum((2, 3))) < 1e-11   # linear in V
+        wq, wk = 1.0 + np.maximum(q, 0.0), 1.0 + np.maximum(k, 0.0)
+        assert np.abs((dq * wq).sum(-1)).max() < 1e-10 * np.abs(dq * wq).sum(-1).max()
+        assert np.abs((dk * wk).sum((2, 3))).max() < 1e-10 * np.abs(dk * wk).sum()
+
+    B, H, N, D, M = 1, 1, 6, 3, 2
+    q, k, v, g = _rand(320, B, H, N, D), _rand(321, B, H, N, D), _rand(322, B, H, N, M), _rand(323, B, H, N, M)
+    dq, dk, dv = oracle.backward_noncausal(q, k, v, g, lib=lib)
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        it = np.nditer(num, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            p = [x.copy() for x in (q, k, v)]
+            m_ = [x.copy() for x in (q, k, v)]
+            p[which][idx] += eps
+            m_[which][idx] -= eps
+            num[idx] = ((oracle.forward_noncausal(*p, lib=lib) - oracle.forward_noncausal(*m_, lib=lib)) * g).sum() \
+                / (2 * eps)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-8), (which, np.abs(grad - num).max())
+
+    B, H, N, D, M = 2, 2, 40, 6, 5
+    arrs = [_rand(330 + i, B, H, N, x) for i, x in enumerate((D, D, M, M))]
+    tq, tk, tv, tg = (torch.tensor(a, dtype=torch.float64) for a in arrs)
+    tq.requires_grad_(True); tk.requires_grad_(True); tv.requires_grad_(True)
+    a = (torch.nn.functional.elu(tq) + 1.0) @ (torch.nn.functional.elu(tk) + 1.0).transpose(-1, -2).contiguous()
+    out = (a @ tv) / a.sum(-1, keepdim=True)
+    (out * tg).sum().backward()
+    dq, dk, dv = oracle.backward_noncausal(*arrs, lib=lib)
+    assert _rel(dq, tq.grad.numpy()) < 1e-11 and _rel(dk, tk.grad.numpy()) < 1e-11 and _rel(dv, tv.grad.numpy()) < 1e-11
+
+
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,
               check_initial_state, check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
-              check_backward_identities]
+              check_backward_identities, check_backward_noncausal]

@@ -56,6 +56,14 @@ MUTATIONS = [
      "if (Z_io) memcpy(Z, Z_io + bh * D, (size_t)D * sizeof(double));",
      "if (Z_io && N < 0) memcpy(Z, Z_io + bh * D, (size_t)D * sizeof(double));",
      [oc.check_initial_state]),
+    ("noncausal_backward_drops_u",
+     "                double acc = u[d];",
+     "                double acc = 0.0 * u[d];",
+     [oc.check_backward_noncausal]),
+    ("noncausal_backward_h_sign",
+     "            const double h = -go / dd;",
+     "            const double h = go / dd;",
+     [oc.check_backward_noncausal]),
     ("decode_reads_before_update_of_s",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m];",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m] * (m > 0);",
