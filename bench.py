@@ -15,7 +15,8 @@ In the same run, each timed with HIP events on the stream the library launches
 on, and reported next to the headline:
   * decode: 3072 sequential la_decode_step calls for B=256 streams x H=8 heads,
     D=M=64 (steps/s), eager launches and a replayed HIP graph of the same calls;
-  * backward: la_backward_causal on the long-sequence workload;
+  * backward: la_backward_causal and la_backward_noncausal on the long-sequence
+    workload;
   * non-causal forward on the long-sequence workload;
   * the causal forward of the three smaller workloads;
   * optionally (--sweep) the causal forward for N = 512 .. 65536.
@@ -277,7 +278,24 @@ def main():
         results["backward"]["median"] = {"reps": reps, "alternating_ms": t_alt * 1e3, "cold_ms": t_cold * 1e3}
         log(f"causal backward: {t / nb * 1e3:.4f} ms/call; medians over {reps}: alternating "
             f"{t_alt * 1e3:.4f}, cold {t_cold * 1e3:.4f} ms")
-        del dq, dk, dv, ws_b
+        ws_nb = torch.empty(la.la_workspace_size(la.LA_OP_BWD_NONCAUSAL, w4.B, w4.H, w4.N, w4.D, w4.M,
+                                                 torch.bfloat16), dtype=torch.uint8, device=dev)
+
+        def bwd_nc(i):
+            q, k, v, g = sets[i % 2]
+            st = lib.la_backward_noncausal(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), dq.data_ptr(),
+                                           dk.data_ptr(), dv.data_ptr(), w4.B, w4.H, w4.N, w4.D, w4.M,
+                                           la.LA_DTYPE_BF16, ws_nb.data_ptr(), ws_nb.numel(), sptr)
+            if st != 0:
+                raise la.LAError("backward_noncausal", st)
+
+        for i in range(2):
+            bwd_nc(i)
+        t = time_events(bwd_nc, nb)
+        results["backward_noncausal"] = dict(ms_per_call=t / nb * 1e3, tok_heads_per_s=tok_heads * nb / t,
+                                             hbm_frac=bwd_bytes / (t / nb) / 1e9 / HBM_PEAK_GBS)
+        log(f"non-causal backward: {t / nb * 1e3:.4f} ms/call")
+        del dq, dk, dv, ws_b, ws_nb
     if a.only in ("all",):
         for i in range(2):
             fwd(i, causal=False)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
 
@@ -60,7 +60,12 @@ typedef enum {
     LA_ERR_HIP = 4               /* a kernel launch failed */
 } la_status_t;
 
-typedef enum { LA_OP_FWD_CAUSAL = 0, LA_OP_FWD_NONCAUSAL = 1, LA_OP_BWD_CAUSAL = 2 } la_op_t;
+typedef enum {
+    LA_OP_FWD_CAUSAL = 0,     /* la_forward_causal, la_forward_causal_state */
+    LA_OP_FWD_NONCAUSAL = 1,  /* la_forward_noncausal */
+    LA_OP_BWD_CAUSAL = 2,     /* la_backward_causal */
+    LA_OP_BWD_NONCAUSAL = 3   /* la_backward_noncausal */
+} la_op_t;
 
 /*
  * Causal forward ([deck] slide 4; [review] "Proposed method"; [summary] 3.3,
@@ -137,6 +142,25 @@ la_status_t la_backward_causal(const void *q, const void *k, const void *v, cons
                                int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                                la_dtype_t dt, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/*
+ * Non-causal backward: the gradients of la_forward_noncausal with every sum
+ * over the whole sequence ([summary] 3.2: the non-causal form through
+ * associativity; 3.3.1 and appendix A give the causal case, whose
+ * derivation carries over with the mask removed).  With S, Z the full sums,
+ * d_i = phi(Q_i) . Z, g_i = dout_i / d_i, h_i = -(dout_i . out_i) / d_i:
+ *   dL/dphi(Q_i) = S g_i + h_i Z,
+ *   dL/dphi(K_j) = R V_j + u,  dv_j = R^T phi(K_j),
+ *   R = sum_i phi(Q_i) g_i^T,  u = sum_i h_i phi(Q_i)  (all i),
+ * and dq = dL/dphi(Q) * phi'(Q), dk = dL/dphi(K) * phi'(K).
+ * Arguments, layouts and errors as la_backward_causal; workspace sized by
+ * la_workspace_size(LA_OP_BWD_NONCAUSAL, ...).
+ */
+la_status_t la_backward_noncausal(const void *q, const void *k, const void *v, const void *dout,
+                                  void *dq, void *dk, void *dv,
+                                  int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                  la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * One RNN-style decode step for B*H independent streams ([review] "Proposed

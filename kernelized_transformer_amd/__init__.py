@@ -12,6 +12,7 @@ Functions carry the C names:
   la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None)
   la_forward_noncausal(q, k, v, out=None, workspace=None)
   la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
+  la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_decode_step(q, k, v, S, Z, out=None)
   la_workspace_size(op, B, H, N, D, M, dtype)
   la_status_string(status), la_abi_version()
@@ -23,12 +24,13 @@ import os
 
 import torch
 
-__all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal", "la_decode_step",
+__all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
+           "la_decode_step",
            "la_workspace_size", "la_status_string", "la_abi_version", "LAError", "lib_path", "load",
-           "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
+           "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
-LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL = 0, 1, 2
+LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3
 _DT = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,10 +58,11 @@ def load():
     lib.la_forward_causal.argtypes = fwd
     lib.la_forward_noncausal.argtypes = fwd
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_backward_noncausal.argtypes = lib.la_backward_causal.argtypes
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal",
-              "la_decode_step"):
+              "la_backward_noncausal", "la_decode_step"):
         getattr(lib, f).restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
     lib.la_workspace_size.restype = sz
@@ -173,6 +176,15 @@ def la_forward_noncausal(q, k, v, out=None, workspace=None):
 
 def la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None):
     """Gradients of sum(dout * la_forward_causal(q, k, v)); returns (dq, dk, dv)."""
+    return _backward("la_backward_causal", LA_OP_BWD_CAUSAL, q, k, v, dout, dq, dk, dv, workspace)
+
+
+def la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of sum(dout * la_forward_noncausal(q, k, v)); returns (dq, dk, dv)."""
+    return _backward("la_backward_noncausal", LA_OP_BWD_NONCAUSAL, q, k, v, dout, dq, dk, dv, workspace)
+
+
+def _backward(func, op, q, k, v, dout, dq, dk, dv, workspace):
     dev = _dev(q, k, v, dout)
     if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in _DT:
         raise ValueError("q, k, v, dout must share dtype float32 or bfloat16")
@@ -182,11 +194,11 @@ def la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _dev(q, dq, dk, dv)
-    ws, wsb = _ws(LA_OP_BWD_CAUSAL, B, H, N, D, M, q.dtype, workspace, dev)
-    st = load().la_backward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                                   dk.data_ptr(), dv.data_ptr(), B, H, N, D, M, _DT[q.dtype], ws.data_ptr(), wsb,
-                                   _stream(dev))
-    _check("la_backward_causal", st)
+    ws, wsb = _ws(op, B, H, N, D, M, q.dtype, workspace, dev)
+    st = getattr(load(), func)(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                               dk.data_ptr(), dv.data_ptr(), B, H, N, D, M, _DT[q.dtype], ws.data_ptr(), wsb,
+                               _stream(dev))
+    _check(func, st)
     return dq, dk, dv
 
 

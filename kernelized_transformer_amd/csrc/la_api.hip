@@ -136,9 +136,13 @@ la_status_t la_forward_noncausal(const void *q, const void *k, const void *v, vo
     return forward_common(false, q, k, v, out, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
 }
 
-la_status_t la_backward_causal(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
-                               void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt,
-                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+} // extern "C"
+
+namespace {
+
+la_status_t backward_common(bool causal, const void *q, const void *k, const void *v, const void *dout, void *dq,
+                            void *dk, void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                            la_dtype_t dt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     la_status_t st = check_shape(B, H, N, D, M, dt);
     if (st != LA_OK) return st;
     const size_t es = esize(dt);
@@ -149,12 +153,28 @@ la_status_t la_backward_causal(const void *q, const void *k, const void *v, cons
                        span(dv, size_t(BH * N * M) * es)};
     if ((st = check_buffers(in, 4, o, 3)) != LA_OK) return st;
     const Span all[7] = {in[0], in[1], in[2], in[3], o[0], o[1], o[2]};
-    if ((st = check_workspace(workspace, workspace_bytes, la::backward_workspace_bytes(BH, N, D, M, es), all, 7)) !=
-        LA_OK)
-        return st;
-    const hipError_t e = la::launch_backward(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, dout, dq, dk, dv, BH, N, D, M,
-                                             static_cast<float *>(workspace), stream);
+    const size_t need = causal ? la::backward_workspace_bytes(BH, N, D, M, es)
+                               : la::backward_noncausal_workspace_bytes(BH, N, D, M);
+    if ((st = check_workspace(workspace, workspace_bytes, need, all, 7)) != LA_OK) return st;
+    const hipError_t e = la::launch_backward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, dout, dq, dk, dv, BH, N, D,
+                                             M, static_cast<float *>(workspace), stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+la_status_t la_backward_causal(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                               void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return backward_common(true, q, k, v, dout, dq, dk, dv, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
+}
+
+la_status_t la_backward_noncausal(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                                  void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return backward_common(false, q, k, v, dout, dq, dk, dv, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
 }
 
 la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S, float *Z, void *out, int64_t B,
@@ -180,6 +200,8 @@ size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D,
         return la::forward_workspace_bytes(B * H, N, D, M);
     case LA_OP_BWD_CAUSAL:
         return la::backward_workspace_bytes(B * H, N, D, M, esize(dt));
+    case LA_OP_BWD_NONCAUSAL:
+        return la::backward_noncausal_workspace_bytes(B * H, N, D, M);
     }
     return 0;
 }

@@ -25,6 +25,9 @@
 //   3. reverse scan            -> R_aug after the end of every segment;
 //   4. k_bwd_dkdv  (reverse direction): walk the chunks backwards carrying
 //      R_aug, write dK and dV.
+// The non-causal backward is the same with every sum taken over the whole
+// sequence (a_ij for all i, j): 1. gives the full S_aug, 2. reads only Q and
+// dout against it, 3. totals R_aug, 4. reads only K and V against it.
 #include "la_chunk.h"
 #include "la_internal.h"
 
@@ -41,7 +44,10 @@ template <int D, int M>
 constexpr int kBwdTile = 16 * ((D > M ? D : M) + kStagePad);
 
 // ---- pass 2: forward direction --------------------------------------------
-template <typename T, int D, int M>
+// Non-causal (CAUSAL = false): every query sees the full sums S_aug (record 0
+// of the head), so K, V are not read, there is no intra-chunk term and no
+// state to carry, and g, h are not stored (gbuf, hbuf unused).
+template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                const T *__restrict__ v, const T *__restrict__ dout,
                                                T *__restrict__ dq, const float *__restrict__ wsS,
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
     T *GB = gbuf + bh * N * M;
     float *HB = hbuf + bh * N;
 
-    const float *srec = wsS + (bh * nseg + seg) * rec;
+    const float *srec = wsS + (bh * nseg + (CAUSAL ? seg : 0)) * rec;
     f32x4 St[DT][MT + 1];      // S_aug, rows d
     f32x4 Ra[DT][MT + 1];      // this segment's sum_i qh_i gh_i^T, rows d
     state_load<D, M>(St, srec);
@@ -77,22 +83,28 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
     load_chunk<T, D, BTT>(rq, Q, t_begin, t_end);
-    load_chunk<T, D, BTT>(rk, K, t_begin, t_end);
-    load_chunk<T, M, BTT>(rv, V, t_begin, t_end);
+    if (CAUSAL) {
+        load_chunk<T, D, BTT>(rk, K, t_begin, t_end);
+        load_chunk<T, M, BTT>(rv, V, t_begin, t_end);
+    }
     load_chunk<T, M, BTT>(rg, G, t_begin, t_end);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += BCH) {
         Fr Qn[BTT][DT], Kn[BTT][DT], Vn[BTT][MT];
         phi_frags<T, D, BTT>(Qn, rq, t0, t_end);
-        phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
-        raw_frags<T, M, BTT>(Vn, rv, t0, t_end);
+        if (CAUSAL) {
+            phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
+            raw_frags<T, M, BTT>(Vn, rv, t0, t_end);
+        }
         f32x4 qraw[DT], graw[MT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) qraw[dt] = IO<T>::to_f32(rq[0][dt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) graw[mt] = IO<T>::to_f32(rg[0][mt]);
         load_chunk<T, D, BTT>(rq, Q, t0 + BCH, t_end);
-        load_chunk<T, D, BTT>(rk, K, t0 + BCH, t_end);
-        load_chunk<T, M, BTT>(rv, V, t0 + BCH, t_end);
+        if (CAUSAL) {
+            load_chunk<T, D, BTT>(rk, K, t0 + BCH, t_end);
+            load_chunk<T, M, BTT>(rv, V, t0 + BCH, t_end);
+        }
         load_chunk<T, M, BTT>(rg, G, t0 + BCH, t_end);
         const int64_t t = t0 + c;   // this lane's query token
         const bool valid = t < t_end;
@@ -108,23 +120,28 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         transpose_frags<DT, MT + 1>(SFT, SF, stage);
 
         Fr KT[BTT][DT], VT[BTT][MT];
-        transpose_frags<DT, BTT>(KT, Kn, stage);
-        transpose_frags<MT, BTT>(VT, Vn, stage + stage_elems<DT, BTT>());
+        if (CAUSAL) {
+            transpose_frags<DT, BTT>(KT, Kn, stage);
+            transpose_frags<MT, BTT>(VT, Vn, stage + stage_elems<DT, BTT>());
+        }
 
         // recompute out^T (and den in the normalizer block) as the forward does
         f32x4 Ot[MT + 1];
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        Fr PT = frag_zero<Fr>();
+        if (CAUSAL) {
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[0][dt], Kn[0][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
+            for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[0][dt], Kn[0][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-        const Fr PT = IO<T>::to_frag(p);
+            for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+            PT = IO<T>::to_frag(p);
+        }
 #pragma unroll
         for (int mt = 0; mt <= MT; ++mt) {
             Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt], SF[mt][dt], SF[mt][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
-            mma1(Ot[mt], mt < MT ? VT[0][mt] : ones, PT);
+            if (CAUSAL) mma1(Ot[mt], mt < MT ? VT[0][mt] : ones, PT);
         }
         const float den = __shfl(Ot[MT][0], c);
         const float inv = valid ? __builtin_amdgcn_rcpf(den) : 0.f;
@@ -145,33 +162,36 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<T>::to_frag(gv[mt]);
         Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (CAUSAL && sizeof(T) == 2) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) tile_put_bf16<M>(otile, mt, IO<bf16>::from_f32(gv[mt]));
             tile_flush_bf16<M>((bf16 *)GB, t0, t_end, otile);
-        } else if (valid) {
+        } else if (CAUSAL && valid) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) store4<T>(GB + t * M + 16 * mt + 4 * g, IO<T>::from_f32(gv[mt]));
         }
-        if (valid && g == 0) HB[t] = h;
+        if (CAUSAL && valid && g == 0) HB[t] = h;
 
         // dA^T[j][i] = vh_j . gh_i, masked to j <= i
-        f32x4 da = {0.f, 0.f, 0.f, 0.f};
+        Fr dAT = frag_zero<Fr>();
+        if (CAUSAL) {
+            f32x4 da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt + 1 <= MT; mt += 2) {
-            const Fr a1 = (mt + 1 < MT) ? Vn[0][mt + 1] : k0ones;
-            mma2(da, Vn[0][mt], a1, Gn[0][mt], Gn[0][mt + 1]);
+            for (int mt = 0; mt + 1 <= MT; mt += 2) {
+                const Fr a1 = (mt + 1 < MT) ? Vn[0][mt + 1] : k0ones;
+                mma2(da, Vn[0][mt], a1, Gn[0][mt], Gn[0][mt + 1]);
+            }
+            if ((MT & 1) == 0) mma1(da, k0ones, Gn[0][MT]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
+            dAT = IO<T>::to_frag(da);
         }
-        if ((MT & 1) == 0) mma1(da, k0ones, Gn[0][MT]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
-        const Fr dAT = IO<T>::to_frag(da);
 
         // dL/dqh^T[d][i] = sum_j kh[j][d] dA^T[j][i] + sum_m' S_aug[d][m'] gh[i][m']
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma1(acc, KT[0][dt], dAT);
+            if (CAUSAL) mma1(acc, KT[0][dt], dAT);
 #pragma unroll
             for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, SFT[mt][dt], SFT[mt + 1][dt], Gn[0][mt], Gn[0][mt + 1]);
             if ((MT & 1) == 0) mma1(acc, SFT[MT][dt], Gn[0][MT]);
@@ -193,13 +213,16 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
             for (int mt = 0; mt <= MT; ++mt) mma1(Ra[dt][mt], QT[0][dt], GT[0][mt]);
 
         // carry S_aug past this chunk
-        state_accumulate<Fr, D, M, BTT>(St, KT, VT);
+        if (CAUSAL) state_accumulate<Fr, D, M, BTT>(St, KT, VT);
     }
     state_store<D, M>(wsR + (bh * nseg + seg) * rec, Ra);
 }
 
 // ---- pass 4: reverse direction --------------------------------------------
-template <typename T, int D, int M>
+// Non-causal (CAUSAL = false): every key sees the full sums R_aug (record 0 of
+// the head), so Q, g, h are not read, there is no intra-chunk term and no
+// sum to carry.
+template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const T *__restrict__ k,
                                                  const T *__restrict__ v, const T *__restrict__ gbuf,
                                                  const float *__restrict__ hbuf, T *__restrict__ dk,
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     T *DK = dk + bh * N * D;
     T *DV = dv + bh * N * M;
 
-    const float *rrec = wsR + (bh * nseg + seg) * rec;
+    const float *rrec = wsR + (bh * nseg + (CAUSAL ? seg : 0)) * rec;
     f32x4 Rr[DT][MT + 1];      // R_aug = [R | u], rows d
     state_load<D, M>(Rr, rrec);
 
@@ -233,17 +256,19 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
     float rh;
     auto load_all = [&](int64_t t0) {
-        load_chunk<T, D, BTT>(rq, Q, t0, t_end);
+        if (CAUSAL) load_chunk<T, D, BTT>(rq, Q, t0, t_end);
         load_chunk<T, D, BTT>(rk, K, t0, t_end);
         load_chunk<T, M, BTT>(rv, V, t0, t_end);
-        load_chunk<T, M, BTT>(rg, GB, t0, t_end);
-        rh = (t0 + c < t_end) ? HB[t0 + c] : 0.f;
+        if (CAUSAL) {
+            load_chunk<T, M, BTT>(rg, GB, t0, t_end);
+            rh = (t0 + c < t_end) ? HB[t0 + c] : 0.f;
+        }
     };
     load_all(t_begin + (nch - 1) * BCH);
     for (int64_t ci = nch - 1; ci >= 0; --ci) {
         const int64_t t0 = t_begin + ci * BCH;
         Fr Qn[BTT][DT], Kn[BTT][DT], Vn[BTT][MT + 1], Gn[BTT][MT + 1];
-        phi_frags<T, D, BTT>(Qn, rq, t0, t_end);
+        if (CAUSAL) phi_frags<T, D, BTT>(Qn, rq, t0, t_end);
         phi_frags<T, D, BTT>(Kn, rk, t0, t_end);
         {
             Fr tmp[BTT][MT];
@@ -251,10 +276,12 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) Vn[0][mt] = tmp[0][mt];
             Vn[0][MT] = k0ones;
-            raw_frags<T, M, BTT>(tmp, rg, t0, t_end);
+            if (CAUSAL) {
+                raw_frags<T, M, BTT>(tmp, rg, t0, t_end);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = tmp[0][mt];
-            Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
+                for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = tmp[0][mt];
+                Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
+            }
         }
         f32x4 kraw[DT];
 #pragma unroll
@@ -273,29 +300,33 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
         transpose_frags<DT, MT + 1>(RFT, RF, stage);
 
         Fr QT[BTT][DT], GT[BTT][MT + 1];
-        transpose_frags<DT, BTT>(QT, Qn, stage);
-        transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
+        Fr Pf = frag_zero<Fr>(), dAf = frag_zero<Fr>();
+        if (CAUSAL) {
+            transpose_frags<DT, BTT>(QT, Qn, stage);
+            transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
 
-        // P[i][j] = qh_i . kh_j and dA[i][j] = gh_i . vh_j, masked to i >= j
-        f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+            // P[i][j] = qh_i . kh_j and dA[i][j] = gh_i . vh_j, masked to i >= j
+            f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dt = 0; dt < DT; dt += 2) mma2(p, Qn[0][dt], Qn[0][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
+            for (int dt = 0; dt < DT; dt += 2) mma2(p, Qn[0][dt], Qn[0][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
 #pragma unroll
-        for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(da, Gn[0][mt], Gn[0][mt + 1], Vn[0][mt], Vn[0][mt + 1]);
-        if ((MT & 1) == 0) mma1(da, Gn[0][MT], Vn[0][MT]);
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(da, Gn[0][mt], Gn[0][mt + 1], Vn[0][mt], Vn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(da, Gn[0][MT], Vn[0][MT]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool keep = 4 * g + r >= c;
-            p[r] = keep ? p[r] : 0.f;
-            da[r] = keep ? da[r] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = 4 * g + r >= c;
+                p[r] = keep ? p[r] : 0.f;
+                da[r] = keep ? da[r] : 0.f;
+            }
+            Pf = IO<T>::to_frag(p);
+            dAf = IO<T>::to_frag(da);
         }
-        const Fr Pf = IO<T>::to_frag(p), dAf = IO<T>::to_frag(da);
 
         // dL/dkh^T[d][j] = sum_i qh[i][d] dA[i][j] + sum_m' R_aug[d][m'] vh[j][m']
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma1(acc, QT[0][dt], dAf);
+            if (CAUSAL) mma1(acc, QT[0][dt], dAf);
 #pragma unroll
             for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, RFT[mt][dt], RFT[mt + 1][dt], Vn[0][mt], Vn[0][mt + 1]);
             if ((MT & 1) == 0) mma1(acc, RFT[MT][dt], Vn[0][MT]);
@@ -310,7 +341,7 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma1(acc, GT[0][mt], Pf);
+            if (CAUSAL) mma1(acc, GT[0][mt], Pf);
 #pragma unroll
             for (int dt = 0; dt < DT; dt += 2) mma2(acc, RF[mt][dt], RF[mt][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
             if constexpr (sizeof(T) == 2)
@@ -321,16 +352,18 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
         if constexpr (sizeof(T) == 2) tile_flush_bf16<M>((bf16 *)DV, t0, t_end, otile);
 
         // carry R_aug past this chunk, towards earlier tokens
+        if (CAUSAL) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int mt = 0; mt <= MT; ++mt) mma1(Rr[dt][mt], QT[0][dt], GT[0][mt]);
+                for (int mt = 0; mt <= MT; ++mt) mma1(Rr[dt][mt], QT[0][dt], GT[0][mt]);
+        }
     }
 }
 
 template <typename T, int D, int M>
-static hipError_t run_backward(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
-                               void *dv, int64_t BH, int64_t N, float *ws, hipStream_t s) {
+static hipError_t run_backward(bool causal, const void *q, const void *k, const void *v, const void *dout, void *dq,
+                               void *dk, void *dv, int64_t BH, int64_t N, float *ws, hipStream_t s) {
     const SegPlan p = make_plan(BH, N, D, M);
     const BwdLayout L = backward_layout(BH, N, D, M, sizeof(T));
     float *wsS = ws;
@@ -341,32 +374,45 @@ static hipError_t run_backward(const void *q, const void *k, const void *v, cons
     const int dt = sizeof(T) == 4 ? 0 : 1;
     hipError_t e = launch_segment_state(dt, k, v, wsS, BH, N, D, M, s);
     if (e != hipSuccess) return e;
+    if (!causal) {   // full sums S_aug, then R_aug, each into record 0 of the head
+        if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_dq<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, (T *)nullptr,
+                           (float *)nullptr, N, p.nseg, p.seg_tokens, p.rec);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)nullptr, (const float *)nullptr, (T *)dk, (T *)dv,
+                           (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
+        return hipGetLastError();
+    }
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_dq<T, D, M>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
+    hipLaunchKernelGGL((k_bwd_dq<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
                        (const T *)dout, (T *)dq, (const float *)wsS, wsR, gbuf, hbuf, N, p.nseg, p.seg_tokens, p.rec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_dkdv<T, D, M>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
+    hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
                        (const T *)gbuf, (const float *)hbuf, (T *)dk, (T *)dv, (const float *)wsR, N, p.nseg,
                        p.seg_tokens, p.rec);
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t run_backward_t(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
-                                 void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s) {
-    if (D == 32 && M == 32) return run_backward<T, 32, 32>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
-    if (D == 32 && M == 64) return run_backward<T, 32, 64>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
-    if (D == 64 && M == 32) return run_backward<T, 64, 32>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
-    if (D == 64 && M == 64) return run_backward<T, 64, 64>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+static hipError_t run_backward_t(bool causal, const void *q, const void *k, const void *v, const void *dout,
+                                 void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+                                 hipStream_t s) {
+    if (D == 32 && M == 32) return run_backward<T, 32, 32>(causal, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 32 && M == 64) return run_backward<T, 32, 64>(causal, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 32) return run_backward<T, 64, 32>(causal, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 64) return run_backward<T, 64, 64>(causal, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_backward(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq,
-                           void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+hipError_t launch_backward(bool causal, int dt, const void *q, const void *k, const void *v, const void *dout,
+                           void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
                            hipStream_t s) {
-    if (dt == 0) return run_backward_t<float>(q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
-    return run_backward_t<bf16>(q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+    if (dt == 0) return run_backward_t<float>(causal, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+    return run_backward_t<bf16>(causal, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
 }
 
 } // namespace la

@@ -134,6 +134,11 @@ inline size_t backward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t
     return backward_layout(BH, N, D, M, esize).total;
 }
 
+// The non-causal backward keeps only the two record arrays (no g, h).
+inline size_t backward_noncausal_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
+    return 2 * backward_layout(BH, N, D, M, 4).states;
+}
+
 // Optional fp32 state of the causal forward, [BH][D][M] and [BH][D] (the
 // decode layout): s0/z0 start the recurrence (null: zero), s1/z1 receive the
 // state after the last token (null: not written); s1 may equal s0.
@@ -152,8 +157,8 @@ hipError_t launch_segment_state(int dt, const void *k, const void *v, float *ws,
 // 2: exclusive suffix (sum of the later segments).
 hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, const float *init, float *fin,
                        hipStream_t s);
-hipError_t launch_backward(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq,
-                           void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+hipError_t launch_backward(bool causal, int dt, const void *q, const void *k, const void *v, const void *dout,
+                           void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
                            hipStream_t s);
 hipError_t launch_decode(int dt, const void *q, const void *k, const void *v, float *S, float *Z, void *out,
                          int64_t BH, int64_t D, int64_t M, hipStream_t s);

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal",
-              "la_decode_step", "la_workspace_size", "la_status_string", "la_abi_version"):
+              "la_backward_noncausal", "la_decode_step", "la_workspace_size", "la_status_string", "la_abi_version"):
         assert f in fns
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 2
+    assert la.la_abi_version() == 3
     names = [la.la_status_string(s) for s in range(5)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
     assert la.la_status_string(99) == "LA_ERR_UNKNOWN"
@@ -54,6 +54,11 @@ def test_workspace_size():
     c = f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
     assert c > 0 and c % 256 == 0 and c >= 2 * (32 * 32 + 32) * 4
     assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32) > 2 * n
+    # non-causal backward: two record arrays, no per-token buffers
+    nb = f(la.LA_OP_BWD_NONCAUSAL, 1, 2, 256, 32, 32, torch.float32)
+    assert nb > 0 and nb % 256 == 0 and nb < f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
+    assert f(la.LA_OP_BWD_NONCAUSAL, 1, 8, 65536, 64, 64, torch.bfloat16) < 64 * 2 ** 20
+    assert f(7, 1, 2, 256, 32, 32, torch.float32) == 0                        # unknown op
     assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) == 0     # unsupported D
     # grows linearly in N at fixed segment count ceiling
@@ -115,14 +120,18 @@ def test_backward_and_decode_argument_errors():
     base = [FAKE + (i << 24) for i in range(8)]
     ok = dict(B=1, H=1, N=8, D=32, M=32, dt=1)
 
-    def bwd(ptrs, B=1, H=1, N=8, D=32, M=32, dt=1, ws=base[7], wsb=0):
-        return lib.la_backward_causal(*ptrs, B, H, N, D, M, dt, ws, wsb, None)
+    for fn in ("la_backward_causal", "la_backward_noncausal"):
+        def bwd(ptrs, B=1, H=1, N=8, D=32, M=32, dt=1, ws=base[7], wsb=0):
+            return getattr(lib, fn)(*ptrs, B, H, N, D, M, dt, ws, wsb, None)
 
-    assert bwd(base[:7]) == 3                                   # no workspace bytes
-    assert bwd([0] + base[1:7]) == 1
-    assert bwd(base[:4] + [base[0], base[5], base[6]]) == 1     # dq aliases q
-    assert bwd(base[:4] + [base[4], base[4], base[6]]) == 1     # dq aliases dk
-    assert bwd(base[:7], D=128) == 2
+        assert bwd(base[:7]) == 3                                   # no workspace bytes
+        assert bwd([0] + base[1:7]) == 1
+        assert bwd(base[:4] + [base[0], base[5], base[6]]) == 1     # dq aliases q
+        assert bwd(base[:4] + [base[4], base[4], base[6]]) == 1     # dq aliases dk
+        assert bwd(base[:3] + [base[6]] + base[4:7]) == 1           # dv aliases dout
+        assert bwd(base[:7], D=128) == 2
+        assert bwd(base[:7], N=0) == 1
+        assert bwd(base[:7], ws=base[2], wsb=1 << 20) == 3          # workspace overlaps v
     assert ok
 
     def dec(q=base[0], k=base[1], v=base[2], S=base[3], Z=base[4], out=base[5], B=2, H=2, D=64, M=64, dt=1):

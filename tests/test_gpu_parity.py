@@ -144,6 +144,37 @@ def test_backward_causal(name, w):
     check(f"dv[{name}]", host(dv), rv, w.dtype)
 
 
+BWD_NC_CASES = [
+    ("w1", wl.WORKLOADS[1]),
+    ("w3", wl.WORKLOADS[3]),
+    ("w4_full", wl.WORKLOADS[4]),
+    ("n1_bf16", _wl(201, 2, 2, 1, 64, 64, "bf16")),
+    ("n17_d32m64_f32", _wl(202, 2, 3, 17, 32, 64, "f32")),
+    ("n50_d64m32_bf16", _wl(203, 1, 3, 50, 64, 32, "bf16")),
+    ("n3001_ragged_f32", _wl(204, 1, 2, 3001, 64, 64, "f32")),
+    ("n100000_many_segments", _wl(205, 1, 1, 100000, 32, 32, "bf16")),
+]
+
+
+@pytest.mark.parametrize("name,w", BWD_NC_CASES, ids=[c[0] for c in BWD_NC_CASES])
+def test_backward_noncausal(name, w):
+    q, k, v, g = wl.forward_inputs(w, with_dout=True)
+    _say(f"backward non-causal {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    dq, dk, dv = la.la_backward_noncausal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), dev(g, w.dtype))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_noncausal(q, k, v, g)
+    if w.N == 1:
+        # out_1 = V_1: dQ = dK = 0 as the difference of two equal terms (S g and
+        # h Z, each of order |dout| |V|), formed from I/O-precision operands
+        scale = TOL[w.dtype] * np.abs(g).max() * np.abs(v).max()
+        assert np.abs(host(dq)).max() <= scale and np.abs(host(dk)).max() <= scale
+        check(f"dv[{name}]", host(dv), rv, w.dtype)
+        return
+    check(f"dq[{name}]", host(dq), rq, w.dtype)
+    check(f"dk[{name}]", host(dk), rk, w.dtype)
+    check(f"dv[{name}]", host(dv), rv, w.dtype)
+
+
 def _decode_run(w, steps, sample=None):
     stream = wl.DecodeStream(w)
     qs, ks, vs = stream.take(steps)
