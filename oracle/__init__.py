@@ -50,8 +50,11 @@ def _bind(lib):
     lib.orc_backward_causal.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_backward_noncausal.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_decode_step.argtypes = [d, d, d, d, d, d, i64, i64, i64, i64]
+    lib.orc_rff_features.argtypes = [d, d, d, d, i64, i64, i64]
+    lib.orc_forward_causal_features.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     for f in ("orc_feature_map", "orc_forward_causal", "orc_forward_noncausal",
-              "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step"):
+              "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step", "orc_rff_features",
+              "orc_forward_causal_features"):
         getattr(lib, f).restype = None
     return lib
 
@@ -155,6 +158,30 @@ def backward_noncausal(q, k, v, dout, lib=None):
     dv = np.empty_like(v)
     lib.orc_backward_noncausal(_p(q), _p(k), _p(v), _p(g), _p(dq), _p(dk), _p(dv), B, H, N, D, M)
     return dq, dk, dv
+
+
+def rff_features(x, omega, b, lib=None):
+    """Random Fourier features sqrt(2/R) cos(x omega + b) of the last axis of x
+    ([..., D] -> [..., R]); omega [D, R], b [R]."""
+    lib = lib or load()
+    x, omega, b = _f64(x), _f64(omega), _f64(b)
+    D, R = omega.shape
+    assert x.shape[-1] == D and b.shape == (R,)
+    out = np.empty(x.shape[:-1] + (R,), np.float64)
+    lib.orc_rff_features(_p(x), _p(omega), _p(b), _p(out), int(np.prod(x.shape[:-1])), D, R)
+    return out
+
+
+def forward_causal_features(fq, fk, v, lib=None):
+    """Causal linear attention on given features fq, fk [B,H,N,F] (no feature map applied)."""
+    lib = lib or load()
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    B, H, N, F = fq.shape
+    M = v.shape[-1]
+    assert fk.shape == fq.shape and v.shape == (B, H, N, M)
+    out = np.empty((B, H, N, M), np.float64)
+    lib.orc_forward_causal_features(_p(fq), _p(fk), _p(v), _p(out), B, H, N, F, M)
+    return out
 
 
 def decode_step(q, k, v, S, Z, lib=None):

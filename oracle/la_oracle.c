@@ -333,6 +333,64 @@ void orc_backward_noncausal(const double *q, const double *k, const double *v,
 }
 
 /*
+ * Random Fourier features ([summary] 5: approximating the RBF kernel with
+ * random Fourier features is named as a way to reuse softmax-pretrained
+ * models; the construction is the standard one of Rahimi and Recht):
+ *   phi_r(x) = sqrt(2 / R) cos(sum_d x_d omega[d][r] + b_r),  r < R,
+ * with omega [D][R] and b [R] drawn by the caller (omega ~ N(0, 1/sigma^2),
+ * b ~ U[0, 2 pi)), so that phi(q) . phi(k) estimates the RBF kernel
+ * exp(-|q - k|^2 / (2 sigma^2)).  x: [rows][D]; out: [rows][R].
+ */
+void orc_rff_features(const double *x, const double *omega, const double *b, double *out,
+                      int64_t rows, int64_t D, int64_t R)
+{
+    const double scale = sqrt(2.0 / (double)R);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t r = 0; r < R; ++r) {
+            double a = b[r];
+            for (int64_t d = 0; d < D; ++d) a += x[i * D + d] * omega[d * R + r];
+            out[i * R + r] = scale * cos(a);
+        }
+    }
+}
+
+/*
+ * Causal forward with the feature map already applied: fq = phi(Q) and
+ * fk = phi(K) are given, [B][H][N][F].  The recurrence of orc_forward_causal
+ * with phi the identity: S_i = S_{i-1} + fk_i V_i^T, Z_i = Z_{i-1} + fk_i,
+ * out_i = S_i^T fq_i / (fq_i . Z_i).  Features of any sign are accepted; the
+ * result is whatever the division gives.
+ */
+void orc_forward_causal_features(const double *fq, const double *fk, const double *v, double *out,
+                                 int64_t B, int64_t H, int64_t N, int64_t F, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = fq + bh * N * F, *K = fk + bh * N * F;
+        const double *V = v + bh * N * M;
+        double *O = out + bh * N * M;
+        double *S = (double *)calloc((size_t)(F * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)F, sizeof(double));
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t f = 0; f < F; ++f) {
+                for (int64_t m = 0; m < M; ++m) S[f * M + m] += K[i * F + f] * V[i * M + m];
+                Z[f] += K[i * F + f];
+            }
+            double dd = 0.0;
+            for (int64_t f = 0; f < F; ++f) dd += Q[i * F + f] * Z[f];
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t f = 0; f < F; ++f) n += Q[i * F + f] * S[f * M + m];
+                O[i * M + m] = n / dd;
+            }
+        }
+        free(S); free(Z);
+    }
+}
+
+/*
  * One RNN-style decode step for B*H independent streams ([review] "Proposed
  * method", attention memory s and normalizer memory z; [summary] 3.3.2, 3.4;
  * [deck] slide 4): S += phi(k) v^T, Z += phi(k), then

@@ -291,6 +291,56 @@ def check_backward_noncausal(lib):
     assert _rel(dq, tq.grad.numpy()) < 1e-11 and _rel(dk, tk.grad.numpy()) < 1e-11 and _rel(dv, tv.grad.numpy()) < 1e-11
 
 
+def check_rff_worked_example(lib):
+    """Random Fourier features on a hand-worked case.  D = 2, R = 4,
+    omega = [[0, 1, 0, 2], [1, 0, 0, 0]] (omega[d][r]), b = (0, pi/2, pi, 0),
+    x = (pi/3, pi/4).  The angles x . omega[:, r] + b_r are pi/4, pi/3 + pi/2,
+    pi and 2 pi/3, whose cosines are sqrt(2)/2, -sqrt(3)/2, -1 and -1/2;
+    times sqrt(2/R) = 1/sqrt(2) that is 1/2, -sqrt(6)/4, -1/sqrt(2),
+    -1/(2 sqrt(2)).  An omega read transposed, a missing scale, sin for cos or
+    a dropped b each change these numbers."""
+    omega = np.array([[0.0, 1.0, 0.0, 2.0], [1.0, 0.0, 0.0, 0.0]])
+    b = np.array([0.0, np.pi / 2, np.pi, 0.0])
+    x = np.array([[np.pi / 3, np.pi / 4]])
+    want = np.array([[0.5, -np.sqrt(6.0) / 4, -1.0 / np.sqrt(2.0), -1.0 / (2.0 * np.sqrt(2.0))]])
+    got = oracle.rff_features(x, omega, b, lib=lib)
+    assert np.abs(got - want).max() < 1e-15, got
+
+
+def check_rff_estimates_rbf_kernel(lib):
+    """With many features, phi(q) . phi(k) converges to the RBF kernel
+    exp(-|q - k|^2 / (2 sigma^2)) (standard deviation about 1/sqrt(2R))."""
+    D, R, sigma = 6, 40000, 1.7
+    rng = np.random.default_rng(77)
+    omega = rng.standard_normal((D, R)) / sigma
+    b = rng.uniform(0.0, 2.0 * np.pi, R)
+    q = rng.standard_normal((12, D)) * 0.8
+    k = rng.standard_normal((12, D)) * 0.8
+    fq, fk = oracle.rff_features(q, omega, b, lib=lib), oracle.rff_features(k, omega, b, lib=lib)
+    est = (fq * fk).sum(-1)
+    exact = np.exp(-((q - k) ** 2).sum(-1) / (2.0 * sigma ** 2))
+    assert np.abs(est - exact).max() < 0.03, np.abs(est - exact).max()
+    assert np.abs((fq * fq).sum(-1) - 1.0).max() < 0.03           # k(q, q) = 1
+
+
+def check_forward_features(lib):
+    """Causal forward on given features: the quadratic form with
+    a_ij = fq_i . fk_j (j <= i) for features of either sign, and the elu + 1
+    path when the given features are phi(Q), phi(K)."""
+    B, H, N, F, M = 2, 2, 57, 7, 5
+    fq = _rand(400, B, H, N, F) * 0.6 + 1.0         # mixed signs, positive denominators
+    fk = _rand(401, B, H, N, F) * 0.6 + 1.0
+    v = _rand(402, B, H, N, M)
+    a = np.tril(fq @ np.swapaxes(fk, -1, -2))
+    ref = (a @ v) / a.sum(-1, keepdims=True)
+    assert (fq < 0).any() and (fk < 0).any() and (a.sum(-1) > 0).all()
+    assert _rel(oracle.forward_causal_features(fq, fk, v, lib=lib), ref) < 1e-12
+    q, k = _rand(403, B, H, N, F), _rand(404, B, H, N, F)
+    assert _rel(oracle.forward_causal_features(bf.phi(q), bf.phi(k), v, lib=lib),
+                oracle.forward_causal(q, k, v, lib=lib)) < 1e-14
+
+
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,
               check_initial_state, check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
-              check_backward_identities, check_backward_noncausal]
+              check_backward_identities, check_backward_noncausal, check_rff_worked_example,
+              check_rff_estimates_rbf_kernel, check_forward_features]

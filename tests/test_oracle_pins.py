@@ -64,6 +64,22 @@ MUTATIONS = [
      "            const double h = -go / dd;",
      "            const double h = go / dd;",
      [oc.check_backward_noncausal]),
+    ("rff_sin_for_cos",
+     "out[i * R + r] = scale * cos(a);",
+     "out[i * R + r] = scale * sin(a);",
+     [oc.check_rff_worked_example, oc.check_rff_estimates_rbf_kernel]),
+    ("rff_omega_transposed",
+     "for (int64_t d = 0; d < D; ++d) a += x[i * D + d] * omega[d * R + r];",
+     "for (int64_t d = 0; d < D; ++d) a += x[i * D + d] * omega[(r % D) * R + d];",
+     [oc.check_rff_worked_example, oc.check_rff_estimates_rbf_kernel]),
+    ("rff_scale_1_over_r",
+     "const double scale = sqrt(2.0 / (double)R);",
+     "const double scale = 2.0 / (double)R;",
+     [oc.check_rff_worked_example, oc.check_rff_estimates_rbf_kernel]),
+    ("features_forward_reads_before_update",
+     "for (int64_t m = 0; m < M; ++m) S[f * M + m] += K[i * F + f] * V[i * M + m];",
+     "for (int64_t m = 0; m < M; ++m) S[f * M + m] += (i > 0) * K[(i - (i > 0)) * F + f] * V[(i - (i > 0)) * M + m];",
+     [oc.check_forward_features]),
     ("decode_reads_before_update_of_s",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m];",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m] * (m > 0);",
