@@ -18,6 +18,7 @@ on, and reported next to the headline:
   * backward: la_backward_causal and la_backward_noncausal on the long-sequence
     workload;
   * non-causal forward on the long-sequence workload;
+  * random Fourier features (R = 64) of q and k and the causal forward on them;
   * the causal forward of the three smaller workloads;
   * optionally (--sweep) the causal forward for N = 512 .. 65536.
 ``roofline`` relates the forward's algorithmic HBM bytes (Q, K, V read once,
@@ -50,7 +51,7 @@ def _args():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "decode", "backward"], default="all",
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff"], default="all",
                     help="restrict the timed work (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device three times (a plain copy kernel of known size, "
@@ -296,6 +297,45 @@ def main():
                                              hbm_frac=bwd_bytes / (t / nb) / 1e9 / HBM_PEAK_GBS)
         log(f"non-causal backward: {t / nb * 1e3:.4f} ms/call")
         del dq, dk, dv, ws_b, ws_nb
+    if a.only in ("all", "rff"):
+        # random Fourier features (R = 64) of q and k, then the causal forward on them
+        om, bias = wl.rff_params(w4.D, 64, seed=4004)
+        omd, bd = to_dev(om, "f32"), to_dev(bias, "f32")
+        fq = torch.empty((w4.B, w4.H, w4.N, 64), dtype=torch.bfloat16, device=dev)
+        fk = torch.empty_like(fq)
+
+        def feats(i):
+            q, k, _, _ = sets[i % 2]
+            for x, f in ((q, fq), (k, fk)):
+                st = lib.la_rff_features(x.data_ptr(), omd.data_ptr(), bd.data_ptr(), f.data_ptr(), w4.B, w4.H, w4.N,
+                                         w4.D, 64, la.LA_DTYPE_BF16, sptr)
+                if st != 0:
+                    raise la.LAError("rff_features", st)
+
+        def rff_fwd(i):
+            feats(i)
+            v = sets[i % 2][2]
+            st = lib.la_forward_causal_features(fq.data_ptr(), fk.data_ptr(), v.data_ptr(), out.data_ptr(), w4.B,
+                                                w4.H, w4.N, 64, w4.M, la.LA_DTYPE_BF16, ws_f.data_ptr(), ws_f.numel(),
+                                                sptr)
+            if st != 0:
+                raise la.LAError("forward_causal_features", st)
+
+        for i in range(2):
+            rff_fwd(i)
+        nr = max(5, a.steps // 2)
+        t_all = time_events(rff_fwd, nr)
+        t_feat = time_events(feats, nr)
+        feat_bytes = 2 * tok_heads * (w4.D + 64) * 2        # read q (k), write its features, bf16
+        results["rff_forward"] = dict(
+            ms_per_call=t_all / nr * 1e3, tok_heads_per_s=tok_heads * nr / t_all,
+            features_ms_per_call=t_feat / nr * 1e3,
+            features_hbm_frac=feat_bytes / (t_feat / nr) / 1e9 / HBM_PEAK_GBS,
+            note="R = 64 random Fourier features of q and k (two la_rff_features calls), then "
+                 "la_forward_causal_features on them; features materialized in HBM")
+        log(f"rff forward: {t_all / nr * 1e3:.4f} ms/call (features {t_feat / nr * 1e3:.4f} ms)")
+        del fq, fk
+
     if a.only in ("all",):
         for i in range(2):
             fwd(i, causal=False)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 3
+#define LA_ABI_VERSION 4
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
 
@@ -61,7 +61,8 @@ typedef enum {
 } la_status_t;
 
 typedef enum {
-    LA_OP_FWD_CAUSAL = 0,     /* la_forward_causal, la_forward_causal_state */
+    LA_OP_FWD_CAUSAL = 0,     /* la_forward_causal, la_forward_causal_state,
+                                 la_forward_causal_features (with D = F) */
     LA_OP_FWD_NONCAUSAL = 1,  /* la_forward_noncausal */
     LA_OP_BWD_CAUSAL = 2,     /* la_backward_causal */
     LA_OP_BWD_NONCAUSAL = 3   /* la_backward_noncausal */
@@ -112,6 +113,40 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
                                     float *z_final, int64_t B, int64_t H, int64_t N, int64_t D,
                                     int64_t M, la_dtype_t dt, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Random Fourier features ([summary] 5: approximating the RBF kernel with
+ * random Fourier features is named as a feature map for reusing
+ * softmax-pretrained models; the map is the standard construction):
+ *   out[row][r] = sqrt(2/R) cos(sum_d x[row][d] omega[d][r] + bias[r]).
+ * With omega ~ N(0, 1/sigma^2) and bias ~ U[0, 2 pi), drawn by the caller,
+ * out(q) . out(k) estimates exp(-|q - k|^2 / (2 sigma^2)).
+ * x: [B][H][N][D] in dt (input); omega: [D][R] fp32, bias: [R] fp32 (inputs);
+ * out: [B][H][N][R] in dt (output, fully written).  D, R in {32, 64}.
+ * No workspace.  The features can be negative: attention on them
+ * (la_forward_causal_features) is only as well conditioned as its
+ * denominators.
+ */
+la_status_t la_rff_features(const void *x, const float *omega, const float *bias, void *out,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int64_t R,
+                            la_dtype_t dt, hipStream_t stream);
+
+/*
+ * Causal forward on features that are already applied ([summary] 3.2: any
+ * feature map phi gives a kernel phi(q) . phi(k); 3.2.1: the map can be
+ * chosen, e.g. elu + 1, a polynomial, or random features):
+ *   out_i = sum_{j<=i} (fq_i . fk_j) v_j / sum_{j<=i} (fq_i . fk_j),
+ * i.e. la_forward_causal with phi the identity.  fq, fk: [B][H][N][F]; v,
+ * out: [B][H][N][M]; F, M in {32, 64}; workspace
+ * la_workspace_size(LA_OP_FWD_CAUSAL, B, H, N, F, M, dt).  Features of any
+ * sign are accepted and nothing guards the denominators: a zero or negative
+ * one gives what the division gives.  Errors and diagnostic word as
+ * la_forward_causal.
+ */
+la_status_t la_forward_causal_features(const void *fq, const void *fk, const void *v, void *out,
+                                       int64_t B, int64_t H, int64_t N, int64_t F, int64_t M,
+                                       la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
 
 /*
  * Non-causal forward through associativity ([review] "Proposed method";

@@ -10,6 +10,8 @@ built, every call raises.
 Functions carry the C names:
   la_forward_causal(q, k, v, out=None, workspace=None)
   la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None)
+  la_forward_causal_features(fq, fk, v, out=None, workspace=None)
+  la_rff_features(x, omega, bias, out=None)
   la_forward_noncausal(q, k, v, out=None, workspace=None)
   la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
@@ -24,7 +26,8 @@ import os
 
 import torch
 
-__all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
+__all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
+           "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
            "la_decode_step",
            "la_workspace_size", "la_status_string", "la_abi_version", "LAError", "lib_path", "load",
            "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
@@ -61,8 +64,10 @@ def load():
     lib.la_backward_noncausal.argtypes = lib.la_backward_causal.argtypes
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
-    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal",
-              "la_backward_noncausal", "la_decode_step"):
+    lib.la_forward_causal_features.argtypes = fwd
+    lib.la_rff_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
+              "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step"):
         getattr(lib, f).restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
     lib.la_workspace_size.restype = sz
@@ -167,6 +172,31 @@ def la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=Non
                                         _stream(dev))
     _check("la_forward_causal_state", st)
     return out, s_final, z_final
+
+
+def la_forward_causal_features(fq, fk, v, out=None, workspace=None):
+    """Causal linear attention on given features fq, fk [B,H,N,F] (no feature map applied); returns out."""
+    return _forward("la_forward_causal_features", LA_OP_FWD_CAUSAL, fq, fk, v, out, workspace)
+
+
+def la_rff_features(x, omega, bias, out=None):
+    """Random Fourier features sqrt(2/R) cos(x omega + bias) of x [B,H,N,D]; omega [D,R] and bias [R]
+    float32; returns [B,H,N,R] in x's dtype."""
+    dev = _dev(x, omega, bias)
+    if x.dim() != 4 or x.dtype not in _DT:
+        raise ValueError("x: [B,H,N,D] float32 or bfloat16")
+    if omega.dtype != torch.float32 or bias.dtype != torch.float32 or omega.dim() != 2 or \
+            omega.shape[0] != x.shape[-1] or tuple(bias.shape) != (omega.shape[1],):
+        raise ValueError("omega: float32 [D,R]; bias: float32 [R]")
+    B, H, N, D = x.shape
+    R = omega.shape[1]
+    if out is None:
+        out = torch.empty((B, H, N, R), dtype=x.dtype, device=dev)
+    _dev(x, out)
+    st = load().la_rff_features(x.data_ptr(), omega.data_ptr(), bias.data_ptr(), out.data_ptr(), B, H, N, D, R,
+                                _DT[x.dtype], _stream(dev))
+    _check("la_rff_features", st)
+    return out
 
 
 def la_forward_noncausal(q, k, v, out=None, workspace=None):

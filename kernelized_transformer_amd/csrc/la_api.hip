@@ -130,6 +130,40 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+la_status_t la_forward_causal_features(const void *fq, const void *fk, const void *v, void *out, int64_t B,
+                                       int64_t H, int64_t N, int64_t F, int64_t M, la_dtype_t dt, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, F, M, dt);
+    if (st != LA_OK) return st;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[3] = {span(fq, size_t(BH * N * F) * es), span(fk, size_t(BH * N * F) * es),
+                        span(v, size_t(BH * N * M) * es)};
+    const Span o[1] = {span(out, size_t(BH * N * M) * es)};
+    if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
+    const Span all[4] = {in[0], in[1], in[2], o[0]};
+    if ((st = check_workspace(workspace, workspace_bytes, la::causal_workspace_bytes(BH, N, F, M), all, 4)) != LA_OK)
+        return st;
+    la::StateIO sio;
+    sio.features_given = true;
+    const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, fq, fk, v, out, BH, N, F, M,
+                                            static_cast<float *>(workspace), stream, sio);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status_t la_rff_features(const void *x, const float *omega, const float *bias, void *out, int64_t B, int64_t H,
+                            int64_t N, int64_t D, int64_t R, la_dtype_t dt, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, D, R, dt);
+    if (st != LA_OK) return st;
+    const size_t es = esize(dt);
+    const int64_t rows = B * H * N;
+    const Span in[3] = {span(x, size_t(rows * D) * es), span(omega, size_t(D * R) * 4), span(bias, size_t(R) * 4)};
+    const Span o[1] = {span(out, size_t(rows * R) * es)};
+    if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
+    const hipError_t e = la::launch_rff_features(dt == LA_DTYPE_F32 ? 0 : 1, x, omega, bias, out, rows, D, R, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 la_status_t la_forward_noncausal(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
                                  int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {

@@ -73,6 +73,17 @@ __device__ __forceinline__ void raw_frags(typename IO<T>::frag (&y)[TT][F / 16],
     }
 }
 
+// Query/key fragments: phi applied (PHI) or the given features as they are;
+// rows at or beyond t_end zeroed either way.
+template <typename T, int F, int TT, bool PHI>
+__device__ __forceinline__ void feat_frags(typename IO<T>::frag (&y)[TT][F / 16],
+                                           const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
+    if constexpr (PHI)
+        phi_frags<T, F, TT>(y, x, t0, t_end);
+    else
+        raw_frags<T, F, TT>(y, x, t0, t_end);
+}
+
 // ---- LDS staging (bf16) ---------------------------------------------------
 // A wavefront's private staging area for one chunk of one tensor: rows of
 // 16*NF features (bf16), padded to kStagePad extra elements per row.

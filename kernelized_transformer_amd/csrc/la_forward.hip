@@ -44,7 +44,8 @@ constexpr int kPrefetch = 2; // chunks in flight ahead of the one being computed
 // PF chunks are kept in flight: the loop is unrolled by PF so that chunk i
 // always lives in buffer i % PF (a register copy between buffers would force
 // a wait on the loads in flight).
-template <typename T, int D, int M, int PF>
+// PHI: apply the feature map to K (otherwise K holds the features already).
+template <typename T, int D, int M, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *__restrict__ V, int64_t t_begin,
                                               int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
                                               lds_bf16 *stage_v) {
@@ -61,7 +62,7 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
         for (int b = 0; b < PF; ++b) {
             const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
             Fr Kn[TT][D / 16], Vn[TT][M / 16];
-            phi_frags<T, D, TT>(Kn, rk[b], t0, t_end);
+            feat_frags<T, D, TT, PHI>(Kn, rk[b], t0, t_end);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -87,7 +88,7 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
 //   intra:    Ot[mt][it] += V^T[m][j] P^T[j][i], P^T[j][i] = phi(K_j).phi(Q_i), j <= i
 //   update:   St += phi(K)^T [V, 1]
 // The normalizer row block of Ot gets den_i in row 0.
-template <typename T, int D, int M, bool CAUSAL, int PF>
+template <typename T, int D, int M, bool CAUSAL, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__restrict__ K,
                                            const T *__restrict__ V, T *__restrict__ O, int64_t t_begin,
                                            int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
@@ -113,9 +114,9 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
     for (int b = 0; b < PF; ++b) {
         const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
         Fr Qn[TT][DT], Kn[TT][DT], Vn[TT][MT];
-        phi_frags<T, D, TT>(Qn, rq[b], t0, t_end);
+        feat_frags<T, D, TT, PHI>(Qn, rq[b], t0, t_end);
         if (CAUSAL) {
-            phi_frags<T, D, TT>(Kn, rk[b], t0, t_end);
+            feat_frags<T, D, TT, PHI>(Kn, rk[b], t0, t_end);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -229,7 +230,7 @@ __device__ __forceinline__ void store_tile_bf16(bf16 *__restrict__ O, int64_t t0
 // staged in the wavefront's LDS area, from which the natural and the
 // token-contiguous fragments are read.
 
-template <int D, int M, int PF>
+template <int D, int M, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, const bf16 *__restrict__ V,
                                                    int64_t t_begin, int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1],
                                                    lds_bf16 *sk, lds_bf16 *sv) {
@@ -244,7 +245,7 @@ __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, c
 #pragma unroll
         for (int b = 0; b < PF; ++b) {
             const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked
-            stage_lines<D, TT, true>(sk, rk[b], t0, t_end);
+            stage_lines<D, TT, PHI, true>(sk, rk[b], t0, t_end);
             stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
             load_lines<D, TT>(rk[b], K, t0 + PF * CH, t_end);
             load_lines<M, TT>(rv[b], V, t0 + PF * CH, t_end);
@@ -257,7 +258,7 @@ __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, c
     }
 }
 
-template <int D, int M, bool CAUSAL, int PF>
+template <int D, int M, bool CAUSAL, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                 const bf16 *__restrict__ V, bf16 *__restrict__ O, int64_t t_begin,
                                                 int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *sq,
@@ -285,9 +286,9 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
         // no row masks: rows past t_end hold copies of the last valid row (finite),
         // their outputs are not stored, the causal mask keeps them out of every
         // stored output, and the state is not used after the last chunk
-        stage_lines<D, TT, true, false>(sq, rq[b], t0, t_end);
+        stage_lines<D, TT, PHI, false>(sq, rq[b], t0, t_end);
         if (CAUSAL) {
-            stage_lines<D, TT, true, false>(sk, rk[b], t0, t_end);
+            stage_lines<D, TT, PHI, false>(sk, rk[b], t0, t_end);
             stage_lines<M, TT, false, false>(sv, rv[b], t0, t_end);
         }
         load_lines<D, TT>(rq[b], Q, t0 + PF * CH, t_end);
@@ -628,7 +629,8 @@ __device__ __forceinline__ void wait_flags(const unsigned long long *flags, int 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // later loads stay below (compiler)
 }
 
-template <typename T, int D, int M>
+// PHI = false: q and k hold the features already (no feature map applied).
+template <typename T, int D, int M, bool PHI>
 __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd_fused(const T *__restrict__ q, const T *__restrict__ k,
                                                                 const T *__restrict__ v, T *__restrict__ out,
                                                                 int *__restrict__ header,
@@ -675,9 +677,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     lds_bf16 *stage_k = stage_q + SK;
     lds_bf16 *stage_v = stage_k + SK;
     if constexpr (sizeof(T) == 2)
-        seg_aggregate_bf16<D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
+        seg_aggregate_bf16<D, M, kPrefetch, PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
     else
-        seg_aggregate<T, D, M, kPrefetch>(K, V, t_begin, t_end, St, stage_k, stage_v);
+        seg_aggregate<T, D, M, kPrefetch, PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
     __syncthreads();   // every wavefront is done with its staging area
     state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
@@ -800,10 +802,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     state_load_frag2<D, M>(St, pbuf, wave > 0 ? slot(wave) : nullptr);
     __syncthreads();   // the prefix is read: the staging area is free again
     if constexpr (sizeof(T) == 2)
-        seg_output_bf16<D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q, stage_k,
-                                               stage_v, stage_v + SV);
+        seg_output_bf16<D, M, true, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q,
+                                                    stage_k, stage_v, stage_v + SV);
     else
-        seg_output<T, D, M, true, kPrefetch>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_k, stage_v);
+        seg_output<T, D, M, true, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_k, stage_v);
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -828,9 +830,15 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
         int *header = reinterpret_cast<int *>(base);
         unsigned long long *flags = reinterpret_cast<unsigned long long *>(base + p.flags_off);
         float *recs = reinterpret_cast<float *>(base + p.recs_off);
-        hipLaunchKernelGGL((k_fwd_fused<T, D, M>), dim3(unsigned(BH * p.nblk)), dim3(64 * kFusedWaves), 0, s,
-                           (const T *)q, (const T *)k, (const T *)v, (T *)out, header, flags, next_call_tag(), recs,
-                           N, p.nblk, p.sub_tokens, sio);
+        const dim3 grid(unsigned(BH * p.nblk)), block(64 * kFusedWaves);
+        if (sio.features_given)
+            hipLaunchKernelGGL((k_fwd_fused<T, D, M, false>), grid, block, 0, s, (const T *)q, (const T *)k,
+                               (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens,
+                               sio);
+        else
+            hipLaunchKernelGGL((k_fwd_fused<T, D, M, true>), grid, block, 0, s, (const T *)q, (const T *)k,
+                               (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens,
+                               sio);
         return hipGetLastError();
     }
     const SegPlan p = make_plan(BH, N, D, M);
@@ -865,7 +873,7 @@ static hipError_t run_forward_t(bool causal, const void *q, const void *k, const
 
 hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out, int64_t BH,
                           int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s, StateIO sio) {
-    if (!causal && (sio.s0 || sio.s1)) return hipErrorInvalidValue;
+    if (!causal && (sio.s0 || sio.s1 || sio.features_given)) return hipErrorInvalidValue;
     if (dt == 0) return run_forward_t<float>(causal, q, k, v, out, BH, N, D, M, ws, sio, s);
     return run_forward_t<bf16>(causal, q, k, v, out, BH, N, D, M, ws, sio, s);
 }

@@ -139,13 +139,21 @@ inline size_t backward_noncausal_workspace_bytes(int64_t BH, int64_t N, int64_t 
     return 2 * backward_layout(BH, N, D, M, 4).states;
 }
 
-// Optional fp32 state of the causal forward, [BH][D][M] and [BH][D] (the
-// decode layout): s0/z0 start the recurrence (null: zero), s1/z1 receive the
-// state after the last token (null: not written); s1 may equal s0.
+// Options of the causal forward.  Optional fp32 state, [BH][D][M] and
+// [BH][D] (the decode layout): s0/z0 start the recurrence (null: zero),
+// s1/z1 receive the state after the last token (null: not written); s1 may
+// equal s0.  features_given: q and k already hold the features (the feature
+// map is not applied).
 struct StateIO {
     const float *s0 = nullptr, *z0 = nullptr;
     float *s1 = nullptr, *z1 = nullptr;
+    bool features_given = false;
 };
+
+// Random Fourier features of rows x [rows][D] into out [rows][R]; omega
+// [D][R] and bias [R] fp32.
+hipError_t launch_rff_features(int dt, const void *x, const float *omega, const float *bias, void *out, int64_t rows,
+                               int64_t D, int64_t R, hipStream_t s);
 
 // Launchers (hipError_t of the last launch).  dt: 0 = fp32, 1 = bf16.
 hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,

@@ -27,8 +27,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_noncausal", "la_backward_causal",
-              "la_backward_noncausal", "la_decode_step", "la_workspace_size", "la_status_string", "la_abi_version"):
+    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
+              "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
+              "la_workspace_size", "la_status_string", "la_abi_version"):
         assert f in fns
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 3
+    assert la.la_abi_version() == 4
     names = [la.la_status_string(s) for s in range(5)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
     assert la.la_status_string(99) == "LA_ERR_UNKNOWN"
@@ -74,7 +75,7 @@ def _fwd(lib, fn, q=FAKE, k=FAKE + (1 << 24), v=FAKE + (2 << 24), out=FAKE + (3 
     return getattr(lib, fn)(q, k, v, out, B, H, N, D, M, dt, ws, wsb, None)
 
 
-@pytest.mark.parametrize("fn", ["la_forward_causal", "la_forward_noncausal"])
+@pytest.mark.parametrize("fn", ["la_forward_causal", "la_forward_noncausal", "la_forward_causal_features"])
 def test_forward_argument_errors(fn):
     lib = la.load()
     assert _fwd(lib, fn, q=0) == 1                      # null input
@@ -113,6 +114,23 @@ def test_forward_state_argument_errors():
     assert fs(s1=b[0]) == 1                         # final state over q
     assert fs(D=48) == 2
     assert fs(ws=b[6], wsb=1 << 20) == 3            # workspace overlaps the final state
+
+
+def test_rff_argument_errors():
+    lib = la.load()
+    b = [FAKE + (i << 24) for i in range(4)]   # x omega bias out
+
+    def rff(x=b[0], om=b[1], bias=b[2], out=b[3], B=1, H=2, N=8, D=64, R=32, dt=1):
+        return lib.la_rff_features(x, om, bias, out, B, H, N, D, R, dt, None)
+
+    assert rff(x=0) == 1
+    assert rff(om=0) == 1
+    assert rff(bias=b[2] + 4) == 1                  # misaligned
+    assert rff(out=b[1]) == 1                       # output over omega
+    assert rff(out=b[0] + 16) == 1                  # output overlaps x
+    assert rff(R=48) == 2 and rff(D=16) == 2        # unsupported sizes
+    assert rff(N=0) == 1
+    assert rff(dt=5) == 2
 
 
 def test_backward_and_decode_argument_errors():

@@ -339,6 +339,63 @@ def test_forward_state_full_long_sequence():
     check("Z_N", host(Z), Z_ref, w.dtype)
 
 
+# Random Fourier features and the causal forward on given features.
+RFF_CASES = [
+    ("w1_r32_f32", wl.WORKLOADS[1], 32),
+    ("d32_r64_f32_ragged", _wl(211, 2, 3, 100, 32, 32, "f32"), 64),
+    ("d64_r32_bf16_ragged", _wl(212, 1, 3, 1001, 64, 64, "bf16"), 32),
+    ("w4_full_r64", wl.WORKLOADS[4], 64),
+]
+
+
+@pytest.mark.parametrize("name,w,R", RFF_CASES, ids=[c[0] for c in RFF_CASES])
+def test_rff_features(name, w, R):
+    x, _, _ = wl.forward_inputs(w)
+    om, b = wl.rff_params(w.D, R, seed=w.wid + 2000)
+    _say(f"rff features {name}: B{w.B} H{w.H} N{w.N} D{w.D} R{R} {w.dtype}")
+    got = la.la_rff_features(dev(x, w.dtype), dev(om, "f32"), dev(b, "f32"))
+    torch.cuda.synchronize()
+    check(f"features[{name}]", host(got), oracle.rff_features(x, om, b), w.dtype)
+
+
+@pytest.mark.parametrize("name,w,R", RFF_CASES, ids=[c[0] for c in RFF_CASES])
+def test_rff_attention(name, w, R):
+    """The causal forward on random Fourier features: given the oracle's
+    features (rounded to the I/O type) the GPU forward matches the oracle's
+    forward on the same features; and the whole GPU path (features, then
+    forward) matches the oracle's whole path from the same q, k, v, omega, b."""
+    q, k, v = wl.forward_inputs(w)
+    om, b = wl.rff_params(w.D, R, seed=w.wid + 2000)
+    _say(f"rff attention {name}: B{w.B} H{w.H} N{w.N} D{w.D} R{R} M{w.M} {w.dtype}")
+    fq_o, fk_o = oracle.rff_features(q, om, b), oracle.rff_features(k, om, b)
+    fq_r, fk_r = wl.round_to(fq_o, w.dtype), wl.round_to(fk_o, w.dtype)
+    vd = dev(v, w.dtype)
+    out_given = la.la_forward_causal_features(dev(fq_r, w.dtype), dev(fk_r, w.dtype), vd)
+    omd, bd = dev(om, "f32"), dev(b, "f32")
+    fq_g = la.la_rff_features(dev(q, w.dtype), omd, bd)
+    fk_g = la.la_rff_features(dev(k, w.dtype), omd, bd)
+    out_path = la.la_forward_causal_features(fq_g, fk_g, vd)
+    torch.cuda.synchronize()
+    check(f"out on given features[{name}]", host(out_given), oracle.forward_causal_features(fq_r, fk_r, v), w.dtype)
+    check(f"out, whole path[{name}]", host(out_path), oracle.forward_causal_features(fq_o, fk_o, v), w.dtype)
+
+
+@pytest.mark.parametrize("name,w", [("mixed_sign_bf16_many_blocks", _wl(213, 1, 2, 40000, 64, 64, "bf16")),
+                                    ("mixed_sign_f32_d32m64", _wl(214, 2, 2, 777, 32, 64, "f32"))],
+                         ids=["mixed_sign_bf16_many_blocks", "mixed_sign_f32_d32m64"])
+def test_forward_features_mixed_sign(name, w):
+    """Given features of either sign (1 + 0.6 N(0, 1), about 5% negative) with
+    positive denominators: no feature map may be applied to them."""
+    fq, fk, v = wl.forward_inputs(w)
+    fq = wl.round_to(np.float32(1.0) + np.float32(0.6) * fq, w.dtype)
+    fk = wl.round_to(np.float32(1.0) + np.float32(0.6) * fk, w.dtype)
+    assert (fq < 0).any() and (fk < 0).any()
+    _say(f"forward on mixed-sign features {name}: B{w.B} H{w.H} N{w.N} F{w.D} M{w.M} {w.dtype}")
+    out = la.la_forward_causal_features(dev(fq, w.dtype), dev(fk, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    check(f"out[{name}]", host(out), oracle.forward_causal_features(fq, fk, v), w.dtype)
+
+
 def test_forward_deterministic_and_guarded():
     w = _wl(141, 2, 3, 1500, 64, 64, "bf16")
     q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))

@@ -114,6 +114,18 @@ def start_state(w: Workload, seed: int):
     return np.ascontiguousarray(S0), np.ascontiguousarray(Z0)
 
 
+def rff_params(D: int, R: int, seed: int, sigma: float | None = None):
+    """omega [D, R] ~ N(0, 1/sigma^2) and bias [R] ~ U[0, 2 pi), float32, for
+    random Fourier features; sigma defaults to 2 sqrt(D), which keeps the RBF
+    kernel of N(0, 1) queries and keys near exp(-1/4) (well-conditioned
+    attention)."""
+    sigma = 2.0 * np.sqrt(D) if sigma is None else sigma
+    g = rng(seed)
+    omega = g.standard_normal((D, R), dtype=np.float32) * np.float32(1.0 / sigma)
+    bias = g.uniform(0.0, 2.0 * np.pi, R).astype(np.float32)
+    return np.ascontiguousarray(omega), np.ascontiguousarray(bias)
+
+
 class DecodeStream:
     """Per-step decode inputs, drawn in order q_t, k_t, v_t for t = 0, 1, ..."""
 
