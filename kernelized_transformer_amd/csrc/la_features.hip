@@ -21,6 +21,7 @@
 namespace la {
 
 constexpr int kFeatRowsPerWave = 256;   // 16 tiles of 16 rows
+constexpr int kFeatAhead = 4;           // tiles of rows in flight
 constexpr int kFeatWavesPerBlock = 4;
 
 template <typename T, int D, int R>
@@ -61,11 +62,25 @@ __global__ __launch_bounds__(64 * kFeatWavesPerBlock) void k_rff_features(const 
     __shared__ bf16 tiles[kFeatWavesPerBlock][16 * (R + kStagePad)];
     lds_bf16 *otile = (lds_bf16 *)tiles[wave];
 
-    for (int64_t t0 = r0; t0 < r_end; t0 += 16) {
-        const int64_t t = min(t0 + c, r_end - 1);   // rows past the end read a valid row, not stored
+    // rows past the end read a valid row and are not stored; kFeatAhead tiles
+    // of rows are in flight (tile i lives in slot i % kFeatAhead)
+    typename IO<T>::frag xr[kFeatAhead][DT];
+#pragma unroll
+    for (int a = 0; a < kFeatAhead; ++a)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            xr[a][dt] = load4<T>(x + min(r0 + 16 * a + c, r_end - 1) * D + 16 * dt + 4 * g);
+    for (int64_t t00 = r0; t00 < r_end; t00 += 16 * kFeatAhead) {
+#pragma unroll
+    for (int a = 0; a < kFeatAhead; ++a) {
+        const int64_t t0 = t00 + 16 * a;   // may lie past r_end: computed, not stored
         typename IO<T>::frag xf[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) xf[dt] = load4<T>(x + t * D + 16 * dt + 4 * g);
+        for (int dt = 0; dt < DT; ++dt) xf[dt] = xr[a][dt];
+        const int64_t tn = min(t0 + 16 * kFeatAhead + c, r_end - 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) xr[a][dt] = load4<T>(x + tn * D + 16 * dt + 4 * g);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -85,6 +100,7 @@ __global__ __launch_bounds__(64 * kFeatWavesPerBlock) void k_rff_features(const 
                 store4<T>(out + (t0 + c) * R + 16 * rt + 4 * g, y);
         }
         if constexpr (sizeof(T) == 2) tile_flush_bf16<R>((bf16 *)out, t0, r_end, otile);
+    }
     }
 }
 
