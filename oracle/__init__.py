@@ -52,9 +52,10 @@ def _bind(lib):
     lib.orc_decode_step.argtypes = [d, d, d, d, d, d, i64, i64, i64, i64]
     lib.orc_rff_features.argtypes = [d, d, d, d, i64, i64, i64]
     lib.orc_forward_causal_features.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
+    lib.orc_forward_causal_poly2.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     for f in ("orc_feature_map", "orc_forward_causal", "orc_forward_noncausal",
               "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step", "orc_rff_features",
-              "orc_forward_causal_features"):
+              "orc_forward_causal_features", "orc_forward_causal_poly2"):
         getattr(lib, f).restype = None
     return lib
 
@@ -181,6 +182,19 @@ def forward_causal_features(fq, fk, v, lib=None):
     assert fk.shape == fq.shape and v.shape == (B, H, N, M)
     out = np.empty((B, H, N, M), np.float64)
     lib.orc_forward_causal_features(_p(fq), _p(fk), _p(v), _p(out), B, H, N, F, M)
+    return out
+
+
+def forward_causal_poly2(q, k, v, lib=None):
+    """Causal linear attention with the degree-2 polynomial kernel (q . k)^2,
+    through its explicit D^2 feature map.  q,k: [B,H,N,D]; v: [B,H,N,M]."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (B, H, N, M)
+    out = np.empty((B, H, N, M), np.float64)
+    lib.orc_forward_causal_poly2(_p(q), _p(k), _p(v), _p(out), B, H, N, D, M)
     return out
 
 

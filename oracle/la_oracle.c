@@ -391,6 +391,50 @@ void orc_forward_causal_features(const double *fq, const double *fk, const doubl
 }
 
 /*
+ * Causal forward with the degree-2 polynomial kernel ([summary] 3.2.1: a
+ * degree-2 polynomial kernel has an exact finite feature map).  Reading:
+ * sim(q, k) = (q . k)^2, whose feature map is phi(x) = vec(x x^T) (D^2
+ * features, phi(q) . phi(k) = sum_{a,b} q_a q_b k_a k_b = (q . k)^2).  The
+ * recurrence of orc_forward_causal with that phi: S_i = S_{i-1} +
+ * phi(K_i) V_i^T (D^2 x M), Z_i = Z_{i-1} + phi(K_i), out_i =
+ * S_i^T phi(Q_i) / (phi(Q_i) . Z_i).  q, k: [B][H][N][D]; v, out: [B][H][N][M].
+ */
+void orc_forward_causal_poly2(const double *q, const double *k, const double *v, double *out,
+                              int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H, F = D * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M;
+        double *O = out + bh * N * M;
+        double *S = (double *)calloc((size_t)(F * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)F, sizeof(double));
+        double *pq = (double *)malloc((size_t)F * sizeof(double));
+        double *pk = (double *)malloc((size_t)F * sizeof(double));
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t a = 0; a < D; ++a)
+                for (int64_t b = 0; b < D; ++b) {
+                    pq[a * D + b] = Q[i * D + a] * Q[i * D + b];
+                    pk[a * D + b] = K[i * D + a] * K[i * D + b];
+                }
+            for (int64_t f = 0; f < F; ++f) {
+                for (int64_t m = 0; m < M; ++m) S[f * M + m] += pk[f] * V[i * M + m];
+                Z[f] += pk[f];
+            }
+            double dd = 0.0;
+            for (int64_t f = 0; f < F; ++f) dd += pq[f] * Z[f];
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t f = 0; f < F; ++f) n += pq[f] * S[f * M + m];
+                O[i * M + m] = n / dd;
+            }
+        }
+        free(S); free(Z); free(pq); free(pk);
+    }
+}
+
+/*
  * One RNN-style decode step for B*H independent streams ([review] "Proposed
  * method", attention memory s and normalizer memory z; [summary] 3.3.2, 3.4;
  * [deck] slide 4): S += phi(k) v^T, Z += phi(k), then

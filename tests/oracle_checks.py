@@ -340,7 +340,23 @@ def check_forward_features(lib):
                 oracle.forward_causal(q, k, v, lib=lib)) < 1e-14
 
 
+def check_poly2(lib):
+    """Degree-2 polynomial kernel: the oracle's explicit D^2 feature map
+    against brute force with the kernel itself, a_ij = (q_i . k_j)^2 for
+    j <= i; N = 1 gives V_1; the last row equals the non-causal form."""
+    for s, (B, H, N, D, M) in enumerate([(1, 2, 40, 5, 3), (2, 1, 17, 8, 6), (1, 1, 1, 4, 4), (1, 1, 64, 32, 32)]):
+        q, k, v = _rand(500 + 3 * s, B, H, N, D), _rand(501 + 3 * s, B, H, N, D), _rand(502 + 3 * s, B, H, N, M)
+        a = np.tril((q @ np.swapaxes(k, -1, -2)) ** 2)
+        ref = (a @ v) / a.sum(-1, keepdims=True)
+        got = oracle.forward_causal_poly2(q, k, v, lib=lib)
+        assert _rel(got, ref) < 1e-12, (B, H, N, D, M, _rel(got, ref))
+        if N == 1:
+            assert _rel(got, v) < 1e-15
+        full = (q @ np.swapaxes(k, -1, -2)) ** 2
+        assert _rel(got[:, :, -1], ((full @ v) / full.sum(-1, keepdims=True))[:, :, -1]) < 1e-12
+
+
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,
               check_initial_state, check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
               check_backward_identities, check_backward_noncausal, check_rff_worked_example,
-              check_rff_estimates_rbf_kernel, check_forward_features]
+              check_rff_estimates_rbf_kernel, check_forward_features, check_poly2]

@@ -80,6 +80,14 @@ MUTATIONS = [
      "for (int64_t m = 0; m < M; ++m) S[f * M + m] += K[i * F + f] * V[i * M + m];",
      "for (int64_t m = 0; m < M; ++m) S[f * M + m] += (i > 0) * K[(i - (i > 0)) * F + f] * V[(i - (i > 0)) * M + m];",
      [oc.check_forward_features]),
+    ("poly2_diagonal_features_only",
+     "pk[a * D + b] = K[i * D + a] * K[i * D + b];",
+     "pk[a * D + b] = (a == b) * K[i * D + a] * K[i * D + b];",
+     [oc.check_poly2]),
+    ("poly2_query_features_from_keys",
+     "pq[a * D + b] = Q[i * D + a] * Q[i * D + b];",
+     "pq[a * D + b] = Q[i * D + a] * K[i * D + b];",
+     [oc.check_poly2]),
     ("decode_reads_before_update_of_s",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m];",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m] * (m > 0);",
