@@ -19,6 +19,7 @@ on, and reported next to the headline:
     workload;
   * non-causal forward on the long-sequence workload;
   * random Fourier features (R = 64) of q and k and the causal forward on them;
+  * the causal forward with the degree-2 polynomial kernel at D = M = 32;
   * the causal forward of the three smaller workloads;
   * optionally (--sweep) the causal forward for N = 512 .. 65536.
 ``roofline`` relates the forward's algorithmic HBM bytes (Q, K, V read once,
@@ -51,7 +52,7 @@ def _args():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff"], default="all",
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly"], default="all",
                     help="restrict the timed work (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device three times (a plain copy kernel of known size, "
@@ -335,6 +336,32 @@ def main():
                  "la_forward_causal_features on them; features materialized in HBM")
         log(f"rff forward: {t_all / nr * 1e3:.4f} ms/call (features {t_feat / nr * 1e3:.4f} ms)")
         del fq, fk
+
+    if a.only in ("all", "poly"):
+        # degree-2 polynomial kernel (q . k)^2, D = M = 32, on the long-sequence length
+        wp = wl.Workload(4, "polynomial kernel, B1 H8 N65536 D=M=32 bf16", 1, 8, w4.N, 32, 32, "bf16")
+        qp, kp, vp = (to_dev(x, "bf16") for x in wl.forward_inputs(wp))
+        op = torch.empty_like(vp)
+        wsp = torch.empty(la.la_workspace_size(la.LA_OP_FWD_CAUSAL_POLY2, wp.B, wp.H, wp.N, 32, 32, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+
+        def poly(i):
+            st = lib.la_forward_causal_poly2(qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), op.data_ptr(), wp.B, wp.H,
+                                             wp.N, 32, 32, la.LA_DTYPE_BF16, wsp.data_ptr(), wsp.numel(), sptr)
+            if st != 0:
+                raise la.LAError("forward_causal_poly2", st)
+
+        for i in range(2):
+            poly(i)
+        npl = max(5, a.steps // 2)
+        t = time_events(poly, npl)
+        th = wp.B * wp.H * wp.N
+        flops = th * (4 * 32 * 32 * (32 + 1) + 2 * 32 * 32)   # recurrence on the D^2 features
+        results["poly2_forward"] = dict(
+            workload=wp.name, ms_per_call=t / npl * 1e3, tok_heads_per_s=th * npl / t,
+            algorithmic_flops=flops, mfma_frac=flops / (t / npl) / 1e12 / BF16_PEAK_TFLOPS)
+        log(f"polynomial forward: {t / npl * 1e3:.4f} ms/call")
+        del qp, kp, vp, op, wsp
 
     if a.only in ("all",):
         for i in range(2):

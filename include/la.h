@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 4
+#define LA_ABI_VERSION 5
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
 
@@ -65,7 +65,8 @@ typedef enum {
                                  la_forward_causal_features (with D = F) */
     LA_OP_FWD_NONCAUSAL = 1,  /* la_forward_noncausal */
     LA_OP_BWD_CAUSAL = 2,     /* la_backward_causal */
-    LA_OP_BWD_NONCAUSAL = 3   /* la_backward_noncausal */
+    LA_OP_BWD_NONCAUSAL = 3,  /* la_backward_noncausal */
+    LA_OP_FWD_CAUSAL_POLY2 = 4 /* la_forward_causal_poly2 */
 } la_op_t;
 
 /*
@@ -113,6 +114,23 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
                                     float *z_final, int64_t B, int64_t H, int64_t N, int64_t D,
                                     int64_t M, la_dtype_t dt, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal forward with the degree-2 polynomial kernel ([summary] 3.2.1: a
+ * degree-2 polynomial kernel has an exact finite feature map).  Reading:
+ * sim(q, k) = (q . k)^2, i.e. phi(x) = vec(x x^T) with D^2 features:
+ *   out_i = sum_{j<=i} (q_i . k_j)^2 v_j / sum_{j<=i} (q_i . k_j)^2.
+ * No feature map is applied to q, k beyond that (no elu).  q, k:
+ * [B][H][N][D]; v, out: [B][H][N][M]; D = 32 only (LA_ERR_UNSUPPORTED
+ * otherwise), M in {32, 64}; workspace
+ * la_workspace_size(LA_OP_FWD_CAUSAL_POLY2, ...): one fp32 record of
+ * (M + 1) D^2 floats per segment.  A query orthogonal to every earlier key
+ * has a zero denominator; nothing guards it.  Errors as la_forward_causal.
+ */
+la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v, void *out,
+                                    int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                    la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /*
  * Random Fourier features ([summary] 5: approximating the RBF kernel with

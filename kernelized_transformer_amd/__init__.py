@@ -12,6 +12,7 @@ Functions carry the C names:
   la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None)
   la_forward_causal_features(fq, fk, v, out=None, workspace=None)
   la_rff_features(x, omega, bias, out=None)
+  la_forward_causal_poly2(q, k, v, out=None, workspace=None)
   la_forward_noncausal(q, k, v, out=None, workspace=None)
   la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
@@ -27,13 +28,14 @@ import os
 import torch
 
 __all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
-           "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
+           "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
            "la_decode_step",
            "la_workspace_size", "la_status_string", "la_abi_version", "LAError", "lib_path", "load",
-           "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
+           "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL",
+           "LA_OP_FWD_CAUSAL_POLY2", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
-LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3
+LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL, LA_OP_FWD_CAUSAL_POLY2 = 0, 1, 2, 3, 4
 _DT = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,8 +67,10 @@ def load():
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_causal_features.argtypes = fwd
+    lib.la_forward_causal_poly2.argtypes = fwd
     lib.la_rff_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
+              "la_forward_causal_poly2",
               "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step"):
         getattr(lib, f).restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
@@ -177,6 +181,11 @@ def la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=Non
 def la_forward_causal_features(fq, fk, v, out=None, workspace=None):
     """Causal linear attention on given features fq, fk [B,H,N,F] (no feature map applied); returns out."""
     return _forward("la_forward_causal_features", LA_OP_FWD_CAUSAL, fq, fk, v, out, workspace)
+
+
+def la_forward_causal_poly2(q, k, v, out=None, workspace=None):
+    """Causal attention with the degree-2 polynomial kernel (q . k)^2 (D = 32); returns out [B,H,N,M]."""
+    return _forward("la_forward_causal_poly2", LA_OP_FWD_CAUSAL_POLY2, q, k, v, out, workspace)
 
 
 def la_rff_features(x, omega, bias, out=None):

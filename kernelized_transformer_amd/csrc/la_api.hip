@@ -151,6 +151,26 @@ la_status_t la_forward_causal_features(const void *fq, const void *fk, const voi
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
+                                    int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, D, M, dt);
+    if (st != LA_OK) return st;
+    if (D != 32) return LA_ERR_UNSUPPORTED;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[3] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
+                        span(v, size_t(BH * N * M) * es)};
+    const Span o[1] = {span(out, size_t(BH * N * M) * es)};
+    if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
+    const Span all[4] = {in[0], in[1], in[2], o[0]};
+    if ((st = check_workspace(workspace, workspace_bytes, la::poly_workspace_bytes(BH, N, M), all, 4)) != LA_OK)
+        return st;
+    const hipError_t e = la::launch_poly_forward(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+                                                 static_cast<float *>(workspace), stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 la_status_t la_rff_features(const void *x, const float *omega, const float *bias, void *out, int64_t B, int64_t H,
                             int64_t N, int64_t D, int64_t R, la_dtype_t dt, hipStream_t stream) {
     la_status_t st = check_shape(B, H, N, D, R, dt);
@@ -236,6 +256,8 @@ size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D,
         return la::backward_workspace_bytes(B * H, N, D, M, esize(dt));
     case LA_OP_BWD_NONCAUSAL:
         return la::backward_noncausal_workspace_bytes(B * H, N, D, M);
+    case LA_OP_FWD_CAUSAL_POLY2:
+        return D == 32 ? la::poly_workspace_bytes(B * H, N, M) : 0;
     }
     return 0;
 }

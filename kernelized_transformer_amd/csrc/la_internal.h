@@ -155,6 +155,12 @@ struct StateIO {
 hipError_t launch_rff_features(int dt, const void *x, const float *omega, const float *bias, void *out, int64_t rows,
                                int64_t D, int64_t R, hipStream_t s);
 
+// Causal forward with the degree-2 polynomial kernel (q . k)^2, D = 32,
+// M in {32, 64}; workspace: one [M + 1][32][32] fp32 record per segment.
+size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t M);
+hipError_t launch_poly_forward(int dt, const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N,
+                               int64_t D, int64_t M, float *ws, hipStream_t s);
+
 // Launchers (hipError_t of the last launch).  dt: 0 = fp32, 1 = bf16.
 hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
                           int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s,

@@ -22,13 +22,13 @@ HEADER = os.path.join(ROOT, "include", "la.h")
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(la_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
-              "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
+              "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
               "la_workspace_size", "la_status_string", "la_abi_version"):
         assert f in fns
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 4
+    assert la.la_abi_version() == 5
     names = [la.la_status_string(s) for s in range(5)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
     assert la.la_status_string(99) == "LA_ERR_UNKNOWN"
@@ -60,6 +60,10 @@ def test_workspace_size():
     assert nb > 0 and nb % 256 == 0 and nb < f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
     assert f(la.LA_OP_BWD_NONCAUSAL, 1, 8, 65536, 64, 64, torch.bfloat16) < 64 * 2 ** 20
     assert f(7, 1, 2, 256, 32, 32, torch.float32) == 0                        # unknown op
+    # polynomial kernel: one (M + 1) x 32 x 32 fp32 record per segment, D = 32 only
+    pw = f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 32, 64, torch.bfloat16)
+    assert pw > 0 and pw % 256 == 0 and pw >= 2 * 65 * 32 * 32 * 4
+    assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 64, 64, torch.bfloat16) == 0
     assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) == 0     # unsupported D
     # grows linearly in N at fixed segment count ceiling
@@ -114,6 +118,15 @@ def test_forward_state_argument_errors():
     assert fs(s1=b[0]) == 1                         # final state over q
     assert fs(D=48) == 2
     assert fs(ws=b[6], wsb=1 << 20) == 3            # workspace overlaps the final state
+
+
+def test_poly2_argument_errors():
+    lib = la.load()
+    assert _fwd(lib, "la_forward_causal_poly2", D=64) == 2           # D = 32 only
+    assert _fwd(lib, "la_forward_causal_poly2", M=16) == 2
+    assert _fwd(lib, "la_forward_causal_poly2", q=0) == 1
+    assert _fwd(lib, "la_forward_causal_poly2", out=FAKE + 64) == 1
+    assert _fwd(lib, "la_forward_causal_poly2", wsb=16) == 3
 
 
 def test_rff_argument_errors():

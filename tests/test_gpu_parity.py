@@ -396,6 +396,28 @@ def test_forward_features_mixed_sign(name, w):
     check(f"out[{name}]", host(out), oracle.forward_causal_features(fq, fk, v), w.dtype)
 
 
+# Degree-2 polynomial kernel (q . k)^2, D = 32.
+POLY_CASES = [
+    ("w1_f32", wl.WORKLOADS[1]),
+    ("w2_f32", wl.WORKLOADS[2]),
+    ("w3_bf16", wl.WORKLOADS[3]),
+    ("n1_bf16_m64", _wl(221, 2, 2, 1, 32, 64, "bf16")),
+    ("n17_f32_m64", _wl(222, 1, 3, 17, 32, 64, "f32")),
+    ("n1001_ragged_bf16_m64", _wl(223, 2, 3, 1001, 32, 64, "bf16")),
+    ("n100000_many_segments", _wl(224, 1, 1, 100000, 32, 32, "bf16")),
+    ("long_b1h8n65536_d32", _wl(225, 1, 8, 65536, 32, 32, "bf16")),
+]
+
+
+@pytest.mark.parametrize("name,w", POLY_CASES, ids=[c[0] for c in POLY_CASES])
+def test_forward_causal_poly2(name, w):
+    q, k, v = wl.forward_inputs(w)
+    _say(f"polynomial forward {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    out = la.la_forward_causal_poly2(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    check(f"out[{name}]", host(out), oracle.forward_causal_poly2(q, k, v), w.dtype)
+
+
 def test_forward_deterministic_and_guarded():
     w = _wl(141, 2, 3, 1500, 64, 64, "bf16")
     q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
