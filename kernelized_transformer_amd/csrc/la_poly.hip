@@ -76,50 +76,86 @@ __device__ __forceinline__ void poly_store(float *rec, const f32x4 (&X)[NX][2][2
     }
 }
 
-// The chunk's inputs as one wavefront needs them.  Rows at or beyond t_end
-// read row t_end - 1; their K rows are zeroed, which removes them from every
-// product (the rows of Q only reach outputs that are not stored).
-template <typename T, int M> struct PolyChunk {
+// Two consecutive chunks (32 tokens from t0) as one wavefront needs them.
+// Rows at or beyond t_end read row t_end - 1 (addresses: a uniform base
+// pointer per pair plus 32-bit lane offsets).
+template <typename T, int M> struct PolyPair {
     typedef PolyCfg<T, M> C;
     typedef typename IO<T>::vec4 V4;
-    V4 rq[1][C::DT], rk[1][C::DT];
-    f32x4 wv[C::MW];   // wv[x][r] = v[t0 + 4g + r][m0 + x]
+    V4 rq[2][C::DT], rk[2][C::DT];   // natural rows: token 16h + c, features 16 ft + 4g ..
+    V4 rv[2][4];                     // rv[h][r] = v[t0 + 16h + 4g + r][m0 .. m0 + 3]
 
-    __device__ __forceinline__ void load(const T *Q, const T *K, const T *V, int64_t t0, int64_t t_end, int m0,
+    __device__ __forceinline__ void load(const T *Qh, const T *Kh, const T *Vh, int64_t t0, int64_t t_end, int m0,
                                          bool with_q) {
-        if (with_q) load_chunk<T, kPolyD, 1>(rq, Q, t0, t_end);
-        load_chunk<T, kPolyD, 1>(rk, K, t0, t_end);
-        const int g = lane_id() >> 4;
+        const int c = lane_id() & 15, g = lane_id() >> 4;
+        const int lim = int(min<int64_t>(t_end - 1 - t0, 64));   // last valid row, relative (may be < 0)
+        const T *qb = Qh + t0 * kPolyD, *kb = Kh + t0 * kPolyD, *vb = Vh + t0 * M;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t t = min(t0 + 4 * g + r, t_end - 1);
+        for (int h = 0; h < 2; ++h) {
+            const int row = min(16 * h + c, lim);
 #pragma unroll
-            for (int x = 0; x < C::MW; x += 4) {
-                const f32x4 v4 = IO<T>::to_f32(load4<T>(V + t * M + m0 + x));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) wv[x + e][r] = v4[e];
+            for (int ft = 0; ft < C::DT; ++ft) {
+                if (with_q) rq[h][ft] = load4<T>(qb + row * kPolyD + 16 * ft + 4 * g);
+                rk[h][ft] = load4<T>(kb + row * kPolyD + 16 * ft + 4 * g);
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rv[h][r] = load4<T>(vb + min(16 * h + 4 * g + r, lim) * M + m0);
         }
+    }
+    // wv[h][x][r] = v[t0 + 16h + 4g + r][m0 + x]
+    __device__ __forceinline__ void values(f32x4 (&wv)[2][C::MW]) const {
+        static_assert(C::MW == 4, "four columns per wavefront");
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 v4 = IO<T>::to_f32(rv[h][r]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) wv[h][x][r] = v4[x];
+            }
     }
 };
 
-// X += (w o K)^T K for every matrix of the wavefront: KT are the chunk's
-// token-contiguous K fragments (lane (c, g): k[4g + r][16 at + c]).
-template <typename T, int M, int NX>
-__device__ __forceinline__ void poly_update(f32x4 (&X)[NX][2][2], const typename IO<T>::frag (&KT)[1][kPolyD / 16],
-                                            const f32x4 (&KTf)[kPolyD / 16], const f32x4 *wv, int nx) {
+// Pairs of chunks in flight per wavefront (the loops are unrolled by this
+// many so that pair i always lives in buffer i % PF).
+template <typename T, int M> constexpr int poly_ahead() { return (sizeof(T) == 2 && M == 32) ? 2 : 1; }
+
+// X += (w o K)^T K over the pair's 32 tokens (one 32-deep product per tile):
+// KT[h] are token-contiguous K fragments of chunk h (lane (c, g):
+// k[16h + 4g + r][16 at + c]), KTf the same in fp32.
+template <typename T, int NX>
+__device__ __forceinline__ void poly_update(f32x4 (&X)[NX][2][2], const typename IO<T>::frag (&KT)[2][kPolyD / 16],
+                                            const f32x4 (&KTf)[2][kPolyD / 16], const f32x4 (&wv)[2][NX - 1],
+                                            int nx) {
     typedef typename IO<T>::frag Fr;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
         if (x < nx) {
 #pragma unroll
             for (int at = 0; at < 2; ++at) {
-                const Fr a = (x < NX - 1) ? IO<T>::to_frag(KTf[at] * wv[x]) : KT[0][at];
+                const Fr a0 = (x < NX - 1) ? IO<T>::to_frag(KTf[0][at] * wv[0][x]) : KT[0][at];
+                const Fr a1 = (x < NX - 1) ? IO<T>::to_frag(KTf[1][at] * wv[1][x]) : KT[1][at];
 #pragma unroll
-                for (int bt = 0; bt < 2; ++bt) mma1(X[x][at][bt], a, KT[0][bt]);
+                for (int bt = 0; bt < 2; ++bt) mma2(X[x][at][bt], a0, a1, KT[0][bt], KT[1][bt]);
             }
         }
     }
+}
+
+// Zero the token-contiguous rows (tokens 16h + 4g + r) at or beyond lim + 1.
+template <typename T>
+__device__ __forceinline__ void poly_mask_rows(typename IO<T>::frag (&KT)[2][kPolyD / 16], f32x4 (&KTf)[2][kPolyD / 16],
+                                               int lim) {
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ft = 0; ft < kPolyD / 16; ++ft) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * h + 4 * g + r > lim) KTf[h][ft][r] = 0.f;
+            KT[h][ft] = IO<T>::to_frag(KTf[h][ft]);
+        }
 }
 
 template <typename T, int M>
@@ -137,7 +173,7 @@ __global__ __launch_bounds__(64 * kPolyWaves) void k_poly_segment_state(const T 
     const int m0 = cb * kPolyCols + wave * C::MW;
     const T *K = k + bh * N * kPolyD;
     const T *V = v + bh * N * M;
-    __shared__ bf16 stage_mem[kPolyWaves][stage_elems<C::DT, 1>()];
+    __shared__ bf16 stage_mem[kPolyWaves][stage_elems<C::DT, 2>()];
     lds_bf16 *stage = (lds_bf16 *)stage_mem[wave];
     const bool owns_z = cb == 0 && wave == 0;   // Z is summed and stored once per segment
 
@@ -150,19 +186,33 @@ __global__ __launch_bounds__(64 * kPolyWaves) void k_poly_segment_state(const T 
             for (int bt = 0; bt < 2; ++bt) X[x][at][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nx = owns_z ? C::NX : C::NX - 1;
 
+    constexpr int PF = poly_ahead<T, M>();
     if (t_begin < t_end) {
-        PolyChunk<T, M> cur, nxt;
-        cur.load(nullptr, K, V, t_begin, t_end, m0, false);
-        for (int64_t t0 = t_begin; t0 < t_end; t0 += 16) {
-            if (t0 + 16 < t_end) nxt.load(nullptr, K, V, t0 + 16, t_end, m0, false);
-            Fr Kn[1][C::DT], KT[1][C::DT];
-            raw_frags<T, kPolyD, 1>(Kn, cur.rk, t0, t_end);
-            transpose_frags<C::DT, 1>(KT, Kn, stage);
-            f32x4 KTf[C::DT];
+        PolyPair<T, M> buf[PF];
 #pragma unroll
-            for (int at = 0; at < C::DT; ++at) KTf[at] = IO<T>::to_f32(KT[0][at]);
-            poly_update<T, M, C::NX>(X, KT, KTf, cur.wv, nx);
-            cur = nxt;
+        for (int b = 0; b < PF; ++b) buf[b].load(nullptr, K, V, t_begin + 32 * b, t_end, m0, false);
+        for (int64_t t00 = t_begin; t00 < t_end; t00 += 32 * PF) {
+#pragma unroll
+            for (int b = 0; b < PF; ++b) {
+                const int64_t t0 = t00 + 32 * b;   // may lie past t_end: every row masked, adds nothing
+                Fr Kn[2][C::DT], KT[2][C::DT];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int ft = 0; ft < C::DT; ++ft) Kn[h][ft] = IO<T>::to_frag(IO<T>::to_f32(buf[b].rk[h][ft]));
+                f32x4 wv[2][C::MW];
+                buf[b].values(wv);
+                buf[b].load(nullptr, K, V, t0 + 32 * PF, t_end, m0, false);
+                transpose_frags<C::DT, 2>(KT, Kn, stage);
+                f32x4 KTf[2][C::DT];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int at = 0; at < C::DT; ++at) KTf[h][at] = IO<T>::to_f32(KT[h][at]);
+                const int lim = int(min<int64_t>(t_end - 1 - t0, 64));
+                if (lim < 31) poly_mask_rows<T>(KT, KTf, lim);   // the segment's last, partial pair
+                poly_update<T, C::NX>(X, KT, KTf, wv, nx);
+            }
         }
     }
     poly_store<M, C::NX>(ws + (bh * nseg + seg) * rec, X, m0, owns_z);
@@ -186,62 +236,102 @@ __global__ __launch_bounds__(64 * kPolyWaves) void k_poly_output(const T *__rest
     const T *K = k + bh * N * kPolyD;
     const T *V = v + bh * N * M;
     T *O = out + bh * N * M;
-    __shared__ bf16 stage_mem[kPolyWaves][stage_elems<C::DT, 1>()];
+    __shared__ bf16 stage_mem[kPolyWaves][stage_elems<C::DT, 2>()];
     lds_bf16 *stage = (lds_bf16 *)stage_mem[wave];
 
     f32x4 X[C::NX][2][2];
     poly_load<M, C::NX>(X, ws + (bh * nseg + seg) * rec, m0);
     const Fr ones = frag_ones<Fr>();
     const bool diag = (c >> 2) == g;   // this lane holds token c's results
+    const int e = c & 3;               // ... in element c % 4
 
-    PolyChunk<T, M> cur, nxt;
-    cur.load(Q, K, V, t_begin, t_end, m0, true);
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 16) {
-        if (t0 + 16 < t_end) nxt.load(Q, K, V, t0 + 16, t_end, m0, true);
-        Fr Qn[1][C::DT], Kn[1][C::DT], KT[1][C::DT];
-        raw_frags<T, kPolyD, 1>(Qn, cur.rq, t0, t_end);
-        raw_frags<T, kPolyD, 1>(Kn, cur.rk, t0, t_end);
-        transpose_frags<C::DT, 1>(KT, Kn, stage);
-        f32x4 KTf[C::DT];
+    // No row masks: rows past t_end only reach outputs that are not stored
+    // (the causal mask keeps them out of the others), and the state is not
+    // used after the segment's last pair.  fp32 pairs are loaded where they
+    // are used (a pair in flight would cost 64 more registers).
+    constexpr int PF = poly_ahead<T, M>();
+    constexpr bool kAhead = sizeof(T) == 2;
+    PolyPair<T, M> buf[PF];
+    if (kAhead) {
 #pragma unroll
-        for (int at = 0; at < C::DT; ++at) KTf[at] = IO<T>::to_f32(KT[0][at]);
-
-        // P^T[j][i] = (q_i . k_j)^2, j <= i; as a fragment it is P (rows i, contraction j)
-        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
-        mma2(pt, Kn[0][0], Kn[0][1], Qn[0][0], Qn[0][1]);
+        for (int b = 0; b < PF; ++b) buf[b].load(Q, K, V, t_begin + 32 * b, t_end, m0, true);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += 32 * PF) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pt[r] = (4 * g + r <= c) ? pt[r] * pt[r] : 0.f;
-        const Fr Pf = IO<T>::to_frag(pt);
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + 32 * b;   // may lie past t_end: nothing stored
+        if (!kAhead) buf[b].load(Q, K, V, t0, t_end, m0, true);
+        Fr Qn[2][C::DT], Kn[2][C::DT], KT[2][C::DT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ft = 0; ft < C::DT; ++ft) {
+                Qn[h][ft] = IO<T>::to_frag(IO<T>::to_f32(buf[b].rq[h][ft]));
+                Kn[h][ft] = IO<T>::to_frag(IO<T>::to_f32(buf[b].rk[h][ft]));
+            }
+        f32x4 wv[2][C::MW];
+        buf[b].values(wv);
+        if (kAhead) buf[b].load(Q, K, V, t0 + 32 * PF, t_end, m0, true);
+        transpose_frags<C::DT, 2>(KT, Kn, stage);
+        f32x4 KTf[2][C::DT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int at = 0; at < C::DT; ++at) KTf[h][at] = IO<T>::to_f32(KT[h][at]);
 
-        float res[C::NX];
+        // P^T[j][i] = (q_i . k_j)^2 for key chunk hk, query chunk hq (masked to
+        // j <= i on the diagonal blocks); as fragments they are P (rows i,
+        // contraction j)
+        Fr Pf[3];   // (keys 0, queries 0), (keys 0, queries 1), (keys 1, queries 1)
+#pragma unroll
+        for (int pi = 0; pi < 3; ++pi) {
+            const int hk = pi == 2 ? 1 : 0, hq = pi == 0 ? 0 : 1;
+            f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+            mma2(pt, Kn[hk][0], Kn[hk][1], Qn[hq][0], Qn[hq][1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pt[r] = (hk != hq || 4 * g + r <= c) ? pt[r] * pt[r] : 0.f;
+            Pf[pi] = IO<T>::to_frag(pt);
+        }
+
+        float res[2][C::NX];
 #pragma unroll
         for (int x = 0; x < C::NX; ++x) {
-            // U^T tiles (rows b, cols tokens) from X^T (the Acc tile is the operand as it is)
-            f32x4 u[2];
+            Fr Xf[2][2];
 #pragma unroll
-            for (int bt = 0; bt < 2; ++bt) {
-                u[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mma2(u[bt], IO<T>::to_frag(X[x][0][bt]), IO<T>::to_frag(X[x][1][bt]), Qn[0][0], Qn[0][1]);
+            for (int at = 0; at < 2; ++at)
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt) Xf[at][bt] = IO<T>::to_frag(X[x][at][bt]);
+            const Fr w0 = (x < C::NX - 1) ? IO<T>::to_frag(wv[0][x]) : ones;
+            const Fr w1 = (x < C::NX - 1) ? IO<T>::to_frag(wv[1][x]) : ones;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // U^T tiles (rows b, cols tokens of chunk h) from X^T (the Acc tile is the operand)
+                f32x4 u[2];
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt) {
+                    u[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    mma2(u[bt], Xf[0][bt], Xf[1][bt], Qn[h][0], Qn[h][1]);
+                }
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                mma2(d, IO<T>::to_frag(u[0]), IO<T>::to_frag(u[1]), Qn[h][0], Qn[h][1]);
+                if (h == 0)
+                    mma1(d, Pf[0], w0);
+                else
+                    mma2(d, Pf[1], Pf[2], w0, w1);
+                res[h][x] = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
             }
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            mma2(d, IO<T>::to_frag(u[0]), IO<T>::to_frag(u[1]), Qn[0][0], Qn[0][1]);
-            const Fr w = (x < C::NX - 1) ? IO<T>::to_frag(cur.wv[x]) : ones;
-            mma1(d, Pf, w);
-            // diagonal: token c sits in element c % 4 of lane (c, c / 4)
-            const int e = c & 3;
-            res[x] = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
         }
-        poly_update<T, M, C::NX>(X, KT, KTf, cur.wv, C::NX);
+        poly_update<T, C::NX>(X, KT, KTf, wv, C::NX);
 
-        const float inv = __builtin_amdgcn_rcpf(res[C::NX - 1]);
-        const int64_t t = t0 + c;
-        if (diag && t < t_end) {
 #pragma unroll
-            for (int x = 0; x < C::MW; x += 4)
-                store4<T>(O + t * M + m0 + x,
-                          IO<T>::from_f32(f32x4{res[x] * inv, res[x + 1] * inv, res[x + 2] * inv, res[x + 3] * inv}));
+        for (int h = 0; h < 2; ++h) {
+            const float inv = __builtin_amdgcn_rcpf(res[h][C::NX - 1]);
+            const int64_t t = t0 + 16 * h + c;
+            if (diag && t < t_end)
+                store4<T>(O + t * M + m0, IO<T>::from_f32(f32x4{res[h][0] * inv, res[h][1] * inv, res[h][2] * inv,
+                                                                res[h][3] * inv}));
         }
-        cur = nxt;
+    }
     }
 }
 
