@@ -258,27 +258,39 @@ __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, c
     }
 }
 
+// The rows of the first PF chunks of seg_output_bf16, loaded ahead (the
+// causal forward issues them before its cross-workgroup hand-off, while the
+// memory system is idle).
+template <int D, int M, int PF> struct OutAhead {
+    dwordx4 rq[PF][Lines<D, TT>::n], rk[PF][Lines<D, TT>::n], rv[PF][Lines<M, TT>::n];
+    template <bool CAUSAL>
+    __device__ __forceinline__ void load(const bf16 *Q, const bf16 *K, const bf16 *V, int64_t t_begin,
+                                         int64_t t_end) {
+#pragma unroll
+        for (int b = 0; b < PF; ++b) {
+            load_lines<D, TT>(rq[b], Q, t_begin + b * CH, t_end);
+            if (CAUSAL) {
+                load_lines<D, TT>(rk[b], K, t_begin + b * CH, t_end);
+                load_lines<M, TT>(rv[b], V, t_begin + b * CH, t_end);
+            }
+        }
+    }
+};
+
 template <int D, int M, bool CAUSAL, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                 const bf16 *__restrict__ V, bf16 *__restrict__ O, int64_t t_begin,
                                                 int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *sq,
-                                                lds_bf16 *sk, lds_bf16 *sv, lds_bf16 *so) {
+                                                lds_bf16 *sk, lds_bf16 *sv, lds_bf16 *so, OutAhead<D, M, PF> &ahead) {
     typedef bf16x4 Fr;
     constexpr int DT = D / 16, MT = M / 16;
-    constexpr int NQ = Lines<D, TT>::n, NV = Lines<M, TT>::n;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
     const Fr ones = frag_ones<Fr>();
     const Fr zero = frag_zero<Fr>();
 
-    dwordx4 rq[PF][NQ], rk[PF][NQ], rv[PF][NV];
-#pragma unroll
-    for (int b = 0; b < PF; ++b) {
-        load_lines<D, TT>(rq[b], Q, t_begin + b * CH, t_end);
-        if (CAUSAL) {
-            load_lines<D, TT>(rk[b], K, t_begin + b * CH, t_end);
-            load_lines<M, TT>(rv[b], V, t_begin + b * CH, t_end);
-        }
-    }
+    auto &rq = ahead.rq;
+    auto &rk = ahead.rk;
+    auto &rv = ahead.rv;
     for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
@@ -684,6 +696,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
 
+    // pass 2's first chunks, loaded while the workgroups exchange their state
+    OutAhead<D, M, kPrefetch> ahead;
+    if constexpr (sizeof(T) == 2) ahead.template load<true>(Q, K, V, t_begin, t_end);
+
     // Initial state (zero unless given), this thread's record elements.  Read
     // here, before the block publishes anything: the last block of the head
     // writes the final state only after every block has published, so the
@@ -803,7 +819,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     __syncthreads();   // the prefix is read: the staging area is free again
     if constexpr (sizeof(T) == 2)
         seg_output_bf16<D, M, true, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q,
-                                                    stage_k, stage_v, stage_v + SV);
+                                                    stage_k, stage_v, stage_v + SV, ahead);
     else
         seg_output<T, D, M, true, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_k, stage_v);
 }
