@@ -234,26 +234,36 @@ template <int D, int M, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, const bf16 *__restrict__ V,
                                                    int64_t t_begin, int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1],
                                                    lds_bf16 *sk, lds_bf16 *sv) {
+    // The chunks are visited last to first, so that the wavefront's first
+    // chunks are the most recently read when its output pass starts with them
+    // (and are often still in L2).  Step s visits chunk nch - 1 - s; steps
+    // past the first chunk (s >= nch) re-read chunk 0 and add nothing.
     constexpr int NK = Lines<D, TT>::n, NV = Lines<M, TT>::n;
+    const int64_t nch = (t_end - t_begin + CH - 1) / CH;
+    auto chunk = [&](int64_t step) { return t_begin + max<int64_t>(nch - 1 - step, 0) * CH; };
     dwordx4 rk[PF][NK], rv[PF][NV];
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
-        load_lines<D, TT>(rk[b], K, t_begin + b * CH, t_end);
-        load_lines<M, TT>(rv[b], V, t_begin + b * CH, t_end);
+        load_lines<D, TT>(rk[b], K, chunk(b), t_end);
+        load_lines<M, TT>(rv[b], V, chunk(b), t_end);
     }
-    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
+    for (int64_t s0 = 0; s0 < nch; s0 += PF) {
 #pragma unroll
         for (int b = 0; b < PF; ++b) {
-            const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked
-            stage_lines<D, TT, PHI, true>(sk, rk[b], t0, t_end);
-            stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
-            load_lines<D, TT>(rk[b], K, t0 + PF * CH, t_end);
-            load_lines<M, TT>(rv[b], V, t0 + PF * CH, t_end);
+            const int64_t step = s0 + b, t0 = chunk(step);
+            if (step < nch) {   // uniform
+                stage_lines<D, TT, PHI, true>(sk, rk[b], t0, t_end);   // rows past t_end masked
+                stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
+            }
+            load_lines<D, TT>(rk[b], K, chunk(step + PF), t_end);
+            load_lines<M, TT>(rv[b], V, chunk(step + PF), t_end);
             __builtin_amdgcn_sched_barrier(0);
-            bf16x4 KT[TT][D / 16], VT[TT][M / 16];
-            transposed_frags_lds<D, TT>(KT, sk);
-            transposed_frags_lds<M, TT>(VT, sv);
-            state_accumulate<bf16x4, D, M, TT, true>(St, KT, VT);
+            if (step < nch) {
+                bf16x4 KT[TT][D / 16], VT[TT][M / 16];
+                transposed_frags_lds<D, TT>(KT, sk);
+                transposed_frags_lds<M, TT>(VT, sv);
+                state_accumulate<bf16x4, D, M, TT, true>(St, KT, VT);
+            }
         }
     }
 }
