@@ -418,6 +418,37 @@ def test_forward_causal_poly2(name, w):
     check(f"out[{name}]", host(out), oracle.forward_causal_poly2(q, k, v), w.dtype)
 
 
+def test_forward_causal_longest_sequence():
+    """One head of 2^20 tokens (64 workgroups of 8 wavefronts, 2048 tokens
+    each), checked element by element, with its final state."""
+    w = _wl(231, 1, 1, 1 << 20, 32, 32, "bf16")
+    q, k, v = wl.forward_inputs(w)
+    _say(f"longest sequence: B1 H1 N{w.N} D32 M32 bf16")
+    out, S, Z = la.la_forward_causal_state(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    ref, S_ref, Z_ref = oracle.forward_causal(q, k, v, return_state=True)
+    check("out", host(out), ref, w.dtype)
+    check("S_N", host(S), S_ref, w.dtype)
+    check("Z_N", host(Z), Z_ref, w.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_causal_closed_forms(dtype):
+    """Constant V gives V back; identical keys give the running mean of V
+    whatever Q is (closed forms of the method, no oracle involved)."""
+    w = _wl(232, 2, 3, 5000, 64, 64, dtype)
+    q, k, v = wl.forward_inputs(w)
+    _say(f"closed forms on the GPU, {dtype}")
+    vc = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    out_c = host(la.la_forward_causal(dev(q, dtype), dev(k, dtype), dev(vc, dtype)))
+    ks = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    out_k = host(la.la_forward_causal(dev(q, dtype), dev(ks, dtype), dev(v, dtype)))
+    torch.cuda.synchronize()
+    check("constant V", out_c, vc.astype(np.float64), dtype)
+    mean = np.cumsum(v.astype(np.float64), axis=2) / np.arange(1, w.N + 1)[None, None, :, None]
+    check("identical keys", out_k, mean, dtype)
+
+
 def test_forward_deterministic_and_guarded():
     w = _wl(141, 2, 3, 1500, 64, 64, "bf16")
     q, k, v = (dev(x, w.dtype) for x in wl.forward_inputs(w))
