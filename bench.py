@@ -52,7 +52,8 @@ def _args():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly"], default="all",
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal"],
+                    default="all",
                     help="restrict the timed work (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device three times (a plain copy kernel of known size, "
@@ -363,7 +364,7 @@ def main():
         log(f"polynomial forward: {t / npl * 1e3:.4f} ms/call")
         del qp, kp, vp, op, wsp
 
-    if a.only in ("all",):
+    if a.only in ("all", "noncausal"):
         for i in range(2):
             fwd(i, causal=False)
         t = time_events(lambda i: fwd(i, causal=False), a.steps)

@@ -170,7 +170,10 @@ la_status_t la_forward_causal_features(const void *fq, const void *fk, const voi
  * Non-causal forward through associativity ([review] "Proposed method";
  * [summary] 3.2; [deck] slide 3): S = sum_j phi(K_j) V_j^T and
  * Z = sum_j phi(K_j) over all N tokens of each (b, h), then
- * out_i = phi(Q_i)^T S / (phi(Q_i)^T Z).  Same arguments as the causal call.
+ * out_i = phi(Q_i)^T S / (phi(Q_i)^T Z).  Same arguments as the causal call,
+ * and the same execution: one launch whose workgroups of a (b, h) exchange
+ * their partial sums through the workspace and wait for each other (bounded
+ * waits; the same co-residency limits and diagnostic word at byte 4).
  */
 la_status_t la_forward_noncausal(const void *q, const void *k, const void *v, void *out,
                                  int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,

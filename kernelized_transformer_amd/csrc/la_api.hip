@@ -71,7 +71,7 @@ la_status_t forward_common(bool causal, const void *q, const void *k, const void
     const Span o[1] = {span(out, size_t(BH * N * M) * es)};
     if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
     const Span all[4] = {in[0], in[1], in[2], o[0]};
-    const size_t need = causal ? la::causal_workspace_bytes(BH, N, D, M) : la::forward_workspace_bytes(BH, N, D, M);
+    const size_t need = la::causal_workspace_bytes(BH, N, D, M);   // the same plan for both forwards
     if ((st = check_workspace(workspace, workspace_bytes, need, all, 4)) != LA_OK) return st;
     const hipError_t e = la::launch_forward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
                                             static_cast<float *>(workspace), stream);
@@ -251,7 +251,7 @@ size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D,
     case LA_OP_FWD_CAUSAL:
         return la::causal_workspace_bytes(B * H, N, D, M);
     case LA_OP_FWD_NONCAUSAL:
-        return la::forward_workspace_bytes(B * H, N, D, M);
+        return la::causal_workspace_bytes(B * H, N, D, M);
     case LA_OP_BWD_CAUSAL:
         return la::backward_workspace_bytes(B * H, N, D, M, esize(dt));
     case LA_OP_BWD_NONCAUSAL:

@@ -37,6 +37,10 @@ constexpr int TT = 1;        // token tiles per chunk in the forward kernels
 constexpr int CH = 16 * TT;  // = kChunk
 static_assert(CH == kChunk, "forward chunk");
 constexpr int kPrefetch = 2; // chunks in flight ahead of the one being computed
+// fp32 operands at D = M = 64 take twice the registers: one chunk ahead there
+template <typename T, int D, int M> constexpr int fwd_prefetch() {
+    return (sizeof(T) == 4 && D == 64 && M == 64) ? 1 : kPrefetch;
+}
 
 // ---- chunk loops ------------------------------------------------------------
 
@@ -413,96 +417,6 @@ __global__ __launch_bounds__(64) void k_segment_state(const T *__restrict__ k, c
     state_store<D, M>(ws + (bh * nseg + seg) * rec, St);
 }
 
-// Non-causal readout: out_i = phi(Q_i)^T S / phi(Q_i)^T Z with the head's
-// total (S, Z).  The state never changes, so each wavefront converts it to
-// operand tiles once and then only streams its tokens: contiguous loads of
-// Q, the feature map, one LDS staging round trip for the fragments, the
-// products, normalization and stores.  Four wavefronts per workgroup, each
-// with its own token range (kNcWaves per SIMD in flight).
-constexpr int kNcWavesPerBlock = 4;
-constexpr int64_t kNcTargetWaves = 4096;
-
-template <typename T, int D, int M>
-__global__ __launch_bounds__(64 * kNcWavesPerBlock) void k_noncausal_output(
-    const T *__restrict__ q, T *__restrict__ out, const float *__restrict__ ws, int64_t BH, int64_t N, int64_t nsub,
-    int64_t sub_tokens, int64_t nseg_rec, int64_t rec) {
-    constexpr int DT = D / 16, MT = M / 16;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = int64_t(blockIdx.x) * kNcWavesPerBlock + wave;
-    const int64_t bh = gw / nsub, sub = gw % nsub;
-    if (bh >= BH) return;   // whole wavefront; no workgroup barrier below
-    const int64_t t_begin = sub * sub_tokens;
-    const int64_t t_end = min(N, t_begin + sub_tokens);
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-    const T *Q = q + bh * N * D;
-    T *O = out + bh * N * M;
-    typedef typename IO<T>::frag Fr;
-    Fr SF[MT + 1][DT];
-    {
-        f32x4 St[DT][MT + 1];
-        state_load<D, M, true>(St, ws + bh * nseg_rec * rec);
-#pragma unroll
-        for (int mt = 0; mt <= MT; ++mt)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = IO<T>::to_frag(St[dt][mt]);
-    }
-    constexpr int SQ = stage_elems<DT, TT>(), SO = 16 * (M + kStagePad);
-    __shared__ bf16 stage_mem[kNcWavesPerBlock][SQ + SO];
-    lds_bf16 *sq = (lds_bf16 *)(&stage_mem[wave][0]);
-    lds_bf16 *so = sq + SQ;   // one 16-token output tile
-
-    auto readout = [&](int64_t t0, const Fr (&Qn)[TT][DT]) {
-#pragma unroll
-        for (int it = 0; it < TT; ++it) {
-            f32x4 Ot[MT + 1];
-#pragma unroll
-            for (int mt = 0; mt <= MT; ++mt) {
-                Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int dt = 0; dt < DT; dt += 2) mma2(Ot[mt], SF[mt][dt], SF[mt][dt + 1], Qn[it][dt], Qn[it][dt + 1]);
-            }
-            if constexpr (sizeof(T) == 2) {
-                store_tile_bf16<M>(O, t0 + 16 * it, t_end, Ot, so);
-            } else {
-                const float inv = __builtin_amdgcn_rcpf(Ot[MT][0]);   // every row of the block holds den
-                const int64_t t = t0 + 16 * it + c;
-                if (t < t_end) {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        store4<T>(O + t * M + 16 * mt + 4 * g, IO<T>::from_f32(Ot[mt] * inv));
-                }
-            }
-        }
-    };
-    if constexpr (sizeof(T) == 2) {
-        constexpr int NQ = Lines<D, TT>::n;
-        dwordx4 rq[2][NQ];
-        load_lines<D, TT>(rq[0], Q, t_begin, t_end);
-        load_lines<D, TT>(rq[1], Q, t_begin + CH, t_end);
-        for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * CH) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int64_t t0 = t00 + b * CH;   // may lie past t_end: no stores
-                stage_lines<D, TT, true, false>(sq, rq[b], t0, t_end);
-                load_lines<D, TT>(rq[b], Q, t0 + 2 * CH, t_end);
-                __builtin_amdgcn_sched_barrier(0);
-                Fr Qn[TT][DT];
-                natural_frags_lds<D, TT>(Qn, sq);
-                readout(t0, Qn);
-            }
-        }
-    } else {
-        typedef typename IO<T>::vec4 V4;
-        V4 rq[TT][DT];
-        load_chunk<T, D, TT>(rq, Q, t_begin, t_end);
-        for (int64_t t0 = t_begin; t0 < t_end; t0 += CH) {
-            Fr Qn[TT][DT];
-            phi_frags<T, D, TT>(Qn, rq, t0, t_end);
-            load_chunk<T, D, TT>(rq, Q, t0 + CH, t_end);
-            readout(t0, Qn);
-        }
-    }
-}
 
 // ---- scan over segments ---------------------------------------------------
 // Block = kScanCols float4 columns of the records x kScanG groups of
@@ -652,7 +566,10 @@ __device__ __forceinline__ void wait_flags(const unsigned long long *flags, int 
 }
 
 // PHI = false: q and k hold the features already (no feature map applied).
-template <typename T, int D, int M, bool PHI>
+// CAUSAL = false: the non-causal forward -- every block publishes its total,
+// the slice owners form the head's full sum (one record), and every
+// wavefront reads its queries out against it.
+template <typename T, int D, int M, bool PHI, bool CAUSAL = true>
 __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_fwd_fused(const T *__restrict__ q, const T *__restrict__ k,
                                                                 const T *__restrict__ v, T *__restrict__ out,
                                                                 int *__restrict__ header,
@@ -678,7 +595,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     f32x4 *slot4 = reinterpret_cast<f32x4 *>(lds_raw);
     auto slot = [&](int w) { return reinterpret_cast<float *>(slot4 + w * SLOT4); };
     float *pbuf = slot(0);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
 
     const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
@@ -701,14 +618,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     if constexpr (sizeof(T) == 2)
         seg_aggregate_bf16<D, M, kPrefetch, PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
     else
-        seg_aggregate<T, D, M, kPrefetch, PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
+        seg_aggregate<T, D, M, fwd_prefetch<T, D, M>(), PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
     __syncthreads();   // every wavefront is done with its staging area
     state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
 
     // pass 2's first chunks, loaded while the workgroups exchange their state
     OutAhead<D, M, kPrefetch> ahead;
-    if constexpr (sizeof(T) == 2) ahead.template load<true>(Q, K, V, t_begin, t_end);
+    if constexpr (sizeof(T) == 2) ahead.template load<CAUSAL>(Q, K, V, t_begin, t_end);
 
     // Initial state (zero unless given), this thread's record elements.  Read
     // here, before the block publishes anything: the last block of the head
@@ -733,7 +650,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int w = 1; w < kFusedWaves; ++w) {
                 const float x = slot(w)[e];
-                slot(w)[e] = run;
+                if (CAUSAL) slot(w)[e] = run;
                 run += x;
             }
             slot(0)[e] = run;
@@ -747,14 +664,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int j = 0; j < NJ4; ++j)
         tot[j] = (last && tid + NT * j < REC4) ? slot4[tid + NT * j] : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (sb < nb - 1) {   // every thread stores a share of the total
+    if (nb > 1 && (!CAUSAL || sb < nb - 1)) {   // every thread stores a share of the total
         f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + blk * 2 * REC);
 #pragma unroll
         for (int j = 0; j < (REC4 + NT - 1) / NT; ++j)
             if (tid + NT * j < REC4) dev_store(dst + tid + NT * j, slot4[tid + NT * j]);
         block_publish(&flag_tot[blk], tag);
     }
-    if (wave == 0 && nb > 1) wait_flags(flag_tot, nb - 1, tag, &header[1]);
+    if (wave == 0 && nb > 1) wait_flags(flag_tot, CAUSAL ? nb - 1 : nb, tag, &header[1]);
     __syncthreads();
 
     if (nb > 1) {
@@ -763,7 +680,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         // nr = nb - 1 totals; a unit sums its rows, the group sums go through
         // LDS, and each row's prefix is (sum of the earlier groups) + (running
         // sum within the group) -- a fixed order for every element.
-        const int nr = nb - 1;
+        const int nr = CAUSAL ? nb - 1 : nb;   // non-causal: every total, summed into one record
         const int per = (REC4 + nb - 1) / nb;
         const int c0 = min(REC4, sb * per), ncol = min(REC4, c0 + per) - c0;
         const int G = ncol > 0 ? max(1, min(nr, NT / max(ncol, 1))) : 1;
@@ -785,7 +702,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
             for (int k = 1; k < RMAX; ++k) run[k] += run[k - 1];
             if (on) gsum[g * ncol + cc] = run[RMAX - 1];
             __syncthreads();
-            if (on) {
+            if (!CAUSAL) {   // the head's total, at block 0's prefix slot
+                if (on && g == 0) {
+                    f32x4 tot4 = gsum[cc];
+                    for (int h = 1; h < G; ++h) tot4 += gsum[h * ncol + cc];
+                    dev_store(reinterpret_cast<f32x4 *>(head_recs + REC) + c0 + cc, tot4);
+                }
+            } else if (on) {
                 f32x4 off = {0.f, 0.f, 0.f, 0.f};
                 for (int h = 0; h < g; ++h) off += gsum[h * ncol + cc];
                 f32x4 *dst = reinterpret_cast<f32x4 *>(head_recs + 3 * REC) + c0 + cc;   // prefix of block r + 1
@@ -796,17 +719,21 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
             __syncthreads();
         }
         block_publish(&flag_pre[blk], tag);
-        if (wave == 0 && sb > 0) wait_flags(flag_pre, nb, tag, &header[1]);
+        if (wave == 0 && (sb > 0 || !CAUSAL)) wait_flags(flag_pre, nb, tag, &header[1]);
         __syncthreads();
     }
     // 2c. P_s = initial state + the earlier blocks' totals into LDS; the last
     // block also forms the final state P_s + A_s
     {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(head_recs + (blk * 2 + 1) * REC);
+        // causal: P_s (zero for the first block); non-causal: the head's total
+        // (a single block already holds it in slot 0)
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(head_recs + (CAUSAL ? blk * 2 + 1 : 1) * REC);
+        const bool fetch = CAUSAL ? sb > 0 : nb > 1;
         f32x4 buf[NJ4];
 #pragma unroll
         for (int j = 0; j < NJ4; ++j)
-            buf[j] = (sb > 0 && tid + NT * j < REC4) ? dev_load(src + tid + NT * j) : f32x4{0.f, 0.f, 0.f, 0.f};
+            buf[j] = fetch ? (tid + NT * j < REC4 ? dev_load(src + tid + NT * j) : f32x4{0.f, 0.f, 0.f, 0.f})
+                           : (CAUSAL || tid + NT * j >= REC4 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot4[tid + NT * j]);
 #pragma unroll
         for (int j = 0; j < NJ4; ++j) {
             const int i4 = tid + NT * j;
@@ -825,13 +752,15 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     __syncthreads();
 
     // 3. outputs, starting from P_s + the totals of the earlier wavefronts
-    state_load_frag2<D, M>(St, pbuf, wave > 0 ? slot(wave) : nullptr);
+    // (non-causal: from the head's total)
+    state_load_frag2<D, M>(St, pbuf, (CAUSAL && wave > 0) ? slot(wave) : nullptr);
     __syncthreads();   // the prefix is read: the staging area is free again
     if constexpr (sizeof(T) == 2)
-        seg_output_bf16<D, M, true, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q,
-                                                    stage_k, stage_v, stage_v + SV, ahead);
+        seg_output_bf16<D, M, CAUSAL, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q,
+                                                      stage_k, stage_v, stage_v + SV, ahead);
     else
-        seg_output<T, D, M, true, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_k, stage_v);
+        seg_output<T, D, M, CAUSAL, fwd_prefetch<T, D, M>(), PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St,
+                                                                  stage_k, stage_v);
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -849,41 +778,23 @@ uint64_t next_call_tag() {
 template <typename T, int D, int M>
 static hipError_t run_forward(bool causal, const void *q, const void *k, const void *v, void *out, int64_t BH,
                               int64_t N, float *ws, StateIO sio, hipStream_t s) {
-    if (causal) {
-        const FusedPlan p = make_fused_plan(BH, N, D, M);
-        if (fused_slice_rows(p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows) return hipErrorInvalidValue;
-        char *base = reinterpret_cast<char *>(ws);
-        int *header = reinterpret_cast<int *>(base);
-        unsigned long long *flags = reinterpret_cast<unsigned long long *>(base + p.flags_off);
-        float *recs = reinterpret_cast<float *>(base + p.recs_off);
-        const dim3 grid(unsigned(BH * p.nblk)), block(64 * kFusedWaves);
-        if (sio.features_given)
-            hipLaunchKernelGGL((k_fwd_fused<T, D, M, false>), grid, block, 0, s, (const T *)q, (const T *)k,
-                               (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens,
-                               sio);
-        else
-            hipLaunchKernelGGL((k_fwd_fused<T, D, M, true>), grid, block, 0, s, (const T *)q, (const T *)k,
-                               (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens,
-                               sio);
-        return hipGetLastError();
-    }
-    const SegPlan p = make_plan(BH, N, D, M);
-    const dim3 grid(unsigned(BH * p.nseg));
-    hipLaunchKernelGGL((k_segment_state<T, D, M>), grid, dim3(64), 0, s, (const T *)k, (const T *)v, ws, N, p.nseg,
-                       p.seg_tokens, p.rec);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = launch_scan(ws, BH, p.nseg, p.rec, 1, nullptr, nullptr, s);
-    if (e != hipSuccess) return e;
-    // readout with its own, finer split: ~kNcTargetWaves wavefronts in all
-    const int64_t nch = ceil_div(N, kChunk);
-    const int64_t per_head = std::max<int64_t>(1, std::min<int64_t>(nch, ceil_div(kNcTargetWaves, BH)));
-    const int64_t sub_tokens = ceil_div(nch, per_head) * kChunk;
-    const int64_t nsub = ceil_div(N, sub_tokens);
-    const int64_t nwaves = BH * nsub;
-    hipLaunchKernelGGL((k_noncausal_output<T, D, M>), dim3(unsigned(ceil_div(nwaves, kNcWavesPerBlock))),
-                       dim3(64 * kNcWavesPerBlock), 0, s, (const T *)q, (T *)out, (const float *)ws, BH, N, nsub,
-                       sub_tokens, p.nseg, p.rec);
+    const FusedPlan p = make_fused_plan(BH, N, D, M);
+    if (fused_slice_rows(p.nblk, causal ? p.nblk - 1 : p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows)
+        return hipErrorInvalidValue;
+    char *base = reinterpret_cast<char *>(ws);
+    int *header = reinterpret_cast<int *>(base);
+    unsigned long long *flags = reinterpret_cast<unsigned long long *>(base + p.flags_off);
+    float *recs = reinterpret_cast<float *>(base + p.recs_off);
+    const dim3 grid(unsigned(BH * p.nblk)), block(64 * kFusedWaves);
+    if (!causal)
+        hipLaunchKernelGGL((k_fwd_fused<T, D, M, true, false>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens, sio);
+    else if (sio.features_given)
+        hipLaunchKernelGGL((k_fwd_fused<T, D, M, false>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens, sio);
+    else
+        hipLaunchKernelGGL((k_fwd_fused<T, D, M, true>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens, sio);
     return hipGetLastError();
 }
 

@@ -44,13 +44,7 @@ inline SegPlan make_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace of the non-causal forward: one fp32 state record per segment.
-inline size_t forward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
-    const SegPlan p = make_plan(BH, N, D, M);
-    return align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
-}
-
-// The causal forward runs as one pass: workgroups of kFusedWaves wavefronts,
+// Both forwards run as one pass: workgroups of kFusedWaves wavefronts,
 // each workgroup owning a block of kFusedWaves consecutive sub-segments (one
 // per wavefront) of one (b, h).  Blocks exchange fp32 state records through
 // the workspace (block totals, then their exclusive prefix sums, computed
@@ -86,14 +80,14 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     return p;
 }
 
-// Rows of block totals one thread sums while forming its slice of the
-// prefixes (the kernel keeps at most kFusedSliceRows in registers): block sb
-// of nb owns ncol = its share of the rec4 float4 columns; nthreads threads
-// cover ncol columns x G row groups.
+// Rows of block totals one thread sums while forming its slice (the kernel
+// keeps at most kFusedSliceRows in registers): block sb of nb owns ncol = its
+// share of the rec4 float4 columns; nthreads threads cover ncol columns x G
+// row groups of the nr totals summed (nb - 1 causal, nb non-causal).
 constexpr int kFusedSliceRows = 4;
-inline int64_t fused_slice_rows(int64_t nb, int64_t rec4, int64_t nthreads) {
+inline int64_t fused_slice_rows(int64_t nb, int64_t nr, int64_t rec4, int64_t nthreads) {
     int64_t worst = 0;
-    const int64_t nr = nb - 1, per = ceil_div(rec4, nb);
+    const int64_t per = ceil_div(rec4, nb);
     for (int64_t sb = 0; sb < nb && nr > 0; ++sb) {
         const int64_t c0 = std::min(rec4, sb * per), ncol = std::min(rec4, c0 + per) - c0;
         if (ncol <= 0) continue;
