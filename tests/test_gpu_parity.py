@@ -90,7 +90,20 @@ def test_forward_causal_plans(name, w, nb):
     check(f"out[{name}]", host(out), ref, w.dtype)
 
 
-NC_CASES = [("w1", wl.WORKLOADS[1]), ("w3_noncausal", wl.WORKLOADS[3]),
+@pytest.mark.parametrize("name,w,nb", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_forward_noncausal_plans(name, w, nb):
+    """The non-causal forward runs the same single-launch plan: every block
+    publishes its total and the slice owners sum all of them."""
+    assert _fused_nb(w.B * w.H, w.N) == nb
+    q, k, v = wl.forward_inputs(w)
+    _say(f"forward non-causal plan {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}, {nb} workgroups per head")
+    out = la.la_forward_noncausal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    check(f"out[{name}]", host(out), oracle.forward_noncausal(q, k, v), w.dtype)
+
+
+NC_CASES = [("w1", wl.WORKLOADS[1]), ("w2_noncausal", wl.WORKLOADS[2]), ("w3_noncausal", wl.WORKLOADS[3]),
+            ("w4_full_noncausal", wl.WORKLOADS[4]),
             ("n1", _wl(111, 1, 1, 1, 32, 32, "f32")), ("n77_d64m32", _wl(112, 2, 2, 77, 64, 32, "bf16")),
             ("n5000_f32", _wl(113, 1, 3, 5000, 64, 64, "f32"))]
 
@@ -502,9 +515,14 @@ def test_fused_forward_workspace_needs_no_clearing():
     la.la_forward_causal(q2, k2, v2, workspace=ws[:la.la_workspace_size(la.LA_OP_FWD_CAUSAL, 1, 2, 30000, 64, 64,
                                                                            torch.bfloat16)])
     out3 = la.la_forward_causal(q, k, v, workspace=ws)
+    # the non-causal forward uses the same flags: alternate with the causal one in the same bytes
+    nc_ref = la.la_forward_noncausal(q, k, v, workspace=torch.zeros((n,), dtype=torch.uint8, device="cuda"))
+    nc1 = la.la_forward_noncausal(q, k, v, workspace=ws)
+    out4 = la.la_forward_causal(q, k, v, workspace=ws)
     torch.cuda.synchronize()
-    for o in (out1, out2, out3):
+    for o in (out1, out2, out3, out4):
         assert torch.equal(o, ref)
+    assert torch.equal(nc1, nc_ref)
 
 
 def test_segment_plan_independence():
