@@ -671,10 +671,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
             if (tid + NT * j < REC4) dev_store(dst + tid + NT * j, slot4[tid + NT * j]);
         block_publish(&flag_tot[blk], tag);
     }
-    if (wave == 0 && nb > 1) wait_flags(flag_tot, CAUSAL ? nb - 1 : nb, tag, &header[1]);
+    // With few blocks per head each block sums the totals it needs itself (one
+    // exchange); otherwise the slices below form the prefixes (two exchanges,
+    // but a block reads 3 records however many precede it).
+    const bool direct = nb <= kFusedDirectBlocks;
+    if (wave == 0 && nb > 1) wait_flags(flag_tot, CAUSAL ? (direct ? sb : nb - 1) : nb, tag, &header[1]);
     __syncthreads();
 
-    if (nb > 1) {
+    if (nb > 1 && !direct) {
         // 2b. this block's slice [c0, c0 + ncol) of every prefix P_1 .. P_{nb-1}.
         // Work unit (column cc, row group g): rows g R .. g R + R - 1 of the
         // nr = nb - 1 totals; a unit sums its rows, the group sums go through
@@ -730,10 +734,27 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         const f32x4 *src = reinterpret_cast<const f32x4 *>(head_recs + (CAUSAL ? blk * 2 + 1 : 1) * REC);
         const bool fetch = CAUSAL ? sb > 0 : nb > 1;
         f32x4 buf[NJ4];
+        if (direct && fetch) {
+            // the totals of blocks 0 .. sb - 1 (non-causal: all nb), summed in block order
+            const int nsum = CAUSAL ? sb : nb;
+            const f32x4 *tot0 = reinterpret_cast<const f32x4 *>(head_recs);
 #pragma unroll
-        for (int j = 0; j < NJ4; ++j)
-            buf[j] = fetch ? (tid + NT * j < REC4 ? dev_load(src + tid + NT * j) : f32x4{0.f, 0.f, 0.f, 0.f})
-                           : (CAUSAL || tid + NT * j >= REC4 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot4[tid + NT * j]);
+            for (int j = 0; j < NJ4; ++j) {
+                f32x4 x[kFusedDirectBlocks];
+#pragma unroll
+                for (int r = 0; r < kFusedDirectBlocks; ++r)   // all loads in flight first
+                    x[r] = (r < nsum && tid + NT * j < REC4) ? dev_load(tot0 + int64_t(r) * 2 * REC4 + tid + NT * j)
+                                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+                buf[j] = x[0];
+#pragma unroll
+                for (int r = 1; r < kFusedDirectBlocks; ++r) buf[j] += x[r];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NJ4; ++j)
+                buf[j] = fetch ? (tid + NT * j < REC4 ? dev_load(src + tid + NT * j) : f32x4{0.f, 0.f, 0.f, 0.f})
+                               : (CAUSAL || tid + NT * j >= REC4 ? f32x4{0.f, 0.f, 0.f, 0.f} : slot4[tid + NT * j]);
+        }
 #pragma unroll
         for (int j = 0; j < NJ4; ++j) {
             const int i4 = tid + NT * j;

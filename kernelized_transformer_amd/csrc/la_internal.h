@@ -52,6 +52,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kFusedWaves = 8;
 constexpr int64_t kMaxBlkPerHead = 64;   // flags of a head fit one wavefront
 constexpr int64_t kTargetWaves = 2048;   // two wavefronts per SIMD of the 256 CUs
+constexpr int kFusedDirectBlocks = 4;    // up to this many blocks per head: one exchange, no slices
 
 struct FusedPlan {
     int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
