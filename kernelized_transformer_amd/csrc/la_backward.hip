@@ -361,6 +361,468 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     }
 }
 
+// ---- bf16, D = 64: two wavefronts per segment ------------------------------
+// The kernels above carry D x (M + 16) fp32 states in one wavefront (the
+// forward-direction pass two of them) and run one wavefront per SIMD.  Here
+// a segment is walked by a workgroup of two wavefronts; wavefront w owns the
+// state rows d in [32 w, 32 w + 32) (S_aug and this segment's sum of
+// phi(Q) gh^T in the forward direction, R_aug in the reverse one), so each
+// carries half the registers and two workgroups share a SIMD pair.  Every
+// product that contracts over d (the recomputed out and den, the dV readout)
+// is formed as two partial sums, one per wavefront, exchanged once per chunk
+// through LDS; the rest is local to a wavefront's rows or (the small [g, h]
+// and dA products) computed by both.  Rows move through LDS staging as
+// 16-byte loads (a wavefront loads its own 32 columns of Q and K and all of
+// V and dout / g), and phi'(x) = min(phi(x), 1) is read off the staged
+// phi(x) (phi(x) <= 1 exactly when x <= 0, where phi' = phi = exp(x)).
+constexpr int kW2Half = 32;   // feature columns per wavefront
+
+// 16 rows x 32 bf16 columns of a row-major tensor with row stride S (base
+// already offset to the first column): lane l moves row l / 4, columns
+// 8 (l % 4) .. + 7.  Rows at or beyond t_end read row t_end - 1.
+template <int S>
+__device__ __forceinline__ dwordx4 load_cols32(const bf16 *__restrict__ base, int64_t t0, int64_t t_end) {
+    const int l = lane_id();
+    const int64_t t = min(t0 + (l >> 2), t_end - 1);
+    return *reinterpret_cast<const dwordx4 *>(base + t * S + 8 * (l & 3));
+}
+// ... into staging rows of 32 + kStagePad, phi applied.
+__device__ __forceinline__ void stage_cols32_phi(lds_bf16 *stage, dwordx4 x) {
+    const int l = lane_id();
+    *reinterpret_cast<lds_dwordx4 *>(stage + (l >> 2) * (kW2Half + kStagePad) + 8 * (l & 3)) = phi8(x);
+}
+// Rows [r0, r0 + NR) of a 16-row LDS tile (row stride F + kStagePad, F
+// columns) to rows t0 + r of a tensor with row stride S (dst already offset
+// to the first column); rows at or beyond t_end are not written.
+template <int F, int S, int NR>
+__device__ __forceinline__ void flush_rows(bf16 *__restrict__ dst, int64_t t0, int64_t t_end, const lds_bf16 *tile,
+                                           int r0) {
+    constexpr int PR = F / 8, NP = NR * PR;   // 16-byte pieces per row, in all
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < (NP + 63) / 64; ++i) {
+        const int p = 64 * i + l;
+        if (NP % 64 == 0 || p < NP) {
+            const int row = r0 + p / PR, col = 8 * (p % PR);
+            const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(tile + row * (F + kStagePad) + col);
+            if (t0 + row < t_end) *reinterpret_cast<dwordx4 *>(dst + (t0 + row) * S + col) = y;
+        }
+    }
+}
+// Both wavefronts of the workgroup have finished their LDS accesses so far
+// (global loads in flight are not waited for).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Rows [d0, d0 + 16 DTH) of a row-major record, as Acc tiles (the layout of
+// state_load: REP puts Z in every column of the normalizer tile, otherwise
+// in column 0).
+template <int D, int M, int DTH, bool REP>
+__device__ __forceinline__ void rows_load(f32x4 (&St)[DTH][M / 16 + 1], const float *__restrict__ rec, int d0) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt) {
+        const int d = d0 + 16 * dt + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St[dt][mt][r] = rec[(d + r) * M + 16 * mt + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[dt][M / 16][r] = (REP || c == 0) ? rec[D * M + d + r] : 0.f;
+    }
+}
+template <int D, int M, int DTH>
+__device__ __forceinline__ void rows_store(float *__restrict__ rec, const f32x4 (&St)[DTH][M / 16 + 1], int d0) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt) {
+        const int d = d0 + 16 * dt + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rec[(d + r) * M + 16 * mt + c] = St[dt][mt][r];
+        if (c == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rec[D * M + d + r] = St[dt][M / 16][r];
+        }
+    }
+}
+
+// Natural fragments y[tt][ft] written row-major into LDS (row stride
+// 16 NF + kStagePad), to be read back transposed by transposed_frags_lds
+// (the two halves of transpose_frags_lds, split so that other work can
+// run in between).
+template <int NF, int TT>
+__device__ __forceinline__ void put_frags_lds(lds_bf16 *stage, const bf16x4 (&y)[TT][NF]) {
+    constexpr int S = 16 * NF + kStagePad;
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < NF; ++ft)
+            *reinterpret_cast<lds_bf16x4 *>(stage + (16 * tt + c) * S + 16 * ft + 4 * g) = y[tt][ft];
+}
+
+template <int M> struct W2Stage {   // one wavefront's private LDS, in elements
+    static constexpr int SQ = 16 * (kW2Half + kStagePad);   // phi(Q) or phi(K) columns of the wavefront
+    static constexpr int SV = 16 * (M + kStagePad);         // V, dout or g rows
+    static constexpr int ROWS = 2 * SQ + 2 * SV;
+    static constexpr int ST = stage_elems<kW2Half / 16, M / 16 + 1>();   // a state transpose
+    static constexpr int N = ROWS > ST ? ROWS : ST;
+    static constexpr int NQ = ROWS > SV + ST ? ROWS : SV + ST;   // the forward-direction layout
+};
+
+// Forward direction (see k_bwd_dq): recompute out and den, write dQ, g, h,
+// and this segment's sum of phi(Q) gh^T.
+template <int D, int M>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq_w2(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, bf16 *__restrict__ dq, const float *__restrict__ wsS, float *__restrict__ wsR,
+    bf16 *__restrict__ gbuf, float *__restrict__ hbuf, int64_t N, int64_t nseg, int64_t seg_tokens, int64_t rec) {
+    static_assert(D == 2 * kW2Half, "two wavefronts of 32 feature rows");
+    typedef bf16x4 Fr;
+    constexpr int DTH = kW2Half / 16, MT = M / 16, PF = 1;
+    constexpr int NV = Lines<M, 1>::n;
+    typedef W2Stage<M> SL;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    const bf16 *Qw = q + bh * N * D + w * kW2Half;
+    const bf16 *Kw = k + bh * N * D + w * kW2Half;
+    const bf16 *V = v + bh * N * M;
+    const bf16 *G = dout + bh * N * M;
+    bf16 *DQw = dq + bh * N * D + w * kW2Half;
+    bf16 *GB = gbuf + bh * N * M;
+    float *HB = hbuf + bh * N;
+
+    // per wavefront: dout rows first, then phi(Q), phi(K), V; the state's
+    // transpose goes right after the dout rows, which are read last
+    __shared__ __align__(16) bf16 priv_mem[2][SL::NQ];
+    __shared__ __align__(16) f32x4 xbuf[2][2][MT + 1][64];   // [chunk parity][wavefront][tile][lane]
+    lds_bf16 *sg = (lds_bf16 *)priv_mem[w];
+    lds_bf16 *sq = sg + SL::SV;
+    lds_bf16 *sk = sq + SL::SQ;
+    lds_bf16 *sv = sk + SL::SQ;
+    lds_bf16 *sst = sq;   // S_aug^T, over the phi(Q), phi(K), V rows once they are read
+
+    f32x4 St[DTH][MT + 1];   // S_aug rows of this wavefront, normalizer tile replicated
+    f32x4 Ra[DTH][MT + 1];   // this segment's sum_i qh_i gh_i^T, same rows
+    rows_load<D, M, DTH, true>(St, wsS + (bh * nseg + seg) * rec, w * kW2Half);
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) Ra[dt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const Fr ones = frag_ones<Fr>();
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    dwordx4 lq[PF], lk[PF], lv[PF][NV], lg[PF][NV];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t_begin + b * BCH;
+        lq[b] = load_cols32<D>(Qw, t0, t_end);
+        lk[b] = load_cols32<D>(Kw, t0, t_end);
+        load_lines<M, 1>(lv[b], V, t0, t_end);
+        load_lines<M, 1>(lg[b], G, t0, t_end);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * BCH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + b * BCH;
+        if (t0 >= t_end) break;   // uniform over the workgroup
+        // no row masks: rows past t_end copy row t_end - 1; their g, h are zero
+        // (inv = 0 below), the causal mask keeps their keys out of every valid
+        // query, and the state is not used after the segment
+        stage_cols32_phi(sq, lq[b]);
+        stage_cols32_phi(sk, lk[b]);
+        stage_lines<M, 1, false, false>(sv, lv[b], t0, t_end);
+        stage_lines<M, 1, false, false>(sg, lg[b], t0, t_end);
+        {
+            const int64_t tn = t0 + PF * BCH;
+            lq[b] = load_cols32<D>(Qw, tn, t_end);
+            lk[b] = load_cols32<D>(Kw, tn, t_end);
+            load_lines<M, 1>(lv[b], V, tn, t_end);
+            load_lines<M, 1>(lg[b], G, tn, t_end);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t t = t0 + c;   // this lane's query token
+        const bool valid = t < t_end;
+
+        Fr Qn[1][DTH], QT[1][DTH], Kn[1][DTH], KT[1][DTH], VT[1][MT], Vn[1][MT];
+        natural_frags_lds<kW2Half, 1>(Qn, sq);
+        transposed_frags_lds<kW2Half, 1>(QT, sq);
+        natural_frags_lds<kW2Half, 1>(Kn, sk);
+        transposed_frags_lds<kW2Half, 1>(KT, sk);
+        natural_frags_lds<M, 1>(Vn, sv);
+        transposed_frags_lds<M, 1>(VT, sv);
+
+        // S_aug as operand tiles: SF[mt][dt] (rows m', contraction d) is the
+        // accumulator itself; its transpose (rows d, contraction m') is
+        // written to LDS now and read back for dQ
+        Fr SF[MT + 1][DTH];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DTH; ++dt) SF[mt][dt] = IO<bf16>::to_frag(St[dt][mt]);
+        put_frags_lds<DTH, MT + 1>(sst, SF);
+
+        // this wavefront's share (its 32 rows d) of out^T and den
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DTH; dt += 2) mma2(p, Kn[0][dt], Kn[0][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+        const Fr PT = IO<bf16>::to_frag(p);
+        f32x4 Ot[MT + 1];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) {
+            Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dt = 0; dt < DTH; dt += 2) mma2(Ot[mt], SF[mt][dt], SF[mt][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
+            mma1(Ot[mt], mt < MT ? VT[0][mt] : ones, PT);
+        }
+        // exchange the shares: both wavefronts then hold the same full sums
+        const int par = int((t0 - t_begin) / BCH) & 1;
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) xbuf[par][w][mt][lane] = Ot[mt];
+        lds_barrier();
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) Ot[mt] += xbuf[par][1 - w][mt][lane];
+
+        // gh = [G / d, -(G . out) / d]; lane (c, g) holds m = 16 mt + 4g + r of token c
+        const float inv = valid ? __builtin_amdgcn_rcpf(Ot[MT][0]) : 0.f;
+        Fr Gr[1][MT];
+        natural_frags_lds<M, 1>(Gr, sg);
+        float go = 0.f;
+        f32x4 gv[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 graw = IO<bf16>::to_f32(Gr[0][mt]);
+            const f32x4 o = Ot[mt] * inv;
+            go += graw[0] * o[0] + graw[1] * o[1] + graw[2] * o[2] + graw[3] * o[3];
+            gv[mt] = graw * inv;
+        }
+        go += __shfl_xor(go, 16);
+        go += __shfl_xor(go, 32);
+        const float h = -go * inv;
+        Fr Gn[1][MT + 1];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<bf16>::to_frag(gv[mt]);
+        Gn[0][MT] = IO<bf16>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
+
+        // g rows 8w .. 8w + 7 and h (wavefront 1) leave from here
+        lds_bf16 *otile = sg;   // the dout rows are read
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) tile_put_bf16<M>(otile, mt, Gn[0][mt]);
+        flush_rows<M, M, 8>(GB, t0, t_end, otile, 8 * w);
+        if (w == 1 && valid && g == 0) HB[t] = h;
+
+        // dA^T[j][i] = vh_j . gh_i, masked to j <= i (both wavefronts)
+        f32x4 da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt + 1 <= MT; mt += 2) {
+            const Fr a1 = (mt + 1 < MT) ? Vn[0][mt + 1] : k0ones;
+            mma2(da, Vn[0][mt], a1, Gn[0][mt], Gn[0][mt + 1]);
+        }
+        if ((MT & 1) == 0) mma1(da, k0ones, Gn[0][MT]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
+        const Fr dAT = IO<bf16>::to_frag(da);
+
+        // dL/dqh^T for this wavefront's rows d, times phi'(q) = min(phi(q), 1)
+        Fr SFT[MT + 1][DTH];
+        transposed_frags_lds<16 * DTH, MT + 1>(SFT, sst);
+        lds_bf16 *dtile = sg;   // the g tile is flushed
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma1(acc, KT[0][dt], dAT);
+#pragma unroll
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, SFT[mt][dt], SFT[mt + 1][dt], Gn[0][mt], Gn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, SFT[MT][dt], Gn[0][MT]);
+            const f32x4 qh = IO<bf16>::to_f32(Qn[0][dt]);
+            const f32x4 dp = {__builtin_fminf(qh[0], 1.f), __builtin_fminf(qh[1], 1.f), __builtin_fminf(qh[2], 1.f),
+                              __builtin_fminf(qh[3], 1.f)};
+            tile_put_bf16<kW2Half>(dtile, dt, IO<bf16>::from_f32(acc * dp));
+        }
+        flush_rows<kW2Half, D, 16>(DQw, t0, t_end, dtile, 0);
+
+        // this segment's reverse-sum contribution (rows d of this wavefront)
+        Fr GT[1][MT + 1];
+        static_assert(stage_elems<MT + 1, 1>() <= SL::NQ, "transpose of gh fits");
+        transpose_frags<MT + 1, 1>(GT, Gn, sg);   // the dQ tile is flushed
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt) mma1(Ra[dt][mt], QT[0][dt], GT[0][mt]);
+        // carry S_aug past this chunk
+        state_accumulate<Fr, kW2Half, M, 1, true>(St, KT, VT);
+    }
+    }
+    rows_store<D, M, DTH>(wsR + (bh * nseg + seg) * rec, Ra, w * kW2Half);
+}
+
+// Reverse direction (see k_bwd_dkdv): walk the chunks last to first carrying
+// R_aug, write dK and dV.
+template <int D, int M>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv_w2(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ gbuf, const float *__restrict__ hbuf, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    const float *__restrict__ wsR, int64_t N, int64_t nseg, int64_t seg_tokens, int64_t rec) {
+    static_assert(D == 2 * kW2Half, "two wavefronts of 32 feature rows");
+    typedef bf16x4 Fr;
+    constexpr int DTH = kW2Half / 16, MT = M / 16, MH = MT / 2, PF = 2;
+    constexpr int NV = Lines<M, 1>::n;
+    typedef W2Stage<M> SL;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    const bf16 *Qw = q + bh * N * D + w * kW2Half;
+    const bf16 *Kw = k + bh * N * D + w * kW2Half;
+    const bf16 *V = v + bh * N * M;
+    const bf16 *GB = gbuf + bh * N * M;
+    const float *HB = hbuf + bh * N;
+    bf16 *DKw = dk + bh * N * D + w * kW2Half;
+    bf16 *DVw = dv + bh * N * M + w * (M / 2);
+
+    __shared__ __align__(16) bf16 priv_mem[2][SL::N];
+    __shared__ __align__(16) f32x4 xbuf[2][2][MH][64];   // [chunk parity][wavefront][tile][lane]
+    lds_bf16 *sq = (lds_bf16 *)priv_mem[w];
+    lds_bf16 *sk = sq + SL::SQ;
+    lds_bf16 *sv = sk + SL::SQ;
+    lds_bf16 *sg = sv + SL::SV;
+
+    f32x4 Rr[DTH][MT + 1];   // R_aug = [R | u], this wavefront's rows d
+    rows_load<D, M, DTH, false>(Rr, wsR + (bh * nseg + seg) * rec, w * kW2Half);
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
+    auto chunk = [&](int64_t step) { return t_begin + max<int64_t>(nch - 1 - step, 0) * BCH; };
+    dwordx4 lq[PF], lk[PF], lv[PF][NV], lg[PF][NV];
+    float lh[PF];
+    auto load_all = [&](int b, int64_t t0) {
+        lq[b] = load_cols32<D>(Qw, t0, t_end);
+        lk[b] = load_cols32<D>(Kw, t0, t_end);
+        load_lines<M, 1>(lv[b], V, t0, t_end);
+        load_lines<M, 1>(lg[b], GB, t0, t_end);
+        lh[b] = HB[min(t0 + c, t_end - 1)];
+    };
+#pragma unroll
+    for (int b = 0; b < PF; ++b) load_all(b, chunk(b));
+    for (int64_t s0 = 0; s0 < nch; s0 += PF) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t step = s0 + b;
+        if (step >= nch) break;   // uniform over the workgroup
+        const int64_t t0 = chunk(step);
+        // rows past t_end belong to the next segment: their g and h must not
+        // enter (zeroed); Q, K, V there only meet those zeros or unstored outputs
+        stage_cols32_phi(sq, lq[b]);
+        stage_cols32_phi(sk, lk[b]);
+        stage_lines<M, 1, false, false>(sv, lv[b], t0, t_end);
+        stage_lines<M, 1, false, true>(sg, lg[b], t0, t_end);
+        const float hc = (t0 + c < t_end) ? lh[b] : 0.f;
+        load_all(b, chunk(step + PF));
+        __builtin_amdgcn_sched_barrier(0);
+
+        Fr Qn[1][DTH], QT[1][DTH], Kn[1][DTH], Vn[1][MT + 1], Gn[1][MT + 1], GT[1][MT + 1];
+        natural_frags_lds<kW2Half, 1>(Qn, sq);
+        transposed_frags_lds<kW2Half, 1>(QT, sq);
+        natural_frags_lds<kW2Half, 1>(Kn, sk);
+        {
+            Fr tv[1][MT], tg[1][MT], tgt[1][MT];
+            natural_frags_lds<M, 1>(tv, sv);
+            natural_frags_lds<M, 1>(tg, sg);
+            transposed_frags_lds<M, 1>(tgt, sg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                Vn[0][mt] = tv[0][mt];
+                Gn[0][mt] = tg[0][mt];
+                GT[0][mt] = tgt[0][mt];
+            }
+        }
+        Vn[0][MT] = k0ones;
+        Gn[0][MT] = IO<bf16>::to_frag(f32x4{g == 0 ? hc : 0.f, 0.f, 0.f, 0.f});
+        {   // GT[MT]: row 0 holds h of tokens 4g + r (lanes c = 0)
+            f32x4 h4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h4[r] = __shfl(hc, 4 * g + r);
+            GT[0][MT] = IO<bf16>::to_frag(c == 0 ? h4 : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+
+        // R_aug as operand tiles in both orientations
+        Fr RF[MT + 1][DTH], RFT[MT + 1][DTH];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DTH; ++dt) RF[mt][dt] = IO<bf16>::to_frag(Rr[dt][mt]);
+        transpose_frags<DTH, MT + 1>(RFT, RF, sq);
+
+        // P (this wavefront's share over its rows d) and dA (both), masked to i >= j
+        f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DTH; dt += 2) mma2(p, Qn[0][dt], Qn[0][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
+#pragma unroll
+        for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(da, Gn[0][mt], Gn[0][mt + 1], Vn[0][mt], Vn[0][mt + 1]);
+        if ((MT & 1) == 0) mma1(da, Gn[0][MT], Vn[0][MT]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool keep = 4 * g + r >= c;
+            p[r] = keep ? p[r] : 0.f;
+            da[r] = keep ? da[r] : 0.f;
+        }
+        const Fr Pf = IO<bf16>::to_frag(p), dAf = IO<bf16>::to_frag(da);
+
+        // dV^T[m][j] shares: sum_i g[i][m] P[i][j] + sum_d R[d][m] kh[j][d];
+        // wavefront w finishes the tiles mt in [w MH, w MH + MH)
+        f32x4 dvs[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            dvs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma1(dvs[mt], GT[0][mt], Pf);
+#pragma unroll
+            for (int dt = 0; dt < DTH; dt += 2) mma2(dvs[mt], RF[mt][dt], RF[mt][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
+        }
+        // (explicit selects: an index computed from w would make the compiler
+        // index the register file at run time)
+        const int par = int(step & 1);
+#pragma unroll
+        for (int i = 0; i < MH; ++i) xbuf[par][w][i][lane] = w ? dvs[i] : dvs[MH + i];
+
+        // dL/dkh^T for this wavefront's rows d, times phi'(k) = min(phi(k), 1)
+        lds_bf16 *dtile = sv;   // the staged rows are all in registers by now
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma1(acc, QT[0][dt], dAf);
+#pragma unroll
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, RFT[mt][dt], RFT[mt + 1][dt], Vn[0][mt], Vn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, RFT[MT][dt], Vn[0][MT]);
+            const f32x4 kh = IO<bf16>::to_f32(Kn[0][dt]);
+            const f32x4 dp = {__builtin_fminf(kh[0], 1.f), __builtin_fminf(kh[1], 1.f), __builtin_fminf(kh[2], 1.f),
+                              __builtin_fminf(kh[3], 1.f)};
+            tile_put_bf16<kW2Half>(dtile, dt, IO<bf16>::from_f32(acc * dp));
+        }
+        flush_rows<kW2Half, D, 16>(DKw, t0, t_end, dtile, 0);
+
+        // carry R_aug past this chunk, towards earlier tokens
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt) mma1(Rr[dt][mt], QT[0][dt], GT[0][mt]);
+
+        lds_barrier();
+        lds_bf16 *vtile = dtile;
+#pragma unroll
+        for (int i = 0; i < MH; ++i)
+            tile_put_bf16<M / 2>(vtile, i, IO<bf16>::from_f32((w ? dvs[MH + i] : dvs[i]) + xbuf[par][1 - w][i][lane]));
+        flush_rows<M / 2, M, 16>(DVw, t0, t_end, vtile, 0);
+    }
+    }
+}
+
 template <typename T, int D, int M>
 static hipError_t run_backward(bool causal, const void *q, const void *k, const void *v, const void *dout, void *dq,
                                void *dk, void *dv, int64_t BH, int64_t N, float *ws, hipStream_t s) {
@@ -387,14 +849,27 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
         return hipGetLastError();
     }
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_dq<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
-                       (const T *)dout, (T *)dq, (const float *)wsS, wsR, gbuf, hbuf, N, p.nseg, p.seg_tokens, p.rec);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k, (const T *)v,
-                       (const T *)gbuf, (const float *)hbuf, (T *)dk, (T *)dv, (const float *)wsR, N, p.nseg,
-                       p.seg_tokens, p.rec);
-    return hipGetLastError();
+    if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) {   // two wavefronts per segment
+        hipLaunchKernelGGL((k_bwd_dq_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
+                           (const bf16 *)v, (const bf16 *)dout, (bf16 *)dq, (const float *)wsS, wsR, (bf16 *)gbuf,
+                           hbuf, N, p.nseg, p.seg_tokens, p.rec);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_dkdv_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
+                           (const bf16 *)v, (const bf16 *)gbuf, (const float *)hbuf, (bf16 *)dk, (bf16 *)dv,
+                           (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
+        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((k_bwd_dq<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, gbuf, hbuf, N, p.nseg,
+                           p.seg_tokens, p.rec);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)gbuf, (const float *)hbuf, (T *)dk, (T *)dv, (const float *)wsR,
+                           N, p.nseg, p.seg_tokens, p.rec);
+        return hipGetLastError();
+    }
 }
 
 template <typename T>

@@ -138,6 +138,12 @@ BWD_CASES = [
     ("n50_d64m32_bf16", _wl(123, 1, 3, 50, 64, 32, "bf16")),
     ("n3001_ragged_f32", _wl(124, 1, 2, 3001, 64, 64, "f32")),
     ("n100000_many_segments", _wl(125, 1, 1, 100000, 32, 32, "bf16")),
+    # bf16 at D = 64 runs two wavefronts per segment: one token, a partial
+    # chunk, ragged multi-segment and the M = 32 variant
+    ("n1_d64_bf16", _wl(126, 1, 2, 1, 64, 64, "bf16")),
+    ("n17_d64m64_bf16", _wl(127, 2, 3, 17, 64, 64, "bf16")),
+    ("n3001_ragged_bf16", _wl(128, 1, 2, 3001, 64, 64, "bf16")),
+    ("n20000_d64m32_bf16", _wl(129, 2, 2, 20000, 64, 32, "bf16")),
 ]
 
 
@@ -149,7 +155,10 @@ def test_backward_causal(name, w):
     torch.cuda.synchronize()
     rq, rk, rv = oracle.backward_causal(q, k, v, g)
     if w.N == 1:   # out_1 = V_1: dQ = dK = 0, dV = dout
-        assert np.abs(host(dq)).max() < 1e-6 and np.abs(host(dk)).max() < 1e-6
+        # dA_11 = g.v/d - (g.out)/d cancels exactly only in exact arithmetic;
+        # with g/d and h rounded to bf16 operands it is a rounding residue
+        bound = 1e-6 if w.dtype == "f32" else TOL[w.dtype] * np.abs(g).max() * np.abs(v).max()
+        assert np.abs(host(dq)).max() < bound and np.abs(host(dk)).max() < bound
         check(f"dv[{name}]", host(dv), rv, w.dtype)
         return
     check(f"dq[{name}]", host(dq), rq, w.dtype)
