@@ -30,6 +30,7 @@
 // dout against it, 3. totals R_aug, 4. reads only K and V against it.
 #include "la_chunk.h"
 #include "la_internal.h"
+#include "la_split.h"
 
 namespace la {
 
@@ -375,93 +376,6 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 // 16-byte loads (a wavefront loads its own 32 columns of Q and K and all of
 // V and dout / g), and phi'(x) = min(phi(x), 1) is read off the staged
 // phi(x) (phi(x) <= 1 exactly when x <= 0, where phi' = phi = exp(x)).
-constexpr int kW2Half = 32;   // feature columns per wavefront
-
-// 16 rows x 32 bf16 columns of a row-major tensor with row stride S (base
-// already offset to the first column): lane l moves row l / 4, columns
-// 8 (l % 4) .. + 7.  Rows at or beyond t_end read row t_end - 1.
-template <int S>
-__device__ __forceinline__ dwordx4 load_cols32(const bf16 *__restrict__ base, int64_t t0, int64_t t_end) {
-    const int l = lane_id();
-    const int64_t t = min(t0 + (l >> 2), t_end - 1);
-    return *reinterpret_cast<const dwordx4 *>(base + t * S + 8 * (l & 3));
-}
-// ... into staging rows of 32 + kStagePad, phi applied.
-__device__ __forceinline__ void stage_cols32_phi(lds_bf16 *stage, dwordx4 x) {
-    const int l = lane_id();
-    *reinterpret_cast<lds_dwordx4 *>(stage + (l >> 2) * (kW2Half + kStagePad) + 8 * (l & 3)) = phi8(x);
-}
-// Rows [r0, r0 + NR) of a 16-row LDS tile (row stride F + kStagePad, F
-// columns) to rows t0 + r of a tensor with row stride S (dst already offset
-// to the first column); rows at or beyond t_end are not written.
-template <int F, int S, int NR>
-__device__ __forceinline__ void flush_rows(bf16 *__restrict__ dst, int64_t t0, int64_t t_end, const lds_bf16 *tile,
-                                           int r0) {
-    constexpr int PR = F / 8, NP = NR * PR;   // 16-byte pieces per row, in all
-    const int l = lane_id();
-#pragma unroll
-    for (int i = 0; i < (NP + 63) / 64; ++i) {
-        const int p = 64 * i + l;
-        if (NP % 64 == 0 || p < NP) {
-            const int row = r0 + p / PR, col = 8 * (p % PR);
-            const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(tile + row * (F + kStagePad) + col);
-            if (t0 + row < t_end) *reinterpret_cast<dwordx4 *>(dst + (t0 + row) * S + col) = y;
-        }
-    }
-}
-// Both wavefronts of the workgroup have finished their LDS accesses so far
-// (global loads in flight are not waited for).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Rows [d0, d0 + 16 DTH) of a row-major record, as Acc tiles (the layout of
-// state_load: REP puts Z in every column of the normalizer tile, otherwise
-// in column 0).
-template <int D, int M, int DTH, bool REP>
-__device__ __forceinline__ void rows_load(f32x4 (&St)[DTH][M / 16 + 1], const float *__restrict__ rec, int d0) {
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-#pragma unroll
-    for (int dt = 0; dt < DTH; ++dt) {
-        const int d = d0 + 16 * dt + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < M / 16; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) St[dt][mt][r] = rec[(d + r) * M + 16 * mt + c];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) St[dt][M / 16][r] = (REP || c == 0) ? rec[D * M + d + r] : 0.f;
-    }
-}
-template <int D, int M, int DTH>
-__device__ __forceinline__ void rows_store(float *__restrict__ rec, const f32x4 (&St)[DTH][M / 16 + 1], int d0) {
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-#pragma unroll
-    for (int dt = 0; dt < DTH; ++dt) {
-        const int d = d0 + 16 * dt + 4 * g;
-#pragma unroll
-        for (int mt = 0; mt < M / 16; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rec[(d + r) * M + 16 * mt + c] = St[dt][mt][r];
-        if (c == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rec[D * M + d + r] = St[dt][M / 16][r];
-        }
-    }
-}
-
-// Natural fragments y[tt][ft] written row-major into LDS (row stride
-// 16 NF + kStagePad), to be read back transposed by transposed_frags_lds
-// (the two halves of transpose_frags_lds, split so that other work can
-// run in between).
-template <int NF, int TT>
-__device__ __forceinline__ void put_frags_lds(lds_bf16 *stage, const bf16x4 (&y)[TT][NF]) {
-    constexpr int S = 16 * NF + kStagePad;
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int ft = 0; ft < NF; ++ft)
-            *reinterpret_cast<lds_bf16x4 *>(stage + (16 * tt + c) * S + 16 * ft + 4 * g) = y[tt][ft];
-}
-
 template <int M> struct W2Stage {   // one wavefront's private LDS, in elements
     static constexpr int SQ = 16 * (kW2Half + kStagePad);   // phi(Q) or phi(K) columns of the wavefront
     static constexpr int SV = 16 * (M + kStagePad);         // V, dout or g rows
@@ -522,8 +436,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t t0 = t_begin + b * BCH;
         lq[b] = load_cols32<D>(Qw, t0, t_end);
         lk[b] = load_cols32<D>(Kw, t0, t_end);
-        load_lines<M, 1>(lv[b], V, t0, t_end);
-        load_lines<M, 1>(lg[b], G, t0, t_end);
+        load_rows32<M>(lv[b], V, t0, t_end);
+        load_rows32<M>(lg[b], G, t0, t_end);
     }
     for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * BCH) {
 #pragma unroll
@@ -541,8 +455,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int64_t tn = t0 + PF * BCH;
             lq[b] = load_cols32<D>(Qw, tn, t_end);
             lk[b] = load_cols32<D>(Kw, tn, t_end);
-            load_lines<M, 1>(lv[b], V, tn, t_end);
-            load_lines<M, 1>(lg[b], G, tn, t_end);
+            load_rows32<M>(lv[b], V, tn, t_end);
+            load_rows32<M>(lg[b], G, tn, t_end);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int64_t t = t0 + c;   // this lane's query token
@@ -585,6 +499,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int par = int((t0 - t_begin) / BCH) & 1;
 #pragma unroll
         for (int mt = 0; mt <= MT; ++mt) xbuf[par][w][mt][lane] = Ot[mt];
+        // carry S_aug past this chunk (its operand copies are taken): work
+        // that does not need the other wavefront's share, before waiting for it
+        state_accumulate<Fr, kW2Half, M, 1, true>(St, KT, VT);
         lds_barrier();
 #pragma unroll
         for (int mt = 0; mt <= MT; ++mt) Ot[mt] += xbuf[par][1 - w][mt][lane];
@@ -615,7 +532,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tile_put_bf16<M>(otile, mt, Gn[0][mt]);
         flush_rows<M, M, 8>(GB, t0, t_end, otile, 8 * w);
-        if (w == 1 && valid && g == 0) HB[t] = h;
+        if (w == 1 && valid && g == 0) HB[uint32_t(t)] = h;
 
         // dA^T[j][i] = vh_j . gh_i, masked to j <= i (both wavefronts)
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
@@ -655,8 +572,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int dt = 0; dt < DTH; ++dt)
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt) mma1(Ra[dt][mt], QT[0][dt], GT[0][mt]);
-        // carry S_aug past this chunk
-        state_accumulate<Fr, kW2Half, M, 1, true>(St, KT, VT);
     }
     }
     rows_store<D, M, DTH>(wsR + (bh * nseg + seg) * rec, Ra, w * kW2Half);
@@ -705,9 +620,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto load_all = [&](int b, int64_t t0) {
         lq[b] = load_cols32<D>(Qw, t0, t_end);
         lk[b] = load_cols32<D>(Kw, t0, t_end);
-        load_lines<M, 1>(lv[b], V, t0, t_end);
-        load_lines<M, 1>(lg[b], GB, t0, t_end);
-        lh[b] = HB[min(t0 + c, t_end - 1)];
+        load_rows32<M>(lv[b], V, t0, t_end);
+        load_rows32<M>(lg[b], GB, t0, t_end);
+        lh[b] = HB[min(uint32_t(t0) + uint32_t(c), uint32_t(t_end - 1))];
     };
 #pragma unroll
     for (int b = 0; b < PF; ++b) load_all(b, chunk(b));
@@ -849,7 +764,10 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
         return hipGetLastError();
     }
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
-    if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) {   // two wavefronts per segment
+    // two wavefronts per segment (their kernels address a head with 32-bit
+    // element offsets)
+    const bool w2 = sizeof(T) == 2 && D == 2 * kW2Half && N * (D > M ? D : M) <= int64_t(INT32_MAX);
+    if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) if (w2) {
         hipLaunchKernelGGL((k_bwd_dq_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
                            (const bf16 *)v, (const bf16 *)dout, (bf16 *)dq, (const float *)wsS, wsR, (bf16 *)gbuf,
                            hbuf, N, p.nseg, p.seg_tokens, p.rec);
@@ -859,7 +777,8 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
                            (const bf16 *)v, (const bf16 *)gbuf, (const float *)hbuf, (bf16 *)dk, (bf16 *)dv,
                            (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
         return hipGetLastError();
-    } else {
+    }
+    {
         hipLaunchKernelGGL((k_bwd_dq<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
                            (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, gbuf, hbuf, N, p.nseg,
                            p.seg_tokens, p.rec);

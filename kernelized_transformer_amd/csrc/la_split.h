@@ -1,0 +1,120 @@
+// la_split.h -- helpers for the kernels that walk one segment with two
+// wavefronts (bf16, D = 64), each owning half of the feature rows d.
+#pragma once
+
+#include "la_chunk.h"
+
+namespace la {
+
+// ---- two wavefronts per segment (bf16, D = 64) ---------------------------
+// A segment's states are split by feature row d between two wavefronts:
+// wavefront w owns rows [32 w, 32 w + 32) and loads only its 32 columns of
+// the d-indexed inputs.  Helpers for those kernels; their global accesses
+// use 32-bit element offsets from a per-head base pointer (callers check
+// that a head's elements fit).
+constexpr int kW2Half = 32;   // feature columns per wavefront
+
+// 16 rows x 32 bf16 columns of a row-major tensor with row stride S (base
+// already offset to the first column): lane l moves row l / 4, columns
+// 8 (l % 4) .. + 7.  Rows at or beyond t_end read row t_end - 1.
+template <int S>
+__device__ __forceinline__ dwordx4 load_cols32(const bf16 *__restrict__ base, int64_t t0, int64_t t_end) {
+    // 32-bit element offsets from the (uniform) per-head base: one address add per load
+    const int l = lane_id();
+    const uint32_t t = min(uint32_t(t0) + uint32_t(l >> 2), uint32_t(t_end - 1));
+    return *reinterpret_cast<const dwordx4 *>(base + (t * uint32_t(S) + uint32_t(8 * (l & 3))));
+}
+// 16 whole rows of F bf16 features (as load_lines, 32-bit offsets).
+template <int F>
+__device__ __forceinline__ void load_rows32(dwordx4 (&x)[F / 32], const bf16 *__restrict__ base, int64_t t0,
+                                            int64_t t_end) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < F / 32; ++i) {
+        const int e = (64 * i + l) * 8;
+        const uint32_t t = min(uint32_t(t0) + uint32_t(e / F), uint32_t(t_end - 1));
+        x[i] = *reinterpret_cast<const dwordx4 *>(base + (t * uint32_t(F) + uint32_t(e % F)));
+    }
+}
+// ... into staging rows of 32 + kStagePad, phi applied (with MASK, rows at
+// or beyond t_end become 0).
+template <bool MASK = false>
+__device__ __forceinline__ void stage_cols32_phi(lds_bf16 *stage, dwordx4 x, int64_t t0 = 0, int64_t t_end = 0) {
+    const int l = lane_id();
+    dwordx4 y = phi8(x);
+    if (MASK && t0 + (l >> 2) >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<lds_dwordx4 *>(stage + (l >> 2) * (kW2Half + kStagePad) + 8 * (l & 3)) = y;
+}
+// Rows [r0, r0 + NR) of a 16-row LDS tile (row stride F + kStagePad, F
+// columns) to rows t0 + r of a tensor with row stride S (dst already offset
+// to the first column); rows at or beyond t_end are not written.
+template <int F, int S, int NR>
+__device__ __forceinline__ void flush_rows(bf16 *__restrict__ dst, int64_t t0, int64_t t_end, const lds_bf16 *tile,
+                                           int r0) {
+    constexpr int PR = F / 8, NP = NR * PR;   // 16-byte pieces per row, in all
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < (NP + 63) / 64; ++i) {
+        const int p = 64 * i + l;
+        if (NP % 64 == 0 || p < NP) {
+            const int row = r0 + p / PR, col = 8 * (p % PR);
+            const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(tile + row * (F + kStagePad) + col);
+            const uint32_t t = uint32_t(t0) + uint32_t(row);
+            if (t < uint32_t(t_end)) *reinterpret_cast<dwordx4 *>(dst + (t * uint32_t(S) + uint32_t(col))) = y;
+        }
+    }
+}
+// Both wavefronts of the workgroup have finished their LDS accesses so far
+// (global loads in flight are not waited for).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Rows [d0, d0 + 16 DTH) of a row-major record, as Acc tiles (the layout of
+// state_load: REP puts Z in every column of the normalizer tile, otherwise
+// in column 0).
+template <int D, int M, int DTH, bool REP>
+__device__ __forceinline__ void rows_load(f32x4 (&St)[DTH][M / 16 + 1], const float *__restrict__ rec, int d0) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt) {
+        const int d = d0 + 16 * dt + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) St[dt][mt][r] = rec[(d + r) * M + 16 * mt + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[dt][M / 16][r] = (REP || c == 0) ? rec[D * M + d + r] : 0.f;
+    }
+}
+template <int D, int M, int DTH>
+__device__ __forceinline__ void rows_store(float *__restrict__ rec, const f32x4 (&St)[DTH][M / 16 + 1], int d0) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt) {
+        const int d = d0 + 16 * dt + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rec[(d + r) * M + 16 * mt + c] = St[dt][mt][r];
+        if (c == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rec[D * M + d + r] = St[dt][M / 16][r];
+        }
+    }
+}
+
+// Natural fragments y[tt][ft] written row-major into LDS (row stride
+// 16 NF + kStagePad), to be read back transposed by transposed_frags_lds
+// (the two halves of transpose_frags_lds, split so that other work can
+// run in between).
+template <int NF, int TT>
+__device__ __forceinline__ void put_frags_lds(lds_bf16 *stage, const bf16x4 (&y)[TT][NF]) {
+    constexpr int S = 16 * NF + kStagePad;
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < NF; ++ft)
+            *reinterpret_cast<lds_bf16x4 *>(stage + (16 * tt + c) * S + 16 * ft + 4 * g) = y[tt][ft];
+}
+
+} // namespace la
