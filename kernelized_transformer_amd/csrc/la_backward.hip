@@ -738,6 +738,233 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Non-causal, two wavefronts per segment: every query sees the full S_aug
+// and every key the full R_aug (record 0 of the head), so each wavefront
+// converts its rows of the sums to operand tiles, in both orientations, once
+// before its chunk loop.  dQ pass: Q (its 32 columns) and dout against S_aug,
+// the partial sums over d of out and den exchanged per chunk, plus this
+// segment's sum of phi(Q) gh^T.
+template <int D, int M>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq_nc_w2(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ dout, bf16 *__restrict__ dq,
+    const float *__restrict__ wsS, float *__restrict__ wsR, int64_t N, int64_t nseg, int64_t seg_tokens,
+    int64_t rec) {
+    static_assert(D == 2 * kW2Half, "two wavefronts of 32 feature rows");
+    typedef bf16x4 Fr;
+    constexpr int DTH = kW2Half / 16, MT = M / 16, PF = 2;
+    constexpr int NV = M / 32;
+    constexpr int SQ = 16 * (kW2Half + kStagePad), SV = 16 * (M + kStagePad);
+    constexpr int ST = stage_elems<DTH, MT + 1>(), SGT = stage_elems<MT + 1, 1>();
+    constexpr int NP = (SQ + SV > ST ? SQ + SV : ST) > SGT ? (SQ + SV > ST ? SQ + SV : ST) : SGT;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    const bf16 *Qw = q + bh * N * D + w * kW2Half;
+    const bf16 *G = dout + bh * N * M;
+    bf16 *DQw = dq + bh * N * D + w * kW2Half;
+
+    __shared__ __align__(16) bf16 priv_mem[2][NP];
+    __shared__ __align__(16) f32x4 xbuf[2][2][MT + 1][64];   // [chunk parity][wavefront][tile][lane]
+    lds_bf16 *sq = (lds_bf16 *)priv_mem[w];
+    lds_bf16 *sg = sq + SQ;
+
+    Fr SF[MT + 1][DTH], SFT[MT + 1][DTH];   // S_aug rows of this wavefront, both orientations
+    {
+        f32x4 St[DTH][MT + 1];
+        rows_load<D, M, DTH, true>(St, wsS + bh * nseg * rec, w * kW2Half);
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DTH; ++dt) SF[mt][dt] = IO<bf16>::to_frag(St[dt][mt]);
+        transpose_frags<DTH, MT + 1>(SFT, SF, sq);
+    }
+    f32x4 Ra[DTH][MT + 1];
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) Ra[dt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    dwordx4 lq[PF], lg[PF][NV];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        lq[b] = load_cols32<D>(Qw, t_begin + b * BCH, t_end);
+        load_rows32<M>(lg[b], G, t_begin + b * BCH, t_end);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * BCH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + b * BCH;
+        if (t0 >= t_end) break;   // uniform over the workgroup
+        stage_cols32_phi(sq, lq[b]);   // rows past t_end: gh = 0 below, so no mask
+        stage_lines<M, 1, false, false>(sg, lg[b], t0, t_end);
+        lq[b] = load_cols32<D>(Qw, t0 + PF * BCH, t_end);
+        load_rows32<M>(lg[b], G, t0 + PF * BCH, t_end);
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t t = t0 + c;
+        const bool valid = t < t_end;
+
+        Fr Qn[1][DTH], QT[1][DTH], Gr[1][MT];
+        natural_frags_lds<kW2Half, 1>(Qn, sq);
+        transposed_frags_lds<kW2Half, 1>(QT, sq);
+        natural_frags_lds<M, 1>(Gr, sg);
+        f32x4 Ot[MT + 1];
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) {
+            Ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dt = 0; dt < DTH; dt += 2) mma2(Ot[mt], SF[mt][dt], SF[mt][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
+        }
+        const int par = int((t0 - t_begin) / BCH) & 1;
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) xbuf[par][w][mt][lane] = Ot[mt];
+        lds_barrier();
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt) Ot[mt] += xbuf[par][1 - w][mt][lane];
+
+        const float inv = valid ? __builtin_amdgcn_rcpf(Ot[MT][0]) : 0.f;
+        float go = 0.f;
+        f32x4 gv[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 graw = IO<bf16>::to_f32(Gr[0][mt]);
+            const f32x4 o = Ot[mt] * inv;
+            go += graw[0] * o[0] + graw[1] * o[1] + graw[2] * o[2] + graw[3] * o[3];
+            gv[mt] = graw * inv;
+        }
+        go += __shfl_xor(go, 16);
+        go += __shfl_xor(go, 32);
+        const float h = -go * inv;
+        Fr Gn[1][MT + 1];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<bf16>::to_frag(gv[mt]);
+        Gn[0][MT] = IO<bf16>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
+
+        // dL/dqh^T for this wavefront's rows d = S_aug gh, times min(phi(q), 1)
+        lds_bf16 *dtile = sg;   // the dout rows are read
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, SFT[mt][dt], SFT[mt + 1][dt], Gn[0][mt], Gn[0][mt + 1]);
+            if ((MT & 1) == 0) mma1(acc, SFT[MT][dt], Gn[0][MT]);
+            const f32x4 qh = IO<bf16>::to_f32(Qn[0][dt]);
+            const f32x4 dp = {__builtin_fminf(qh[0], 1.f), __builtin_fminf(qh[1], 1.f), __builtin_fminf(qh[2], 1.f),
+                              __builtin_fminf(qh[3], 1.f)};
+            tile_put_bf16<kW2Half>(dtile, dt, IO<bf16>::from_f32(acc * dp));
+        }
+        flush_rows<kW2Half, D, 16>(DQw, t0, t_end, dtile, 0);
+
+        Fr GT[1][MT + 1];
+        transpose_frags<MT + 1, 1>(GT, Gn, sq);   // the staged rows are all read
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+            for (int mt = 0; mt <= MT; ++mt) mma1(Ra[dt][mt], QT[0][dt], GT[0][mt]);
+    }
+    }
+    rows_store<D, M, DTH>(wsR + (bh * nseg + seg) * rec, Ra, w * kW2Half);
+}
+
+// dK/dV pass: K (its 32 columns) and V against the full R_aug; dV's partial
+// sums over d are exchanged per chunk.
+template <int D, int M>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv_nc_w2(
+    const bf16 *__restrict__ k, const bf16 *__restrict__ v, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+    const float *__restrict__ wsR, int64_t N, int64_t nseg, int64_t seg_tokens, int64_t rec) {
+    static_assert(D == 2 * kW2Half, "two wavefronts of 32 feature rows");
+    typedef bf16x4 Fr;
+    constexpr int DTH = kW2Half / 16, MT = M / 16, MH = MT / 2, PF = 2;
+    constexpr int NV = M / 32;
+    constexpr int SQ = 16 * (kW2Half + kStagePad), SV = 16 * (M + kStagePad);
+    constexpr int ST = stage_elems<DTH, MT + 1>();
+    constexpr int NP = SQ + SV > ST ? SQ + SV : ST;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens;
+    const int64_t t_end = min(N, t_begin + seg_tokens);
+    const bf16 *Kw = k + bh * N * D + w * kW2Half;
+    const bf16 *V = v + bh * N * M;
+    bf16 *DKw = dk + bh * N * D + w * kW2Half;
+    bf16 *DVw = dv + bh * N * M + w * (M / 2);
+
+    __shared__ __align__(16) bf16 priv_mem[2][NP];
+    __shared__ __align__(16) f32x4 xbuf[2][2][MH][64];   // [chunk parity][wavefront][tile][lane]
+    lds_bf16 *sk = (lds_bf16 *)priv_mem[w];
+    lds_bf16 *sv = sk + SQ;
+
+    Fr RF[MT + 1][DTH], RFT[MT + 1][DTH];   // R_aug rows of this wavefront, both orientations
+    {
+        f32x4 Rr[DTH][MT + 1];
+        rows_load<D, M, DTH, false>(Rr, wsR + bh * nseg * rec, w * kW2Half);
+#pragma unroll
+        for (int mt = 0; mt <= MT; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DTH; ++dt) RF[mt][dt] = IO<bf16>::to_frag(Rr[dt][mt]);
+        transpose_frags<DTH, MT + 1>(RFT, RF, sk);
+    }
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    dwordx4 lk[PF], lv[PF][NV];
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        lk[b] = load_cols32<D>(Kw, t_begin + b * BCH, t_end);
+        load_rows32<M>(lv[b], V, t_begin + b * BCH, t_end);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * BCH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + b * BCH;
+        if (t0 >= t_end) break;   // uniform over the workgroup
+        // rows past t_end only produce outputs that are not stored
+        stage_cols32_phi(sk, lk[b]);
+        stage_lines<M, 1, false, false>(sv, lv[b], t0, t_end);
+        lk[b] = load_cols32<D>(Kw, t0 + PF * BCH, t_end);
+        load_rows32<M>(lv[b], V, t0 + PF * BCH, t_end);
+        __builtin_amdgcn_sched_barrier(0);
+
+        Fr Kn[1][DTH], Vn[1][MT];
+        natural_frags_lds<kW2Half, 1>(Kn, sk);
+        natural_frags_lds<M, 1>(Vn, sv);
+        // dV^T shares over this wavefront's rows d: sum_d R[d][m] kh[j][d]
+        f32x4 dvs[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            dvs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dt = 0; dt < DTH; dt += 2) mma2(dvs[mt], RF[mt][dt], RF[mt][dt + 1], Kn[0][dt], Kn[0][dt + 1]);
+        }
+        const int par = int((t0 - t_begin) / BCH) & 1;
+#pragma unroll
+        for (int i = 0; i < MH; ++i) xbuf[par][w][i][lane] = w ? dvs[i] : dvs[MH + i];
+
+        // dL/dkh^T for this wavefront's rows d = R_aug vh, times min(phi(k), 1)
+        lds_bf16 *dtile = sk;   // the staged rows are read
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt + 1 <= MT; mt += 2) mma2(acc, RFT[mt][dt], RFT[mt + 1][dt], Vn[0][mt], Vn[0][mt + 1]);
+            mma1(acc, RFT[MT][dt], k0ones);
+            const f32x4 kh = IO<bf16>::to_f32(Kn[0][dt]);
+            const f32x4 dp = {__builtin_fminf(kh[0], 1.f), __builtin_fminf(kh[1], 1.f), __builtin_fminf(kh[2], 1.f),
+                              __builtin_fminf(kh[3], 1.f)};
+            tile_put_bf16<kW2Half>(dtile, dt, IO<bf16>::from_f32(acc * dp));
+        }
+        flush_rows<kW2Half, D, 16>(DKw, t0, t_end, dtile, 0);
+
+        lds_barrier();
+        lds_bf16 *vtile = dtile;
+#pragma unroll
+        for (int i = 0; i < MH; ++i)
+            tile_put_bf16<M / 2>(vtile, i, IO<bf16>::from_f32((w ? dvs[MH + i] : dvs[i]) + xbuf[par][1 - w][i][lane]));
+        flush_rows<M / 2, M, 16>(DVw, t0, t_end, vtile, 0);
+    }
+    }
+}
+
 template <typename T, int D, int M>
 static hipError_t run_backward(bool causal, const void *q, const void *k, const void *v, const void *dout, void *dq,
                                void *dk, void *dv, int64_t BH, int64_t N, float *ws, hipStream_t s) {
@@ -751,8 +978,20 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
     const int dt = sizeof(T) == 4 ? 0 : 1;
     hipError_t e = launch_segment_state(dt, k, v, wsS, BH, N, D, M, s);
     if (e != hipSuccess) return e;
+    // two wavefronts per segment (their kernels address a head with 32-bit
+    // element offsets)
+    const bool w2 = sizeof(T) == 2 && D == 2 * kW2Half && N * (D > M ? D : M) <= int64_t(INT32_MAX);
     if (!causal) {   // full sums S_aug, then R_aug, each into record 0 of the head
         if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+        if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) if (w2) {
+            hipLaunchKernelGGL((k_bwd_dq_nc_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)dout,
+                               (bf16 *)dq, (const float *)wsS, wsR, N, p.nseg, p.seg_tokens, p.rec);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+            hipLaunchKernelGGL((k_bwd_dkdv_nc_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)k, (const bf16 *)v,
+                               (bf16 *)dk, (bf16 *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((k_bwd_dq<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
                            (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, (T *)nullptr,
                            (float *)nullptr, N, p.nseg, p.seg_tokens, p.rec);
@@ -764,9 +1003,6 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
         return hipGetLastError();
     }
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
-    // two wavefronts per segment (their kernels address a head with 32-bit
-    // element offsets)
-    const bool w2 = sizeof(T) == 2 && D == 2 * kW2Half && N * (D > M ? D : M) <= int64_t(INT32_MAX);
     if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) if (w2) {
         hipLaunchKernelGGL((k_bwd_dq_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
                            (const bf16 *)v, (const bf16 *)dout, (bf16 *)dq, (const float *)wsS, wsR, (bf16 *)gbuf,

@@ -175,6 +175,9 @@ BWD_NC_CASES = [
     ("n50_d64m32_bf16", _wl(203, 1, 3, 50, 64, 32, "bf16")),
     ("n3001_ragged_f32", _wl(204, 1, 2, 3001, 64, 64, "f32")),
     ("n100000_many_segments", _wl(205, 1, 1, 100000, 32, 32, "bf16")),
+    # bf16 at D = 64: two wavefronts per segment
+    ("n3001_ragged_bf16", _wl(206, 1, 2, 3001, 64, 64, "bf16")),
+    ("n20000_d64m32_bf16", _wl(207, 2, 2, 20000, 64, 32, "bf16")),
 ]
 
 
