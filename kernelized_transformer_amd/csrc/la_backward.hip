@@ -880,7 +880,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int SQ = 16 * (kW2Half + kStagePad), SV = 16 * (M + kStagePad);
     constexpr int ST = stage_elems<DTH, MT + 1>();
     constexpr int NP = SQ + SV > ST ? SQ + SV : ST;
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t t_begin = seg * seg_tokens;
