@@ -6,7 +6,6 @@
 
 namespace la {
 
-// ---- two wavefronts per segment (bf16, D = 64) ---------------------------
 // A segment's states are split by feature row d between two wavefronts:
 // wavefront w owns rows [32 w, 32 w + 32) and loads only its 32 columns of
 // the d-indexed inputs.  Helpers for those kernels; their global accesses
@@ -36,14 +35,11 @@ __device__ __forceinline__ void load_rows32(dwordx4 (&x)[F / 32], const bf16 *__
         x[i] = *reinterpret_cast<const dwordx4 *>(base + (t * uint32_t(F) + uint32_t(e % F)));
     }
 }
-// ... into staging rows of 32 + kStagePad, phi applied (with MASK, rows at
-// or beyond t_end become 0).
-template <bool MASK = false>
-__device__ __forceinline__ void stage_cols32_phi(lds_bf16 *stage, dwordx4 x, int64_t t0 = 0, int64_t t_end = 0) {
+// ... into staging rows of 32 + kStagePad, phi applied (no row masks: the
+// callers keep rows past t_end out of every stored result themselves).
+__device__ __forceinline__ void stage_cols32_phi(lds_bf16 *stage, dwordx4 x) {
     const int l = lane_id();
-    dwordx4 y = phi8(x);
-    if (MASK && t0 + (l >> 2) >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<lds_dwordx4 *>(stage + (l >> 2) * (kW2Half + kStagePad) + 8 * (l & 3)) = y;
+    *reinterpret_cast<lds_dwordx4 *>(stage + (l >> 2) * (kW2Half + kStagePad) + 8 * (l & 3)) = phi8(x);
 }
 // Rows [r0, r0 + NR) of a 16-row LDS tile (row stride F + kStagePad, F
 // columns) to rows t0 + r of a tensor with row stride S (dst already offset
