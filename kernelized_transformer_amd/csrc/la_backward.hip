@@ -614,7 +614,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const Fr k0ones = frag_k0_ones<Fr>();
 
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
-    auto chunk = [&](int64_t step) { return t_begin + max<int64_t>(nch - 1 - step, 0) * BCH; };
+    auto chunk = [&](int64_t step) { return t_begin + imax64(nch - 1 - step, 0) * BCH; };
     dwordx4 lq[PF], lk[PF], lv[PF][NV], lg[PF][NV];
     float lh[PF];
     auto load_all = [&](int b, int64_t t0) {

@@ -41,6 +41,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Integer min / max for 64-bit indices (plain selects: the templated
+// min / max of the device math headers convert through double).
+__device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (positive).
 // Evaluated as max(exp(-|x|), x + 1) -- for x <= 0, exp(x) >= x + 1; for
 // x > 0, exp(-x) < 1 < x + 1 -- which costs one exponential and no select.

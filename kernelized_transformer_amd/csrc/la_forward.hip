@@ -244,7 +244,7 @@ __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, c
     // past the first chunk (s >= nch) re-read chunk 0 and add nothing.
     constexpr int NK = Lines<D, TT>::n, NV = Lines<M, TT>::n;
     const int64_t nch = (t_end - t_begin + CH - 1) / CH;
-    auto chunk = [&](int64_t step) { return t_begin + max<int64_t>(nch - 1 - step, 0) * CH; };
+    auto chunk = [&](int64_t step) { return t_begin + imax64(nch - 1 - step, 0) * CH; };
     dwordx4 rk[PF][NK], rv[PF][NV];
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
