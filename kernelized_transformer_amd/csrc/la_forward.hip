@@ -396,27 +396,57 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
     }
 }
 
-// ---- per-segment kernels (non-causal path, and the backward's forward state) ----
+// ---- per-segment kernel (the backward's forward and reverse states) ----------
+// Record of segment `seg`: sum over its tokens of phi(K_t) [V_t, 1]^T,
+// written with state_store.  kSegWaves wavefronts share a segment: wave w
+// sums the w-th run of whole chunks, then the partial states are added
+// through LDS in wavefront order (a fixed order: results do not vary from
+// run to run), so that two wavefronts per SIMD keep K and V streaming.
+constexpr int kSegWaves = 2;
 template <typename T, int D, int M>
-__global__ __launch_bounds__(64) void k_segment_state(const T *__restrict__ k, const T *__restrict__ v,
-                                                      float *__restrict__ ws, int64_t N, int64_t nseg,
-                                                      int64_t seg_tokens, int64_t rec) {
+__global__ __launch_bounds__(64 * kSegWaves) void k_segment_state(const T *__restrict__ k, const T *__restrict__ v,
+                                                                  float *__restrict__ ws, int64_t N, int64_t nseg,
+                                                                  int64_t seg_tokens, int64_t rec) {
+    static_assert(kSegWaves == 2, "the partial states are combined pairwise");
+    constexpr int STG = stage_elems<D / 16, TT>() + stage_elems<M / 16, TT>();   // bf16 per wavefront
+    constexpr int NTILE = (D / 16) * (M / 16 + 1);
+    constexpr int STAGE_BYTES = kSegWaves * STG * int(sizeof(bf16));
+    constexpr int SLOT_BYTES = NTILE * 64 * int(sizeof(f32x4));   // one wavefront's St, lane-major
+    __shared__ __align__(16) unsigned char lds_raw[STAGE_BYTES > SLOT_BYTES ? STAGE_BYTES : SLOT_BYTES];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
     const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int64_t t_begin = seg * seg_tokens;
-    const int64_t t_end = min(N, t_begin + seg_tokens);
-    __shared__ bf16 stage[stage_elems<D / 16, TT>() + stage_elems<M / 16, TT>()];
-    lds_bf16 *sk = (lds_bf16 *)(stage);
+    const int64_t s_begin = seg * seg_tokens, s_end = imin64(N, s_begin + seg_tokens);
+    const int64_t nch = (s_end - s_begin + kChunk - 1) / kChunk;
+    const int64_t cpw = (nch + kSegWaves - 1) / kSegWaves;   // chunks per wavefront
+    const int64_t t_begin = imin64(s_end, s_begin + wave * cpw * kChunk);
+    const int64_t t_end = imin64(s_end, t_begin + cpw * kChunk);
+    lds_bf16 *sk = (lds_bf16 *)(reinterpret_cast<bf16 *>(lds_raw) + wave * STG);
+    lds_bf16 *sv = sk + stage_elems<D / 16, TT>();
     f32x4 St[D / 16][M / 16 + 1];
     state_zero<D, M>(St);
-    if constexpr (sizeof(T) == 2)
-        seg_aggregate_bf16<D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk,
-                                            sk + stage_elems<D / 16, TT>());
-    else
-        seg_aggregate<T, D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk,
-                                          sk + stage_elems<D / 16, TT>());
-    state_store<D, M>(ws + (bh * nseg + seg) * rec, St);
+    if (t_begin < t_end) {   // uniform; a short segment can leave wavefront 1 without chunks
+        if constexpr (sizeof(T) == 2)
+            seg_aggregate_bf16<D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
+        else
+            seg_aggregate<T, D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
+    }
+    __syncthreads();   // the staging areas are free
+    f32x4 *slot = reinterpret_cast<f32x4 *>(lds_raw);
+    if (wave == 1) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int mt = 0; mt <= M / 16; ++mt) slot[(dt * (M / 16 + 1) + mt) * 64 + lane] = St[dt][mt];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int mt = 0; mt <= M / 16; ++mt) St[dt][mt] += slot[(dt * (M / 16 + 1) + mt) * 64 + lane];
+        state_store<D, M>(ws + (bh * nseg + seg) * rec, St);
+    }
 }
-
 
 // ---- scan over segments ---------------------------------------------------
 // Block = kScanCols float4 columns of the records x kScanG groups of
@@ -843,8 +873,8 @@ static hipError_t run_segment_state_t(const void *k, const void *v, float *ws, i
     const dim3 grid(unsigned(BH * p.nseg));
 #define LA_SEGSTATE_CASE(DD, MM)                                                                                 \
     if (D == DD && M == MM) {                                                                                    \
-        hipLaunchKernelGGL((k_segment_state<T, DD, MM>), grid, dim3(64), 0, s, (const T *)k, (const T *)v, ws, N, \
-                           p.nseg, p.seg_tokens, p.rec);                                                         \
+        hipLaunchKernelGGL((k_segment_state<T, DD, MM>), grid, dim3(64 * kSegWaves), 0, s, (const T *)k,         \
+                           (const T *)v, ws, N, p.nseg, p.seg_tokens, p.rec);                                    \
         return hipGetLastError();                                                                                \
     }
     LA_SEGSTATE_CASE(32, 32)
