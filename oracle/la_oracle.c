@@ -22,7 +22,7 @@
  * are independent recurrences, so they are spread over OpenMP threads; the
  * order of operations inside one slice is the plain sequential order.
  *
- * Readings where the pages are silent (each one is also listed in the design doc):
+ * Readings where the pages are silent:
  *   - feature map phi(x) = elu(x) + 1 with alpha = 1, i.e. x + 1 for x > 0
  *     and exp(x) otherwise ([deck] slide 3; [summary] 3.2.1).  Both branches
  *     give value 1 and slope 1 at x = 0, so the branch choice at 0 is moot.
