@@ -144,6 +144,9 @@ BWD_CASES = [
     ("n17_d64m64_bf16", _wl(127, 2, 3, 17, 64, 64, "bf16")),
     ("n3001_ragged_bf16", _wl(128, 1, 2, 3001, 64, 64, "bf16")),
     ("n20000_d64m32_bf16", _wl(129, 2, 2, 20000, 64, 32, "bf16")),
+    # many heads: one segment per head (the segment plan's other extreme)
+    ("h256_n300_d64_bf16", _wl(141, 4, 64, 300, 64, 64, "bf16")),
+    ("h512_n40_d32m64_f32", _wl(142, 8, 64, 40, 32, 64, "f32")),
 ]
 
 
@@ -178,6 +181,7 @@ BWD_NC_CASES = [
     # bf16 at D = 64: two wavefronts per segment
     ("n3001_ragged_bf16", _wl(206, 1, 2, 3001, 64, 64, "bf16")),
     ("n20000_d64m32_bf16", _wl(207, 2, 2, 20000, 64, 32, "bf16")),
+    ("h256_n300_d64_bf16", _wl(143, 4, 64, 300, 64, 64, "bf16")),
 ]
 
 
@@ -221,6 +225,19 @@ def test_decode_small_f32():
     Zo = np.zeros((w.B, w.H, w.D))
     ref = np.stack([oracle.decode_step(qs[t], ks[t], vs[t], So, Zo) for t in range(80)])
     check("decode out", outs, ref, "f32", lead=3)
+    check("decode S", S, So, "f32")
+    check("decode Z", Z, Zo, "f32")
+
+
+@pytest.mark.parametrize("D,M", [(64, 32), (32, 64)])
+def test_decode_small_bf16_mixed_head_sizes(D, M):
+    w = _wl(144, 3, 2, 1, D, M, "bf16")
+    _say(f"decode small bf16: B3 H2 D{D} M{M}, 60 steps")
+    qs, ks, vs, outs, S, Z = _decode_run(w, 60)
+    So = np.zeros((w.B, w.H, w.D, w.M))
+    Zo = np.zeros((w.B, w.H, w.D))
+    ref = np.stack([oracle.decode_step(qs[t], ks[t], vs[t], So, Zo) for t in range(60)])
+    check("decode out", outs, ref, "bf16", lead=3)
     check("decode S", S, So, "f32")
     check("decode Z", Z, Zo, "f32")
 
