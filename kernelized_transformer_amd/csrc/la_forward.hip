@@ -30,6 +30,7 @@
 
 #include "la_chunk.h"
 #include "la_internal.h"
+#include "la_split.h"
 
 namespace la {
 
@@ -211,10 +212,11 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
 // Normalizes one 16-token output tile (Ot[mt] = out^T tiles, every row of
 // the normalizer block Ot[M/16] holding the tokens' denominators) and stores
 // it through the wavefront's LDS tile `so` (16 rows of M + kStagePad), so
-// that each store instruction writes 1 KB of whole rows.
+// that each store instruction writes 1 KB of whole rows.  O points at the
+// wavefront's first token; t0 and n count tokens from there.
 template <int M>
-__device__ __forceinline__ void store_tile_bf16(bf16 *__restrict__ O, int64_t t0, int64_t t_end,
-                                                const f32x4 (&Ot)[M / 16 + 1], lds_bf16 *so) {
+__device__ __forceinline__ void store_tile_bf16(bf16 *__restrict__ O, int t0, int n, const f32x4 (&Ot)[M / 16 + 1],
+                                                lds_bf16 *so) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
     const float inv = __builtin_amdgcn_rcpf(Ot[M / 16][0]);
 #pragma unroll
@@ -224,15 +226,18 @@ __device__ __forceinline__ void store_tile_bf16(bf16 *__restrict__ O, int64_t t0
     for (int i = 0; i < M / 32; ++i) {
         const int e = (64 * i + lane) * 8, row = e / M, col = e % M;
         const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(so + row * (M + kStagePad) + col);
-        const int64_t t = t0 + row;
-        if (t < t_end) *reinterpret_cast<dwordx4 *>(O + t * M + col) = y;
+        const uint32_t t = uint32_t(t0 + row);
+        if (t < uint32_t(n))
+            *reinterpret_cast<dwordx4 *>(reinterpret_cast<char *>(O) + (t * uint32_t(2 * M) + uint32_t(2 * col))) = y;
     }
 }
 
 // Same products as above; the chunk's rows are fetched with contiguous
 // 16-byte loads, the feature map is applied in registers, and the rows are
 // staged in the wavefront's LDS area, from which the natural and the
-// token-contiguous fragments are read.
+// token-contiguous fragments are read.  Global addresses are 32-bit element
+// offsets from the wavefront's first token (a sub-segment spans far fewer
+// than 2^31 / 64 tokens), so each load or store costs one address add.
 
 template <int D, int M, int PF, bool PHI = true>
 __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, const bf16 *__restrict__ V,
@@ -242,25 +247,30 @@ __device__ __forceinline__ void seg_aggregate_bf16(const bf16 *__restrict__ K, c
     // chunks are the most recently read when its output pass starts with them
     // (and are often still in L2).  Step s visits chunk nch - 1 - s; steps
     // past the first chunk (s >= nch) re-read chunk 0 and add nothing.
+    static_assert(TT == 1, "16-row chunks");
     constexpr int NK = Lines<D, TT>::n, NV = Lines<M, TT>::n;
-    const int64_t nch = (t_end - t_begin + CH - 1) / CH;
-    auto chunk = [&](int64_t step) { return t_begin + imax64(nch - 1 - step, 0) * CH; };
+    // loads are relative to row tb and clamped to its n rows; an empty range
+    // (t_begin == t_end) keeps a valid row to load and has no chunks
+    const int64_t tb = imin64(t_begin, t_end - 1);
+    const bf16 *Kw = K + tb * D, *Vw = V + tb * M;
+    const int n = int(t_end - tb), nch = int((t_end - t_begin + CH - 1) / CH);
+    auto chunk = [&](int step) { return max(nch - 1 - step, 0) * CH; };
     dwordx4 rk[PF][NK], rv[PF][NV];
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
-        load_lines<D, TT>(rk[b], K, chunk(b), t_end);
-        load_lines<M, TT>(rv[b], V, chunk(b), t_end);
+        load_rows32<D>(rk[b], Kw, chunk(b), n);
+        load_rows32<M>(rv[b], Vw, chunk(b), n);
     }
-    for (int64_t s0 = 0; s0 < nch; s0 += PF) {
+    for (int s0 = 0; s0 < nch; s0 += PF) {
 #pragma unroll
         for (int b = 0; b < PF; ++b) {
-            const int64_t step = s0 + b, t0 = chunk(step);
+            const int step = s0 + b, t0 = chunk(step);
             if (step < nch) {   // uniform
-                stage_lines<D, TT, PHI, true>(sk, rk[b], t0, t_end);   // rows past t_end masked
-                stage_lines<M, TT, false>(sv, rv[b], t0, t_end);
+                stage_lines<D, TT, PHI, true>(sk, rk[b], t0, n);   // rows past the end masked
+                stage_lines<M, TT, false>(sv, rv[b], t0, n);
             }
-            load_lines<D, TT>(rk[b], K, chunk(step + PF), t_end);
-            load_lines<M, TT>(rv[b], V, chunk(step + PF), t_end);
+            load_rows32<D>(rk[b], Kw, chunk(step + PF), n);
+            load_rows32<M>(rv[b], Vw, chunk(step + PF), n);
             __builtin_amdgcn_sched_barrier(0);
             if (step < nch) {
                 bf16x4 KT[TT][D / 16], VT[TT][M / 16];
@@ -280,12 +290,14 @@ template <int D, int M, int PF> struct OutAhead {
     template <bool CAUSAL>
     __device__ __forceinline__ void load(const bf16 *Q, const bf16 *K, const bf16 *V, int64_t t_begin,
                                          int64_t t_end) {
+        const int64_t tb = imin64(t_begin, t_end - 1);   // an empty range loads a valid row
+        const int n = int(t_end - tb);
 #pragma unroll
         for (int b = 0; b < PF; ++b) {
-            load_lines<D, TT>(rq[b], Q, t_begin + b * CH, t_end);
+            load_rows32<D>(rq[b], Q + tb * D, b * CH, n);
             if (CAUSAL) {
-                load_lines<D, TT>(rk[b], K, t_begin + b * CH, t_end);
-                load_lines<M, TT>(rv[b], V, t_begin + b * CH, t_end);
+                load_rows32<D>(rk[b], K + tb * D, b * CH, n);
+                load_rows32<M>(rv[b], V + tb * M, b * CH, n);
             }
         }
     }
@@ -302,25 +314,31 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
     const Fr ones = frag_ones<Fr>();
     const Fr zero = frag_zero<Fr>();
 
+    static_assert(TT == 1, "16-row chunks");
     auto &rq = ahead.rq;
     auto &rk = ahead.rk;
     auto &rv = ahead.rv;
-    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
+    // as in seg_aggregate_bf16: rows relative to tb (an empty range has no chunks)
+    const int64_t tb = imin64(t_begin, t_end - 1);
+    const bf16 *Qw = Q + tb * D, *Kw = K + tb * D, *Vw = V + tb * M;
+    bf16 *Ow = O + tb * M;
+    const int n = int(t_end - tb), len = int(t_end - t_begin);
+    for (int t00 = 0; t00 < len; t00 += PF * CH) {
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
-        const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
-        // no row masks: rows past t_end hold copies of the last valid row (finite),
+        const int t0 = t00 + b * CH;   // may lie past the end: fully masked, no stores
+        // no row masks: rows past the end hold copies of the last valid row (finite),
         // their outputs are not stored, the causal mask keeps them out of every
         // stored output, and the state is not used after the last chunk
-        stage_lines<D, TT, PHI, false>(sq, rq[b], t0, t_end);
+        stage_lines<D, TT, PHI, false>(sq, rq[b], t0, n);
         if (CAUSAL) {
-            stage_lines<D, TT, PHI, false>(sk, rk[b], t0, t_end);
-            stage_lines<M, TT, false, false>(sv, rv[b], t0, t_end);
+            stage_lines<D, TT, PHI, false>(sk, rk[b], t0, n);
+            stage_lines<M, TT, false, false>(sv, rv[b], t0, n);
         }
-        load_lines<D, TT>(rq[b], Q, t0 + PF * CH, t_end);
+        load_rows32<D>(rq[b], Qw, t0 + PF * CH, n);
         if (CAUSAL) {
-            load_lines<D, TT>(rk[b], K, t0 + PF * CH, t_end);
-            load_lines<M, TT>(rv[b], V, t0 + PF * CH, t_end);
+            load_rows32<D>(rk[b], Kw, t0 + PF * CH, n);
+            load_rows32<M>(rv[b], Vw, t0 + PF * CH, n);
         }
         __builtin_amdgcn_sched_barrier(0);
         Fr Qn[TT][DT];
@@ -390,7 +408,7 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
             f32x4 tile[MT + 1];
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt) tile[mt] = Ot[mt][it];
-            store_tile_bf16<M>(O, t0 + 16 * it, t_end, tile, so);
+            store_tile_bf16<M>(Ow, t0 + 16 * it, n, tile, so);
         }
     }
     }

@@ -9,8 +9,9 @@ namespace la {
 // A segment's states are split by feature row d between two wavefronts:
 // wavefront w owns rows [32 w, 32 w + 32) and loads only its 32 columns of
 // the d-indexed inputs.  Helpers for those kernels; their global accesses
-// use 32-bit element offsets from a per-head base pointer (callers check
-// that a head's elements fit).
+// use 32-bit offsets from a per-head base pointer (callers check that a
+// head's bytes fit), computed in bytes so that the compiler adds them to the
+// scalar base in the load or store itself.
 constexpr int kW2Half = 32;   // feature columns per wavefront
 
 // 16 rows x 32 bf16 columns of a row-major tensor with row stride S (base
@@ -18,10 +19,11 @@ constexpr int kW2Half = 32;   // feature columns per wavefront
 // 8 (l % 4) .. + 7.  Rows at or beyond t_end read row t_end - 1.
 template <int S>
 __device__ __forceinline__ dwordx4 load_cols32(const bf16 *__restrict__ base, int64_t t0, int64_t t_end) {
-    // 32-bit element offsets from the (uniform) per-head base: one address add per load
+    // 32-bit byte offsets from the (uniform) per-head base: the load adds them to the scalar base
     const int l = lane_id();
     const uint32_t t = min(uint32_t(t0) + uint32_t(l >> 2), uint32_t(t_end - 1));
-    return *reinterpret_cast<const dwordx4 *>(base + (t * uint32_t(S) + uint32_t(8 * (l & 3))));
+    return *reinterpret_cast<const dwordx4 *>(reinterpret_cast<const char *>(base) +
+                                              (t * uint32_t(2 * S) + uint32_t(16 * (l & 3))));
 }
 // 16 whole rows of F bf16 features (as load_lines, 32-bit offsets).
 template <int F>
@@ -32,7 +34,8 @@ __device__ __forceinline__ void load_rows32(dwordx4 (&x)[F / 32], const bf16 *__
     for (int i = 0; i < F / 32; ++i) {
         const int e = (64 * i + l) * 8;
         const uint32_t t = min(uint32_t(t0) + uint32_t(e / F), uint32_t(t_end - 1));
-        x[i] = *reinterpret_cast<const dwordx4 *>(base + (t * uint32_t(F) + uint32_t(e % F)));
+        x[i] = *reinterpret_cast<const dwordx4 *>(reinterpret_cast<const char *>(base) +
+                                                   (t * uint32_t(2 * F) + uint32_t(2 * (e % F))));
     }
 }
 // ... into staging rows of 32 + kStagePad, phi applied (no row masks: the
@@ -56,7 +59,8 @@ __device__ __forceinline__ void flush_rows(bf16 *__restrict__ dst, int64_t t0, i
             const int row = r0 + p / PR, col = 8 * (p % PR);
             const dwordx4 y = *reinterpret_cast<const lds_dwordx4 *>(tile + row * (F + kStagePad) + col);
             const uint32_t t = uint32_t(t0) + uint32_t(row);
-            if (t < uint32_t(t_end)) *reinterpret_cast<dwordx4 *>(dst + (t * uint32_t(S) + uint32_t(col))) = y;
+            if (t < uint32_t(t_end))
+                *reinterpret_cast<dwordx4 *>(reinterpret_cast<char *>(dst) + (t * uint32_t(2 * S) + uint32_t(2 * col))) = y;
         }
     }
 }
