@@ -52,7 +52,7 @@ def _args():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal"],
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal", "sweep"],
                     default="all",
                     help="restrict the timed work (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -394,8 +394,8 @@ def main():
 
     if a.only == "all":
         results["small_workloads"] = {wl.WORKLOADS[i].name: fwd_rate(wl.WORKLOADS[i]) for i in (1, 2, 3)}
-        if a.sweep:
-            results["sweep"] = {str(n): fwd_rate(w4.with_n(n)) for n in wl.SWEEP_N}
+    if (a.only == "all" and a.sweep) or a.only == "sweep":
+        results["sweep"] = {str(n): fwd_rate(w4.with_n(n)) for n in wl.SWEEP_N}
 
     # ---- decode ------------------------------------------------------------------------------
     # A separate workload: the long-sequence tensors are released first, so that
