@@ -414,7 +414,7 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
     }
 }
 
-// ---- per-segment kernel (the backward's forward and reverse states) ----------
+// ---- per-segment kernel (the backward's forward-direction states) -----------
 // Record of segment `seg`: sum over its tokens of phi(K_t) [V_t, 1]^T,
 // written with state_store.  kSegWaves wavefronts share a segment: wave w
 // sums the w-th run of whole chunks, then the partial states are added
