@@ -850,6 +850,11 @@ static hipError_t run_forward(bool causal, const void *q, const void *k, const v
     const FusedPlan p = make_fused_plan(BH, N, D, M);
     if (fused_slice_rows(p.nblk, causal ? p.nblk - 1 : p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows)
         return hipErrorInvalidValue;
+    // the bf16 chunk loops address a wavefront's rows by 32-bit byte offsets
+    // (far from binding: a wavefront's share of any problem that fits in memory
+    // spans well under 1 GB)
+    if ((p.sub_tokens + 2 * kChunk) * int64_t(D > M ? D : M) * int64_t(sizeof(T)) > int64_t(UINT32_MAX))
+        return hipErrorInvalidValue;
     char *base = reinterpret_cast<char *>(ws);
     int *header = reinterpret_cast<int *>(base);
     unsigned long long *flags = reinterpret_cast<unsigned long long *>(base + p.flags_off);
