@@ -242,6 +242,33 @@ __device__ __forceinline__ void transpose_frags(bf16x4 (&yt)[TT][NF], const bf16
     transpose_frags_lds<NF, TT>(yt, y, stage);
 }
 
+// fp32 token-contiguous copies through LDS instead of the matrix cores (a
+// 16-byte write of each lane's 4 features, four 4-byte reads of its 4
+// tokens; exact).  The wavefront's tile holds 16 TT rows of 16 NF floats at
+// a stride of 16 NF + 4 (the four row groups a read touches then fall in
+// different banks).  Reads follow the writes in the same wavefront, so no
+// barrier is needed; the tile is private to the wavefront.
+typedef __attribute__((address_space(3))) float lds_f32;
+template <int NF, int TT> constexpr int f32_stage_floats() { return 16 * TT * (16 * NF + 4); }
+template <int NF, int TT>
+__device__ __forceinline__ void transpose_frags_f32_lds(f32x4 (&yt)[TT][NF], const f32x4 (&y)[TT][NF],
+                                                        lds_f32 *tile) {
+    constexpr int S = 16 * NF + 4;
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < NF; ++ft)
+            *reinterpret_cast<__attribute__((address_space(3))) f32x4 *>(tile + (16 * tt + c) * S + 16 * ft + 4 * g) =
+                y[tt][ft];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ft = 0; ft < NF; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yt[tt][ft][r] = tile[(16 * tt + 4 * g + r) * S + 16 * ft + c];
+}
+
 // ---- state records --------------------------------------------------------
 // A state record is D*M floats of S (row-major [d][m]) followed by D floats
 // of Z.  In registers the state is an augmented D x (M + 16) matrix of Acc

@@ -26,6 +26,7 @@
 //   non-causal (three launches): per-segment states, their sum per (b, h),
 //     then the readout.
 #include <atomic>
+#include <type_traits>
 #include <chrono>
 
 #include "la_chunk.h"
@@ -45,12 +46,24 @@ template <typename T, int D, int M> constexpr int fwd_prefetch() {
 
 // ---- chunk loops ------------------------------------------------------------
 
+// Token-contiguous copies in the generic chunk loops: fp32 fragments go
+// through the wavefront's LDS area when F32_LDS (the fused forward's area
+// holds both fp32 tiles), otherwise as transpose_frags does (bf16 through
+// LDS, fp32 through an identity product).
+template <int NF, bool F32_LDS, typename Fr>
+__device__ __forceinline__ void tokens_major(Fr (&yt)[TT][NF], const Fr (&y)[TT][NF], lds_bf16 *stage) {
+    if constexpr (F32_LDS && std::is_same<Fr, f32x4>::value)
+        transpose_frags_f32_lds<NF, TT>(yt, y, (lds_f32 *)stage);
+    else
+        transpose_frags<NF, TT>(yt, y, stage);
+}
+
 // St += sum over tokens [t_begin, t_end) of phi(K_t) [V_t, 1]^T.
 // PF chunks are kept in flight: the loop is unrolled by PF so that chunk i
 // always lives in buffer i % PF (a register copy between buffers would force
 // a wait on the loads in flight).
 // PHI: apply the feature map to K (otherwise K holds the features already).
-template <typename T, int D, int M, int PF, bool PHI = true>
+template <typename T, int D, int M, int PF, bool PHI = true, bool F32_LDS = false>
 __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *__restrict__ V, int64_t t_begin,
                                               int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
                                               lds_bf16 *stage_v) {
@@ -78,8 +91,8 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
             // the loads next to their use two chunks later
             __builtin_amdgcn_sched_barrier(0);
             Fr KT[TT][D / 16], VT[TT][M / 16];
-            transpose_frags<D / 16, TT>(KT, Kn, stage_k);
-            transpose_frags<M / 16, TT>(VT, Vn, stage_v);
+            tokens_major<D / 16, F32_LDS>(KT, Kn, stage_k);
+            tokens_major<M / 16, F32_LDS>(VT, Vn, stage_v);
             state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
     }
@@ -93,7 +106,7 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
 //   intra:    Ot[mt][it] += V^T[m][j] P^T[j][i], P^T[j][i] = phi(K_j).phi(Q_i), j <= i
 //   update:   St += phi(K)^T [V, 1]
 // The normalizer row block of Ot gets den_i in row 0.
-template <typename T, int D, int M, bool CAUSAL, int PF, bool PHI = true>
+template <typename T, int D, int M, bool CAUSAL, int PF, bool PHI = true, bool F32_LDS = false>
 __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__restrict__ K,
                                            const T *__restrict__ V, T *__restrict__ O, int64_t t_begin,
                                            int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
@@ -173,8 +186,8 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
                     PT[jt][it] = IO<T>::to_frag(p);
                 }
             Fr KT[TT][DT], VT[TT][MT];
-            transpose_frags<DT, TT>(KT, Kn, stage_k);
-            transpose_frags<MT, TT>(VT, Vn, stage_v);
+            tokens_major<DT, F32_LDS>(KT, Kn, stage_k);
+            tokens_major<MT, F32_LDS>(VT, Vn, stage_v);
             // intra-chunk term; the ones block sums P^T into den (every row)
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt)
@@ -663,10 +676,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     lds_bf16 *stage_q = (lds_bf16 *)(lds_stage + wave * SW);
     lds_bf16 *stage_k = stage_q + SK;
     lds_bf16 *stage_v = stage_k + SK;
+    // fp32 I/O: the same area holds the K tile from stage_q on, then the V tile
+    constexpr int F32K = 2 * f32_stage_floats<D / 16, TT>(), F32V = 2 * f32_stage_floats<M / 16, TT>();
+    static_assert(F32K + F32V <= SW, "fp32 tiles fit the wavefront's staging area");
+    lds_bf16 *stage_f32v = stage_q + F32K;
     if constexpr (sizeof(T) == 2)
         seg_aggregate_bf16<D, M, kPrefetch, PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
     else
-        seg_aggregate<T, D, M, fwd_prefetch<T, D, M>(), PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
+        seg_aggregate<T, D, M, fwd_prefetch<T, D, M>(), PHI, true>(K, V, t_begin, t_end, St, stage_q, stage_f32v);
     __syncthreads();   // every wavefront is done with its staging area
     state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
@@ -828,8 +845,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         seg_output_bf16<D, M, CAUSAL, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q,
                                                       stage_k, stage_v, stage_v + SV, ahead);
     else
-        seg_output<T, D, M, CAUSAL, fwd_prefetch<T, D, M>(), PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St,
-                                                                  stage_k, stage_v);
+        seg_output<T, D, M, CAUSAL, fwd_prefetch<T, D, M>(), PHI, true>(Q, K, V, out + bh * N * M, t_begin, t_end,
+                                                                        St, stage_q, stage_f32v);
 }
 
 // ---- host side ---------------------------------------------------------------
