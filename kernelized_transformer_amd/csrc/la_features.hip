@@ -17,6 +17,7 @@
 // rounded once to the I/O type.
 #include "la_chunk.h"
 #include "la_internal.h"
+#include "la_split.h"
 
 namespace la {
 
@@ -61,25 +62,47 @@ __global__ __launch_bounds__(64 * kFeatWavesPerBlock) void k_rff_features(const 
 
     __shared__ bf16 tiles[kFeatWavesPerBlock][16 * (R + kStagePad)];
     lds_bf16 *otile = (lds_bf16 *)tiles[wave];
+    // bf16 rows arrive as 16-byte pieces of whole rows (1 KB per load
+    // instruction) and are staged here, from which the fragments are read
+    __shared__ bf16 xstage[kFeatWavesPerBlock][16 * (D + kStagePad)];
+    lds_bf16 *xtile = (lds_bf16 *)xstage[wave];
 
     // rows past the end read a valid row and are not stored; kFeatAhead tiles
     // of rows are in flight (tile i lives in slot i % kFeatAhead)
+    constexpr int NL = Lines<D, 1>::n;
     typename IO<T>::frag xr[kFeatAhead][DT];
+    dwordx4 xl[kFeatAhead][NL];
+    const bf16 *xw = reinterpret_cast<const bf16 *>(x) + r0 * D;   // bf16: this wavefront's first row
+    const int nrows = int(r_end - r0);
 #pragma unroll
-    for (int a = 0; a < kFeatAhead; ++a)
+    for (int a = 0; a < kFeatAhead; ++a) {
+        if constexpr (sizeof(T) == 2) {
+            load_rows32<D>(xl[a], xw, 16 * a, nrows);
+        } else {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            xr[a][dt] = load4<T>(x + min(r0 + 16 * a + c, r_end - 1) * D + 16 * dt + 4 * g);
+            for (int dt = 0; dt < DT; ++dt)
+                xr[a][dt] = load4<T>(x + min(r0 + 16 * a + c, r_end - 1) * D + 16 * dt + 4 * g);
+        }
+    }
     for (int64_t t00 = r0; t00 < r_end; t00 += 16 * kFeatAhead) {
 #pragma unroll
     for (int a = 0; a < kFeatAhead; ++a) {
         const int64_t t0 = t00 + 16 * a;   // may lie past r_end: computed, not stored
         typename IO<T>::frag xf[DT];
+        if constexpr (sizeof(T) == 2) {
+            stage_lines<D, 1, false, false>(xtile, xl[a], 0, 16);
+            bf16x4 xn[1][DT];
+            natural_frags_lds<D, 1>(xn, xtile);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) xf[dt] = xr[a][dt];
-        const int64_t tn = min(t0 + 16 * kFeatAhead + c, r_end - 1);
+            for (int dt = 0; dt < DT; ++dt) xf[dt] = xn[0][dt];
+            load_rows32<D>(xl[a], xw, int(t0 - r0) + 16 * kFeatAhead, nrows);
+        } else {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) xr[a][dt] = load4<T>(x + tn * D + 16 * dt + 4 * g);
+            for (int dt = 0; dt < DT; ++dt) xf[dt] = xr[a][dt];
+            const int64_t tn = min(t0 + 16 * kFeatAhead + c, r_end - 1);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) xr[a][dt] = load4<T>(x + tn * D + 16 * dt + 4 * g);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
