@@ -489,6 +489,10 @@ constexpr int kScanG = 8;
 constexpr int kScanCols = 32;
 constexpr int kScanRows = int(kMaxSegPerHead / kScanG);
 
+// ROWS >= the rows of a group (per = ceil(nseg / kScanG)); the host picks the
+// smallest power of two, so no thread issues loads for rows it does not have
+// and the register count follows the segment count.
+template <int ROWS>
 __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int64_t nseg, int64_t rec, int mode,
                                                     const float *__restrict__ init, float *__restrict__ fin) {
     // mode 0: exclusive prefix in place; 1: total into record 0 (non-causal);
@@ -501,20 +505,25 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int6
     const int64_t c4 = (blockIdx.x % nblk_c) * kScanCols + cl;
     const bool ok = c4 < rec4;
     const bool rev = mode == 2;
-    const int64_t per = (nseg + kScanG - 1) / kScanG;
-    const int64_t s0 = grp * per;   // position in scan order
+    const int per = int((nseg + kScanG - 1) / kScanG);
+    const int s0 = grp * per;                        // position in scan order
+    const int nrow = max(0, min(per, int(nseg) - s0));   // rows this group has
     f32x4 *base = reinterpret_cast<f32x4 *>(ws + bh * nseg * rec) + (ok ? c4 : 0);
+    // row j of the group is record (rev ? nseg - 1 - (s0 + j) : s0 + j): a
+    // fixed step of +-rec4 float4s from the group's first record (a group
+    // without rows, s0 >= nseg, points at the last valid one and stores nothing)
+    const int sc = min(s0, int(nseg) - 1);
+    f32x4 *first = base + (rev ? nseg - 1 - sc : sc) * rec4;
+    const int64_t step = rev ? -rec4 : rec4;
 
-    f32x4 x[kScanRows];
+    f32x4 x[ROWS];
 #pragma unroll
-    for (int j = 0; j < kScanRows; ++j) {
-        const int64_t s = min(s0 + j, nseg - 1);
-        x[j] = base[(rev ? nseg - 1 - s : s) * rec4];
-    }
+    for (int j = 0; j < ROWS; ++j)   // all loads in flight first; rows past the group's end read its last row
+        x[j] = first[int64_t(min(j, max(nrow - 1, 0))) * step];
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kScanRows; ++j) {
-        if (!(j < per && s0 + j < nseg)) x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < ROWS; ++j) {
+        if (j >= nrow) x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         sum += x[j];
     }
     part[grp][cl] = sum;
@@ -528,10 +537,9 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int6
     if (!ok) return;
     if (mode != 1) {
 #pragma unroll
-        for (int j = 0; j < kScanRows; ++j) {
-            const int64_t s = s0 + j;
-            if (j < per && s < nseg) {
-                base[(rev ? nseg - 1 - s : s) * rec4] = run;
+        for (int j = 0; j < ROWS; ++j) {
+            if (j < nrow) {
+                first[int64_t(j) * step] = run;
                 run += x[j];
             }
         }
@@ -545,7 +553,14 @@ hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mod
                        hipStream_t s) {
     if (rec % 4 != 0 || nseg > kMaxSegPerHead) return hipErrorInvalidValue;
     const int64_t nblk = BH * ((rec / 4 + kScanCols - 1) / kScanCols);
-    hipLaunchKernelGGL(k_state_scan, dim3(unsigned(nblk)), dim3(256), 0, s, ws, nseg, rec, mode, init, fin);
+    const int64_t per = (nseg + kScanG - 1) / kScanG;
+    const dim3 grid{unsigned(nblk)}, block{256};
+    if (per <= 1) hipLaunchKernelGGL(k_state_scan<1>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
+    else if (per <= 2) hipLaunchKernelGGL(k_state_scan<2>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
+    else if (per <= 4) hipLaunchKernelGGL(k_state_scan<4>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
+    else if (per <= 8) hipLaunchKernelGGL(k_state_scan<8>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
+    else if (per <= 16) hipLaunchKernelGGL(k_state_scan<16>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
+    else hipLaunchKernelGGL(k_state_scan<kScanRows>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
     return hipGetLastError();
 }
 
