@@ -387,6 +387,10 @@ RFF_CASES = [
     ("d32_r64_f32_ragged", _wl(211, 2, 3, 100, 32, 32, "f32"), 64),
     ("d64_r32_bf16_ragged", _wl(212, 1, 3, 1001, 64, 64, "bf16"), 32),
     ("w4_full_r64", wl.WORKLOADS[4], 64),
+    # bf16 rows staged through LDS: D = 32 rows (one 16-byte piece per lane), fewer
+    # rows than one 16-row tile, and a last wavefront with a partial tile
+    ("d32_r64_bf16_ragged", _wl(214, 2, 2, 777, 32, 32, "bf16"), 64),
+    ("d32_r32_bf16_5_rows", _wl(215, 1, 1, 5, 32, 32, "bf16"), 32),
 ]
 
 
