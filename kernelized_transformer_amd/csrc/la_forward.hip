@@ -818,16 +818,25 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
             // the totals of blocks 0 .. sb - 1 (non-causal: all nb), summed in block order
             const int nsum = CAUSAL ? sb : nb;
             const f32x4 *tot0 = reinterpret_cast<const f32x4 *>(head_recs);
+            // in batches of 4 totals, all loads of a batch in flight first; the
+            // second batch only for blocks with more than 4 predecessors (uniform)
+            static_assert(kFusedDirectBlocks % 4 == 0, "batches of 4 totals");
 #pragma unroll
-            for (int j = 0; j < NJ4; ++j) {
-                f32x4 x[kFusedDirectBlocks];
+            for (int r0 = 0; r0 < kFusedDirectBlocks; r0 += 4) {
+                if (r0 > 0 && nsum <= r0) break;
 #pragma unroll
-                for (int r = 0; r < kFusedDirectBlocks; ++r)   // all loads in flight first
-                    x[r] = (r < nsum && tid + NT * j < REC4) ? dev_load(tot0 + int64_t(r) * 2 * REC4 + tid + NT * j)
-                                                             : f32x4{0.f, 0.f, 0.f, 0.f};
-                buf[j] = x[0];
+                for (int j = 0; j < NJ4; ++j) {
+                    f32x4 x[4];
 #pragma unroll
-                for (int r = 1; r < kFusedDirectBlocks; ++r) buf[j] += x[r];
+                    for (int r = 0; r < 4; ++r)
+                        x[r] = (r0 + r < nsum && tid + NT * j < REC4)
+                                   ? dev_load(tot0 + int64_t(r0 + r) * 2 * REC4 + tid + NT * j)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (r0 == 0) buf[j] = x[0];
+                    else buf[j] += x[0];
+#pragma unroll
+                    for (int r = 1; r < 4; ++r) buf[j] += x[r];
+                }
             }
         } else {
 #pragma unroll

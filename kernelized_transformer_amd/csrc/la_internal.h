@@ -52,7 +52,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kFusedWaves = 8;
 constexpr int64_t kMaxBlkPerHead = 64;   // flags of a head fit one wavefront
 constexpr int64_t kTargetWaves = 2048;   // two wavefronts per SIMD of the 256 CUs
-constexpr int kFusedDirectBlocks = 4;    // up to this many blocks per head: one exchange, no slices
+constexpr int kFusedDirectBlocks = 8;    // up to this many blocks per head: one exchange, no slices
 
 struct FusedPlan {
     int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
@@ -74,6 +74,13 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     if (cpw < min_cpw) cpw = min_cpw;
     p.sub_tokens = cpw * kChunk;
     p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
+    // a short problem that leaves most CUs idle anyway: up to twice the chunks
+    // per wavefront if that brings a head within the single-exchange hand-off
+    if (p.nblk > kFusedDirectBlocks && p.nblk <= 2 * kFusedDirectBlocks && BH * p.nblk <= 128) {
+        cpw = ceil_div(nch, kFusedWaves * kFusedDirectBlocks);
+        p.sub_tokens = cpw * kChunk;
+        p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
+    }
     p.rec = D * M + D;
     p.flags_off = 256;
     p.recs_off = p.flags_off + align256(size_t(2 * BH * p.nblk) * sizeof(unsigned long long));

@@ -60,8 +60,9 @@ def test_forward_causal(name, w):
 
 # Plans of the single-launch causal forward (workgroups per (b, h), nb) that
 # exercise its cross-workgroup hand-off: nb = 1 (no hand-off, more workgroups
-# than CUs), 2, 3 (ragged last workgroup), 36, 63 (fp32, D = M = 64) and 64
-# (the largest; some workgroups own an empty slice of the state record).
+# than CUs), 2, 3 (ragged last workgroup), 7 and 8 (the single exchange at its
+# largest), 36, 63 (fp32, D = M = 64) and 64 (the largest; some workgroups own
+# an empty slice of the state record).
 PLAN_CASES = [
     ("nb64_empty_slices", _wl(181, 1, 1, 262144, 64, 64, "bf16"), 64),
     ("nb63_f32_d64m64", _wl(182, 1, 2, 40000, 64, 64, "f32"), 63),
@@ -69,14 +70,22 @@ PLAN_CASES = [
     ("nb3_ragged_96_heads", _wl(184, 6, 16, 3000, 32, 32, "bf16"), 3),
     ("nb1_1024_heads", _wl(185, 64, 16, 512, 32, 64, "bf16"), 1),
     ("nb36_d32m64", _wl(186, 1, 3, 9000, 32, 64, "bf16"), 36),
+    # single-exchange hand-off at its largest: 16 workgroups per head halved to 8
+    # (a short problem), and 7 with a ragged last workgroup
+    ("nb8_halved_b1h8", _wl(187, 1, 8, 2048, 64, 64, "bf16"), 8),
+    ("nb7_direct_ragged", _wl(188, 4, 8, 1700, 64, 64, "bf16"), 7),
 ]
 
 
-def _fused_nb(BH, N, chunk=16, waves=8, target_waves=2048, max_blk=64):
+def _fused_nb(BH, N, chunk=16, waves=8, target_waves=2048, max_blk=64, direct=8):
     """Workgroups per (b, h) the library plans for the causal forward."""
     nch = -(-N // chunk)
     cpw = max(1, -(-BH * nch // target_waves), -(-nch // (waves * max_blk)))
-    return -(-N // (waves * cpw * chunk))
+    nb = -(-N // (waves * cpw * chunk))
+    if direct < nb <= 2 * direct and BH * nb <= 128:
+        cpw = -(-nch // (waves * direct))
+        nb = -(-N // (waves * cpw * chunk))
+    return nb
 
 
 @pytest.mark.parametrize("name,w,nb", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
