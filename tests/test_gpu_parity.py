@@ -487,6 +487,71 @@ def test_forward_causal_longest_sequence():
     check("Z_N", host(Z), Z_ref, w.dtype)
 
 
+def test_backward_longest_head_identities():
+    """The causal backward on one head of the longest length its two-wavefront
+    kernels take (N * 64 < 2^31 elements: byte offsets into the head pass 2^31),
+    checked through identities that hold at any length (the oracle would need
+    hours): out_i is 0-homogeneous in phi(q_i) and in all phi(k) together, so
+    s_i = sum_d dQ_id (1 + max(Q_id, 0)) = 0 for every token and the same sum over
+    dK is 0 for the head; out is an average of the V rows, so sum_j dV_j =
+    sum_i G_i and sum_j V_j . dV_j = sum_i G_i . out_i.  Each bound is 2^-5 of the
+    summed magnitudes of the terms: eight bf16 roundings, since several roundings
+    act systematically here (the reverse state, rounded to bf16 once per chunk,
+    changes slowly along the sequence, so its rounding error repeats over many
+    tokens); random rows of the right scale exceed it about fourfold.  The dQ
+    identity is checked per block of 4096 tokens (sum of |s_i| against the summed
+    magnitudes): a single token's s_i is a rounding residue of two cancelling terms
+    (token 1's whole dQ is one), but any block of wrong rows breaks it.  Every
+    output starts as NaN, so rows a kernel failed to write cannot pass as zeros.
+    Inputs are seeded N(0, 1) draws made on the device."""
+    N = (2 ** 31 - 1) // 64
+    _say(f"longest backward head: B1 H1 N{N} D=M=64 bf16")
+    gen = torch.Generator(device="cuda").manual_seed(241)
+
+    def draw():
+        return torch.randn((1, 1, N, 64), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    q, k, v, g = draw(), draw(), draw(), draw()
+    dq, dk, dv, out = (torch.full_like(q, float("nan")) for _ in range(4))
+    la.la_backward_causal(q, k, v, g, dq=dq, dk=dk, dv=dv)
+    la.la_forward_causal(q, k, v, out=out)
+    torch.cuda.synchronize()
+    for name, x in (("dQ", dq), ("dK", dk), ("dV", dv), ("out", out)):
+        assert bool(torch.isfinite(x).all()), f"{name}: rows left unwritten or non-finite"
+    tol = 2.0 ** -5
+    sum_dv = torch.zeros(64, dtype=torch.float64, device="cuda")
+    abs_dv = torch.zeros(64, dtype=torch.float64, device="cuda")
+    sum_g = torch.zeros(64, dtype=torch.float64, device="cuda")
+    vdv = gout = abs_vdv = abs_gout = dkr = abs_dkr = 0.0
+    worst_q = 0.0
+    step = 1 << 22
+    for t0 in range(0, N, step):
+        sl = slice(t0, min(N, t0 + step))
+        f = lambda x: x[0, 0, sl].double()
+        Q, K, V, G, DQ, DK, DV, O = (f(x) for x in (q, k, v, g, dq, dk, dv, out))
+        tq = DQ * (1 + Q.clamp(min=0))
+        si, ai = tq.sum(1).abs(), tq.abs().sum(1)
+        nb = (si.numel() + 4095) // 4096
+        pad = nb * 4096 - si.numel()
+        si = torch.nn.functional.pad(si, (0, pad)).view(nb, 4096).sum(1)
+        ai = torch.nn.functional.pad(ai, (0, pad)).view(nb, 4096).sum(1)
+        worst_q = max(worst_q, float((si / (tol * ai + 1e-30)).max()))
+        tk = DK * (1 + K.clamp(min=0))
+        dkr += float(tk.sum()); abs_dkr += float(tk.abs().sum())
+        sum_dv += DV.sum(0); abs_dv += DV.abs().sum(0); sum_g += G.sum(0)
+        vdv += float((V * DV).sum()); abs_vdv += float((V * DV).abs().sum())
+        gout += float((G * O).sum()); abs_gout += float((G * O).abs().sum())
+    print(f"  dQ identity per 4096 tokens: worst sum |s_i| / bound {worst_q:.3f}", flush=True)
+    assert worst_q <= 1.0
+    print(f"  dK identity: |sum| / bound {abs(dkr) / (tol * abs_dkr):.3e}", flush=True)
+    assert abs(dkr) <= tol * abs_dkr
+    ratio = (sum_dv - sum_g).abs() / (tol * abs_dv)
+    print(f"  sum dV - sum G per column: worst |difference| / bound {float(ratio.max()):.3f}", flush=True)
+    assert float(ratio.max()) <= 1.0
+    print(f"  V.dV - G.out: |difference| / bound {abs(vdv - gout) / (tol * (abs_vdv + abs_gout)):.3e}", flush=True)
+    assert abs(vdv - gout) <= tol * (abs_vdv + abs_gout)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_forward_causal_closed_forms(dtype):
     """Constant V gives V back; identical keys give the running mean of V
