@@ -487,8 +487,9 @@ def test_forward_causal_longest_sequence():
     check("Z_N", host(Z), Z_ref, w.dtype)
 
 
-def test_backward_longest_head_identities():
-    """The causal backward on one head of the longest length its two-wavefront
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_backward_longest_head_identities(causal):
+    """The backward on one head of the longest length its two-wavefront
     kernels take (N * 64 < 2^31 elements: byte offsets into the head pass 2^31),
     checked through identities that hold at any length (the oracle would need
     hours): out_i is 0-homogeneous in phi(q_i) and in all phi(k) together, so
@@ -503,9 +504,14 @@ def test_backward_longest_head_identities():
     magnitudes): a single token's s_i is a rounding residue of two cancelling terms
     (token 1's whole dQ is one), but any block of wrong rows breaks it.  Every
     output starts as NaN, so rows a kernel failed to write cannot pass as zeros.
-    Inputs are seeded N(0, 1) draws made on the device."""
+    Inputs are seeded N(0, 1) draws made on the device.  The non-causal form
+    satisfies the same identities with every sum over the whole sequence, but
+    there every token's dV is read from one reverse state rounded to bf16 once,
+    and each column's dV keeps one sign along the sequence, so the sum over
+    tokens keeps that rounding undiluted (3-5% of sum |dV| at every length from
+    2^20 tokens up, measured): the sum of dV is checked for the causal form only."""
     N = (2 ** 31 - 1) // 64
-    _say(f"longest backward head: B1 H1 N{N} D=M=64 bf16")
+    _say(f"longest backward head ({'causal' if causal else 'non-causal'}): B1 H1 N{N} D=M=64 bf16")
     gen = torch.Generator(device="cuda").manual_seed(241)
 
     def draw():
@@ -513,8 +519,8 @@ def test_backward_longest_head_identities():
 
     q, k, v, g = draw(), draw(), draw(), draw()
     dq, dk, dv, out = (torch.full_like(q, float("nan")) for _ in range(4))
-    la.la_backward_causal(q, k, v, g, dq=dq, dk=dk, dv=dv)
-    la.la_forward_causal(q, k, v, out=out)
+    (la.la_backward_causal if causal else la.la_backward_noncausal)(q, k, v, g, dq=dq, dk=dk, dv=dv)
+    (la.la_forward_causal if causal else la.la_forward_noncausal)(q, k, v, out=out)
     torch.cuda.synchronize()
     for name, x in (("dQ", dq), ("dK", dk), ("dV", dv), ("out", out)):
         assert bool(torch.isfinite(x).all()), f"{name}: rows left unwritten or non-finite"
@@ -547,7 +553,8 @@ def test_backward_longest_head_identities():
     assert abs(dkr) <= tol * abs_dkr
     ratio = (sum_dv - sum_g).abs() / (tol * abs_dv)
     print(f"  sum dV - sum G per column: worst |difference| / bound {float(ratio.max()):.3f}", flush=True)
-    assert float(ratio.max()) <= 1.0
+    if causal:
+        assert float(ratio.max()) <= 1.0
     print(f"  V.dV - G.out: |difference| / bound {abs(vdv - gout) / (tol * (abs_vdv + abs_gout)):.3e}", flush=True)
     assert abs(vdv - gout) <= tol * (abs_vdv + abs_gout)
 
