@@ -400,6 +400,7 @@ RFF_CASES = [
     # rows than one 16-row tile, and a last wavefront with a partial tile
     ("d32_r64_bf16_ragged", _wl(214, 2, 2, 777, 32, 32, "bf16"), 64),
     ("d32_r32_bf16_5_rows", _wl(215, 1, 1, 5, 32, 32, "bf16"), 32),
+    ("d64_r64_f32_ragged", _wl(216, 1, 2, 333, 64, 64, "f32"), 64),
 ]
 
 
