@@ -433,7 +433,10 @@ __device__ __forceinline__ void seg_output_bf16(const bf16 *__restrict__ Q, cons
 // sums the w-th run of whole chunks, then the partial states are added
 // through LDS in wavefront order (a fixed order: results do not vary from
 // run to run), so that two wavefronts per SIMD keep K and V streaming.
+// The kernel holds no output tiles, so bf16 chunks are loaded four ahead of
+// the one being summed (two ahead in the forward's passes).
 constexpr int kSegWaves = 2;
+constexpr int kSegPrefetch = 4;
 template <typename T, int D, int M>
 __global__ __launch_bounds__(64 * kSegWaves) void k_segment_state(const T *__restrict__ k, const T *__restrict__ v,
                                                                   float *__restrict__ ws, int64_t N, int64_t nseg,
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(64 * kSegWaves) void k_segment_state(const T *__res
     state_zero<D, M>(St);
     if (t_begin < t_end) {   // uniform; a short segment can leave wavefront 1 without chunks
         if constexpr (sizeof(T) == 2)
-            seg_aggregate_bf16<D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
+            seg_aggregate_bf16<D, M, kSegPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
         else
             seg_aggregate<T, D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
     }
