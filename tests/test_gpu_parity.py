@@ -74,6 +74,7 @@ PLAN_CASES = [
     # (a short problem), and 7 with a ragged last workgroup
     ("nb8_halved_b1h8", _wl(187, 1, 8, 2048, 64, 64, "bf16"), 8),
     ("nb7_direct_ragged", _wl(188, 4, 8, 1700, 64, 64, "bf16"), 7),
+    ("nb6_halved_f32_d32m64_ragged", _wl(189, 1, 4, 1500, 32, 64, "f32"), 6),
 ]
 
 
