@@ -29,12 +29,33 @@
  *     Workspace contents need no initialization and are clobbered.
  *   - Argument errors are reported before anything is launched and leave all
  *     buffers untouched.  LA_ERR_HIP reports a failed launch.  Non-finite
- *     inputs are not errors; they propagate to the outputs.
+ *     inputs are not errors; they propagate to every output that depends on
+ *     them.  The matrix products also carry them a little further, since
+ *     0 * NaN = NaN: a non-finite key or value (or, in the backward, output
+ *     gradient) can reach outputs of the other tokens of its 16-token chunk
+ *     that do not depend on it; outputs outside that chunk that do not
+ *     depend on it are unaffected (bit-identical).
  *   - The library keeps no global state beyond a process-wide call counter
- *     (it tags the causal forward's cross-workgroup flags, so the workspace
- *     needs no clearing between calls); calls on different streams are
- *     independent as long as their buffers (workspace included) are
+ *     (it tags the forwards' cross-workgroup flags, so the workspace needs
+ *     no clearing between calls), the wait limit of la_set_wait_limit and a
+ *     per-device cache of the compute-unit count; calls on different streams
+ *     are independent as long as their buffers (workspace included) are
  *     disjoint.
+ *   - The forwards (la_forward_causal, _state, _features, _noncausal) may be
+ *     captured into a HIP graph: a captured call records a small kernel that
+ *     clears its hand-off flags before the forward itself, so every replay
+ *     is correct even with changed inputs.
+ *
+ * Co-residency contract of the forwards.  Each (b, h) is split into blocks
+ * of 8 wavefronts that exchange fp32 state through the workspace and wait for
+ * each other with bounded waits.  The plan gives a head at most
+ * min(64, number of CUs of the current device) blocks (one CU holds a block,
+ * and blocks are dispatched in index order, so every block of a head can be
+ * resident once the heads before it are done); the CU count is read from the
+ * device that is current when the call is made.  Only other work that keeps
+ * most CUs busy for the whole length of a wait (about a second) can make a
+ * wait give up; the call then still returns LA_OK but its output is wrong,
+ * and la_workspace_check reports LA_ERR_TIMEOUT.
  */
 #ifndef LA_H
 #define LA_H
@@ -48,19 +69,30 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 5
+#define LA_ABI_VERSION 6
 
-typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+/* The enums are int-sized in C; C++ gets the same fixed underlying type, so
+ * any int a C caller passes (an unknown dtype, op or status included) is a
+ * valid value to validate rather than undefined behaviour. */
+#ifdef __cplusplus
+#define LA_ENUM_BASE : int
+#else
+#define LA_ENUM_BASE
+#endif
 
-typedef enum {
+typedef enum la_dtype_e LA_ENUM_BASE { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+
+typedef enum la_status_e LA_ENUM_BASE {
     LA_OK = 0,
     LA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, overlap */
-    LA_ERR_UNSUPPORTED = 2,      /* D or M outside the supported set, unknown dtype */
+    LA_ERR_UNSUPPORTED = 2,      /* D or M outside the supported set, unknown dtype,
+                                    or a shape beyond the kernels' plan limits */
     LA_ERR_WORKSPACE = 3,        /* workspace missing, misaligned or too small */
-    LA_ERR_HIP = 4               /* a kernel launch failed */
+    LA_ERR_HIP = 4,              /* a kernel launch (or a copy) failed */
+    LA_ERR_TIMEOUT = 5           /* la_workspace_check: a hand-off wait gave up */
 } la_status_t;
 
-typedef enum {
+typedef enum la_op_e LA_ENUM_BASE {
     LA_OP_FWD_CAUSAL = 0,     /* la_forward_causal, la_forward_causal_state,
                                  la_forward_causal_features (with D = F) */
     LA_OP_FWD_NONCAUSAL = 1,  /* la_forward_noncausal */
@@ -78,12 +110,10 @@ typedef enum {
  * q, k: [B][H][N][D]; v: [B][H][N][M] (inputs, read only).
  * out: [B][H][N][M] (output, fully written).
  * The workgroups of one (b, h) exchange state through the workspace and
- * wait for each other (each wait is bounded), so they must be able to run
- * at the same time: at most 64 workgroups per (b, h), about 256 in all.
- * Diagnostic: if a wait ever timed out (only possible when other work keeps
- * most of the GPU busy), the call or-s 1 into the 32-bit word at byte 4 of
- * the workspace and its output is wrong; the library never clears that
- * word, so a caller who wants the diagnostic zeroes it first.
+ * wait for each other (see the co-residency contract above).  Diagnostic:
+ * if a wait ever gave up, the call or-s 1 into the 32-bit error word at
+ * byte 4 of the workspace and its output is wrong; the library never clears
+ * that word by itself: la_workspace_check reads (and optionally clears) it.
  */
 la_status_t la_forward_causal(const void *q, const void *k, const void *v, void *out,
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
@@ -233,7 +263,31 @@ la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S
                            void *out, int64_t B, int64_t H, int64_t D, int64_t M,
                            la_dtype_t dt, hipStream_t stream);
 
-/* Bytes of workspace `op` needs for this shape (0 if the shape is invalid). */
+/*
+ * Reads the error word of a forward's workspace (see the co-residency
+ * contract): waits for the work queued on `stream` (this call synchronizes,
+ * unlike the others), returns LA_ERR_TIMEOUT if a hand-off wait of a call
+ * that used this workspace gave up since the word was last cleared, LA_OK
+ * otherwise; with `clear` != 0 it then zeroes the word.  A new workspace's
+ * word holds whatever the memory held: clear it once (clear = 1, ignoring
+ * the result) before relying on the report.  workspace: device memory of at
+ * least 256 bytes, 256-byte aligned (else LA_ERR_WORKSPACE); LA_ERR_HIP if
+ * the copy or the synchronization failed.
+ */
+la_status_t la_workspace_check(void *workspace, size_t workspace_bytes, int clear, hipStream_t stream);
+
+/*
+ * Process-wide limit on the polls one hand-off wait of the forwards makes
+ * before it gives up (default 2^20, about a second; a negative value
+ * restores the default); returns the previous limit.  A debugging and
+ * testing aid: with 0 every wait that has anything to wait for gives up at
+ * once, which lets a test see a give-up reported by la_workspace_check while
+ * every kernel still exits normally.  Takes effect for calls made after it.
+ */
+int64_t la_set_wait_limit(int64_t polls);
+
+/* Bytes of workspace `op` needs for this shape (0 if the shape is invalid).
+ * The forwards' plan depends on the current device's CU count. */
 size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                          la_dtype_t dt);
 

@@ -18,7 +18,15 @@ Functions carry the C names:
   la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_decode_step(q, k, v, S, Z, out=None)
   la_workspace_size(op, B, H, N, D, M, dtype)
+  la_workspace_check(workspace, clear=False)
+  la_set_wait_limit(polls)
   la_status_string(status), la_abi_version()
+
+With the environment variable LA_CHECK_WAITS=1 (the test suite sets it) every
+forward call made through this module clears its workspace's error word first
+and checks it afterwards (la_workspace_check, which synchronizes the stream),
+raising LAError(LA_ERR_TIMEOUT) if a cross-workgroup wait gave up; calls being
+captured into a graph are not checked.
 """
 from __future__ import annotations
 
@@ -30,13 +38,17 @@ import torch
 __all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
            "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
            "la_decode_step",
-           "la_workspace_size", "la_status_string", "la_abi_version", "LAError", "lib_path", "load",
+           "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
+           "LAError", "lib_path", "load", "LA_ERR_TIMEOUT",
            "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL",
            "LA_OP_FWD_CAUSAL_POLY2", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL, LA_OP_FWD_CAUSAL_POLY2 = 0, 1, 2, 3, 4
 _DT = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
+
+LA_ERR_TIMEOUT = 5
+CHECK_WAITS = os.environ.get("LA_CHECK_WAITS", "0") not in ("", "0")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libla.so")
@@ -79,6 +91,10 @@ def load():
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_abi_version.argtypes = []
     lib.la_abi_version.restype = i32
+    lib.la_workspace_check.argtypes = [vp, sz, i32, vp]
+    lib.la_workspace_check.restype = i32
+    lib.la_set_wait_limit.argtypes = [i64]
+    lib.la_set_wait_limit.restype = i64
     _lib = lib
     return lib
 
@@ -94,6 +110,37 @@ def la_abi_version() -> int:
 def la_workspace_size(op: int, B: int, H: int, N: int, D: int, M: int, dtype) -> int:
     dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(load().la_workspace_size(int(op), B, H, N, D, M, dt))
+
+
+def la_workspace_check(workspace: torch.Tensor, clear: bool = False) -> int:
+    """Status of a forward workspace's error word (0 = LA_OK, 5 = LA_ERR_TIMEOUT);
+    synchronizes the current stream; ``clear`` zeroes the word afterwards."""
+    st = load().la_workspace_check(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   1 if clear else 0, _stream(workspace.device))
+    if st not in (0, LA_ERR_TIMEOUT):
+        raise LAError("la_workspace_check", st)
+    return int(st)
+
+
+def la_set_wait_limit(polls: int) -> int:
+    """Polls a forward's hand-off wait makes before giving up (process-wide;
+    negative restores the default); returns the previous limit."""
+    return int(load().la_set_wait_limit(int(polls)))
+
+
+def _checking(dev) -> bool:
+    return CHECK_WAITS and not torch.cuda.is_current_stream_capturing()
+
+
+def _checked_call(func: str, call, ws):
+    """Runs a forward call; in LA_CHECK_WAITS mode its error word is cleared
+    before and checked after."""
+    check = _checking(ws.device)
+    if check:
+        la_workspace_check(ws, clear=True)
+    _check(func, call())
+    if check and la_workspace_check(ws) != 0:
+        raise LAError(func, LA_ERR_TIMEOUT)
 
 
 def _dev(*ts: torch.Tensor):
@@ -132,9 +179,12 @@ def _forward(func: str, op: int, q, k, v, out, workspace):
         out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
     _dev(q, out)
     ws, wsb = _ws(op, B, H, N, D, M, q.dtype, workspace, dev)
-    st = getattr(load(), func)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
-                               _DT[q.dtype], ws.data_ptr(), wsb, _stream(dev))
-    _check(func, st)
+    if op == LA_OP_FWD_CAUSAL_POLY2:
+        _check(func, getattr(load(), func)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
+                                           _DT[q.dtype], ws.data_ptr(), wsb, _stream(dev)))
+        return out
+    _checked_call(func, lambda: getattr(load(), func)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H,
+                                                      N, D, M, _DT[q.dtype], ws.data_ptr(), wsb, _stream(dev)), ws)
     return out
 
 
@@ -169,12 +219,10 @@ def la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=Non
         out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
     _dev(q, out)
     ws, wsb = _ws(LA_OP_FWD_CAUSAL, B, H, N, D, M, q.dtype, workspace, dev)
-    st = load().la_forward_causal_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                        s0.data_ptr() if s0 is not None else None,
-                                        z0.data_ptr() if z0 is not None else None, s_final.data_ptr(),
-                                        z_final.data_ptr(), B, H, N, D, M, _DT[q.dtype], ws.data_ptr(), wsb,
-                                        _stream(dev))
-    _check("la_forward_causal_state", st)
+    _checked_call("la_forward_causal_state", lambda: load().la_forward_causal_state(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), s0.data_ptr() if s0 is not None else None,
+        z0.data_ptr() if z0 is not None else None, s_final.data_ptr(), z_final.data_ptr(), B, H, N, D, M,
+        _DT[q.dtype], ws.data_ptr(), wsb, _stream(dev)), ws)
     return out, s_final, z_final
 
 

@@ -1,5 +1,6 @@
 // la_api.hip -- the C ABI declared in include/la.h: argument validation,
-// workspace sizing and dispatch to the kernel launchers.  Stateless.
+// workspace sizing, dispatch to the kernel launchers, and the forwards'
+// diagnostics (error word, wait limit).
 #include "la.h"
 #include "la_internal.h"
 
@@ -73,6 +74,7 @@ la_status_t forward_common(bool causal, const void *q, const void *k, const void
     const Span all[4] = {in[0], in[1], in[2], o[0]};
     const size_t need = la::causal_workspace_bytes(BH, N, D, M);   // the same plan for both forwards
     if ((st = check_workspace(workspace, workspace_bytes, need, all, 4)) != LA_OK) return st;
+    if (!la::forward_plan_supported(BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
     const hipError_t e = la::launch_forward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
                                             static_cast<float *>(workspace), stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
@@ -120,6 +122,7 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
     if ((st = check_workspace(workspace, workspace_bytes, la::causal_workspace_bytes(BH, N, D, M), all, nall)) !=
         LA_OK)
         return st;
+    if (!la::forward_plan_supported(BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
     la::StateIO sio;
     sio.s0 = s0;
     sio.z0 = z0;
@@ -144,6 +147,7 @@ la_status_t la_forward_causal_features(const void *fq, const void *fk, const voi
     const Span all[4] = {in[0], in[1], in[2], o[0]};
     if ((st = check_workspace(workspace, workspace_bytes, la::causal_workspace_bytes(BH, N, F, M), all, 4)) != LA_OK)
         return st;
+    if (!la::forward_plan_supported(BH, N, F, M, es)) return LA_ERR_UNSUPPORTED;
     la::StateIO sio;
     sio.features_given = true;
     const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, fq, fk, v, out, BH, N, F, M,
@@ -269,9 +273,25 @@ const char *la_status_string(la_status_t s) {
     case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
     case LA_ERR_HIP: return "LA_ERR_HIP";
+    case LA_ERR_TIMEOUT: return "LA_ERR_TIMEOUT";
     }
     return "LA_ERR_UNKNOWN";
 }
+
+la_status_t la_workspace_check(void *workspace, size_t workspace_bytes, int clear, hipStream_t stream) {
+    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < 256) return LA_ERR_WORKSPACE;
+    int word = 0;
+    int *err = static_cast<int *>(workspace) + 1;
+    if (hipMemcpyAsync(&word, err, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return LA_ERR_HIP;
+    if (clear) {
+        static const int zero = 0;
+        if (hipMemcpyAsync(err, &zero, sizeof(int), hipMemcpyHostToDevice, stream) != hipSuccess) return LA_ERR_HIP;
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess) return LA_ERR_HIP;
+    return word != 0 ? LA_ERR_TIMEOUT : LA_OK;
+}
+
+int64_t la_set_wait_limit(int64_t polls) { return la::set_wait_limit(polls); }
 
 int la_abi_version(void) { return LA_ABI_VERSION; }
 

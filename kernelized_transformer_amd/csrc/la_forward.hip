@@ -595,7 +595,6 @@ hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mod
 // the error word and carries on, so every wavefront always exits.  All blocks
 // of a head must be able to run at the same time (at most kMaxBlkPerHead
 // blocks of kFusedWaves wavefronts); the chip holds hundreds.
-constexpr int kSpinLimit = 1 << 20;
 constexpr int kWaitVmcnt0 = 0x0f70;   // s_waitcnt vmcnt(0), other counters untouched
 
 __device__ __forceinline__ void dev_store(f32x4 *p, f32x4 x) {
@@ -628,20 +627,32 @@ __device__ __forceinline__ void block_publish(unsigned long long *flag, unsigned
 }
 
 // Wavefront-wide wait until flags[0 .. count) all hold tag (count <= 64).
+// At most `limit` polls: a wait that gives up or-s 1 into *err (the results
+// are then wrong, and the error word says so) and lets the block carry on,
+// so every wavefront always exits; limit 0 gives up at once.
 __device__ __forceinline__ void wait_flags(const unsigned long long *flags, int count, unsigned long long tag,
-                                           int *err) {
+                                           int *err, int64_t limit) {
     const int lane = lane_id();
-    for (int iter = 0;; ++iter) {
-        const bool set = (lane >= count) ||
-                         __hip_atomic_load(&flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-        if (__ballot(!set) == 0) break;
-        if (iter >= kSpinLimit) {
-            if (lane == 0) atomicOr(err, 1);   // gave up: results are wrong, the error word says so
-            break;
+    if (count > 0) {
+        for (int64_t iter = 0;; ++iter) {
+            if (iter >= limit) {
+                if (lane == 0) atomicOr(err, 1);
+                break;
+            }
+            const bool set = (lane >= count) ||
+                             __hip_atomic_load(&flags[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+            if (__ballot(!set) == 0) break;
+            __builtin_amdgcn_s_sleep(2);
         }
-        __builtin_amdgcn_s_sleep(2);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // later loads stay below (compiler)
+}
+
+// Zeroes the hand-off flags of a call that is being captured into a graph:
+// its tag is fixed at capture, so the flags a replay waits for must not
+// still hold it from the replay before.  A kernel rather than a memset node.
+__global__ __launch_bounds__(256) void k_clear_flags(unsigned long long *__restrict__ flags, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) flags[i] = 0;
 }
 
 // PHI = false: q and k hold the features already (no feature map applied).
@@ -655,7 +666,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
                                                                 unsigned long long *__restrict__ flags,
                                                                 unsigned long long tag,
                                                                 float *__restrict__ recs, int64_t N, int64_t nblk,
-                                                                int64_t sub_tokens, StateIO sio) {
+                                                                int64_t sub_tokens, int64_t limit, StateIO sio) {
     constexpr int REC = D * M + D, REC4 = REC / 4;
     static_assert(REC % 4 == 0, "records move as f32x4");
     constexpr int NT = 64 * kFusedWaves;
@@ -758,7 +769,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     // exchange); otherwise the slices below form the prefixes (two exchanges,
     // but a block reads 3 records however many precede it).
     const bool direct = nb <= kFusedDirectBlocks;
-    if (wave == 0 && nb > 1) wait_flags(flag_tot, CAUSAL ? (direct ? sb : nb - 1) : nb, tag, &header[1]);
+    if (wave == 0 && nb > 1) wait_flags(flag_tot, CAUSAL ? (direct ? sb : nb - 1) : nb, tag, &header[1], limit);
     __syncthreads();
 
     if (nb > 1 && !direct) {
@@ -806,7 +817,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
             __syncthreads();
         }
         block_publish(&flag_pre[blk], tag);
-        if (wave == 0 && (sb > 0 || !CAUSAL)) wait_flags(flag_pre, nb, tag, &header[1]);
+        if (wave == 0 && (sb > 0 || !CAUSAL)) wait_flags(flag_pre, nb, tag, &header[1], limit);
         __syncthreads();
     }
     // 2c. P_s = initial state + the earlier blocks' totals into LDS; the last
@@ -888,31 +899,69 @@ uint64_t next_call_tag() {
     return z ? z : 1;
 }
 
+constexpr int64_t kDefaultWaitLimit = int64_t(1) << 20;   // about a second of polling
+static std::atomic<int64_t> g_wait_limit{kDefaultWaitLimit};
+int64_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+int64_t set_wait_limit(int64_t polls) {
+    return g_wait_limit.exchange(polls < 0 ? kDefaultWaitLimit : polls, std::memory_order_relaxed);
+}
+
+int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// A plan the fused kernel cannot run (too many record rows for one thread to
+// sum while forming a prefix slice, or a wavefront's rows past 32-bit byte
+// offsets) -- a limit of this implementation, checked before any launch.
+bool forward_plan_supported(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+    const FusedPlan p = make_fused_plan(BH, N, D, M);
+    for (int causal = 0; causal < 2; ++causal)
+        if (fused_slice_rows(p.nblk, causal ? p.nblk - 1 : p.nblk, (D * M + D) / 4, 64 * kFusedWaves) >
+            kFusedSliceRows)
+            return false;
+    // the bf16 chunk loops address a wavefront's rows by 32-bit byte offsets
+    // (far from binding: a wavefront's share of any problem that fits in memory
+    // spans well under 1 GB)
+    return (p.sub_tokens + 2 * kChunk) * std::max(D, M) * int64_t(esize) <= int64_t(UINT32_MAX);
+}
+
 template <typename T, int D, int M>
 static hipError_t run_forward(bool causal, const void *q, const void *k, const void *v, void *out, int64_t BH,
                               int64_t N, float *ws, StateIO sio, hipStream_t s) {
     const FusedPlan p = make_fused_plan(BH, N, D, M);
-    if (fused_slice_rows(p.nblk, causal ? p.nblk - 1 : p.nblk, (D * M + D) / 4, 64 * kFusedWaves) > kFusedSliceRows)
-        return hipErrorInvalidValue;
-    // the bf16 chunk loops address a wavefront's rows by 32-bit byte offsets
-    // (far from binding: a wavefront's share of any problem that fits in memory
-    // spans well under 1 GB)
-    if ((p.sub_tokens + 2 * kChunk) * int64_t(D > M ? D : M) * int64_t(sizeof(T)) > int64_t(UINT32_MAX))
-        return hipErrorInvalidValue;
+    if (!forward_plan_supported(BH, N, D, M, sizeof(T))) return hipErrorInvalidValue;
     char *base = reinterpret_cast<char *>(ws);
     int *header = reinterpret_cast<int *>(base);
     unsigned long long *flags = reinterpret_cast<unsigned long long *>(base + p.flags_off);
     float *recs = reinterpret_cast<float *>(base + p.recs_off);
+    // Under graph capture the tag below is fixed for every replay: the flags
+    // are cleared by a kernel node first, so no replay sees its predecessor's.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) == hipSuccess && cap == hipStreamCaptureStatusActive) {
+        const int64_t nflags = 2 * BH * p.nblk;
+        const unsigned blocks = unsigned(std::min<int64_t>(1024, ceil_div(nflags, 256)));
+        hipLaunchKernelGGL(k_clear_flags, dim3(blocks), dim3(256), 0, s, flags, nflags);
+    }
+    const unsigned long long tag = next_call_tag();
+    const int64_t limit = wait_limit();
     const dim3 grid(unsigned(BH * p.nblk)), block(64 * kFusedWaves);
     if (!causal)
         hipLaunchKernelGGL((k_fwd_fused<T, D, M, true, false>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens, sio);
+                           (const T *)v, (T *)out, header, flags, tag, recs, N, p.nblk, p.sub_tokens, limit, sio);
     else if (sio.features_given)
         hipLaunchKernelGGL((k_fwd_fused<T, D, M, false>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens, sio);
+                           (const T *)v, (T *)out, header, flags, tag, recs, N, p.nblk, p.sub_tokens, limit, sio);
     else
         hipLaunchKernelGGL((k_fwd_fused<T, D, M, true>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, header, flags, next_call_tag(), recs, N, p.nblk, p.sub_tokens, sio);
+                           (const T *)v, (T *)out, header, flags, tag, recs, N, p.nblk, p.sub_tokens, limit, sio);
     return hipGetLastError();
 }
 

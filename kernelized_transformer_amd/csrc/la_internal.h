@@ -51,8 +51,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // slice by slice by all blocks of the head), so no scan launch is needed.
 constexpr int kFusedWaves = 8;
 constexpr int64_t kMaxBlkPerHead = 64;   // flags of a head fit one wavefront
-constexpr int64_t kTargetWaves = 2048;   // two wavefronts per SIMD of the 256 CUs
 constexpr int kFusedDirectBlocks = 8;    // up to this many blocks per head: one exchange, no slices
+
+// Compute units of the current device (queried once per device and cached;
+// 256, MI355X's count, when no device can be queried).  The fused forward's
+// plan follows it: about two wavefronts per SIMD in all (8 per CU), and at
+// most one block per CU for each head, so that all blocks of a head can be
+// resident at once (a block always fits a CU by itself).
+int device_cus();
 
 struct FusedPlan {
     int64_t sub_tokens = 0;  // tokens per wavefront (multiple of kChunk)
@@ -65,18 +71,20 @@ struct FusedPlan {
     size_t total = 0;
 };
 
-inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
+inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M, int cus = device_cus()) {
     FusedPlan p;
+    const int64_t target_waves = int64_t(cus) * kFusedWaves;
+    const int64_t max_blk = std::min<int64_t>(kMaxBlkPerHead, cus);
     const int64_t nch = ceil_div(N, kChunk);
-    int64_t cpw = ceil_div(BH * nch, kTargetWaves);
+    int64_t cpw = ceil_div(BH * nch, target_waves);
     if (cpw < 1) cpw = 1;
-    const int64_t min_cpw = ceil_div(nch, kFusedWaves * kMaxBlkPerHead);
+    const int64_t min_cpw = ceil_div(nch, kFusedWaves * max_blk);
     if (cpw < min_cpw) cpw = min_cpw;
     p.sub_tokens = cpw * kChunk;
     p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
     // a short problem that leaves most CUs idle anyway: up to twice the chunks
     // per wavefront if that brings a head within the single-exchange hand-off
-    if (p.nblk > kFusedDirectBlocks && p.nblk <= 2 * kFusedDirectBlocks && BH * p.nblk <= 128) {
+    if (p.nblk > kFusedDirectBlocks && p.nblk <= 2 * kFusedDirectBlocks && BH * p.nblk <= cus / 2) {
         cpw = ceil_div(nch, kFusedWaves * kFusedDirectBlocks);
         p.sub_tokens = cpw * kChunk;
         p.nblk = ceil_div(N, kFusedWaves * p.sub_tokens);
@@ -87,6 +95,16 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     p.total = p.recs_off + align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float));
     return p;
 }
+
+// Polls a hand-off wait makes before it gives up (process-wide; see
+// la_set_wait_limit); set_wait_limit returns the previous value (a negative
+// argument restores the default).
+int64_t wait_limit();
+int64_t set_wait_limit(int64_t polls);
+
+// Whether the fused forward's plan for this shape is within the kernel's
+// limits (checked by the ABI before any launch).
+bool forward_plan_supported(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize);
 
 // Rows of block totals one thread sums while forming its slice (the kernel
 // keeps at most kFusedSliceRows in registers): block sb of nb owns ncol = its

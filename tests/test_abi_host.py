@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
               "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
-              "la_workspace_size", "la_status_string", "la_abi_version"):
+              "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version"):
         assert f in fns
 
 
@@ -40,9 +40,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 5
-    names = [la.la_status_string(s) for s in range(5)]
-    assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP"]
+    assert la.la_abi_version() == 6
+    names = [la.la_status_string(s) for s in range(6)]
+    assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP",
+                     "LA_ERR_TIMEOUT"]
     assert la.la_status_string(99) == "LA_ERR_UNKNOWN"
 
 
@@ -180,3 +181,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(la, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         la.load()
+
+
+def test_workspace_check_argument_errors():
+    """la_workspace_check validates the workspace before touching it."""
+    lib = la.load()
+    assert lib.la_workspace_check(None, 1 << 20, 0, None) == 3          # missing
+    assert lib.la_workspace_check(FAKE + 16, 1 << 20, 0, None) == 3     # misaligned
+    assert lib.la_workspace_check(FAKE, 128, 1, None) == 3              # smaller than the header
+
+
+def test_wait_limit_round_trip():
+    lib = la.load()
+    default = lib.la_set_wait_limit(5)
+    assert default == 1 << 20
+    assert lib.la_set_wait_limit(0) == 5
+    assert lib.la_set_wait_limit(-1) == 0          # back to the default
+    assert lib.la_set_wait_limit(-1) == default
