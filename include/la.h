@@ -121,6 +121,28 @@ la_status_t la_forward_causal(const void *q, const void *k, const void *v, void 
                               hipStream_t stream);
 
 /*
+ * la_forward_causal for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and kernels, with no workspace argument
+ * and no allocation of any kind.  Its workspace is a library-owned static
+ * device array of LA_NOALLOC_SCRATCH_BYTES (16 MiB), one per GPU, held until
+ * the process ends; shapes whose workspace (la_workspace_size(
+ * LA_OP_FWD_CAUSAL, ...)) exceeds it return LA_ERR_WORKSPACE before anything
+ * is launched (B1 H8 N65536 D=M=64 needs about 8.1 MiB).  The array keeps
+ * the last call's contents and needs no clearing (the hand-off flags are
+ * tagged per call).  All calls on one GPU share it: calls that can overlap
+ * in time on one GPU (other streams, other threads) race and give wrong
+ * results; calls ordered on one stream are safe.  `stream` must belong to
+ * the current device.  A hand-off wait that gives up is not reported (the
+ * error word lives in the array).  Arguments and errors otherwise as
+ * la_forward_causal.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (16u << 20)
+la_status_t la_forward_causal_noalloc(const void *q, const void *k, const void *v, void *out,
+                                      int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                      la_dtype_t dt, hipStream_t stream);
+
+/*
  * Causal forward continuing from a given recurrent state, and/or returning
  * the state after the last token ([summary] 3.3.2 and 3.4: the memory s_i,
  * z_i is all a step needs; 4.2.1: only s_i and z_i are kept between pixels;

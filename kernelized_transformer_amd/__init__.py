@@ -9,6 +9,7 @@ built, every call raises.
 
 Functions carry the C names:
   la_forward_causal(q, k, v, out=None, workspace=None)
+  la_forward_causal_noalloc(q, k, v, out=None)
   la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None)
   la_forward_causal_features(fq, fk, v, out=None, workspace=None)
   la_rff_features(x, omega, bias, out=None)
@@ -35,7 +36,7 @@ import os
 
 import torch
 
-__all__ = ["la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
+__all__ = ["la_forward_causal", "la_forward_causal_noalloc", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
            "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
            "la_decode_step",
            "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
@@ -77,11 +78,12 @@ def load():
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_backward_noncausal.argtypes = lib.la_backward_causal.argtypes
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.la_forward_causal_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_causal_features.argtypes = fwd
     lib.la_forward_causal_poly2.argtypes = fwd
     lib.la_rff_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
-    for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
+    for f in ("la_forward_causal", "la_forward_causal_noalloc", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
               "la_forward_causal_poly2",
               "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step"):
         getattr(lib, f).restype = i32
@@ -191,6 +193,24 @@ def _forward(func: str, op: int, q, k, v, out, workspace):
 def la_forward_causal(q, k, v, out=None, workspace=None):
     """Causal linear attention forward; returns out [B,H,N,M]."""
     return _forward("la_forward_causal", LA_OP_FWD_CAUSAL, q, k, v, out, workspace)
+
+
+def la_forward_causal_noalloc(q, k, v, out=None):
+    """la_forward_causal on the library's own scratch (no workspace, no
+    allocation in the library; ``out`` is allocated here unless given)."""
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k: [B,H,N,D]; v: [B,H,N,M]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    _dev(q, out)
+    _check("la_forward_causal_noalloc", load().la_forward_causal_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M, _DT[q.dtype], _stream(dev)))
+    return out
 
 
 def la_forward_causal_state(q, k, v, s0=None, z0=None, s_final=None, z_final=None, out=None, workspace=None):

@@ -90,6 +90,27 @@ la_status_t la_forward_causal(const void *q, const void *k, const void *v, void 
     return forward_common(true, q, k, v, out, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
 }
 
+la_status_t la_forward_causal_noalloc(const void *q, const void *k, const void *v, void *out, int64_t B,
+                                      int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt,
+                                      hipStream_t stream) {
+    static_assert(la::kNoAllocScratchBytes == LA_NOALLOC_SCRATCH_BYTES, "scratch size in la.h");
+    la_status_t st = check_shape(B, H, N, D, M, dt);
+    if (st != LA_OK) return st;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[3] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
+                        span(v, size_t(BH * N * M) * es)};
+    const Span o[1] = {span(out, size_t(BH * N * M) * es)};
+    if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
+    if (la::causal_workspace_bytes(BH, N, D, M) > la::kNoAllocScratchBytes) return LA_ERR_WORKSPACE;
+    if (!la::forward_plan_supported(BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
+    void *ws = la::noalloc_scratch();
+    if (ws == nullptr) return LA_ERR_HIP;
+    const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+                                            static_cast<float *>(ws), stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 la_status_t la_forward_causal_state(const void *q, const void *k, const void *v, void *out, const float *s0,
                                     const float *z0, float *s_final, float *z_final, int64_t B, int64_t H, int64_t N,
                                     int64_t D, int64_t M, la_dtype_t dt, void *workspace, size_t workspace_bytes,

@@ -906,6 +906,27 @@ int64_t set_wait_limit(int64_t polls) {
     return g_wait_limit.exchange(polls < 0 ? kDefaultWaitLimit : polls, std::memory_order_relaxed);
 }
 
+// Scratch of la_forward_causal_noalloc: the workspace of its causal forward
+// (header, hand-off flags, state records), owned by the library, one copy per
+// GPU, held until the process ends.  The flags are tagged per call and never
+// need clearing; calls that overlap on one GPU share it and race.  In host
+// code `scratch` is only a stand-in for the symbol: its device address on the
+// current device comes from hipGetSymbolAddress (cached per device) and is
+// the only thing ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void *noalloc_scratch() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    cache[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 int device_cus() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cache[kMaxDevices];

@@ -92,7 +92,8 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M, in
     p.rec = D * M + D;
     p.flags_off = 256;
     p.recs_off = p.flags_off + align256(size_t(2 * BH * p.nblk) * sizeof(unsigned long long));
-    p.total = p.recs_off + align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float));
+    // a single block per head exchanges nothing: no records
+    p.total = p.recs_off + (p.nblk > 1 ? align256(size_t(BH * p.nblk * 2 * p.rec) * sizeof(float)) : 0);
     return p;
 }
 
@@ -101,6 +102,12 @@ inline FusedPlan make_fused_plan(int64_t BH, int64_t N, int64_t D, int64_t M, in
 // argument restores the default).
 int64_t wait_limit();
 int64_t set_wait_limit(int64_t polls);
+
+// The library-owned scratch of la_forward_causal_noalloc on the current
+// device (device address, 256-byte aligned, kNoAllocScratchBytes long), or
+// null if it cannot be resolved.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+void *noalloc_scratch();
 
 // Whether the fused forward's plan for this shape is within the kernel's
 // limits (checked by the ABI before any launch).

@@ -90,6 +90,12 @@ int main(void) {
     EXPECT(la_decode_step(P(0), P(1), P(2), (float *)P(3), (float *)P(4), P(5), 2, 2, 32, 96, LA_DTYPE_BF16, 0),
            LA_ERR_UNSUPPORTED);
 
+    /* the no-allocation forward: a workspace beyond its scratch (about 17 MB) */
+    EXPECT(la_forward_causal_noalloc(P(0), P(64), P(128), P(192), 1, 255, 32768, 64, 64, LA_DTYPE_BF16, 0),
+           LA_ERR_WORKSPACE);
+    EXPECT(la_forward_causal_noalloc(P(0), P(1), P(2), P(0), 1, 1, 8, 32, 32, LA_DTYPE_F32, 0),
+           LA_ERR_INVALID_ARGUMENT);
+
     /* diagnostics */
     EXPECT(la_workspace_check(NULL, 1 << 20, 0, 0), LA_ERR_WORKSPACE);
     EXPECT(la_workspace_check((char *)P(0) + 16, 1 << 20, 0, 0), LA_ERR_WORKSPACE);

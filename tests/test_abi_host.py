@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
               "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
-              "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version"):
+              "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
+              "la_forward_causal_noalloc"):
         assert f in fns
 
 
@@ -198,3 +199,20 @@ def test_wait_limit_round_trip():
     assert lib.la_set_wait_limit(0) == 5
     assert lib.la_set_wait_limit(-1) == 0          # back to the default
     assert lib.la_set_wait_limit(-1) == default
+
+
+def test_noalloc_argument_errors():
+    """The no-allocation forward validates like la_forward_causal and rejects a
+    shape whose workspace exceeds its 16 MiB scratch, before any launch."""
+    lib = la.load()
+    b = [FAKE + (i << 34) for i in range(4)]   # far enough apart for a 1 GB tensor each
+
+    def na(q=b[0], k=b[1], v=b[2], out=b[3], B=1, H=8, N=65536, D=64, M=64, dt=1):
+        return lib.la_forward_causal_noalloc(q, k, v, out, B, H, N, D, M, dt, None)
+
+    big = dict(H=255, N=32768)               # 510 blocks of 2 records of 16.6 KB: about 17 MB
+    assert la.la_workspace_size(la.LA_OP_FWD_CAUSAL, 1, 255, 32768, 64, 64, 1) > 16 * 2 ** 20
+    assert na(**big) == 3
+    assert na(q=0, **big) == 1               # argument errors come first
+    assert na(D=48) == 2
+    assert na(out=b[0]) == 1                 # output aliases q
