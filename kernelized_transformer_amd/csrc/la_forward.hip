@@ -737,17 +737,17 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     // 2a. in place: slot w = A_w0 + ... + A_{w-1} for w >= 1, slot 0 = the
     // block total A_s (wavefront 0's partial sum is zero)
 #pragma unroll
-    for (int j = 0; j < (REC + NT - 1) / NT; ++j) {
+    for (int j = 0; j < NJ4; ++j) {   // as f32x4: four elements per LDS access
         const int e = tid + NT * j;
-        if (e < REC) {
-            float run = slot(0)[e];
+        if (e < REC4) {
+            f32x4 run = slot4[e];
 #pragma unroll
             for (int w = 1; w < kFusedWaves; ++w) {
-                const float x = slot(w)[e];
-                if (CAUSAL) slot(w)[e] = run;
+                const f32x4 x = slot4[w * SLOT4 + e];
+                if (CAUSAL) slot4[w * SLOT4 + e] = run;
                 run += x;
             }
-            slot(0)[e] = run;
+            slot4[e] = run;
         }
     }
     __syncthreads();
