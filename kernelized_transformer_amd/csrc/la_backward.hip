@@ -20,8 +20,10 @@
 // fp32 states of a wavefront fit in registers):
 //   1. k_segment_state + scan  -> S_aug at the start of every segment;
 //   2. k_bwd_dq    (forward direction, one wavefront per segment): recompute
-//      out and d for the chunk, form gh, write dQ, store g and h for pass 4,
-//      and accumulate the segment's sum_i qh_i gh_i^T;
+//      out and d for the chunk, form gh, write dQ, store 1/d and h for pass 4
+//      (8 bytes per token; pass 4 forms g = dout / d again from dout, with the
+//      same fp32 product and rounding), and accumulate the segment's
+//      sum_i qh_i gh_i^T;
 //   3. reverse scan            -> R_aug after the end of every segment;
 //   4. k_bwd_dkdv  (reverse direction): walk the chunks backwards carrying
 //      R_aug, write dK and dV.
@@ -47,12 +49,12 @@ constexpr int kBwdTile = 16 * ((D > M ? D : M) + kStagePad);
 // ---- pass 2: forward direction --------------------------------------------
 // Non-causal (CAUSAL = false): every query sees the full sums S_aug (record 0
 // of the head), so K, V are not read, there is no intra-chunk term and no
-// state to carry, and g, h are not stored (gbuf, hbuf unused).
+// state to carry, and 1/d, h are not stored (ibuf, hbuf unused).
 template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                const T *__restrict__ v, const T *__restrict__ dout,
                                                T *__restrict__ dq, const float *__restrict__ wsS,
-                                               float *__restrict__ wsR, T *__restrict__ gbuf,
+                                               float *__restrict__ wsR, float *__restrict__ ibuf,
                                                float *__restrict__ hbuf, int64_t N, int64_t nseg,
                                                int64_t seg_tokens, int64_t rec) {
     typedef typename IO<T>::frag Fr;
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
     const T *V = v + bh * N * M;
     const T *G = dout + bh * N * M;
     T *DQ = dq + bh * N * D;
-    T *GB = gbuf + bh * N * M;
+    float *IB = ibuf + bh * N;
     float *HB = hbuf + bh * N;
 
     const float *srec = wsS + (bh * nseg + (CAUSAL ? seg : 0)) * rec;
@@ -163,15 +165,10 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<T>::to_frag(gv[mt]);
         Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
-        if constexpr (CAUSAL && sizeof(T) == 2) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) tile_put_bf16<M>(otile, mt, IO<bf16>::from_f32(gv[mt]));
-            tile_flush_bf16<M>((bf16 *)GB, t0, t_end, otile);
-        } else if (CAUSAL && valid) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) store4<T>(GB + t * M + 16 * mt + 4 * g, IO<T>::from_f32(gv[mt]));
+        if (CAUSAL && valid && g == 0) {
+            IB[t] = inv;
+            HB[t] = h;
         }
-        if (CAUSAL && valid && g == 0) HB[t] = h;
 
         // dA^T[j][i] = vh_j . gh_i, masked to j <= i
         Fr dAT = frag_zero<Fr>();
@@ -225,8 +222,9 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 // sum to carry.
 template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const T *__restrict__ k,
-                                                 const T *__restrict__ v, const T *__restrict__ gbuf,
-                                                 const float *__restrict__ hbuf, T *__restrict__ dk,
+                                                 const T *__restrict__ v, const T *__restrict__ dout,
+                                                 const float *__restrict__ ibuf, const float *__restrict__ hbuf,
+                                                 T *__restrict__ dk,
                                                  T *__restrict__ dv, const float *__restrict__ wsR, int64_t N,
                                                  int64_t nseg, int64_t seg_tokens, int64_t rec) {
     typedef typename IO<T>::frag Fr;
@@ -239,7 +237,8 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     const T *Q = q + bh * N * D;
     const T *K = k + bh * N * D;
     const T *V = v + bh * N * M;
-    const T *GB = gbuf + bh * N * M;
+    const T *G = dout + bh * N * M;
+    const float *IB = ibuf + bh * N;
     const float *HB = hbuf + bh * N;
     T *DK = dk + bh * N * D;
     T *DV = dv + bh * N * M;
@@ -255,14 +254,15 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
-    float rh;
+    float rh, ri;
     auto load_all = [&](int64_t t0) {
         if (CAUSAL) load_chunk<T, D, BTT>(rq, Q, t0, t_end);
         load_chunk<T, D, BTT>(rk, K, t0, t_end);
         load_chunk<T, M, BTT>(rv, V, t0, t_end);
         if (CAUSAL) {
-            load_chunk<T, M, BTT>(rg, GB, t0, t_end);
+            load_chunk<T, M, BTT>(rg, G, t0, t_end);
             rh = (t0 + c < t_end) ? HB[t0 + c] : 0.f;
+            ri = (t0 + c < t_end) ? IB[t0 + c] : 0.f;
         }
     };
     load_all(t_begin + (nch - 1) * BCH);
@@ -277,10 +277,13 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) Vn[0][mt] = tmp[0][mt];
             Vn[0][MT] = k0ones;
-            if (CAUSAL) {
-                raw_frags<T, M, BTT>(tmp, rg, t0, t_end);
+            if (CAUSAL) {   // g = dout / d, formed as in the forward-direction pass; rows past t_end are 0
+                const bool ok = t0 + c < t_end;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = tmp[0][mt];
+                for (int mt = 0; mt < MT; ++mt) {
+                    const f32x4 gv = IO<T>::to_f32(rg[0][mt]) * ri;
+                    Gn[0][mt] = IO<T>::to_frag(ok ? gv : f32x4{0.f, 0.f, 0.f, 0.f});
+                }
                 Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
             }
         }
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 // through LDS; the rest is local to a wavefront's rows or (the small [g, h]
 // and dA products) computed by both.  Rows move through LDS staging as
 // 16-byte loads (a wavefront loads its own 32 columns of Q and K and all of
-// V and dout / g), and phi'(x) = min(phi(x), 1) is read off the staged
+// V and dout), and phi'(x) = min(phi(x), 1) is read off the staged
 // phi(x) (phi(x) <= 1 exactly when x <= 0, where phi' = phi = exp(x)).
 template <int M> struct W2Stage {   // one wavefront's private LDS, in elements
     static constexpr int SQ = 16 * (kW2Half + kStagePad);   // phi(Q) or phi(K) columns of the wavefront
@@ -391,7 +394,7 @@ template <int D, int M>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq_w2(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, bf16 *__restrict__ dq, const float *__restrict__ wsS, float *__restrict__ wsR,
-    bf16 *__restrict__ gbuf, float *__restrict__ hbuf, int64_t N, int64_t nseg, int64_t seg_tokens, int64_t rec) {
+    float *__restrict__ ibuf, float *__restrict__ hbuf, int64_t N, int64_t nseg, int64_t seg_tokens, int64_t rec) {
     static_assert(D == 2 * kW2Half, "two wavefronts of 32 feature rows");
     typedef bf16x4 Fr;
     constexpr int DTH = kW2Half / 16, MT = M / 16, PF = 1;
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16 *V = v + bh * N * M;
     const bf16 *G = dout + bh * N * M;
     bf16 *DQw = dq + bh * N * D + w * kW2Half;
-    bf16 *GB = gbuf + bh * N * M;
+    float *IB = ibuf + bh * N;
     float *HB = hbuf + bh * N;
 
     // per wavefront: dout rows first, then phi(Q), phi(K), V; the state's
@@ -527,12 +530,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<bf16>::to_frag(gv[mt]);
         Gn[0][MT] = IO<bf16>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
 
-        // g rows 8w .. 8w + 7 and h (wavefront 1) leave from here
-        lds_bf16 *otile = sg;   // the dout rows are read
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) tile_put_bf16<M>(otile, mt, Gn[0][mt]);
-        flush_rows<M, M, 8>(GB, t0, t_end, otile, 8 * w);
-        if (w == 1 && valid && g == 0) HB[uint32_t(t)] = h;
+        // 1/d and h leave from here (wavefront 1); the reverse pass forms g itself
+        if (w == 1 && valid && g == 0) {
+            IB[uint32_t(t)] = inv;
+            HB[uint32_t(t)] = h;
+        }
 
         // dA^T[j][i] = vh_j . gh_i, masked to j <= i (both wavefronts)
         f32x4 da = {0.f, 0.f, 0.f, 0.f};
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // dL/dqh^T for this wavefront's rows d, times phi'(q) = min(phi(q), 1)
         Fr SFT[MT + 1][DTH];
         transposed_frags_lds<16 * DTH, MT + 1>(SFT, sst);
-        lds_bf16 *dtile = sg;   // the g tile is flushed
+        lds_bf16 *dtile = sg;   // the dout rows are read
 #pragma unroll
         for (int dt = 0; dt < DTH; ++dt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -582,8 +584,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int D, int M>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv_w2(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ gbuf, const float *__restrict__ hbuf, bf16 *__restrict__ dk, bf16 *__restrict__ dv,
-    const float *__restrict__ wsR, int64_t N, int64_t nseg, int64_t seg_tokens, int64_t rec) {
+    const bf16 *__restrict__ dout, const float *__restrict__ ibuf, const float *__restrict__ hbuf,
+    bf16 *__restrict__ dk, bf16 *__restrict__ dv, const float *__restrict__ wsR, int64_t N, int64_t nseg,
+    int64_t seg_tokens, int64_t rec) {
     static_assert(D == 2 * kW2Half, "two wavefronts of 32 feature rows");
     typedef bf16x4 Fr;
     constexpr int DTH = kW2Half / 16, MT = M / 16, MH = MT / 2, PF = 2;
@@ -597,7 +600,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16 *Qw = q + bh * N * D + w * kW2Half;
     const bf16 *Kw = k + bh * N * D + w * kW2Half;
     const bf16 *V = v + bh * N * M;
-    const bf16 *GB = gbuf + bh * N * M;
+    const bf16 *G = dout + bh * N * M;
+    const float *IB = ibuf + bh * N;
     const float *HB = hbuf + bh * N;
     bf16 *DKw = dk + bh * N * D + w * kW2Half;
     bf16 *DVw = dv + bh * N * M + w * (M / 2);
@@ -616,13 +620,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
     auto chunk = [&](int64_t step) { return t_begin + imax64(nch - 1 - step, 0) * BCH; };
     dwordx4 lq[PF], lk[PF], lv[PF][NV], lg[PF][NV];
-    float lh[PF];
+    float lh[PF], li[PF];
     auto load_all = [&](int b, int64_t t0) {
         lq[b] = load_cols32<D>(Qw, t0, t_end);
         lk[b] = load_cols32<D>(Kw, t0, t_end);
         load_rows32<M>(lv[b], V, t0, t_end);
-        load_rows32<M>(lg[b], GB, t0, t_end);
-        lh[b] = HB[min(uint32_t(t0) + uint32_t(c), uint32_t(t_end - 1))];
+        load_rows32<M>(lg[b], G, t0, t_end);
+        const uint32_t tc = min(uint32_t(t0) + uint32_t(c), uint32_t(t_end - 1));
+        lh[b] = HB[tc];
+        li[b] = IB[tc];
     };
 #pragma unroll
     for (int b = 0; b < PF; ++b) load_all(b, chunk(b));
@@ -637,7 +643,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         stage_cols32_phi(sq, lq[b]);
         stage_cols32_phi(sk, lk[b]);
         stage_lines<M, 1, false, false>(sv, lv[b], t0, t_end);
-        stage_lines<M, 1, false, true>(sg, lg[b], t0, t_end);
+        stage_rows_scaled<M>(sg, lg[b], li[b], t0, t_end);   // g = dout / d, as the forward-direction pass forms it
         const float hc = (t0 + c < t_end) ? lh[b] : 0.f;
         load_all(b, chunk(step + PF));
         __builtin_amdgcn_sched_barrier(0);
@@ -972,7 +978,7 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
     const BwdLayout L = backward_layout(BH, N, D, M, sizeof(T));
     float *wsS = ws;
     float *wsR = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.states);
-    T *gbuf = reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + L.g_off);
+    float *ibuf = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.inv_off);
     float *hbuf = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.h_off);
     const dim3 grid(unsigned(BH * p.nseg));
     const int dt = sizeof(T) == 4 ? 0 : 1;
@@ -993,36 +999,36 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
             return hipGetLastError();
         }
         hipLaunchKernelGGL((k_bwd_dq<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, (T *)nullptr,
+                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, (float *)nullptr,
                            (float *)nullptr, N, p.nseg, p.seg_tokens, p.rec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (const T *)nullptr, (const float *)nullptr, (T *)dk, (T *)dv,
-                           (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
+                           (const T *)v, (const T *)nullptr, (const float *)nullptr, (const float *)nullptr,
+                           (T *)dk, (T *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
         return hipGetLastError();
     }
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
     if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) if (w2) {
         hipLaunchKernelGGL((k_bwd_dq_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
-                           (const bf16 *)v, (const bf16 *)dout, (bf16 *)dq, (const float *)wsS, wsR, (bf16 *)gbuf,
+                           (const bf16 *)v, (const bf16 *)dout, (bf16 *)dq, (const float *)wsS, wsR, ibuf,
                            hbuf, N, p.nseg, p.seg_tokens, p.rec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((k_bwd_dkdv_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
-                           (const bf16 *)v, (const bf16 *)gbuf, (const float *)hbuf, (bf16 *)dk, (bf16 *)dv,
-                           (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
+                           (const bf16 *)v, (const bf16 *)dout, (const float *)ibuf, (const float *)hbuf,
+                           (bf16 *)dk, (bf16 *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
         return hipGetLastError();
     }
     {
         hipLaunchKernelGGL((k_bwd_dq<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, gbuf, hbuf, N, p.nseg,
+                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, p.nseg,
                            p.seg_tokens, p.rec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (const T *)gbuf, (const float *)hbuf, (T *)dk, (T *)dv, (const float *)wsR,
-                           N, p.nseg, p.seg_tokens, p.rec);
+                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
+                           (T *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
         return hipGetLastError();
     }
 }

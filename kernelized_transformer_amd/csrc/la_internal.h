@@ -140,19 +140,20 @@ inline size_t causal_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M
 }
 
 // Backward workspace, in order: forward state records, reverse state records
-// (same size), the per-token normalized output gradient g_i = dout_i / d_i
-// ([BH][N][M] in the I/O type) and h_i = -(dout_i . out_i) / d_i ([BH][N]
-// fp32).
+// (same size), the per-token reciprocal denominators 1/d_i and
+// h_i = -(dout_i . out_i) / d_i ([BH][N] fp32 each).  The reverse pass forms
+// g_i = dout_i / d_i from dout and 1/d_i itself, exactly as the forward pass
+// does, instead of reading a staged copy of g.
 struct BwdLayout {
-    size_t states = 0, g_off = 0, h_off = 0, total = 0;
+    size_t states = 0, inv_off = 0, h_off = 0, total = 0;
 };
 
-inline BwdLayout backward_layout(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+inline BwdLayout backward_layout(int64_t BH, int64_t N, int64_t D, int64_t M, size_t) {
     const SegPlan p = make_plan(BH, N, D, M);
     BwdLayout L;
     L.states = align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
-    L.g_off = 2 * L.states;
-    L.h_off = L.g_off + align256(size_t(BH * N * M) * esize);
+    L.inv_off = 2 * L.states;
+    L.h_off = L.inv_off + align256(size_t(BH * N) * sizeof(float));
     L.total = L.h_off + align256(size_t(BH * N) * sizeof(float));
     return L;
 }

@@ -38,6 +38,29 @@ __device__ __forceinline__ void load_rows32(dwordx4 (&x)[F / 32], const bf16 *__
                                                    (t * uint32_t(2 * F) + uint32_t(2 * (e % F))));
     }
 }
+// 16 whole rows loaded by load_rows32<F>, each scaled by its token's factor
+// (lane c < 16 holds the factor of row c in `scale_c`) and rounded to bf16,
+// into staging rows of F + kStagePad; rows at or beyond t_end become 0.
+template <int F>
+__device__ __forceinline__ void stage_rows_scaled(lds_bf16 *stage, const dwordx4 (&x)[F / 32], float scale_c,
+                                                  int64_t t0, int64_t t_end) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < F / 32; ++i) {
+        const int e = (64 * i + l) * 8, row = e / F, col = e % F;
+        const float sc = __shfl(scale_c, row);
+        dwordx4 y;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float lo = __builtin_bit_cast(float, x[i][w] << 16);
+            const float hi = __builtin_bit_cast(float, x[i][w] & 0xffff0000u);
+            const bf16x2 p = {(bf16)(lo * sc), (bf16)(hi * sc)};
+            y[w] = __builtin_bit_cast(unsigned int, p);
+        }
+        if (t0 + row >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<lds_dwordx4 *>(stage + row * (F + kStagePad) + col) = y;
+    }
+}
 // ... into staging rows of 32 + kStagePad, phi applied (no row masks: the
 // callers keep rows past t_end out of every stored result themselves).
 __device__ __forceinline__ void stage_cols32_phi(lds_bf16 *stage, dwordx4 x) {
