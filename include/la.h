@@ -20,7 +20,13 @@
  *     q, k are [B][H][N][D]; v, out, dout are [B][H][N][M] (decode: no N).
  *     dt gives the element type of q, k, v, out, dout, dq, dk, dv (fp32 or
  *     bf16).  All state and accumulation is fp32 inside the kernels.
- *   - Supported head sizes: D, M in {32, 64}.  B, H, N >= 1.
+ *   - Head sizes: the forwards (la_forward_causal, _state, _features,
+ *     _noalloc, _noncausal) and la_decode_step take D, M (F for features)
+ *     any multiple of 16 from 16 to 128 -- D, M in {32, 64} run the fused
+ *     single-launch kernels, the others a three-launch path (per-segment sums,
+ *     scan, outputs, one wavefront per 16 columns of V); the backwards, the
+ *     polynomial kernel and the random features take D, M in {32, 64}.
+ *     Other sizes return LA_ERR_UNSUPPORTED.  B, H, N >= 1.
  *   - Every tensor pointer must be 16-byte aligned; outputs must not overlap
  *     any input or each other.
  *   - Calls are asynchronous on `stream` (0 = the null stream).  The library
@@ -46,7 +52,7 @@
  *     clears its hand-off flags before the forward itself, so every replay
  *     is correct even with changed inputs.
  *
- * Co-residency contract of the forwards.  Each (b, h) is split into blocks
+ * Co-residency contract of the fused forwards.  Each (b, h) is split into blocks
  * of 8 wavefronts that exchange fp32 state through the workspace and wait for
  * each other with bounded waits.  The plan gives a head at most
  * min(64, number of CUs of the current device) blocks (one CU holds a block,
@@ -69,7 +75,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 6
+#define LA_ABI_VERSION 7
 
 /* The enums are int-sized in C; C++ gets the same fixed underlying type, so
  * any int a C caller passes (an unknown dtype, op or status included) is a
@@ -207,7 +213,7 @@ la_status_t la_rff_features(const void *x, const float *omega, const float *bias
  * chosen, e.g. elu + 1, a polynomial, or random features):
  *   out_i = sum_{j<=i} (fq_i . fk_j) v_j / sum_{j<=i} (fq_i . fk_j),
  * i.e. la_forward_causal with phi the identity.  fq, fk: [B][H][N][F]; v,
- * out: [B][H][N][M]; F, M in {32, 64}; workspace
+ * out: [B][H][N][M]; F, M multiples of 16 up to 128; workspace
  * la_workspace_size(LA_OP_FWD_CAUSAL, B, H, N, F, M, dt).  Features of any
  * sign are accepted and nothing guards the denominators: a zero or negative
  * one gives what the division gives.  Errors and diagnostic word as

@@ -27,13 +27,29 @@ size_t esize(la_dtype_t dt) { return dt == LA_DTYPE_F32 ? 4 : 2; }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
-la_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt) {
+// any_size: every multiple of 16 up to 128 (decode, the forwards); otherwise
+// D, M in {32, 64} (backward, polynomial and random-feature kernels).
+la_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt, bool any_size = false) {
     if (B < 1 || H < 1 || N < 1 || D < 1 || M < 1) return LA_ERR_INVALID_ARGUMENT;
     if (B > kMaxElems || H > kMaxElems || N > kMaxElems) return LA_ERR_INVALID_ARGUMENT;
     if (B * H > kMaxElems / N) return LA_ERR_INVALID_ARGUMENT;
     if (dt != LA_DTYPE_F32 && dt != LA_DTYPE_BF16) return LA_ERR_UNSUPPORTED;
-    if ((D != 32 && D != 64) || (M != 32 && M != 64)) return LA_ERR_UNSUPPORTED;
+    if (any_size ? !(la::head_size_ok(D) && la::head_size_ok(M)) : !la::fused_head_sizes(D, M))
+        return LA_ERR_UNSUPPORTED;
     return LA_OK;
+}
+
+// The forwards: the fused single-launch kernels for D, M in {32, 64}, the
+// generic path for the other head sizes.
+hipError_t launch_any_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out, int64_t BH,
+                              int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s,
+                              la::StateIO sio = la::StateIO()) {
+    if (la::fused_head_sizes(D, M)) return la::launch_forward(causal, dt, q, k, v, out, BH, N, D, M, ws, s, sio);
+    return la::launch_forward_generic(causal, dt, q, k, v, out, BH, N, D, M, ws, s, sio);
+}
+
+bool forward_supported(bool causal, int64_t BH, int64_t N, int64_t D, int64_t M, size_t es) {
+    return !la::fused_head_sizes(D, M) || la::forward_plan_supported(BH, N, D, M, es);
 }
 
 // Pointers: all non-null and 16-byte aligned; no output overlaps any other
@@ -63,7 +79,7 @@ la_status_t check_workspace(void *ws, size_t have, size_t need, const Span *bufs
 la_status_t forward_common(bool causal, const void *q, const void *k, const void *v, void *out, int64_t B,
                            int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-    la_status_t st = check_shape(B, H, N, D, M, dt);
+    la_status_t st = check_shape(B, H, N, D, M, dt, true);
     if (st != LA_OK) return st;
     const size_t es = esize(dt);
     const int64_t BH = B * H;
@@ -74,8 +90,8 @@ la_status_t forward_common(bool causal, const void *q, const void *k, const void
     const Span all[4] = {in[0], in[1], in[2], o[0]};
     const size_t need = la::causal_workspace_bytes(BH, N, D, M);   // the same plan for both forwards
     if ((st = check_workspace(workspace, workspace_bytes, need, all, 4)) != LA_OK) return st;
-    if (!la::forward_plan_supported(BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
-    const hipError_t e = la::launch_forward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+    if (!forward_supported(causal, BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
+    const hipError_t e = launch_any_forward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
                                             static_cast<float *>(workspace), stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -94,7 +110,7 @@ la_status_t la_forward_causal_noalloc(const void *q, const void *k, const void *
                                       int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt,
                                       hipStream_t stream) {
     static_assert(la::kNoAllocScratchBytes == LA_NOALLOC_SCRATCH_BYTES, "scratch size in la.h");
-    la_status_t st = check_shape(B, H, N, D, M, dt);
+    la_status_t st = check_shape(B, H, N, D, M, dt, true);
     if (st != LA_OK) return st;
     const size_t es = esize(dt);
     const int64_t BH = B * H;
@@ -103,10 +119,10 @@ la_status_t la_forward_causal_noalloc(const void *q, const void *k, const void *
     const Span o[1] = {span(out, size_t(BH * N * M) * es)};
     if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
     if (la::causal_workspace_bytes(BH, N, D, M) > la::kNoAllocScratchBytes) return LA_ERR_WORKSPACE;
-    if (!la::forward_plan_supported(BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
+    if (!forward_supported(true, BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
     void *ws = la::noalloc_scratch();
     if (ws == nullptr) return LA_ERR_HIP;
-    const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+    const hipError_t e = launch_any_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
                                             static_cast<float *>(ws), stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -115,7 +131,7 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
                                     const float *z0, float *s_final, float *z_final, int64_t B, int64_t H, int64_t N,
                                     int64_t D, int64_t M, la_dtype_t dt, void *workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
-    la_status_t st = check_shape(B, H, N, D, M, dt);
+    la_status_t st = check_shape(B, H, N, D, M, dt, true);
     if (st != LA_OK) return st;
     if ((s0 == nullptr) != (z0 == nullptr) || (s_final == nullptr) != (z_final == nullptr))
         return LA_ERR_INVALID_ARGUMENT;
@@ -143,13 +159,13 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
     if ((st = check_workspace(workspace, workspace_bytes, la::causal_workspace_bytes(BH, N, D, M), all, nall)) !=
         LA_OK)
         return st;
-    if (!la::forward_plan_supported(BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
+    if (!forward_supported(true, BH, N, D, M, es)) return LA_ERR_UNSUPPORTED;
     la::StateIO sio;
     sio.s0 = s0;
     sio.z0 = z0;
     sio.s1 = s_final;
     sio.z1 = z_final;
-    const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
+    const hipError_t e = launch_any_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
                                             static_cast<float *>(workspace), stream, sio);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -157,7 +173,7 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
 la_status_t la_forward_causal_features(const void *fq, const void *fk, const void *v, void *out, int64_t B,
                                        int64_t H, int64_t N, int64_t F, int64_t M, la_dtype_t dt, void *workspace,
                                        size_t workspace_bytes, hipStream_t stream) {
-    la_status_t st = check_shape(B, H, N, F, M, dt);
+    la_status_t st = check_shape(B, H, N, F, M, dt, true);
     if (st != LA_OK) return st;
     const size_t es = esize(dt);
     const int64_t BH = B * H;
@@ -168,10 +184,10 @@ la_status_t la_forward_causal_features(const void *fq, const void *fk, const voi
     const Span all[4] = {in[0], in[1], in[2], o[0]};
     if ((st = check_workspace(workspace, workspace_bytes, la::causal_workspace_bytes(BH, N, F, M), all, 4)) != LA_OK)
         return st;
-    if (!la::forward_plan_supported(BH, N, F, M, es)) return LA_ERR_UNSUPPORTED;
+    if (!forward_supported(true, BH, N, F, M, es)) return LA_ERR_UNSUPPORTED;
     la::StateIO sio;
     sio.features_given = true;
-    const hipError_t e = la::launch_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, fq, fk, v, out, BH, N, F, M,
+    const hipError_t e = launch_any_forward(true, dt == LA_DTYPE_F32 ? 0 : 1, fq, fk, v, out, BH, N, F, M,
                                             static_cast<float *>(workspace), stream, sio);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
@@ -258,7 +274,7 @@ la_status_t la_backward_noncausal(const void *q, const void *k, const void *v, c
 
 la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S, float *Z, void *out, int64_t B,
                            int64_t H, int64_t D, int64_t M, la_dtype_t dt, hipStream_t stream) {
-    la_status_t st = check_shape(B, H, 1, D, M, dt);
+    la_status_t st = check_shape(B, H, 1, D, M, dt, true);
     if (st != LA_OK) return st;
     const size_t es = esize(dt);
     const int64_t BH = B * H;
@@ -271,7 +287,8 @@ la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S
 }
 
 size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt) {
-    if (check_shape(B, H, N, D, M, dt) != LA_OK) return 0;
+    const bool fwd = op == LA_OP_FWD_CAUSAL || op == LA_OP_FWD_NONCAUSAL;
+    if (check_shape(B, H, N, D, M, dt, fwd) != LA_OK) return 0;
     switch (op) {
     case LA_OP_FWD_CAUSAL:
         return la::causal_workspace_bytes(B * H, N, D, M);

@@ -988,12 +988,12 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
     // element offsets)
     const bool w2 = sizeof(T) == 2 && D == 2 * kW2Half && N * (D > M ? D : M) <= int64_t(INT32_MAX);
     if (!causal) {   // full sums S_aug, then R_aug, each into record 0 of the head
-        if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+        if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 1, s)) != hipSuccess) return e;
         if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) if (w2) {
             hipLaunchKernelGGL((k_bwd_dq_nc_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)dout,
                                (bf16 *)dq, (const float *)wsS, wsR, N, p.nseg, p.seg_tokens, p.rec);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+            if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, s)) != hipSuccess) return e;
             hipLaunchKernelGGL((k_bwd_dkdv_nc_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)k, (const bf16 *)v,
                                (bf16 *)dk, (bf16 *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
             return hipGetLastError();
@@ -1002,19 +1002,19 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
                            (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, (float *)nullptr,
                            (float *)nullptr, N, p.nseg, p.seg_tokens, p.rec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, nullptr, nullptr, s)) != hipSuccess) return e;
+        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 1, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, false>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
                            (const T *)v, (const T *)nullptr, (const float *)nullptr, (const float *)nullptr,
                            (T *)dk, (T *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
         return hipGetLastError();
     }
-    if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
+    if ((e = launch_scan(wsS, BH, p.nseg, p.rec, 0, s)) != hipSuccess) return e;
     if constexpr (sizeof(T) == 2 && D == 2 * kW2Half) if (w2) {
         hipLaunchKernelGGL((k_bwd_dq_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
                            (const bf16 *)v, (const bf16 *)dout, (bf16 *)dq, (const float *)wsS, wsR, ibuf,
                            hbuf, N, p.nseg, p.seg_tokens, p.rec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
+        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((k_bwd_dkdv_w2<D, M>), grid, dim3(128), 0, s, (const bf16 *)q, (const bf16 *)k,
                            (const bf16 *)v, (const bf16 *)dout, (const float *)ibuf, (const float *)hbuf,
                            (bf16 *)dk, (bf16 *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);
@@ -1025,7 +1025,7 @@ static hipError_t run_backward(bool causal, const void *q, const void *k, const 
                            (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, p.nseg,
                            p.seg_tokens, p.rec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, nullptr, nullptr, s)) != hipSuccess) return e;
+        if ((e = launch_scan(wsR, BH, p.nseg, p.rec, 2, s)) != hipSuccess) return e;
         hipLaunchKernelGGL((k_bwd_dkdv<T, D, M, true>), grid, dim3(64), 0, s, (const T *)q, (const T *)k,
                            (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
                            (T *)dv, (const float *)wsR, N, p.nseg, p.seg_tokens, p.rec);

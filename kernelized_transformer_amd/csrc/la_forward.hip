@@ -497,12 +497,14 @@ constexpr int kScanRows = int(kMaxSegPerHead / kScanG);
 // and the register count follows the segment count.
 template <int ROWS>
 __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int64_t nseg, int64_t rec, int mode,
-                                                    const float *__restrict__ init, float *__restrict__ fin) {
+                                                    ScanIO io) {
     // mode 0: exclusive prefix in place; 1: total into record 0 (non-causal);
     // 2: exclusive suffix in place (scan from the last segment backwards).
+    // io: an optional start state added to every prefix (mode 0) and the
+    // final state (start + total), each as S [srec] and Z [rec - srec].
     __shared__ f32x4 part[kScanG][kScanCols];
     const int cl = threadIdx.x % kScanCols, grp = threadIdx.x / kScanCols;
-    const int64_t rec4 = rec / 4;
+    const int64_t rec4 = rec / 4, s4 = io.srec / 4;
     const int64_t nblk_c = (rec4 + kScanCols - 1) / kScanCols;
     const int64_t bh = blockIdx.x / nblk_c;
     const int64_t c4 = (blockIdx.x % nblk_c) * kScanCols + cl;
@@ -519,6 +521,12 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int6
     f32x4 *first = base + (rev ? nseg - 1 - sc : sc) * rec4;
     const int64_t step = rev ? -rec4 : rec4;
 
+    // the start state is read before any thread writes the final state (they
+    // may be the same memory)
+    f32x4 init = {0.f, 0.f, 0.f, 0.f};
+    if (ok && io.s0)
+        init = c4 < s4 ? reinterpret_cast<const f32x4 *>(io.s0 + bh * io.srec)[c4]
+                       : reinterpret_cast<const f32x4 *>(io.z0 + bh * (rec - io.srec))[c4 - s4];
     f32x4 x[ROWS];
 #pragma unroll
     for (int j = 0; j < ROWS; ++j)   // all loads in flight first; rows past the group's end read its last row
@@ -531,7 +539,7 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int6
     }
     part[grp][cl] = sum;
     __syncthreads();
-    f32x4 run = (ok && init) ? reinterpret_cast<const f32x4 *>(init + bh * rec)[c4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 run = init;
     f32x4 total = run;
     for (int p = 0; p < kScanG; ++p) {
         if (p < grp) run += part[p][cl];
@@ -549,21 +557,23 @@ __global__ __launch_bounds__(256) void k_state_scan(float *__restrict__ ws, int6
     } else if (grp == 0) {
         base[0] = total;
     }
-    if (fin && grp == 0) reinterpret_cast<f32x4 *>(fin + bh * rec)[c4] = total;
+    if (io.s1 && grp == 0) {
+        if (c4 < s4) reinterpret_cast<f32x4 *>(io.s1 + bh * io.srec)[c4] = total;
+        else reinterpret_cast<f32x4 *>(io.z1 + bh * (rec - io.srec))[c4 - s4] = total;
+    }
 }
 
-hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, const float *init, float *fin,
-                       hipStream_t s) {
-    if (rec % 4 != 0 || nseg > kMaxSegPerHead) return hipErrorInvalidValue;
+hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, hipStream_t s, ScanIO io) {
+    if (rec % 4 != 0 || io.srec % 4 != 0 || nseg > kMaxSegPerHead) return hipErrorInvalidValue;
     const int64_t nblk = BH * ((rec / 4 + kScanCols - 1) / kScanCols);
     const int64_t per = (nseg + kScanG - 1) / kScanG;
     const dim3 grid{unsigned(nblk)}, block{256};
-    if (per <= 1) hipLaunchKernelGGL(k_state_scan<1>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
-    else if (per <= 2) hipLaunchKernelGGL(k_state_scan<2>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
-    else if (per <= 4) hipLaunchKernelGGL(k_state_scan<4>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
-    else if (per <= 8) hipLaunchKernelGGL(k_state_scan<8>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
-    else if (per <= 16) hipLaunchKernelGGL(k_state_scan<16>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
-    else hipLaunchKernelGGL(k_state_scan<kScanRows>, grid, block, 0, s, ws, nseg, rec, mode, init, fin);
+    if (per <= 1) hipLaunchKernelGGL(k_state_scan<1>, grid, block, 0, s, ws, nseg, rec, mode, io);
+    else if (per <= 2) hipLaunchKernelGGL(k_state_scan<2>, grid, block, 0, s, ws, nseg, rec, mode, io);
+    else if (per <= 4) hipLaunchKernelGGL(k_state_scan<4>, grid, block, 0, s, ws, nseg, rec, mode, io);
+    else if (per <= 8) hipLaunchKernelGGL(k_state_scan<8>, grid, block, 0, s, ws, nseg, rec, mode, io);
+    else if (per <= 16) hipLaunchKernelGGL(k_state_scan<16>, grid, block, 0, s, ws, nseg, rec, mode, io);
+    else hipLaunchKernelGGL(k_state_scan<kScanRows>, grid, block, 0, s, ws, nseg, rec, mode, io);
     return hipGetLastError();
 }
 

@@ -20,6 +20,12 @@ constexpr int64_t kTargetSegments = 1024;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Head sizes: the fused forward kernels (and the backward, the polynomial and
+// random-feature kernels) take D, M in {32, 64}; decode and the generic
+// forward every multiple of 16 up to 128.
+inline bool fused_head_sizes(int64_t D, int64_t M) { return (D == 32 || D == 64) && (M == 32 || M == 64); }
+inline bool head_size_ok(int64_t x) { return x >= 16 && x <= 128 && x % 16 == 0; }
+
 // How a (B*H, N) problem is cut into segments of whole chunks.  Each
 // segment is processed by one wavefront, chunk after chunk, carrying the
 // fp32 state; segment states are combined by a scan across segments.
@@ -135,8 +141,10 @@ inline int64_t fused_slice_rows(int64_t nb, int64_t nr, int64_t rec4, int64_t nt
 // flags count as set only when they hold the current call's tag.
 uint64_t next_call_tag();
 
+// Workspace of the forwards (the fused kernels or the generic path, by head size).
+size_t generic_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M);
 inline size_t causal_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
-    return make_fused_plan(BH, N, D, M).total;
+    return fused_head_sizes(D, M) ? make_fused_plan(BH, N, D, M).total : generic_workspace_bytes(BH, N, D, M);
 }
 
 // Backward workspace, in order: forward state records, reverse state records
@@ -189,16 +197,31 @@ size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t M);
 hipError_t launch_poly_forward(int dt, const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N,
                                int64_t D, int64_t M, float *ws, hipStream_t s);
 
+// The generic forward (la_generic.hip: segment sums, scan, outputs, with V
+// and out cut into 16-column groups); its workspace is one row-major record
+// (S [D][M], Z [D]) per segment.
+hipError_t launch_forward_generic(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
+                                  int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s,
+                                  StateIO sio = StateIO());
+
 // Launchers (hipError_t of the last launch).  dt: 0 = fp32, 1 = bf16.
 hipError_t launch_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
                           int64_t BH, int64_t N, int64_t D, int64_t M, float *ws, hipStream_t s,
                           StateIO sio = StateIO());
 hipError_t launch_segment_state(int dt, const void *k, const void *v, float *ws, int64_t BH, int64_t N, int64_t D,
                                 int64_t M, hipStream_t s);
+// Optional start state of a scan (added to every exclusive prefix) and final
+// state (start + total), per (b, h) as S [srec] then Z [rec - srec] floats in
+// separate arrays; s1 may equal s0 and z1 z0.
+struct ScanIO {
+    const float *s0 = nullptr, *z0 = nullptr;
+    float *s1 = nullptr, *z1 = nullptr;
+    int64_t srec = 0;
+};
 // mode 0: exclusive prefix over segments; 1: total into record 0;
 // 2: exclusive suffix (sum of the later segments).
-hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, const float *init, float *fin,
-                       hipStream_t s);
+hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mode, hipStream_t s,
+                       ScanIO io = ScanIO());
 hipError_t launch_backward(bool causal, int dt, const void *q, const void *k, const void *v, const void *dout,
                            void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
                            hipStream_t s);

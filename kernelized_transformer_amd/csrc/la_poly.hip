@@ -362,7 +362,7 @@ static hipError_t run_poly(const void *q, const void *k, const void *v, void *ou
                        p.seg_tokens, p.rec);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if ((e = launch_scan(ws, BH, p.nseg, p.rec, 0, nullptr, nullptr, s)) != hipSuccess) return e;
+    if ((e = launch_scan(ws, BH, p.nseg, p.rec, 0, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((k_poly_output<T, M>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v, (T *)out,
                        (const float *)ws, N, p.nseg, p.seg_tokens, p.rec);
     return hipGetLastError();

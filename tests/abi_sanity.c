@@ -46,7 +46,9 @@ int main(void) {
     }
     EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, 0, 1, 1, 32, 32, LA_DTYPE_F32), 0);
     EXPECT(la_workspace_size((la_op_t)9, 1, 1, 1, 32, 32, LA_DTYPE_F32), 0);
-    EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, 1, 1, 1, 48, 32, LA_DTYPE_F32), 0);
+    EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, 1, 1, 1, 40, 32, LA_DTYPE_F32), 0);
+    EXPECT(la_workspace_size(LA_OP_BWD_CAUSAL, 1, 1, 1, 48, 32, LA_DTYPE_F32), 0);
+    if (la_workspace_size(LA_OP_FWD_CAUSAL, 1, 1, 100, 48, 128, LA_DTYPE_F32) == 0) ++failures;
     EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, INT64_MAX, INT64_MAX, INT64_MAX, 32, 32, LA_DTYPE_F32), 0);
 
     /* forwards */
@@ -54,7 +56,9 @@ int main(void) {
            LA_ERR_INVALID_ARGUMENT);
     EXPECT(la_forward_causal(P(0), P(1), P(2), P(3), 1, 1, 0, 32, 32, LA_DTYPE_F32, P(4), 1 << 20, 0),
            LA_ERR_INVALID_ARGUMENT);
-    EXPECT(la_forward_causal(P(0), P(1), P(2), P(3), 1, 1, 8, 48, 32, LA_DTYPE_F32, P(4), 1 << 20, 0),
+    EXPECT(la_forward_causal(P(0), P(1), P(2), P(3), 1, 1, 8, 40, 32, LA_DTYPE_F32, P(4), 1 << 20, 0),
+           LA_ERR_UNSUPPORTED);
+    EXPECT(la_forward_causal(P(0), P(1), P(2), P(3), 1, 1, 8, 32, 144, LA_DTYPE_F32, P(4), 1 << 20, 0),
            LA_ERR_UNSUPPORTED);
     EXPECT(la_forward_causal(P(0), P(1), P(2), P(3), 1, 1, 8, 32, 32, (la_dtype_t)7, P(4), 1 << 20, 0),
            LA_ERR_UNSUPPORTED);
@@ -87,7 +91,7 @@ int main(void) {
            LA_ERR_WORKSPACE);
     EXPECT(la_decode_step(P(0), P(1), P(2), (float *)P(3), (float *)P(3), P(5), 2, 2, 32, 32, LA_DTYPE_BF16, 0),
            LA_ERR_INVALID_ARGUMENT);
-    EXPECT(la_decode_step(P(0), P(1), P(2), (float *)P(3), (float *)P(4), P(5), 2, 2, 32, 96, LA_DTYPE_BF16, 0),
+    EXPECT(la_decode_step(P(0), P(1), P(2), (float *)P(3), (float *)P(4), P(5), 2, 2, 32, 100, LA_DTYPE_BF16, 0),
            LA_ERR_UNSUPPORTED);
 
     /* the no-allocation forward: a workspace beyond its scratch (about 17 MB) */

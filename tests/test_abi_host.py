@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 6
+    assert la.la_abi_version() == 7
     names = [la.la_status_string(s) for s in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP",
                      "LA_ERR_TIMEOUT"]
@@ -67,7 +67,9 @@ def test_workspace_size():
     assert pw > 0 and pw % 256 == 0 and pw >= 2 * 65 * 32 * 32 * 4
     assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 64, 64, torch.bfloat16) == 0
     assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
-    assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) == 0     # unsupported D
+    assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 40, 32, torch.float32) == 0     # unsupported D
+    assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 128, torch.float32) > 0     # the generic path
+    assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) == 0     # backward: {32, 64} only
     # grows linearly in N at fixed segment count ceiling
     a = f(la.LA_OP_FWD_CAUSAL, 1, 8, 65536, 64, 64, torch.bfloat16)
     assert a <= 8 * 64 * 2 * (64 * 64 + 64) * 4 + 4096
@@ -89,8 +91,8 @@ def test_forward_argument_errors(fn):
     assert _fwd(lib, fn, q=FAKE + 8) == 1               # misaligned
     assert _fwd(lib, fn, N=0) == 1                      # empty
     assert _fwd(lib, fn, B=-1) == 1
-    assert _fwd(lib, fn, D=48) == 2                     # unsupported head size
-    assert _fwd(lib, fn, M=16) == 2
+    assert _fwd(lib, fn, D=40) == 2                     # not a multiple of 16
+    assert _fwd(lib, fn, M=144) == 2                    # beyond 128
     assert _fwd(lib, fn, dt=7) == 2                     # unknown dtype
     assert _fwd(lib, fn, out=FAKE + 64) == 1            # output overlaps q
     assert _fwd(lib, fn, ws=0, wsb=1 << 20) == 3        # missing workspace
@@ -118,7 +120,7 @@ def test_forward_state_argument_errors():
     assert fs(s1=b[6], z1=b[6] + 256) == 1          # z_final overlaps s_final
     assert fs(s1=b[4], z1=b[4] + 16) == 1           # in place S, z_final inside it
     assert fs(s1=b[0]) == 1                         # final state over q
-    assert fs(D=48) == 2
+    assert fs(D=40) == 2
     assert fs(ws=b[6], wsb=1 << 20) == 3            # workspace overlaps the final state
 
 
@@ -214,5 +216,5 @@ def test_noalloc_argument_errors():
     assert la.la_workspace_size(la.LA_OP_FWD_CAUSAL, 1, 255, 32768, 64, 64, 1) > 16 * 2 ** 20
     assert na(**big) == 3
     assert na(q=0, **big) == 1               # argument errors come first
-    assert na(D=48) == 2
+    assert na(D=40) == 2
     assert na(out=b[0]) == 1                 # output aliases q
