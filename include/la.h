@@ -179,10 +179,12 @@ la_status_t la_forward_causal_state(const void *q, const void *k, const void *v,
  * sim(q, k) = (q . k)^2, i.e. phi(x) = vec(x x^T) with D^2 features:
  *   out_i = sum_{j<=i} (q_i . k_j)^2 v_j / sum_{j<=i} (q_i . k_j)^2.
  * No feature map is applied to q, k beyond that (no elu).  q, k:
- * [B][H][N][D]; v, out: [B][H][N][M]; D = 32 only (LA_ERR_UNSUPPORTED
- * otherwise), M in {32, 64}; workspace
- * la_workspace_size(LA_OP_FWD_CAUSAL_POLY2, ...): one fp32 record of
- * (M + 1) D^2 floats per segment.  A query orthogonal to every earlier key
+ * [B][H][N][D]; v, out: [B][H][N][M]; D, M in {32, 64} (LA_ERR_UNSUPPORTED
+ * otherwise).  The kernels use the D (D + 1) / 2 distinct products q_a q_b,
+ * a <= b, as features (the same sums as vec(x x^T)).  Workspace
+ * la_workspace_size(LA_OP_FWD_CAUSAL_POLY2, ...): per segment one fp32 record
+ * of the segment's feature state and its D x D normalizer sum (256 bytes when
+ * each (b, h) is a single segment).  A query orthogonal to every earlier key
  * has a zero denominator; nothing guards it.  Errors as la_forward_causal.
  */
 la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v, void *out,

@@ -252,7 +252,7 @@ def la_forward_causal_features(fq, fk, v, out=None, workspace=None):
 
 
 def la_forward_causal_poly2(q, k, v, out=None, workspace=None):
-    """Causal attention with the degree-2 polynomial kernel (q . k)^2 (D = 32); returns out [B,H,N,M]."""
+    """Causal attention with the degree-2 polynomial kernel (q . k)^2 (D, M in {32, 64}); returns out [B,H,N,M]."""
     return _forward("la_forward_causal_poly2", LA_OP_FWD_CAUSAL_POLY2, q, k, v, out, workspace)
 
 

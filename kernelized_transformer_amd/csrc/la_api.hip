@@ -197,7 +197,7 @@ la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v,
                                     size_t workspace_bytes, hipStream_t stream) {
     la_status_t st = check_shape(B, H, N, D, M, dt);
     if (st != LA_OK) return st;
-    if (D != 32) return LA_ERR_UNSUPPORTED;
+    if (!la::poly_head_sizes(D, M)) return LA_ERR_UNSUPPORTED;
     const size_t es = esize(dt);
     const int64_t BH = B * H;
     const Span in[3] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
@@ -205,7 +205,7 @@ la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v,
     const Span o[1] = {span(out, size_t(BH * N * M) * es)};
     if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
     const Span all[4] = {in[0], in[1], in[2], o[0]};
-    if ((st = check_workspace(workspace, workspace_bytes, la::poly_workspace_bytes(BH, N, M), all, 4)) != LA_OK)
+    if ((st = check_workspace(workspace, workspace_bytes, la::poly_workspace_bytes(BH, N, D, M), all, 4)) != LA_OK)
         return st;
     const hipError_t e = la::launch_poly_forward(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
                                                  static_cast<float *>(workspace), stream);
@@ -299,7 +299,7 @@ size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D,
     case LA_OP_BWD_NONCAUSAL:
         return la::backward_noncausal_workspace_bytes(B * H, N, D, M);
     case LA_OP_FWD_CAUSAL_POLY2:
-        return D == 32 ? la::poly_workspace_bytes(B * H, N, M) : 0;
+        return la::poly_workspace_bytes(B * H, N, D, M);
     }
     return 0;
 }

@@ -191,9 +191,11 @@ struct StateIO {
 hipError_t launch_rff_features(int dt, const void *x, const float *omega, const float *bias, void *out, int64_t rows,
                                int64_t D, int64_t R, hipStream_t s);
 
-// Causal forward with the degree-2 polynomial kernel (q . k)^2, D = 32,
-// M in {32, 64}; workspace: one [M + 1][32][32] fp32 record per segment.
-size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t M);
+// Causal forward with the degree-2 polynomial kernel (q . k)^2, D, M in
+// {32, 64}; workspace: one fp32 record of the segment's feature state and
+// D x D normalizer per segment (256 bytes when a (b, h) is one segment).
+bool poly_head_sizes(int64_t D, int64_t M);
+size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M);
 hipError_t launch_poly_forward(int dt, const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N,
                                int64_t D, int64_t M, float *ws, hipStream_t s);
 

@@ -435,6 +435,38 @@ void orc_forward_causal_poly2(const double *q, const double *k, const double *v,
 }
 
 /*
+ * Selected rows of the same causal forward, each from the kernel itself
+ * ([summary] 3.2.1; the attention form sim(q_i, k_j) summed over j <= i):
+ *   out_i = sum_{j<=i} (q_i . k_j)^2 v_j / sum_{j<=i} (q_i . k_j)^2,
+ * O(i (D + M)) per row, for checking long sequences at sampled rows.
+ * rows: nrows token indices in [0, N); out: [B][H][nrows][M].
+ */
+void orc_forward_causal_poly2_rows(const double *q, const double *k, const double *v, const int64_t *rows,
+                                   double *out, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                   int64_t nrows)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t i = rows[r];
+            const double *qi = q + (bh * N + i) * D;
+            double *o = out + (bh * nrows + r) * M;
+            double den = 0.0;
+            for (int64_t m = 0; m < M; ++m) o[m] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                const double *kj = k + (bh * N + j) * D, *vj = v + (bh * N + j) * M;
+                double dot = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += qi[a] * kj[a];
+                const double w = dot * dot;
+                den += w;
+                for (int64_t m = 0; m < M; ++m) o[m] += w * vj[m];
+            }
+            for (int64_t m = 0; m < M; ++m) o[m] /= den;
+        }
+}
+
+/*
  * One RNN-style decode step for B*H independent streams ([review] "Proposed
  * method", attention memory s and normalizer memory z; [summary] 3.3.2, 3.4;
  * [deck] slide 4): S += phi(k) v^T, Z += phi(k), then

@@ -354,6 +354,9 @@ def check_poly2(lib):
             assert _rel(got, v) < 1e-15
         full = (q @ np.swapaxes(k, -1, -2)) ** 2
         assert _rel(got[:, :, -1], ((full @ v) / full.sum(-1, keepdims=True))[:, :, -1]) < 1e-12
+        rows = np.unique(np.array([0, N // 3, N // 2, N - 1]))
+        sampled = oracle.forward_causal_poly2_rows(q, k, v, rows, lib=lib)
+        assert _rel(sampled, ref[:, :, rows]) < 1e-12, (B, H, N, D, M, _rel(sampled, ref[:, :, rows]))
 
 
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,

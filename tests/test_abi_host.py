@@ -62,10 +62,17 @@ def test_workspace_size():
     assert nb > 0 and nb % 256 == 0 and nb < f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
     assert f(la.LA_OP_BWD_NONCAUSAL, 1, 8, 65536, 64, 64, torch.bfloat16) < 64 * 2 ** 20
     assert f(7, 1, 2, 256, 32, 32, torch.float32) == 0                        # unknown op
-    # polynomial kernel: one (M + 1) x 32 x 32 fp32 record per segment, D = 32 only
+    # polynomial kernel: per segment one fp32 record of 33 (D = 32) or 130
+    # (D = 64) feature tiles per 16 columns and the D x D normalizer, in
+    # 16 x 16 tiles; a (b, h) that is one segment needs no records
+    rec = lambda D, M: ((D // 16) * (D // 16 + 1) // 2 + 15 * (D // 16) ** 2 // 2) * (M // 16) * 1024 + (D // 16) ** 2 * 1024
     pw = f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 32, 64, torch.bfloat16)
-    assert pw > 0 and pw % 256 == 0 and pw >= 2 * 65 * 32 * 32 * 4
-    assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 64, 64, torch.bfloat16) == 0
+    assert pw > 0 and pw % 256 == 0 and pw >= 2 * 2 * rec(32, 64)
+    p64 = f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 64, 64, torch.bfloat16)
+    assert p64 % 256 == 0 and p64 >= 2 * 2 * rec(64, 64)
+    assert f(la.LA_OP_FWD_CAUSAL_POLY2, 64, 8, 256, 32, 32, torch.bfloat16) == 256
+    assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 48, 64, torch.bfloat16) == 0
+    assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 32, 16, torch.bfloat16) == 0
     assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 40, 32, torch.float32) == 0     # unsupported D
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 128, torch.float32) > 0     # the generic path
@@ -126,8 +133,9 @@ def test_forward_state_argument_errors():
 
 def test_poly2_argument_errors():
     lib = la.load()
-    assert _fwd(lib, "la_forward_causal_poly2", D=64) == 2           # D = 32 only
+    assert _fwd(lib, "la_forward_causal_poly2", D=48) == 2           # D, M in {32, 64}
     assert _fwd(lib, "la_forward_causal_poly2", M=16) == 2
+    assert _fwd(lib, "la_forward_causal_poly2", D=128) == 2
     assert _fwd(lib, "la_forward_causal_poly2", q=0) == 1
     assert _fwd(lib, "la_forward_causal_poly2", out=FAKE + 64) == 1
     assert _fwd(lib, "la_forward_causal_poly2", wsb=16) == 3

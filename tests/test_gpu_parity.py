@@ -469,7 +469,7 @@ def test_forward_features_mixed_sign(name, w):
     check(f"out[{name}]", host(out), oracle.forward_causal_features(fq, fk, v), w.dtype)
 
 
-# Degree-2 polynomial kernel (q . k)^2, D = 32.
+# Degree-2 polynomial kernel (q . k)^2, D, M in {32, 64}.
 POLY_CASES = [
     ("w1_f32", wl.WORKLOADS[1]),
     ("w2_f32", wl.WORKLOADS[2]),
@@ -479,6 +479,11 @@ POLY_CASES = [
     ("n1001_ragged_bf16_m64", _wl(223, 2, 3, 1001, 32, 64, "bf16")),
     ("n100000_many_segments", _wl(224, 1, 1, 100000, 32, 32, "bf16")),
     ("long_b1h8n65536_d32", _wl(225, 1, 8, 65536, 32, 32, "bf16")),
+    ("d64_n1_bf16", _wl(226, 2, 2, 1, 64, 64, "bf16")),
+    ("d64_n33_f32_m32", _wl(227, 1, 2, 33, 64, 32, "f32")),
+    ("d64_n700_ragged_f32", _wl(228, 2, 2, 700, 64, 64, "f32")),
+    ("d64_n1500_bf16_m32", _wl(229, 1, 3, 1500, 64, 32, "bf16")),
+    ("d64_b8h8n512_single_segment_bf16", _wl(230, 8, 8, 512, 64, 64, "bf16")),
 ]
 
 
@@ -489,6 +494,39 @@ def test_forward_causal_poly2(name, w):
     out = la.la_forward_causal_poly2(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
     torch.cuda.synchronize()
     check(f"out[{name}]", host(out), oracle.forward_causal_poly2(q, k, v), w.dtype)
+
+
+def _poly_rows(N, seg, n_random, seed):
+    """Rows to check on a long sequence: both ends, the chunk edges of the
+    first tokens, both sides of every multiple of seg, and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, 15, 16, 31, 32, 33, N - 2, N - 1}
+    for b in range(seg, N, seg):
+        rows.update({b - 1, b, b + 1})
+    rows.update(int(x) for x in rng.integers(0, N, n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@pytest.mark.parametrize("name,w,seg", [
+    ("b1h8n65536_d64m64_bf16", _wl(231, 1, 8, 65536, 64, 64, "bf16"), 4096),
+    ("b1h1n20000_d64m64_f32_many_segments", _wl(232, 1, 1, 20000, 64, 64, "f32"), 160),
+    ("b1h2n30011_d64m32_bf16", _wl(233, 1, 2, 30011, 64, 32, "bf16"), 256),
+], ids=["b1h8n65536_d64m64_bf16", "b1h1n20000_d64m64_f32_many_segments", "b1h2n30011_d64m32_bf16"])
+def test_forward_causal_poly2_long_sampled(name, w, seg):
+    """Long sequences at D = 64, where the oracle's D^2 feature recurrence
+    would take minutes: every output row of the kernel is computed, and
+    sampled rows (both ends, both sides of multiples of the segment length,
+    random rows) are checked one by one against the kernel summed directly,
+    each row under the same relative tolerance."""
+    q, k, v = wl.forward_inputs(w)
+    _say(f"polynomial forward {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}, sampled rows")
+    out = la.la_forward_causal_poly2(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isfinite(got).all()
+    rows = _poly_rows(w.N, seg, 48, w.wid)
+    ref = oracle.forward_causal_poly2_rows(q, k, v, rows)
+    check(f"out[{name}] rows", got[:, :, rows], ref, w.dtype, lead=3)
 
 
 def test_forward_causal_longest_sequence():
