@@ -93,6 +93,27 @@ template <int NL> constexpr PolyTile poly_tile(int f) {
     return PolyTile{-1, 0, 0, 0, 0};
 }
 
+// The groups of four rotated q values (bit 4 i + x / 4: qr[16 i + x .. + 3])
+// that the readout of tiles [f0, f1) reads; group 0 of every block is always
+// included (the intra-chunk products and the normalizer use it).  The others
+// are never loaded, so they take no registers.
+template <int NL> constexpr unsigned poly_qr_groups(int f0, int f1) {
+    unsigned m = 0;
+    for (int i = 0; i < NL; ++i) m |= 1u << (4 * i);
+    for (int f = f0; f < f1; ++f) {
+        const PolyTile t = poly_tile<NL>(f);
+        for (int r = 0; r < 4; ++r) {
+            if (t.kind == 2) {
+                m |= 1u << (4 * t.j + ((r + t.d) % 16) / 4);
+            } else if (t.kind == 3) {
+                m |= 1u << (4 * (t.s % NL) + (r + 8) / 4);
+                m |= 1u << (4 * (NL / 2 + t.s / NL) + (r + 8) / 4);
+            }
+        }
+    }
+    return m;
+}
+
 // x as held by lane (c + d) % 16 of the same row of 16 lanes (a DPP row
 // rotation: with row_ror:n, lane l reads lane l - n of its row).
 template <int d> __device__ __forceinline__ float from_lane_ahead(float x) {
@@ -162,7 +183,7 @@ template <int NL, int F> __device__ __forceinline__ f32x4 phi_q(const float (&qr
 template <typename T, int D, int M> struct PolyCfg {
     static constexpr int NL = D / 16;                   // dimension tiles
     static constexpr int FT = poly_tiles<NL>();         // feature tiles
-    static constexpr int MB = D == 32 ? M : 32;         // output columns per workgroup
+    static constexpr int MB = D == 32 ? M : 16;         // output columns per workgroup
     static constexpr int NMB = M / MB;                  // workgroups per segment
     static constexpr int MT = MB / 16;                  // column tiles per workgroup
     static constexpr int MTOT = M / 16;                 // column tiles of the record
@@ -174,8 +195,8 @@ template <typename T, int D, int M> struct PolyCfg {
     static constexpr int CH = 16 * TT;                  // tokens per chunk (outputs)
     // The segment sums exchange nothing between wavefronts, so they take
     // longer chunks: fewer barriers, more work between them.
-    static constexpr int TT1 = sizeof(T) == 2 ? 8 : 4;
-    static constexpr int PF1 = 2;
+    static constexpr int TT1 = 4;
+    static constexpr int PF1 = 3;
     // State converted to bf16 once per chunk (else once per token tile,
     // which needs fewer registers).
     static constexpr bool SB_CACHE = D == 32;
@@ -362,12 +383,14 @@ __device__ __forceinline__ typename IO<T>::vec4 nat_frag(const T *stage, int tt,
 }
 
 // Rotated q of token tile tt: qr[x + 16 i] = q[16 tt + c][16 i + (4g + x) % 16].
-template <int D, int QS> __device__ __forceinline__ void load_qr(float (&qr)[D], const float *sq, int tt) {
+template <int D, int QS, unsigned MASK = ~0u>
+__device__ __forceinline__ void load_qr(float (&qr)[D], const float *sq, int tt) {
     const int c = lane_id() & 15, g = lane_id() >> 4;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i)
 #pragma unroll
         for (int x0 = 0; x0 < 16; x0 += 4) {
+            if (!((MASK >> (4 * i + x0 / 4)) & 1u)) continue;   // never read by this wavefront
             const f32x4 y =
                 *reinterpret_cast<const f32x4 *>(sq + (16 * tt + c) * QS + 16 * i + 4 * ((g + x0 / 4) & 3));
 #pragma unroll
@@ -714,7 +737,7 @@ __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, 
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             float qr[D];
-            load_qr<D, SM::QS>(qr, sm.q[buf], tt);
+            load_qr<D, SM::QS, poly_qr_groups<C::NL>(PW::F0, PW::F1)>(qr, sm.q[buf], tt);
             w.template readout_tt<0, C::SB_CACHE, TT>(acc, sb, qr, tt, glo);
             dpart[tt] = w.den_part(qr);
             Fr pf[TT];
@@ -815,7 +838,7 @@ inline PolyPlan make_poly_plan(int64_t BH, int64_t N, int64_t D, int64_t M, int 
     PolyPlan p;
     const int64_t NL = D / 16, FT = NL * (NL + 1) / 2 + 15 * NL * NL / 2;
     const int64_t chunk = 128;   // a multiple of both kernels' chunk lengths
-    p.nmb = D == 32 ? 1 : M / 32;
+    p.nmb = D == 32 ? 1 : M / 16;
     p.rec = (FT * (M / 16) + NL * NL) * 256;
     const int64_t nch = ceil_div(N, chunk);
     int64_t nseg = ceil_div(cus, BH * p.nmb);
