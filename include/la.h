@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 7
+#define LA_ABI_VERSION 8
 
 /* The enums are int-sized in C; C++ gets the same fixed underlying type, so
  * any int a C caller passes (an unknown dtype, op or status included) is a
@@ -104,7 +104,8 @@ typedef enum la_op_e LA_ENUM_BASE {
     LA_OP_FWD_NONCAUSAL = 1,  /* la_forward_noncausal */
     LA_OP_BWD_CAUSAL = 2,     /* la_backward_causal */
     LA_OP_BWD_NONCAUSAL = 3,  /* la_backward_noncausal */
-    LA_OP_FWD_CAUSAL_POLY2 = 4 /* la_forward_causal_poly2 */
+    LA_OP_FWD_CAUSAL_POLY2 = 4,   /* la_forward_causal_poly2, la_forward_causal_poly2_state */
+    LA_OP_FWD_NONCAUSAL_POLY2 = 5 /* la_forward_noncausal_poly2 */
 } la_op_t;
 
 /*
@@ -191,6 +192,54 @@ la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v,
                                     int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                                     la_dtype_t dt, void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/*
+ * Floats of one (b, h)'s polynomial-kernel state: the feature state
+ * sum_j phi(k_j) v_j^T and the normalizer sum_j k_j k_j^T, in the library's own
+ * tiled fp32 layout (opaque: only la_forward_causal_poly2_state and
+ * la_decode_step_poly2 read or write it; all zeros is the empty prefix).
+ * 0 for unsupported D, M.
+ */
+int64_t la_poly2_state_floats(int64_t D, int64_t M);
+
+/*
+ * la_forward_causal_poly2 that also writes, for every (b, h), the state
+ * after its last token into state_final [B][H][la_poly2_state_floats(D, M)]
+ * (fp32, caller-owned, 16-byte aligned, overlapping no other buffer), from
+ * which la_decode_step_poly2 continues the sequence ([summary] 3.3.2: the
+ * causal form is an RNN whose state is updated once per token).  Workspace
+ * as la_forward_causal_poly2.  state_final NULL: LA_ERR_INVALID_ARGUMENT.
+ */
+la_status_t la_forward_causal_poly2_state(const void *q, const void *k, const void *v, void *out,
+                                          float *state_final, int64_t B, int64_t H, int64_t N,
+                                          int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Non-causal forward with the degree-2 polynomial kernel ([summary] 3.2.1;
+ * every key attends, as in the non-causal linear form):
+ *   out_i = sum_j (q_i . k_j)^2 v_j / sum_j (q_i . k_j)^2.
+ * Arguments as la_forward_causal_poly2; workspace
+ * la_workspace_size(LA_OP_FWD_NONCAUSAL_POLY2, ...) (one record per segment,
+ * also with a single segment: the (b, h) total).
+ */
+la_status_t la_forward_noncausal_poly2(const void *q, const void *k, const void *v, void *out,
+                                       int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                       la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
+ * One decode step of the polynomial kernel for B*H streams ([summary] 3.3.2:
+ * update the state with the new key and value, then read it out): q, k:
+ * [B][H][D]; v, out: [B][H][M]; state [B][H][la_poly2_state_floats(D, M)]
+ * fp32, updated in place (zeros for an empty prefix, or the state_final of
+ * la_forward_causal_poly2_state).  Out is read after the update, so a run of
+ * steps equals the causal forward over the same tokens.  D, M in {32, 64}.
+ * The state must not overlap q, k, v or out.  Errors as la_decode_step.
+ */
+la_status_t la_decode_step_poly2(const void *q, const void *k, const void *v, float *state,
+                                 void *out, int64_t B, int64_t H, int64_t D, int64_t M,
+                                 la_dtype_t dt, hipStream_t stream);
 
 /*
  * Random Fourier features ([summary] 5: approximating the RBF kernel with

@@ -14,6 +14,10 @@ Functions carry the C names:
   la_forward_causal_features(fq, fk, v, out=None, workspace=None)
   la_rff_features(x, omega, bias, out=None)
   la_forward_causal_poly2(q, k, v, out=None, workspace=None)
+  la_forward_causal_poly2_state(q, k, v, state_final=None, out=None, workspace=None)
+  la_forward_noncausal_poly2(q, k, v, out=None, workspace=None)
+  la_decode_step_poly2(q, k, v, state, out=None)
+  la_poly2_state_floats(D, M)
   la_forward_noncausal(q, k, v, out=None, workspace=None)
   la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
@@ -37,15 +41,18 @@ import os
 import torch
 
 __all__ = ["la_forward_causal", "la_forward_causal_noalloc", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
-           "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
+           "la_forward_causal_poly2", "la_forward_causal_poly2_state", "la_forward_noncausal_poly2",
+           "la_decode_step_poly2", "la_poly2_state_floats",
+           "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
            "la_decode_step",
            "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
            "LAError", "lib_path", "load", "LA_ERR_TIMEOUT",
            "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL",
-           "LA_OP_FWD_CAUSAL_POLY2", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
+           "LA_OP_FWD_CAUSAL_POLY2", "LA_OP_FWD_NONCAUSAL_POLY2", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL, LA_OP_FWD_CAUSAL_POLY2 = 0, 1, 2, 3, 4
+LA_OP_FWD_NONCAUSAL_POLY2 = 5
 _DT = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
 
 LA_ERR_TIMEOUT = 5
@@ -82,9 +89,15 @@ def load():
     lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_causal_features.argtypes = fwd
     lib.la_forward_causal_poly2.argtypes = fwd
+    lib.la_forward_noncausal_poly2.argtypes = fwd
+    lib.la_forward_causal_poly2_state.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_decode_step_poly2.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.la_poly2_state_floats.argtypes = [i64, i64]
+    lib.la_poly2_state_floats.restype = i64
     lib.la_rff_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     for f in ("la_forward_causal", "la_forward_causal_noalloc", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
-              "la_forward_causal_poly2",
+              "la_forward_causal_poly2", "la_forward_causal_poly2_state", "la_forward_noncausal_poly2",
+              "la_decode_step_poly2",
               "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step"):
         getattr(lib, f).restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
@@ -181,7 +194,7 @@ def _forward(func: str, op: int, q, k, v, out, workspace):
         out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
     _dev(q, out)
     ws, wsb = _ws(op, B, H, N, D, M, q.dtype, workspace, dev)
-    if op == LA_OP_FWD_CAUSAL_POLY2:
+    if op in (LA_OP_FWD_CAUSAL_POLY2, LA_OP_FWD_NONCAUSAL_POLY2):
         _check(func, getattr(load(), func)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, M,
                                            _DT[q.dtype], ws.data_ptr(), wsb, _stream(dev)))
         return out
@@ -254,6 +267,64 @@ def la_forward_causal_features(fq, fk, v, out=None, workspace=None):
 def la_forward_causal_poly2(q, k, v, out=None, workspace=None):
     """Causal attention with the degree-2 polynomial kernel (q . k)^2 (D, M in {32, 64}); returns out [B,H,N,M]."""
     return _forward("la_forward_causal_poly2", LA_OP_FWD_CAUSAL_POLY2, q, k, v, out, workspace)
+
+
+def la_forward_noncausal_poly2(q, k, v, out=None, workspace=None):
+    """Non-causal attention with the degree-2 polynomial kernel; returns out [B,H,N,M]."""
+    return _forward("la_forward_noncausal_poly2", LA_OP_FWD_NONCAUSAL_POLY2, q, k, v, out, workspace)
+
+
+def la_poly2_state_floats(D: int, M: int) -> int:
+    """Floats of one (b, h)'s polynomial-kernel state (0 if D, M are not supported)."""
+    return int(load().la_poly2_state_floats(int(D), int(M)))
+
+
+def la_forward_causal_poly2_state(q, k, v, state_final=None, out=None, workspace=None):
+    """la_forward_causal_poly2 that also returns each (b, h)'s state after its last
+    token ([B,H,la_poly2_state_floats(D,M)] float32, opaque), for la_decode_step_poly2."""
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k: [B,H,N,D]; v: [B,H,N,M]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    nst = la_poly2_state_floats(D, M)
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    if state_final is None:
+        state_final = torch.empty((B, H, max(nst, 1)), dtype=torch.float32, device=dev)
+    if state_final.dtype != torch.float32 or tuple(state_final.shape) != (B, H, nst) or \
+            not state_final.is_contiguous():
+        raise ValueError(f"state_final: contiguous float32 [B,H,{nst}]")
+    _dev(q, out, state_final)
+    ws, wsb = _ws(LA_OP_FWD_CAUSAL_POLY2, B, H, N, D, M, q.dtype, workspace, dev)
+    _check("la_forward_causal_poly2_state",
+           load().la_forward_causal_poly2_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                state_final.data_ptr(), B, H, N, D, M, _DT[q.dtype], ws.data_ptr(),
+                                                wsb, _stream(dev)))
+    return out, state_final
+
+
+def la_decode_step_poly2(q, k, v, state, out=None):
+    """One polynomial-kernel decode step: q,k [B,H,D]; v [B,H,M]; state [B,H,la_poly2_state_floats(D,M)]
+    float32 updated in place (zeros: empty prefix); returns out [B,H,M]."""
+    dev = _dev(q, k, v, state)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k: [B,H,D]; v: [B,H,M]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT or state.dtype != torch.float32:
+        raise ValueError("q, k, v float32 or bfloat16; state float32")
+    B, H, D = q.shape
+    M = v.shape[-1]
+    nst = la_poly2_state_floats(D, M)
+    if tuple(state.shape) != (B, H, nst) or not state.is_contiguous():
+        raise ValueError(f"state: contiguous float32 [B,H,{nst}]")
+    if out is None:
+        out = torch.empty((B, H, M), dtype=q.dtype, device=dev)
+    _check("la_decode_step_poly2", load().la_decode_step_poly2(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                               state.data_ptr(), out.data_ptr(), B, H, D, M,
+                                                               _DT[q.dtype], _stream(dev)))
+    return out
 
 
 def la_rff_features(x, omega, bias, out=None):

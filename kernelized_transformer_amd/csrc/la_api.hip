@@ -192,9 +192,10 @@ la_status_t la_forward_causal_features(const void *fq, const void *fk, const voi
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
-                                    int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+// The polynomial forwards: shapes, buffers and workspace, then the launch.
+static la_status_t poly_forward(bool causal, const void *q, const void *k, const void *v, void *out,
+                                float *state_final, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                la_dtype_t dt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     la_status_t st = check_shape(B, H, N, D, M, dt);
     if (st != LA_OK) return st;
     if (!la::poly_head_sizes(D, M)) return LA_ERR_UNSUPPORTED;
@@ -202,15 +203,55 @@ la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v,
     const int64_t BH = B * H;
     const Span in[3] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
                         span(v, size_t(BH * N * M) * es)};
-    const Span o[1] = {span(out, size_t(BH * N * M) * es)};
-    if ((st = check_buffers(in, 3, o, 1)) != LA_OK) return st;
-    const Span all[4] = {in[0], in[1], in[2], o[0]};
-    if ((st = check_workspace(workspace, workspace_bytes, la::poly_workspace_bytes(BH, N, D, M), all, 4)) != LA_OK)
+    const Span o[2] = {span(out, size_t(BH * N * M) * es),
+                       span(state_final, size_t(BH * la::poly_state_floats(D, M)) * 4)};
+    const int no = state_final ? 2 : 1;
+    if ((st = check_buffers(in, 3, o, no)) != LA_OK) return st;
+    const Span all[5] = {in[0], in[1], in[2], o[0], o[1]};
+    if ((st = check_workspace(workspace, workspace_bytes, la::poly_workspace_bytes(BH, N, D, M, causal), all,
+                              3 + no)) != LA_OK)
         return st;
-    const hipError_t e = la::launch_poly_forward(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, BH, N, D, M,
-                                                 static_cast<float *>(workspace), stream);
+    const hipError_t e = la::launch_poly_forward(causal, dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, out, state_final, BH,
+                                                 N, D, M, static_cast<float *>(workspace), stream);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
+
+la_status_t la_forward_causal_poly2(const void *q, const void *k, const void *v, void *out, int64_t B, int64_t H,
+                                    int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    return poly_forward(true, q, k, v, out, nullptr, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
+}
+
+la_status_t la_forward_causal_poly2_state(const void *q, const void *k, const void *v, void *out,
+                                          float *state_final, int64_t B, int64_t H, int64_t N, int64_t D,
+                                          int64_t M, la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+    if (state_final == nullptr) return LA_ERR_INVALID_ARGUMENT;
+    return poly_forward(true, q, k, v, out, state_final, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
+}
+
+la_status_t la_forward_noncausal_poly2(const void *q, const void *k, const void *v, void *out, int64_t B,
+                                       int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return poly_forward(false, q, k, v, out, nullptr, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
+}
+
+la_status_t la_decode_step_poly2(const void *q, const void *k, const void *v, float *state, void *out, int64_t B,
+                                 int64_t H, int64_t D, int64_t M, la_dtype_t dt, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, 1, D, M, dt);
+    if (st != LA_OK) return st;
+    if (!la::poly_head_sizes(D, M)) return LA_ERR_UNSUPPORTED;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    if (BH > int64_t(1) << 31) return LA_ERR_UNSUPPORTED;   // one workgroup per stream
+    const Span in[3] = {span(q, size_t(BH * D) * es), span(k, size_t(BH * D) * es), span(v, size_t(BH * M) * es)};
+    const Span o[2] = {span(state, size_t(BH * la::poly_state_floats(D, M)) * 4), span(out, size_t(BH * M) * es)};
+    if ((st = check_buffers(in, 3, o, 2)) != LA_OK) return st;
+    const hipError_t e = la::launch_poly_decode(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, state, out, BH, D, M, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+int64_t la_poly2_state_floats(int64_t D, int64_t M) { return la::poly_state_floats(D, M); }
 
 la_status_t la_rff_features(const void *x, const float *omega, const float *bias, void *out, int64_t B, int64_t H,
                             int64_t N, int64_t D, int64_t R, la_dtype_t dt, hipStream_t stream) {
@@ -299,7 +340,9 @@ size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D,
     case LA_OP_BWD_NONCAUSAL:
         return la::backward_noncausal_workspace_bytes(B * H, N, D, M);
     case LA_OP_FWD_CAUSAL_POLY2:
-        return la::poly_workspace_bytes(B * H, N, D, M);
+        return la::poly_head_sizes(D, M) ? la::poly_workspace_bytes(B * H, N, D, M, true) : 0;
+    case LA_OP_FWD_NONCAUSAL_POLY2:
+        return la::poly_head_sizes(D, M) ? la::poly_workspace_bytes(B * H, N, D, M, false) : 0;
     }
     return 0;
 }

@@ -195,9 +195,17 @@ hipError_t launch_rff_features(int dt, const void *x, const float *omega, const 
 // {32, 64}; workspace: one fp32 record of the segment's feature state and
 // D x D normalizer per segment (256 bytes when a (b, h) is one segment).
 bool poly_head_sizes(int64_t D, int64_t M);
-size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M);
-hipError_t launch_poly_forward(int dt, const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N,
-                               int64_t D, int64_t M, float *ws, hipStream_t s);
+size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, bool causal);
+// Floats of one (b, h)'s state (feature tiles, then the Z tiles); 0 if D, M
+// are not supported.
+int64_t poly_state_floats(int64_t D, int64_t M);
+// causal or not; state_final (causal only, may be null): the state after the
+// last token of every (b, h), poly_state_floats(D, M) floats each.
+hipError_t launch_poly_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
+                               float *state_final, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+                               hipStream_t s);
+hipError_t launch_poly_decode(int dt, const void *q, const void *k, const void *v, float *state, void *out,
+                              int64_t BH, int64_t D, int64_t M, hipStream_t s);
 
 // The generic forward (la_generic.hip: segment sums, scan, outputs, with V
 // and out cut into 16-column groups); its workspace is one row-major record

@@ -154,13 +154,14 @@ template <int NL, int F> __device__ __forceinline__ f32x4 phi_k(const f32x4 (&ow
 // features come out halved: every partial readout is doubled when the
 // partials are combined, which counts the off-diagonal pairs twice and the
 // diagonal once.
-template <int NL, int F> __device__ __forceinline__ f32x4 phi_q(const float (&qr)[16 * NL], bool glo) {
+template <int NL, int F, bool HALF_DIAG = true>
+__device__ __forceinline__ f32x4 phi_q(const float (&qr)[16 * NL], bool glo) {
     constexpr PolyTile t = poly_tile<NL>(F);
     f32x4 p;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         if constexpr (t.kind == 0) {
-            p[r] = qr[r + 16 * t.i] * (0.5f * qr[r + 16 * t.i]);
+            p[r] = qr[r + 16 * t.i] * (HALF_DIAG ? 0.5f * qr[r + 16 * t.i] : qr[r + 16 * t.i]);
         } else if constexpr (t.kind == 1) {
             p[r] = qr[r + 16 * t.i] * qr[r + 16 * t.j];
         } else if constexpr (t.kind == 2) {
@@ -695,8 +696,11 @@ __global__ __launch_bounds__((64 * PolyCfg<T, D, M>::NWAVE)) void k_poly_segment
     poly_dispatch<C::W>(wave, [&](auto wi) { segment_state_wave<T, D, M, decltype(wi)::value>(K, V, rec, t_begin, t_end, mb, sm); });
 }
 
-template <typename T, int D, int M, int WI>
-__device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, T *O, const float *rec,
+// CAUSAL false: the non-causal form, every token read out from the (b, h)
+// total in rec, with neither the intra-chunk part nor state updates.  fin:
+// where to store the state after the segment's last token (or null).
+template <typename T, int D, int M, int WI, bool CAUSAL>
+__device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, T *O, const float *rec, float *fin,
                                             int64_t t_begin, int64_t t_end, int mb,
                                             PolyShared<T, D, M, PolyCfg<T, D, M>::TT, true> &sm) {
     typedef PolyCfg<T, D, M> C;
@@ -732,6 +736,8 @@ __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, 
             for (int tt = 0; tt < TT; ++tt) acc[mt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         float dpart[TT], pden[TT] = {};
         f32x4 intra[OWN.n > 0 ? OWN.n : 1];
+#pragma unroll
+        for (int u = 0; u < OWN.n; ++u) intra[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         Fr sb[PW::NF][MT];   // filled only when the state fragments are kept
         if constexpr (C::SB_CACHE) w.state_frags(sb);
 #pragma unroll
@@ -744,7 +750,7 @@ __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, 
             bool have = false;
 #pragma unroll
             for (int u = 0; u < OWN.n; ++u) {
-                if (OWN.tt[u] != tt) continue;
+                if (!CAUSAL || OWN.tt[u] != tt) continue;
                 if (!have) {
                     pden[tt] = intra_p<T, D, TT>(pf, sm, buf, qr, tt);
                     have = true;
@@ -762,7 +768,7 @@ __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, 
         }
 
         // 2. state update
-        {
+        if constexpr (CAUSAL) {
             Fr kt[TT][C::NL];
             f32x4 own[TT][C::NL];
             w.read_k(sm, buf, kt, own);
@@ -798,16 +804,17 @@ __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, 
                 store4<T>(O + t * M + m0 + 16 * mt + 4 * g, IO<T>::from_f32(num * __builtin_amdgcn_rcpf(d)));
         }
     }
+    if (fin) w.store_state(fin, mb);
 }
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__((64 * PolyCfg<T, D, M>::NWAVE)) void k_poly_output(const T *__restrict__ q,
                                                                                const T *__restrict__ k,
                                                                                const T *__restrict__ v,
                                                                                T *__restrict__ out,
                                                                                const float *__restrict__ ws,
-                                                                               int64_t N, int64_t nseg,
-                                                                               int64_t seg_tokens) {
+                                                                               float *__restrict__ fin, int64_t N,
+                                                                               int64_t nseg, int64_t seg_tokens) {
     typedef PolyCfg<T, D, M> C;
     __shared__ PolyShared<T, D, M, C::TT, true> sm;
     const int mb = blockIdx.x % C::NMB;
@@ -817,13 +824,18 @@ __global__ __launch_bounds__((64 * PolyCfg<T, D, M>::NWAVE)) void k_poly_output(
     const T *K = k + bh * N * D;
     const T *V = v + bh * N * M;
     T *O = out + bh * N * M;
-    const float *rec = ws ? ws + (bh * nseg + seg) * C::REC : nullptr;
+    // causal: the segment's exclusive prefix (none: zero); non-causal: the
+    // (b, h) total, in its first record
+    const float *rec = CAUSAL ? (ws ? ws + (bh * nseg + seg) * C::REC : nullptr) : ws + bh * nseg * C::REC;
+    float *f = (CAUSAL && fin && seg == nseg - 1) ? fin + bh * C::REC : nullptr;
     const int wave = threadIdx.x >> 6;
     if (C::PROD && wave == C::W) {
         produce_chunks<T, D, M, true, C::TT, C::PF>(Q, K, V, t_begin, t_end, mb * C::MB, sm);
         return;
     }
-    poly_dispatch<C::W>(wave, [&](auto wi) { output_wave<T, D, M, decltype(wi)::value>(Q, K, V, O, rec, t_begin, t_end, mb, sm); });
+    poly_dispatch<C::W>(wave, [&](auto wi) {
+        output_wave<T, D, M, decltype(wi)::value, CAUSAL>(Q, K, V, O, rec, f, t_begin, t_end, mb, sm);
+    });
 }
 
 struct PolyPlan {
@@ -833,8 +845,10 @@ struct PolyPlan {
 
 // Enough (segment, column block) workgroups to give every CU one: a
 // workgroup fills a CU (its wavefronts hold the state in registers).
-// Segments are whole chunks of the kernels' chunk length.
-inline PolyPlan make_poly_plan(int64_t BH, int64_t N, int64_t D, int64_t M, int cus) {
+// Segments are whole chunks of the kernels' chunk length.  The causal form
+// needs records only with several segments; the non-causal one always keeps
+// the (b, h) total.
+inline PolyPlan make_poly_plan(int64_t BH, int64_t N, int64_t D, int64_t M, int cus, bool causal) {
     PolyPlan p;
     const int64_t NL = D / 16, FT = NL * (NL + 1) / 2 + 15 * NL * NL / 2;
     const int64_t chunk = 128;   // a multiple of both kernels' chunk lengths
@@ -845,53 +859,201 @@ inline PolyPlan make_poly_plan(int64_t BH, int64_t N, int64_t D, int64_t M, int 
     nseg = std::max<int64_t>(1, std::min<int64_t>({nseg, nch, kMaxSegPerHead}));
     p.seg_tokens = ceil_div(nch, nseg) * chunk;
     p.nseg = ceil_div(N, p.seg_tokens);
-    if (p.nseg > 1) p.ws_bytes = align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
+    if (p.nseg > 1 || !causal) p.ws_bytes = align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
     return p;
 }
 
 template <typename T, int D, int M>
-static hipError_t run_poly(const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N, float *ws,
-                           hipStream_t s) {
+static hipError_t run_poly(bool causal, const void *q, const void *k, const void *v, void *out, float *fin,
+                           int64_t BH, int64_t N, float *ws, hipStream_t s) {
     typedef PolyCfg<T, D, M> C;
-    const PolyPlan p = make_poly_plan(BH, N, D, M, device_cus());
+    const PolyPlan p = make_poly_plan(BH, N, D, M, device_cus(), causal);
     if (p.seg_tokens % C::CH != 0 || p.seg_tokens % (16 * C::TT1) != 0) return hipErrorInvalidValue;
     const dim3 grid(unsigned(BH * p.nseg * C::NMB)), block(64 * C::NWAVE);
     hipError_t e;
-    if (p.nseg > 1) {
+    if (p.nseg > 1 || !causal) {
         hipLaunchKernelGGL((k_poly_segment_state<T, D, M>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N,
                            p.nseg, p.seg_tokens);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_scan(ws, BH, p.nseg, p.rec, 0, s)) != hipSuccess) return e;
+        if (p.nseg > 1 && (e = launch_scan(ws, BH, p.nseg, p.rec, causal ? 0 : 1, s)) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_poly_output<T, D, M>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v, (T *)out,
-                       p.nseg > 1 ? (const float *)ws : nullptr, N, p.nseg, p.seg_tokens);
+    if (causal)
+        hipLaunchKernelGGL((k_poly_output<T, D, M, true>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (T *)out, p.nseg > 1 ? (const float *)ws : nullptr, fin, N, p.nseg,
+                           p.seg_tokens);
+    else
+        hipLaunchKernelGGL((k_poly_output<T, D, M, false>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (T *)out, (const float *)ws, (float *)nullptr, N, p.nseg, p.seg_tokens);
     return hipGetLastError();
 }
 
+// ---- decode -------------------------------------------------------------------
+// One step for B*H independent streams, one workgroup of four wavefronts per
+// stream, the state in the record layout (feature tiles, then the Z tiles;
+// each tile 64 lanes x 4 floats in the accumulator order of the kernels
+// above):  S_f += phi(k)_f v^T and Z += k k^T, then, read after the update,
+//   out = 2 phi'(q) . S / q^T Z q,
+// phi' being phi with the diagonal features halved (the count of each
+// unordered pair, as in the forwards).  The step reads and writes the state
+// once: it is bound by memory bandwidth, plain fp32 FMAs on the VALU.
+constexpr int kPolyDecodeWaves = 4;
+
+template <typename T, int D> __device__ __forceinline__ void load_rot(float (&xr)[D], const T *x) {
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+        for (int x0 = 0; x0 < 16; x0 += 4) {
+            const f32x4 y = IO<T>::to_f32(load4<T>(x + 16 * i + 4 * ((g + x0 / 4) & 3)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xr[16 * i + x0 + e] = y[e];
+        }
+}
+
+template <typename T, int D, int M, int F>
+__device__ __forceinline__ void decode_tiles(float *st, const float (&kr)[D], const float (&qr)[D],
+                                             const float (&vm)[M / 16], float (&num)[M / 16], int wave, bool glo) {
+    constexpr int NL = D / 16, FT = poly_tiles<NL>(), MT = M / 16;
+    if constexpr (F < FT) {
+        if (F % kPolyDecodeWaves == wave) {
+            const f32x4 pk = phi_q<NL, F, false>(kr, glo), pq = phi_q<NL, F, true>(qr, glo);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x4 *p = reinterpret_cast<f32x4 *>(st + int64_t(F * MT + mt) * 256) + lane_id();
+                f32x4 x = *p;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[r] += pk[r] * vm[mt];
+                    num[mt] += pq[r] * x[r];
+                }
+                *p = x;
+            }
+        }
+        decode_tiles<T, D, M, F + 1>(st, kr, qr, vm, num, wave, glo);
+    }
+}
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__(64 * kPolyDecodeWaves) void k_poly_decode(const T *__restrict__ q,
+                                                                       const T *__restrict__ k,
+                                                                       const T *__restrict__ v,
+                                                                       float *__restrict__ state,
+                                                                       T *__restrict__ out) {
+    constexpr int NL = D / 16, FT = poly_tiles<NL>(), MT = M / 16, NZ = NL * NL;
+    constexpr int64_t REC = int64_t(FT * MT + NZ) * 256;
+    const int64_t s = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = lane_id(), c = lane & 15, g = lane >> 4;
+    float *st = state + s * REC;
+    const T *qs = q + s * D, *ks = k + s * D;
+    float qr[D], kr[D];
+    load_rot<T, D>(qr, qs);
+    load_rot<T, D>(kr, ks);
+    float vm[MT], num[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        vm[mt] = (float)v[s * M + 16 * mt + c];
+        num[mt] = 0.f;
+    }
+    decode_tiles<T, D, M, 0>(st, kr, qr, vm, num, wave, g < 2);
+
+    // Z tiles: lane (c, g) element r of tile (x, y) is Z[16x + 4g + r][16y + c]
+    float den = 0.f;
+#pragma unroll
+    for (int z = 0; z < NZ; ++z) {
+        if (z % kPolyDecodeWaves != wave) continue;
+        const int x = z % NL, y = z / NL;
+        const float ky = (float)ks[16 * y + c], qy = (float)qs[16 * y + c];
+        f32x4 *p = reinterpret_cast<f32x4 *>(st + int64_t(FT * MT + z) * 256) + lane;
+        f32x4 t = *p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            t[r] += kr[16 * x + r] * ky;
+            den += t[r] * qr[16 * x + r] * qy;
+        }
+        *p = t;
+    }
+
+    // numerators: lanes (c, 0..3) share column c; denominator: every lane
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        num[mt] += __shfl_xor(num[mt], 16);
+        num[mt] += __shfl_xor(num[mt], 32);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off);
+    __shared__ float part[kPolyDecodeWaves][M + 1];
+    if (g == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) part[wave][16 * mt + c] = num[mt];
+    }
+    if (lane == 0) part[wave][M] = den;
+    __syncthreads();
+    if (wave == 0 && lane < M) {
+        float n = 0.f, d = 0.f;
+#pragma unroll
+        for (int w = 0; w < kPolyDecodeWaves; ++w) {
+            n += part[w][lane];
+            d += part[w][M];
+        }
+        out[s * M + lane] = (T)(2.f * n * __builtin_amdgcn_rcpf(d));
+    }
+}
+
 template <typename T, int D>
-static hipError_t run_poly_m(const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N, int64_t M,
-                             float *ws, hipStream_t s) {
-    if (M == 32) return run_poly<T, D, 32>(q, k, v, out, BH, N, ws, s);
-    if (M == 64) return run_poly<T, D, 64>(q, k, v, out, BH, N, ws, s);
+static hipError_t run_poly_m(bool causal, const void *q, const void *k, const void *v, void *out, float *fin,
+                             int64_t BH, int64_t N, int64_t M, float *ws, hipStream_t s) {
+    if (M == 32) return run_poly<T, D, 32>(causal, q, k, v, out, fin, BH, N, ws, s);
+    if (M == 64) return run_poly<T, D, 64>(causal, q, k, v, out, fin, BH, N, ws, s);
     return hipErrorInvalidValue;
+}
+
+template <typename T, int D, int M>
+static hipError_t decode_poly(const void *q, const void *k, const void *v, float *state, void *out, int64_t BH,
+                              hipStream_t s) {
+    hipLaunchKernelGGL((k_poly_decode<T, D, M>), dim3(unsigned(BH)), dim3(64 * kPolyDecodeWaves), 0, s,
+                       (const T *)q, (const T *)k, (const T *)v, state, (T *)out);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t decode_poly_dm(const void *q, const void *k, const void *v, float *state, void *out, int64_t BH,
+                                 int64_t D, int64_t M, hipStream_t s) {
+    if (D == 32) return M == 32 ? decode_poly<T, 32, 32>(q, k, v, state, out, BH, s)
+                                : decode_poly<T, 32, 64>(q, k, v, state, out, BH, s);
+    return M == 32 ? decode_poly<T, 64, 32>(q, k, v, state, out, BH, s)
+                   : decode_poly<T, 64, 64>(q, k, v, state, out, BH, s);
 }
 
 } // namespace
 
 bool poly_head_sizes(int64_t D, int64_t M) { return (D == 32 || D == 64) && (M == 32 || M == 64); }
 
-size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
-    return make_poly_plan(BH, N, D, M, device_cus()).ws_bytes;
+int64_t poly_state_floats(int64_t D, int64_t M) {
+    if (!poly_head_sizes(D, M)) return 0;
+    const int64_t NL = D / 16, FT = NL * (NL + 1) / 2 + 15 * NL * NL / 2;
+    return (FT * (M / 16) + NL * NL) * 256;
 }
 
-hipError_t launch_poly_forward(int dt, const void *q, const void *k, const void *v, void *out, int64_t BH, int64_t N,
-                               int64_t D, int64_t M, float *ws, hipStream_t s) {
+size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, bool causal) {
+    return make_poly_plan(BH, N, D, M, device_cus(), causal).ws_bytes;
+}
+
+hipError_t launch_poly_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
+                               float *state_final, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
+                               hipStream_t s) {
     if (!poly_head_sizes(D, M)) return hipErrorInvalidValue;
     if (dt == 0)
-        return D == 32 ? run_poly_m<float, 32>(q, k, v, out, BH, N, M, ws, s)
-                       : run_poly_m<float, 64>(q, k, v, out, BH, N, M, ws, s);
-    return D == 32 ? run_poly_m<bf16, 32>(q, k, v, out, BH, N, M, ws, s)
-                   : run_poly_m<bf16, 64>(q, k, v, out, BH, N, M, ws, s);
+        return D == 32 ? run_poly_m<float, 32>(causal, q, k, v, out, state_final, BH, N, M, ws, s)
+                       : run_poly_m<float, 64>(causal, q, k, v, out, state_final, BH, N, M, ws, s);
+    return D == 32 ? run_poly_m<bf16, 32>(causal, q, k, v, out, state_final, BH, N, M, ws, s)
+                   : run_poly_m<bf16, 64>(causal, q, k, v, out, state_final, BH, N, M, ws, s);
+}
+
+hipError_t launch_poly_decode(int dt, const void *q, const void *k, const void *v, float *state, void *out,
+                              int64_t BH, int64_t D, int64_t M, hipStream_t s) {
+    if (!poly_head_sizes(D, M)) return hipErrorInvalidValue;
+    if (dt == 0) return decode_poly_dm<float>(q, k, v, state, out, BH, D, M, s);
+    return decode_poly_dm<bf16>(q, k, v, state, out, BH, D, M, s);
 }
 
 } // namespace la

@@ -53,10 +53,11 @@ def _bind(lib):
     lib.orc_rff_features.argtypes = [d, d, d, d, i64, i64, i64]
     lib.orc_forward_causal_features.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_forward_causal_poly2.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
-    lib.orc_forward_causal_poly2_rows.argtypes = [d, d, d, ctypes.POINTER(i64), d, i64, i64, i64, i64, i64, i64]
+    lib.orc_forward_noncausal_poly2.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
+    lib.orc_forward_poly2_rows.argtypes = [d, d, d, ctypes.POINTER(i64), d, i64, i64, i64, i64, i64, i64, i64]
     for f in ("orc_feature_map", "orc_forward_causal", "orc_forward_noncausal",
               "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step", "orc_rff_features",
-              "orc_forward_causal_features", "orc_forward_causal_poly2", "orc_forward_causal_poly2_rows"):
+              "orc_forward_causal_features", "orc_forward_causal_poly2", "orc_forward_noncausal_poly2", "orc_forward_poly2_rows"):
         getattr(lib, f).restype = None
     return lib
 
@@ -199,10 +200,20 @@ def forward_causal_poly2(q, k, v, lib=None):
     return out
 
 
-def forward_causal_poly2_rows(q, k, v, rows, lib=None):
-    """Rows ``rows`` of the degree-2 polynomial causal forward, each summed
-    directly from the kernel (q_i . k_j)^2 over j <= i.  Returns
-    [B,H,len(rows),M]."""
+def forward_noncausal_poly2(q, k, v, lib=None):
+    """Non-causal attention with the degree-2 polynomial kernel (q . k)^2, through
+    its explicit D^2 feature map.  q,k: [B,H,N,D]; v: [B,H,N,M]."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (B, H, N, M)
+    out = np.empty((B, H, N, M), np.float64)
+    lib.orc_forward_noncausal_poly2(_p(q), _p(k), _p(v), _p(out), B, H, N, D, M)
+    return out
+
+
+def _poly2_rows(q, k, v, rows, causal, lib):
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, D = q.shape
@@ -211,9 +222,20 @@ def forward_causal_poly2_rows(q, k, v, rows, lib=None):
     assert k.shape == q.shape and v.shape == (B, H, N, M) and r.ndim == 1
     assert r.size == 0 or (r.min() >= 0 and r.max() < N)
     out = np.empty((B, H, r.size, M), np.float64)
-    lib.orc_forward_causal_poly2_rows(_p(q), _p(k), _p(v), r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                      _p(out), B, H, N, D, M, r.size)
+    lib.orc_forward_poly2_rows(_p(q), _p(k), _p(v), r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                               _p(out), B, H, N, D, M, r.size, 1 if causal else 0)
     return out
+
+
+def forward_causal_poly2_rows(q, k, v, rows, lib=None):
+    """Rows ``rows`` of the degree-2 polynomial causal forward, each summed
+    directly from the kernel (q_i . k_j)^2 over j <= i.  Returns [B,H,len(rows),M]."""
+    return _poly2_rows(q, k, v, rows, True, lib)
+
+
+def forward_noncausal_poly2_rows(q, k, v, rows, lib=None):
+    """Rows of the non-causal polynomial forward, summed directly over all j."""
+    return _poly2_rows(q, k, v, rows, False, lib)
 
 
 def decode_step(q, k, v, S, Z, lib=None):

@@ -435,26 +435,68 @@ void orc_forward_causal_poly2(const double *q, const double *k, const double *v,
 }
 
 /*
- * Selected rows of the same causal forward, each from the kernel itself
- * ([summary] 3.2.1; the attention form sim(q_i, k_j) summed over j <= i):
- *   out_i = sum_{j<=i} (q_i . k_j)^2 v_j / sum_{j<=i} (q_i . k_j)^2,
+ * Non-causal forward with the same kernel ([summary] 3.2.1; every key
+ * attends): S = sum_j phi(K_j) V_j^T and Z = sum_j phi(K_j) over all j with
+ * phi(x) = vec(x x^T), then out_i = S^T phi(Q_i) / (phi(Q_i) . Z).
+ */
+void orc_forward_noncausal_poly2(const double *q, const double *k, const double *v, double *out,
+                                 int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H, F = D * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M;
+        double *O = out + bh * N * M;
+        double *S = (double *)calloc((size_t)(F * M), sizeof(double));
+        double *Z = (double *)calloc((size_t)F, sizeof(double));
+        double *pf = (double *)malloc((size_t)F * sizeof(double));
+        for (int64_t j = 0; j < N; ++j) {
+            for (int64_t a = 0; a < D; ++a)
+                for (int64_t b = 0; b < D; ++b) pf[a * D + b] = K[j * D + a] * K[j * D + b];
+            for (int64_t f = 0; f < F; ++f) {
+                for (int64_t m = 0; m < M; ++m) S[f * M + m] += pf[f] * V[j * M + m];
+                Z[f] += pf[f];
+            }
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t a = 0; a < D; ++a)
+                for (int64_t b = 0; b < D; ++b) pf[a * D + b] = Q[i * D + a] * Q[i * D + b];
+            double dd = 0.0;
+            for (int64_t f = 0; f < F; ++f) dd += pf[f] * Z[f];
+            for (int64_t m = 0; m < M; ++m) {
+                double n = 0.0;
+                for (int64_t f = 0; f < F; ++f) n += pf[f] * S[f * M + m];
+                O[i * M + m] = n / dd;
+            }
+        }
+        free(S); free(Z); free(pf);
+    }
+}
+
+/*
+ * Selected rows of the polynomial forwards, each from the kernel itself
+ * ([summary] 3.2.1; the attention form sim(q_i, k_j) summed over j <= i, or
+ * over all j when causal is 0):
+ *   out_i = sum_j (q_i . k_j)^2 v_j / sum_j (q_i . k_j)^2,
  * O(i (D + M)) per row, for checking long sequences at sampled rows.
  * rows: nrows token indices in [0, N); out: [B][H][nrows][M].
  */
-void orc_forward_causal_poly2_rows(const double *q, const double *k, const double *v, const int64_t *rows,
-                                   double *out, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
-                                   int64_t nrows)
+void orc_forward_poly2_rows(const double *q, const double *k, const double *v, const int64_t *rows,
+                            double *out, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                            int64_t nrows, int64_t causal)
 {
     const int64_t BH = B * H;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int64_t bh = 0; bh < BH; ++bh)
         for (int64_t r = 0; r < nrows; ++r) {
             const int64_t i = rows[r];
+            const int64_t last = causal ? i : N - 1;
             const double *qi = q + (bh * N + i) * D;
             double *o = out + (bh * nrows + r) * M;
             double den = 0.0;
             for (int64_t m = 0; m < M; ++m) o[m] = 0.0;
-            for (int64_t j = 0; j <= i; ++j) {
+            for (int64_t j = 0; j <= last; ++j) {
                 const double *kj = k + (bh * N + j) * D, *vj = v + (bh * N + j) * M;
                 double dot = 0.0;
                 for (int64_t a = 0; a < D; ++a) dot += qi[a] * kj[a];

@@ -33,7 +33,7 @@ int main(void) {
                                  {64, 16, 512, 32, 64},  {1, 2, 40000, 64, 64}};
     for (size_t i = 0; i < sizeof shapes / sizeof shapes[0]; ++i) {
         const int64_t *s = shapes[i];
-        for (int op = 0; op <= 4; ++op)
+        for (int op = 0; op <= 5; ++op)
             for (int dt = 0; dt <= 1; ++dt) {
                 size_t n = la_workspace_size((la_op_t)op, s[0], s[1], s[2], s[3], s[4], (la_dtype_t)dt);
                 if (n == 0 || n % 256 != 0) {
@@ -77,6 +77,17 @@ int main(void) {
            LA_ERR_INVALID_ARGUMENT);
     EXPECT(la_forward_causal_poly2(P(0), P(1), P(2), P(3), 1, 1, 8, 48, 32, LA_DTYPE_BF16, P(4), 1 << 20, 0),
            LA_ERR_UNSUPPORTED);
+    EXPECT(la_forward_noncausal_poly2(P(0), P(1), P(2), P(3), 1, 1, 8, 32, 32, LA_DTYPE_BF16, P(4), 16, 0),
+           LA_ERR_WORKSPACE);
+    EXPECT(la_forward_causal_poly2_state(P(0), P(1), P(2), P(3), NULL, 1, 1, 8, 32, 32, LA_DTYPE_BF16, P(4),
+                                         1 << 20, 0),
+           LA_ERR_INVALID_ARGUMENT);
+    EXPECT(la_decode_step_poly2(P(0), P(1), P(2), (float *)P(3), P(3), 2, 2, 32, 32, LA_DTYPE_BF16, 0),
+           LA_ERR_INVALID_ARGUMENT);
+    EXPECT(la_decode_step_poly2(P(0), P(1), P(2), (float *)P(3), P(4), 2, 2, 48, 32, LA_DTYPE_BF16, 0),
+           LA_ERR_UNSUPPORTED);
+    EXPECT(la_poly2_state_floats(32, 32), (33 * 2 + 4) * 256);
+    EXPECT(la_poly2_state_floats(40, 32), 0);
     EXPECT(la_rff_features(P(0), (const float *)P(1), (const float *)P(2), P(0), 1, 1, 8, 32, 32, LA_DTYPE_F32, 0),
            LA_ERR_INVALID_ARGUMENT);
 

@@ -343,7 +343,9 @@ def check_forward_features(lib):
 def check_poly2(lib):
     """Degree-2 polynomial kernel: the oracle's explicit D^2 feature map
     against brute force with the kernel itself, a_ij = (q_i . k_j)^2 for
-    j <= i; N = 1 gives V_1; the last row equals the non-causal form."""
+    j <= i (all j for the non-causal form, also through the feature map); N = 1
+    gives V_1; the last causal row equals the non-causal form; sampled rows
+    match the full passes."""
     for s, (B, H, N, D, M) in enumerate([(1, 2, 40, 5, 3), (2, 1, 17, 8, 6), (1, 1, 1, 4, 4), (1, 1, 64, 32, 32)]):
         q, k, v = _rand(500 + 3 * s, B, H, N, D), _rand(501 + 3 * s, B, H, N, D), _rand(502 + 3 * s, B, H, N, M)
         a = np.tril((q @ np.swapaxes(k, -1, -2)) ** 2)
@@ -357,6 +359,11 @@ def check_poly2(lib):
         rows = np.unique(np.array([0, N // 3, N // 2, N - 1]))
         sampled = oracle.forward_causal_poly2_rows(q, k, v, rows, lib=lib)
         assert _rel(sampled, ref[:, :, rows]) < 1e-12, (B, H, N, D, M, _rel(sampled, ref[:, :, rows]))
+        # the non-causal form: every key attends
+        ref_nc = (full @ v) / full.sum(-1, keepdims=True)
+        got_nc = oracle.forward_noncausal_poly2(q, k, v, lib=lib)
+        assert _rel(got_nc, ref_nc) < 1e-12, (B, H, N, D, M, _rel(got_nc, ref_nc))
+        assert _rel(oracle.forward_noncausal_poly2_rows(q, k, v, rows, lib=lib), ref_nc[:, :, rows]) < 1e-12
 
 
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,

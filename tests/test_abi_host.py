@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     for f in ("la_forward_causal", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
               "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
               "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
-              "la_forward_causal_noalloc"):
+              "la_forward_causal_noalloc", "la_forward_causal_poly2_state", "la_forward_noncausal_poly2",
+              "la_decode_step_poly2", "la_poly2_state_floats"):
         assert f in fns
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 7
+    assert la.la_abi_version() == 8
     names = [la.la_status_string(s) for s in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP",
                      "LA_ERR_TIMEOUT"]
@@ -73,6 +74,13 @@ def test_workspace_size():
     assert f(la.LA_OP_FWD_CAUSAL_POLY2, 64, 8, 256, 32, 32, torch.bfloat16) == 256
     assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 48, 64, torch.bfloat16) == 0
     assert f(la.LA_OP_FWD_CAUSAL_POLY2, 1, 2, 256, 32, 16, torch.bfloat16) == 0
+    # the non-causal polynomial form keeps the (b, h) total even with one segment
+    assert f(la.LA_OP_FWD_NONCAUSAL_POLY2, 64, 8, 256, 32, 32, torch.bfloat16) >= 64 * 8 * rec(32, 32)
+    assert f(la.LA_OP_FWD_NONCAUSAL_POLY2, 1, 2, 256, 64, 64, torch.bfloat16) >= 2 * rec(64, 64)
+    assert f(la.LA_OP_FWD_NONCAUSAL_POLY2, 1, 2, 256, 48, 64, torch.bfloat16) == 0
+    assert la.la_poly2_state_floats(32, 32) * 4 == rec(32, 32)
+    assert la.la_poly2_state_floats(64, 64) * 4 == rec(64, 64)
+    assert la.la_poly2_state_floats(48, 32) == 0 and la.la_poly2_state_floats(32, 128) == 0
     assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 40, 32, torch.float32) == 0     # unsupported D
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 128, torch.float32) > 0     # the generic path
@@ -139,6 +147,28 @@ def test_poly2_argument_errors():
     assert _fwd(lib, "la_forward_causal_poly2", q=0) == 1
     assert _fwd(lib, "la_forward_causal_poly2", out=FAKE + 64) == 1
     assert _fwd(lib, "la_forward_causal_poly2", wsb=16) == 3
+    assert _fwd(lib, "la_forward_noncausal_poly2", D=48) == 2
+    assert _fwd(lib, "la_forward_noncausal_poly2", q=FAKE + 8) == 1
+    assert _fwd(lib, "la_forward_noncausal_poly2", wsb=16) == 3          # the total needs a record
+    b = [FAKE + (i << 30) for i in range(6)]   # q k v out state ws
+
+    def fs(q=b[0], k=b[1], v=b[2], out=b[3], st=b[4], D=32, M=32, ws=b[5], wsb=1 << 30):
+        return lib.la_forward_causal_poly2_state(q, k, v, out, st, 1, 2, 64, D, M, 1, ws, wsb, None)
+    assert fs(st=0) == 1                            # the state is required
+    assert fs(st=b[4] + 8) == 1                     # misaligned
+    assert fs(st=b[0]) == 1                         # overlaps q
+    assert fs(st=b[3]) == 1                         # overlaps out
+    assert fs(D=16) == 2
+    assert fs(ws=b[4], wsb=1 << 30) == 3            # workspace overlaps the state
+
+    def dec(q=b[0], k=b[1], v=b[2], st=b[4], out=b[3], B=2, H=3, D=32, M=32, dt=1):
+        return lib.la_decode_step_poly2(q, k, v, st, out, B, H, D, M, dt, None)
+    assert dec(st=0) == 1
+    assert dec(st=b[3]) == 1                        # state overlaps out
+    assert dec(D=48) == 2
+    assert dec(M=128) == 2
+    assert dec(B=0) == 1
+    assert dec(dt=9) == 2
 
 
 def test_rff_argument_errors():

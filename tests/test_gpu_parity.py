@@ -529,6 +529,66 @@ def test_forward_causal_poly2_long_sampled(name, w, seg):
     check(f"out[{name}] rows", got[:, :, rows], ref, w.dtype, lead=3)
 
 
+NONCAUSAL_POLY_CASES = [
+    ("w1_f32", wl.WORKLOADS[1]),
+    ("d32m64_n1001_ragged_bf16", _wl(241, 2, 3, 1001, 32, 64, "bf16")),
+    ("d64m32_n700_f32", _wl(242, 1, 2, 700, 64, 32, "f32")),
+    ("d64m64_b8h8n512_single_segment_bf16", _wl(243, 8, 8, 512, 64, 64, "bf16")),
+    ("d32_n1_bf16", _wl(244, 2, 2, 1, 32, 32, "bf16")),
+]
+
+
+@pytest.mark.parametrize("name,w", NONCAUSAL_POLY_CASES, ids=[c[0] for c in NONCAUSAL_POLY_CASES])
+def test_forward_noncausal_poly2(name, w):
+    q, k, v = wl.forward_inputs(w)
+    _say(f"polynomial non-causal forward {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    out = la.la_forward_noncausal_poly2(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    check(f"out[{name}]", host(out), oracle.forward_noncausal_poly2(q, k, v), w.dtype)
+
+
+def test_forward_noncausal_poly2_long_sampled():
+    """B1 H8 N65536 D = M = 32 (several segments, their totals summed by the
+    scan): every row computed, sampled rows checked against the kernel summed
+    over all keys."""
+    w = _wl(245, 1, 8, 65536, 32, 32, "bf16")
+    q, k, v = wl.forward_inputs(w)
+    _say("polynomial non-causal forward B1 H8 N65536 D32 M32 bf16, sampled rows")
+    out = la.la_forward_noncausal_poly2(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype))
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isfinite(got).all()
+    rows = _poly_rows(w.N, 2048, 32, w.wid)
+    check("out rows", got[:, :, rows], oracle.forward_noncausal_poly2_rows(q, k, v, rows), w.dtype, lead=3)
+
+
+@pytest.mark.parametrize("D,M,dtype,n0,steps", [(32, 32, "bf16", 3000, 40), (64, 64, "f32", 777, 20),
+                                                (32, 64, "bf16", 0, 30), (64, 32, "bf16", 1, 25)],
+                         ids=["d32m32_bf16", "d64m64_f32", "d32m64_bf16_from_zero", "d64m32_bf16_one_token"])
+def test_poly2_state_then_decode(D, M, dtype, n0, steps):
+    """A prompt of n0 tokens through la_forward_causal_poly2_state, then
+    `steps` decode steps from its final state: the outputs of both equal the
+    causal forward over the whole sequence (n0 = 0: decode from a zero
+    state)."""
+    w = _wl(250 + D + M + n0 % 7, 2, 3, n0 + steps, D, M, dtype)
+    q, k, v = wl.forward_inputs(w)
+    _say(f"polynomial state + decode D{D} M{M} {dtype}: B2 H3 prompt {n0}, {steps} steps")
+    ref = oracle.forward_causal_poly2(q, k, v)
+    nst = la.la_poly2_state_floats(D, M)
+    if n0 > 0:
+        out0, state = la.la_forward_causal_poly2_state(*(dev(np.ascontiguousarray(x[:, :, :n0]), dtype)
+                                                          for x in (q, k, v)))
+    else:
+        state = torch.zeros((w.B, w.H, nst), dtype=torch.float32, device="cuda")
+    qd, kd, vd = (dev(np.ascontiguousarray(np.moveaxis(x[:, :, n0:], 2, 0)), dtype) for x in (q, k, v))
+    outs = torch.stack([la.la_decode_step_poly2(qd[t], kd[t], vd[t], state) for t in range(steps)])
+    torch.cuda.synchronize()
+    if n0 > 0:
+        check("prompt out", host(out0), ref[:, :, :n0], dtype)
+    check("decode out (per row)", host(outs), np.moveaxis(ref[:, :, n0:], 2, 0), dtype, lead=3)
+    assert nst > 0 and np.isfinite(host(state)).all()
+
+
 def test_forward_causal_longest_sequence():
     """One head of 2^20 tokens (64 workgroups of 8 wavefronts, 2048 tokens
     each), checked element by element, with its final state."""
