@@ -19,7 +19,8 @@ on, and reported next to the headline:
     workload;
   * non-causal forward on the long-sequence workload;
   * random Fourier features (R = 64) of q and k and the causal forward on them;
-  * the causal forward with the degree-2 polynomial kernel at D = M = 32;
+  * the degree-2 polynomial kernel: causal and non-causal at D = M = 32,
+    causal at D = M = 64;
   * the causal forward of the three smaller workloads;
   * the causal forward at B=1, H=8, D=M=64 bf16 for N = 512 .. 65536 (the
     sweep; --no-sweep leaves it out).
@@ -340,30 +341,50 @@ def main():
         del fq, fk
 
     if a.only in ("all", "poly"):
-        # degree-2 polynomial kernel (q . k)^2, D = M = 32, on the long-sequence length
-        wp = wl.Workload(4, "polynomial kernel, B1 H8 N65536 D=M=32 bf16", 1, 8, w4.N, 32, 32, "bf16")
-        qp, kp, vp = (to_dev(x, "bf16") for x in wl.forward_inputs(wp))
-        op = torch.empty_like(vp)
-        wsp = torch.empty(la.la_workspace_size(la.LA_OP_FWD_CAUSAL_POLY2, wp.B, wp.H, wp.N, 32, 32, torch.bfloat16),
-                          dtype=torch.uint8, device=dev)
+        # degree-2 polynomial kernel (q . k)^2 on the long-sequence length, D = M = 32 (the causal and the
+        # non-causal form) and D = M = 64.  Algorithmic flops per token*head: the recurrence on the pages'
+        # map vec(x x^T) (D^2 features): 4 D^2 (M + 1) (update and readout, numerator and normalizer);
+        # the kernels run it on the D (D + 1) / 2 distinct products, 4 D (D + 1) / 2 (M + 1) flops, which
+        # is reported beside it (executed_mfma_frac).
+        def poly_case(D, M, causal, reps):
+            wp = wl.Workload(4, f"polynomial kernel, B1 H8 N65536 D={D} M={M} bf16", 1, 8, w4.N, D, M, "bf16")
+            qp, kp, vp = (to_dev(x, "bf16") for x in wl.forward_inputs(wp))
+            op = torch.empty_like(vp)
+            opc = la.LA_OP_FWD_CAUSAL_POLY2 if causal else la.LA_OP_FWD_NONCAUSAL_POLY2
+            wsp = torch.empty(la.la_workspace_size(opc, wp.B, wp.H, wp.N, D, M, torch.bfloat16),
+                              dtype=torch.uint8, device=dev)
+            fn = lib.la_forward_causal_poly2 if causal else lib.la_forward_noncausal_poly2
 
-        def poly(i):
-            st = lib.la_forward_causal_poly2(qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), op.data_ptr(), wp.B, wp.H,
-                                             wp.N, 32, 32, la.LA_DTYPE_BF16, wsp.data_ptr(), wsp.numel(), sptr)
-            if st != 0:
-                raise la.LAError("forward_causal_poly2", st)
+            def call(i):
+                st = fn(qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), op.data_ptr(), wp.B, wp.H, wp.N, D, M,
+                        la.LA_DTYPE_BF16, wsp.data_ptr(), wsp.numel(), sptr)
+                if st != 0:
+                    raise la.LAError("forward_causal_poly2" if causal else "forward_noncausal_poly2", st)
 
-        for i in range(2):
-            poly(i)
+            for i in range(2):
+                call(i)
+            t = time_events(call, reps)
+            th = wp.B * wp.H * wp.N
+            # non-causal: the totals (update) and the readout each once per token, as in the causal form
+            flops = th * 4 * D * D * (M + 1)
+            flops_exec = th * 4 * (D * (D + 1) // 2) * (M + 1)
+            ms = t / reps * 1e3
+            del qp, kp, vp, op, wsp
+            return dict(workload=wp.name, causal=causal, ms_per_call=ms, tok_heads_per_s=th * reps / t,
+                        algorithmic_flops=flops, mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                        executed_flops=flops_exec,
+                        executed_mfma_frac=flops_exec / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+
         npl = max(5, a.steps // 2)
-        t = time_events(poly, npl)
-        th = wp.B * wp.H * wp.N
-        flops = th * (4 * 32 * 32 * (32 + 1) + 2 * 32 * 32)   # recurrence on the D^2 features
-        results["poly2_forward"] = dict(
-            workload=wp.name, ms_per_call=t / npl * 1e3, tok_heads_per_s=th * npl / t,
-            algorithmic_flops=flops, mfma_frac=flops / (t / npl) / 1e12 / BF16_PEAK_TFLOPS)
-        log(f"polynomial forward: {t / npl * 1e3:.4f} ms/call")
-        del qp, kp, vp, op, wsp
+        results["poly2_forward"] = poly_case(32, 32, True, npl)
+        results["poly2_forward"]["note"] = (
+            "mfma_frac counts the recurrence on the D^2 features of vec(x x^T); the kernels use the "
+            "D(D+1)/2 distinct products (executed_mfma_frac)")
+        log(f"polynomial forward D=M=32: {results['poly2_forward']['ms_per_call']:.4f} ms/call")
+        results["poly2_forward_noncausal"] = poly_case(32, 32, False, npl)
+        log(f"polynomial non-causal forward D=M=32: {results['poly2_forward_noncausal']['ms_per_call']:.4f} ms/call")
+        results["poly2_forward_d64"] = poly_case(64, 64, True, max(3, npl // 4))
+        log(f"polynomial forward D=M=64: {results['poly2_forward_d64']['ms_per_call']:.4f} ms/call")
 
     if a.only in ("all", "noncausal"):
         for i in range(2):
