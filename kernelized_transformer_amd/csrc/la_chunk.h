@@ -33,8 +33,8 @@ __device__ __forceinline__ void load_chunk(typename IO<T>::vec4 (&x)[TT][F / 16]
 
 // phi on load: fragments of phi(X); rows at or beyond t_end become exact
 // zeros (so they add nothing to any state or sum).
-template <typename T, int F, int TT>
-__device__ __forceinline__ void phi_frags(typename IO<T>::frag (&y)[TT][F / 16],
+template <typename T, int F, int TT, typename Fr>
+__device__ __forceinline__ void phi_frags(Fr (&y)[TT][F / 16],
                                           const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
     const int c = lane_id() & 15;
 #pragma unroll
@@ -44,7 +44,7 @@ __device__ __forceinline__ void phi_frags(typename IO<T>::frag (&y)[TT][F / 16],
         for (int ft = 0; ft < F / 16; ++ft) {
             f32x4 p = phi4(IO<T>::to_f32(x[tt][ft]));
             if (!ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
-            y[tt][ft] = IO<T>::to_frag(p);
+            y[tt][ft] = frag_from<Fr>(p);
         }
     }
 }
@@ -55,10 +55,11 @@ __device__ __forceinline__ void phi_frags(typename IO<T>::frag (&y)[TT][F / 16],
 // whenever the data is).
 __device__ __forceinline__ void value_frags_unmasked(bf16x4 &y, bf16x4 x) { y = x; }
 __device__ __forceinline__ void value_frags_unmasked(f32x4 &y, f32x4 x) { y = x; }
+__device__ __forceinline__ void value_frags_unmasked(split4 &y, f32x4 x) { y = split_f32(x); }
 
 // The loaded values as fragments, rows at or beyond t_end zeroed.
-template <typename T, int F, int TT>
-__device__ __forceinline__ void raw_frags(typename IO<T>::frag (&y)[TT][F / 16],
+template <typename T, int F, int TT, typename Fr>
+__device__ __forceinline__ void raw_frags(Fr (&y)[TT][F / 16],
                                           const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
     const int c = lane_id() & 15;
 #pragma unroll
@@ -68,15 +69,15 @@ __device__ __forceinline__ void raw_frags(typename IO<T>::frag (&y)[TT][F / 16],
         for (int ft = 0; ft < F / 16; ++ft) {
             f32x4 p = IO<T>::to_f32(x[tt][ft]);
             if (!ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
-            y[tt][ft] = IO<T>::to_frag(p);
+            y[tt][ft] = frag_from<Fr>(p);
         }
     }
 }
 
 // Query/key fragments: phi applied (PHI) or the given features as they are;
 // rows at or beyond t_end zeroed either way.
-template <typename T, int F, int TT, bool PHI>
-__device__ __forceinline__ void feat_frags(typename IO<T>::frag (&y)[TT][F / 16],
+template <typename T, int F, int TT, bool PHI, typename Fr>
+__device__ __forceinline__ void feat_frags(Fr (&y)[TT][F / 16],
                                            const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
     if constexpr (PHI)
         phi_frags<T, F, TT>(y, x, t0, t_end);
@@ -145,7 +146,6 @@ __device__ __forceinline__ void load_lines(dwordx4 (&x)[TT * F / 32], const bf16
 }
 
 // phi of 8 packed bf16 values (two per dword), rounded back to bf16.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ dwordx4 phi8(dwordx4 x) {
     dwordx4 y;
 #pragma unroll
@@ -240,33 +240,6 @@ __device__ __forceinline__ void transpose_frags(f32x4 (&yt)[TT][NF], const f32x4
 template <int NF, int TT>
 __device__ __forceinline__ void transpose_frags(bf16x4 (&yt)[TT][NF], const bf16x4 (&y)[TT][NF], lds_bf16 *stage) {
     transpose_frags_lds<NF, TT>(yt, y, stage);
-}
-
-// fp32 token-contiguous copies through LDS instead of the matrix cores (a
-// 16-byte write of each lane's 4 features, four 4-byte reads of its 4
-// tokens; exact).  The wavefront's tile holds 16 TT rows of 16 NF floats at
-// a stride of 16 NF + 4 (the four row groups a read touches then fall in
-// different banks).  Reads follow the writes in the same wavefront, so no
-// barrier is needed; the tile is private to the wavefront.
-typedef __attribute__((address_space(3))) float lds_f32;
-template <int NF, int TT> constexpr int f32_stage_floats() { return 16 * TT * (16 * NF + 4); }
-template <int NF, int TT>
-__device__ __forceinline__ void transpose_frags_f32_lds(f32x4 (&yt)[TT][NF], const f32x4 (&y)[TT][NF],
-                                                        lds_f32 *tile) {
-    constexpr int S = 16 * NF + 4;
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int ft = 0; ft < NF; ++ft)
-            *reinterpret_cast<__attribute__((address_space(3))) f32x4 *>(tile + (16 * tt + c) * S + 16 * ft + 4 * g) =
-                y[tt][ft];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int ft = 0; ft < NF; ++ft)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yt[tt][ft][r] = tile[(16 * tt + 4 * g + r) * S + 16 * ft + c];
 }
 
 // ---- state records --------------------------------------------------------

@@ -24,7 +24,8 @@
 //      it as an Acc with tokens as rows (exact: x * 1 + 0).
 //
 // bf16 operands use v_mfma_f32_16x16x32_bf16 (two tiles per instruction);
-// fp32 operands use four v_mfma_f32_16x16x4_f32.
+// fp32 operands use four v_mfma_f32_16x16x4_f32, or are split into bf16
+// parts (split4) for the bf16 instruction.
 // Accumulation is always fp32.
 #pragma once
 
@@ -34,6 +35,7 @@
 namespace la {
 
 typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -106,8 +108,52 @@ __device__ __forceinline__ void mma2(f32x4 &acc, f32x4 a0, f32x4 a1, f32x4 b0, f
     mma1(acc, a1, b1);
 }
 
+// An fp32 operand carried as two bf16 parts, x = hi + lo: hi is x rounded
+// to bf16 (RNE, 8 significant bits), lo the exact remainder x - hi rounded
+// to bf16, so that |x - hi - lo| <= 2^-16 |x|.  Products take hi*hi + lo*hi
+// + hi*lo (the dropped lo*lo is at most 2^-16 |a||b|), so each product is
+// within about 3 * 2^-16 of |a||b| (errors of random sign, which average
+// out in the sums).  On the bf16 matrix instruction a 16-deep tile costs two
+// 32-deep instructions (a pair of tiles three) instead of four 4-deep fp32
+// ones of twice the duration each.
+struct split4 {
+    bf16x4 hi, lo;
+};
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ split4 split_f32(f32x4 a) {
+    // each pair rounded once (one v_cvt_pk_bf16_f32); the fp32 values of the
+    // rounded halves are the packed word shifted / masked.  The empty asm
+    // (no instruction) keeps the compiler from re-deriving the low half with a
+    // second, single-value conversion.
+    unsigned h01 = __builtin_bit_cast(unsigned, bf16x2{(bf16)a[0], (bf16)a[1]});
+    unsigned h23 = __builtin_bit_cast(unsigned, bf16x2{(bf16)a[2], (bf16)a[3]});
+    __asm__("" : "+v"(h01), "+v"(h23));
+    const f32x4 hf = {__builtin_bit_cast(float, h01 << 16), __builtin_bit_cast(float, h01 & 0xffff0000u),
+                      __builtin_bit_cast(float, h23 << 16), __builtin_bit_cast(float, h23 & 0xffff0000u)};
+    const f32x4 r = a - hf;
+    const unsigned l01 = __builtin_bit_cast(unsigned, bf16x2{(bf16)r[0], (bf16)r[1]});
+    const unsigned l23 = __builtin_bit_cast(unsigned, bf16x2{(bf16)r[2], (bf16)r[3]});
+    return split4{__builtin_bit_cast(bf16x4, u32x2{h01, h23}), __builtin_bit_cast(bf16x4, u32x2{l01, l23})};
+}
+__device__ __forceinline__ void mma1(f32x4 &acc, split4 a, split4 b) {
+    bf16x8 a8 = __builtin_shufflevector(a.hi, a.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x8 b8 = __builtin_shufflevector(b.hi, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+    mma1(acc, a.hi, b.lo);
+}
+__device__ __forceinline__ void mma2(f32x4 &acc, split4 a0, split4 a1, split4 b0, split4 b1) {
+    bf16x8 a = __builtin_shufflevector(a0.hi, a0.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+    bf16x8 b = __builtin_shufflevector(b0.hi, b0.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    a = __builtin_shufflevector(a1.hi, a1.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+    b = __builtin_shufflevector(b1.hi, b1.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    mma2(acc, a0.hi, a1.hi, b0.lo, b1.lo);
+}
+
 __device__ __forceinline__ bf16x4 acc_to_frag(f32x4 a, bf16x4) { return IO<bf16>::to_frag(a); }
 __device__ __forceinline__ f32x4 acc_to_frag(f32x4 a, f32x4) { return a; }
+__device__ __forceinline__ split4 acc_to_frag(f32x4 a, split4) { return split_f32(a); }
 template <typename F> __device__ __forceinline__ F frag_from(f32x4 x) { return acc_to_frag(x, F{}); }
 
 template <typename F> __device__ __forceinline__ F frag_zero() { return frag_from<F>(f32x4{0.f, 0.f, 0.f, 0.f}); }

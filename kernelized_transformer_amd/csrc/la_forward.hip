@@ -46,16 +46,30 @@ template <typename T, int D, int M> constexpr int fwd_prefetch() {
 
 // ---- chunk loops ------------------------------------------------------------
 
-// Token-contiguous copies in the generic chunk loops: fp32 fragments go
-// through the wavefront's LDS area when F32_LDS (the fused forward's area
-// holds both fp32 tiles), otherwise as transpose_frags does (bf16 through
-// LDS, fp32 through an identity product).
-template <int NF, bool F32_LDS, typename Fr>
+// Token-contiguous copies in the generic chunk loops: bf16 fragments go
+// through the wavefront's LDS area (transpose_frags_lds); split fp32
+// fragments the same way, hi parts at `stage`, lo parts after them (two
+// areas of stage_elems<NF, TT>()); plain fp32 through an identity product.
+template <int NF, typename Fr>
 __device__ __forceinline__ void tokens_major(Fr (&yt)[TT][NF], const Fr (&y)[TT][NF], lds_bf16 *stage) {
-    if constexpr (F32_LDS && std::is_same<Fr, f32x4>::value)
-        transpose_frags_f32_lds<NF, TT>(yt, y, (lds_f32 *)stage);
-    else
+    if constexpr (std::is_same<Fr, split4>::value) {
+        bf16x4 h[TT][NF], l[TT][NF], ht[TT][NF], lt[TT][NF];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                h[tt][f] = y[tt][f].hi;
+                l[tt][f] = y[tt][f].lo;
+            }
+        transpose_frags_lds<NF, TT>(ht, h, stage);
+        transpose_frags_lds<NF, TT>(lt, l, stage + stage_elems<NF, TT>());
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) yt[tt][f] = split4{ht[tt][f], lt[tt][f]};
+    } else {
         transpose_frags<NF, TT>(yt, y, stage);
+    }
 }
 
 // St += sum over tokens [t_begin, t_end) of phi(K_t) [V_t, 1]^T.
@@ -63,11 +77,12 @@ __device__ __forceinline__ void tokens_major(Fr (&yt)[TT][NF], const Fr (&y)[TT]
 // always lives in buffer i % PF (a register copy between buffers would force
 // a wait on the loads in flight).
 // PHI: apply the feature map to K (otherwise K holds the features already).
-template <typename T, int D, int M, int PF, bool PHI = true, bool F32_LDS = false>
+// Fr: the operand fragment type (split4 runs fp32 data on the bf16 matrix
+// instruction; the staging areas then hold two bf16 tiles each).
+template <typename T, int D, int M, int PF, bool PHI = true, typename Fr = typename IO<T>::frag>
 __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *__restrict__ V, int64_t t_begin,
                                               int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
                                               lds_bf16 *stage_v) {
-    typedef typename IO<T>::frag Fr;
     typedef typename IO<T>::vec4 V4;
     V4 rk[PF][TT][D / 16], rv[PF][TT][M / 16];
 #pragma unroll
@@ -91,8 +106,8 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
             // the loads next to their use two chunks later
             __builtin_amdgcn_sched_barrier(0);
             Fr KT[TT][D / 16], VT[TT][M / 16];
-            tokens_major<D / 16, F32_LDS>(KT, Kn, stage_k);
-            tokens_major<M / 16, F32_LDS>(VT, Vn, stage_v);
+            tokens_major<D / 16>(KT, Kn, stage_k);
+            tokens_major<M / 16>(VT, Vn, stage_v);
             state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
     }
@@ -106,27 +121,35 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
 //   intra:    Ot[mt][it] += V^T[m][j] P^T[j][i], P^T[j][i] = phi(K_j).phi(Q_i), j <= i
 //   update:   St += phi(K)^T [V, 1]
 // The normalizer row block of Ot gets den_i in row 0.
-template <typename T, int D, int M, bool CAUSAL, int PF, bool PHI = true, bool F32_LDS = false>
+// The first PF chunks of seg_output, loaded ahead (the fused forward issues
+// them before its cross-workgroup hand-off, while the memory system is idle).
+template <typename T, int D, int M, int PF> struct ChunkAhead {
+    typename IO<T>::vec4 rq[PF][TT][D / 16], rk[PF][TT][D / 16], rv[PF][TT][M / 16];
+    template <bool CAUSAL>
+    __device__ __forceinline__ void load(const T *Q, const T *K, const T *V, int64_t t_begin, int64_t t_end) {
+#pragma unroll
+        for (int b = 0; b < PF; ++b) {
+            load_chunk<T, D, TT>(rq[b], Q, t_begin + b * CH, t_end);
+            if (CAUSAL) {
+                load_chunk<T, D, TT>(rk[b], K, t_begin + b * CH, t_end);
+                load_chunk<T, M, TT>(rv[b], V, t_begin + b * CH, t_end);
+            }
+        }
+    }
+};
+
+template <typename T, int D, int M, bool CAUSAL, int PF, bool PHI = true, typename Fr = typename IO<T>::frag>
 __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__restrict__ K,
                                            const T *__restrict__ V, T *__restrict__ O, int64_t t_begin,
                                            int64_t t_end, f32x4 (&St)[D / 16][M / 16 + 1], lds_bf16 *stage_k,
-                                           lds_bf16 *stage_v) {
-    typedef typename IO<T>::frag Fr;
-    typedef typename IO<T>::vec4 V4;
+                                           lds_bf16 *stage_v, ChunkAhead<T, D, M, PF> &ahead) {
     constexpr int DT = D / 16, MT = M / 16;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
     const Fr ones = frag_ones<Fr>();
     const Fr zero = frag_zero<Fr>();
-
-    V4 rq[PF][TT][DT], rk[PF][TT][DT], rv[PF][TT][MT];
-#pragma unroll
-    for (int b = 0; b < PF; ++b) {
-        load_chunk<T, D, TT>(rq[b], Q, t_begin + b * CH, t_end);
-        if (CAUSAL) {
-            load_chunk<T, D, TT>(rk[b], K, t_begin + b * CH, t_end);
-            load_chunk<T, M, TT>(rv[b], V, t_begin + b * CH, t_end);
-        }
-    }
+    auto &rq = ahead.rq;
+    auto &rk = ahead.rk;
+    auto &rv = ahead.rv;
     for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * CH) {
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
@@ -158,7 +181,7 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
         for (int mt = 0; mt <= MT; ++mt) {
             Fr SF[DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<T>::to_frag(St[dt][mt]);
+            for (int dt = 0; dt < DT; ++dt) SF[dt] = frag_from<Fr>(St[dt][mt]);
 #pragma unroll
             for (int it = 0; it < TT; ++it)
 #pragma unroll
@@ -183,11 +206,11 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
 #pragma unroll
                         for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
                     }
-                    PT[jt][it] = IO<T>::to_frag(p);
+                    PT[jt][it] = frag_from<Fr>(p);
                 }
             Fr KT[TT][DT], VT[TT][MT];
-            tokens_major<DT, F32_LDS>(KT, Kn, stage_k);
-            tokens_major<MT, F32_LDS>(VT, Vn, stage_v);
+            tokens_major<DT>(KT, Kn, stage_k);
+            tokens_major<MT>(VT, Vn, stage_v);
             // intra-chunk term; the ones block sums P^T into den (every row)
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt)
@@ -715,21 +738,22 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
     lds_bf16 *stage_q = (lds_bf16 *)(lds_stage + wave * SW);
     lds_bf16 *stage_k = stage_q + SK;
     lds_bf16 *stage_v = stage_k + SK;
-    // fp32 I/O: the same area holds the K tile from stage_q on, then the V tile
-    constexpr int F32K = 2 * f32_stage_floats<D / 16, TT>(), F32V = 2 * f32_stage_floats<M / 16, TT>();
-    static_assert(F32K + F32V <= SW, "fp32 tiles fit the wavefront's staging area");
-    lds_bf16 *stage_f32v = stage_q + F32K;
+    // fp32 I/O (split into bf16 parts): the same area holds the two K tiles
+    // from stage_q on, then the two V tiles
+    static_assert(2 * SK + 2 * SV <= SW, "split fp32 tiles fit the wavefront's staging area");
+    lds_bf16 *stage_f32v = stage_q + 2 * SK;
     if constexpr (sizeof(T) == 2)
         seg_aggregate_bf16<D, M, kPrefetch, PHI>(K, V, t_begin, t_end, St, stage_k, stage_v);
     else
-        seg_aggregate<T, D, M, fwd_prefetch<T, D, M>(), PHI, true>(K, V, t_begin, t_end, St, stage_q, stage_f32v);
+        seg_aggregate<T, D, M, fwd_prefetch<T, D, M>(), PHI, split4>(K, V, t_begin, t_end, St, stage_q, stage_f32v);
     __syncthreads();   // every wavefront is done with its staging area
     state_store_frag<D, M>(slot(wave), St);
     __syncthreads();
 
     // pass 2's first chunks, loaded while the workgroups exchange their state
-    OutAhead<D, M, kPrefetch> ahead;
-    if constexpr (sizeof(T) == 2) ahead.template load<CAUSAL>(Q, K, V, t_begin, t_end);
+    typename std::conditional<sizeof(T) == 2, OutAhead<D, M, kPrefetch>,
+                              ChunkAhead<T, D, M, fwd_prefetch<T, D, M>()>>::type ahead;
+    ahead.template load<CAUSAL>(Q, K, V, t_begin, t_end);
 
     // Initial state (zero unless given), this thread's record elements.  Read
     // here, before the block publishes anything: the last block of the head
@@ -893,8 +917,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) __attribute__((amdgpu_waves_per_e
         seg_output_bf16<D, M, CAUSAL, kPrefetch, PHI>(Q, K, V, out + bh * N * M, t_begin, t_end, St, stage_q,
                                                       stage_k, stage_v, stage_v + SV, ahead);
     else
-        seg_output<T, D, M, CAUSAL, fwd_prefetch<T, D, M>(), PHI, true>(Q, K, V, out + bh * N * M, t_begin, t_end,
-                                                                        St, stage_q, stage_f32v);
+        seg_output<T, D, M, CAUSAL, fwd_prefetch<T, D, M>(), PHI, split4>(Q, K, V, out + bh * N * M, t_begin, t_end,
+                                                                        St, stage_q, stage_f32v, ahead);
 }
 
 // ---- host side ---------------------------------------------------------------
