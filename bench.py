@@ -54,7 +54,7 @@ def _args():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal", "sweep"],
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal", "sweep", "small"],
                     default="all",
                     help="restrict the timed work (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -416,7 +416,7 @@ def main():
         return dict(us_per_call=t / iters * 1e6, tok_heads_per_s=th * iters / t,
                     hbm_frac=by / (t / iters) / 1e9 / HBM_PEAK_GBS)
 
-    if a.only == "all":
+    if a.only in ("all", "small"):
         results["small_workloads"] = {wl.WORKLOADS[i].name: fwd_rate(wl.WORKLOADS[i]) for i in (1, 2, 3)}
     if (a.only == "all" and not a.no_sweep) or a.only == "sweep":
         results["sweep"] = {str(n): fwd_rate(w4.with_n(n)) for n in wl.SWEEP_N}
