@@ -31,9 +31,9 @@ __device__ __forceinline__ void load_chunk(typename IO<T>::vec4 (&x)[TT][F / 16]
     }
 }
 
-// phi on load: fragments of phi(X); rows at or beyond t_end become exact
-// zeros (so they add nothing to any state or sum).
-template <typename T, int F, int TT, typename Fr>
+// phi on load: fragments of phi(X); with MASK rows at or beyond t_end become
+// exact zeros (so they add nothing to any state or sum).
+template <typename T, int F, int TT, bool MASK = true, typename Fr>
 __device__ __forceinline__ void phi_frags(Fr (&y)[TT][F / 16],
                                           const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
     const int c = lane_id() & 15;
@@ -43,7 +43,7 @@ __device__ __forceinline__ void phi_frags(Fr (&y)[TT][F / 16],
 #pragma unroll
         for (int ft = 0; ft < F / 16; ++ft) {
             f32x4 p = phi4(IO<T>::to_f32(x[tt][ft]));
-            if (!ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (MASK && !ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
             y[tt][ft] = frag_from<Fr>(p);
         }
     }
@@ -57,8 +57,8 @@ __device__ __forceinline__ void value_frags_unmasked(bf16x4 &y, bf16x4 x) { y = 
 __device__ __forceinline__ void value_frags_unmasked(f32x4 &y, f32x4 x) { y = x; }
 __device__ __forceinline__ void value_frags_unmasked(split4 &y, f32x4 x) { y = split_f32(x); }
 
-// The loaded values as fragments, rows at or beyond t_end zeroed.
-template <typename T, int F, int TT, typename Fr>
+// The loaded values as fragments, rows at or beyond t_end zeroed (MASK).
+template <typename T, int F, int TT, bool MASK = true, typename Fr>
 __device__ __forceinline__ void raw_frags(Fr (&y)[TT][F / 16],
                                           const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
     const int c = lane_id() & 15;
@@ -68,21 +68,21 @@ __device__ __forceinline__ void raw_frags(Fr (&y)[TT][F / 16],
 #pragma unroll
         for (int ft = 0; ft < F / 16; ++ft) {
             f32x4 p = IO<T>::to_f32(x[tt][ft]);
-            if (!ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (MASK && !ok) p = f32x4{0.f, 0.f, 0.f, 0.f};
             y[tt][ft] = frag_from<Fr>(p);
         }
     }
 }
 
 // Query/key fragments: phi applied (PHI) or the given features as they are;
-// rows at or beyond t_end zeroed either way.
-template <typename T, int F, int TT, bool PHI, typename Fr>
+// rows at or beyond t_end zeroed either way (MASK).
+template <typename T, int F, int TT, bool PHI, bool MASK = true, typename Fr>
 __device__ __forceinline__ void feat_frags(Fr (&y)[TT][F / 16],
                                            const typename IO<T>::vec4 (&x)[TT][F / 16], int64_t t0, int64_t t_end) {
     if constexpr (PHI)
-        phi_frags<T, F, TT>(y, x, t0, t_end);
+        phi_frags<T, F, TT, MASK>(y, x, t0, t_end);
     else
-        raw_frags<T, F, TT>(y, x, t0, t_end);
+        raw_frags<T, F, TT, MASK>(y, x, t0, t_end);
 }
 
 // ---- LDS staging (bf16) ---------------------------------------------------

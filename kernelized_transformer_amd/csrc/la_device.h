@@ -110,16 +110,18 @@ __device__ __forceinline__ void mma2(f32x4 &acc, f32x4 a0, f32x4 a1, f32x4 b0, f
 
 // An fp32 operand carried as two bf16 parts, x = hi + lo: hi is x rounded
 // to bf16 (RNE, 8 significant bits), lo the exact remainder x - hi rounded
-// to bf16, so that |x - hi - lo| <= 2^-16 |x|.  Products take hi*hi + lo*hi
-// + hi*lo (the dropped lo*lo is at most 2^-16 |a||b|), so each product is
-// within about 3 * 2^-16 of |a||b| (errors of random sign, which average
-// out in the sums).  On the bf16 matrix instruction a 16-deep tile costs two
-// 32-deep instructions (a pair of tiles three) instead of four 4-deep fp32
-// ones of twice the duration each.
+// to bf16, so that |x - hi - lo| <= 2^-16 |x|.  The parts sit in one 8-wide
+// operand [hi, lo], and a 16-deep tile product is two 32-deep bf16
+// instructions: [hi, lo] . [hi, lo] + [hi, lo] . [lo, hi] = (a_hi + a_lo)
+// (b_hi + b_lo), the product of the split values with no term dropped, so
+// each product is within about 2 * 2^-16 of |a||b| (errors of random sign,
+// which average out in the sums), at 32 cycles per 16-deep tile against 128
+// for four 4-deep fp32 instructions.  Only the swapped copy of the second
+// operand is ever moved between registers; no operand is zero-padded.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct split4 {
-    bf16x4 hi, lo;
+    bf16x8 hl;   // elements 0-3: hi, 4-7: lo
 };
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ split4 split_f32(f32x4 a) {
     // each pair rounded once (one v_cvt_pk_bf16_f32); the fp32 values of the
     // rounded halves are the packed word shifted / masked.  The empty asm
@@ -133,22 +135,21 @@ __device__ __forceinline__ split4 split_f32(f32x4 a) {
     const f32x4 r = a - hf;
     const unsigned l01 = __builtin_bit_cast(unsigned, bf16x2{(bf16)r[0], (bf16)r[1]});
     const unsigned l23 = __builtin_bit_cast(unsigned, bf16x2{(bf16)r[2], (bf16)r[3]});
-    return split4{__builtin_bit_cast(bf16x4, u32x2{h01, h23}), __builtin_bit_cast(bf16x4, u32x2{l01, l23})};
+    return split4{__builtin_bit_cast(bf16x8, u32x4{h01, h23, l01, l23})};
+}
+__device__ __forceinline__ bf16x4 split_hi(split4 x) { return __builtin_shufflevector(x.hl, x.hl, 0, 1, 2, 3); }
+__device__ __forceinline__ bf16x4 split_lo(split4 x) { return __builtin_shufflevector(x.hl, x.hl, 4, 5, 6, 7); }
+__device__ __forceinline__ split4 split_join(bf16x4 hi, bf16x4 lo) {
+    return split4{__builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7)};
 }
 __device__ __forceinline__ void mma1(f32x4 &acc, split4 a, split4 b) {
-    bf16x8 a8 = __builtin_shufflevector(a.hi, a.lo, 0, 1, 2, 3, 4, 5, 6, 7);
-    bf16x8 b8 = __builtin_shufflevector(b.hi, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
-    mma1(acc, a.hi, b.lo);
+    const bf16x8 bs = __builtin_shufflevector(b.hl, b.hl, 4, 5, 6, 7, 0, 1, 2, 3);   // [lo, hi]
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hl, b.hl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hl, bs, acc, 0, 0, 0);
 }
 __device__ __forceinline__ void mma2(f32x4 &acc, split4 a0, split4 a1, split4 b0, split4 b1) {
-    bf16x8 a = __builtin_shufflevector(a0.hi, a0.lo, 0, 1, 2, 3, 4, 5, 6, 7);
-    bf16x8 b = __builtin_shufflevector(b0.hi, b0.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    a = __builtin_shufflevector(a1.hi, a1.lo, 0, 1, 2, 3, 4, 5, 6, 7);
-    b = __builtin_shufflevector(b1.hi, b1.hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    mma2(acc, a0.hi, a1.hi, b0.lo, b1.lo);
+    mma1(acc, a0, b0);
+    mma1(acc, a1, b1);
 }
 
 __device__ __forceinline__ bf16x4 acc_to_frag(f32x4 a, bf16x4) { return IO<bf16>::to_frag(a); }

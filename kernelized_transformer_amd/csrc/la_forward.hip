@@ -58,15 +58,15 @@ __device__ __forceinline__ void tokens_major(Fr (&yt)[TT][NF], const Fr (&y)[TT]
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                h[tt][f] = y[tt][f].hi;
-                l[tt][f] = y[tt][f].lo;
+                h[tt][f] = split_hi(y[tt][f]);
+                l[tt][f] = split_lo(y[tt][f]);
             }
         transpose_frags_lds<NF, TT>(ht, h, stage);
         transpose_frags_lds<NF, TT>(lt, l, stage + stage_elems<NF, TT>());
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int f = 0; f < NF; ++f) yt[tt][f] = split4{ht[tt][f], lt[tt][f]};
+            for (int f = 0; f < NF; ++f) yt[tt][f] = split_join(ht[tt][f], lt[tt][f]);
     } else {
         transpose_frags<NF, TT>(yt, y, stage);
     }
@@ -154,10 +154,14 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
 #pragma unroll
     for (int b = 0; b < PF; ++b) {
         const int64_t t0 = t00 + b * CH;   // may lie past t_end: fully masked, no stores
+        // no row masks (as in seg_output_bf16): rows past the end hold copies of
+        // the last valid row (finite whenever the data is), their outputs are
+        // not stored, the causal mask keeps them out of every stored output,
+        // and the state is not used after the last chunk
         Fr Qn[TT][DT], Kn[TT][DT], Vn[TT][MT];
-        feat_frags<T, D, TT, PHI>(Qn, rq[b], t0, t_end);
+        feat_frags<T, D, TT, PHI, false>(Qn, rq[b], t0, t_end);
         if (CAUSAL) {
-            feat_frags<T, D, TT, PHI>(Kn, rk[b], t0, t_end);
+            feat_frags<T, D, TT, PHI, false>(Kn, rk[b], t0, t_end);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
