@@ -21,12 +21,14 @@
  *     dt gives the element type of q, k, v, out, dout, dq, dk, dv (fp32 or
  *     bf16).  All state and accumulation is fp32 inside the kernels.
  *   - Head sizes: the forwards (la_forward_causal, _state, _features,
- *     _noalloc, _noncausal) and la_decode_step take D, M (F for features)
- *     any multiple of 16 from 16 to 128 -- D, M in {32, 64} run the fused
- *     single-launch kernels, the others a three-launch path (per-segment sums,
- *     scan, outputs, one wavefront per 16 columns of V); the backwards, the
- *     polynomial kernel and the random features take D, M in {32, 64}.
- *     Other sizes return LA_ERR_UNSUPPORTED.  B, H, N >= 1.
+ *     _noalloc, _noncausal), the backwards and la_decode_step take D, M (F
+ *     for features) any multiple of 16 from 16 to 128 -- D, M in {32, 64}
+ *     run the fused single-launch forwards and the two-state backward
+ *     kernels, the others a path that splits V (and dout) into 16-column
+ *     groups, one wavefront each (forward: per-segment sums, scan, outputs;
+ *     backward: the same sums and scan, a dQ pass, the scan in reverse, a
+ *     dK/dV pass); the polynomial kernel and the random features take D, M
+ *     in {32, 64}.  Other sizes return LA_ERR_UNSUPPORTED.  B, H, N >= 1.
  *   - Every tensor pointer must be 16-byte aligned; outputs must not overlap
  *     any input or each other.
  *   - Calls are asynchronous on `stream` (0 = the null stream).  The library
@@ -75,7 +77,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 8
+#define LA_ABI_VERSION 9
 
 /* The enums are int-sized in C; C++ gets the same fixed underlying type, so
  * any int a C caller passes (an unknown dtype, op or status included) is a

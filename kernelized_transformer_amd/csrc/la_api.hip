@@ -27,8 +27,9 @@ size_t esize(la_dtype_t dt) { return dt == LA_DTYPE_F32 ? 4 : 2; }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
-// any_size: every multiple of 16 up to 128 (decode, the forwards); otherwise
-// D, M in {32, 64} (backward, polynomial and random-feature kernels).
+// any_size: every multiple of 16 up to 128 (decode, the forwards, the
+// backwards); otherwise D, M in {32, 64} (polynomial and random-feature
+// kernels).
 la_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt, bool any_size = false) {
     if (B < 1 || H < 1 || N < 1 || D < 1 || M < 1) return LA_ERR_INVALID_ARGUMENT;
     if (B > kMaxElems || H > kMaxElems || N > kMaxElems) return LA_ERR_INVALID_ARGUMENT;
@@ -196,7 +197,7 @@ la_status_t la_forward_causal_features(const void *fq, const void *fk, const voi
 static la_status_t poly_forward(bool causal, const void *q, const void *k, const void *v, void *out,
                                 float *state_final, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                                 la_dtype_t dt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    la_status_t st = check_shape(B, H, N, D, M, dt);
+    la_status_t st = check_shape(B, H, N, D, M, dt, true);
     if (st != LA_OK) return st;
     if (!la::poly_head_sizes(D, M)) return LA_ERR_UNSUPPORTED;
     const size_t es = esize(dt);
@@ -279,7 +280,7 @@ namespace {
 la_status_t backward_common(bool causal, const void *q, const void *k, const void *v, const void *dout, void *dq,
                             void *dk, void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                             la_dtype_t dt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    la_status_t st = check_shape(B, H, N, D, M, dt);
+    la_status_t st = check_shape(B, H, N, D, M, dt, true);
     if (st != LA_OK) return st;
     const size_t es = esize(dt);
     const int64_t BH = B * H;
@@ -328,8 +329,9 @@ la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S
 }
 
 size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, la_dtype_t dt) {
-    const bool fwd = op == LA_OP_FWD_CAUSAL || op == LA_OP_FWD_NONCAUSAL;
-    if (check_shape(B, H, N, D, M, dt, fwd) != LA_OK) return 0;
+    const bool any_size = op == LA_OP_FWD_CAUSAL || op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_CAUSAL ||
+                          op == LA_OP_BWD_NONCAUSAL;
+    if (check_shape(B, H, N, D, M, dt, any_size) != LA_OK) return 0;
     switch (op) {
     case LA_OP_FWD_CAUSAL:
         return la::causal_workspace_bytes(B * H, N, D, M);

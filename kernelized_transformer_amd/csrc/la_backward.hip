@@ -1047,6 +1047,8 @@ static hipError_t run_backward_t(bool causal, const void *q, const void *k, cons
 hipError_t launch_backward(bool causal, int dt, const void *q, const void *k, const void *v, const void *dout,
                            void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
                            hipStream_t s) {
+    if (!fused_head_sizes(D, M))
+        return launch_backward_generic(causal, dt, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
     if (dt == 0) return run_backward_t<float>(causal, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
     return run_backward_t<bf16>(causal, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
 }

@@ -19,10 +19,29 @@
 // phi(K) [V, 1]^T into row-major records (each wavefront its columns), the
 // scan of la_forward.hip over segments (with the optional start state and
 // final state), then the outputs.
+//
+// The backward for the same head sizes (the two-state kernels of
+// la_backward.hip take D, M in {32, 64}) splits the same way: a workgroup
+// walks one segment with one wavefront per 16-column group of V and dout.
+// With g_i = dout_i / d_i, h_i = -(dout_i . out_i) / d_i ([summary] 3.3.1
+// and appendix A, denominator terms written out as in la_backward.hip),
+//   dL/dphi(q_i) = sum_{j<=i} (g_i . v_j + h_i) phi(k_j) = S_i g_i + Z_i h_i,
+//   dL/dphi(k_j) = sum_{i>=j} (g_i . v_j + h_i) phi(q_i) = R_j v_j + u_j,
+//   dV_j         = sum_{i>=j} (phi(q_i) . phi(k_j)) g_i  = R_j^T phi(k_j),
+// every term is a sum over column groups (S_i g_i over the groups' columns
+// of S and g, R_j v_j likewise) plus the h part, which the first group
+// adds; dV is per group.  So each wavefront carries the D x 16 slices of S
+// (with Z) and of R (with u on the first group), and the only values that
+// need all groups -- dout . out for h, and the dQ and dK sums -- are added
+// through LDS in group order, a fixed order, so results do not vary from run
+// to run.  Launches: the per-segment sums above and the scan (forward
+// states), the dQ pass (also 1/d and h per token and the segment's reverse
+// sums), the scan in reverse, the dK/dV pass.
 #include <type_traits>
 
 #include "la_chunk.h"
 #include "la_internal.h"
+#include "la_split.h"
 
 namespace la {
 
@@ -213,6 +232,339 @@ __global__ __launch_bounds__(512) void k_gen_output(const T *__restrict__ q, con
     }
 }
 
+
+// ---- backward ----------------------------------------------------------------------
+// LDS per wavefront for the token-contiguous copies (bf16: the D x 32 state
+// slice, or one chunk of phi(Q) and the two g columns tiles); fp32 copies go
+// through identity products.
+template <typename T, int DT>
+constexpr int gbwd_stage_elems() {
+    return sizeof(T) == 4 ? 8
+                          : (stage_elems<DT, 2>() > stage_elems<DT, 1>() + stage_elems<2, 1>()
+                                 ? stage_elems<DT, 2>()
+                                 : stage_elems<DT, 1>() + stage_elems<2, 1>());
+}
+
+// Partial sums of the wavefronts (one per column group) in LDS: part[cg][dt]
+// holds wavefront cg's D-row tile dt, 64 lanes x 4 floats.  reduce_rows
+// returns the sum over groups 0 .. ng - 1 of tile dt for this lane.
+template <int DT>
+__device__ __forceinline__ f32x4 reduce_rows(const f32x4 (*part)[DT][64], int ng, int dt) {
+    const int lane = lane_id();
+    f32x4 s = part[0][dt][lane];
+    for (int w = 1; w < ng; ++w) s += part[w][dt][lane];
+    return s;
+}
+
+// Forward direction.  Wavefront cg: S and Z slice St (Z replicated, as in
+// k_gen_output), this segment's reverse sums Ra = sum_i phi(q_i) [g_i, h_i]^T
+// restricted to its columns (u, in column 0 of the second tile, on group 0).
+template <typename T, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const T *__restrict__ k,
+                                                 const T *__restrict__ v, const T *__restrict__ dout,
+                                                 T *__restrict__ dq, const float *__restrict__ wsS,
+                                                 float *__restrict__ wsR, float *__restrict__ ibuf,
+                                                 float *__restrict__ hbuf, int64_t N, int64_t M, int64_t nseg,
+                                                 int64_t seg_tokens) {
+    constexpr int D = 16 * DT;
+    typedef typename IO<T>::frag Fr;
+    typedef typename IO<T>::vec4 V4;
+    __shared__ __align__(16) bf16 stage_mem[8][gbwd_stage_elems<T, DT>()];
+    __shared__ __align__(16) f32x4 part[8][DT][64];
+    __shared__ float hpart[8][16];
+    const int ng = int(M / 16);
+    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
+    const int64_t rec = int64_t(D) * M + D;
+    const T *Q = q + bh * N * D;
+    const T *K = k + bh * N * D;
+    const T *V = v + bh * N * M;
+    const T *G = dout + bh * N * M;
+    T *DQ = dq + bh * N * D;
+    lds_bf16 *stage = (lds_bf16 *)stage_mem[cg];
+
+    f32x4 St[DT][2], Ra[DT][2];
+    {
+        const float *r0 = wsS + (bh * nseg + (CAUSAL ? seg : 0)) * rec;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                St[dt][0][r] = r0[(16 * dt + 4 * g + r) * M + 16 * cg + c];
+                St[dt][1][r] = r0[int64_t(D) * M + 16 * dt + 4 * g + r];
+            }
+            Ra[dt][0] = Ra[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const Fr ones = frag_ones<Fr>();
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    V4 rq[1][DT], rk[1][DT], rv, rg;
+    auto load_all = [&](int64_t t0) {
+        load_chunk<T, D, 1>(rq, Q, t0, t_end);
+        if (CAUSAL) {
+            load_chunk<T, D, 1>(rk, K, t0, t_end);
+            rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
+        }
+        rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
+    };
+    load_all(t_begin);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
+        Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
+        phi_frags<T, D, 1>(Qn, rq, t0, t_end);
+        if (CAUSAL) {
+            phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+            const V4 one[1][1] = {{rv}};
+            raw_frags<T, 16, 1>(Vn, one, t0, t_end);
+        }
+        f32x4 qraw[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) qraw[dt] = IO<T>::to_f32(rq[0][dt]);
+        const f32x4 graw = IO<T>::to_f32(rg);
+        load_all(t0 + GCH);   // rows past t_end read row t_end - 1
+        const int64_t t = t0 + c;   // this lane's query token
+        const bool valid = t < t_end;
+
+        // out^T of this group's columns (Ot[0]) and den (every row of Ot[1])
+        f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        Fr SF[2][DT];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = IO<T>::to_frag(St[dt][mt]);
+            mma_tiles<Fr, DT>(Ot[mt], SF[mt], Qn[0]);
+        }
+        Fr KT[1][DT], VT[1][1];
+        if (CAUSAL) {
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+            mma_tiles<Fr, DT>(p, Kn[0], Qn[0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+            const Fr PT = IO<T>::to_frag(p);
+            transpose_frags<DT, 1>(KT, Kn, stage);
+            transpose_frags<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
+            mma1(Ot[0], VT[0][0], PT);
+            mma1(Ot[1], ones, PT);
+        }
+        const float inv = valid ? __builtin_amdgcn_rcpf(Ot[1][0]) : 0.f;
+
+        // h = -(dout . out) / d: this group's share, then the sum over groups
+        const f32x4 o = Ot[0] * inv;
+        float go = graw[0] * o[0] + graw[1] * o[1] + graw[2] * o[2] + graw[3] * o[3];
+        go += __shfl_xor(go, 16);
+        go += __shfl_xor(go, 32);
+        if (g == 0) hpart[cg][c] = go;
+        lds_barrier();
+        float gsum = hpart[0][c];
+        for (int w = 1; w < ng; ++w) gsum += hpart[w][c];
+        const float h = -gsum * inv;
+        if (CAUSAL && cg == 0 && valid && g == 0) {
+            ibuf[bh * N + t] = inv;
+            hbuf[bh * N + t] = h;
+        }
+        const Fr Gn = IO<T>::to_frag(graw * inv);                           // rows past t_end: inv = 0
+        const Fr Gh = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});   // h in column 0
+
+        // dA^T[j][i] = v_j . g_i over this group's columns (group 0 adds h_i), j <= i
+        Fr dAT = frag_zero<Fr>();
+        if (CAUSAL) {
+            f32x4 da = {0.f, 0.f, 0.f, 0.f};
+            mma1(da, Vn[0][0], Gn);
+            if (cg == 0) mma1(da, k0ones, Gh);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
+            dAT = IO<T>::to_frag(da);
+        }
+
+        // this group's part of dL/dphi(q)^T[d][i]: sum_j phi(k_j)[d] dA^T[j][i]
+        // + S[d][its columns] g_i (+ Z[d] h_i on group 0)
+        Fr SFT[2][DT];
+        transpose_frags<DT, 2>(SFT, SF, stage);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (CAUSAL) mma1(acc, KT[0][dt], dAT);
+            mma1(acc, SFT[0][dt], Gn);
+            if (cg == 0) mma1(acc, SFT[1][dt], Gh);
+            part[cg][dt][lane] = acc;
+        }
+        lds_barrier();
+        for (int dt = cg; dt < DT; dt += ng) {   // the groups' sum, tiles dealt out over the wavefronts
+            const f32x4 dqv = reduce_rows<DT>(part, ng, dt) * dphi4(qraw[dt]);
+            if (valid) store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dqv));
+        }
+
+        // this segment's reverse sums: Ra += phi(Q)^T [g | h] (its columns)
+        Fr QT[1][DT], GT[1][2];
+        transpose_frags<DT, 1>(QT, Qn, stage);
+        {
+            const Fr gg[1][2] = {{Gn, Gh}};
+            transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            mma1(Ra[dt][0], QT[0][dt], GT[0][0]);
+            if (cg == 0) mma1(Ra[dt][1], QT[0][dt], GT[0][1]);
+        }
+
+        if (CAUSAL) state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
+    }
+    float *r1 = wsR + (bh * nseg + seg) * rec;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) r1[(16 * dt + 4 * g + r) * M + 16 * cg + c] = Ra[dt][0][r];
+        if (cg == 0 && c == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) r1[int64_t(D) * M + 16 * dt + 4 * g + r] = Ra[dt][1][r];
+        }
+    }
+}
+
+// Reverse direction.  Wavefront cg carries R[:, its columns] and (group 0)
+// u, walking the chunks last to first; writes dV of its columns and, with
+// the other groups, dK.
+template <typename T, int DT, bool CAUSAL>
+__global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, const T *__restrict__ k,
+                                                   const T *__restrict__ v, const T *__restrict__ dout,
+                                                   const float *__restrict__ ibuf, const float *__restrict__ hbuf,
+                                                   T *__restrict__ dk, T *__restrict__ dv,
+                                                   const float *__restrict__ wsR, int64_t N, int64_t M,
+                                                   int64_t nseg, int64_t seg_tokens) {
+    constexpr int D = 16 * DT;
+    typedef typename IO<T>::frag Fr;
+    typedef typename IO<T>::vec4 V4;
+    __shared__ __align__(16) bf16 stage_mem[8][gbwd_stage_elems<T, DT>()];
+    __shared__ __align__(16) f32x4 part[8][DT][64];
+    const int ng = int(M / 16);
+    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
+    const int64_t rec = int64_t(D) * M + D;
+    const T *Q = q + bh * N * D;
+    const T *K = k + bh * N * D;
+    const T *V = v + bh * N * M;
+    const T *G = dout + bh * N * M;
+    T *DK = dk + bh * N * D;
+    T *DV = dv + bh * N * M;
+    lds_bf16 *stage = (lds_bf16 *)stage_mem[cg];
+
+    f32x4 Rr[DT][2];   // R[:, its columns]; u in column 0 of the second tile (group 0 only)
+    {
+        const float *r0 = wsR + (bh * nseg + (CAUSAL ? seg : 0)) * rec;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Rr[dt][0][r] = r0[(16 * dt + 4 * g + r) * M + 16 * cg + c];
+                Rr[dt][1][r] = (cg == 0 && c == 0) ? r0[int64_t(D) * M + 16 * dt + 4 * g + r] : 0.f;
+            }
+    }
+    const Fr k0ones = frag_k0_ones<Fr>();
+
+    const int64_t nch = (t_end - t_begin + GCH - 1) / GCH;
+    V4 rq[1][DT], rk[1][DT], rv, rg;
+    float rh = 0.f, ri = 0.f;
+    auto load_all = [&](int64_t t0) {
+        if (CAUSAL) load_chunk<T, D, 1>(rq, Q, t0, t_end);
+        load_chunk<T, D, 1>(rk, K, t0, t_end);
+        rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
+        if (CAUSAL) {
+            rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
+            rh = (t0 + c < t_end) ? hbuf[bh * N + t0 + c] : 0.f;
+            ri = (t0 + c < t_end) ? ibuf[bh * N + t0 + c] : 0.f;
+        }
+    };
+    load_all(t_begin + (nch - 1) * GCH);
+    for (int64_t ci = nch - 1; ci >= 0; --ci) {
+        const int64_t t0 = t_begin + ci * GCH;
+        Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
+        Fr Gn = frag_zero<Fr>(), Gh = frag_zero<Fr>();
+        if (CAUSAL) phi_frags<T, D, 1>(Qn, rq, t0, t_end);
+        phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+        {
+            const V4 one[1][1] = {{rv}};
+            raw_frags<T, 16, 1>(Vn, one, t0, t_end);
+        }
+        if (CAUSAL) {   // g = dout / d as in the forward-direction pass; rows past t_end are 0 (ri = 0)
+            Gn = IO<T>::to_frag(IO<T>::to_f32(rg) * ri);
+            Gh = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
+        }
+        f32x4 kraw[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) kraw[dt] = IO<T>::to_f32(rk[0][dt]);
+        if (ci > 0) load_all(t0 - GCH);
+        const int64_t t = t0 + c;   // this lane's key token
+        const bool valid = t < t_end;
+
+        Fr RF[2][DT], RFT[2][DT];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) RF[mt][dt] = IO<T>::to_frag(Rr[dt][mt]);
+        transpose_frags<DT, 2>(RFT, RF, stage);
+
+        Fr QT[1][DT], GT[1][2];
+        Fr Pf = frag_zero<Fr>(), dAf = frag_zero<Fr>();
+        if (CAUSAL) {
+            transpose_frags<DT, 1>(QT, Qn, stage);
+            {
+                const Fr gg[1][2] = {{Gn, Gh}};
+                transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
+            }
+            // P[i][j] = phi(q_i) . phi(k_j); dA[i][j] = g_i . v_j over this group's columns
+            // (group 0 adds h_i); both masked to i >= j
+            f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+            mma_tiles<Fr, DT>(p, Qn[0], Kn[0]);
+            mma1(da, Gn, Vn[0][0]);
+            if (cg == 0) mma1(da, Gh, k0ones);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = 4 * g + r >= c;
+                p[r] = keep ? p[r] : 0.f;
+                da[r] = keep ? da[r] : 0.f;
+            }
+            Pf = IO<T>::to_frag(p);
+            dAf = IO<T>::to_frag(da);
+        }
+
+        // this group's part of dL/dphi(k)^T[d][j]: sum_i phi(q_i)[d] dA[i][j]
+        // + R[d][its columns] v_j (+ u[d] on group 0)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (CAUSAL) mma1(acc, QT[0][dt], dAf);
+            mma1(acc, RFT[0][dt], Vn[0][0]);
+            if (cg == 0) mma1(acc, RFT[1][dt], k0ones);
+            part[cg][dt][lane] = acc;
+        }
+        lds_barrier();
+        for (int dt = cg; dt < DT; dt += ng) {
+            const f32x4 dkv = reduce_rows<DT>(part, ng, dt) * dphi4(kraw[dt]);
+            if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dkv));
+        }
+        // dV^T[m][j] (its columns) = sum_i g[i][m] P[i][j] + sum_d R[d][m] phi(k_j)[d]
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (CAUSAL) mma1(acc, GT[0][0], Pf);
+            mma_tiles<Fr, DT>(acc, RF[0], Kn[0]);
+            if (valid) store4<T>(DV + t * M + 16 * cg + 4 * g, IO<T>::from_f32(acc));
+        }
+        // carry R (and u) towards earlier tokens
+        if (CAUSAL) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                mma1(Rr[dt][0], QT[0][dt], GT[0][0]);
+                if (cg == 0) mma1(Rr[dt][1], QT[0][dt], GT[0][1]);
+            }
+        }
+        lds_barrier();   // every group has read `part` before the next chunk writes it
+    }
+}
+
 // ---- host side -------------------------------------------------------------------
 // The workspace starts with the same 256-byte header as the fused forwards'
 // (its error word stays as the caller left it: nothing here waits), then one
@@ -279,6 +631,70 @@ hipError_t launch_forward_generic(bool causal, int dt, const void *q, const void
     const bool phi = !sio.features_given;
     if (dt == 0) return run_generic_t<float>(causal, phi, q, k, v, out, BH, N, D, M, ws, sio, s);
     return run_generic_t<bf16>(causal, phi, q, k, v, out, BH, N, D, M, ws, sio, s);
+}
+
+
+template <typename T, int DT>
+static hipError_t run_generic_backward(bool causal, const void *q, const void *k, const void *v, const void *dout,
+                                       void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t M, float *ws,
+                                       hipStream_t s) {
+    constexpr int D = 16 * DT;
+    const SegPlan p = make_plan(BH, N, D, M);
+    const BwdLayout L = backward_layout(BH, N, D, M, sizeof(T));
+    float *wsS = ws;
+    float *wsR = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.states);
+    float *ibuf = causal ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.inv_off) : nullptr;
+    float *hbuf = causal ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.h_off) : nullptr;
+    const dim3 grid(unsigned(BH * p.nseg)), block(unsigned(64 * (M / 16)));
+    hipLaunchKernelGGL((k_gen_segstate<T, DT, true>), grid, block, 0, s, (const T *)k, (const T *)v, wsS, N, M,
+                       p.nseg, p.seg_tokens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if ((e = launch_scan(wsS, BH, p.nseg, p.rec, causal ? 0 : 1, s)) != hipSuccess) return e;
+    if (causal)
+        hipLaunchKernelGGL((k_gbwd_dq<T, DT, true>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v,
+                           (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, M, p.nseg,
+                           p.seg_tokens);
+    else
+        hipLaunchKernelGGL((k_gbwd_dq<T, DT, false>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v,
+                           (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, M, p.nseg,
+                           p.seg_tokens);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_scan(wsR, BH, p.nseg, p.rec, causal ? 2 : 1, s)) != hipSuccess) return e;
+    if (causal)
+        hipLaunchKernelGGL((k_gbwd_dkdv<T, DT, true>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
+                           (T *)dv, (const float *)wsR, N, M, p.nseg, p.seg_tokens);
+    else
+        hipLaunchKernelGGL((k_gbwd_dkdv<T, DT, false>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
+                           (T *)dv, (const float *)wsR, N, M, p.nseg, p.seg_tokens);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t run_generic_backward_t(bool causal, const void *q, const void *k, const void *v,
+                                         const void *dout, void *dq, void *dk, void *dv, int64_t BH, int64_t N,
+                                         int64_t D, int64_t M, float *ws, hipStream_t s) {
+    switch (D) {
+    case 16: return run_generic_backward<T, 1>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 32: return run_generic_backward<T, 2>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 48: return run_generic_backward<T, 3>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 64: return run_generic_backward<T, 4>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 80: return run_generic_backward<T, 5>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 96: return run_generic_backward<T, 6>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 112: return run_generic_backward<T, 7>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    case 128: return run_generic_backward<T, 8>(causal, q, k, v, dout, dq, dk, dv, BH, N, M, ws, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_generic(bool causal, int dt, const void *q, const void *k, const void *v,
+                                   const void *dout, void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D,
+                                   int64_t M, float *ws, hipStream_t s) {
+    if (M % 16 != 0 || M < 16 || M > 128) return hipErrorInvalidValue;
+    if (dt == 0) return run_generic_backward_t<float>(causal, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+    return run_generic_backward_t<bf16>(causal, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
 }
 
 }  // namespace la

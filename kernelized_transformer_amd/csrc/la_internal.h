@@ -235,6 +235,11 @@ hipError_t launch_scan(float *ws, int64_t BH, int64_t nseg, int64_t rec, int mod
 hipError_t launch_backward(bool causal, int dt, const void *q, const void *k, const void *v, const void *dout,
                            void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
                            hipStream_t s);
+// The backward for head sizes outside {32, 64} (la_generic.hip), on the same
+// workspace layout (backward_layout).
+hipError_t launch_backward_generic(bool causal, int dt, const void *q, const void *k, const void *v,
+                                   const void *dout, void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t D,
+                                   int64_t M, float *ws, hipStream_t s);
 hipError_t launch_decode(int dt, const void *q, const void *k, const void *v, float *S, float *Z, void *out,
                          int64_t BH, int64_t D, int64_t M, hipStream_t s);
 

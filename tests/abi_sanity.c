@@ -45,7 +45,9 @@ int main(void) {
     EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, 0, 1, 1, 32, 32, LA_DTYPE_F32), 0);
     EXPECT(la_workspace_size((la_op_t)9, 1, 1, 1, 32, 32, LA_DTYPE_F32), 0);
     EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, 1, 1, 1, 40, 32, LA_DTYPE_F32), 0);
-    EXPECT(la_workspace_size(LA_OP_BWD_CAUSAL, 1, 1, 1, 48, 32, LA_DTYPE_F32), 0);
+    EXPECT(la_workspace_size(LA_OP_BWD_CAUSAL, 1, 1, 1, 40, 32, LA_DTYPE_F32), 0);
+    if (la_workspace_size(LA_OP_BWD_CAUSAL, 1, 1, 100, 48, 32, LA_DTYPE_F32) == 0) ++failures;
+    EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL_POLY2, 1, 1, 1, 48, 32, LA_DTYPE_F32), 0);
     if (la_workspace_size(LA_OP_FWD_CAUSAL, 1, 1, 100, 48, 128, LA_DTYPE_F32) == 0) ++failures;
     EXPECT(la_workspace_size(LA_OP_FWD_CAUSAL, INT64_MAX, INT64_MAX, INT64_MAX, 32, 32, LA_DTYPE_F32), 0);
 

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 8
+    assert la.la_abi_version() == 9
     names = [la.la_status_string(s) for s in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP",
                      "LA_ERR_TIMEOUT"]
@@ -84,7 +84,9 @@ def test_workspace_size():
     assert f(la.LA_OP_FWD_CAUSAL, 0, 2, 256, 32, 32, torch.float32) == 0     # invalid shape
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 40, 32, torch.float32) == 0     # unsupported D
     assert f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 48, 128, torch.float32) > 0     # the generic path
-    assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) == 0     # backward: {32, 64} only
+    assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 48, 32, torch.float32) > 0      # backward: the generic path too
+    assert f(la.LA_OP_BWD_NONCAUSAL, 1, 2, 256, 128, 16, torch.bfloat16) > 0
+    assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 40, 32, torch.float32) == 0     # not a multiple of 16
     # grows linearly in N at fixed segment count ceiling
     a = f(la.LA_OP_FWD_CAUSAL, 1, 8, 65536, 64, 64, torch.bfloat16)
     assert a <= 8 * 64 * 2 * (64 * 64 + 64) * 4 + 4096
@@ -202,7 +204,9 @@ def test_backward_and_decode_argument_errors():
         assert bwd(base[:4] + [base[0], base[5], base[6]]) == 1     # dq aliases q
         assert bwd(base[:4] + [base[4], base[4], base[6]]) == 1     # dq aliases dk
         assert bwd(base[:3] + [base[6]] + base[4:7]) == 1           # dv aliases dout
-        assert bwd(base[:7], D=128) == 2
+        assert bwd(base[:7], D=144) == 2                             # beyond 128
+        assert bwd(base[:7], M=40) == 2                              # not a multiple of 16
+        assert bwd(base[:7], D=128) == 3                             # supported: then the missing workspace
         assert bwd(base[:7], N=0) == 1
         assert bwd(base[:7], ws=base[2], wsb=1 << 20) == 3          # workspace overlaps v
     assert ok

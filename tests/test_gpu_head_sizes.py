@@ -1,10 +1,11 @@
 """GPU parity for head sizes outside {32, 64}: every multiple of 16 up to 128.
 
 The forwards (causal, non-causal, from a start state, on given features, the
-no-allocation entry point) run the generic path for these sizes, decode its
-general kernel; each case is gated against the fp64 oracle like the rest of
-the parity suite (normwise per slice and per 16-token chunk).  The backward,
-polynomial and random-feature kernels keep D, M in {32, 64} and must say so.
+no-allocation entry point) and the backwards run the generic path for these
+sizes, decode its general kernel; each case is gated against the fp64 oracle
+like the rest of the parity suite (normwise per slice and per 16-token chunk;
+dQ and dK with the gradient floor).  The polynomial and random-feature
+kernels keep D, M in {32, 64} and must say so.
 """
 from __future__ import annotations
 
@@ -125,10 +126,68 @@ def test_decode_head_sizes(D, M, dtype):
     check("decode Z", host(Z), Z_ref, "f32")
 
 
+BWD_CASES = [
+    ("d128m128_bf16", _w(521, 1, 2, 2000, 128, 128, "bf16")),
+    ("d16m16_f32_ragged", _w(522, 2, 3, 1001, 16, 16, "f32")),
+    ("d48m80_bf16", _w(523, 1, 2, 3000, 48, 80, "bf16")),
+    ("d96m32_f32", _w(524, 1, 3, 1500, 96, 32, "f32")),
+    ("d112m64_bf16", _w(525, 2, 2, 1000, 112, 64, "bf16")),
+    ("d128m16_f32", _w(526, 1, 2, 777, 128, 16, "f32")),
+    ("d32m128_bf16_many_segments", _w(527, 1, 2, 40000, 32, 128, "bf16")),
+    ("d80m112_f32_one_token", _w(528, 1, 2, 1, 80, 112, "f32")),
+    ("d64m48_bf16", _w(529, 1, 4, 2048, 64, 48, "bf16")),
+    ("d128m128_f32", _w(530, 1, 2, 1200, 128, 128, "f32")),
+]
+
+
+def _check_grads(name, w, got, ref):
+    dq, dk, dv = (host(x) for x in got)
+    if w.N == 1:   # out_1 = V_1: dQ = dK = 0 up to the rounding residue of two equal terms
+        from tests.test_gpu_parity import _check_single_token_grads
+        q, k, v, g = wl.forward_inputs(w, with_dout=True)
+        _check_single_token_grads(q, k, v, g, dq, dk, w.dtype)
+        check(f"dv[{name}]", dv, ref[2], w.dtype)
+        return
+    check(f"dq[{name}]", dq, ref[0], w.dtype, floor=True)
+    check(f"dk[{name}]", dk, ref[1], w.dtype, floor=True)
+    check(f"dv[{name}]", dv, ref[2], w.dtype)
+
+
+@pytest.mark.parametrize("name,w", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_causal_head_sizes(name, w):
+    q, k, v, g = wl.forward_inputs(w, with_dout=True)
+    _say(f"backward causal {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    got = la.la_backward_causal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), dev(g, w.dtype))
+    torch.cuda.synchronize()
+    _check_grads(name, w, got, oracle.backward_causal(q, k, v, g))
+
+
+@pytest.mark.parametrize("name,w", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_noncausal_head_sizes(name, w):
+    q, k, v, g = wl.forward_inputs(w, with_dout=True)
+    _say(f"backward non-causal {name}: B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    got = la.la_backward_noncausal(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), dev(g, w.dtype))
+    torch.cuda.synchronize()
+    _check_grads(name, w, got, oracle.backward_noncausal(q, k, v, g))
+
+
+def test_backward_head_sizes_deterministic():
+    """The groups' partial sums are added in a fixed order: two calls give
+    bit-identical gradients."""
+    w = _w(531, 1, 2, 3000, 80, 112, "bf16")
+    q, k, v, g = (dev(x, w.dtype) for x in wl.forward_inputs(w, with_dout=True))
+    _say("backward determinism D80 M112 bf16")
+    a = la.la_backward_causal(q, k, v, g)
+    b = la.la_backward_causal(q, k, v, g)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def test_other_kernels_keep_their_head_sizes():
     q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(la.LAError) as e:
-        la.la_backward_causal(q, q, q, q)
+        la.la_forward_causal_poly2(q, q, q)
     assert e.value.status == 2
     with pytest.raises(la.LAError) as e:
         la.la_forward_causal(q[..., :40].contiguous(), q[..., :40].contiguous(), q)
