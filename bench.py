@@ -21,6 +21,10 @@ on, and reported next to the headline:
   * random Fourier features (R = 64) of q and k and the causal forward on them;
   * the degree-2 polynomial kernel: causal and non-causal at D = M = 32,
     causal at D = M = 64;
+  * the causal forward from a start state, returning the final state, on the
+    long-sequence workload;
+  * a head size outside {32, 64}: causal forward and backward at B=1, H=8,
+    N=16384, D=M=128 bf16 (the 16-column-group path);
   * the causal forward of the three smaller workloads;
   * the causal forward at B=1, H=8, D=M=64 bf16 for N = 512 .. 65536 (the
     sweep; --no-sweep leaves it out).
@@ -54,7 +58,8 @@ def _args():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal", "sweep", "small"],
+    ap.add_argument("--only", choices=["all", "forward", "decode", "backward", "rff", "poly", "noncausal", "sweep", "small",
+                                       "headsize"],
                     default="all",
                     help="restrict the timed work (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -254,6 +259,31 @@ def main():
         results["forward_median"]["reps"] = reps
         log(f"causal forward medians over {reps}: alternating {t_alt * 1e3:.4f}, cold {t_cold * 1e3:.4f}, "
             f"warm {t_warm * 1e3:.4f} ms")
+        # the same forward from a start state, returning the final state (a
+        # prompt handed to decode, or one piece of a cut sequence): the states
+        # are read and written in fp32 beside Q, K, V and out
+        gen = torch.Generator(device=dev).manual_seed(44)
+        s0 = torch.randn((w4.B, w4.H, w4.D, w4.M), generator=gen, device=dev)
+        z0 = torch.rand((w4.B, w4.H, w4.D), generator=gen, device=dev) + 0.5
+        s1, z1 = torch.empty_like(s0), torch.empty_like(z0)
+
+        def fwd_state(i):
+            q, k, v, _ = sets[i % 2]
+            st = lib.la_forward_causal_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), s0.data_ptr(),
+                                             z0.data_ptr(), s1.data_ptr(), z1.data_ptr(), w4.B, w4.H, w4.N, w4.D,
+                                             w4.M, la.LA_DTYPE_BF16, ws_f.data_ptr(), ws_f.numel(), sptr)
+            if st != 0:
+                raise la.LAError("forward_state", st)
+
+        for i in range(2):
+            fwd_state(i)
+        t = time_events(fwd_state, a.steps)
+        state_bytes = 2 * BH * (w4.D * w4.M + w4.D) * 4
+        results["forward_state"] = dict(ms_per_call=t / a.steps * 1e3, tok_heads_per_s=tok_heads * a.steps / t,
+                                        algorithmic_bytes=fwd_bytes + state_bytes,
+                                        hbm_frac=(fwd_bytes + state_bytes) / (t / a.steps) / 1e9 / HBM_PEAK_GBS)
+        log(f"causal forward from a start state, final state out: {t / a.steps * 1e3:.4f} ms/call")
+        del s0, z0, s1, z1
 
     # ---- backward / non-causal on the long-sequence workload --------------------------
     if a.only in ("all", "backward"):
@@ -416,6 +446,42 @@ def main():
         return dict(us_per_call=t / iters * 1e6, tok_heads_per_s=th * iters / t,
                     hbm_frac=by / (t / iters) / 1e9 / HBM_PEAK_GBS)
 
+    if a.only in ("all", "headsize"):
+        # a head size outside {32, 64}: the column-group path, forward and backward
+        wg = wl.Workload(12, "head size 128, B1 H8 N16384 D=M=128 bf16", 1, 8, 16384, 128, 128, "bf16")
+        qg, kg, vg, gg = (to_dev(x, "bf16") for x in wl.forward_inputs(wg, with_dout=True))
+        og = torch.empty_like(vg)
+        dqg, dkg, dvg = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+        wsf = torch.empty(la.la_workspace_size(la.LA_OP_FWD_CAUSAL, 1, 8, wg.N, 128, 128, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        wsb = torch.empty(la.la_workspace_size(la.LA_OP_BWD_CAUSAL, 1, 8, wg.N, 128, 128, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+
+        def gfwd(i):
+            st = lib.la_forward_causal(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), og.data_ptr(), 1, 8, wg.N, 128,
+                                       128, la.LA_DTYPE_BF16, wsf.data_ptr(), wsf.numel(), sptr)
+            if st != 0:
+                raise la.LAError("forward", st)
+
+        def gbwd(i):
+            st = lib.la_backward_causal(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), gg.data_ptr(), dqg.data_ptr(),
+                                        dkg.data_ptr(), dvg.data_ptr(), 1, 8, wg.N, 128, 128, la.LA_DTYPE_BF16,
+                                        wsb.data_ptr(), wsb.numel(), sptr)
+            if st != 0:
+                raise la.LAError("backward", st)
+
+        th = 8 * wg.N
+        res = {"workload": wg.name}
+        for name, fn, per_tok in (("forward", gfwd, 4 * 128 * 2), ("backward", gbwd, 7 * 128 * 2)):
+            for i in range(2):
+                fn(i)
+            t = time_events(fn, 10)
+            res[name] = dict(ms_per_call=t / 10 * 1e3, tok_heads_per_s=th * 10 / t,
+                             hbm_frac=th * per_tok / (t / 10) / 1e9 / HBM_PEAK_GBS)
+        results["head_size_128"] = res
+        log(f"head size 128: forward {res['forward']['ms_per_call']:.4f} ms, "
+            f"backward {res['backward']['ms_per_call']:.4f} ms")
+        del qg, kg, vg, gg, og, dqg, dkg, dvg, wsf, wsb
     if a.only in ("all", "small"):
         results["small_workloads"] = {wl.WORKLOADS[i].name: fwd_rate(wl.WORKLOADS[i]) for i in (1, 2, 3)}
     if (a.only == "all" and not a.no_sweep) or a.only == "sweep":
