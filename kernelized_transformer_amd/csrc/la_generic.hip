@@ -74,6 +74,51 @@ __device__ __forceinline__ typename IO<T>::vec4 load_col_tile(const T *__restric
 // Per-wavefront LDS staging for the token-contiguous copies (bf16 only).
 template <int DT> constexpr int gen_stage_elems() { return stage_elems<DT, 1>() + stage_elems<1, 1>(); }
 
+// ---- bf16: the chunk's Q and K rows shared by the column groups ---------------
+// The wavefronts of a workgroup (one per 16-column group) all need phi of
+// the same 16 rows of Q and K.  They load those rows together, as 16-byte
+// pieces of whole rows (piece p = 64 (w + ng i) + lane of the 2F pieces of 16
+// rows of F features), apply phi once per element, and stage them in one LDS
+// area that every wavefront reads its fragments from; the feature map is not
+// repeated per group.
+template <int F> struct CoopRows {
+    static constexpr int NP = (2 * F + 63) / 64;   // most pieces a lane moves (one wavefront)
+    dwordx4 x[NP];
+};
+template <int F>
+__device__ __forceinline__ void coop_load(CoopRows<F> &r, const bf16 *__restrict__ base, int64_t t0, int64_t t_end,
+                                          int w, int ng) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < CoopRows<F>::NP; ++i) {
+        const int p = 64 * (w + ng * i) + l;
+        if (p < 2 * F) {
+            const int e = 8 * p, row = e / F, col = e % F;
+            const int64_t t = imin64(t0 + row, t_end - 1);   // rows past the end read the last row
+            r.x[i] = *reinterpret_cast<const dwordx4 *>(base + t * F + col);
+        }
+    }
+}
+// Rows of F + kStagePad elements; PHI applies the feature map, MASK zeroes
+// rows at or beyond t_end.
+template <int F, bool PHI, bool MASK>
+__device__ __forceinline__ void coop_stage(lds_bf16 *stage, const CoopRows<F> &r, int64_t t0, int64_t t_end, int w,
+                                           int ng) {
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < CoopRows<F>::NP; ++i) {
+        const int p = 64 * (w + ng * i) + l;
+        if (p < 2 * F) {
+            const int e = 8 * p, row = e / F, col = e % F;
+            dwordx4 y = r.x[i];
+            if (PHI) y = phi8(y);
+            if (MASK && t0 + row >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<lds_dwordx4 *>(stage + row * (F + kStagePad) + col) = y;
+        }
+    }
+}
+template <int F> constexpr int coop_rows_elems() { return 16 * (F + kStagePad); }
+
 }  // namespace
 
 // ---- per-segment sums ---------------------------------------------------------
@@ -232,6 +277,161 @@ __global__ __launch_bounds__(512) void k_gen_output(const T *__restrict__ q, con
     }
 }
 
+
+// ---- bf16 variants: phi(Q), phi(K) staged once per chunk for all groups ----------
+// Same results as the kernels above up to the order of nothing (every
+// product and sum is formed the same way); the rows arrive as whole 16-byte
+// pieces, phi is applied once per element, and the staging is double
+// buffered: the wavefronts stage chunk c into buffer c % 2, meet at one
+// barrier, and read their fragments from it, so a wavefront that stages chunk
+// c + 2 has passed the barrier of chunk c + 1, which every wavefront reaches
+// only after its reads of chunk c.
+template <int DT, bool PHI>
+__global__ __launch_bounds__(512) void k_gen_segstate_bf16(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+                                                           float *__restrict__ ws, int64_t N, int64_t M, int64_t nseg,
+                                                           int64_t seg_tokens) {
+    constexpr int D = 16 * DT;
+    typedef bf16x4 Fr;
+    __shared__ __align__(16) bf16 shk[2][coop_rows_elems<D>()];
+    __shared__ __align__(16) bf16 sv_mem[8][stage_elems<1, 1>()];
+    const int ng = int(M / 16);
+    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
+    const bf16 *K = k + bh * N * D;
+    const bf16 *V = v + bh * N * M;
+    lds_bf16 *sv = (lds_bf16 *)sv_mem[cg];
+
+    f32x4 St[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) St[dt][0] = St[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    CoopRows<D> rk;
+    bf16x4 rv;
+    coop_load<D>(rk, K, t_begin, t_end, cg, ng);
+    rv = load_col_tile<bf16>(V, M, 16 * cg, t_begin, t_end);
+    int buf = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
+        lds_bf16 *sk = (lds_bf16 *)shk[buf];
+        coop_stage<D, PHI, true>(sk, rk, t0, t_end, cg, ng);   // rows past t_end are zero
+        Fr Vn[1][1];
+        {
+            const bf16x4 one[1][1] = {{rv}};
+            raw_frags<bf16, 16, 1>(Vn, one, t0, t_end);
+        }
+        coop_load<D>(rk, K, t0 + GCH, t_end, cg, ng);
+        rv = load_col_tile<bf16>(V, M, 16 * cg, t0 + GCH, t_end);
+        lds_barrier();
+        Fr KT[1][DT], VT[1][1];
+        transposed_frags_lds<D, 1>(KT, sk);
+        transpose_frags<1, 1>(VT, Vn, sv);
+        state_accumulate<Fr, D, 16, 1, false>(St, KT, VT);
+        buf ^= 1;
+    }
+    float *rec = ws + (bh * nseg + seg) * (int64_t(D) * M + D);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rec[(16 * dt + 4 * g + r) * M + 16 * cg + c] = St[dt][0][r];
+        if (cg == 0 && c == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rec[int64_t(D) * M + 16 * dt + 4 * g + r] = St[dt][1][r];
+        }
+    }
+}
+
+// Outputs, as k_gen_output.  No row masks (as in the fused forward's output
+// pass): rows past the end are copies of the last valid row, their outputs are
+// not stored, the causal mask keeps them out of every stored output, and the
+// state is not used after the last chunk.
+template <int DT, bool CAUSAL, bool PHI>
+__global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                                                         const bf16 *__restrict__ v, bf16 *__restrict__ out,
+                                                         const float *__restrict__ ws, int64_t N, int64_t M,
+                                                         int64_t nseg, int64_t seg_tokens) {
+    constexpr int D = 16 * DT;
+    typedef bf16x4 Fr;
+    __shared__ __align__(16) bf16 shq[2][coop_rows_elems<D>()];
+    __shared__ __align__(16) bf16 shk[CAUSAL ? 2 : 1][CAUSAL ? coop_rows_elems<D>() : 8];
+    __shared__ __align__(16) bf16 sv_mem[8][stage_elems<1, 1>()];
+    const int ng = int(M / 16);
+    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
+    const bf16 *Q = q + bh * N * D;
+    const bf16 *K = k + bh * N * D;
+    const bf16 *V = v + bh * N * M;
+    bf16 *O = out + bh * N * M;
+    lds_bf16 *sv = (lds_bf16 *)sv_mem[cg];
+
+    f32x4 St[DT][2];
+    {
+        const float *rec = ws + (bh * nseg + (CAUSAL ? seg : 0)) * (int64_t(D) * M + D);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                St[dt][0][r] = rec[(16 * dt + 4 * g + r) * M + 16 * cg + c];
+                St[dt][1][r] = rec[int64_t(D) * M + 16 * dt + 4 * g + r];
+            }
+    }
+    const Fr ones = frag_ones<Fr>();
+
+    CoopRows<D> rq, rk;
+    bf16x4 rv;
+    coop_load<D>(rq, Q, t_begin, t_end, cg, ng);
+    if (CAUSAL) {
+        coop_load<D>(rk, K, t_begin, t_end, cg, ng);
+        rv = load_col_tile<bf16>(V, M, 16 * cg, t_begin, t_end);
+    }
+    int buf = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
+        lds_bf16 *sq = (lds_bf16 *)shq[buf];
+        lds_bf16 *sk = (lds_bf16 *)shk[CAUSAL ? buf : 0];
+        coop_stage<D, PHI, false>(sq, rq, t0, t_end, cg, ng);
+        Fr Vn[1][1];
+        if (CAUSAL) {
+            coop_stage<D, PHI, false>(sk, rk, t0, t_end, cg, ng);
+            value_frags_unmasked(Vn[0][0], rv);
+        }
+        coop_load<D>(rq, Q, t0 + GCH, t_end, cg, ng);
+        if (CAUSAL) {
+            coop_load<D>(rk, K, t0 + GCH, t_end, cg, ng);
+            rv = load_col_tile<bf16>(V, M, 16 * cg, t0 + GCH, t_end);
+        }
+        lds_barrier();
+        Fr Qn[1][DT];
+        natural_frags_lds<D, 1>(Qn, sq);
+
+        f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            Fr SF[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<bf16>::to_frag(St[dt][mt]);
+            mma_tiles<Fr, DT>(Ot[mt], SF, Qn[0]);
+        }
+        if (CAUSAL) {
+            Fr Kn[1][DT], KT[1][DT], VT[1][1];
+            natural_frags_lds<D, 1>(Kn, sk);
+            transposed_frags_lds<D, 1>(KT, sk);
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+            mma_tiles<Fr, DT>(p, Kn[0], Qn[0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
+            const Fr PT = IO<bf16>::to_frag(p);
+            transpose_frags<1, 1>(VT, Vn, sv);
+            mma1(Ot[0], VT[0][0], PT);
+            mma1(Ot[1], ones, PT);
+            state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
+        }
+        const float inv = __builtin_amdgcn_rcpf(Ot[1][0]);
+        const int64_t t = t0 + c;
+        if (t < t_end) store4<bf16>(O + t * M + 16 * cg + 4 * g, IO<bf16>::from_f32(Ot[0] * inv));
+        buf ^= 1;
+    }
+}
 
 // ---- backward ----------------------------------------------------------------------
 // LDS per wavefront for the token-contiguous copies (bf16: the D x 32 state
@@ -575,6 +775,27 @@ size_t generic_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
     return kGenHeader + align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
 }
 
+// Per-segment sums of phi(K) [V, 1]^T (bf16: the shared-staging kernel).
+template <typename T, int DT>
+static void launch_gen_segstate(bool phi, dim3 grid, dim3 block, const void *k, const void *v, float *ws, int64_t N,
+                                int64_t M, const SegPlan &p, hipStream_t s) {
+    if constexpr (sizeof(T) == 2) {
+        if (phi)
+            hipLaunchKernelGGL((k_gen_segstate_bf16<DT, true>), grid, block, 0, s, (const bf16 *)k, (const bf16 *)v,
+                               ws, N, M, p.nseg, p.seg_tokens);
+        else
+            hipLaunchKernelGGL((k_gen_segstate_bf16<DT, false>), grid, block, 0, s, (const bf16 *)k,
+                               (const bf16 *)v, ws, N, M, p.nseg, p.seg_tokens);
+    } else {
+        if (phi)
+            hipLaunchKernelGGL((k_gen_segstate<T, DT, true>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N,
+                               M, p.nseg, p.seg_tokens);
+        else
+            hipLaunchKernelGGL((k_gen_segstate<T, DT, false>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N,
+                               M, p.nseg, p.seg_tokens);
+    }
+}
+
 template <typename T, int DT>
 static hipError_t run_generic(bool causal, bool phi, const void *q, const void *k, const void *v, void *out,
                               int64_t BH, int64_t N, int64_t M, float *ws, StateIO sio, hipStream_t s) {
@@ -582,12 +803,7 @@ static hipError_t run_generic(bool causal, bool phi, const void *q, const void *
     const SegPlan p = make_plan(BH, N, D, M);
     const dim3 grid(unsigned(BH * p.nseg)), block(unsigned(64 * (M / 16)));
     ws = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + kGenHeader);
-    if (phi)
-        hipLaunchKernelGGL((k_gen_segstate<T, DT, true>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N, M,
-                           p.nseg, p.seg_tokens);
-    else
-        hipLaunchKernelGGL((k_gen_segstate<T, DT, false>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N, M,
-                           p.nseg, p.seg_tokens);
+    launch_gen_segstate<T, DT>(phi, grid, block, k, v, ws, N, M, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ScanIO io;
@@ -598,11 +814,19 @@ static hipError_t run_generic(bool causal, bool phi, const void *q, const void *
     io.srec = int64_t(D) * M;
     if ((e = launch_scan(ws, BH, p.nseg, p.rec, causal ? 0 : 1, s, io)) != hipSuccess) return e;
 #define LA_GEN_OUT(C, P)                                                                                          \
-    hipLaunchKernelGGL((k_gen_output<T, DT, C, P>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v,   \
-                       (T *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens)
-    if (!causal) LA_GEN_OUT(false, true);
-    else if (phi) LA_GEN_OUT(true, true);
-    else LA_GEN_OUT(true, false);
+    if constexpr (sizeof(T) == 2)                                                                                 \
+        hipLaunchKernelGGL((k_gen_output_bf16<DT, C, P>), grid, block, 0, s, (const bf16 *)q, (const bf16 *)k,    \
+                           (const bf16 *)v, (bf16 *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens);          \
+    else                                                                                                          \
+        hipLaunchKernelGGL((k_gen_output<T, DT, C, P>), grid, block, 0, s, (const T *)q, (const T *)k,            \
+                           (const T *)v, (T *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens)
+    if (!causal) {
+        LA_GEN_OUT(false, true);
+    } else if (phi) {
+        LA_GEN_OUT(true, true);
+    } else {
+        LA_GEN_OUT(true, false);
+    }
 #undef LA_GEN_OUT
     return hipGetLastError();
 }
@@ -646,8 +870,7 @@ static hipError_t run_generic_backward(bool causal, const void *q, const void *k
     float *ibuf = causal ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.inv_off) : nullptr;
     float *hbuf = causal ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.h_off) : nullptr;
     const dim3 grid(unsigned(BH * p.nseg)), block(unsigned(64 * (M / 16)));
-    hipLaunchKernelGGL((k_gen_segstate<T, DT, true>), grid, block, 0, s, (const T *)k, (const T *)v, wsS, N, M,
-                       p.nseg, p.seg_tokens);
+    launch_gen_segstate<T, DT>(true, grid, block, k, v, wsS, N, M, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, causal ? 0 : 1, s)) != hipSuccess) return e;
