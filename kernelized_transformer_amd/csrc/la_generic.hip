@@ -469,9 +469,15 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     constexpr int D = 16 * DT;
     typedef typename IO<T>::frag Fr;
     typedef typename IO<T>::vec4 V4;
+    // bf16 (SHARED): phi(Q) and phi(K) rows staged once per chunk for every
+    // group, double-buffered (see k_gen_output_bf16); phi'(x) = min(phi(x), 1)
+    // is read off the staged phi
+    constexpr bool SHARED = sizeof(T) == 2;
+    constexpr int SR = SHARED ? coop_rows_elems<D>() : 8;
     __shared__ __align__(16) bf16 stage_mem[8][gbwd_stage_elems<T, DT>()];
     __shared__ __align__(16) f32x4 part[8][DT][64];
     __shared__ float hpart[8][16];
+    __shared__ __align__(16) bf16 shq[SHARED ? 2 : 1][SR], shk[SHARED && CAUSAL ? 2 : 1][SR];
     const int ng = int(M / 16);
     const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
@@ -502,28 +508,50 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     const Fr k0ones = frag_k0_ones<Fr>();
 
     V4 rq[1][DT], rk[1][DT], rv, rg;
+    CoopRows<D> cq, ck;
     auto load_all = [&](int64_t t0) {
-        load_chunk<T, D, 1>(rq, Q, t0, t_end);
-        if (CAUSAL) {
-            load_chunk<T, D, 1>(rk, K, t0, t_end);
-            rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
+        if constexpr (SHARED) {
+            coop_load<D>(cq, (const bf16 *)Q, t0, t_end, cg, ng);
+            if (CAUSAL) coop_load<D>(ck, (const bf16 *)K, t0, t_end, cg, ng);
+        } else {
+            load_chunk<T, D, 1>(rq, Q, t0, t_end);
+            if (CAUSAL) load_chunk<T, D, 1>(rk, K, t0, t_end);
         }
+        if (CAUSAL) rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
         rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
     };
     load_all(t_begin);
+    int buf = 0;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
         Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
-        phi_frags<T, D, 1>(Qn, rq, t0, t_end);
+        f32x4 dphq[DT];   // phi'(Q) of this lane's (token, 4 features) per tile
+        lds_bf16 *sq = (lds_bf16 *)shq[SHARED ? buf : 0];
+        lds_bf16 *sk = (lds_bf16 *)shk[SHARED && CAUSAL ? buf : 0];
         if (CAUSAL) {
-            phi_frags<T, D, 1>(Kn, rk, t0, t_end);
             const V4 one[1][1] = {{rv}};
             raw_frags<T, 16, 1>(Vn, one, t0, t_end);
         }
-        f32x4 qraw[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) qraw[dt] = IO<T>::to_f32(rq[0][dt]);
         const f32x4 graw = IO<T>::to_f32(rg);
-        load_all(t0 + GCH);   // rows past t_end read row t_end - 1
+        if constexpr (SHARED) {
+            coop_stage<D, true, true>(sq, cq, t0, t_end, cg, ng);   // rows past t_end are zero
+            if (CAUSAL) coop_stage<D, true, true>(sk, ck, t0, t_end, cg, ng);
+            load_all(t0 + GCH);   // rows past t_end read row t_end - 1
+            lds_barrier();
+            natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Qn), sq);
+            if (CAUSAL) natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Kn), sk);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 ph = IO<T>::to_f32(Qn[0][dt]);
+                dphq[dt] = f32x4{__builtin_fminf(ph[0], 1.f), __builtin_fminf(ph[1], 1.f),
+                                 __builtin_fminf(ph[2], 1.f), __builtin_fminf(ph[3], 1.f)};
+            }
+        } else {
+            phi_frags<T, D, 1>(Qn, rq, t0, t_end);
+            if (CAUSAL) phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) dphq[dt] = dphi4(IO<T>::to_f32(rq[0][dt]));
+            load_all(t0 + GCH);   // rows past t_end read row t_end - 1
+        }
         const int64_t t = t0 + c;   // this lane's query token
         const bool valid = t < t_end;
 
@@ -543,7 +571,10 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
             const Fr PT = IO<T>::to_frag(p);
-            transpose_frags<DT, 1>(KT, Kn, stage);
+            if constexpr (SHARED)
+                transposed_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&KT), sk);
+            else
+                transpose_frags<DT, 1>(KT, Kn, stage);
             transpose_frags<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
             mma1(Ot[0], VT[0][0], PT);
             mma1(Ot[1], ones, PT);
@@ -592,13 +623,16 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         }
         lds_barrier();
         for (int dt = cg; dt < DT; dt += ng) {   // the groups' sum, tiles dealt out over the wavefronts
-            const f32x4 dqv = reduce_rows<DT>(part, ng, dt) * dphi4(qraw[dt]);
+            const f32x4 dqv = reduce_rows<DT>(part, ng, dt) * dphq[dt];
             if (valid) store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dqv));
         }
 
         // this segment's reverse sums: Ra += phi(Q)^T [g | h] (its columns)
         Fr QT[1][DT], GT[1][2];
-        transpose_frags<DT, 1>(QT, Qn, stage);
+        if constexpr (SHARED)
+            transposed_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&QT), sq);
+        else
+            transpose_frags<DT, 1>(QT, Qn, stage);
         {
             const Fr gg[1][2] = {{Gn, Gh}};
             transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
@@ -610,6 +644,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         }
 
         if (CAUSAL) state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
+        buf ^= 1;
     }
     float *r1 = wsR + (bh * nseg + seg) * rec;
 #pragma unroll
@@ -636,8 +671,11 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
     constexpr int D = 16 * DT;
     typedef typename IO<T>::frag Fr;
     typedef typename IO<T>::vec4 V4;
+    constexpr bool SHARED = sizeof(T) == 2;   // as in k_gbwd_dq
+    constexpr int SR = SHARED ? coop_rows_elems<D>() : 8;
     __shared__ __align__(16) bf16 stage_mem[8][gbwd_stage_elems<T, DT>()];
     __shared__ __align__(16) f32x4 part[8][DT][64];
+    __shared__ __align__(16) bf16 shq[SHARED && CAUSAL ? 2 : 1][SR], shk[SHARED ? 2 : 1][SR];
     const int ng = int(M / 16);
     const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
@@ -667,10 +705,16 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
 
     const int64_t nch = (t_end - t_begin + GCH - 1) / GCH;
     V4 rq[1][DT], rk[1][DT], rv, rg;
+    CoopRows<D> cq, ck;
     float rh = 0.f, ri = 0.f;
     auto load_all = [&](int64_t t0) {
-        if (CAUSAL) load_chunk<T, D, 1>(rq, Q, t0, t_end);
-        load_chunk<T, D, 1>(rk, K, t0, t_end);
+        if constexpr (SHARED) {
+            if (CAUSAL) coop_load<D>(cq, (const bf16 *)Q, t0, t_end, cg, ng);
+            coop_load<D>(ck, (const bf16 *)K, t0, t_end, cg, ng);
+        } else {
+            if (CAUSAL) load_chunk<T, D, 1>(rq, Q, t0, t_end);
+            load_chunk<T, D, 1>(rk, K, t0, t_end);
+        }
         rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
         if (CAUSAL) {
             rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
@@ -679,12 +723,23 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         }
     };
     load_all(t_begin + (nch - 1) * GCH);
+    int buf = 0;
     for (int64_t ci = nch - 1; ci >= 0; --ci) {
         const int64_t t0 = t_begin + ci * GCH;
         Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
         Fr Gn = frag_zero<Fr>(), Gh = frag_zero<Fr>();
-        if (CAUSAL) phi_frags<T, D, 1>(Qn, rq, t0, t_end);
-        phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+        f32x4 dphk[DT];   // phi'(K) of this lane's (token, 4 features) per tile
+        lds_bf16 *sq = (lds_bf16 *)shq[SHARED && CAUSAL ? buf : 0];
+        lds_bf16 *sk = (lds_bf16 *)shk[SHARED ? buf : 0];
+        if constexpr (SHARED) {
+            if (CAUSAL) coop_stage<D, true, true>(sq, cq, t0, t_end, cg, ng);   // rows past t_end are zero
+            coop_stage<D, true, true>(sk, ck, t0, t_end, cg, ng);
+        } else {
+            if (CAUSAL) phi_frags<T, D, 1>(Qn, rq, t0, t_end);
+            phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) dphk[dt] = dphi4(IO<T>::to_f32(rk[0][dt]));
+        }
         {
             const V4 one[1][1] = {{rv}};
             raw_frags<T, 16, 1>(Vn, one, t0, t_end);
@@ -693,10 +748,18 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             Gn = IO<T>::to_frag(IO<T>::to_f32(rg) * ri);
             Gh = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
         }
-        f32x4 kraw[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) kraw[dt] = IO<T>::to_f32(rk[0][dt]);
         if (ci > 0) load_all(t0 - GCH);
+        if constexpr (SHARED) {
+            lds_barrier();
+            if (CAUSAL) natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Qn), sq);
+            natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Kn), sk);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 ph = IO<T>::to_f32(Kn[0][dt]);
+                dphk[dt] = f32x4{__builtin_fminf(ph[0], 1.f), __builtin_fminf(ph[1], 1.f),
+                                 __builtin_fminf(ph[2], 1.f), __builtin_fminf(ph[3], 1.f)};
+            }
+        }
         const int64_t t = t0 + c;   // this lane's key token
         const bool valid = t < t_end;
 
@@ -710,7 +773,10 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         Fr QT[1][DT], GT[1][2];
         Fr Pf = frag_zero<Fr>(), dAf = frag_zero<Fr>();
         if (CAUSAL) {
-            transpose_frags<DT, 1>(QT, Qn, stage);
+            if constexpr (SHARED)
+                transposed_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&QT), sq);
+            else
+                transpose_frags<DT, 1>(QT, Qn, stage);
             {
                 const Fr gg[1][2] = {{Gn, Gh}};
                 transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
@@ -743,7 +809,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         }
         lds_barrier();
         for (int dt = cg; dt < DT; dt += ng) {
-            const f32x4 dkv = reduce_rows<DT>(part, ng, dt) * dphi4(kraw[dt]);
+            const f32x4 dkv = reduce_rows<DT>(part, ng, dt) * dphk[dt];
             if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dkv));
         }
         // dV^T[m][j] (its columns) = sum_i g[i][m] P[i][j] + sum_d R[d][m] phi(k_j)[d]
@@ -762,6 +828,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             }
         }
         lds_barrier();   // every group has read `part` before the next chunk writes it
+        buf ^= 1;
     }
 }
 
