@@ -537,8 +537,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             if (CAUSAL) coop_stage<D, true, true>(sk, ck, t0, t_end, cg, ng);
             load_all(t0 + GCH);   // rows past t_end read row t_end - 1
             lds_barrier();
-            natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Qn), sq);
-            if (CAUSAL) natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Kn), sk);
+            natural_frags_lds<D, 1>(Qn, sq);
+            if (CAUSAL) natural_frags_lds<D, 1>(Kn, sk);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const f32x4 ph = IO<T>::to_f32(Qn[0][dt]);
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
             const Fr PT = IO<T>::to_frag(p);
             if constexpr (SHARED)
-                transposed_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&KT), sk);
+                transposed_frags_lds<D, 1>(KT, sk);
             else
                 transpose_frags<DT, 1>(KT, Kn, stage);
             transpose_frags<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         // this segment's reverse sums: Ra += phi(Q)^T [g | h] (its columns)
         Fr QT[1][DT], GT[1][2];
         if constexpr (SHARED)
-            transposed_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&QT), sq);
+            transposed_frags_lds<D, 1>(QT, sq);
         else
             transpose_frags<DT, 1>(QT, Qn, stage);
         {
@@ -751,8 +751,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         if (ci > 0) load_all(t0 - GCH);
         if constexpr (SHARED) {
             lds_barrier();
-            if (CAUSAL) natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Qn), sq);
-            natural_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&Kn), sk);
+            if (CAUSAL) natural_frags_lds<D, 1>(Qn, sq);
+            natural_frags_lds<D, 1>(Kn, sk);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const f32x4 ph = IO<T>::to_f32(Kn[0][dt]);
@@ -774,7 +774,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         Fr Pf = frag_zero<Fr>(), dAf = frag_zero<Fr>();
         if (CAUSAL) {
             if constexpr (SHARED)
-                transposed_frags_lds<D, 1>(*reinterpret_cast<bf16x4(*)[1][DT]>(&QT), sq);
+                transposed_frags_lds<D, 1>(QT, sq);
             else
                 transpose_frags<DT, 1>(QT, Qn, stage);
             {
