@@ -81,16 +81,19 @@ template <int DT> constexpr int gen_stage_elems() { return stage_elems<DT, 1>() 
 // rows of F features), apply phi once per element, and stage them in one LDS
 // area that every wavefront reads its fragments from; the feature map is not
 // repeated per group.
-template <int F> struct CoopRows {
-    static constexpr int NP = (2 * F + 63) / 64;   // most pieces a lane moves (one wavefront)
+// NPW: the most pieces one lane moves, (2F + 63) / 64 when one wavefront
+// does all; the host may pass fewer when the segment's ng wavefronts cover the
+// 2F pieces with that many each (64 ng NPW >= 2F), which saves registers.
+template <int F, int NPW = (2 * F + 63) / 64> struct CoopRows {
+    static constexpr int NP = NPW;
     dwordx4 x[NP];
 };
-template <int F>
-__device__ __forceinline__ void coop_load(CoopRows<F> &r, const bf16 *__restrict__ base, int64_t t0, int64_t t_end,
-                                          int w, int ng) {
+template <int F, int NPW>
+__device__ __forceinline__ void coop_load(CoopRows<F, NPW> &r, const bf16 *__restrict__ base, int64_t t0,
+                                          int64_t t_end, int w, int ng) {
     const int l = lane_id();
 #pragma unroll
-    for (int i = 0; i < CoopRows<F>::NP; ++i) {
+    for (int i = 0; i < NPW; ++i) {
         const int p = 64 * (w + ng * i) + l;
         if (p < 2 * F) {
             const int e = 8 * p, row = e / F, col = e % F;
@@ -101,12 +104,12 @@ __device__ __forceinline__ void coop_load(CoopRows<F> &r, const bf16 *__restrict
 }
 // Rows of F + kStagePad elements; PHI applies the feature map, MASK zeroes
 // rows at or beyond t_end.
-template <int F, bool PHI, bool MASK>
-__device__ __forceinline__ void coop_stage(lds_bf16 *stage, const CoopRows<F> &r, int64_t t0, int64_t t_end, int w,
-                                           int ng) {
+template <int F, bool PHI, bool MASK, int NPW>
+__device__ __forceinline__ void coop_stage(lds_bf16 *stage, const CoopRows<F, NPW> &r, int64_t t0, int64_t t_end,
+                                           int w, int ng) {
     const int l = lane_id();
 #pragma unroll
-    for (int i = 0; i < CoopRows<F>::NP; ++i) {
+    for (int i = 0; i < NPW; ++i) {
         const int p = 64 * (w + ng * i) + l;
         if (p < 2 * F) {
             const int e = 8 * p, row = e / F, col = e % F;
@@ -118,6 +121,28 @@ __device__ __forceinline__ void coop_stage(lds_bf16 *stage, const CoopRows<F> &r
     }
 }
 template <int F> constexpr int coop_rows_elems() { return 16 * (F + kStagePad); }
+
+// One token-contiguous tile (the layout of transposed_frags_lds) of bf16 rows
+// staged in LDS with a row stride of S elements: rows 16 tt .. 16 tt + 15,
+// feature tile ft.
+__device__ __forceinline__ bf16x4 transposed_tile_lds(const lds_bf16 *stage, int S, int tt, int ft) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4 *>(
+        const_cast<lds_bf16 *>(stage) + (16 * tt + 4 * g + (c >> 2)) * S + 16 * ft + 4 * (c & 3)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// phi'(x) = min(phi(x), 1) of tile ft of rows staged by coop_stage<F, true, .>
+// (phi(x) <= 1 exactly where x <= 0, where phi' = phi = exp(x)), in the
+// natural layout: lane (c, g) gets row c, features 16 ft + 4g .. + 3.  Read at
+// the point of use, so no wavefront holds phi' of every tile through a chunk.
+template <int F>
+__device__ __forceinline__ f32x4 dphi_staged(const lds_bf16 *stage, int ft) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+    const f32x4 ph = IO<bf16>::to_f32(*reinterpret_cast<const lds_bf16x4 *>(stage + c * (F + kStagePad) + 16 * ft + 4 * g));
+    return f32x4{__builtin_fminf(ph[0], 1.f), __builtin_fminf(ph[1], 1.f), __builtin_fminf(ph[2], 1.f),
+                 __builtin_fminf(ph[3], 1.f)};
+}
 
 }  // namespace
 
@@ -459,7 +484,11 @@ __device__ __forceinline__ f32x4 reduce_rows(const f32x4 (*part)[DT][64], int ng
 // Forward direction.  Wavefront cg: S and Z slice St (Z replicated, as in
 // k_gen_output), this segment's reverse sums Ra = sum_i phi(q_i) [g_i, h_i]^T
 // restricted to its columns (u, in column 0 of the second tile, on group 0).
-template <typename T, int DT, bool CAUSAL>
+// bf16 keeps the register count within two wavefronts per SIMD for every D:
+// the state's bf16 copy goes to LDS as soon as it is formed, and the operand
+// tiles of the dQ products (S^T, phi(K)^T) are read back from LDS one tile at
+// a time where they are used.
+template <typename T, int DT, bool CAUSAL, int NPW>
 __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const T *__restrict__ k,
                                                  const T *__restrict__ v, const T *__restrict__ dout,
                                                  T *__restrict__ dq, const float *__restrict__ wsS,
@@ -474,6 +503,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     // is read off the staged phi
     constexpr bool SHARED = sizeof(T) == 2;
     constexpr int SR = SHARED ? coop_rows_elems<D>() : 8;
+    constexpr int SS = D + kStagePad;   // row stride of the staged rows and of the state copy
     __shared__ __align__(16) bf16 stage_mem[8][gbwd_stage_elems<T, DT>()];
     __shared__ __align__(16) f32x4 part[8][DT][64];
     __shared__ float hpart[8][16];
@@ -507,8 +537,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     const Fr ones = frag_ones<Fr>();
     const Fr k0ones = frag_k0_ones<Fr>();
 
-    V4 rq[1][DT], rk[1][DT], rv, rg;
-    CoopRows<D> cq, ck;
+    V4 rq[1][SHARED ? 1 : DT], rk[1][SHARED ? 1 : DT], rv, rg;
+    CoopRows<D, SHARED ? NPW : 1> cq, ck;
     auto load_all = [&](int64_t t0) {
         if constexpr (SHARED) {
             coop_load<D>(cq, (const bf16 *)Q, t0, t_end, cg, ng);
@@ -524,7 +554,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     int buf = 0;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
         Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
-        f32x4 dphq[DT];   // phi'(Q) of this lane's (token, 4 features) per tile
+        f32x4 dphq[SHARED ? 1 : DT];   // fp32: phi'(Q) of this lane's (token, 4 features) per tile
         lds_bf16 *sq = (lds_bf16 *)shq[SHARED ? buf : 0];
         lds_bf16 *sk = (lds_bf16 *)shk[SHARED && CAUSAL ? buf : 0];
         if (CAUSAL) {
@@ -539,12 +569,6 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             lds_barrier();
             natural_frags_lds<D, 1>(Qn, sq);
             if (CAUSAL) natural_frags_lds<D, 1>(Kn, sk);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f32x4 ph = IO<T>::to_f32(Qn[0][dt]);
-                dphq[dt] = f32x4{__builtin_fminf(ph[0], 1.f), __builtin_fminf(ph[1], 1.f),
-                                 __builtin_fminf(ph[2], 1.f), __builtin_fminf(ph[3], 1.f)};
-            }
         } else {
             phi_frags<T, D, 1>(Qn, rq, t0, t_end);
             if (CAUSAL) phi_frags<T, D, 1>(Kn, rk, t0, t_end);
@@ -555,27 +579,43 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         const int64_t t = t0 + c;   // this lane's query token
         const bool valid = t < t_end;
 
-        // out^T of this group's columns (Ot[0]) and den (every row of Ot[1])
-        f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        Fr SF[2][DT];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = IO<T>::to_frag(St[dt][mt]);
-            mma_tiles<Fr, DT>(Ot[mt], SF[mt], Qn[0]);
-        }
-        Fr KT[1][DT], VT[1][1];
+        // V^T before the state copy takes the staging area (bf16: the
+        // transposing write and read use the area the copy overwrites next)
+        Fr VT[1][1];
+        if (CAUSAL) transpose_frags<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
+
+        // intra-chunk scores P^T[j][i] = phi(k_j) . phi(q_i), j <= i (first, so
+        // that phi(K) is no longer held while the state is read out)
+        Fr PT = frag_zero<Fr>();
+        Fr KT[1][SHARED ? 1 : DT];
         if (CAUSAL) {
             f32x4 p = {0.f, 0.f, 0.f, 0.f};
             mma_tiles<Fr, DT>(p, Kn[0], Qn[0]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-            const Fr PT = IO<T>::to_frag(p);
-            if constexpr (SHARED)
-                transposed_frags_lds<D, 1>(KT, sk);
-            else
-                transpose_frags<DT, 1>(KT, Kn, stage);
-            transpose_frags<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
+            PT = IO<T>::to_frag(p);
+            if constexpr (!SHARED) transpose_frags<DT, 1>(KT, Kn, stage);
+        }
+
+        // out^T of this group's columns (Ot[0]) and den (every row of Ot[1]);
+        // fp32 keeps the state's operand copy SF for the dQ products, bf16
+        // writes it to LDS (tile row mt, feature tile dt) as it goes
+        f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        Fr SF[2][SHARED ? 1 : DT];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            Fr sf[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                sf[dt] = IO<T>::to_frag(St[dt][mt]);
+                if constexpr (SHARED)
+                    *reinterpret_cast<lds_bf16x4 *>(stage + (16 * mt + c) * SS + 16 * dt + 4 * g) = sf[dt];
+                else
+                    SF[mt][dt] = sf[dt];
+            }
+            mma_tiles<Fr, DT>(Ot[mt], sf, Qn[0]);
+        }
+        if (CAUSAL) {
             mma1(Ot[0], VT[0][0], PT);
             mma1(Ot[1], ones, PT);
         }
@@ -611,19 +651,35 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
 
         // this group's part of dL/dphi(q)^T[d][i]: sum_j phi(k_j)[d] dA^T[j][i]
         // + S[d][its columns] g_i (+ Z[d] h_i on group 0)
-        Fr SFT[2][DT];
-        transpose_frags<DT, 2>(SFT, SF, stage);
+        if constexpr (SHARED) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (CAUSAL) mma1(acc, KT[0][dt], dAT);
-            mma1(acc, SFT[0][dt], Gn);
-            if (cg == 0) mma1(acc, SFT[1][dt], Gh);
-            part[cg][dt][lane] = acc;
+            for (int dt = 0; dt < DT; ++dt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (CAUSAL) mma1(acc, transposed_tile_lds(sk, SS, 0, dt), dAT);
+                mma1(acc, transposed_tile_lds(stage, SS, 0, dt), Gn);
+                if (cg == 0) mma1(acc, transposed_tile_lds(stage, SS, 1, dt), Gh);
+                part[cg][dt][lane] = acc;
+            }
+        } else {
+            Fr SFT[2][DT];
+            transpose_frags<DT, 2>(SFT, SF, stage);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (CAUSAL) mma1(acc, KT[0][dt], dAT);
+                mma1(acc, SFT[0][dt], Gn);
+                if (cg == 0) mma1(acc, SFT[1][dt], Gh);
+                part[cg][dt][lane] = acc;
+            }
         }
         lds_barrier();
         for (int dt = cg; dt < DT; dt += ng) {   // the groups' sum, tiles dealt out over the wavefronts
-            const f32x4 dqv = reduce_rows<DT>(part, ng, dt) * dphq[dt];
+            f32x4 dph;
+            if constexpr (SHARED)
+                dph = dphi_staged<D>(sq, dt);
+            else
+                dph = dphq[dt];
+            const f32x4 dqv = reduce_rows<DT>(part, ng, dt) * dph;
             if (valid) store4<T>(DQ + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dqv));
         }
 
@@ -643,7 +699,15 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             if (cg == 0) mma1(Ra[dt][1], QT[0][dt], GT[0][1]);
         }
 
-        if (CAUSAL) state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
+        if (CAUSAL) {
+            if constexpr (SHARED) {
+                Fr KTs[1][DT];
+                transposed_frags_lds<D, 1>(KTs, sk);
+                state_accumulate<Fr, D, 16, 1, true>(St, KTs, VT);
+            } else {
+                state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
+            }
+        }
         buf ^= 1;
     }
     float *r1 = wsR + (bh * nseg + seg) * rec;
@@ -660,8 +724,9 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
 
 // Reverse direction.  Wavefront cg carries R[:, its columns] and (group 0)
 // u, walking the chunks last to first; writes dV of its columns and, with
-// the other groups, dK.
-template <typename T, int DT, bool CAUSAL>
+// the other groups, dK.  bf16 holds the state's operand copy in LDS and reads
+// the transposed tiles (R^T, phi(Q)^T) where they are used, as k_gbwd_dq does.
+template <typename T, int DT, bool CAUSAL, int NPW>
 __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, const T *__restrict__ k,
                                                    const T *__restrict__ v, const T *__restrict__ dout,
                                                    const float *__restrict__ ibuf, const float *__restrict__ hbuf,
@@ -673,6 +738,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
     typedef typename IO<T>::vec4 V4;
     constexpr bool SHARED = sizeof(T) == 2;   // as in k_gbwd_dq
     constexpr int SR = SHARED ? coop_rows_elems<D>() : 8;
+    constexpr int SS = D + kStagePad;
     __shared__ __align__(16) bf16 stage_mem[8][gbwd_stage_elems<T, DT>()];
     __shared__ __align__(16) f32x4 part[8][DT][64];
     __shared__ __align__(16) bf16 shq[SHARED && CAUSAL ? 2 : 1][SR], shk[SHARED ? 2 : 1][SR];
@@ -704,8 +770,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
     const Fr k0ones = frag_k0_ones<Fr>();
 
     const int64_t nch = (t_end - t_begin + GCH - 1) / GCH;
-    V4 rq[1][DT], rk[1][DT], rv, rg;
-    CoopRows<D> cq, ck;
+    V4 rq[1][SHARED ? 1 : DT], rk[1][SHARED ? 1 : DT], rv, rg;
+    CoopRows<D, SHARED ? NPW : 1> cq, ck;
     float rh = 0.f, ri = 0.f;
     auto load_all = [&](int64_t t0) {
         if constexpr (SHARED) {
@@ -728,7 +794,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         const int64_t t0 = t_begin + ci * GCH;
         Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
         Fr Gn = frag_zero<Fr>(), Gh = frag_zero<Fr>();
-        f32x4 dphk[DT];   // phi'(K) of this lane's (token, 4 features) per tile
+        f32x4 dphk[SHARED ? 1 : DT];   // fp32: phi'(K) of this lane's (token, 4 features) per tile
         lds_bf16 *sq = (lds_bf16 *)shq[SHARED && CAUSAL ? buf : 0];
         lds_bf16 *sk = (lds_bf16 *)shk[SHARED ? buf : 0];
         if constexpr (SHARED) {
@@ -753,36 +819,22 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             lds_barrier();
             if (CAUSAL) natural_frags_lds<D, 1>(Qn, sq);
             natural_frags_lds<D, 1>(Kn, sk);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f32x4 ph = IO<T>::to_f32(Kn[0][dt]);
-                dphk[dt] = f32x4{__builtin_fminf(ph[0], 1.f), __builtin_fminf(ph[1], 1.f),
-                                 __builtin_fminf(ph[2], 1.f), __builtin_fminf(ph[3], 1.f)};
-            }
         }
         const int64_t t = t0 + c;   // this lane's key token
         const bool valid = t < t_end;
 
-        Fr RF[2][DT], RFT[2][DT];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) RF[mt][dt] = IO<T>::to_frag(Rr[dt][mt]);
-        transpose_frags<DT, 2>(RFT, RF, stage);
+        // [g | h]^T before the state copy takes the staging area (bf16: the
+        // transposing write and read use the area the copy overwrites next)
+        Fr GT[1][2];
+        if (CAUSAL) {
+            const Fr gg[1][2] = {{Gn, Gh}};
+            transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
+        }
 
-        Fr QT[1][DT], GT[1][2];
+        // P[i][j] = phi(q_i) . phi(k_j); dA[i][j] = g_i . v_j over this group's columns
+        // (group 0 adds h_i); both masked to i >= j
         Fr Pf = frag_zero<Fr>(), dAf = frag_zero<Fr>();
         if (CAUSAL) {
-            if constexpr (SHARED)
-                transposed_frags_lds<D, 1>(QT, sq);
-            else
-                transpose_frags<DT, 1>(QT, Qn, stage);
-            {
-                const Fr gg[1][2] = {{Gn, Gh}};
-                transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
-            }
-            // P[i][j] = phi(q_i) . phi(k_j); dA[i][j] = g_i . v_j over this group's columns
-            // (group 0 adds h_i); both masked to i >= j
             f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
             mma_tiles<Fr, DT>(p, Qn[0], Kn[0]);
             mma1(da, Gn, Vn[0][0]);
@@ -797,34 +849,75 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             dAf = IO<T>::to_frag(da);
         }
 
-        // this group's part of dL/dphi(k)^T[d][j]: sum_i phi(q_i)[d] dA[i][j]
-        // + R[d][its columns] v_j (+ u[d] on group 0)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (CAUSAL) mma1(acc, QT[0][dt], dAf);
-            mma1(acc, RFT[0][dt], Vn[0][0]);
-            if (cg == 0) mma1(acc, RFT[1][dt], k0ones);
-            part[cg][dt][lane] = acc;
-        }
-        lds_barrier();
-        for (int dt = cg; dt < DT; dt += ng) {
-            const f32x4 dkv = reduce_rows<DT>(part, ng, dt) * dphk[dt];
-            if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dkv));
-        }
-        // dV^T[m][j] (its columns) = sum_i g[i][m] P[i][j] + sum_d R[d][m] phi(k_j)[d]
+        // dV^T[m][j] (its columns) = sum_i g[i][m] P[i][j] + sum_d R[d][m] phi(k_j)[d];
+        // the state's operand copy RF is formed here (bf16: written to LDS,
+        // tile row mt, feature tile dt, for the transposed reads below)
+        Fr RF[2][SHARED ? 1 : DT];
         {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (CAUSAL) mma1(acc, GT[0][0], Pf);
-            mma_tiles<Fr, DT>(acc, RF[0], Kn[0]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                Fr rf[DT];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    rf[dt] = IO<T>::to_frag(Rr[dt][mt]);
+                    if constexpr (SHARED)
+                        *reinterpret_cast<lds_bf16x4 *>(stage + (16 * mt + c) * SS + 16 * dt + 4 * g) = rf[dt];
+                    else
+                        RF[mt][dt] = rf[dt];
+                }
+                if (mt == 0) mma_tiles<Fr, DT>(acc, rf, Kn[0]);
+            }
             if (valid) store4<T>(DV + t * M + 16 * cg + 4 * g, IO<T>::from_f32(acc));
+        }
+
+        // this group's part of dL/dphi(k)^T[d][j]: sum_i phi(q_i)[d] dA[i][j]
+        // + R[d][its columns] v_j (+ u[d] on group 0)
+        Fr QT[1][SHARED ? 1 : DT];
+        if constexpr (SHARED) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (CAUSAL) mma1(acc, transposed_tile_lds(sq, SS, 0, dt), dAf);
+                mma1(acc, transposed_tile_lds(stage, SS, 0, dt), Vn[0][0]);
+                if (cg == 0) mma1(acc, transposed_tile_lds(stage, SS, 1, dt), k0ones);
+                part[cg][dt][lane] = acc;
+            }
+        } else {
+            Fr RFT[2][DT];
+            transpose_frags<DT, 2>(RFT, RF, stage);
+            if (CAUSAL) transpose_frags<DT, 1>(QT, Qn, stage);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (CAUSAL) mma1(acc, QT[0][dt], dAf);
+                mma1(acc, RFT[0][dt], Vn[0][0]);
+                if (cg == 0) mma1(acc, RFT[1][dt], k0ones);
+                part[cg][dt][lane] = acc;
+            }
+        }
+        lds_barrier();
+        for (int dt = cg; dt < DT; dt += ng) {
+            f32x4 dph;
+            if constexpr (SHARED)
+                dph = dphi_staged<D>(sk, dt);
+            else
+                dph = dphk[dt];
+            const f32x4 dkv = reduce_rows<DT>(part, ng, dt) * dph;
+            if (valid) store4<T>(DK + t * D + 16 * dt + 4 * g, IO<T>::from_f32(dkv));
         }
         // carry R (and u) towards earlier tokens
         if (CAUSAL) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                mma1(Rr[dt][0], QT[0][dt], GT[0][0]);
-                if (cg == 0) mma1(Rr[dt][1], QT[0][dt], GT[0][1]);
+                Fr qt;
+                if constexpr (SHARED)
+                    qt = transposed_tile_lds(sq, SS, 0, dt);
+                else
+                    qt = QT[0][dt];
+                mma1(Rr[dt][0], qt, GT[0][0]);
+                if (cg == 0) mma1(Rr[dt][1], qt, GT[0][1]);
             }
         }
         lds_barrier();   // every group has read `part` before the next chunk writes it
@@ -925,6 +1018,35 @@ hipError_t launch_forward_generic(bool causal, int dt, const void *q, const void
 }
 
 
+// The dQ pass, the reverse scan and the dK/dV pass, with NPW pieces of each
+// chunk's Q and K rows per lane (bf16; unused for fp32).
+template <typename T, int DT, int NPW>
+static hipError_t run_gbwd_passes(bool causal, dim3 grid, dim3 block, const void *q, const void *k, const void *v,
+                                  const void *dout, void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t M,
+                                  const SegPlan &p, float *wsS, float *wsR, float *ibuf, float *hbuf,
+                                  hipStream_t s) {
+    if (causal)
+        hipLaunchKernelGGL((k_gbwd_dq<T, DT, true, NPW>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, M, p.nseg,
+                           p.seg_tokens);
+    else
+        hipLaunchKernelGGL((k_gbwd_dq<T, DT, false, NPW>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, M, p.nseg,
+                           p.seg_tokens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if ((e = launch_scan(wsR, BH, p.nseg, p.rec, causal ? 2 : 1, s)) != hipSuccess) return e;
+    if (causal)
+        hipLaunchKernelGGL((k_gbwd_dkdv<T, DT, true, NPW>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
+                           (T *)dv, (const float *)wsR, N, M, p.nseg, p.seg_tokens);
+    else
+        hipLaunchKernelGGL((k_gbwd_dkdv<T, DT, false, NPW>), grid, block, 0, s, (const T *)q, (const T *)k,
+                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
+                           (T *)dv, (const float *)wsR, N, M, p.nseg, p.seg_tokens);
+    return hipGetLastError();
+}
+
 template <typename T, int DT>
 static hipError_t run_generic_backward(bool causal, const void *q, const void *k, const void *v, const void *dout,
                                        void *dq, void *dk, void *dv, int64_t BH, int64_t N, int64_t M, float *ws,
@@ -941,25 +1063,16 @@ static hipError_t run_generic_backward(bool causal, const void *q, const void *k
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, causal ? 0 : 1, s)) != hipSuccess) return e;
-    if (causal)
-        hipLaunchKernelGGL((k_gbwd_dq<T, DT, true>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v,
-                           (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, M, p.nseg,
-                           p.seg_tokens);
-    else
-        hipLaunchKernelGGL((k_gbwd_dq<T, DT, false>), grid, block, 0, s, (const T *)q, (const T *)k, (const T *)v,
-                           (const T *)dout, (T *)dq, (const float *)wsS, wsR, ibuf, hbuf, N, M, p.nseg,
-                           p.seg_tokens);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_scan(wsR, BH, p.nseg, p.rec, causal ? 2 : 1, s)) != hipSuccess) return e;
-    if (causal)
-        hipLaunchKernelGGL((k_gbwd_dkdv<T, DT, true>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
-                           (T *)dv, (const float *)wsR, N, M, p.nseg, p.seg_tokens);
-    else
-        hipLaunchKernelGGL((k_gbwd_dkdv<T, DT, false>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (const T *)dout, (const float *)ibuf, (const float *)hbuf, (T *)dk,
-                           (T *)dv, (const float *)wsR, N, M, p.nseg, p.seg_tokens);
-    return hipGetLastError();
+    // one piece per lane when the M / 16 wavefronts cover a chunk's 2 D
+    // sixteen-byte pieces of Q (or K) once: 64 (M / 16) >= 2 D
+    constexpr int NP = CoopRows<D>::NP;
+    if (sizeof(T) == 4 || NP == 1 || 64 * (M / 16) >= 2 * D)
+        return run_gbwd_passes<T, DT, 1>(causal, grid, block, q, k, v, dout, dq, dk, dv, BH, N, M, p, wsS, wsR, ibuf,
+                                         hbuf, s);
+    if constexpr (sizeof(T) == 2 && NP > 1)
+        return run_gbwd_passes<T, DT, NP>(causal, grid, block, q, k, v, dout, dq, dk, dv, BH, N, M, p, wsS, wsR,
+                                          ibuf, hbuf, s);
+    return hipErrorInvalidValue;
 }
 
 template <typename T>
