@@ -42,6 +42,14 @@ inline SegPlan make_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     cps = cps < 1 ? 1 : cps;
     const int64_t min_cps = ceil_div(nch, kMaxSegPerHead);
     if (cps < min_cps) cps = min_cps;
+    if (!fused_head_sizes(D, M)) {
+        // The column-group kernels' records grow as D M: keep the record
+        // traffic (written, scanned in place, read back: four passes of
+        // 4 (D M + D) bytes per segment) within half of the bf16 input and
+        // output bytes of the segment's tokens, 2 (2 D + 2 M) per token.
+        const int64_t rec_cps = ceil_div(ceil_div(16 * (D * M + D), 2 * (D + M)), kChunk);
+        if (cps < rec_cps) cps = rec_cps;
+    }
     p.seg_tokens = cps * kChunk;
     p.nseg = ceil_div(N, p.seg_tokens);
     p.rec = D * M + D;
