@@ -311,7 +311,7 @@ __global__ __launch_bounds__(512) void k_gen_output(const T *__restrict__ q, con
 // barrier, and read their fragments from it, so a wavefront that stages chunk
 // c + 2 has passed the barrier of chunk c + 1, which every wavefront reaches
 // only after its reads of chunk c.
-template <int DT, bool PHI>
+template <int DT, bool PHI, int NPW>
 __global__ __launch_bounds__(512) void k_gen_segstate_bf16(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
                                                            float *__restrict__ ws, int64_t N, int64_t M, int64_t nseg,
                                                            int64_t seg_tokens) {
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(512) void k_gen_segstate_bf16(const bf16 *__restric
     f32x4 St[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) St[dt][0] = St[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    CoopRows<D> rk;
+    CoopRows<D, NPW> rk;
     bf16x4 rv;
     coop_load<D>(rk, K, t_begin, t_end, cg, ng);
     rv = load_col_tile<bf16>(V, M, 16 * cg, t_begin, t_end);
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(512) void k_gen_segstate_bf16(const bf16 *__restric
 // pass): rows past the end are copies of the last valid row, their outputs are
 // not stored, the causal mask keeps them out of every stored output, and the
 // state is not used after the last chunk.
-template <int DT, bool CAUSAL, bool PHI>
+template <int DT, bool CAUSAL, bool PHI, int NPW>
 __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                                          const bf16 *__restrict__ v, bf16 *__restrict__ out,
                                                          const float *__restrict__ ws, int64_t N, int64_t M,
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict_
     }
     const Fr ones = frag_ones<Fr>();
 
-    CoopRows<D> rq, rk;
+    CoopRows<D, NPW> rq, rk;
     bf16x4 rv;
     coop_load<D>(rq, Q, t_begin, t_end, cg, ng);
     if (CAUSAL) {
@@ -935,17 +935,32 @@ size_t generic_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
     return kGenHeader + align256(size_t(BH * p.nseg * p.rec) * sizeof(float));
 }
 
+// Whether each lane moves at most one piece of a chunk's shared Q or K rows
+// (CoopRows NPW = 1): the segment's M / 16 wavefronts cover the 2 D
+// sixteen-byte pieces once, 64 (M / 16) >= 2 D.
+template <int DT> static bool gen_one_piece(int64_t M) { return CoopRows<16 * DT>::NP == 1 || 64 * (M / 16) >= 32 * DT; }
+
 // Per-segment sums of phi(K) [V, 1]^T (bf16: the shared-staging kernel).
 template <typename T, int DT>
 static void launch_gen_segstate(bool phi, dim3 grid, dim3 block, const void *k, const void *v, float *ws, int64_t N,
                                 int64_t M, const SegPlan &p, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
-        if (phi)
-            hipLaunchKernelGGL((k_gen_segstate_bf16<DT, true>), grid, block, 0, s, (const bf16 *)k, (const bf16 *)v,
-                               ws, N, M, p.nseg, p.seg_tokens);
-        else
-            hipLaunchKernelGGL((k_gen_segstate_bf16<DT, false>), grid, block, 0, s, (const bf16 *)k,
-                               (const bf16 *)v, ws, N, M, p.nseg, p.seg_tokens);
+        constexpr int NP = CoopRows<16 * DT>::NP;
+#define LA_GEN_SEG(P, W)                                                                                          \
+    hipLaunchKernelGGL((k_gen_segstate_bf16<DT, P, W>), grid, block, 0, s, (const bf16 *)k, (const bf16 *)v, ws, N, \
+                       M, p.nseg, p.seg_tokens)
+        if (gen_one_piece<DT>(M)) {
+            if (phi)
+                LA_GEN_SEG(true, 1);
+            else
+                LA_GEN_SEG(false, 1);
+        } else if constexpr (NP > 1) {
+            if (phi)
+                LA_GEN_SEG(true, NP);
+            else
+                LA_GEN_SEG(false, NP);
+        }
+#undef LA_GEN_SEG
     } else {
         if (phi)
             hipLaunchKernelGGL((k_gen_segstate<T, DT, true>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N,
@@ -973,11 +988,19 @@ static hipError_t run_generic(bool causal, bool phi, const void *q, const void *
     io.z1 = sio.z1;
     io.srec = int64_t(D) * M;
     if ((e = launch_scan(ws, BH, p.nseg, p.rec, causal ? 0 : 1, s, io)) != hipSuccess) return e;
+    constexpr int NP = CoopRows<D>::NP;
+    const bool one = gen_one_piece<DT>(M);
 #define LA_GEN_OUT(C, P)                                                                                          \
-    if constexpr (sizeof(T) == 2)                                                                                 \
-        hipLaunchKernelGGL((k_gen_output_bf16<DT, C, P>), grid, block, 0, s, (const bf16 *)q, (const bf16 *)k,    \
-                           (const bf16 *)v, (bf16 *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens);          \
-    else                                                                                                          \
+    if constexpr (sizeof(T) == 2) {                                                                               \
+        if (one)                                                                                                  \
+            hipLaunchKernelGGL((k_gen_output_bf16<DT, C, P, 1>), grid, block, 0, s, (const bf16 *)q,              \
+                               (const bf16 *)k, (const bf16 *)v, (bf16 *)out, (const float *)ws, N, M, p.nseg,    \
+                               p.seg_tokens);                                                                     \
+        else if constexpr (NP > 1)                                                                                \
+            hipLaunchKernelGGL((k_gen_output_bf16<DT, C, P, NP>), grid, block, 0, s, (const bf16 *)q,             \
+                               (const bf16 *)k, (const bf16 *)v, (bf16 *)out, (const float *)ws, N, M, p.nseg,    \
+                               p.seg_tokens);                                                                     \
+    } else                                                                                                        \
         hipLaunchKernelGGL((k_gen_output<T, DT, C, P>), grid, block, 0, s, (const T *)q, (const T *)k,            \
                            (const T *)v, (T *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens)
     if (!causal) {
@@ -1063,10 +1086,8 @@ static hipError_t run_generic_backward(bool causal, const void *q, const void *k
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, causal ? 0 : 1, s)) != hipSuccess) return e;
-    // one piece per lane when the M / 16 wavefronts cover a chunk's 2 D
-    // sixteen-byte pieces of Q (or K) once: 64 (M / 16) >= 2 D
     constexpr int NP = CoopRows<D>::NP;
-    if (sizeof(T) == 4 || NP == 1 || 64 * (M / 16) >= 2 * D)
+    if (sizeof(T) == 4 || gen_one_piece<DT>(M))
         return run_gbwd_passes<T, DT, 1>(causal, grid, block, q, k, v, dout, dq, dk, dv, BH, N, M, p, wsS, wsR, ibuf,
                                          hbuf, s);
     if constexpr (sizeof(T) == 2 && NP > 1)
