@@ -331,27 +331,35 @@ __global__ __launch_bounds__(512) void k_gen_segstate_bf16(const bf16 *__restric
     f32x4 St[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) St[dt][0] = St[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    CoopRows<D, NPW> rk;
-    bf16x4 rv;
-    coop_load<D>(rk, K, t_begin, t_end, cg, ng);
-    rv = load_col_tile<bf16>(V, M, 16 * cg, t_begin, t_end);
-    int buf = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
-        lds_bf16 *sk = (lds_bf16 *)shk[buf];
-        coop_stage<D, PHI, true>(sk, rk, t0, t_end, cg, ng);   // rows past t_end are zero
-        Fr Vn[1][1];
-        {
-            const bf16x4 one[1][1] = {{rv}};
-            raw_frags<bf16, 16, 1>(Vn, one, t0, t_end);
+    // chunks loaded two ahead of the one being summed; chunk parity b picks
+    // the register set and the LDS buffer
+    CoopRows<D, NPW> rk[2];
+    bf16x4 rv[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        coop_load<D>(rk[b], K, t_begin + b * GCH, t_end, cg, ng);
+        rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t_begin + b * GCH, t_end);
+    }
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * GCH) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int64_t t0 = t00 + b * GCH;
+            if (t0 >= t_end) break;   // uniform over the workgroup
+            lds_bf16 *sk = (lds_bf16 *)shk[b];
+            coop_stage<D, PHI, true>(sk, rk[b], t0, t_end, cg, ng);   // rows past t_end are zero
+            Fr Vn[1][1];
+            {
+                const bf16x4 one[1][1] = {{rv[b]}};
+                raw_frags<bf16, 16, 1>(Vn, one, t0, t_end);
+            }
+            coop_load<D>(rk[b], K, t0 + 2 * GCH, t_end, cg, ng);
+            rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t0 + 2 * GCH, t_end);
+            lds_barrier();
+            Fr KT[1][DT], VT[1][1];
+            transposed_frags_lds<D, 1>(KT, sk);
+            transpose_frags<1, 1>(VT, Vn, sv);
+            state_accumulate<Fr, D, 16, 1, false>(St, KT, VT);
         }
-        coop_load<D>(rk, K, t0 + GCH, t_end, cg, ng);
-        rv = load_col_tile<bf16>(V, M, 16 * cg, t0 + GCH, t_end);
-        lds_barrier();
-        Fr KT[1][DT], VT[1][1];
-        transposed_frags_lds<D, 1>(KT, sk);
-        transpose_frags<1, 1>(VT, Vn, sv);
-        state_accumulate<Fr, D, 16, 1, false>(St, KT, VT);
-        buf ^= 1;
     }
     float *rec = ws + (bh * nseg + seg) * (int64_t(D) * M + D);
 #pragma unroll
@@ -403,27 +411,35 @@ __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict_
     }
     const Fr ones = frag_ones<Fr>();
 
-    CoopRows<D, NPW> rq, rk;
-    bf16x4 rv;
-    coop_load<D>(rq, Q, t_begin, t_end, cg, ng);
-    if (CAUSAL) {
-        coop_load<D>(rk, K, t_begin, t_end, cg, ng);
-        rv = load_col_tile<bf16>(V, M, 16 * cg, t_begin, t_end);
+    // chunks loaded two ahead of the one being computed; chunk parity b
+    // picks the register set and the LDS buffer
+    CoopRows<D, NPW> rq[2], rk[2];
+    bf16x4 rv[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        coop_load<D>(rq[b], Q, t_begin + b * GCH, t_end, cg, ng);
+        if (CAUSAL) {
+            coop_load<D>(rk[b], K, t_begin + b * GCH, t_end, cg, ng);
+            rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t_begin + b * GCH, t_end);
+        }
     }
-    int buf = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
-        lds_bf16 *sq = (lds_bf16 *)shq[buf];
-        lds_bf16 *sk = (lds_bf16 *)shk[CAUSAL ? buf : 0];
-        coop_stage<D, PHI, false>(sq, rq, t0, t_end, cg, ng);
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * GCH) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t t0 = t00 + b * GCH;
+        if (t0 >= t_end) break;   // uniform over the workgroup
+        lds_bf16 *sq = (lds_bf16 *)shq[b];
+        lds_bf16 *sk = (lds_bf16 *)shk[CAUSAL ? b : 0];
+        coop_stage<D, PHI, false>(sq, rq[b], t0, t_end, cg, ng);
         Fr Vn[1][1];
         if (CAUSAL) {
-            coop_stage<D, PHI, false>(sk, rk, t0, t_end, cg, ng);
-            value_frags_unmasked(Vn[0][0], rv);
+            coop_stage<D, PHI, false>(sk, rk[b], t0, t_end, cg, ng);
+            value_frags_unmasked(Vn[0][0], rv[b]);
         }
-        coop_load<D>(rq, Q, t0 + GCH, t_end, cg, ng);
+        coop_load<D>(rq[b], Q, t0 + 2 * GCH, t_end, cg, ng);
         if (CAUSAL) {
-            coop_load<D>(rk, K, t0 + GCH, t_end, cg, ng);
-            rv = load_col_tile<bf16>(V, M, 16 * cg, t0 + GCH, t_end);
+            coop_load<D>(rk[b], K, t0 + 2 * GCH, t_end, cg, ng);
+            rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t0 + 2 * GCH, t_end);
         }
         lds_barrier();
         Fr Qn[1][DT];
@@ -454,7 +470,7 @@ __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict_
         const float inv = __builtin_amdgcn_rcpf(Ot[1][0]);
         const int64_t t = t0 + c;
         if (t < t_end) store4<bf16>(O + t * M + 16 * cg + 4 * g, IO<bf16>::from_f32(Ot[0] * inv));
-        buf ^= 1;
+    }
     }
 }
 
