@@ -553,44 +553,54 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     const Fr ones = frag_ones<Fr>();
     const Fr k0ones = frag_k0_ones<Fr>();
 
-    V4 rq[1][SHARED ? 1 : DT], rk[1][SHARED ? 1 : DT], rv, rg;
-    CoopRows<D, SHARED ? NPW : 1> cq, ck;
-    auto load_all = [&](int64_t t0) {
+    // a chunk's inputs in registers; bf16 loads them two chunks ahead (chunk
+    // parity b picks the set and the LDS buffer)
+    constexpr int PF = SHARED ? 2 : 1;
+    struct In {
+        V4 rq[1][SHARED ? 1 : DT], rk[1][SHARED ? 1 : DT], rv, rg;
+        CoopRows<D, SHARED ? NPW : 1> cq, ck;
+    } in[PF];
+    auto load_all = [&](In &x, int64_t t0) {
         if constexpr (SHARED) {
-            coop_load<D>(cq, (const bf16 *)Q, t0, t_end, cg, ng);
-            if (CAUSAL) coop_load<D>(ck, (const bf16 *)K, t0, t_end, cg, ng);
+            coop_load<D>(x.cq, (const bf16 *)Q, t0, t_end, cg, ng);
+            if (CAUSAL) coop_load<D>(x.ck, (const bf16 *)K, t0, t_end, cg, ng);
         } else {
-            load_chunk<T, D, 1>(rq, Q, t0, t_end);
-            if (CAUSAL) load_chunk<T, D, 1>(rk, K, t0, t_end);
+            load_chunk<T, D, 1>(x.rq, Q, t0, t_end);
+            if (CAUSAL) load_chunk<T, D, 1>(x.rk, K, t0, t_end);
         }
-        if (CAUSAL) rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
-        rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
+        if (CAUSAL) x.rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
+        x.rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
     };
-    load_all(t_begin);
-    int buf = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += GCH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) load_all(in[b], t_begin + b * GCH);   // rows past t_end read row t_end - 1
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += PF * GCH) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t t0 = t00 + b * GCH;
+        if (t0 >= t_end) break;   // uniform over the workgroup
+        In &cur = in[b];
         Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
         f32x4 dphq[SHARED ? 1 : DT];   // fp32: phi'(Q) of this lane's (token, 4 features) per tile
-        lds_bf16 *sq = (lds_bf16 *)shq[SHARED ? buf : 0];
-        lds_bf16 *sk = (lds_bf16 *)shk[SHARED && CAUSAL ? buf : 0];
+        lds_bf16 *sq = (lds_bf16 *)shq[SHARED ? b : 0];
+        lds_bf16 *sk = (lds_bf16 *)shk[SHARED && CAUSAL ? b : 0];
         if (CAUSAL) {
-            const V4 one[1][1] = {{rv}};
+            const V4 one[1][1] = {{cur.rv}};
             raw_frags<T, 16, 1>(Vn, one, t0, t_end);
         }
-        const f32x4 graw = IO<T>::to_f32(rg);
+        const f32x4 graw = IO<T>::to_f32(cur.rg);
         if constexpr (SHARED) {
-            coop_stage<D, true, true>(sq, cq, t0, t_end, cg, ng);   // rows past t_end are zero
-            if (CAUSAL) coop_stage<D, true, true>(sk, ck, t0, t_end, cg, ng);
-            load_all(t0 + GCH);   // rows past t_end read row t_end - 1
+            coop_stage<D, true, true>(sq, cur.cq, t0, t_end, cg, ng);   // rows past t_end are zero
+            if (CAUSAL) coop_stage<D, true, true>(sk, cur.ck, t0, t_end, cg, ng);
+            load_all(cur, t0 + PF * GCH);   // rows past t_end read row t_end - 1
             lds_barrier();
             natural_frags_lds<D, 1>(Qn, sq);
             if (CAUSAL) natural_frags_lds<D, 1>(Kn, sk);
         } else {
-            phi_frags<T, D, 1>(Qn, rq, t0, t_end);
-            if (CAUSAL) phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+            phi_frags<T, D, 1>(Qn, cur.rq, t0, t_end);
+            if (CAUSAL) phi_frags<T, D, 1>(Kn, cur.rk, t0, t_end);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) dphq[dt] = dphi4(IO<T>::to_f32(rq[0][dt]));
-            load_all(t0 + GCH);   // rows past t_end read row t_end - 1
+            for (int dt = 0; dt < DT; ++dt) dphq[dt] = dphi4(IO<T>::to_f32(cur.rq[0][dt]));
+            load_all(cur, t0 + PF * GCH);   // rows past t_end read row t_end - 1
         }
         const int64_t t = t0 + c;   // this lane's query token
         const bool valid = t < t_end;
@@ -724,7 +734,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
                 state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
             }
         }
-        buf ^= 1;
+    }
     }
     float *r1 = wsR + (bh * nseg + seg) * rec;
 #pragma unroll
@@ -786,51 +796,61 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
     const Fr k0ones = frag_k0_ones<Fr>();
 
     const int64_t nch = (t_end - t_begin + GCH - 1) / GCH;
-    V4 rq[1][SHARED ? 1 : DT], rk[1][SHARED ? 1 : DT], rv, rg;
-    CoopRows<D, SHARED ? NPW : 1> cq, ck;
-    float rh = 0.f, ri = 0.f;
-    auto load_all = [&](int64_t t0) {
+    // a chunk's inputs in registers; bf16 loads them two chunks ahead (step s
+    // visits chunk nch - 1 - s from set and LDS buffer s % 2)
+    constexpr int PF = SHARED ? 2 : 1;
+    struct In {
+        V4 rq[1][SHARED ? 1 : DT], rk[1][SHARED ? 1 : DT], rv, rg;
+        CoopRows<D, SHARED ? NPW : 1> cq, ck;
+        float rh, ri;
+    } in[PF];
+    auto load_all = [&](In &x, int64_t t0) {
         if constexpr (SHARED) {
-            if (CAUSAL) coop_load<D>(cq, (const bf16 *)Q, t0, t_end, cg, ng);
-            coop_load<D>(ck, (const bf16 *)K, t0, t_end, cg, ng);
+            if (CAUSAL) coop_load<D>(x.cq, (const bf16 *)Q, t0, t_end, cg, ng);
+            coop_load<D>(x.ck, (const bf16 *)K, t0, t_end, cg, ng);
         } else {
-            if (CAUSAL) load_chunk<T, D, 1>(rq, Q, t0, t_end);
-            load_chunk<T, D, 1>(rk, K, t0, t_end);
+            if (CAUSAL) load_chunk<T, D, 1>(x.rq, Q, t0, t_end);
+            load_chunk<T, D, 1>(x.rk, K, t0, t_end);
         }
-        rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
+        x.rv = load_col_tile<T>(V, M, 16 * cg, t0, t_end);
         if (CAUSAL) {
-            rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
-            rh = (t0 + c < t_end) ? hbuf[bh * N + t0 + c] : 0.f;
-            ri = (t0 + c < t_end) ? ibuf[bh * N + t0 + c] : 0.f;
+            x.rg = load_col_tile<T>(G, M, 16 * cg, t0, t_end);
+            x.rh = (t0 + c < t_end) ? hbuf[bh * N + t0 + c] : 0.f;
+            x.ri = (t0 + c < t_end) ? ibuf[bh * N + t0 + c] : 0.f;
         }
     };
-    load_all(t_begin + (nch - 1) * GCH);
-    int buf = 0;
-    for (int64_t ci = nch - 1; ci >= 0; --ci) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) load_all(in[b], t_begin + imax64(nch - 1 - b, 0) * GCH);
+    for (int64_t s0 = 0; s0 < nch; s0 += PF) {
+#pragma unroll
+    for (int b = 0; b < PF; ++b) {
+        const int64_t ci = nch - 1 - (s0 + b);
+        if (ci < 0) break;   // uniform over the workgroup
         const int64_t t0 = t_begin + ci * GCH;
+        In &cur = in[b];
         Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
         Fr Gn = frag_zero<Fr>(), Gh = frag_zero<Fr>();
         f32x4 dphk[SHARED ? 1 : DT];   // fp32: phi'(K) of this lane's (token, 4 features) per tile
-        lds_bf16 *sq = (lds_bf16 *)shq[SHARED && CAUSAL ? buf : 0];
-        lds_bf16 *sk = (lds_bf16 *)shk[SHARED ? buf : 0];
+        lds_bf16 *sq = (lds_bf16 *)shq[SHARED && CAUSAL ? b : 0];
+        lds_bf16 *sk = (lds_bf16 *)shk[SHARED ? b : 0];
         if constexpr (SHARED) {
-            if (CAUSAL) coop_stage<D, true, true>(sq, cq, t0, t_end, cg, ng);   // rows past t_end are zero
-            coop_stage<D, true, true>(sk, ck, t0, t_end, cg, ng);
+            if (CAUSAL) coop_stage<D, true, true>(sq, cur.cq, t0, t_end, cg, ng);   // rows past t_end are zero
+            coop_stage<D, true, true>(sk, cur.ck, t0, t_end, cg, ng);
         } else {
-            if (CAUSAL) phi_frags<T, D, 1>(Qn, rq, t0, t_end);
-            phi_frags<T, D, 1>(Kn, rk, t0, t_end);
+            if (CAUSAL) phi_frags<T, D, 1>(Qn, cur.rq, t0, t_end);
+            phi_frags<T, D, 1>(Kn, cur.rk, t0, t_end);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) dphk[dt] = dphi4(IO<T>::to_f32(rk[0][dt]));
+            for (int dt = 0; dt < DT; ++dt) dphk[dt] = dphi4(IO<T>::to_f32(cur.rk[0][dt]));
         }
         {
-            const V4 one[1][1] = {{rv}};
+            const V4 one[1][1] = {{cur.rv}};
             raw_frags<T, 16, 1>(Vn, one, t0, t_end);
         }
         if (CAUSAL) {   // g = dout / d as in the forward-direction pass; rows past t_end are 0 (ri = 0)
-            Gn = IO<T>::to_frag(IO<T>::to_f32(rg) * ri);
-            Gh = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
+            Gn = IO<T>::to_frag(IO<T>::to_f32(cur.rg) * cur.ri);
+            Gh = IO<T>::to_frag(f32x4{g == 0 ? cur.rh : 0.f, 0.f, 0.f, 0.f});
         }
-        if (ci > 0) load_all(t0 - GCH);
+        if (ci >= PF) load_all(cur, t0 - PF * GCH);
         if constexpr (SHARED) {
             lds_barrier();
             if (CAUSAL) natural_frags_lds<D, 1>(Qn, sq);
@@ -937,7 +957,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             }
         }
         lds_barrier();   // every group has read `part` before the next chunk writes it
-        buf ^= 1;
+    }
     }
 }
 
