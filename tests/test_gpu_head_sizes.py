@@ -41,6 +41,10 @@ CASES = [
     ("d80m112_f32_one_token", _w(508, 1, 2, 1, 80, 112, "f32")),
     ("d64m96_bf16", _w(509, 1, 8, 4096, 64, 96, "bf16")),
     ("d128m128_f32", _w(510, 1, 2, 2000, 128, 128, "f32")),
+    # fewer column groups than wavefront loads of the shared Q, K rows: each
+    # lane moves several pieces (D=128, M=16: four; D=96, M=32: three)
+    ("d128m16_bf16", _w(511, 1, 2, 1500, 128, 16, "bf16")),
+    ("d96m32_bf16_ragged", _w(512, 2, 2, 1777, 96, 32, "bf16")),
 ]
 
 
@@ -137,6 +141,8 @@ BWD_CASES = [
     ("d80m112_f32_one_token", _w(528, 1, 2, 1, 80, 112, "f32")),
     ("d64m48_bf16", _w(529, 1, 4, 2048, 64, 48, "bf16")),
     ("d128m128_f32", _w(530, 1, 2, 1200, 128, 128, "f32")),
+    ("d128m16_bf16", _w(532, 1, 2, 1200, 128, 16, "bf16")),   # several pieces per lane, as above
+    ("d96m32_bf16_ragged", _w(533, 2, 2, 1333, 96, 32, "bf16")),
 ]
 
 
