@@ -154,13 +154,13 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         f32x4 gv[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 o = Ot[mt] * inv;
+            const f32x4 o = Ot[mt];   // out times d: the 1/d factors are applied to the sum
             go += graw[mt][0] * o[0] + graw[mt][1] * o[1] + graw[mt][2] * o[2] + graw[mt][3] * o[3];
             gv[mt] = graw[mt] * inv;
         }
         go += __shfl_xor(go, 16);
         go += __shfl_xor(go, 32);
-        const float h = -go * inv;
+        const float h = -(go * inv) * inv;   // -(dout . out) / d with out = Ot / d
         Fr Gn[BTT][MT + 1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<T>::to_frag(gv[mt]);
@@ -518,13 +518,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const f32x4 graw = IO<bf16>::to_f32(Gr[0][mt]);
-            const f32x4 o = Ot[mt] * inv;
+            const f32x4 o = Ot[mt];   // out times d: the 1/d factors are applied to the sum
             go += graw[0] * o[0] + graw[1] * o[1] + graw[2] * o[2] + graw[3] * o[3];
             gv[mt] = graw * inv;
         }
         go += __shfl_xor(go, 16);
         go += __shfl_xor(go, 32);
-        const float h = -go * inv;
+        const float h = -(go * inv) * inv;   // -(dout . out) / d with out = Ot / d
         Fr Gn[1][MT + 1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<bf16>::to_frag(gv[mt]);
@@ -835,13 +835,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const f32x4 graw = IO<bf16>::to_f32(Gr[0][mt]);
-            const f32x4 o = Ot[mt] * inv;
+            const f32x4 o = Ot[mt];   // out times d: the 1/d factors are applied to the sum
             go += graw[0] * o[0] + graw[1] * o[1] + graw[2] * o[2] + graw[3] * o[3];
             gv[mt] = graw * inv;
         }
         go += __shfl_xor(go, 16);
         go += __shfl_xor(go, 32);
-        const float h = -go * inv;
+        const float h = -(go * inv) * inv;   // -(dout . out) / d with out = Ot / d
         Fr Gn[1][MT + 1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<bf16>::to_frag(gv[mt]);
