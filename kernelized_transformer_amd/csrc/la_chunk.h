@@ -187,6 +187,16 @@ __device__ __forceinline__ void natural_frags_lds(bf16x4 (&y)[TT][F / 16], const
             y[tt][ft] = *reinterpret_cast<const lds_bf16x4 *>(stage + (16 * tt + c) * (F + kStagePad) + 16 * ft + 4 * g);
 }
 
+// One token-contiguous tile of rows staged with a row stride of S elements:
+// rows 16 tt .. 16 tt + 15, feature tile ft (the tile yt[tt][ft] of
+// transposed_frags_lds), for reading operand tiles where they are used.
+__device__ __forceinline__ bf16x4 transposed_tile_lds(const lds_bf16 *stage, int S, int tt, int ft) {
+    const int c = lane_id() & 15, g = lane_id() >> 4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4 *>(
+        const_cast<lds_bf16 *>(stage) + (16 * tt + 4 * g + (c >> 2)) * S + 16 * ft + 4 * (c & 3)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // Token-contiguous fragments from staging (see transpose_frags_lds).
 template <int F, int TT>
 __device__ __forceinline__ void transposed_frags_lds(bf16x4 (&yt)[TT][F / 16], const lds_bf16 *stage) {

@@ -122,16 +122,6 @@ __device__ __forceinline__ void coop_stage(lds_bf16 *stage, const CoopRows<F, NP
 }
 template <int F> constexpr int coop_rows_elems() { return 16 * (F + kStagePad); }
 
-// One token-contiguous tile (the layout of transposed_frags_lds) of bf16 rows
-// staged in LDS with a row stride of S elements: rows 16 tt .. 16 tt + 15,
-// feature tile ft.
-__device__ __forceinline__ bf16x4 transposed_tile_lds(const lds_bf16 *stage, int S, int tt, int ft) {
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4 *>(
-        const_cast<lds_bf16 *>(stage) + (16 * tt + 4 * g + (c >> 2)) * S + 16 * ft + 4 * (c & 3)));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
 // phi'(x) = min(phi(x), 1) of tile ft of rows staged by coop_stage<F, true, .>
 // (phi(x) <= 1 exactly where x <= 0, where phi' = phi = exp(x)), in the
 // natural layout: lane (c, g) gets row c, features 16 ft + 4g .. + 3.  Read at
