@@ -815,6 +815,71 @@ def test_forward_graph_replays(causal):
     del g
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("D", [64, 128], ids=["d64", "d128"])
+def test_backward_graph_replays(causal, D):
+    """A backward captured into a HIP graph and replayed with new inputs
+    copied into the captured tensors gives, on every replay, exactly the
+    gradients of an eager call on the same inputs and workspace (eager calls
+    in between), for the two-wavefront kernels (D = 64) and the column-group
+    kernels (D = 128).  The backward keeps no state between calls: every
+    workspace word it reads it wrote earlier in the same call."""
+    w = _wl(178, 1, 4, 6000, D, D, "bf16")
+    _say(f"backward graph replays ({'causal' if causal else 'non-causal'}): B{w.B} H{w.H} N{w.N} D{w.D} M{w.M}")
+    sets = [tuple(dev(x, w.dtype) for x in wl.forward_inputs(w, with_dout=True, seed=s)) for s in (178, 179, 180)]
+    q, k, v, g = (torch.empty_like(t) for t in sets[0])
+    grads = tuple(torch.empty_like(t) for t in (q, k, v))
+    op = la.LA_OP_BWD_CAUSAL if causal else la.LA_OP_BWD_NONCAUSAL
+    ws = torch.empty((la.la_workspace_size(op, w.B, w.H, w.N, w.D, w.M, q.dtype),), dtype=torch.uint8, device="cuda")
+    f = la.la_backward_causal if causal else la.la_backward_noncausal
+    for dst, src in zip((q, k, v, g), sets[0]):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        f(q, k, v, g, *grads, workspace=ws)
+    for rep in (0, 1, 2, 1):
+        for dst, src in zip((q, k, v, g), sets[rep]):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = tuple(x.clone() for x in grads)
+        ref = f(*sets[rep], workspace=ws)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(a, b), f"{name}: replay with input set {rep} differs from the eager call"
+    del graph
+
+
+def test_forward_graph_replays_head_size_128():
+    """The column-group forward (head size 128) captured into a graph: every
+    replay equals an eager call on the same inputs (its records are written
+    before they are read in each call)."""
+    w = _wl(181, 1, 4, 6000, 128, 128, "bf16")
+    _say(f"graph replays (head size 128): B{w.B} H{w.H} N{w.N} D{w.D} M{w.M} {w.dtype}")
+    sets = [tuple(dev(x, w.dtype) for x in wl.forward_inputs(w, seed=s)) for s in (181, 182, 183)]
+    q, k, v = (torch.empty_like(t) for t in sets[0])
+    out = torch.empty((w.B, w.H, w.N, w.M), dtype=q.dtype, device="cuda")
+    ws = torch.empty((la.la_workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.D, w.M, q.dtype),),
+                     dtype=torch.uint8, device="cuda")
+    for dst, src in zip((q, k, v), sets[0]):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        la.la_forward_causal(q, k, v, out=out, workspace=ws)
+    for rep in (0, 1, 2, 1):
+        for dst, src in zip((q, k, v), sets[rep]):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = la.la_forward_causal(*sets[rep], workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay with input set {rep} differs from the eager call"
+    del graph
+
+
 def test_forward_wait_give_up_is_reported():
     """With the wait limit at 0 every hand-off wait gives up at once: the
     kernels still exit, the call returns LA_OK, and la_workspace_check reports
