@@ -38,11 +38,18 @@ namespace la {
 
 constexpr int BTT = 1;  // token tiles per chunk in the backward kernels
 constexpr int BCH = 16 * BTT;
-// LDS per wavefront: the chunk transposes, or the state's (M + 16) x D transpose
-template <int D, int M>
-constexpr int kBwdStage = (stage_elems<D / 16, BTT>() + stage_elems<M / 16 + 1, BTT>() > stage_elems<D / 16, M / 16 + 1>())
-                              ? stage_elems<D / 16, BTT>() + stage_elems<M / 16 + 1, BTT>()
-                              : stage_elems<D / 16, M / 16 + 1>();
+// Operand fragments of the one-wavefront kernels: fp32 data runs on the bf16
+// matrix instruction split into hi + lo parts (split4, as in the fp32
+// forward), bf16 as is.
+template <typename T> using BwdFrag = typename std::conditional<sizeof(T) == 4, split4, typename IO<T>::frag>::type;
+// LDS per wavefront: the chunk transposes, or the state's (M + 16) x D
+// transpose (split operands: two areas each)
+template <typename T, int D, int M>
+constexpr int kBwdStage =
+    (transpose_stage_elems<BwdFrag<T>, D / 16, BTT>() + transpose_stage_elems<BwdFrag<T>, M / 16 + 1, BTT>() >
+     transpose_stage_elems<BwdFrag<T>, D / 16, M / 16 + 1>())
+        ? transpose_stage_elems<BwdFrag<T>, D / 16, BTT>() + transpose_stage_elems<BwdFrag<T>, M / 16 + 1, BTT>()
+        : transpose_stage_elems<BwdFrag<T>, D / 16, M / 16 + 1>();
 template <int D, int M>
 constexpr int kBwdTile = 16 * ((D > M ? D : M) + kStagePad);
 
@@ -57,7 +64,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
                                                float *__restrict__ wsR, float *__restrict__ ibuf,
                                                float *__restrict__ hbuf, int64_t N, int64_t nseg,
                                                int64_t seg_tokens, int64_t rec) {
-    typedef typename IO<T>::frag Fr;
+    typedef BwdFrag<T> Fr;
     typedef typename IO<T>::vec4 V4;
     constexpr int DT = D / 16, MT = M / 16;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
@@ -80,9 +87,9 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 
     const Fr ones = frag_row0_ones<Fr>();
     const Fr k0ones = frag_k0_ones<Fr>();
-    __shared__ bf16 stage_mem[kBwdStage<D, M> + kBwdTile<D, M>];
+    __shared__ bf16 stage_mem[kBwdStage<T, D, M> + kBwdTile<D, M>];
     lds_bf16 *stage = (lds_bf16 *)(stage_mem);
-    lds_bf16 *otile = stage + kBwdStage<D, M>;   // one 16-token output tile (bf16)
+    lds_bf16 *otile = stage + kBwdStage<T, D, M>;   // one 16-token output tile (bf16)
 
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
     load_chunk<T, D, BTT>(rq, Q, t_begin, t_end);
@@ -119,13 +126,13 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
 #pragma unroll
         for (int mt = 0; mt <= MT; ++mt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = IO<T>::to_frag(St[dt][mt]);
+            for (int dt = 0; dt < DT; ++dt) SF[mt][dt] = frag_from<Fr>(St[dt][mt]);
         transpose_frags<DT, MT + 1>(SFT, SF, stage);
 
         Fr KT[BTT][DT], VT[BTT][MT];
         if (CAUSAL) {
             transpose_frags<DT, BTT>(KT, Kn, stage);
-            transpose_frags<MT, BTT>(VT, Vn, stage + stage_elems<DT, BTT>());
+            transpose_frags<MT, BTT>(VT, Vn, stage + transpose_stage_elems<Fr, DT, BTT>());
         }
 
         // recompute out^T (and den in the normalizer block) as the forward does
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
             for (int dt = 0; dt < DT; dt += 2) mma2(p, Kn[0][dt], Kn[0][dt + 1], Qn[0][dt], Qn[0][dt + 1]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-            PT = IO<T>::to_frag(p);
+            PT = frag_from<Fr>(p);
         }
 #pragma unroll
         for (int mt = 0; mt <= MT; ++mt) {
@@ -163,8 +170,8 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         const float h = -(go * inv) * inv;   // -(dout . out) / d with out = Ot / d
         Fr Gn[BTT][MT + 1];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = IO<T>::to_frag(gv[mt]);
-        Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
+        for (int mt = 0; mt < MT; ++mt) Gn[0][mt] = frag_from<Fr>(gv[mt]);
+        Gn[0][MT] = frag_from<Fr>(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});
         if (CAUSAL && valid && g == 0) {
             IB[t] = inv;
             HB[t] = h;
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
             if ((MT & 1) == 0) mma1(da, k0ones, Gn[0][MT]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
-            dAT = IO<T>::to_frag(da);
+            dAT = frag_from<Fr>(da);
         }
 
         // dL/dqh^T[d][i] = sum_j kh[j][d] dA^T[j][i] + sum_m' S_aug[d][m'] gh[i][m']
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(64) void k_bwd_dq(const T *__restrict__ q, const T 
         // this segment's reverse-sum contribution: Ra += sum_i qh_i gh_i^T
         Fr QT[BTT][DT], GT[BTT][MT + 1];
         transpose_frags<DT, BTT>(QT, Qn, stage);
-        transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
+        transpose_frags<MT + 1, BTT>(GT, Gn, stage + transpose_stage_elems<Fr, DT, BTT>());
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
                                                  T *__restrict__ dk,
                                                  T *__restrict__ dv, const float *__restrict__ wsR, int64_t N,
                                                  int64_t nseg, int64_t seg_tokens, int64_t rec) {
-    typedef typename IO<T>::frag Fr;
+    typedef BwdFrag<T> Fr;
     typedef typename IO<T>::vec4 V4;
     constexpr int DT = D / 16, MT = M / 16;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
@@ -248,9 +255,9 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
     state_load<D, M>(Rr, rrec);
 
     const Fr k0ones = frag_k0_ones<Fr>();
-    __shared__ bf16 stage_mem[kBwdStage<D, M> + kBwdTile<D, M>];
+    __shared__ bf16 stage_mem[kBwdStage<T, D, M> + kBwdTile<D, M>];
     lds_bf16 *stage = (lds_bf16 *)(stage_mem);
-    lds_bf16 *otile = stage + kBwdStage<D, M>;   // one 16-token output tile (bf16)
+    lds_bf16 *otile = stage + kBwdStage<T, D, M>;   // one 16-token output tile (bf16)
 
     const int64_t nch = (t_end - t_begin + BCH - 1) / BCH;
     V4 rq[BTT][DT], rk[BTT][DT], rv[BTT][MT], rg[BTT][MT];
@@ -282,9 +289,9 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const f32x4 gv = IO<T>::to_f32(rg[0][mt]) * ri;
-                    Gn[0][mt] = IO<T>::to_frag(ok ? gv : f32x4{0.f, 0.f, 0.f, 0.f});
+                    Gn[0][mt] = frag_from<Fr>(ok ? gv : f32x4{0.f, 0.f, 0.f, 0.f});
                 }
-                Gn[0][MT] = IO<T>::to_frag(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
+                Gn[0][MT] = frag_from<Fr>(f32x4{g == 0 ? rh : 0.f, 0.f, 0.f, 0.f});
             }
         }
         f32x4 kraw[DT];
@@ -300,14 +307,14 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
 #pragma unroll
         for (int mt = 0; mt <= MT; ++mt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) RF[mt][dt] = IO<T>::to_frag(Rr[dt][mt]);
+            for (int dt = 0; dt < DT; ++dt) RF[mt][dt] = frag_from<Fr>(Rr[dt][mt]);
         transpose_frags<DT, MT + 1>(RFT, RF, stage);
 
         Fr QT[BTT][DT], GT[BTT][MT + 1];
         Fr Pf = frag_zero<Fr>(), dAf = frag_zero<Fr>();
         if (CAUSAL) {
             transpose_frags<DT, BTT>(QT, Qn, stage);
-            transpose_frags<MT + 1, BTT>(GT, Gn, stage + stage_elems<DT, BTT>());
+            transpose_frags<MT + 1, BTT>(GT, Gn, stage + transpose_stage_elems<Fr, DT, BTT>());
 
             // P[i][j] = qh_i . kh_j and dA[i][j] = gh_i . vh_j, masked to i >= j
             f32x4 p = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
@@ -322,8 +329,8 @@ __global__ __launch_bounds__(64) void k_bwd_dkdv(const T *__restrict__ q, const 
                 p[r] = keep ? p[r] : 0.f;
                 da[r] = keep ? da[r] : 0.f;
             }
-            Pf = IO<T>::to_frag(p);
-            dAf = IO<T>::to_frag(da);
+            Pf = frag_from<Fr>(p);
+            dAf = frag_from<Fr>(da);
         }
 
         // dL/dkh^T[d][j] = sum_i qh[i][d] dA[i][j] + sum_m' R_aug[d][m'] vh[j][m']

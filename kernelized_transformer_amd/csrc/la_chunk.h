@@ -7,6 +7,7 @@
 // (c, g), the 4 features 16*ft + 4g .. 16*ft + 4g + 3 of token 16*tt + c:
 // one 8-byte (bf16) or 16-byte (fp32) load per lane.
 #pragma once
+#include <type_traits>
 
 #include "la_device.h"
 
@@ -250,6 +251,30 @@ __device__ __forceinline__ void transpose_frags(f32x4 (&yt)[TT][NF], const f32x4
 template <int NF, int TT>
 __device__ __forceinline__ void transpose_frags(bf16x4 (&yt)[TT][NF], const bf16x4 (&y)[TT][NF], lds_bf16 *stage) {
     transpose_frags_lds<NF, TT>(yt, y, stage);
+}
+// Split fp32 operands (split4): the hi parts through the LDS area at `stage`,
+// the lo parts through the one after it, so the area is twice
+// stage_elems<NF, TT>() elements.  Exact (copies).
+template <int NF, int TT>
+__device__ __forceinline__ void transpose_frags(split4 (&yt)[TT][NF], const split4 (&y)[TT][NF], lds_bf16 *stage) {
+    bf16x4 h[TT][NF], l[TT][NF], ht[TT][NF], lt[TT][NF];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            h[tt][f] = split_hi(y[tt][f]);
+            l[tt][f] = split_lo(y[tt][f]);
+        }
+    transpose_frags_lds<NF, TT>(ht, h, stage);
+    transpose_frags_lds<NF, TT>(lt, l, stage + stage_elems<NF, TT>());
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) yt[tt][f] = split_join(ht[tt][f], lt[tt][f]);
+}
+// LDS elements a transpose_frags of fragment type Fr takes (split4: two areas).
+template <typename Fr, int NF, int TT> constexpr int transpose_stage_elems() {
+    return (std::is_same<Fr, split4>::value ? 2 : 1) * stage_elems<NF, TT>();
 }
 
 // ---- state records --------------------------------------------------------

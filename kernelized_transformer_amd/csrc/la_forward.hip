@@ -46,32 +46,6 @@ template <typename T, int D, int M> constexpr int fwd_prefetch() {
 
 // ---- chunk loops ------------------------------------------------------------
 
-// Token-contiguous copies in the generic chunk loops: bf16 fragments go
-// through the wavefront's LDS area (transpose_frags_lds); split fp32
-// fragments the same way, hi parts at `stage`, lo parts after them (two
-// areas of stage_elems<NF, TT>()); plain fp32 through an identity product.
-template <int NF, typename Fr>
-__device__ __forceinline__ void tokens_major(Fr (&yt)[TT][NF], const Fr (&y)[TT][NF], lds_bf16 *stage) {
-    if constexpr (std::is_same<Fr, split4>::value) {
-        bf16x4 h[TT][NF], l[TT][NF], ht[TT][NF], lt[TT][NF];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                h[tt][f] = split_hi(y[tt][f]);
-                l[tt][f] = split_lo(y[tt][f]);
-            }
-        transpose_frags_lds<NF, TT>(ht, h, stage);
-        transpose_frags_lds<NF, TT>(lt, l, stage + stage_elems<NF, TT>());
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int f = 0; f < NF; ++f) yt[tt][f] = split_join(ht[tt][f], lt[tt][f]);
-    } else {
-        transpose_frags<NF, TT>(yt, y, stage);
-    }
-}
-
 // St += sum over tokens [t_begin, t_end) of phi(K_t) [V_t, 1]^T.
 // PF chunks are kept in flight: the loop is unrolled by PF so that chunk i
 // always lives in buffer i % PF (a register copy between buffers would force
@@ -106,8 +80,8 @@ __device__ __forceinline__ void seg_aggregate(const T *__restrict__ K, const T *
             // the loads next to their use two chunks later
             __builtin_amdgcn_sched_barrier(0);
             Fr KT[TT][D / 16], VT[TT][M / 16];
-            tokens_major<D / 16>(KT, Kn, stage_k);
-            tokens_major<M / 16>(VT, Vn, stage_v);
+            transpose_frags<D / 16>(KT, Kn, stage_k);
+            transpose_frags<M / 16>(VT, Vn, stage_v);
             state_accumulate<Fr, D, M, TT, true>(St, KT, VT);
         }
     }
@@ -213,8 +187,8 @@ __device__ __forceinline__ void seg_output(const T *__restrict__ Q, const T *__r
                     PT[jt][it] = frag_from<Fr>(p);
                 }
             Fr KT[TT][DT], VT[TT][MT];
-            tokens_major<DT>(KT, Kn, stage_k);
-            tokens_major<MT>(VT, Vn, stage_v);
+            transpose_frags<DT>(KT, Kn, stage_k);
+            transpose_frags<MT>(VT, Vn, stage_v);
             // intra-chunk term; the ones block sums P^T into den (every row)
 #pragma unroll
             for (int mt = 0; mt <= MT; ++mt)
@@ -469,7 +443,10 @@ __global__ __launch_bounds__(64 * kSegWaves) void k_segment_state(const T *__res
                                                                   float *__restrict__ ws, int64_t N, int64_t nseg,
                                                                   int64_t seg_tokens, int64_t rec) {
     static_assert(kSegWaves == 2, "the partial states are combined pairwise");
-    constexpr int STG = stage_elems<D / 16, TT>() + stage_elems<M / 16, TT>();   // bf16 per wavefront
+    // fp32 runs on split operands (split4), whose transposes take two LDS areas
+    typedef typename std::conditional<sizeof(T) == 4, split4, typename IO<T>::frag>::type Fr;
+    constexpr int SK = transpose_stage_elems<Fr, D / 16, TT>(), SV = transpose_stage_elems<Fr, M / 16, TT>();
+    constexpr int STG = SK + SV;   // bf16 per wavefront
     constexpr int NTILE = (D / 16) * (M / 16 + 1);
     constexpr int STAGE_BYTES = kSegWaves * STG * int(sizeof(bf16));
     constexpr int SLOT_BYTES = NTILE * 64 * int(sizeof(f32x4));   // one wavefront's St, lane-major
@@ -482,14 +459,15 @@ __global__ __launch_bounds__(64 * kSegWaves) void k_segment_state(const T *__res
     const int64_t t_begin = imin64(s_end, s_begin + wave * cpw * kChunk);
     const int64_t t_end = imin64(s_end, t_begin + cpw * kChunk);
     lds_bf16 *sk = (lds_bf16 *)(reinterpret_cast<bf16 *>(lds_raw) + wave * STG);
-    lds_bf16 *sv = sk + stage_elems<D / 16, TT>();
+    lds_bf16 *sv = sk + SK;
     f32x4 St[D / 16][M / 16 + 1];
     state_zero<D, M>(St);
     if (t_begin < t_end) {   // uniform; a short segment can leave wavefront 1 without chunks
         if constexpr (sizeof(T) == 2)
             seg_aggregate_bf16<D, M, kSegPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
         else
-            seg_aggregate<T, D, M, kPrefetch>(k + bh * N * D, v + bh * N * M, t_begin, t_end, St, sk, sv);
+            seg_aggregate<T, D, M, fwd_prefetch<T, D, M>(), true, Fr>(k + bh * N * D, v + bh * N * M, t_begin, t_end,
+                                                                    St, sk, sv);
     }
     __syncthreads();   // the staging areas are free
     f32x4 *slot = reinterpret_cast<f32x4 *>(lds_raw);
