@@ -25,7 +25,8 @@ on, and reported next to the headline:
     long-sequence workload;
   * a head size outside {32, 64}: causal forward and backward at B=1, H=8,
     N=16384, D=M=128 bf16 (the 16-column-group path);
-  * the causal forward of the three smaller workloads;
+  * the causal forward of the three smaller workloads, and the causal backward
+    of the 784-token fp32 one;
   * the causal forward at B=1, H=8, D=M=64 bf16 for N = 512 .. 65536 (the
     sweep; --no-sweep leaves it out).
 ``roofline`` relates the forward's algorithmic HBM bytes (Q, K, V read once,
@@ -482,8 +483,34 @@ def main():
         log(f"head size 128: forward {res['forward']['ms_per_call']:.4f} ms, "
             f"backward {res['backward']['ms_per_call']:.4f} ms")
         del qg, kg, vg, gg, og, dqg, dkg, dvg, wsf, wsb
+    def bwd_rate(w, iters=20):
+        q, k, v, g = (to_dev(x, w.dtype) for x in wl.forward_inputs(w, with_dout=True))
+        grads = [torch.empty_like(x) for x in (q, k, v)]
+        dtc = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+        ws = torch.empty(max(1, la.la_workspace_size(la.LA_OP_BWD_CAUSAL, w.B, w.H, w.N, w.D, w.M, dtc)),
+                         dtype=torch.uint8, device=dev)
+
+        def f(i):
+            st = lib.la_backward_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), grads[0].data_ptr(),
+                                        grads[1].data_ptr(), grads[2].data_ptr(), w.B, w.H, w.N, w.D, w.M, dtc,
+                                        ws.data_ptr(), ws.numel(), sptr)
+            if st != 0:
+                raise la.LAError("backward", st)
+
+        for i in range(3):
+            f(i)
+        t = time_events(f, iters)
+        th = w.B * w.H * w.N
+        by = th * ((2 * w.D + 2 * w.M) + (2 * w.D + w.M)) * (2 if w.dtype == "bf16" else 4)
+        return dict(us_per_call=t / iters * 1e6, tok_heads_per_s=th * iters / t,
+                    hbm_frac=by / (t / iters) / 1e9 / HBM_PEAK_GBS)
+
     if a.only in ("all", "small"):
         results["small_workloads"] = {wl.WORKLOADS[i].name: fwd_rate(wl.WORKLOADS[i]) for i in (1, 2, 3)}
+        # the causal backward on the 784-token fp32 workload (split fp32 operands)
+        results["small_workloads"]["backward, " + wl.WORKLOADS[2].name] = bwd_rate(wl.WORKLOADS[2])
+        for name_, r_ in results["small_workloads"].items():
+            log(f"{name_}: {r_['us_per_call']:.1f} us/call, {r_['hbm_frac']:.3f} of HBM")
     if (a.only == "all" and not a.no_sweep) or a.only == "sweep":
         results["sweep"] = {str(n): fwd_rate(w4.with_n(n)) for n in wl.SWEEP_N}
 
