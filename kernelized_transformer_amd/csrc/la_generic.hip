@@ -48,18 +48,6 @@ namespace la {
 namespace {
 
 constexpr int GCH = 16;   // tokens per chunk
-// chunks in flight ahead of the one being computed (one for fp32 at D > 64,
-// whose Q and K chunks take twice the registers)
-template <typename T, int DT> constexpr int gen_prefetch() { return (sizeof(T) == 4 && DT > 4) ? 1 : 2; }
-
-// acc += A * B^T over NT contraction tiles (pairs on bf16, a lone last tile padded).
-template <typename Fr, int NT>
-__device__ __forceinline__ void mma_run(f32x4 &acc, const Fr (&a)[NT], const Fr (&b)[NT]) {
-#pragma unroll
-    for (int t = 0; t + 1 < NT; t += 2) mma2(acc, a[t], a[t + 1], b[t], b[t + 1]);
-    if (NT & 1) mma1(acc, a[NT - 1], b[NT - 1]);
-}
-
 // 16 rows x 16 columns [col0, col0 + 16) of a row-major [.][ld] tensor as a
 // natural fragment: lane (c, g) holds row t0 + c, columns col0 + 4g .. + 3.
 // Rows at or beyond t_end read row t_end - 1.
@@ -71,56 +59,101 @@ __device__ __forceinline__ typename IO<T>::vec4 load_col_tile(const T *__restric
     return load4<T>(base + t * ld + col0 + 4 * g);
 }
 
-// Per-wavefront LDS staging for the token-contiguous copies (bf16 only).
-template <int DT> constexpr int gen_stage_elems() { return stage_elems<DT, 1>() + stage_elems<1, 1>(); }
-
-// ---- bf16: the chunk's Q and K rows shared by the column groups ---------------
+// ---- the chunk's Q and K rows shared by the column groups -----------------------
 // The wavefronts of a workgroup (one per 16-column group) all need phi of
 // the same 16 rows of Q and K.  They load those rows together, as 16-byte
-// pieces of whole rows (piece p = 64 (w + ng i) + lane of the 2F pieces of 16
-// rows of F features), apply phi once per element, and stage them in one LDS
-// area that every wavefront reads its fragments from; the feature map is not
-// repeated per group.
-// NPW: the most pieces one lane moves, (2F + 63) / 64 when one wavefront
+// pieces of whole rows (piece p = 64 (w + ng i) + lane of the 16 F sizeof(T)
+// / 16 pieces of 16 rows of F features), apply phi once per element, and
+// stage them in one LDS area that every wavefront reads its fragments from;
+// the feature map is not repeated per group.  bf16 rows are staged as they
+// are; fp32 rows as two bf16 areas, the hi and lo parts of each value (the
+// split operands of la_device.h), so the products run on the bf16 matrix
+// instruction as in the fused fp32 forward.
+template <typename T> constexpr int coop_pieces(int F) { return F * int(sizeof(T)); }   // per 16 rows
+template <typename T, int F> constexpr int coop_np() { return (coop_pieces<T>(F) + 63) / 64; }
+// CoopFrag<T>: the operand fragment of staged rows (bf16x4, or split4 for fp32).
+template <typename T> using CoopFrag = typename std::conditional<sizeof(T) == 4, split4, bf16x4>::type;
+// NPW: the most pieces one lane moves, coop_np<T, F>() when one wavefront
 // does all; the host may pass fewer when the segment's ng wavefronts cover the
-// 2F pieces with that many each (64 ng NPW >= 2F), which saves registers.
-template <int F, int NPW = (2 * F + 63) / 64> struct CoopRows {
+// pieces with that many each (64 ng NPW >= the piece count), which saves
+// registers.
+template <int F, int NPW> struct CoopRows {
     static constexpr int NP = NPW;
     dwordx4 x[NP];
 };
-template <int F, int NPW>
-__device__ __forceinline__ void coop_load(CoopRows<F, NPW> &r, const bf16 *__restrict__ base, int64_t t0,
+template <typename T, int F, int NPW>
+__device__ __forceinline__ void coop_load(CoopRows<F, NPW> &r, const T *__restrict__ base, int64_t t0,
                                           int64_t t_end, int w, int ng) {
+    constexpr int EPP = 16 / int(sizeof(T));   // elements per piece
     const int l = lane_id();
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
         const int p = 64 * (w + ng * i) + l;
-        if (p < 2 * F) {
-            const int e = 8 * p, row = e / F, col = e % F;
+        if (p < coop_pieces<T>(F)) {
+            const int e = EPP * p, row = e / F, col = e % F;
             const int64_t t = imin64(t0 + row, t_end - 1);   // rows past the end read the last row
             r.x[i] = *reinterpret_cast<const dwordx4 *>(base + t * F + col);
         }
     }
 }
-// Rows of F + kStagePad elements; PHI applies the feature map, MASK zeroes
-// rows at or beyond t_end.
-template <int F, bool PHI, bool MASK, int NPW>
+// LDS elements of one staged chunk: rows of F + kStagePad elements, twice
+// for fp32 (hi area, then lo area).
+template <int F> constexpr int coop_rows_elems() { return 16 * (F + kStagePad); }
+template <typename T, int F> constexpr int coop_stage_elems() { return (sizeof(T) == 4 ? 2 : 1) * coop_rows_elems<F>(); }
+// PHI applies the feature map, MASK zeroes rows at or beyond t_end.
+template <typename T, int F, bool PHI, bool MASK, int NPW>
 __device__ __forceinline__ void coop_stage(lds_bf16 *stage, const CoopRows<F, NPW> &r, int64_t t0, int64_t t_end,
                                            int w, int ng) {
+    constexpr int EPP = 16 / int(sizeof(T));
     const int l = lane_id();
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
         const int p = 64 * (w + ng * i) + l;
-        if (p < 2 * F) {
-            const int e = 8 * p, row = e / F, col = e % F;
-            dwordx4 y = r.x[i];
-            if (PHI) y = phi8(y);
-            if (MASK && t0 + row >= t_end) y = dwordx4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<lds_dwordx4 *>(stage + row * (F + kStagePad) + col) = y;
+        if (p < coop_pieces<T>(F)) {
+            const int e = EPP * p, row = e / F, col = e % F;
+            const bool zero = MASK && t0 + row >= t_end;
+            if constexpr (sizeof(T) == 2) {
+                dwordx4 y = r.x[i];
+                if (PHI) y = phi8(y);
+                if (zero) y = dwordx4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<lds_dwordx4 *>(stage + row * (F + kStagePad) + col) = y;
+            } else {
+                f32x4 y = __builtin_bit_cast(f32x4, r.x[i]);
+                if (PHI) y = phi4(y);
+                if (zero) y = f32x4{0.f, 0.f, 0.f, 0.f};
+                const split4 sp = split_f32(y);
+                *reinterpret_cast<lds_bf16x4 *>(stage + row * (F + kStagePad) + col) = split_hi(sp);
+                *reinterpret_cast<lds_bf16x4 *>(stage + coop_rows_elems<F>() + row * (F + kStagePad) + col) =
+                    split_lo(sp);
+            }
         }
     }
 }
-template <int F> constexpr int coop_rows_elems() { return 16 * (F + kStagePad); }
+// Natural and token-contiguous fragments of staged rows.
+template <int F>
+__device__ __forceinline__ void coop_natural(bf16x4 (&y)[1][F / 16], const lds_bf16 *stage) {
+    natural_frags_lds<F, 1>(y, stage);
+}
+template <int F>
+__device__ __forceinline__ void coop_natural(split4 (&y)[1][F / 16], const lds_bf16 *stage) {
+    bf16x4 h[1][F / 16], l[1][F / 16];
+    natural_frags_lds<F, 1>(h, stage);
+    natural_frags_lds<F, 1>(l, stage + coop_rows_elems<F>());
+#pragma unroll
+    for (int f = 0; f < F / 16; ++f) y[0][f] = split_join(h[0][f], l[0][f]);
+}
+template <int F>
+__device__ __forceinline__ void coop_transposed(bf16x4 (&y)[1][F / 16], const lds_bf16 *stage) {
+    transposed_frags_lds<F, 1>(y, stage);
+}
+template <int F>
+__device__ __forceinline__ void coop_transposed(split4 (&y)[1][F / 16], const lds_bf16 *stage) {
+    bf16x4 h[1][F / 16], l[1][F / 16];
+    transposed_frags_lds<F, 1>(h, stage);
+    transposed_frags_lds<F, 1>(l, stage + coop_rows_elems<F>());
+#pragma unroll
+    for (int f = 0; f < F / 16; ++f) y[0][f] = split_join(h[0][f], l[0][f]);
+}
 
 // phi'(x) = min(phi(x), 1) of tile ft of rows staged by coop_stage<F, true, .>
 // (phi(x) <= 1 exactly where x <= 0, where phi' = phi = exp(x)), in the
@@ -139,51 +172,67 @@ __device__ __forceinline__ f32x4 dphi_staged(const lds_bf16 *stage, int ft) {
 // ---- per-segment sums ---------------------------------------------------------
 // Record of segment `seg` (row-major S [D][M], then Z [D]): wavefront cg of the
 // segment's workgroup writes columns [16 cg, 16 cg + 16) of S, wavefront 0 Z.
-template <typename T, int DT, bool PHI>
-__global__ __launch_bounds__(512) void k_gen_segstate(const T *__restrict__ k, const T *__restrict__ v,
-                                                      float *__restrict__ ws, int64_t N, int64_t M, int64_t nseg,
-                                                      int64_t seg_tokens) {
-    constexpr int D = 16 * DT, GPF = gen_prefetch<T, DT>();
-    typedef typename IO<T>::frag Fr;
-    typedef typename IO<T>::vec4 V4;
-    __shared__ __align__(16) bf16 stage_mem[8][gen_stage_elems<DT>()];
+// The chunk's K rows arrive as whole 16-byte pieces loaded by all the
+// segment's wavefronts together (see coop_load), phi is applied once per
+// element, and the staging is double buffered: the wavefronts stage chunk c
+// into buffer c % 2, meet at one barrier, and read their fragments from it, so
+// a wavefront that stages chunk c + 2 has passed the barrier of chunk c + 1,
+// which every wavefront reaches only after its reads of chunk c.
+template <typename T, int DT, bool PHI, int NPW, bool HELP>
+__global__ __launch_bounds__(512) void k_gen_segstate_coop(const T *__restrict__ k, const T *__restrict__ v,
+                                                           float *__restrict__ ws, int64_t N, int64_t M, int64_t nseg,
+                                                           int64_t seg_tokens) {
+    constexpr int D = 16 * DT;
+    typedef CoopFrag<T> Fr;
+    __shared__ __align__(16) bf16 shk[2][coop_stage_elems<T, D>()];
+    __shared__ __align__(16) bf16 sv_mem[8][transpose_stage_elems<Fr, 1, 1>()];
+    const int ng = int(M / 16), nw = int(blockDim.x >> 6);   // column groups; wavefronts (nw >= ng)
     const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // HELP: wavefronts past the column groups only load and stage rows
+    const bool active = !HELP || cg < ng;
     const int c = lane_id() & 15, g = lane_id() >> 4;
     const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
     const T *K = k + bh * N * D;
     const T *V = v + bh * N * M;
-    lds_bf16 *sk = (lds_bf16 *)stage_mem[cg];
-    lds_bf16 *sv = sk + stage_elems<DT, 1>();
+    lds_bf16 *sv = (lds_bf16 *)sv_mem[cg];
 
-    f32x4 St[DT][2];   // S[:, 16 cg .. + 16] and (column 0) Z
+    f32x4 St[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) St[dt][0] = St[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    V4 rk[GPF][1][DT], rv[GPF];
+    // chunks loaded two ahead of the one being summed; chunk parity b picks
+    // the register set and the LDS buffer
+    CoopRows<D, NPW> rk[2];
+    typename IO<T>::vec4 rv[2];
 #pragma unroll
-    for (int b = 0; b < GPF; ++b) {
-        load_chunk<T, D, 1>(rk[b], K, t_begin + b * GCH, t_end);
-        rv[b] = load_col_tile<T>(V, M, 16 * cg, t_begin + b * GCH, t_end);
+    for (int b = 0; b < 2; ++b) {
+        coop_load<T, D>(rk[b], K, t_begin + b * GCH, t_end, cg, nw);
+        if (active) rv[b] = load_col_tile<T>(V, M, 16 * cg, t_begin + b * GCH, t_end);
     }
-    for (int64_t t00 = t_begin; t00 < t_end; t00 += GPF * GCH) {
+    for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * GCH) {
 #pragma unroll
-        for (int b = 0; b < GPF; ++b) {
-            const int64_t t0 = t00 + b * GCH;   // may lie past t_end: all rows masked, nothing added
-            Fr Kn[1][DT], Vn[1][1];
-            feat_frags<T, D, 1, PHI>(Kn, rk[b], t0, t_end);   // rows past t_end are zero
-            {
-                const V4 one[1][1] = {{rv[b]}};
+        for (int b = 0; b < 2; ++b) {
+            const int64_t t0 = t00 + b * GCH;
+            if (t0 >= t_end) break;   // uniform over the workgroup
+            lds_bf16 *sk = (lds_bf16 *)shk[b];
+            coop_stage<T, D, PHI, true>(sk, rk[b], t0, t_end, cg, nw);   // rows past t_end are zero
+            Fr Vn[1][1];
+            if (active) {
+                const typename IO<T>::vec4 one[1][1] = {{rv[b]}};
                 raw_frags<T, 16, 1>(Vn, one, t0, t_end);
             }
-            load_chunk<T, D, 1>(rk[b], K, t0 + GPF * GCH, t_end);
-            rv[b] = load_col_tile<T>(V, M, 16 * cg, t0 + GPF * GCH, t_end);
-            __builtin_amdgcn_sched_barrier(0);
-            Fr KT[1][DT], VT[1][1];
-            transpose_frags<DT, 1>(KT, Kn, sk);
-            transpose_frags<1, 1>(VT, Vn, sv);
-            state_accumulate<Fr, D, 16, 1, false>(St, KT, VT);
+            coop_load<T, D>(rk[b], K, t0 + 2 * GCH, t_end, cg, nw);
+            if (active) rv[b] = load_col_tile<T>(V, M, 16 * cg, t0 + 2 * GCH, t_end);
+            lds_barrier();
+            if (active) {
+                Fr KT[1][DT], VT[1][1];
+                coop_transposed<D>(KT, sk);
+                transpose_frags<1, 1>(VT, Vn, sv);
+                state_accumulate<Fr, D, 16, 1, false>(St, KT, VT);
+            }
         }
     }
+    if (!active) return;
     float *rec = ws + (bh * nseg + seg) * (int64_t(D) * M + D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -199,17 +248,25 @@ __global__ __launch_bounds__(512) void k_gen_segstate(const T *__restrict__ k, c
 // ---- outputs --------------------------------------------------------------------
 // Wavefront cg walks the segment's chunks from the state of everything before
 // it (causal: the segment's exclusive prefix; non-causal: the total in record
-// 0), writing columns [16 cg, 16 cg + 16) of out.
-template <typename T, int DT, bool CAUSAL, bool PHI>
-__global__ __launch_bounds__(512) void k_gen_output(const T *__restrict__ q, const T *__restrict__ k,
-                                                    const T *__restrict__ v, T *__restrict__ out,
-                                                    const float *__restrict__ ws, int64_t N, int64_t M, int64_t nseg,
-                                                    int64_t seg_tokens) {
-    constexpr int D = 16 * DT, GPF = gen_prefetch<T, DT>();
-    typedef typename IO<T>::frag Fr;
-    typedef typename IO<T>::vec4 V4;
-    __shared__ __align__(16) bf16 stage_mem[8][gen_stage_elems<DT>()];
+// 0), writing columns [16 cg, 16 cg + 16) of out; Q and K rows staged as in
+// the segment sums.  No row masks (as in the fused forward's output pass):
+// rows past the end are copies of the last valid row, their outputs are not
+// stored, the causal mask keeps them out of every stored output, and the state
+// is not used after the last chunk.
+template <typename T, int DT, bool CAUSAL, bool PHI, int NPW, bool HELP>
+__global__ __launch_bounds__(512) void k_gen_output_coop(const T *__restrict__ q, const T *__restrict__ k,
+                                                         const T *__restrict__ v, T *__restrict__ out,
+                                                         const float *__restrict__ ws, int64_t N, int64_t M,
+                                                         int64_t nseg, int64_t seg_tokens) {
+    constexpr int D = 16 * DT;
+    typedef CoopFrag<T> Fr;
+    __shared__ __align__(16) bf16 shq[2][coop_stage_elems<T, D>()];
+    __shared__ __align__(16) bf16 shk[CAUSAL ? 2 : 1][CAUSAL ? coop_stage_elems<T, D>() : 8];
+    __shared__ __align__(16) bf16 sv_mem[8][transpose_stage_elems<Fr, 1, 1>()];
+    const int ng = int(M / 16), nw = int(blockDim.x >> 6);   // column groups; wavefronts (nw >= ng)
     const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // HELP: wavefronts past the column groups only load and stage rows
+    const bool active = !HELP || cg < ng;
     const int c = lane_id() & 15, g = lane_id() >> 4;
     const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
@@ -217,179 +274,10 @@ __global__ __launch_bounds__(512) void k_gen_output(const T *__restrict__ q, con
     const T *K = k + bh * N * D;
     const T *V = v + bh * N * M;
     T *O = out + bh * N * M;
-    lds_bf16 *sk = (lds_bf16 *)stage_mem[cg];
-    lds_bf16 *sv = sk + stage_elems<DT, 1>();
-
-    // St[dt][0]: S rows 16 dt.., columns 16 cg..; St[dt][1]: Z replicated in every column
-    f32x4 St[DT][2];
-    {
-        const float *rec = ws + (bh * nseg + (CAUSAL ? seg : 0)) * (int64_t(D) * M + D);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                St[dt][0][r] = rec[(16 * dt + 4 * g + r) * M + 16 * cg + c];
-                St[dt][1][r] = rec[int64_t(D) * M + 16 * dt + 4 * g + r];
-            }
-    }
-    const Fr ones = frag_ones<Fr>();
-
-    V4 rq[GPF][1][DT], rk[GPF][1][DT], rv[GPF];
-#pragma unroll
-    for (int b = 0; b < GPF; ++b) {
-        load_chunk<T, D, 1>(rq[b], Q, t_begin + b * GCH, t_end);
-        if (CAUSAL) {
-            load_chunk<T, D, 1>(rk[b], K, t_begin + b * GCH, t_end);
-            rv[b] = load_col_tile<T>(V, M, 16 * cg, t_begin + b * GCH, t_end);
-        }
-    }
-    for (int64_t t00 = t_begin; t00 < t_end; t00 += GPF * GCH) {
-#pragma unroll
-        for (int b = 0; b < GPF; ++b) {
-            const int64_t t0 = t00 + b * GCH;   // may lie past t_end: nothing stored
-            Fr Qn[1][DT], Kn[1][DT], Vn[1][1];
-            feat_frags<T, D, 1, PHI>(Qn, rq[b], t0, t_end);
-            if (CAUSAL) {
-                feat_frags<T, D, 1, PHI>(Kn, rk[b], t0, t_end);
-                const V4 one[1][1] = {{rv[b]}};
-                raw_frags<T, 16, 1>(Vn, one, t0, t_end);
-            }
-            load_chunk<T, D, 1>(rq[b], Q, t0 + GPF * GCH, t_end);
-            if (CAUSAL) {
-                load_chunk<T, D, 1>(rk[b], K, t0 + GPF * GCH, t_end);
-                rv[b] = load_col_tile<T>(V, M, 16 * cg, t0 + GPF * GCH, t_end);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-
-            // out^T (16 columns, then the normalizer rows) against the carried state
-            f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                Fr SF[DT];
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<T>::to_frag(St[dt][mt]);
-                mma_run<Fr, DT>(Ot[mt], SF, Qn[0]);
-            }
-            if (CAUSAL) {
-                // P^T[j][i] = phi(K_j) . phi(Q_i), j <= i
-                f32x4 p = {0.f, 0.f, 0.f, 0.f};
-                mma_run<Fr, DT>(p, Kn[0], Qn[0]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-                const Fr PT = IO<T>::to_frag(p);
-                Fr KT[1][DT], VT[1][1];
-                transpose_frags<DT, 1>(KT, Kn, sk);
-                transpose_frags<1, 1>(VT, Vn, sv);
-                mma1(Ot[0], VT[0][0], PT);
-                mma1(Ot[1], ones, PT);
-                state_accumulate<Fr, D, 16, 1, true>(St, KT, VT);
-            }
-            // every row of the normalizer tile holds den: lane (c, g) element 0 is token c's
-            const float inv = __builtin_amdgcn_rcpf(Ot[1][0]);
-            const int64_t t = t0 + c;
-            if (t < t_end) store4<T>(O + t * M + 16 * cg + 4 * g, IO<T>::from_f32(Ot[0] * inv));
-        }
-    }
-}
-
-
-// ---- bf16 variants: phi(Q), phi(K) staged once per chunk for all groups ----------
-// Same results as the kernels above up to the order of nothing (every
-// product and sum is formed the same way); the rows arrive as whole 16-byte
-// pieces, phi is applied once per element, and the staging is double
-// buffered: the wavefronts stage chunk c into buffer c % 2, meet at one
-// barrier, and read their fragments from it, so a wavefront that stages chunk
-// c + 2 has passed the barrier of chunk c + 1, which every wavefront reaches
-// only after its reads of chunk c.
-template <int DT, bool PHI, int NPW>
-__global__ __launch_bounds__(512) void k_gen_segstate_bf16(const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-                                                           float *__restrict__ ws, int64_t N, int64_t M, int64_t nseg,
-                                                           int64_t seg_tokens) {
-    constexpr int D = 16 * DT;
-    typedef bf16x4 Fr;
-    __shared__ __align__(16) bf16 shk[2][coop_rows_elems<D>()];
-    __shared__ __align__(16) bf16 sv_mem[8][stage_elems<1, 1>()];
-    const int ng = int(M / 16);
-    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
-    const bf16 *K = k + bh * N * D;
-    const bf16 *V = v + bh * N * M;
     lds_bf16 *sv = (lds_bf16 *)sv_mem[cg];
 
     f32x4 St[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) St[dt][0] = St[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // chunks loaded two ahead of the one being summed; chunk parity b picks
-    // the register set and the LDS buffer
-    CoopRows<D, NPW> rk[2];
-    bf16x4 rv[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        coop_load<D>(rk[b], K, t_begin + b * GCH, t_end, cg, ng);
-        rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t_begin + b * GCH, t_end);
-    }
-    for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * GCH) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int64_t t0 = t00 + b * GCH;
-            if (t0 >= t_end) break;   // uniform over the workgroup
-            lds_bf16 *sk = (lds_bf16 *)shk[b];
-            coop_stage<D, PHI, true>(sk, rk[b], t0, t_end, cg, ng);   // rows past t_end are zero
-            Fr Vn[1][1];
-            {
-                const bf16x4 one[1][1] = {{rv[b]}};
-                raw_frags<bf16, 16, 1>(Vn, one, t0, t_end);
-            }
-            coop_load<D>(rk[b], K, t0 + 2 * GCH, t_end, cg, ng);
-            rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t0 + 2 * GCH, t_end);
-            lds_barrier();
-            Fr KT[1][DT], VT[1][1];
-            transposed_frags_lds<D, 1>(KT, sk);
-            transpose_frags<1, 1>(VT, Vn, sv);
-            state_accumulate<Fr, D, 16, 1, false>(St, KT, VT);
-        }
-    }
-    float *rec = ws + (bh * nseg + seg) * (int64_t(D) * M + D);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rec[(16 * dt + 4 * g + r) * M + 16 * cg + c] = St[dt][0][r];
-        if (cg == 0 && c == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rec[int64_t(D) * M + 16 * dt + 4 * g + r] = St[dt][1][r];
-        }
-    }
-}
-
-// Outputs, as k_gen_output.  No row masks (as in the fused forward's output
-// pass): rows past the end are copies of the last valid row, their outputs are
-// not stored, the causal mask keeps them out of every stored output, and the
-// state is not used after the last chunk.
-template <int DT, bool CAUSAL, bool PHI, int NPW>
-__global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                                                         const bf16 *__restrict__ v, bf16 *__restrict__ out,
-                                                         const float *__restrict__ ws, int64_t N, int64_t M,
-                                                         int64_t nseg, int64_t seg_tokens) {
-    constexpr int D = 16 * DT;
-    typedef bf16x4 Fr;
-    __shared__ __align__(16) bf16 shq[2][coop_rows_elems<D>()];
-    __shared__ __align__(16) bf16 shk[CAUSAL ? 2 : 1][CAUSAL ? coop_rows_elems<D>() : 8];
-    __shared__ __align__(16) bf16 sv_mem[8][stage_elems<1, 1>()];
-    const int ng = int(M / 16);
-    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane_id() & 15, g = lane_id() >> 4;
-    const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
-    const bf16 *Q = q + bh * N * D;
-    const bf16 *K = k + bh * N * D;
-    const bf16 *V = v + bh * N * M;
-    bf16 *O = out + bh * N * M;
-    lds_bf16 *sv = (lds_bf16 *)sv_mem[cg];
-
-    f32x4 St[DT][2];
-    {
+    if (active) {
         const float *rec = ws + (bh * nseg + (CAUSAL ? seg : 0)) * (int64_t(D) * M + D);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -404,13 +292,13 @@ __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict_
     // chunks loaded two ahead of the one being computed; chunk parity b
     // picks the register set and the LDS buffer
     CoopRows<D, NPW> rq[2], rk[2];
-    bf16x4 rv[2];
+    typename IO<T>::vec4 rv[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        coop_load<D>(rq[b], Q, t_begin + b * GCH, t_end, cg, ng);
+        coop_load<T, D>(rq[b], Q, t_begin + b * GCH, t_end, cg, nw);
         if (CAUSAL) {
-            coop_load<D>(rk[b], K, t_begin + b * GCH, t_end, cg, ng);
-            rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t_begin + b * GCH, t_end);
+            coop_load<T, D>(rk[b], K, t_begin + b * GCH, t_end, cg, nw);
+            if (active) rv[b] = load_col_tile<T>(V, M, 16 * cg, t_begin + b * GCH, t_end);
         }
     }
     for (int64_t t00 = t_begin; t00 < t_end; t00 += 2 * GCH) {
@@ -420,38 +308,39 @@ __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict_
         if (t0 >= t_end) break;   // uniform over the workgroup
         lds_bf16 *sq = (lds_bf16 *)shq[b];
         lds_bf16 *sk = (lds_bf16 *)shk[CAUSAL ? b : 0];
-        coop_stage<D, PHI, false>(sq, rq[b], t0, t_end, cg, ng);
+        coop_stage<T, D, PHI, false>(sq, rq[b], t0, t_end, cg, nw);
         Fr Vn[1][1];
         if (CAUSAL) {
-            coop_stage<D, PHI, false>(sk, rk[b], t0, t_end, cg, ng);
-            value_frags_unmasked(Vn[0][0], rv[b]);
+            coop_stage<T, D, PHI, false>(sk, rk[b], t0, t_end, cg, nw);
+            if (active) value_frags_unmasked(Vn[0][0], rv[b]);
         }
-        coop_load<D>(rq[b], Q, t0 + 2 * GCH, t_end, cg, ng);
+        coop_load<T, D>(rq[b], Q, t0 + 2 * GCH, t_end, cg, nw);
         if (CAUSAL) {
-            coop_load<D>(rk[b], K, t0 + 2 * GCH, t_end, cg, ng);
-            rv[b] = load_col_tile<bf16>(V, M, 16 * cg, t0 + 2 * GCH, t_end);
+            coop_load<T, D>(rk[b], K, t0 + 2 * GCH, t_end, cg, nw);
+            if (active) rv[b] = load_col_tile<T>(V, M, 16 * cg, t0 + 2 * GCH, t_end);
         }
         lds_barrier();
+        if (!active) continue;   // uniform: the load-only wavefronts go on to the next chunk
         Fr Qn[1][DT];
-        natural_frags_lds<D, 1>(Qn, sq);
+        coop_natural<D>(Qn, sq);
 
         f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             Fr SF[DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) SF[dt] = IO<bf16>::to_frag(St[dt][mt]);
+            for (int dt = 0; dt < DT; ++dt) SF[dt] = frag_from<Fr>(St[dt][mt]);
             mma_tiles<Fr, DT>(Ot[mt], SF, Qn[0]);
         }
         if (CAUSAL) {
             Fr Kn[1][DT], KT[1][DT], VT[1][1];
-            natural_frags_lds<D, 1>(Kn, sk);
-            transposed_frags_lds<D, 1>(KT, sk);
+            coop_natural<D>(Kn, sk);
+            coop_transposed<D>(KT, sk);
             f32x4 p = {0.f, 0.f, 0.f, 0.f};
             mma_tiles<Fr, DT>(p, Kn[0], Qn[0]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-            const Fr PT = IO<bf16>::to_frag(p);
+            const Fr PT = frag_from<Fr>(p);
             transpose_frags<1, 1>(VT, Vn, sv);
             mma1(Ot[0], VT[0][0], PT);
             mma1(Ot[1], ones, PT);
@@ -459,7 +348,7 @@ __global__ __launch_bounds__(512) void k_gen_output_bf16(const bf16 *__restrict_
         }
         const float inv = __builtin_amdgcn_rcpf(Ot[1][0]);
         const int64_t t = t0 + c;
-        if (t < t_end) store4<bf16>(O + t * M + 16 * cg + 4 * g, IO<bf16>::from_f32(Ot[0] * inv));
+        if (t < t_end) store4<T>(O + t * M + 16 * cg + 4 * g, IO<T>::from_f32(Ot[0] * inv));
     }
     }
 }
@@ -552,8 +441,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     } in[PF];
     auto load_all = [&](In &x, int64_t t0) {
         if constexpr (SHARED) {
-            coop_load<D>(x.cq, (const bf16 *)Q, t0, t_end, cg, ng);
-            if (CAUSAL) coop_load<D>(x.ck, (const bf16 *)K, t0, t_end, cg, ng);
+            coop_load<bf16, D>(x.cq, (const bf16 *)Q, t0, t_end, cg, ng);
+            if (CAUSAL) coop_load<bf16, D>(x.ck, (const bf16 *)K, t0, t_end, cg, ng);
         } else {
             load_chunk<T, D, 1>(x.rq, Q, t0, t_end);
             if (CAUSAL) load_chunk<T, D, 1>(x.rk, K, t0, t_end);
@@ -579,8 +468,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         }
         const f32x4 graw = IO<T>::to_f32(cur.rg);
         if constexpr (SHARED) {
-            coop_stage<D, true, true>(sq, cur.cq, t0, t_end, cg, ng);   // rows past t_end are zero
-            if (CAUSAL) coop_stage<D, true, true>(sk, cur.ck, t0, t_end, cg, ng);
+            coop_stage<bf16, D, true, true>(sq, cur.cq, t0, t_end, cg, ng);   // rows past t_end are zero
+            if (CAUSAL) coop_stage<bf16, D, true, true>(sk, cur.ck, t0, t_end, cg, ng);
             load_all(cur, t0 + PF * GCH);   // rows past t_end read row t_end - 1
             lds_barrier();
             natural_frags_lds<D, 1>(Qn, sq);
@@ -796,8 +685,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
     } in[PF];
     auto load_all = [&](In &x, int64_t t0) {
         if constexpr (SHARED) {
-            if (CAUSAL) coop_load<D>(x.cq, (const bf16 *)Q, t0, t_end, cg, ng);
-            coop_load<D>(x.ck, (const bf16 *)K, t0, t_end, cg, ng);
+            if (CAUSAL) coop_load<bf16, D>(x.cq, (const bf16 *)Q, t0, t_end, cg, ng);
+            coop_load<bf16, D>(x.ck, (const bf16 *)K, t0, t_end, cg, ng);
         } else {
             if (CAUSAL) load_chunk<T, D, 1>(x.rq, Q, t0, t_end);
             load_chunk<T, D, 1>(x.rk, K, t0, t_end);
@@ -824,8 +713,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         lds_bf16 *sq = (lds_bf16 *)shq[SHARED && CAUSAL ? b : 0];
         lds_bf16 *sk = (lds_bf16 *)shk[SHARED ? b : 0];
         if constexpr (SHARED) {
-            if (CAUSAL) coop_stage<D, true, true>(sq, cur.cq, t0, t_end, cg, ng);   // rows past t_end are zero
-            coop_stage<D, true, true>(sk, cur.ck, t0, t_end, cg, ng);
+            if (CAUSAL) coop_stage<bf16, D, true, true>(sq, cur.cq, t0, t_end, cg, ng);   // rows past t_end are zero
+            coop_stage<bf16, D, true, true>(sk, cur.ck, t0, t_end, cg, ng);
         } else {
             if (CAUSAL) phi_frags<T, D, 1>(Qn, cur.rq, t0, t_end);
             phi_frags<T, D, 1>(Kn, cur.rk, t0, t_end);
@@ -964,37 +853,44 @@ size_t generic_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M) {
 // Whether each lane moves at most one piece of a chunk's shared Q or K rows
 // (CoopRows NPW = 1): the segment's M / 16 wavefronts cover the 2 D
 // sixteen-byte pieces once, 64 (M / 16) >= 2 D.
-template <int DT> static bool gen_one_piece(int64_t M) { return CoopRows<16 * DT>::NP == 1 || 64 * (M / 16) >= 32 * DT; }
+// Whether each lane moves at most one piece of a chunk's shared Q or K rows
+// (CoopRows NPW = 1): the segment's M / 16 wavefronts cover the pieces once.
+// Wavefronts of a forward workgroup: one per column group, and at least
+// enough that each lane moves at most two pieces of a chunk's shared Q or K
+// rows (the extra wavefronts only load and stage rows).
+template <typename T, int DT> static int gen_waves(int64_t M) {
+    const int need = int((coop_pieces<T>(16 * DT) + 127) / 128);
+    return int(M / 16) > need ? int(M / 16) : need;
+}
+// Pieces per lane (NPW) of a forward launch with nw wavefronts: 1 or 2.
+template <typename T, int DT> static int gen_npw(int nw) { return 64 * nw >= coop_pieces<T>(16 * DT) ? 1 : 2; }
+// Whether each lane of the backward's M / 16 wavefronts moves one piece (bf16).
+template <typename T, int DT> static bool gen_one_piece(int64_t M) {
+    return coop_np<T, 16 * DT>() == 1 || 64 * (M / 16) >= coop_pieces<T>(16 * DT);
+}
 
-// Per-segment sums of phi(K) [V, 1]^T (bf16: the shared-staging kernel).
+// Per-segment sums of phi(K) [V, 1]^T (the block is 64 gen_waves(M) threads).
 template <typename T, int DT>
-static void launch_gen_segstate(bool phi, dim3 grid, dim3 block, const void *k, const void *v, float *ws, int64_t N,
-                                int64_t M, const SegPlan &p, hipStream_t s) {
-    if constexpr (sizeof(T) == 2) {
-        constexpr int NP = CoopRows<16 * DT>::NP;
-#define LA_GEN_SEG(P, W)                                                                                          \
-    hipLaunchKernelGGL((k_gen_segstate_bf16<DT, P, W>), grid, block, 0, s, (const bf16 *)k, (const bf16 *)v, ws, N, \
-                       M, p.nseg, p.seg_tokens)
-        if (gen_one_piece<DT>(M)) {
-            if (phi)
-                LA_GEN_SEG(true, 1);
-            else
-                LA_GEN_SEG(false, 1);
-        } else if constexpr (NP > 1) {
-            if (phi)
-                LA_GEN_SEG(true, NP);
-            else
-                LA_GEN_SEG(false, NP);
-        }
+static void launch_gen_segstate(bool phi, dim3 grid, const void *k, const void *v, float *ws, int64_t N, int64_t M,
+                                const SegPlan &p, hipStream_t s) {
+    const int nw = gen_waves<T, DT>(M);
+    const dim3 block(unsigned(64 * nw));
+#define LA_GEN_SEG(W, H)                                                                                          \
+    do {                                                                                                          \
+        if (phi)                                                                                                  \
+            hipLaunchKernelGGL((k_gen_segstate_coop<T, DT, true, W, H>), grid, block, 0, s, (const T *)k,          \
+                               (const T *)v, ws, N, M, p.nseg, p.seg_tokens);                                     \
+        else                                                                                                      \
+            hipLaunchKernelGGL((k_gen_segstate_coop<T, DT, false, W, H>), grid, block, 0, s, (const T *)k,         \
+                               (const T *)v, ws, N, M, p.nseg, p.seg_tokens);                                     \
+    } while (0)
+    if (gen_npw<T, DT>(nw) == 1)
+        LA_GEN_SEG(1, false);
+    else if (nw == M / 16)
+        LA_GEN_SEG(2, false);
+    else if constexpr (coop_pieces<T>(16 * DT) > 128)
+        LA_GEN_SEG(2, true);
 #undef LA_GEN_SEG
-    } else {
-        if (phi)
-            hipLaunchKernelGGL((k_gen_segstate<T, DT, true>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N,
-                               M, p.nseg, p.seg_tokens);
-        else
-            hipLaunchKernelGGL((k_gen_segstate<T, DT, false>), grid, block, 0, s, (const T *)k, (const T *)v, ws, N,
-                               M, p.nseg, p.seg_tokens);
-    }
 }
 
 template <typename T, int DT>
@@ -1002,9 +898,9 @@ static hipError_t run_generic(bool causal, bool phi, const void *q, const void *
                               int64_t BH, int64_t N, int64_t M, float *ws, StateIO sio, hipStream_t s) {
     constexpr int D = 16 * DT;
     const SegPlan p = make_plan(BH, N, D, M);
-    const dim3 grid(unsigned(BH * p.nseg)), block(unsigned(64 * (M / 16)));
+    const dim3 grid(unsigned(BH * p.nseg));
     ws = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + kGenHeader);
-    launch_gen_segstate<T, DT>(phi, grid, block, k, v, ws, N, M, p, s);
+    launch_gen_segstate<T, DT>(phi, grid, k, v, ws, N, M, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ScanIO io;
@@ -1014,21 +910,21 @@ static hipError_t run_generic(bool causal, bool phi, const void *q, const void *
     io.z1 = sio.z1;
     io.srec = int64_t(D) * M;
     if ((e = launch_scan(ws, BH, p.nseg, p.rec, causal ? 0 : 1, s, io)) != hipSuccess) return e;
-    constexpr int NP = CoopRows<D>::NP;
-    const bool one = gen_one_piece<DT>(M);
+    const int nw = gen_waves<T, DT>(M);
+    const dim3 block(unsigned(64 * nw));
+    const int npw = gen_npw<T, DT>(nw);
+#define LA_GEN_OUT_K(C, P, W, H)                                                                                  \
+    hipLaunchKernelGGL((k_gen_output_coop<T, DT, C, P, W, H>), grid, block, 0, s, (const T *)q, (const T *)k,       \
+                       (const T *)v, (T *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens)
 #define LA_GEN_OUT(C, P)                                                                                          \
-    if constexpr (sizeof(T) == 2) {                                                                               \
-        if (one)                                                                                                  \
-            hipLaunchKernelGGL((k_gen_output_bf16<DT, C, P, 1>), grid, block, 0, s, (const bf16 *)q,              \
-                               (const bf16 *)k, (const bf16 *)v, (bf16 *)out, (const float *)ws, N, M, p.nseg,    \
-                               p.seg_tokens);                                                                     \
-        else if constexpr (NP > 1)                                                                                \
-            hipLaunchKernelGGL((k_gen_output_bf16<DT, C, P, NP>), grid, block, 0, s, (const bf16 *)q,             \
-                               (const bf16 *)k, (const bf16 *)v, (bf16 *)out, (const float *)ws, N, M, p.nseg,    \
-                               p.seg_tokens);                                                                     \
-    } else                                                                                                        \
-        hipLaunchKernelGGL((k_gen_output<T, DT, C, P>), grid, block, 0, s, (const T *)q, (const T *)k,            \
-                           (const T *)v, (T *)out, (const float *)ws, N, M, p.nseg, p.seg_tokens)
+    do {                                                                                                          \
+        if (npw == 1)                                                                                             \
+            LA_GEN_OUT_K(C, P, 1, false);                                                                         \
+        else if (nw == M / 16)                                                                                    \
+            LA_GEN_OUT_K(C, P, 2, false);                                                                         \
+        else if constexpr (coop_pieces<T>(D) > 128)                                                               \
+            LA_GEN_OUT_K(C, P, 2, true);                                                                          \
+    } while (0)
     if (!causal) {
         LA_GEN_OUT(false, true);
     } else if (phi) {
@@ -1037,6 +933,7 @@ static hipError_t run_generic(bool causal, bool phi, const void *q, const void *
         LA_GEN_OUT(true, false);
     }
 #undef LA_GEN_OUT
+#undef LA_GEN_OUT_K
     return hipGetLastError();
 }
 
@@ -1108,12 +1005,12 @@ static hipError_t run_generic_backward(bool causal, const void *q, const void *k
     float *ibuf = causal ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.inv_off) : nullptr;
     float *hbuf = causal ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.h_off) : nullptr;
     const dim3 grid(unsigned(BH * p.nseg)), block(unsigned(64 * (M / 16)));
-    launch_gen_segstate<T, DT>(true, grid, block, k, v, wsS, N, M, p, s);
+    launch_gen_segstate<T, DT>(true, grid, k, v, wsS, N, M, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_scan(wsS, BH, p.nseg, p.rec, causal ? 0 : 1, s)) != hipSuccess) return e;
-    constexpr int NP = CoopRows<D>::NP;
-    if (sizeof(T) == 4 || gen_one_piece<DT>(M))
+    constexpr int NP = coop_np<bf16, D>();
+    if (sizeof(T) == 4 || gen_one_piece<bf16, DT>(M))
         return run_gbwd_passes<T, DT, 1>(causal, grid, block, q, k, v, dout, dq, dk, dv, BH, N, M, p, wsS, wsR, ibuf,
                                          hbuf, s);
     if constexpr (sizeof(T) == 2 && NP > 1)
