@@ -12,10 +12,11 @@
 // by 16-column groups of V (and out): one wavefront owns a (segment, column
 // group) pair and carries only its D x 16 slice of S plus the normalizer
 // block (2 D / 16 accumulator tiles, 32 fp32 registers per 16 rows of D),
-// which fits every D up to 128.  Each wavefront applies the feature map to
-// the whole of Q and K for its chunks and forms the chunk's D-deep products
-// itself; the M / 16 wavefronts of a segment read the same Q, K rows (from
-// the caches after the first).  Three launches: per-segment sums of
+// which fits every D up to 128.  The chunk's Q and K rows are loaded by the
+// segment's wavefronts together, mapped through phi once and staged in LDS,
+// from which every wavefront reads the operands of its chunk's D-deep
+// products (fp32 rows as split bf16 parts for the bf16 matrix instruction).
+// Three launches: per-segment sums of
 // phi(K) [V, 1]^T into row-major records (each wavefront its columns), the
 // scan of la_forward.hip over segments (with the optional start state and
 // final state), then the outputs.
@@ -377,7 +378,7 @@ __device__ __forceinline__ f32x4 reduce_rows(const f32x4 (*part)[DT][64], int ng
 }
 
 // Forward direction.  Wavefront cg: S and Z slice St (Z replicated, as in
-// k_gen_output), this segment's reverse sums Ra = sum_i phi(q_i) [g_i, h_i]^T
+// k_gen_output_coop), this segment's reverse sums Ra = sum_i phi(q_i) [g_i, h_i]^T
 // restricted to its columns (u, in column 0 of the second tile, on group 0).
 // bf16 keeps the register count within two wavefronts per SIMD for every D:
 // the state's bf16 copy goes to LDS as soon as it is formed, and the operand
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
     typedef typename IO<T>::frag Fr;
     typedef typename IO<T>::vec4 V4;
     // bf16 (SHARED): phi(Q) and phi(K) rows staged once per chunk for every
-    // group, double-buffered (see k_gen_output_bf16); phi'(x) = min(phi(x), 1)
+    // group, double-buffered (see k_gen_output_coop); phi'(x) = min(phi(x), 1)
     // is read off the staged phi
     constexpr bool SHARED = sizeof(T) == 2;
     constexpr int SR = SHARED ? coop_rows_elems<D>() : 8;
