@@ -355,6 +355,26 @@ __global__ __launch_bounds__(512) void k_gen_output_coop(const T *__restrict__ q
 }
 
 // ---- backward ----------------------------------------------------------------------
+// Token-contiguous copies in the column-group backward: bf16 through the
+// wavefront's LDS area; fp32 operands, split (split4) or not, by identity
+// products on the matrix cores, exact, since the groups' partial sums leave
+// no LDS for the two-area copies of split operands.
+template <int NF, int TT>
+__device__ __forceinline__ void gtrans(bf16x4 (&yt)[TT][NF], const bf16x4 (&y)[TT][NF], lds_bf16 *stage) {
+    transpose_frags<NF, TT>(yt, y, stage);
+}
+template <int NF, int TT>
+__device__ __forceinline__ void gtrans(f32x4 (&yt)[TT][NF], const f32x4 (&y)[TT][NF], lds_bf16 *stage) {
+    transpose_frags<NF, TT>(yt, y, stage);   // identity products on the fp32 instruction
+}
+template <int NF, int TT>
+__device__ __forceinline__ void gtrans(split4 (&yt)[TT][NF], const split4 (&y)[TT][NF], lds_bf16 *) {
+    const split4 ident = frag_identity<split4>();
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) yt[tt][f] = transpose_frag(y[tt][f], ident);
+}
 // LDS per wavefront for the token-contiguous copies (bf16: the D x 32 state
 // slice, or one chunk of phi(Q) and the two g columns tiles); fp32 copies go
 // through identity products.
@@ -392,7 +412,10 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
                                                  float *__restrict__ hbuf, int64_t N, int64_t M, int64_t nseg,
                                                  int64_t seg_tokens) {
     constexpr int D = 16 * DT;
-    typedef typename IO<T>::frag Fr;
+    // fp32: split operands up to D = 64; beyond, their conversions and
+    // identity-product copies cost more registers than the loops have, and
+    // the fp32 instruction is faster there
+    typedef typename std::conditional<(sizeof(T) == 4 && DT > 4), f32x4, CoopFrag<T>>::type Fr;
     typedef typename IO<T>::vec4 V4;
     // bf16 (SHARED): phi(Q) and phi(K) rows staged once per chunk for every
     // group, double-buffered (see k_gen_output_coop); phi'(x) = min(phi(x), 1)
@@ -488,7 +511,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         // V^T before the state copy takes the staging area (bf16: the
         // transposing write and read use the area the copy overwrites next)
         Fr VT[1][1];
-        if (CAUSAL) transpose_frags<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
+        if (CAUSAL) gtrans<1, 1>(VT, Vn, stage + stage_elems<DT, 1>());
 
         // intra-chunk scores P^T[j][i] = phi(k_j) . phi(q_i), j <= i (first, so
         // that phi(K) is no longer held while the state is read out)
@@ -499,8 +522,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             mma_tiles<Fr, DT>(p, Kn[0], Qn[0]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= c) ? p[r] : 0.f;
-            PT = IO<T>::to_frag(p);
-            if constexpr (!SHARED) transpose_frags<DT, 1>(KT, Kn, stage);
+            PT = frag_from<Fr>(p);
+            if constexpr (!SHARED) gtrans<DT, 1>(KT, Kn, stage);
         }
 
         // out^T of this group's columns (Ot[0]) and den (every row of Ot[1]);
@@ -513,7 +536,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             Fr sf[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                sf[dt] = IO<T>::to_frag(St[dt][mt]);
+                sf[dt] = frag_from<Fr>(St[dt][mt]);
                 if constexpr (SHARED)
                     *reinterpret_cast<lds_bf16x4 *>(stage + (16 * mt + c) * SS + 16 * dt + 4 * g) = sf[dt];
                 else
@@ -541,8 +564,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             ibuf[bh * N + t] = inv;
             hbuf[bh * N + t] = h;
         }
-        const Fr Gn = IO<T>::to_frag(graw * inv);                           // rows past t_end: inv = 0
-        const Fr Gh = IO<T>::to_frag(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});   // h in column 0
+        const Fr Gn = frag_from<Fr>(graw * inv);                           // rows past t_end: inv = 0
+        const Fr Gh = frag_from<Fr>(f32x4{g == 0 ? h : 0.f, 0.f, 0.f, 0.f});   // h in column 0
 
         // dA^T[j][i] = v_j . g_i over this group's columns (group 0 adds h_i), j <= i
         Fr dAT = frag_zero<Fr>();
@@ -552,7 +575,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             if (cg == 0) mma1(da, k0ones, Gh);
 #pragma unroll
             for (int r = 0; r < 4; ++r) da[r] = (4 * g + r <= c) ? da[r] : 0.f;
-            dAT = IO<T>::to_frag(da);
+            dAT = frag_from<Fr>(da);
         }
 
         // this group's part of dL/dphi(q)^T[d][i]: sum_j phi(k_j)[d] dA^T[j][i]
@@ -568,7 +591,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
             }
         } else {
             Fr SFT[2][DT];
-            transpose_frags<DT, 2>(SFT, SF, stage);
+            gtrans<DT, 2>(SFT, SF, stage);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -594,10 +617,10 @@ __global__ __launch_bounds__(512) void k_gbwd_dq(const T *__restrict__ q, const 
         if constexpr (SHARED)
             transposed_frags_lds<D, 1>(QT, sq);
         else
-            transpose_frags<DT, 1>(QT, Qn, stage);
+            gtrans<DT, 1>(QT, Qn, stage);
         {
             const Fr gg[1][2] = {{Gn, Gh}};
-            transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
+            gtrans<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -640,7 +663,10 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
                                                    const float *__restrict__ wsR, int64_t N, int64_t M,
                                                    int64_t nseg, int64_t seg_tokens) {
     constexpr int D = 16 * DT;
-    typedef typename IO<T>::frag Fr;
+    // fp32: split operands up to D = 64; beyond, their conversions and
+    // identity-product copies cost more registers than the loops have, and
+    // the fp32 instruction is faster there
+    typedef typename std::conditional<(sizeof(T) == 4 && DT > 4), f32x4, CoopFrag<T>>::type Fr;
     typedef typename IO<T>::vec4 V4;
     constexpr bool SHARED = sizeof(T) == 2;   // as in k_gbwd_dq
     constexpr int SR = SHARED ? coop_rows_elems<D>() : 8;
@@ -727,8 +753,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             raw_frags<T, 16, 1>(Vn, one, t0, t_end);
         }
         if (CAUSAL) {   // g = dout / d as in the forward-direction pass; rows past t_end are 0 (ri = 0)
-            Gn = IO<T>::to_frag(IO<T>::to_f32(cur.rg) * cur.ri);
-            Gh = IO<T>::to_frag(f32x4{g == 0 ? cur.rh : 0.f, 0.f, 0.f, 0.f});
+            Gn = frag_from<Fr>(IO<T>::to_f32(cur.rg) * cur.ri);
+            Gh = frag_from<Fr>(f32x4{g == 0 ? cur.rh : 0.f, 0.f, 0.f, 0.f});
         }
         if (ci >= PF) load_all(cur, t0 - PF * GCH);
         if constexpr (SHARED) {
@@ -744,7 +770,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
         Fr GT[1][2];
         if (CAUSAL) {
             const Fr gg[1][2] = {{Gn, Gh}};
-            transpose_frags<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
+            gtrans<2, 1>(GT, gg, stage + stage_elems<DT, 1>());
         }
 
         // P[i][j] = phi(q_i) . phi(k_j); dA[i][j] = g_i . v_j over this group's columns
@@ -761,8 +787,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
                 p[r] = keep ? p[r] : 0.f;
                 da[r] = keep ? da[r] : 0.f;
             }
-            Pf = IO<T>::to_frag(p);
-            dAf = IO<T>::to_frag(da);
+            Pf = frag_from<Fr>(p);
+            dAf = frag_from<Fr>(da);
         }
 
         // dV^T[m][j] (its columns) = sum_i g[i][m] P[i][j] + sum_d R[d][m] phi(k_j)[d];
@@ -777,7 +803,7 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
                 Fr rf[DT];
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    rf[dt] = IO<T>::to_frag(Rr[dt][mt]);
+                    rf[dt] = frag_from<Fr>(Rr[dt][mt]);
                     if constexpr (SHARED)
                         *reinterpret_cast<lds_bf16x4 *>(stage + (16 * mt + c) * SS + 16 * dt + 4 * g) = rf[dt];
                     else
@@ -802,8 +828,8 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
             }
         } else {
             Fr RFT[2][DT];
-            transpose_frags<DT, 2>(RFT, RF, stage);
-            if (CAUSAL) transpose_frags<DT, 1>(QT, Qn, stage);
+            gtrans<DT, 2>(RFT, RF, stage);
+            if (CAUSAL) gtrans<DT, 1>(QT, Qn, stage);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};

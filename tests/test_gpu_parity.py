@@ -186,9 +186,10 @@ def _check_single_token_grads(q, k, v, g, dq, dk, dtype):
     with d = phi(q).phi(k), from operands rounded to the I/O type, so what
     remains is a rounding residue of those terms: per element at most
     8 u phi(k)_d phi'(q)_d sum_m |g_m v_m| / d (and the same with q and k
-    swapped), u = 2^-8 for bf16 and 2^-23 for fp32 (a few roundings of each
-    term, with room to spare)."""
-    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    swapped), u = 2^-8 for bf16 and 2^-16 for fp32, whose operands enter the
+    matrix products split into bf16 hi + lo parts within 2^-16 of each value
+    (a few roundings of each term, with room to spare)."""
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -16
     pq, dpq = oracle.feature_map(q)
     pk, dpk = oracle.feature_map(k)
     d = (pq * pk).sum(-1, keepdims=True)
