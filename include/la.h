@@ -22,11 +22,11 @@
  *     bf16).  All state and accumulation is fp32 inside the kernels.  Matrix
  *     products take bf16 operands (bf16 I/O: the inputs as they are, the
  *     carried fp32 state rounded once per product); with fp32 I/O the
- *     forwards at every head size and the backwards at D, M in {32, 64} split
- *     every fp32 operand into two bf16 parts, x = hi + lo within 2^-16 |x|,
- *     and form the exact product of the split values, while the other
- *     kernels (the backwards at other head sizes, the polynomial kernel, the
- *     random-feature projection) use fp32 products.
+ *     forwards at every head size and the backwards at D <= 64 split every
+ *     fp32 operand into two bf16 parts, x = hi + lo within 2^-16 |x|, and
+ *     form the exact product of the split values, while the other kernels
+ *     (the backwards at D >= 80, the polynomial kernel, the random-feature
+ *     projection) use fp32 products.
  *   - Head sizes: the forwards (la_forward_causal, _state, _features,
  *     _noalloc, _noncausal), the backwards and la_decode_step take D, M (F
  *     for features) any multiple of 16 from 16 to 128 -- D, M in {32, 64}
