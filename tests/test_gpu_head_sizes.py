@@ -143,6 +143,9 @@ BWD_CASES = [
     ("d128m128_f32", _w(530, 1, 2, 1200, 128, 128, "f32")),
     ("d128m16_bf16", _w(532, 1, 2, 1200, 128, 16, "bf16")),   # several pieces per lane, as above
     ("d96m32_bf16_ragged", _w(533, 2, 2, 1333, 96, 32, "bf16")),
+    # fp32 at D <= 64 on split operands: a ragged multi-segment case and one token
+    ("d48m48_f32_ragged", _w(534, 2, 2, 3001, 48, 48, "f32")),
+    ("d48m16_f32_one_token", _w(535, 1, 3, 1, 48, 16, "f32")),
 ]
 
 
