@@ -75,8 +75,8 @@ template <typename T, int F> constexpr int coop_np() { return (coop_pieces<T>(F)
 // CoopFrag<T>: the operand fragment of staged rows (bf16x4, or split4 for fp32).
 template <typename T> using CoopFrag = typename std::conditional<sizeof(T) == 4, split4, bf16x4>::type;
 // NPW: the most pieces one lane moves, coop_np<T, F>() when one wavefront
-// does all; the host may pass fewer when the segment's ng wavefronts cover the
-// pieces with that many each (64 ng NPW >= the piece count), which saves
+// does all; the host passes fewer when the workgroup's w wavefronts cover the
+// pieces with that many each (64 w NPW >= the piece count), which saves
 // registers.
 template <int F, int NPW> struct CoopRows {
     static constexpr int NP = NPW;
