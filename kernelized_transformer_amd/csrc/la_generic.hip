@@ -862,7 +862,10 @@ __global__ __launch_bounds__(512) void k_gbwd_dkdv(const T *__restrict__ q, cons
                 if (cg == 0) mma1(Rr[dt][1], qt, GT[0][1]);
             }
         }
-        lds_barrier();   // every group has read `part` before the next chunk writes it
+        // every group has read `part` before the next chunk writes it: with
+        // shared staging (bf16) the next chunk's staging barrier, which comes
+        // before those writes, already ensures it
+        if constexpr (!SHARED) lds_barrier();
     }
     }
 }
