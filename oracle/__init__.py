@@ -55,9 +55,11 @@ def _bind(lib):
     lib.orc_forward_causal_poly2.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_forward_noncausal_poly2.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_forward_poly2_rows.argtypes = [d, d, d, ctypes.POINTER(i64), d, i64, i64, i64, i64, i64, i64, i64]
+    lib.orc_backward_causal_poly2.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
     for f in ("orc_feature_map", "orc_forward_causal", "orc_forward_noncausal",
               "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step", "orc_rff_features",
-              "orc_forward_causal_features", "orc_forward_causal_poly2", "orc_forward_noncausal_poly2", "orc_forward_poly2_rows"):
+              "orc_forward_causal_features", "orc_forward_causal_poly2", "orc_forward_noncausal_poly2", "orc_forward_poly2_rows",
+              "orc_backward_causal_poly2"):
         getattr(lib, f).restype = None
     return lib
 
@@ -198,6 +200,19 @@ def forward_causal_poly2(q, k, v, lib=None):
     out = np.empty((B, H, N, M), np.float64)
     lib.orc_forward_causal_poly2(_p(q), _p(k), _p(v), _p(out), B, H, N, D, M)
     return out
+
+
+def backward_causal_poly2(q, k, v, dout, lib=None):
+    """Gradients (dQ, dK, dV) of sum(dout * forward_causal_poly2(q,k,v)) w.r.t.
+    q, k, v, summed pair by pair (O(N^2) per head)."""
+    lib = lib or load()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    assert k.shape == q.shape and v.shape == (B, H, N, M) and g.shape == v.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    lib.orc_backward_causal_poly2(_p(q), _p(k), _p(v), _p(g), _p(dq), _p(dk), _p(dv), B, H, N, D, M)
+    return dq, dk, dv
 
 
 def forward_noncausal_poly2(q, k, v, lib=None):

@@ -37,6 +37,10 @@
  *     numerator part ([summary] appendix A) and leave the rest to autograd;
  *     the formulas used here are derived in the comments of
  *     orc_backward_causal and pinned by finite differences in the tests.
+ *   - the gradient of the degree-2 polynomial form is written as its plain
+ *     pairwise definition (every pair j <= i, by the chain rule), not as a
+ *     recurrence: an independent form, pinned by finite differences of the
+ *     polynomial forward.
  */
 #include <math.h>
 #include <stdint.h>
@@ -506,6 +510,61 @@ void orc_forward_poly2_rows(const double *q, const double *k, const double *v, c
             }
             for (int64_t m = 0; m < M; ++m) o[m] /= den;
         }
+}
+
+/*
+ * Gradients of L = sum(dout * out) for the causal forward with the degree-2
+ * polynomial kernel ([summary] 3.2.1 for the kernel; 3.3.1: the gradient of
+ * the linear form).  Plain definition by the chain rule, O(N^2) per (b, h):
+ *   s_ij = (q_i . k_j)^2 (j <= i), d_i = sum_j s_ij, out_i = sum_j s_ij v_j / d_i;
+ *   dL/ds_ij = (dout_i . v_j - dout_i . out_i) / d_i = e_ij;
+ *   dq_i = sum_{j<=i} e_ij 2 (q_i . k_j) k_j,  dk_j = sum_{i>=j} e_ij 2 (q_i . k_j) q_i,
+ *   dv_j = sum_{i>=j} s_ij dout_i / d_i.
+ * q, k, dq, dk: [B][H][N][D]; v, dout, dv: [B][H][N][M].
+ */
+void orc_backward_causal_poly2(const double *q, const double *k, const double *v, const double *dout,
+                               double *dq, double *dk, double *dv,
+                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M, *G = dout + bh * N * M;
+        double *dQ = dq + bh * N * D, *dK = dk + bh * N * D, *dV = dv + bh * N * M;
+        for (int64_t x = 0; x < N * D; ++x) { dQ[x] = 0.0; dK[x] = 0.0; }
+        for (int64_t x = 0; x < N * M; ++x) dV[x] = 0.0;
+        double *o = (double *)malloc((size_t)M * sizeof(double));
+        for (int64_t i = 0; i < N; ++i) {
+            const double *qi = Q + i * D, *gi = G + i * M;
+            /* the forward row: d_i and out_i */
+            double den = 0.0;
+            for (int64_t m = 0; m < M; ++m) o[m] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dot = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += qi[a] * K[j * D + a];
+                den += dot * dot;
+                for (int64_t m = 0; m < M; ++m) o[m] += dot * dot * V[j * M + m];
+            }
+            for (int64_t m = 0; m < M; ++m) o[m] /= den;
+            double go = 0.0;
+            for (int64_t m = 0; m < M; ++m) go += gi[m] * o[m];
+            /* every pair (i, j <= i) */
+            for (int64_t j = 0; j <= i; ++j) {
+                const double *kj = K + j * D, *vj = V + j * M;
+                double dot = 0.0, gv = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += qi[a] * kj[a];
+                for (int64_t m = 0; m < M; ++m) gv += gi[m] * vj[m];
+                const double e = (gv - go) / den;
+                for (int64_t a = 0; a < D; ++a) {
+                    dQ[i * D + a] += e * 2.0 * dot * kj[a];
+                    dK[j * D + a] += e * 2.0 * dot * qi[a];
+                }
+                for (int64_t m = 0; m < M; ++m) dV[j * M + m] += dot * dot * gi[m] / den;
+            }
+        }
+        free(o);
+    }
 }
 
 /*

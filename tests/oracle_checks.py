@@ -366,7 +366,45 @@ def check_poly2(lib):
         assert _rel(oracle.forward_noncausal_poly2_rows(q, k, v, rows, lib=lib), ref_nc[:, :, rows]) < 1e-12
 
 
+def check_poly2_backward(lib):
+    """Gradients of the polynomial causal forward: central finite differences of
+    the (separately pinned) forward; N = 1 gives dV = dout, dQ = dK = 0; the
+    outputs do not change when one query row, or all key rows together, are
+    scaled (so dq_i . q_i = 0 for every i and sum_j dk_j . k_j = 0); adding a
+    constant to V shifts every output by it (so sum_j dv_j = sum_i dout_i)."""
+    for s, (B, H, N, D, M) in enumerate([(1, 1, 6, 3, 2), (1, 2, 5, 2, 3)]):
+        q, k = _rand(600 + 4 * s, B, H, N, D), _rand(601 + 4 * s, B, H, N, D)
+        v, g = _rand(602 + 4 * s, B, H, N, M), _rand(603 + 4 * s, B, H, N, M)
+        grads = oracle.backward_causal_poly2(q, k, v, g, lib=lib)
+
+        def loss(q_, k_, v_):
+            return float((oracle.forward_causal_poly2(q_, k_, v_, lib=lib) * g).sum())
+
+        eps = 1e-6
+        for which, grad in enumerate(grads):
+            base = [q, k, v]
+            num = np.zeros_like(base[which])
+            it = np.nditer(num, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                p_ = [x.copy() for x in base]
+                m_ = [x.copy() for x in base]
+                p_[which][idx] += eps
+                m_[which][idx] -= eps
+                num[idx] = (loss(*p_) - loss(*m_)) / (2 * eps)
+            assert np.allclose(grad, num, rtol=1e-6, atol=1e-8), (s, which, np.abs(grad - num).max())
+    q, k, v, g = _rand(620, 2, 3, 1, 4), _rand(621, 2, 3, 1, 4), _rand(622, 2, 3, 1, 5), _rand(623, 2, 3, 1, 5)
+    dq, dk, dv = oracle.backward_causal_poly2(q, k, v, g, lib=lib)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12 and _rel(dv, g) < 1e-15
+    q, k, v, g = _rand(630, 1, 2, 33, 8), _rand(631, 1, 2, 33, 8), _rand(632, 1, 2, 33, 6), _rand(633, 1, 2, 33, 6)
+    dq, dk, dv = oracle.backward_causal_poly2(q, k, v, g, lib=lib)
+    scale = np.abs(dq).max() * np.abs(q).max()
+    assert np.abs((dq * q).sum(-1)).max() < 1e-12 * scale * 8
+    assert np.abs((dk * k).sum((-1, -2))).max() < 1e-12 * np.abs(dk).max() * np.abs(k).max() * 33 * 8
+    assert _rel(dv.sum(-2), g.sum(-2)) < 1e-12
+
+
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,
               check_initial_state, check_decode, check_backward_vs_quadratic, check_backward_fd, check_backward_autograd,
               check_backward_identities, check_backward_noncausal, check_rff_worked_example,
-              check_rff_estimates_rbf_kernel, check_forward_features, check_poly2]
+              check_rff_estimates_rbf_kernel, check_forward_features, check_poly2, check_poly2_backward]

@@ -88,6 +88,22 @@ MUTATIONS = [
      "pq[a * D + b] = Q[i * D + a] * Q[i * D + b];",
      "pq[a * D + b] = Q[i * D + a] * K[i * D + b];",
      [oc.check_poly2]),
+    ("poly2_backward_drops_factor_two",
+     "dQ[i * D + a] += e * 2.0 * dot * kj[a];",
+     "dQ[i * D + a] += e * dot * kj[a];",
+     [oc.check_poly2_backward]),
+    ("poly2_backward_drops_output_term",
+     "const double e = (gv - go) / den;",
+     "const double e = (gv - 0.0 * go) / den;",
+     [oc.check_poly2_backward]),
+    ("poly2_backward_dv_unsquared",
+     "for (int64_t m = 0; m < M; ++m) dV[j * M + m] += dot * dot * gi[m] / den;",
+     "for (int64_t m = 0; m < M; ++m) dV[j * M + m] += dot * gi[m] / den;",
+     [oc.check_poly2_backward]),
+    ("poly2_backward_dk_uses_key",
+     "dK[j * D + a] += e * 2.0 * dot * qi[a];",
+     "dK[j * D + a] += e * 2.0 * dot * kj[a];",
+     [oc.check_poly2_backward]),
     ("decode_reads_before_update_of_s",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m];",
      "for (int64_t m = 0; m < M; ++m) SS[d * M + m] += kd * vv[m] * (m > 0);",
