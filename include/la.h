@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 9
+#define LA_ABI_VERSION 10
 
 /* The enums are int-sized in C; C++ gets the same fixed underlying type, so
  * any int a C caller passes (an unknown dtype, op or status included) is a
@@ -114,7 +114,8 @@ typedef enum la_op_e LA_ENUM_BASE {
     LA_OP_BWD_CAUSAL = 2,     /* la_backward_causal */
     LA_OP_BWD_NONCAUSAL = 3,  /* la_backward_noncausal */
     LA_OP_FWD_CAUSAL_POLY2 = 4,   /* la_forward_causal_poly2, la_forward_causal_poly2_state */
-    LA_OP_FWD_NONCAUSAL_POLY2 = 5 /* la_forward_noncausal_poly2 */
+    LA_OP_FWD_NONCAUSAL_POLY2 = 5, /* la_forward_noncausal_poly2 */
+    LA_OP_BWD_CAUSAL_POLY2 = 6     /* la_backward_causal_poly2 */
 } la_op_t;
 
 /*
@@ -249,6 +250,32 @@ la_status_t la_forward_noncausal_poly2(const void *q, const void *k, const void 
 la_status_t la_decode_step_poly2(const void *q, const void *k, const void *v, float *state,
                                  void *out, int64_t B, int64_t H, int64_t D, int64_t M,
                                  la_dtype_t dt, hipStream_t stream);
+
+/*
+ * Gradients of sum(dout * out) for out = la_forward_causal_poly2(q, k, v)
+ * ([summary] 3.2.1 for the kernel; 3.3.1: the gradient of the linear form in
+ * linear time, through running sums in both directions).  With
+ * s_ij = (q_i . k_j)^2 (j <= i), d_i = sum_j s_ij, g_i = dout_i / d_i,
+ * h_i = -(dout_i . out_i) / d_i, e_ij = g_i . v_j + h_i:
+ *   dq_i = 2 sum_{j<=i} e_ij (q_i . k_j) k_j,
+ *   dk_j = 2 sum_{i>=j} e_ij (q_i . k_j) q_i,
+ *   dv_j = sum_{i>=j} s_ij g_i,
+ * computed with the D x D sums sum_j [v_j, 1]_m k_j k_j^T (forwards) and
+ * sum_i [g_i, h_i]_m q_i q_i^T (backwards), one per column m.  out and d are
+ * recomputed (the polynomial forward runs first, into the workspace).
+ * q, k, dq, dk: [B][H][N][D]; v, dout, dv: [B][H][N][M]; dq, dk, dv are
+ * outputs, fully written.  D, M in {32, 64}; bf16 or fp32, fp32 sums.
+ * Workspace: la_workspace_size(LA_OP_BWD_CAUSAL_POLY2, ...) bytes (the
+ * forward's out and d, the weights [g, h], the segments' sums and one
+ * partial dq / dk per block of columns m).  Results do not vary from run to
+ * run.  A zero denominator (a query orthogonal to every earlier key) is not
+ * guarded.  Errors as la_backward_causal.
+ */
+la_status_t la_backward_causal_poly2(const void *q, const void *k, const void *v, const void *dout,
+                                     void *dq, void *dk, void *dv,
+                                     int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                     la_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /*
  * Random Fourier features ([summary] 5: approximating the RBF kernel with

@@ -21,6 +21,7 @@ Functions carry the C names:
   la_forward_noncausal(q, k, v, out=None, workspace=None)
   la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
+  la_backward_causal_poly2(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
   la_decode_step(q, k, v, S, Z, out=None)
   la_workspace_size(op, B, H, N, D, M, dtype)
   la_workspace_check(workspace, clear=False)
@@ -43,16 +44,18 @@ import torch
 __all__ = ["la_forward_causal", "la_forward_causal_noalloc", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
            "la_forward_causal_poly2", "la_forward_causal_poly2_state", "la_forward_noncausal_poly2",
            "la_decode_step_poly2", "la_poly2_state_floats",
-           "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal",
+           "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_backward_causal_poly2",
            "la_decode_step",
            "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
            "LAError", "lib_path", "load", "LA_ERR_TIMEOUT",
            "LA_OP_FWD_CAUSAL", "LA_OP_FWD_NONCAUSAL", "LA_OP_BWD_CAUSAL", "LA_OP_BWD_NONCAUSAL",
-           "LA_OP_FWD_CAUSAL_POLY2", "LA_OP_FWD_NONCAUSAL_POLY2", "LA_DTYPE_F32", "LA_DTYPE_BF16"]
+           "LA_OP_FWD_CAUSAL_POLY2", "LA_OP_FWD_NONCAUSAL_POLY2", "LA_OP_BWD_CAUSAL_POLY2", "LA_DTYPE_F32",
+           "LA_DTYPE_BF16"]
 
 LA_DTYPE_F32, LA_DTYPE_BF16 = 0, 1
 LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL, LA_OP_FWD_CAUSAL_POLY2 = 0, 1, 2, 3, 4
 LA_OP_FWD_NONCAUSAL_POLY2 = 5
+LA_OP_BWD_CAUSAL_POLY2 = 6
 _DT = {torch.float32: LA_DTYPE_F32, torch.bfloat16: LA_DTYPE_BF16}
 
 LA_ERR_TIMEOUT = 5
@@ -84,6 +87,7 @@ def load():
     lib.la_forward_noncausal.argtypes = fwd
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_backward_noncausal.argtypes = lib.la_backward_causal.argtypes
+    lib.la_backward_causal_poly2.argtypes = lib.la_backward_causal.argtypes
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, sz, vp]
@@ -98,7 +102,8 @@ def load():
     for f in ("la_forward_causal", "la_forward_causal_noalloc", "la_forward_causal_state", "la_forward_causal_features", "la_rff_features",
               "la_forward_causal_poly2", "la_forward_causal_poly2_state", "la_forward_noncausal_poly2",
               "la_decode_step_poly2",
-              "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step"):
+              "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_backward_causal_poly2",
+              "la_decode_step"):
         getattr(lib, f).restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32]
     lib.la_workspace_size.restype = sz
@@ -360,6 +365,11 @@ def la_backward_causal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None)
 def la_backward_noncausal(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None):
     """Gradients of sum(dout * la_forward_noncausal(q, k, v)); returns (dq, dk, dv)."""
     return _backward("la_backward_noncausal", LA_OP_BWD_NONCAUSAL, q, k, v, dout, dq, dk, dv, workspace)
+
+
+def la_backward_causal_poly2(q, k, v, dout, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of sum(dout * la_forward_causal_poly2(q, k, v)); returns (dq, dk, dv)."""
+    return _backward("la_backward_causal_poly2", LA_OP_BWD_CAUSAL_POLY2, q, k, v, dout, dq, dk, dv, workspace)
 
 
 def _backward(func, op, q, k, v, dout, dq, dk, dv, workspace):

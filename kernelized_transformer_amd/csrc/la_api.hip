@@ -3,6 +3,7 @@
 // diagnostics (error word, wait limit).
 #include "la.h"
 #include "la_internal.h"
+#include "la_poly_grad.h"
 
 namespace {
 
@@ -314,6 +315,27 @@ la_status_t la_backward_noncausal(const void *q, const void *k, const void *v, c
     return backward_common(false, q, k, v, dout, dq, dk, dv, B, H, N, D, M, dt, workspace, workspace_bytes, stream);
 }
 
+la_status_t la_backward_causal_poly2(const void *q, const void *k, const void *v, const void *dout, void *dq,
+                                     void *dk, void *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                     la_dtype_t dt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    la_status_t st = check_shape(B, H, N, D, M, dt);
+    if (st != LA_OK) return st;
+    if (!la::poly_head_sizes(D, M)) return LA_ERR_UNSUPPORTED;
+    const size_t es = esize(dt);
+    const int64_t BH = B * H;
+    const Span in[4] = {span(q, size_t(BH * N * D) * es), span(k, size_t(BH * N * D) * es),
+                        span(v, size_t(BH * N * M) * es), span(dout, size_t(BH * N * M) * es)};
+    const Span o[3] = {span(dq, size_t(BH * N * D) * es), span(dk, size_t(BH * N * D) * es),
+                       span(dv, size_t(BH * N * M) * es)};
+    if ((st = check_buffers(in, 4, o, 3)) != LA_OK) return st;
+    const Span all[7] = {in[0], in[1], in[2], in[3], o[0], o[1], o[2]};
+    const size_t need = la::poly_backward_workspace_bytes(BH, N, D, M, es);
+    if ((st = check_workspace(workspace, workspace_bytes, need, all, 7)) != LA_OK) return st;
+    const hipError_t e = la::launch_poly_backward(dt == LA_DTYPE_F32 ? 0 : 1, q, k, v, dout, dq, dk, dv, BH, N, D, M,
+                                                  workspace, stream);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 la_status_t la_decode_step(const void *q, const void *k, const void *v, float *S, float *Z, void *out, int64_t B,
                            int64_t H, int64_t D, int64_t M, la_dtype_t dt, hipStream_t stream) {
     la_status_t st = check_shape(B, H, 1, D, M, dt, true);
@@ -345,6 +367,8 @@ size_t la_workspace_size(la_op_t op, int64_t B, int64_t H, int64_t N, int64_t D,
         return la::poly_head_sizes(D, M) ? la::poly_workspace_bytes(B * H, N, D, M, true) : 0;
     case LA_OP_FWD_NONCAUSAL_POLY2:
         return la::poly_head_sizes(D, M) ? la::poly_workspace_bytes(B * H, N, D, M, false) : 0;
+    case LA_OP_BWD_CAUSAL_POLY2:
+        return la::poly_head_sizes(D, M) ? la::poly_backward_workspace_bytes(B * H, N, D, M, esize(dt)) : 0;
     }
     return 0;
 }

@@ -1,0 +1,409 @@
+// la_poly_grad.hip -- gradient of the causal forward with the degree-2
+// polynomial kernel on gfx950.
+//
+// [summary] 3.2.1 (sim(q, k) = (q . k)^2 has an exact finite feature map)
+// and 3.3.1 (the gradient of the linear form takes linear time and constant
+// memory, with running sums in both directions).  With s_ij = (q_i . k_j)^2
+// for j <= i, d_i = sum_j s_ij and out_i = sum_j s_ij v_j / d_i, the chain
+// rule gives dL/ds_ij = e_ij = w_i . u_j with
+//   w_i = [g_i, h_i],  g_i = dout_i / d_i,  h_i = -(dout_i . out_i) / d_i,
+//   u_j = [v_j, 1]    (M + 1 columns, the last one the normalizer),
+// and then
+//   dq_i = 2 sum_{j<=i} e_ij (q_i . k_j) k_j = 2 sum_m w_im A_i^(m) q_i,
+//          A_i^(m) = sum_{j<=i} u_jm k_j k_j^T                (D x D each);
+//   dk_j = 2 sum_{i>=j} e_ij (q_i . k_j) q_i = 2 sum_m u_jm B_j^(m) k_j,
+//          B_j^(m) = sum_{i>=j} w_im q_i q_i^T;
+//   dv_jm = sum_{i>=j} s_ij g_im = k_j^T B_j^(m) k_j          (m < M).
+// Both directions are one computation, run twice: a "query" row x_a reads
+// out against the running sum over the "key" rows y_b of the past (b <= a
+// forwards, b >= a backwards), C^(m) = sum_b u_bm y_b y_b^T, giving
+//   p_a = sum_m w_am C^(m) x_a (plus the chunk's own pairs)  and
+//   r_am = x_a^T C^(m) x_a (plus the chunk's own pairs).
+// Forwards: x = q, y = k, u = [v, 1], w = [g, h]: 2 p = dq.  Backwards:
+// x = k, y = q, u = [g, h], w = [v, 1]: 2 p = dk and r = dv.
+//
+// Precision.  The gradient is a sum of terms that cancel (sum_j s_ij e_ij
+// = 0 for every i), so each product is formed to about 2^-16 of its
+// operands whatever the I/O type: fp32 I/O on the fp32 matrix instruction,
+// bf16 I/O with every operand split into bf16 hi + lo parts (split4, two
+// bf16 instructions per tile); out enters h in fp32 (the forward stores an
+// fp32 copy for it).  Rounding the state operand and the output to bf16
+// instead gave dq errors of 1.5e-2 (per slice) to 2.1e-2 (per chunk) at
+// D = M = 32.
+//
+// Launches: the polynomial forward (out and d), the weights w, then per
+// direction the segments' sums of C, their exclusive scan (prefix or
+// suffix), the pass, and a sum over the column blocks.  The state is kept
+// as plain D x D fp32 matrices (one per column m) in accumulator tiles:
+// a workgroup of 11 wavefronts owns one segment and a block of 11 NMW
+// columns m (NMW = 3 at D = 32, 1 at D = 64, i.e. 48 or 64 state registers
+// per wavefront), so that M + 1 = 33 or 65 columns fill one to six blocks.
+// Per 16-row chunk each wavefront forms, for its columns, T = x C^(m)
+// (matrix cores, the state as the operand), its share of p (T scaled by
+// w_am) and of r, its share of the chunk's own pairs (scores x . y on the
+// matrix cores, masked to the past, weighted by its columns' u . w), and
+// the update C^(m) += y^T diag(u_m) y.  The wavefronts' partial p meet in
+// LDS (added in wavefront order); the column blocks' partial p go to the
+// workspace and are added in block order by the last launch, so results
+// do not vary from run to run.
+#include <type_traits>
+
+#include "la_chunk.h"
+#include "la_internal.h"
+#include "la_poly_grad.h"
+
+namespace la {
+
+namespace {
+
+constexpr int kPgWaves = 11;
+constexpr int kPgThreads = 64 * kPgWaves;
+
+template <int D> struct PgCfg {
+    static constexpr int DT = D / 16;                 // 16-row tiles of D
+    static constexpr int NMW = D == 32 ? 3 : 1;       // columns m per wavefront
+    static constexpr int MBK = kPgWaves * NMW;        // columns m per workgroup
+    static constexpr int XS = D + 4;                  // floats per staged row
+    static constexpr int US = MBK + 1;                // floats per staged u, w row
+};
+
+__host__ __device__ constexpr int64_t pg_blocks(int64_t D, int64_t M) {
+    return (M + 1 + kPgWaves * (D == 32 ? 3 : 1) - 1) / (kPgWaves * (D == 32 ? 3 : 1));
+}
+
+template <typename T> __device__ __forceinline__ float ld1(const T *p) { return static_cast<float>(*p); }
+
+// Element (token t, column m) of u or w: from V ([v, 1]) or from the weights
+// buffer ([g, h]).
+template <typename T, bool FROM_V, int M>
+__device__ __forceinline__ float col_value(const T *V, const float *Wb, int64_t row, int m) {
+    if constexpr (FROM_V) return m < M ? ld1<T>(V + row * M + m) : 1.f;
+    else return Wb[row * (M + 1) + m];
+}
+
+// DIR 0: forwards (x = q, y = k, u = [v, 1], w = [g, h]); DIR 1: backwards
+// (x = k, y = q, u = [g, h], w = [v, 1]).  SEG: only sum the segment's
+// C^(m) from zero and store it (no x, no outputs).
+template <typename T, int D, int M, int DIR, bool SEG>
+__global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, const T *__restrict__ Y,
+                                                   const T *__restrict__ V, const float *__restrict__ Wb,
+                                                   float *__restrict__ recs, float *__restrict__ pbuf,
+                                                   T *__restrict__ dv, int64_t N, int64_t nseg,
+                                                   int64_t seg_tokens, int64_t BH) {
+    typedef PgCfg<D> C;
+    typedef typename std::conditional<sizeof(T) == 2, split4, f32x4>::type Fr;
+    constexpr int DT = C::DT, NMW = C::NMW, MBK = C::MBK, XS = C::XS, US = C::US;
+    constexpr int64_t REC = int64_t(M + 1) * D * D;
+    constexpr int NMB = int(pg_blocks(D, M));
+    constexpr bool U_FROM_V = DIR == 0, W_FROM_V = DIR == 1;
+
+    __shared__ __align__(16) float xs[SEG ? 4 : 16 * XS];
+    __shared__ __align__(16) float ys[16 * XS];
+    __shared__ float us[16 * US];
+    __shared__ float wsh[SEG ? 1 : 16 * US];
+    __shared__ f32x4 pred[SEG ? 1 : kPgWaves * DT * 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int mb = int(blockIdx.x % NMB);
+    const int64_t seg = (blockIdx.x / NMB) % nseg, bh = blockIdx.x / NMB / nseg;
+    const int64_t t_begin = seg * seg_tokens, t_end = imin64(N, t_begin + seg_tokens);
+    const int64_t nch = (t_end - t_begin + 15) / 16;
+    const T *Xh = X + bh * N * D;
+    const T *Yh = Y + bh * N * D;
+    const T *Vh = V + bh * N * M;
+    const float *Wh = Wb + bh * N * (M + 1);
+    float *rec = recs ? recs + (bh * nseg + seg) * REC : nullptr;
+
+    // this wavefront's columns: m = mb MBK + wave NMW + k, valid while m <= M
+    f32x4 A[NMW][DT][DT];
+#pragma unroll
+    for (int k = 0; k < NMW; ++k) {
+        const int m = mb * MBK + wave * NMW + k;
+#pragma unroll
+        for (int db = 0; db < DT; ++db)
+#pragma unroll
+            for (int eb = 0; eb < DT; ++eb)
+                A[k][db][eb] = (!SEG && rec && m <= M)
+                                   ? reinterpret_cast<const f32x4 *>(rec + int64_t(m) * D * D +
+                                                                     (db * DT + eb) * 256)[lane]
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int64_t cc = DIR == 0 ? ci : nch - 1 - ci;
+        const int64_t t0 = t_begin + 16 * cc;
+        __syncthreads();   // the previous chunk's LDS reads are done
+        for (int e = tid; e < 16 * D; e += kPgThreads) {
+            const int row = e / D, col = e % D;
+            const int64_t t = t0 + row;
+            ys[row * XS + col] = t < t_end ? ld1<T>(Yh + t * D + col) : 0.f;
+            if constexpr (!SEG) xs[row * XS + col] = t < t_end ? ld1<T>(Xh + t * D + col) : 0.f;
+        }
+        for (int e = tid; e < 16 * MBK; e += kPgThreads) {
+            const int row = e / MBK, j = e % MBK, m = mb * MBK + j;
+            const int64_t t = t0 + row;
+            const bool on = t < t_end && m <= M;
+            us[row * US + j] = on ? col_value<T, U_FROM_V, M>(Vh, Wh, t, m) : 0.f;
+            if constexpr (!SEG) wsh[row * US + j] = on ? col_value<T, W_FROM_V, M>(Vh, Wh, t, m) : 0.f;
+        }
+        __syncthreads();
+
+        // y as token-contiguous tiles: lane (c, g) element r = y[4g + r][16 db + c]
+        f32x4 ytf[DT];
+#pragma unroll
+        for (int db = 0; db < DT; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ytf[db][r] = ys[(4 * g + r) * XS + 16 * db + c];
+        Fr yt[DT];
+#pragma unroll
+        for (int db = 0; db < DT; ++db) yt[db] = frag_from<Fr>(ytf[db]);
+        float u[NMW][4];
+#pragma unroll
+        for (int k = 0; k < NMW; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u[k][r] = us[(4 * g + r) * US + wave * NMW + k];
+
+        if constexpr (!SEG) {
+            // x and y as row tiles: lane (c, g) element r = x[c][16 db + 4g + r]
+            f32x4 xf[DT];
+            Fr xn[DT], yn[DT];
+#pragma unroll
+            for (int db = 0; db < DT; ++db) {
+                xf[db] = *reinterpret_cast<const f32x4 *>(&xs[c * XS + 16 * db + 4 * g]);
+                xn[db] = frag_from<Fr>(xf[db]);
+                yn[db] = frag_from<Fr>(*reinterpret_cast<const f32x4 *>(&ys[c * XS + 16 * db + 4 * g]));
+            }
+            // scores: lane (c, g) element r = x_c . y_{4g + r}, kept where b = 4g + r
+            // lies in a's past (b <= a forwards, b >= a backwards)
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int db = 0; db < DT; db += 2) mma2(P, yn[db], yn[db + 1], xn[db], xn[db + 1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int b = 4 * g + r;
+                if (DIR == 0 ? b > c : b < c) P[r] = 0.f;
+            }
+            f32x4 pacc[DT];
+#pragma unroll
+            for (int eb = 0; eb < DT; ++eb) pacc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 E = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < NMW; ++k) {
+                const int m = mb * MBK + wave * NMW + k;
+                if (m > M) continue;   // uniform per wavefront
+                const float wa = wsh[c * US + wave * NMW + k];
+                float rv = 0.f;
+#pragma unroll
+                for (int eb = 0; eb < DT; ++eb) {
+                    // T[a = c][e = 16 eb + 4g + r] = sum_d x[c][d] C[d][e]
+                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int db = 0; db < DT; db += 2)
+                        mma2(t, frag_from<Fr>(A[k][db][eb]), frag_from<Fr>(A[k][db + 1][eb]), xn[db], xn[db + 1]);
+                    pacc[eb] += wa * t;
+                    if constexpr (DIR == 1) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rv += t[r] * xf[eb][r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) E[r] += u[k][r] * wa;
+                if constexpr (DIR == 1) {
+                    if (m < M) {
+                        // r_am: the state part (lanes of every g) and the chunk's own pairs
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rv += P[r] * P[r] * u[k][r];
+                        rv += __shfl_xor(rv, 16);
+                        rv += __shfl_xor(rv, 32);
+                        const int64_t t = t0 + c;
+                        if (g == 0 && t < t_end) dv[(bh * N + t) * M + m] = static_cast<T>(rv);
+                    }
+                }
+            }
+            // the chunk's own pairs: p_a += sum_b (u_b . w_a) (x_a . y_b) y_b
+            f32x4 Z;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Z[r] = E[r] * P[r];
+            const Fr zf = frag_from<Fr>(Z);
+#pragma unroll
+            for (int eb = 0; eb < DT; ++eb) mma1(pacc[eb], yt[eb], zf);
+
+            // partial p of the wavefronts, added in wavefront order
+#pragma unroll
+            for (int eb = 0; eb < DT; ++eb) pred[(wave * DT + eb) * 64 + lane] = pacc[eb];
+            __syncthreads();
+            for (int e = tid; e < DT * 64; e += kPgThreads) {
+                const int eb = e / 64, ln = e % 64, a = ln & 15, ga = ln >> 4;
+                f32x4 sum = pred[eb * 64 + ln];
+                for (int w2 = 1; w2 < kPgWaves; ++w2) sum += pred[(w2 * DT + eb) * 64 + ln];
+                const int64_t t = t0 + a;
+                if (t < t_end)
+                    *reinterpret_cast<f32x4 *>(pbuf + ((int64_t(mb) * BH + bh) * N + t) * D + 16 * eb + 4 * ga) = sum;
+            }
+        }
+
+        // C^(m) += y^T diag(u_m) y over the chunk
+#pragma unroll
+        for (int k = 0; k < NMW; ++k) {
+            const int m = mb * MBK + wave * NMW + k;
+            if (m > M) continue;
+#pragma unroll
+            for (int eb = 0; eb < DT; ++eb) {
+                f32x4 sy;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sy[r] = ytf[eb][r] * u[k][r];
+                const Fr sf = frag_from<Fr>(sy);
+#pragma unroll
+                for (int db = 0; db < DT; ++db) mma1(A[k][db][eb], yt[db], sf);
+            }
+        }
+    }
+
+    if constexpr (SEG) {
+#pragma unroll
+        for (int k = 0; k < NMW; ++k) {
+            const int m = mb * MBK + wave * NMW + k;
+            if (m > M) continue;
+#pragma unroll
+            for (int db = 0; db < DT; ++db)
+#pragma unroll
+                for (int eb = 0; eb < DT; ++eb)
+                    reinterpret_cast<f32x4 *>(rec + int64_t(m) * D * D + (db * DT + eb) * 256)[lane] = A[k][db][eb];
+        }
+    }
+}
+
+// w = [dout / d, -(dout . out) / d] per token (out in fp32).
+template <typename T, int M>
+__global__ __launch_bounds__(256) void k_pg_weights(const T *__restrict__ dout, const float *__restrict__ out,
+                                                    const float *__restrict__ den, float *__restrict__ Wb,
+                                                    int64_t rows) {
+    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= rows) return;
+    const float inv = 1.f / den[t];
+    float go = 0.f;
+    for (int m = 0; m < M; ++m) {
+        const float gm = static_cast<float>(dout[t * M + m]);
+        go += gm * out[t * M + m];
+        Wb[t * (M + 1) + m] = gm * inv;
+    }
+    Wb[t * (M + 1) + M] = -go * inv;
+}
+
+// grad = 2 * (sum over the column blocks of the partial p), block order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_pg_sum(const float *__restrict__ pbuf, T *__restrict__ grad, int64_t n4,
+                                                int nmb) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 s = reinterpret_cast<const f32x4 *>(pbuf)[i];
+    for (int b = 1; b < nmb; ++b) s += reinterpret_cast<const f32x4 *>(pbuf)[int64_t(b) * n4 + i];
+    store4<T>(grad + 4 * i, IO<T>::from_f32(2.f * s));
+}
+
+struct PgPlan {
+    int64_t nmb = 1, nseg = 1, seg_tokens = 16, rec = 0;
+    size_t out_off = 0, o32_off = 0, den_off = 0, w_off = 0, fwd_off = 0, rec_off = 0, p_off = 0, total = 0;
+};
+
+PgPlan make_pg_plan(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+    PgPlan p;
+    p.nmb = pg_blocks(D, M);
+    p.rec = (M + 1) * D * D;
+    const int64_t nch = ceil_div(N, kChunk);
+    int64_t nseg = ceil_div(int64_t(device_cus()), BH * p.nmb);
+    nseg = std::max<int64_t>(1, std::min<int64_t>({nseg, nch, kMaxSegPerHead}));
+    p.seg_tokens = ceil_div(nch, nseg) * kChunk;
+    p.nseg = ceil_div(N, p.seg_tokens);
+    size_t off = 256;
+    p.out_off = off;
+    off += align256(size_t(BH * N * M) * esize);
+    p.o32_off = off;
+    off += align256(size_t(BH * N * M) * 4);
+    p.den_off = off;
+    off += align256(size_t(BH * N) * 4);
+    p.w_off = off;
+    off += align256(size_t(BH * N * (M + 1)) * 4);
+    p.fwd_off = off;
+    off += align256(poly_workspace_bytes(BH, N, D, M, true));
+    p.rec_off = off;
+    off += p.nseg > 1 ? align256(size_t(BH * p.nseg * p.rec) * 4) : 0;
+    p.p_off = off;
+    off += align256(size_t(p.nmb * BH * N * D) * 4);
+    p.total = off;
+    return p;
+}
+
+template <typename T, int D, int M, int DIR>
+hipError_t pg_direction(const T *X, const T *Y, const T *V, const float *Wb, float *recs, float *pbuf, T *dv,
+                        T *grad, int64_t BH, int64_t N, const PgPlan &p, hipStream_t s) {
+    const dim3 grid(unsigned(BH * p.nseg * p.nmb)), block(kPgThreads);
+    hipError_t e;
+    if (p.nseg > 1) {
+        hipLaunchKernelGGL((k_pg<T, D, M, DIR, true>), grid, block, 0, s, X, Y, V, Wb, recs, (float *)nullptr,
+                           (T *)nullptr, N, p.nseg, p.seg_tokens, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_scan(recs, BH, p.nseg, p.rec, DIR == 0 ? 0 : 2, s)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_pg<T, D, M, DIR, false>), grid, block, 0, s, X, Y, V, Wb, p.nseg > 1 ? recs : nullptr,
+                       pbuf, dv, N, p.nseg, p.seg_tokens, BH);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n4 = BH * N * D / 4;
+    hipLaunchKernelGGL((k_pg_sum<T, D>), dim3(unsigned(ceil_div(n4, 256))), dim3(256), 0, s, (const float *)pbuf,
+                       grad, n4, int(p.nmb));
+    return hipGetLastError();
+}
+
+template <typename T, int D, int M>
+hipError_t run_pg(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                  void *dv, int64_t BH, int64_t N, void *ws, hipStream_t s) {
+    const PgPlan p = make_pg_plan(BH, N, D, M, sizeof(T));
+    char *base = static_cast<char *>(ws);
+    T *out = reinterpret_cast<T *>(base + p.out_off);
+    float *o32 = reinterpret_cast<float *>(base + p.o32_off);
+    float *den = reinterpret_cast<float *>(base + p.den_off);
+    float *Wb = reinterpret_cast<float *>(base + p.w_off);
+    float *fws = reinterpret_cast<float *>(base + p.fwd_off);
+    float *recs = reinterpret_cast<float *>(base + p.rec_off);
+    float *pbuf = reinterpret_cast<float *>(base + p.p_off);
+    hipError_t e = launch_poly_forward_den(true, dt, q, k, v, out, nullptr, den, o32, BH, N, D, M, fws, s);
+    if (e != hipSuccess) return e;
+    const int64_t rows = BH * N;
+    hipLaunchKernelGGL((k_pg_weights<T, M>), dim3(unsigned(ceil_div(rows, 256))), dim3(256), 0, s,
+                       (const T *)dout, (const float *)o32, (const float *)den, Wb, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const T *Q = static_cast<const T *>(q), *K = static_cast<const T *>(k), *Vv = static_cast<const T *>(v);
+    if ((e = pg_direction<T, D, M, 0>(Q, K, Vv, Wb, recs, pbuf, (T *)nullptr, static_cast<T *>(dq), BH, N, p, s)) !=
+        hipSuccess)
+        return e;
+    return pg_direction<T, D, M, 1>(K, Q, Vv, Wb, recs, pbuf, static_cast<T *>(dv), static_cast<T *>(dk), BH, N, p,
+                                    s);
+}
+
+template <typename T>
+hipError_t run_pg_t(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
+                    void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, void *ws, hipStream_t s) {
+    if (D == 32 && M == 32) return run_pg<T, 32, 32>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 32 && M == 64) return run_pg<T, 32, 64>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 32) return run_pg<T, 64, 32>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 64) return run_pg<T, 64, 64>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+size_t poly_backward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+    if (!poly_head_sizes(D, M)) return 0;
+    return make_pg_plan(BH, N, D, M, esize).total;
+}
+
+hipError_t launch_poly_backward(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq,
+                                void *dk, void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, void *ws,
+                                hipStream_t s) {
+    if (!poly_head_sizes(D, M)) return hipErrorInvalidValue;
+    if (dt == 0) return run_pg_t<float>(dt, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+    return run_pg_t<bf16>(dt, q, k, v, dout, dq, dk, dv, BH, N, D, M, ws, s);
+}
+
+} // namespace la

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
               "la_forward_causal_poly2", "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
               "la_workspace_size", "la_workspace_check", "la_set_wait_limit", "la_status_string", "la_abi_version",
               "la_forward_causal_noalloc", "la_forward_causal_poly2_state", "la_forward_noncausal_poly2",
-              "la_decode_step_poly2", "la_poly2_state_floats"):
+              "la_decode_step_poly2", "la_poly2_state_floats", "la_backward_causal_poly2"):
         assert f in fns
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert la.la_abi_version() == 9
+    assert la.la_abi_version() == 10
     names = [la.la_status_string(s) for s in range(6)]
     assert names == ["LA_OK", "LA_ERR_INVALID_ARGUMENT", "LA_ERR_UNSUPPORTED", "LA_ERR_WORKSPACE", "LA_ERR_HIP",
                      "LA_ERR_TIMEOUT"]
@@ -58,6 +58,10 @@ def test_workspace_size():
     c = f(la.LA_OP_FWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
     assert c > 0 and c % 256 == 0 and c >= 2 * (32 * 32 + 32) * 4
     assert f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32) > 2 * n
+    # polynomial gradient: out, d, the weights [g, h] and one partial dq / dk per column block, at least
+    pb = f(la.LA_OP_BWD_CAUSAL_POLY2, 1, 2, 256, 32, 32, torch.float32)
+    assert pb % 256 == 0 and pb >= 2 * 256 * (32 + 1 + 33 + 32) * 4
+    assert f(la.LA_OP_BWD_CAUSAL_POLY2, 1, 2, 256, 48, 32, torch.float32) == 0
     # non-causal backward: two record arrays, no per-token buffers
     nb = f(la.LA_OP_BWD_NONCAUSAL, 1, 2, 256, 32, 32, torch.float32)
     assert nb > 0 and nb % 256 == 0 and nb < f(la.LA_OP_BWD_CAUSAL, 1, 2, 256, 32, 32, torch.float32)
