@@ -417,6 +417,38 @@ def main():
         results["poly2_forward_d64"] = poly_case(64, 64, True, max(3, npl // 4))
         log(f"polynomial forward D=M=64: {results['poly2_forward_d64']['ms_per_call']:.4f} ms/call")
 
+        # its gradient at D = M = 32: the forward again (out, d), then two passes over D x D sums per
+        # column m, each with a readout and an update: 4 D^2 (M + 1) flops for the forward and
+        # 8 D^2 (M + 1) for the passes per token*head on the D^2 count
+        def poly_bwd_case(D, M, reps):
+            wp = wl.Workload(4, f"polynomial kernel gradient, B1 H8 N65536 D={D} M={M} bf16", 1, 8, w4.N, D, M,
+                             "bf16")
+            qp, kp, vp, gp = (to_dev(x, "bf16") for x in wl.forward_inputs(wp, with_dout=True))
+            dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+            wsp = torch.empty(la.la_workspace_size(la.LA_OP_BWD_CAUSAL_POLY2, wp.B, wp.H, wp.N, D, M,
+                                                   torch.bfloat16), dtype=torch.uint8, device=dev)
+
+            def call(i):
+                st = lib.la_backward_causal_poly2(qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), gp.data_ptr(),
+                                                  dqp.data_ptr(), dkp.data_ptr(), dvp.data_ptr(), wp.B, wp.H, wp.N,
+                                                  D, M, la.LA_DTYPE_BF16, wsp.data_ptr(), wsp.numel(), sptr)
+                if st != 0:
+                    raise la.LAError("backward_causal_poly2", st)
+
+            for i in range(2):
+                call(i)
+            t = time_events(call, reps)
+            th = wp.B * wp.H * wp.N
+            flops = th * 12 * D * D * (M + 1)
+            ms = t / reps * 1e3
+            del qp, kp, vp, gp, dqp, dkp, dvp, wsp
+            return dict(workload=wp.name, ms_per_call=ms, tok_heads_per_s=th * reps / t, algorithmic_flops=flops,
+                        mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                        note="flops: 12 D^2 (M + 1) per token*head (forward again, then the two passes)")
+
+        results["poly2_backward"] = poly_bwd_case(32, 32, max(3, npl // 4))
+        log(f"polynomial backward D=M=32: {results['poly2_backward']['ms_per_call']:.4f} ms/call")
+
     if a.only in ("all", "noncausal"):
         for i in range(2):
             fwd(i, causal=False)

@@ -24,10 +24,11 @@
 //
 // Precision.  The gradient is a sum of terms that cancel (sum_j s_ij e_ij
 // = 0 for every i), so each product is formed to about 2^-16 of its
-// operands whatever the I/O type: fp32 I/O on the fp32 matrix instruction,
-// bf16 I/O with every operand split into bf16 hi + lo parts (split4, two
-// bf16 instructions per tile); out enters h in fp32 (the forward stores an
-// fp32 copy for it).  Rounding the state operand and the output to bf16
+// operands whatever the I/O type: fp32 I/O on the fp32 matrix instruction;
+// bf16 I/O with the computed operands (the state, u y, the chunk's pair
+// weights) split into bf16 hi + lo parts and paired with the exact bf16 x or
+// y in one 32-deep instruction per tile ([hi, lo] . [x, x]); out enters h in
+// fp32 (the forward stores an fp32 copy for it).  Rounding the state operand and the output to bf16
 // instead gave dq errors of 1.5e-2 (per slice) to 2.1e-2 (per chunk) at
 // D = M = 32.
 //
@@ -73,6 +74,20 @@ __host__ __device__ constexpr int64_t pg_blocks(int64_t D, int64_t M) {
 
 template <typename T> __device__ __forceinline__ float ld1(const T *p) { return static_cast<float>(*p); }
 
+// acc += A B^T over one 16-wide tile with one operand split into bf16 hi + lo
+// parts and the other exact in bf16: [hi, lo] . [b, b] = (hi + lo) b in one
+// 32-deep instruction.  fp32 operands: the fp32 instruction.
+__device__ __forceinline__ void mma_sx(f32x4 &acc, split4 a, bf16x4 b) {
+    const bf16x8 bb = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hl, bb, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_xs(f32x4 &acc, bf16x4 a, split4 b) {
+    const bf16x8 aa = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, b.hl, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_sx(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
+__device__ __forceinline__ void mma_xs(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
+
 // Element (token t, column m) of u or w: from V ([v, 1]) or from the weights
 // buffer ([g, h]).
 template <typename T, bool FROM_V, int M>
@@ -91,7 +106,10 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                                                    T *__restrict__ dv, int64_t N, int64_t nseg,
                                                    int64_t seg_tokens, int64_t BH) {
     typedef PgCfg<D> C;
-    typedef typename std::conditional<sizeof(T) == 2, split4, f32x4>::type Fr;
+    // XF: operands exact in the I/O type (x, y); SF: computed ones (the
+    // state, u y, the chunk's pair weights), split into hi + lo for bf16
+    typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type XF;
+    typedef typename std::conditional<sizeof(T) == 2, split4, f32x4>::type SF;
     constexpr int DT = C::DT, NMW = C::NMW, MBK = C::MBK, XS = C::XS, US = C::US;
     constexpr int64_t REC = int64_t(M + 1) * D * D;
     constexpr int NMB = int(pg_blocks(D, M));
@@ -130,24 +148,63 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                                    : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int64_t ci = 0; ci < nch; ++ci) {
+    // Each thread moves at most NY elements of the chunk's x and y rows and NU
+    // of its u and w columns.  The rows of the next PF chunks are in flight in
+    // PF register slots while a chunk is worked on, so their latency is hidden
+    // behind PF chunks of work.
+    constexpr int NY = (16 * D + kPgThreads - 1) / kPgThreads, NU = (16 * MBK + kPgThreads - 1) / kPgThreads;
+    constexpr int PF = SEG ? 4 : 2;   // 2 or 4 (the passes hold more registers)
+    float ry[PF][NY], rx[PF][NY], ru[PF][NU], rw[PF][NU];
+    auto fetch = [&](int64_t ci, float(&fy)[NY], float(&fx)[NY], float(&fu)[NU], float(&fw)[NU]) {
+        const int64_t t0 = t_begin + 16 * (DIR == 0 ? ci : nch - 1 - ci);
+#pragma unroll
+        for (int i = 0; i < NY; ++i) {
+            const int e = tid + i * kPgThreads, row = e / D, col = e % D;
+            const int64_t t = t0 + row;
+            const bool on = ci < nch && e < 16 * D && t < t_end;
+            fy[i] = on ? ld1<T>(Yh + t * D + col) : 0.f;
+            if constexpr (!SEG) fx[i] = on ? ld1<T>(Xh + t * D + col) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int e = tid + i * kPgThreads, row = e / MBK, j = e % MBK, m = mb * MBK + j;
+            const int64_t t = t0 + row;
+            const bool on = ci < nch && e < 16 * MBK && t < t_end && m <= M;
+            fu[i] = on ? col_value<T, U_FROM_V, M>(Vh, Wh, t, m) : 0.f;
+            if constexpr (!SEG) fw[i] = on ? col_value<T, W_FROM_V, M>(Vh, Wh, t, m) : 0.f;
+        }
+    };
+    fetch(0, ry[0], rx[0], ru[0], rw[0]);
+    fetch(1, ry[1], rx[1], ru[1], rw[1]);
+    if constexpr (PF > 2) {
+        fetch(2, ry[2], rx[2], ru[2], rw[2]);
+        fetch(3, ry[3], rx[3], ru[3], rw[3]);
+    }
+    // chunks in groups of PF, chunk c0 + U staged from register slot U, which
+    // is then refilled with chunk c0 + U + PF (slots fixed at compile time)
+    auto step = [&](int64_t ci, auto uc) {
+        constexpr int U = decltype(uc)::value;
         const int64_t cc = DIR == 0 ? ci : nch - 1 - ci;
         const int64_t t0 = t_begin + 16 * cc;
         __syncthreads();   // the previous chunk's LDS reads are done
-        for (int e = tid; e < 16 * D; e += kPgThreads) {
-            const int row = e / D, col = e % D;
-            const int64_t t = t0 + row;
-            ys[row * XS + col] = t < t_end ? ld1<T>(Yh + t * D + col) : 0.f;
-            if constexpr (!SEG) xs[row * XS + col] = t < t_end ? ld1<T>(Xh + t * D + col) : 0.f;
+#pragma unroll
+        for (int i = 0; i < NY; ++i) {
+            const int e = tid + i * kPgThreads, row = e / D, col = e % D;
+            if (e < 16 * D) {
+                ys[row * XS + col] = ry[U][i];
+                if constexpr (!SEG) xs[row * XS + col] = rx[U][i];
+            }
         }
-        for (int e = tid; e < 16 * MBK; e += kPgThreads) {
-            const int row = e / MBK, j = e % MBK, m = mb * MBK + j;
-            const int64_t t = t0 + row;
-            const bool on = t < t_end && m <= M;
-            us[row * US + j] = on ? col_value<T, U_FROM_V, M>(Vh, Wh, t, m) : 0.f;
-            if constexpr (!SEG) wsh[row * US + j] = on ? col_value<T, W_FROM_V, M>(Vh, Wh, t, m) : 0.f;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int e = tid + i * kPgThreads, row = e / MBK, j = e % MBK;
+            if (e < 16 * MBK) {
+                us[row * US + j] = ru[U][i];
+                if constexpr (!SEG) wsh[row * US + j] = rw[U][i];
+            }
         }
         __syncthreads();
+        fetch(ci + PF, ry[U], rx[U], ru[U], rw[U]);
 
         // y as token-contiguous tiles: lane (c, g) element r = y[4g + r][16 db + c]
         f32x4 ytf[DT];
@@ -155,9 +212,9 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
         for (int db = 0; db < DT; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) ytf[db][r] = ys[(4 * g + r) * XS + 16 * db + c];
-        Fr yt[DT];
+        XF yt[DT];
 #pragma unroll
-        for (int db = 0; db < DT; ++db) yt[db] = frag_from<Fr>(ytf[db]);
+        for (int db = 0; db < DT; ++db) yt[db] = frag_from<XF>(ytf[db]);
         float u[NMW][4];
 #pragma unroll
         for (int k = 0; k < NMW; ++k)
@@ -167,12 +224,12 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
         if constexpr (!SEG) {
             // x and y as row tiles: lane (c, g) element r = x[c][16 db + 4g + r]
             f32x4 xf[DT];
-            Fr xn[DT], yn[DT];
+            XF xn[DT], yn[DT];
 #pragma unroll
             for (int db = 0; db < DT; ++db) {
                 xf[db] = *reinterpret_cast<const f32x4 *>(&xs[c * XS + 16 * db + 4 * g]);
-                xn[db] = frag_from<Fr>(xf[db]);
-                yn[db] = frag_from<Fr>(*reinterpret_cast<const f32x4 *>(&ys[c * XS + 16 * db + 4 * g]));
+                xn[db] = frag_from<XF>(xf[db]);
+                yn[db] = frag_from<XF>(*reinterpret_cast<const f32x4 *>(&ys[c * XS + 16 * db + 4 * g]));
             }
             // scores: lane (c, g) element r = x_c . y_{4g + r}, kept where b = 4g + r
             // lies in a's past (b <= a forwards, b >= a backwards)
@@ -199,8 +256,7 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                     // T[a = c][e = 16 eb + 4g + r] = sum_d x[c][d] C[d][e]
                     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int db = 0; db < DT; db += 2)
-                        mma2(t, frag_from<Fr>(A[k][db][eb]), frag_from<Fr>(A[k][db + 1][eb]), xn[db], xn[db + 1]);
+                    for (int db = 0; db < DT; ++db) mma_sx(t, frag_from<SF>(A[k][db][eb]), xn[db]);
                     pacc[eb] += wa * t;
                     if constexpr (DIR == 1) {
 #pragma unroll
@@ -225,9 +281,9 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
             f32x4 Z;
 #pragma unroll
             for (int r = 0; r < 4; ++r) Z[r] = E[r] * P[r];
-            const Fr zf = frag_from<Fr>(Z);
+            const SF zf = frag_from<SF>(Z);
 #pragma unroll
-            for (int eb = 0; eb < DT; ++eb) mma1(pacc[eb], yt[eb], zf);
+            for (int eb = 0; eb < DT; ++eb) mma_xs(pacc[eb], yt[eb], zf);
 
             // partial p of the wavefronts, added in wavefront order
 #pragma unroll
@@ -253,10 +309,18 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                 f32x4 sy;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sy[r] = ytf[eb][r] * u[k][r];
-                const Fr sf = frag_from<Fr>(sy);
+                const SF sf = frag_from<SF>(sy);
 #pragma unroll
-                for (int db = 0; db < DT; ++db) mma1(A[k][db][eb], yt[db], sf);
+                for (int db = 0; db < DT; ++db) mma_xs(A[k][db][eb], yt[db], sf);
             }
+        }
+    };
+    for (int64_t c0 = 0; c0 < nch; c0 += PF) {
+        step(c0, std::integral_constant<int, 0>());
+        if (c0 + 1 < nch) step(c0 + 1, std::integral_constant<int, 1>());
+        if constexpr (PF > 2) {
+            if (c0 + 2 < nch) step(c0 + 2, std::integral_constant<int, 2>());
+            if (c0 + 3 < nch) step(c0 + 3, std::integral_constant<int, 3>());
         }
     }
 
@@ -274,7 +338,8 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
     }
 }
 
-// w = [dout / d, -(dout . out) / d] per token (out in fp32).
+// w = [dout / d, -(dout . out) / d] per token (out in fp32), one thread per
+// token.
 template <typename T, int M>
 __global__ __launch_bounds__(256) void k_pg_weights(const T *__restrict__ dout, const float *__restrict__ out,
                                                     const float *__restrict__ den, float *__restrict__ Wb,
