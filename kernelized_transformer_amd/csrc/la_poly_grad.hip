@@ -23,14 +23,17 @@
 // x = k, y = q, u = [g, h], w = [v, 1]: 2 p = dk and r = dv.
 //
 // Precision.  The gradient is a sum of terms that cancel (sum_j s_ij e_ij
-// = 0 for every i), so each product is formed to about 2^-16 of its
-// operands whatever the I/O type: fp32 I/O on the fp32 matrix instruction;
-// bf16 I/O with the computed operands (the state, u y, the chunk's pair
-// weights) split into bf16 hi + lo parts and paired with the exact bf16 x or
-// y in one 32-deep instruction per tile ([hi, lo] . [x, x]); out enters h in
-// fp32 (the forward stores an fp32 copy for it).  Rounding the state operand and the output to bf16
-// instead gave dq errors of 1.5e-2 (per slice) to 2.1e-2 (per chunk) at
-// D = M = 32.
+// = 0 for every i).  fp32 I/O runs on the fp32 matrix instruction.  With
+// bf16 I/O, out enters h in fp32 (the forward stores an fp32 copy for it),
+// and the computed operands that multiply exact bf16 rows -- u y in the
+// update and the chunk's pair weights -- are split into bf16 hi + lo parts,
+// paired with the row in one 32-deep instruction per tile ([hi, lo] . [y,
+// y]); the state is rounded to bf16 for its products with x, as in the
+// forward's readout.  Measured on the bf16 parity cases: rounding out and the
+// pair weights to bf16 instead gave dq errors of 1.5e-2 (per slice) and
+// 2.1e-2 (per 16-row chunk) at D = M = 32, against 2.9e-3 and 3.4e-3 now;
+// splitting the state as well changed the worst chunk errors by nothing and
+// the per-slice ones by 10-15%, at 10% more time.
 //
 // Launches: the polynomial forward (out and d), the weights w, then per
 // direction the segments' sums of C, their exclusive scan (prefix or
@@ -74,18 +77,13 @@ __host__ __device__ constexpr int64_t pg_blocks(int64_t D, int64_t M) {
 
 template <typename T> __device__ __forceinline__ float ld1(const T *p) { return static_cast<float>(*p); }
 
-// acc += A B^T over one 16-wide tile with one operand split into bf16 hi + lo
-// parts and the other exact in bf16: [hi, lo] . [b, b] = (hi + lo) b in one
-// 32-deep instruction.  fp32 operands: the fp32 instruction.
-__device__ __forceinline__ void mma_sx(f32x4 &acc, split4 a, bf16x4 b) {
-    const bf16x8 bb = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hl, bb, acc, 0, 0, 0);
-}
+// acc += A B^T over one 16-wide tile, A exact in bf16 and B split into bf16
+// hi + lo parts: [a, a] . [hi, lo] = a (hi + lo) in one 32-deep instruction.
+// fp32 operands: the fp32 instruction.
 __device__ __forceinline__ void mma_xs(f32x4 &acc, bf16x4 a, split4 b) {
     const bf16x8 aa = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, b.hl, acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma_sx(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
 __device__ __forceinline__ void mma_xs(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
 
 // Element (token t, column m) of u or w: from V ([v, 1]) or from the weights
@@ -256,7 +254,8 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                     // T[a = c][e = 16 eb + 4g + r] = sum_d x[c][d] C[d][e]
                     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int db = 0; db < DT; ++db) mma_sx(t, frag_from<SF>(A[k][db][eb]), xn[db]);
+                    for (int db = 0; db < DT; db += 2)
+                        mma2(t, frag_from<XF>(A[k][db][eb]), frag_from<XF>(A[k][db + 1][eb]), xn[db], xn[db + 1]);
                     pacc[eb] += wa * t;
                     if constexpr (DIR == 1) {
 #pragma unroll
