@@ -24,16 +24,16 @@
 //
 // Precision.  The gradient is a sum of terms that cancel (sum_j s_ij e_ij
 // = 0 for every i).  fp32 I/O runs on the fp32 matrix instruction.  With
-// bf16 I/O, out enters h in fp32 (the forward stores an fp32 copy for it),
-// and the computed operands that multiply exact bf16 rows -- u y in the
-// update and the chunk's pair weights -- are split into bf16 hi + lo parts,
-// paired with the row in one 32-deep instruction per tile ([hi, lo] . [y,
-// y]); the state is rounded to bf16 for its products with x, as in the
-// forward's readout.  Measured on the bf16 parity cases: rounding out and the
-// pair weights to bf16 instead gave dq errors of 1.5e-2 (per slice) and
-// 2.1e-2 (per 16-row chunk) at D = M = 32, against 2.9e-3 and 3.4e-3 now;
-// splitting the state as well changed the worst chunk errors by nothing and
-// the per-slice ones by 10-15%, at 10% more time.
+// bf16 I/O, out enters h in fp32 (the forward stores an fp32 copy for it)
+// and the chunk's pair weights (u_b . w_a) (x_a . y_b) are split into bf16
+// hi + lo parts, paired with the exact bf16 rows y in one 32-deep
+// instruction per tile ([y, y] . [hi, lo]); the state and u y enter their
+// products rounded to bf16, as the forward's state does.  Measured on the
+// bf16 parity cases: rounding out and the pair weights to bf16 as well gave
+// dq errors of 1.5e-2 (per slice) and 2.1e-2 (per 16-row chunk) at D = M =
+// 32, against 3.2e-3 and 3.5e-3 now; splitting the state and u y too left
+// the worst chunk errors unchanged and lowered the per-slice ones by 10-20%,
+// at 8% and 10% more time.
 //
 // Launches: the polynomial forward (out and d), the weights w, then per
 // direction the segments' sums of C, their exclusive scan (prefix or
@@ -308,9 +308,9 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                 f32x4 sy;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sy[r] = ytf[eb][r] * u[k][r];
-                const SF sf = frag_from<SF>(sy);
+                const XF sf = frag_from<XF>(sy);
 #pragma unroll
-                for (int db = 0; db < DT; ++db) mma_xs(A[k][db][eb], yt[db], sf);
+                for (int db = 0; db < DT; ++db) mma1(A[k][db][eb], yt[db], sf);
             }
         }
     };
