@@ -89,7 +89,7 @@ __device__ __forceinline__ void mma_xs(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc,
 // Element (token t, column m) of u or w: from V ([v, 1]) or from the weights
 // buffer ([g, h]).
 template <typename T, bool FROM_V, int M>
-__device__ __forceinline__ float col_value(const T *V, const float *Wb, int64_t row, int m) {
+__device__ __forceinline__ float col_value(const T *V, const float *Wb, int row, int m) {
     if constexpr (FROM_V) return m < M ? ld1<T>(V + row * M + m) : 1.f;
     else return Wb[row * (M + 1) + m];
 }
@@ -153,23 +153,27 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
     constexpr int NY = (16 * D + kPgThreads - 1) / kPgThreads, NU = (16 * MBK + kPgThreads - 1) / kPgThreads;
     constexpr int PF = SEG ? 4 : 2;   // 2 or 4 (the passes hold more registers)
     float ry[PF][NY], rx[PF][NY], ru[PF][NU], rw[PF][NU];
+    // (row addresses: the chunk's base is uniform, each element a 32-bit offset from it)
     auto fetch = [&](int64_t ci, float(&fy)[NY], float(&fx)[NY], float(&fu)[NU], float(&fw)[NU]) {
         const int64_t t0 = t_begin + 16 * (DIR == 0 ? ci : nch - 1 - ci);
+        const bool live = ci < nch;
+        const int rem = live ? int(imin64(16, t_end - t0)) : 0;   // rows present
+        const T *yb = Yh + (live ? t0 : 0) * D, *xb = Xh + (live ? t0 : 0) * D;
+        const T *vb = Vh + (live ? t0 : 0) * M;
+        const float *wb = Wh + (live ? t0 : 0) * (M + 1);
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
-            const int e = tid + i * kPgThreads, row = e / D, col = e % D;
-            const int64_t t = t0 + row;
-            const bool on = ci < nch && e < 16 * D && t < t_end;
-            fy[i] = on ? ld1<T>(Yh + t * D + col) : 0.f;
-            if constexpr (!SEG) fx[i] = on ? ld1<T>(Xh + t * D + col) : 0.f;
+            const int e = tid + i * kPgThreads, row = e / D;
+            const bool on = e < 16 * D && row < rem;
+            fy[i] = on ? ld1<T>(yb + e) : 0.f;
+            if constexpr (!SEG) fx[i] = on ? ld1<T>(xb + e) : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             const int e = tid + i * kPgThreads, row = e / MBK, j = e % MBK, m = mb * MBK + j;
-            const int64_t t = t0 + row;
-            const bool on = ci < nch && e < 16 * MBK && t < t_end && m <= M;
-            fu[i] = on ? col_value<T, U_FROM_V, M>(Vh, Wh, t, m) : 0.f;
-            if constexpr (!SEG) fw[i] = on ? col_value<T, W_FROM_V, M>(Vh, Wh, t, m) : 0.f;
+            const bool on = e < 16 * MBK && row < rem && m <= M;
+            fu[i] = on ? col_value<T, U_FROM_V, M>(vb, wb, row, m) : 0.f;
+            if constexpr (!SEG) fw[i] = on ? col_value<T, W_FROM_V, M>(vb, wb, row, m) : 0.f;
         }
     };
     fetch(0, ry[0], rx[0], ru[0], rw[0]);
