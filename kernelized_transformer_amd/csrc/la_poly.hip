@@ -53,7 +53,6 @@
 
 #include "la_chunk.h"
 #include "la_internal.h"
-#include "la_poly_grad.h"
 
 namespace la {
 
@@ -699,12 +698,10 @@ __global__ __launch_bounds__((64 * PolyCfg<T, D, M>::NWAVE)) void k_poly_segment
 
 // CAUSAL false: the non-causal form, every token read out from the (b, h)
 // total in rec, with neither the intra-chunk part nor state updates.  fin:
-// where to store the state after the segment's last token (or null); den,
-// o32: where to store each token's denominator and its output in fp32 (or
-// null).
+// where to store the state after the segment's last token (or null).
 template <typename T, int D, int M, int WI, bool CAUSAL>
 __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, T *O, const float *rec, float *fin,
-                                            float *den, float *o32, int64_t t_begin, int64_t t_end, int mb,
+                                            int64_t t_begin, int64_t t_end, int mb,
                                             PolyShared<T, D, M, PolyCfg<T, D, M>::TT, true> &sm) {
     typedef PolyCfg<T, D, M> C;
     typedef PolyShared<T, D, M, C::TT, true> SM;
@@ -803,10 +800,8 @@ __device__ __forceinline__ void output_wave(const T *Q, const T *K, const T *V, 
             d += __shfl_xor(d, 16);
             d += __shfl_xor(d, 32);
             const int64_t t = t0 + 16 * tt + c;
-            const f32x4 res = num * __builtin_amdgcn_rcpf(d);
-            if (t < t_end) store4<T>(O + t * M + m0 + 16 * mt + 4 * g, IO<T>::from_f32(res));
-            if (o32 && t < t_end) *reinterpret_cast<f32x4 *>(o32 + t * M + m0 + 16 * mt + 4 * g) = res;
-            if (den && mb == 0 && mt == 0 && g == 0 && t < t_end) den[t] = d;
+            if (t < t_end)
+                store4<T>(O + t * M + m0 + 16 * mt + 4 * g, IO<T>::from_f32(num * __builtin_amdgcn_rcpf(d)));
         }
     }
     if (fin) w.store_state(fin, mb);
@@ -818,9 +813,7 @@ __global__ __launch_bounds__((64 * PolyCfg<T, D, M>::NWAVE)) void k_poly_output(
                                                                                const T *__restrict__ v,
                                                                                T *__restrict__ out,
                                                                                const float *__restrict__ ws,
-                                                                               float *__restrict__ fin,
-                                                                               float *__restrict__ den,
-                                                                               float *__restrict__ o32, int64_t N,
+                                                                               float *__restrict__ fin, int64_t N,
                                                                                int64_t nseg, int64_t seg_tokens) {
     typedef PolyCfg<T, D, M> C;
     __shared__ PolyShared<T, D, M, C::TT, true> sm;
@@ -841,8 +834,7 @@ __global__ __launch_bounds__((64 * PolyCfg<T, D, M>::NWAVE)) void k_poly_output(
         return;
     }
     poly_dispatch<C::W>(wave, [&](auto wi) {
-        output_wave<T, D, M, decltype(wi)::value, CAUSAL>(Q, K, V, O, rec, f, den ? den + bh * N : nullptr,
-                                                          o32 ? o32 + bh * N * M : nullptr, t_begin, t_end, mb, sm);
+        output_wave<T, D, M, decltype(wi)::value, CAUSAL>(Q, K, V, O, rec, f, t_begin, t_end, mb, sm);
     });
 }
 
@@ -873,7 +865,7 @@ inline PolyPlan make_poly_plan(int64_t BH, int64_t N, int64_t D, int64_t M, int 
 
 template <typename T, int D, int M>
 static hipError_t run_poly(bool causal, const void *q, const void *k, const void *v, void *out, float *fin,
-                           float *den, float *o32, int64_t BH, int64_t N, float *ws, hipStream_t s) {
+                           int64_t BH, int64_t N, float *ws, hipStream_t s) {
     typedef PolyCfg<T, D, M> C;
     const PolyPlan p = make_poly_plan(BH, N, D, M, device_cus(), causal);
     if (p.seg_tokens % C::CH != 0 || p.seg_tokens % (16 * C::TT1) != 0) return hipErrorInvalidValue;
@@ -887,12 +879,11 @@ static hipError_t run_poly(bool causal, const void *q, const void *k, const void
     }
     if (causal)
         hipLaunchKernelGGL((k_poly_output<T, D, M, true>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, p.nseg > 1 ? (const float *)ws : nullptr, fin, den, o32, N,
-                           p.nseg, p.seg_tokens);
+                           (const T *)v, (T *)out, p.nseg > 1 ? (const float *)ws : nullptr, fin, N, p.nseg,
+                           p.seg_tokens);
     else
         hipLaunchKernelGGL((k_poly_output<T, D, M, false>), grid, block, 0, s, (const T *)q, (const T *)k,
-                           (const T *)v, (T *)out, (const float *)ws, (float *)nullptr, den, o32, N, p.nseg,
-                           p.seg_tokens);
+                           (const T *)v, (T *)out, (const float *)ws, (float *)nullptr, N, p.nseg, p.seg_tokens);
     return hipGetLastError();
 }
 
@@ -1010,9 +1001,9 @@ __global__ __launch_bounds__(64 * kPolyDecodeWaves) void k_poly_decode(const T *
 
 template <typename T, int D>
 static hipError_t run_poly_m(bool causal, const void *q, const void *k, const void *v, void *out, float *fin,
-                             float *den, float *o32, int64_t BH, int64_t N, int64_t M, float *ws, hipStream_t s) {
-    if (M == 32) return run_poly<T, D, 32>(causal, q, k, v, out, fin, den, o32, BH, N, ws, s);
-    if (M == 64) return run_poly<T, D, 64>(causal, q, k, v, out, fin, den, o32, BH, N, ws, s);
+                             int64_t BH, int64_t N, int64_t M, float *ws, hipStream_t s) {
+    if (M == 32) return run_poly<T, D, 32>(causal, q, k, v, out, fin, BH, N, ws, s);
+    if (M == 64) return run_poly<T, D, 64>(causal, q, k, v, out, fin, BH, N, ws, s);
     return hipErrorInvalidValue;
 }
 
@@ -1050,18 +1041,12 @@ size_t poly_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, bool ca
 hipError_t launch_poly_forward(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
                                float *state_final, int64_t BH, int64_t N, int64_t D, int64_t M, float *ws,
                                hipStream_t s) {
-    return launch_poly_forward_den(causal, dt, q, k, v, out, state_final, nullptr, nullptr, BH, N, D, M, ws, s);
-}
-
-hipError_t launch_poly_forward_den(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
-                                   float *state_final, float *den, float *o32, int64_t BH, int64_t N, int64_t D,
-                                   int64_t M, float *ws, hipStream_t s) {
     if (!poly_head_sizes(D, M)) return hipErrorInvalidValue;
     if (dt == 0)
-        return D == 32 ? run_poly_m<float, 32>(causal, q, k, v, out, state_final, den, o32, BH, N, M, ws, s)
-                       : run_poly_m<float, 64>(causal, q, k, v, out, state_final, den, o32, BH, N, M, ws, s);
-    return D == 32 ? run_poly_m<bf16, 32>(causal, q, k, v, out, state_final, den, o32, BH, N, M, ws, s)
-                   : run_poly_m<bf16, 64>(causal, q, k, v, out, state_final, den, o32, BH, N, M, ws, s);
+        return D == 32 ? run_poly_m<float, 32>(causal, q, k, v, out, state_final, BH, N, M, ws, s)
+                       : run_poly_m<float, 64>(causal, q, k, v, out, state_final, BH, N, M, ws, s);
+    return D == 32 ? run_poly_m<bf16, 32>(causal, q, k, v, out, state_final, BH, N, M, ws, s)
+                   : run_poly_m<bf16, 64>(causal, q, k, v, out, state_final, BH, N, M, ws, s);
 }
 
 hipError_t launch_poly_decode(int dt, const void *q, const void *k, const void *v, float *state, void *out,

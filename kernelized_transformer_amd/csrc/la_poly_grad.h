@@ -1,18 +1,10 @@
 // la_poly_grad.h -- host entry points of the gradient of the causal forward
-// with the degree-2 polynomial kernel (la_poly_grad.hip), and the forward
-// variant it starts from (la_poly.hip).
+// with the degree-2 polynomial kernel (la_poly_grad.hip).
 #pragma once
 
 #include "la_internal.h"
 
 namespace la {
-
-// The causal (or non-causal) polynomial forward of launch_poly_forward that
-// also stores each token's denominator sum_j (q_i . k_j)^2 (fp32, [BH][N])
-// into den and its output in fp32 ([BH][N][M]) into o32, each when not null.
-hipError_t launch_poly_forward_den(bool causal, int dt, const void *q, const void *k, const void *v, void *out,
-                                   float *state_final, float *den, float *o32, int64_t BH, int64_t N, int64_t D,
-                                   int64_t M, float *ws, hipStream_t s);
 
 // Workspace of launch_poly_backward (bytes); esize: bytes per element of
 // the inputs.

@@ -23,21 +23,21 @@
 // x = k, y = q, u = [g, h], w = [v, 1]: 2 p = dk and r = dv.
 //
 // Precision.  The gradient is a sum of terms that cancel (sum_j s_ij e_ij
-// = 0 for every i).  fp32 I/O runs on the fp32 matrix instruction.  With
-// bf16 I/O, out enters h in fp32 (the forward stores an fp32 copy for it)
-// and the chunk's pair weights (u_b . w_a) (x_a . y_b) are split into bf16
-// hi + lo parts, paired with the exact bf16 rows y in one 32-deep
-// instruction per tile ([y, y] . [hi, lo]); the state and u y enter their
-// products rounded to bf16, as the forward's state does.  Measured on the
-// bf16 parity cases: rounding out and the pair weights to bf16 as well gave
-// dq errors of 1.5e-2 (per slice) and 2.1e-2 (per 16-row chunk) at D = M =
-// 32, against 3.2e-3 and 3.5e-3 now; splitting the state and u y too left
-// the worst chunk errors unchanged and lowered the per-slice ones by 10-20%,
-// at 8% and 10% more time.
+// = 0 for every i, and at N = 65536 the cancelled sums are tens of times the
+// result), so out and d are not taken from the polynomial forward (its state
+// enters the readout rounded to bf16): the forwards direction first reads
+// them out of the same sums its dq pass then uses, which keeps the
+// cancellation exact to the sums' precision.  Taking them from the forward
+// gave dq errors of 13% at B1 H8 N65536 D = M = 32 bf16.  fp32 I/O runs on
+// the fp32 matrix instruction; bf16 I/O carries the computed operands (the
+// state, u y, the chunk's pair weights) as bf16 hi + lo parts, each paired
+// with an exact bf16 row in one 32-deep instruction per tile ([hi, lo] .
+// [x, x]).
 //
-// Launches: the polynomial forward (out and d), the weights w, then per
-// direction the segments' sums of C, their exclusive scan (prefix or
-// suffix), the pass, and a sum over the column blocks.  The state is kept
+// Launches, forwards: the segments' sums of C, their exclusive prefixes,
+// the readout (the forward's numerators and denominators), the weights w,
+// the dq pass and the sum over the column blocks; backwards: the segments'
+// sums, their exclusive suffixes, the dk / dv pass and the sum.  The state is kept
 // as plain D x D fp32 matrices (one per column m) in accumulator tiles:
 // a workgroup of 11 wavefronts owns one segment and a block of 11 NMW
 // columns m (NMW = 3 at D = 32, 1 at D = 64, i.e. 48 or 64 state registers
@@ -77,13 +77,19 @@ __host__ __device__ constexpr int64_t pg_blocks(int64_t D, int64_t M) {
 
 template <typename T> __device__ __forceinline__ float ld1(const T *p) { return static_cast<float>(*p); }
 
-// acc += A B^T over one 16-wide tile, A exact in bf16 and B split into bf16
-// hi + lo parts: [a, a] . [hi, lo] = a (hi + lo) in one 32-deep instruction.
-// fp32 operands: the fp32 instruction.
+// acc += A B^T over one 16-wide tile with one operand split into bf16 hi + lo
+// parts and the other exact in bf16: [hi, lo] . [b, b] = (hi + lo) b in one
+// 32-deep instruction (mma_sx: A split; mma_xs: B split).  fp32 operands: the
+// fp32 instruction.
+__device__ __forceinline__ void mma_sx(f32x4 &acc, split4 a, bf16x4 b) {
+    const bf16x8 bb = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hl, bb, acc, 0, 0, 0);
+}
 __device__ __forceinline__ void mma_xs(f32x4 &acc, bf16x4 a, split4 b) {
     const bf16x8 aa = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, b.hl, acc, 0, 0, 0);
 }
+__device__ __forceinline__ void mma_sx(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
 __device__ __forceinline__ void mma_xs(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
 
 // Element (token t, column m) of u or w: from V ([v, 1]) or from the weights
@@ -97,12 +103,16 @@ __device__ __forceinline__ float col_value(const T *V, const float *Wb, int row,
 // DIR 0: forwards (x = q, y = k, u = [v, 1], w = [g, h]); DIR 1: backwards
 // (x = k, y = q, u = [g, h], w = [v, 1]).  SEG: only sum the segment's
 // C^(m) from zero and store it (no x, no outputs).
-template <typename T, int D, int M, int DIR, bool SEG>
+// RMODE (passes): 0 p only; 1 p and r for m < M into dv (backwards); 2 r for
+// every m <= M into rb (fp32, [BH][N][M + 1]) and no p: the readout of the
+// forward itself, numerators and denominator, from the same sums the dq pass
+// uses.
+template <typename T, int D, int M, int DIR, bool SEG, int RMODE = 0>
 __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, const T *__restrict__ Y,
                                                    const T *__restrict__ V, const float *__restrict__ Wb,
                                                    float *__restrict__ recs, float *__restrict__ pbuf,
-                                                   T *__restrict__ dv, int64_t N, int64_t nseg,
-                                                   int64_t seg_tokens, int64_t BH) {
+                                                   T *__restrict__ dv, float *__restrict__ rb, int64_t N,
+                                                   int64_t nseg, int64_t seg_tokens, int64_t BH) {
     typedef PgCfg<D> C;
     // XF: operands exact in the I/O type (x, y); SF: computed ones (the
     // state, u y, the chunk's pair weights), split into hi + lo for bf16
@@ -112,12 +122,13 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
     constexpr int64_t REC = int64_t(M + 1) * D * D;
     constexpr int NMB = int(pg_blocks(D, M));
     constexpr bool U_FROM_V = DIR == 0, W_FROM_V = DIR == 1;
+    constexpr bool P_OUT = !SEG && RMODE != 2;   // p formed (and w staged)
 
     __shared__ __align__(16) float xs[SEG ? 4 : 16 * XS];
     __shared__ __align__(16) float ys[16 * XS];
     __shared__ float us[16 * US];
-    __shared__ float wsh[SEG ? 1 : 16 * US];
-    __shared__ f32x4 pred[SEG ? 1 : kPgWaves * DT * 64];
+    __shared__ float wsh[P_OUT ? 16 * US : 1];
+    __shared__ f32x4 pred[P_OUT ? kPgWaves * DT * 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
             const int e = tid + i * kPgThreads, row = e / MBK, j = e % MBK, m = mb * MBK + j;
             const bool on = e < 16 * MBK && row < rem && m <= M;
             fu[i] = on ? col_value<T, U_FROM_V, M>(vb, wb, row, m) : 0.f;
-            if constexpr (!SEG) fw[i] = on ? col_value<T, W_FROM_V, M>(vb, wb, row, m) : 0.f;
+            if constexpr (P_OUT) fw[i] = on ? col_value<T, W_FROM_V, M>(vb, wb, row, m) : 0.f;
         }
     };
     fetch(0, ry[0], rx[0], ru[0], rw[0]);
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
             const int e = tid + i * kPgThreads, row = e / MBK, j = e % MBK;
             if (e < 16 * MBK) {
                 us[row * US + j] = ru[U][i];
-                if constexpr (!SEG) wsh[row * US + j] = rw[U][i];
+                if constexpr (P_OUT) wsh[row * US + j] = rw[U][i];
             }
         }
         __syncthreads();
@@ -251,35 +262,38 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
             for (int k = 0; k < NMW; ++k) {
                 const int m = mb * MBK + wave * NMW + k;
                 if (m > M) continue;   // uniform per wavefront
-                const float wa = wsh[c * US + wave * NMW + k];
+                const float wa = P_OUT ? wsh[c * US + wave * NMW + k] : 0.f;
                 float rv = 0.f;
 #pragma unroll
                 for (int eb = 0; eb < DT; ++eb) {
                     // T[a = c][e = 16 eb + 4g + r] = sum_d x[c][d] C[d][e]
                     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int db = 0; db < DT; db += 2)
-                        mma2(t, frag_from<XF>(A[k][db][eb]), frag_from<XF>(A[k][db + 1][eb]), xn[db], xn[db + 1]);
-                    pacc[eb] += wa * t;
-                    if constexpr (DIR == 1) {
+                    for (int db = 0; db < DT; ++db) mma_sx(t, frag_from<SF>(A[k][db][eb]), xn[db]);
+                    if constexpr (P_OUT) pacc[eb] += wa * t;
+                    if constexpr (RMODE != 0) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) rv += t[r] * xf[eb][r];
                     }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) E[r] += u[k][r] * wa;
-                if constexpr (DIR == 1) {
-                    if (m < M) {
+                if constexpr (RMODE != 0) {
+                    if (RMODE == 2 || m < M) {
                         // r_am: the state part (lanes of every g) and the chunk's own pairs
 #pragma unroll
                         for (int r = 0; r < 4; ++r) rv += P[r] * P[r] * u[k][r];
                         rv += __shfl_xor(rv, 16);
                         rv += __shfl_xor(rv, 32);
                         const int64_t t = t0 + c;
-                        if (g == 0 && t < t_end) dv[(bh * N + t) * M + m] = static_cast<T>(rv);
+                        if (g == 0 && t < t_end) {
+                            if constexpr (RMODE == 1) dv[(bh * N + t) * M + m] = static_cast<T>(rv);
+                            else rb[(bh * N + t) * (M + 1) + m] = rv;
+                        }
                     }
                 }
             }
+            if constexpr (P_OUT) {
             // the chunk's own pairs: p_a += sum_b (u_b . w_a) (x_a . y_b) y_b
             f32x4 Z;
 #pragma unroll
@@ -300,6 +314,7 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                 if (t < t_end)
                     *reinterpret_cast<f32x4 *>(pbuf + ((int64_t(mb) * BH + bh) * N + t) * D + 16 * eb + 4 * ga) = sum;
             }
+            }   // P_OUT
         }
 
         // C^(m) += y^T diag(u_m) y over the chunk
@@ -312,9 +327,9 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                 f32x4 sy;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sy[r] = ytf[eb][r] * u[k][r];
-                const XF sf = frag_from<XF>(sy);
+                const SF sf = frag_from<SF>(sy);
 #pragma unroll
-                for (int db = 0; db < DT; ++db) mma1(A[k][db][eb], yt[db], sf);
+                for (int db = 0; db < DT; ++db) mma_xs(A[k][db][eb], yt[db], sf);
             }
         }
     };
@@ -341,22 +356,23 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
     }
 }
 
-// w = [dout / d, -(dout . out) / d] per token (out in fp32), one thread per
-// token.
+// w = [dout / d, -(dout . out) / d] per token from the readout r = [n, d]
+// (out = n / d), in place: row t of rw holds r on entry and w on exit.  One
+// thread per token.
 template <typename T, int M>
-__global__ __launch_bounds__(256) void k_pg_weights(const T *__restrict__ dout, const float *__restrict__ out,
-                                                    const float *__restrict__ den, float *__restrict__ Wb,
+__global__ __launch_bounds__(256) void k_pg_weights(const T *__restrict__ dout, float *__restrict__ rw,
                                                     int64_t rows) {
     const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (t >= rows) return;
-    const float inv = 1.f / den[t];
+    float *row = rw + t * (M + 1);
+    const float inv = 1.f / row[M];
     float go = 0.f;
     for (int m = 0; m < M; ++m) {
         const float gm = static_cast<float>(dout[t * M + m]);
-        go += gm * out[t * M + m];
-        Wb[t * (M + 1) + m] = gm * inv;
+        go += gm * (row[m] * inv);
+        row[m] = gm * inv;
     }
-    Wb[t * (M + 1) + M] = -go * inv;
+    row[M] = -go * inv;
 }
 
 // grad = 2 * (sum over the column blocks of the partial p), block order.
@@ -372,10 +388,10 @@ __global__ __launch_bounds__(256) void k_pg_sum(const float *__restrict__ pbuf, 
 
 struct PgPlan {
     int64_t nmb = 1, nseg = 1, seg_tokens = 16, rec = 0;
-    size_t out_off = 0, o32_off = 0, den_off = 0, w_off = 0, fwd_off = 0, rec_off = 0, p_off = 0, total = 0;
+    size_t w_off = 0, rec_off = 0, p_off = 0, total = 0;
 };
 
-PgPlan make_pg_plan(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
+PgPlan make_pg_plan(int64_t BH, int64_t N, int64_t D, int64_t M) {
     PgPlan p;
     p.nmb = pg_blocks(D, M);
     p.rec = (M + 1) * D * D;
@@ -385,16 +401,8 @@ PgPlan make_pg_plan(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
     p.seg_tokens = ceil_div(nch, nseg) * kChunk;
     p.nseg = ceil_div(N, p.seg_tokens);
     size_t off = 256;
-    p.out_off = off;
-    off += align256(size_t(BH * N * M) * esize);
-    p.o32_off = off;
-    off += align256(size_t(BH * N * M) * 4);
-    p.den_off = off;
-    off += align256(size_t(BH * N) * 4);
-    p.w_off = off;
+    p.w_off = off;   // the readout [n, d], then the weights [g, h], per token
     off += align256(size_t(BH * N * (M + 1)) * 4);
-    p.fwd_off = off;
-    off += align256(poly_workspace_bytes(BH, N, D, M, true));
     p.rec_off = off;
     off += p.nseg > 1 ? align256(size_t(BH * p.nseg * p.rec) * 4) : 0;
     p.p_off = off;
@@ -403,59 +411,61 @@ PgPlan make_pg_plan(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
     return p;
 }
 
-template <typename T, int D, int M, int DIR>
-hipError_t pg_direction(const T *X, const T *Y, const T *V, const float *Wb, float *recs, float *pbuf, T *dv,
-                        T *grad, int64_t BH, int64_t N, const PgPlan &p, hipStream_t s) {
-    const dim3 grid(unsigned(BH * p.nseg * p.nmb)), block(kPgThreads);
-    hipError_t e;
-    if (p.nseg > 1) {
-        hipLaunchKernelGGL((k_pg<T, D, M, DIR, true>), grid, block, 0, s, X, Y, V, Wb, recs, (float *)nullptr,
-                           (T *)nullptr, N, p.nseg, p.seg_tokens, BH);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_scan(recs, BH, p.nseg, p.rec, DIR == 0 ? 0 : 2, s)) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k_pg<T, D, M, DIR, false>), grid, block, 0, s, X, Y, V, Wb, p.nseg > 1 ? recs : nullptr,
-                       pbuf, dv, N, p.nseg, p.seg_tokens, BH);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t n4 = BH * N * D / 4;
-    hipLaunchKernelGGL((k_pg_sum<T, D>), dim3(unsigned(ceil_div(n4, 256))), dim3(256), 0, s, (const float *)pbuf,
-                       grad, n4, int(p.nmb));
-    return hipGetLastError();
-}
-
 template <typename T, int D, int M>
-hipError_t run_pg(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
-                  void *dv, int64_t BH, int64_t N, void *ws, hipStream_t s) {
-    const PgPlan p = make_pg_plan(BH, N, D, M, sizeof(T));
+hipError_t run_pg(const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk, void *dv,
+                  int64_t BH, int64_t N, void *ws, hipStream_t s) {
+    const PgPlan p = make_pg_plan(BH, N, D, M);
     char *base = static_cast<char *>(ws);
-    T *out = reinterpret_cast<T *>(base + p.out_off);
-    float *o32 = reinterpret_cast<float *>(base + p.o32_off);
-    float *den = reinterpret_cast<float *>(base + p.den_off);
     float *Wb = reinterpret_cast<float *>(base + p.w_off);
-    float *fws = reinterpret_cast<float *>(base + p.fwd_off);
-    float *recs = reinterpret_cast<float *>(base + p.rec_off);
+    float *recs = p.nseg > 1 ? reinterpret_cast<float *>(base + p.rec_off) : nullptr;
     float *pbuf = reinterpret_cast<float *>(base + p.p_off);
-    hipError_t e = launch_poly_forward_den(true, dt, q, k, v, out, nullptr, den, o32, BH, N, D, M, fws, s);
-    if (e != hipSuccess) return e;
-    const int64_t rows = BH * N;
-    hipLaunchKernelGGL((k_pg_weights<T, M>), dim3(unsigned(ceil_div(rows, 256))), dim3(256), 0, s,
-                       (const T *)dout, (const float *)o32, (const float *)den, Wb, rows);
+    const T *Q = static_cast<const T *>(q), *K = static_cast<const T *>(k), *V = static_cast<const T *>(v);
+    const dim3 grid(unsigned(BH * p.nseg * p.nmb)), block(kPgThreads);
+    const int64_t rows = BH * N, n4 = BH * N * D / 4;
+    const dim3 gsum(unsigned(ceil_div(n4, 256)));
+    hipError_t e;
+    // forwards: the segments' sums of [v, 1]_m k k^T and their prefixes, the
+    // readout (numerators and denominators), the weights, dq
+    if (p.nseg > 1) {
+        hipLaunchKernelGGL((k_pg<T, D, M, 0, true>), grid, block, 0, s, Q, K, V, (const float *)Wb, recs,
+                           (float *)nullptr, (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_scan(recs, BH, p.nseg, p.rec, 0, s)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 2>), grid, block, 0, s, Q, K, V, (const float *)Wb, recs,
+                       (float *)nullptr, (T *)nullptr, Wb, N, p.nseg, p.seg_tokens, BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const T *Q = static_cast<const T *>(q), *K = static_cast<const T *>(k), *Vv = static_cast<const T *>(v);
-    if ((e = pg_direction<T, D, M, 0>(Q, K, Vv, Wb, recs, pbuf, (T *)nullptr, static_cast<T *>(dq), BH, N, p, s)) !=
-        hipSuccess)
-        return e;
-    return pg_direction<T, D, M, 1>(K, Q, Vv, Wb, recs, pbuf, static_cast<T *>(dv), static_cast<T *>(dk), BH, N, p,
-                                    s);
+    hipLaunchKernelGGL((k_pg_weights<T, M>), dim3(unsigned(ceil_div(rows, 256))), dim3(256), 0, s,
+                       static_cast<const T *>(dout), Wb, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 0>), grid, block, 0, s, Q, K, V, (const float *)Wb, recs, pbuf,
+                       (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_pg_sum<T, D>), gsum, dim3(256), 0, s, (const float *)pbuf, static_cast<T *>(dq), n4,
+                       int(p.nmb));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // backwards: the segments' sums of [g, h]_m q q^T and their suffixes, dk and dv
+    if (p.nseg > 1) {
+        hipLaunchKernelGGL((k_pg<T, D, M, 1, true>), grid, block, 0, s, K, Q, V, (const float *)Wb, recs,
+                           (float *)nullptr, (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_scan(recs, BH, p.nseg, p.rec, 2, s)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_pg<T, D, M, 1, false, 1>), grid, block, 0, s, K, Q, V, (const float *)Wb, recs, pbuf,
+                       static_cast<T *>(dv), (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_pg_sum<T, D>), gsum, dim3(256), 0, s, (const float *)pbuf, static_cast<T *>(dk), n4,
+                       int(p.nmb));
+    return hipGetLastError();
 }
 
 template <typename T>
 hipError_t run_pg_t(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq, void *dk,
                     void *dv, int64_t BH, int64_t N, int64_t D, int64_t M, void *ws, hipStream_t s) {
-    if (D == 32 && M == 32) return run_pg<T, 32, 32>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
-    if (D == 32 && M == 64) return run_pg<T, 32, 64>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
-    if (D == 64 && M == 32) return run_pg<T, 64, 32>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
-    if (D == 64 && M == 64) return run_pg<T, 64, 64>(dt, q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 32 && M == 32) return run_pg<T, 32, 32>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 32 && M == 64) return run_pg<T, 32, 64>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 32) return run_pg<T, 64, 32>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
+    if (D == 64 && M == 64) return run_pg<T, 64, 64>(q, k, v, dout, dq, dk, dv, BH, N, ws, s);
     return hipErrorInvalidValue;
 }
 
@@ -463,7 +473,8 @@ hipError_t run_pg_t(int dt, const void *q, const void *k, const void *v, const v
 
 size_t poly_backward_workspace_bytes(int64_t BH, int64_t N, int64_t D, int64_t M, size_t esize) {
     if (!poly_head_sizes(D, M)) return 0;
-    return make_pg_plan(BH, N, D, M, esize).total;
+    (void)esize;
+    return make_pg_plan(BH, N, D, M).total;
 }
 
 hipError_t launch_poly_backward(int dt, const void *q, const void *k, const void *v, const void *dout, void *dq,

@@ -56,10 +56,12 @@ def _bind(lib):
     lib.orc_forward_noncausal_poly2.argtypes = [d, d, d, d, i64, i64, i64, i64, i64]
     lib.orc_forward_poly2_rows.argtypes = [d, d, d, ctypes.POINTER(i64), d, i64, i64, i64, i64, i64, i64, i64]
     lib.orc_backward_causal_poly2.argtypes = [d, d, d, d, d, d, d, i64, i64, i64, i64, i64]
+    lib.orc_backward_causal_poly2_rows.argtypes = [d, d, d, d, ctypes.POINTER(i64), i64, ctypes.POINTER(i64), i64,
+                                                   d, d, d, i64, i64, i64, i64, i64]
     for f in ("orc_feature_map", "orc_forward_causal", "orc_forward_noncausal",
               "orc_backward_causal", "orc_backward_noncausal", "orc_decode_step", "orc_rff_features",
               "orc_forward_causal_features", "orc_forward_causal_poly2", "orc_forward_noncausal_poly2", "orc_forward_poly2_rows",
-              "orc_backward_causal_poly2"):
+              "orc_backward_causal_poly2", "orc_backward_causal_poly2_rows"):
         getattr(lib, f).restype = None
     return lib
 
@@ -212,6 +214,26 @@ def backward_causal_poly2(q, k, v, dout, lib=None):
     assert k.shape == q.shape and v.shape == (B, H, N, M) and g.shape == v.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     lib.orc_backward_causal_poly2(_p(q), _p(k), _p(v), _p(g), _p(dq), _p(dk), _p(dv), B, H, N, D, M)
+    return dq, dk, dv
+
+
+def backward_causal_poly2_rows(q, k, v, dout, rows_q, rows_k, lib=None):
+    """Rows of backward_causal_poly2, each summed pair by pair: dq at rows_q,
+    dk and dv at rows_k (which should lie near the end: every later token's
+    out and d are formed first)."""
+    lib = lib or load()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    rq = np.ascontiguousarray(rows_q, np.int64)
+    rk = np.ascontiguousarray(rows_k, np.int64)
+    assert ((rq >= 0) & (rq < N)).all() and ((rk >= 0) & (rk < N)).all()
+    dq = np.empty((B, H, len(rq), D), np.float64)
+    dk = np.empty((B, H, len(rk), D), np.float64)
+    dv = np.empty((B, H, len(rk), M), np.float64)
+    P = ctypes.POINTER(ctypes.c_int64)
+    lib.orc_backward_causal_poly2_rows(_p(q), _p(k), _p(v), _p(g), rq.ctypes.data_as(P), len(rq),
+                                       rk.ctypes.data_as(P), len(rk), _p(dq), _p(dk), _p(dv), B, H, N, D, M)
     return dq, dk, dv
 
 

@@ -568,6 +568,88 @@ void orc_backward_causal_poly2(const double *q, const double *k, const double *v
 }
 
 /*
+ * Selected rows of orc_backward_causal_poly2, each summed pair by pair from
+ * the same definition: dq at the rows rq[0 .. nq) (O(i (D + M)) per row),
+ * dk and dv at the rows rk[0 .. nk) (every later token's out_i and d_i are
+ * formed first, once: O((N - min rk) N (D + M)), for rows near the end).
+ * dq: [B][H][nq][D]; dk: [B][H][nk][D]; dv: [B][H][nk][M].
+ */
+void orc_backward_causal_poly2_rows(const double *q, const double *k, const double *v, const double *dout,
+                                    const int64_t *rq, int64_t nq, const int64_t *rk, int64_t nk,
+                                    double *dq, double *dk, double *dv,
+                                    int64_t B, int64_t H, int64_t N, int64_t D, int64_t M)
+{
+    const int64_t BH = B * H;
+    int64_t jmin = N;
+    for (int64_t r = 0; r < nk; ++r) if (rk[r] < jmin) jmin = rk[r];
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double *Q = q + bh * N * D, *K = k + bh * N * D;
+        const double *V = v + bh * N * M, *G = dout + bh * N * M;
+        const int64_t nt = N - jmin;
+        /* out_i . dout_i and d_i of token i (jmin <= i < N) */
+        double *go = (double *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(double));
+        double *den = (double *)malloc((size_t)(nt > 0 ? nt : 1) * sizeof(double));
+        double *o = (double *)malloc((size_t)M * sizeof(double));
+        for (int64_t i = jmin; i < N; ++i) {
+            double dd = 0.0;
+            for (int64_t m = 0; m < M; ++m) o[m] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dot = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += Q[i * D + a] * K[j * D + a];
+                dd += dot * dot;
+                for (int64_t m = 0; m < M; ++m) o[m] += dot * dot * V[j * M + m];
+            }
+            double g = 0.0;
+            for (int64_t m = 0; m < M; ++m) g += G[i * M + m] * o[m] / dd;
+            go[i - jmin] = g;
+            den[i - jmin] = dd;
+        }
+        for (int64_t r = 0; r < nq; ++r) {
+            const int64_t i = rq[r];
+            const double *qi = Q + i * D, *gi = G + i * M;
+            double *out = dq + (bh * nq + r) * D;
+            double dd = 0.0, g = 0.0;
+            for (int64_t m = 0; m < M; ++m) o[m] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dot = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += qi[a] * K[j * D + a];
+                dd += dot * dot;
+                for (int64_t m = 0; m < M; ++m) o[m] += dot * dot * V[j * M + m];
+            }
+            for (int64_t m = 0; m < M; ++m) g += gi[m] * o[m] / dd;
+            for (int64_t a = 0; a < D; ++a) out[a] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                const double *kj = K + j * D, *vj = V + j * M;
+                double dot = 0.0, gv = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += qi[a] * kj[a];
+                for (int64_t m = 0; m < M; ++m) gv += gi[m] * vj[m];
+                const double e = (gv - g) / dd;
+                for (int64_t a = 0; a < D; ++a) out[a] += e * 2.0 * dot * kj[a];
+            }
+        }
+        for (int64_t r = 0; r < nk; ++r) {
+            const int64_t j = rk[r];
+            const double *kj = K + j * D, *vj = V + j * M;
+            double *ok = dk + (bh * nk + r) * D, *ov = dv + (bh * nk + r) * M;
+            for (int64_t a = 0; a < D; ++a) ok[a] = 0.0;
+            for (int64_t m = 0; m < M; ++m) ov[m] = 0.0;
+            for (int64_t i = j; i < N; ++i) {
+                const double *qi = Q + i * D, *gi = G + i * M;
+                double dot = 0.0, gv = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += qi[a] * kj[a];
+                for (int64_t m = 0; m < M; ++m) gv += gi[m] * vj[m];
+                const double dd = den[i - jmin];
+                const double e = (gv - go[i - jmin]) / dd;
+                for (int64_t a = 0; a < D; ++a) ok[a] += e * 2.0 * dot * qi[a];
+                for (int64_t m = 0; m < M; ++m) ov[m] += dot * dot * gi[m] / dd;
+            }
+        }
+        free(go); free(den); free(o);
+    }
+}
+
+/*
  * One RNN-style decode step for B*H independent streams ([review] "Proposed
  * method", attention memory s and normalizer memory z; [summary] 3.3.2, 3.4;
  * [deck] slide 4): S += phi(k) v^T, Z += phi(k), then

@@ -29,6 +29,11 @@ void orc_forward_causal_poly2(const double *q, const double *k, const double *v,
                               int64_t H, int64_t N, int64_t D, int64_t M);
 void orc_decode_step(const double *q, const double *k, const double *v, double *S, double *Z, double *out,
                      int64_t B, int64_t H, int64_t D, int64_t M);
+void orc_backward_causal_poly2(const double *q, const double *k, const double *v, const double *dout, double *dq,
+                               double *dk, double *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M);
+void orc_backward_causal_poly2_rows(const double *q, const double *k, const double *v, const double *dout,
+                                    const int64_t *rq, int64_t nq, const int64_t *rk, int64_t nk, double *dq,
+                                    double *dk, double *dv, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M);
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
 
@@ -85,6 +90,13 @@ static int run(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M) {
         free(om); free(b); free(f);
     }
     orc_forward_causal_poly2(q, k, v, out, B, H, N, D, M);   /* (q.k)^2 may vanish: no finiteness check */
+    orc_backward_causal_poly2(q, k, v, g, dq, dk, dv, B, H, N, D, M);   /* likewise */
+    {   /* the first and last rows, each summed on its own */
+        const int64_t rq[2] = {0, N - 1}, rk[2] = {N - 1, N > 1 ? N - 2 : 0};
+        double *sq = arr(B * H * 2 * D, 0), *sk = arr(B * H * 2 * D, 0), *sv = arr(B * H * 2 * M, 0);
+        orc_backward_causal_poly2_rows(q, k, v, g, rq, 2, rk, 2, sq, sk, sv, B, H, N, D, M);
+        free(sq); free(sk); free(sv);
+    }
     for (int64_t i = 0; i < ns; ++i) S[i] = 0.0;
     for (int64_t i = 0; i < nz; ++i) Z[i] = 0.0;
     for (int64_t t = 0; t < 3; ++t) {

@@ -402,6 +402,10 @@ def check_poly2_backward(lib):
     assert np.abs((dq * q).sum(-1)).max() < 1e-12 * scale * 8
     assert np.abs((dk * k).sum((-1, -2))).max() < 1e-12 * np.abs(dk).max() * np.abs(k).max() * 33 * 8
     assert _rel(dv.sum(-2), g.sum(-2)) < 1e-12
+    # selected rows, each summed on its own, equal the full gradient's rows
+    rq, rk = np.array([0, 5, 16, 31, 32]), np.array([20, 27, 31, 32])
+    sq, sk, sv = oracle.backward_causal_poly2_rows(q, k, v, g, rq, rk, lib=lib)
+    assert _rel(sq, dq[:, :, rq]) < 1e-12 and _rel(sk, dk[:, :, rk]) < 1e-12 and _rel(sv, dv[:, :, rk]) < 1e-12
 
 
 ALL_CHECKS = [check_phi, check_forward_vs_brute, check_forward_exact, check_closed_forms, check_invariants,

@@ -89,3 +89,25 @@ def test_backward_causal_poly2_is_deterministic():
     _, b = _run(w)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_backward_causal_poly2_long_sampled():
+    """The shape the bench times, B1 H8 N65536 D = M = 32 bf16 (32 segments of
+    2048 tokens per head on 256 compute units): dq at sampled rows (both ends,
+    both sides of every multiple of 2048, random rows) and dk, dv at the last
+    40 rows (three 16-row chunks), each summed pair by pair by the oracle."""
+    w = _wl(331, 1, 8, 65536, 32, 32, "bf16")
+    _say("polynomial backward B1 H8 N65536 D32 M32 bf16, sampled rows")
+    (q, k, v, g), (dq, dk, dv) = _run(w)
+    N = w.N
+    rng = np.random.default_rng(331)
+    rows = {0, 1, 15, 16, N - 2, N - 1}
+    for b in range(2048, N, 2048):
+        rows.update({b - 1, b, b + 1})
+    rows.update(int(x) for x in rng.integers(0, N, 32))
+    rq = np.array(sorted(rows))
+    rk = np.arange(N - 40, N)
+    sq, sk, sv = oracle.backward_causal_poly2_rows(q, k, v, g, rq, rk)
+    check("dq[long] rows", host(dq)[:, :, rq], sq, w.dtype, floor=True)
+    check("dk[long] last rows", host(dk)[:, :, rk], sk, w.dtype, floor=True)
+    check("dv[long] last rows", host(dv)[:, :, rk], sv, w.dtype)
