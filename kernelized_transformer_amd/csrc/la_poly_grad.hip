@@ -29,10 +29,12 @@
 // them out of the same sums its dq pass then uses, which keeps the
 // cancellation exact to the sums' precision.  Taking them from the forward
 // gave dq errors of 13% at B1 H8 N65536 D = M = 32 bf16.  fp32 I/O runs on
-// the fp32 matrix instruction; bf16 I/O carries the computed operands (the
-// state, u y, the chunk's pair weights) as bf16 hi + lo parts, each paired
-// with an exact bf16 row in one 32-deep instruction per tile ([hi, lo] .
-// [x, x]).
+// the fp32 matrix instruction.  bf16 I/O rounds the state and u y to bf16
+// operands, as the forward's state is, and carries the chunk's pair weights
+// as bf16 hi + lo parts paired with the exact bf16 rows in one 32-deep
+// instruction per tile ([y, y] . [hi, lo]).  Measured on the bf16 parity
+// cases: dq, dk, dv errors of 2.0e-3 to 3.8e-3 (per 16-row chunk), against
+// 1.7e-3 to 2.1e-3 with the state and u y split as well (23% slower).
 //
 // Launches, forwards: the segments' sums of C, their exclusive prefixes,
 // the readout (the forward's numerators and denominators), the weights w,
@@ -77,19 +79,13 @@ __host__ __device__ constexpr int64_t pg_blocks(int64_t D, int64_t M) {
 
 template <typename T> __device__ __forceinline__ float ld1(const T *p) { return static_cast<float>(*p); }
 
-// acc += A B^T over one 16-wide tile with one operand split into bf16 hi + lo
-// parts and the other exact in bf16: [hi, lo] . [b, b] = (hi + lo) b in one
-// 32-deep instruction (mma_sx: A split; mma_xs: B split).  fp32 operands: the
-// fp32 instruction.
-__device__ __forceinline__ void mma_sx(f32x4 &acc, split4 a, bf16x4 b) {
-    const bf16x8 bb = __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hl, bb, acc, 0, 0, 0);
-}
+// acc += A B^T over one 16-wide tile, A exact in bf16 and B split into bf16
+// hi + lo parts: [a, a] . [hi, lo] = a (hi + lo) in one 32-deep instruction.
+// fp32 operands: the fp32 instruction.
 __device__ __forceinline__ void mma_xs(f32x4 &acc, bf16x4 a, split4 b) {
     const bf16x8 aa = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, b.hl, acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma_sx(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
 __device__ __forceinline__ void mma_xs(f32x4 &acc, f32x4 a, f32x4 b) { mma1(acc, a, b); }
 
 // Element (token t, column m) of u or w: from V ([v, 1]) or from the weights
@@ -269,7 +265,8 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                     // T[a = c][e = 16 eb + 4g + r] = sum_d x[c][d] C[d][e]
                     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int db = 0; db < DT; ++db) mma_sx(t, frag_from<SF>(A[k][db][eb]), xn[db]);
+                    for (int db = 0; db < DT; db += 2)
+                        mma2(t, frag_from<XF>(A[k][db][eb]), frag_from<XF>(A[k][db + 1][eb]), xn[db], xn[db + 1]);
                     if constexpr (P_OUT) pacc[eb] += wa * t;
                     if constexpr (RMODE != 0) {
 #pragma unroll
@@ -327,9 +324,9 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                 f32x4 sy;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sy[r] = ytf[eb][r] * u[k][r];
-                const SF sf = frag_from<SF>(sy);
+                const XF sf = frag_from<XF>(sy);
 #pragma unroll
-                for (int db = 0; db < DT; ++db) mma_xs(A[k][db][eb], yt[db], sf);
+                for (int db = 0; db < DT; ++db) mma1(A[k][db][eb], yt[db], sf);
             }
         }
     };
