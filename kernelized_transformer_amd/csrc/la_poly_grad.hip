@@ -102,11 +102,14 @@ __device__ __forceinline__ float col_value(const T *V, const float *Wb, int row,
 // RMODE (passes): 0 p only; 1 p and r for m < M into dv (backwards); 2 r for
 // every m <= M into rb (fp32, [BH][N][M + 1]) and no p: the readout of the
 // forward itself, numerators and denominator, from the same sums the dq pass
-// uses.
+// uses; 3 (forwards, all M + 1 columns in one workgroup) both in one pass:
+// per chunk the readout r, then w = [dout / d, -(dout . out) / d] from it in
+// LDS (also stored to rb for the backwards direction), then p.
 template <typename T, int D, int M, int DIR, bool SEG, int RMODE = 0>
 __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, const T *__restrict__ Y,
                                                    const T *__restrict__ V, const float *__restrict__ Wb,
-                                                   float *__restrict__ recs, float *__restrict__ pbuf,
+                                                   const T *__restrict__ Gd, float *__restrict__ recs,
+                                                   float *__restrict__ pbuf,
                                                    T *__restrict__ dv, float *__restrict__ rb, int64_t N,
                                                    int64_t nseg, int64_t seg_tokens, int64_t BH) {
     typedef PgCfg<D> C;
@@ -118,13 +121,15 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
     constexpr int64_t REC = int64_t(M + 1) * D * D;
     constexpr int NMB = int(pg_blocks(D, M));
     constexpr bool U_FROM_V = DIR == 0, W_FROM_V = DIR == 1;
-    constexpr bool P_OUT = !SEG && RMODE != 2;   // p formed (and w staged)
+    constexpr bool P_OUT = !SEG && RMODE != 2;   // p formed (and w staged; dout for RMODE 3)
+    static_assert(RMODE != 3 || (DIR == 0 && NMB == 1), "the fused readout needs every column in the workgroup");
 
     __shared__ __align__(16) float xs[SEG ? 4 : 16 * XS];
     __shared__ __align__(16) float ys[16 * XS];
     __shared__ float us[16 * US];
     __shared__ float wsh[P_OUT ? 16 * US : 1];
     __shared__ f32x4 pred[P_OUT ? kPgWaves * DT * 64 : 1];
+    __shared__ float rsh[RMODE == 3 ? 16 * US : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -168,6 +173,7 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
         const T *yb = Yh + (live ? t0 : 0) * D, *xb = Xh + (live ? t0 : 0) * D;
         const T *vb = Vh + (live ? t0 : 0) * M;
         const float *wb = Wh + (live ? t0 : 0) * (M + 1);
+        const T *gb = Gd + (RMODE == 3 && live ? t0 * M + int64_t(bh) * N * M : 0);
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const int e = tid + i * kPgThreads, row = e / D;
@@ -180,7 +186,8 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
             const int e = tid + i * kPgThreads, row = e / MBK, j = e % MBK, m = mb * MBK + j;
             const bool on = e < 16 * MBK && row < rem && m <= M;
             fu[i] = on ? col_value<T, U_FROM_V, M>(vb, wb, row, m) : 0.f;
-            if constexpr (P_OUT) fw[i] = on ? col_value<T, W_FROM_V, M>(vb, wb, row, m) : 0.f;
+            if constexpr (RMODE == 3) fw[i] = on && m < M ? ld1<T>(gb + row * M + m) : 0.f;
+            else if constexpr (P_OUT) fw[i] = on ? col_value<T, W_FROM_V, M>(vb, wb, row, m) : 0.f;
         }
     };
     fetch(0, ry[0], rx[0], ru[0], rw[0]);
@@ -254,6 +261,64 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
 #pragma unroll
             for (int eb = 0; eb < DT; ++eb) pacc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
             f32x4 E = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (RMODE == 3) {
+                // 1. T and the readout r_m of every column; wsh holds this chunk's dout
+                f32x4 tk[NMW][DT];
+#pragma unroll
+                for (int k = 0; k < NMW; ++k) {
+                    const int m = wave * NMW + k;
+                    if (m > M) continue;   // uniform per wavefront
+                    float rv = 0.f;
+#pragma unroll
+                    for (int eb = 0; eb < DT; ++eb) {
+                        tk[k][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int db = 0; db < DT; db += 2)
+                            mma2(tk[k][eb], frag_from<XF>(A[k][db][eb]), frag_from<XF>(A[k][db + 1][eb]), xn[db],
+                                 xn[db + 1]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rv += tk[k][eb][r] * xf[eb][r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) rv += P[r] * P[r] * u[k][r];
+                    rv += __shfl_xor(rv, 16);
+                    rv += __shfl_xor(rv, 32);
+                    if (g == 0) rsh[c * US + m] = rv;
+                }
+                __syncthreads();
+                // 2. w per token (zero past the end), in place of dout in wsh
+                if (tid < 16) {
+                    const int64_t t = t0 + tid;
+                    float *wr = wsh + tid * US;
+                    const float *rr = rsh + tid * US;
+                    if (t < t_end) {
+                        const float inv = 1.f / rr[M];
+                        float go = 0.f;
+                        for (int m = 0; m < M; ++m) {
+                            const float gm = wr[m];
+                            go += gm * (rr[m] * inv);
+                            wr[m] = gm * inv;
+                            rb[(bh * N + t) * (M + 1) + m] = wr[m];
+                        }
+                        wr[M] = -go * inv;
+                        rb[(bh * N + t) * (M + 1) + M] = wr[M];
+                    } else {
+                        for (int m = 0; m <= M; ++m) wr[m] = 0.f;
+                    }
+                }
+                __syncthreads();
+                // 3. p from the kept T
+#pragma unroll
+                for (int k = 0; k < NMW; ++k) {
+                    const int m = wave * NMW + k;
+                    if (m > M) continue;
+                    const float wa = wsh[c * US + m];
+#pragma unroll
+                    for (int eb = 0; eb < DT; ++eb) pacc[eb] += wa * tk[k][eb];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) E[r] += u[k][r] * wa;
+                }
+            } else {
 #pragma unroll
             for (int k = 0; k < NMW; ++k) {
                 const int m = mb * MBK + wave * NMW + k;
@@ -290,6 +355,7 @@ __global__ __launch_bounds__(kPgThreads) void k_pg(const T *__restrict__ X, cons
                     }
                 }
             }
+            }   // RMODE
             if constexpr (P_OUT) {
             // the chunk's own pairs: p_a += sum_b (u_b . w_a) (x_a . y_b) y_b
             f32x4 Z;
@@ -424,31 +490,38 @@ hipError_t run_pg(const void *q, const void *k, const void *v, const void *dout,
     // forwards: the segments' sums of [v, 1]_m k k^T and their prefixes, the
     // readout (numerators and denominators), the weights, dq
     if (p.nseg > 1) {
-        hipLaunchKernelGGL((k_pg<T, D, M, 0, true>), grid, block, 0, s, Q, K, V, (const float *)Wb, recs,
+        hipLaunchKernelGGL((k_pg<T, D, M, 0, true>), grid, block, 0, s, Q, K, V, (const float *)Wb, (const T *)nullptr, recs,
                            (float *)nullptr, (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_scan(recs, BH, p.nseg, p.rec, 0, s)) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 2>), grid, block, 0, s, Q, K, V, (const float *)Wb, recs,
-                       (float *)nullptr, (T *)nullptr, Wb, N, p.nseg, p.seg_tokens, BH);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_pg_weights<T, M>), dim3(unsigned(ceil_div(rows, 256))), dim3(256), 0, s,
-                       static_cast<const T *>(dout), Wb, rows);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 0>), grid, block, 0, s, Q, K, V, (const float *)Wb, recs, pbuf,
-                       (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (pg_blocks(D, M) == 1) {
+        // every column in one workgroup: readout, weights and dq in one pass
+        hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 3>), grid, block, 0, s, Q, K, V, (const float *)nullptr,
+                           static_cast<const T *>(dout), recs, pbuf, (T *)nullptr, Wb, N, p.nseg, p.seg_tokens, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 2>), grid, block, 0, s, Q, K, V, (const float *)Wb, (const T *)nullptr, recs,
+                           (float *)nullptr, (T *)nullptr, Wb, N, p.nseg, p.seg_tokens, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_pg_weights<T, M>), dim3(unsigned(ceil_div(rows, 256))), dim3(256), 0, s,
+                           static_cast<const T *>(dout), Wb, rows);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_pg<T, D, M, 0, false, 0>), grid, block, 0, s, Q, K, V, (const float *)Wb, (const T *)nullptr, recs, pbuf,
+                           (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((k_pg_sum<T, D>), gsum, dim3(256), 0, s, (const float *)pbuf, static_cast<T *>(dq), n4,
                        int(p.nmb));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // backwards: the segments' sums of [g, h]_m q q^T and their suffixes, dk and dv
     if (p.nseg > 1) {
-        hipLaunchKernelGGL((k_pg<T, D, M, 1, true>), grid, block, 0, s, K, Q, V, (const float *)Wb, recs,
+        hipLaunchKernelGGL((k_pg<T, D, M, 1, true>), grid, block, 0, s, K, Q, V, (const float *)Wb, (const T *)nullptr, recs,
                            (float *)nullptr, (T *)nullptr, (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_scan(recs, BH, p.nseg, p.rec, 2, s)) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_pg<T, D, M, 1, false, 1>), grid, block, 0, s, K, Q, V, (const float *)Wb, recs, pbuf,
+    hipLaunchKernelGGL((k_pg<T, D, M, 1, false, 1>), grid, block, 0, s, K, Q, V, (const float *)Wb, (const T *)nullptr, recs, pbuf,
                        static_cast<T *>(dv), (float *)nullptr, N, p.nseg, p.seg_tokens, BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_pg_sum<T, D>), gsum, dim3(256), 0, s, (const float *)pbuf, static_cast<T *>(dk), n4,
