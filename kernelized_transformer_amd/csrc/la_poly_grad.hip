@@ -38,8 +38,9 @@
 //
 // Launches, forwards: the segments' sums of C, their exclusive prefixes,
 // the readout (the forward's numerators and denominators), the weights w,
-// the dq pass and the sum over the column blocks; backwards: the segments'
-// sums, their exclusive suffixes, the dk / dv pass and the sum.  The state is kept
+// the dq pass (these three as one pass when one workgroup holds every column)
+// and the sum over the column blocks; backwards: the segments' sums, their
+// exclusive suffixes, the dk / dv pass and the sum.  The state is kept
 // as plain D x D fp32 matrices (one per column m) in accumulator tiles:
 // a workgroup of 11 wavefronts owns one segment and a block of 11 NMW
 // columns m (NMW = 3 at D = 32, 1 at D = 64, i.e. 48 or 64 state registers
