@@ -262,14 +262,15 @@ la_status_t la_decode_step_poly2(const void *q, const void *k, const void *v, fl
  *   dv_j = sum_{i>=j} s_ij g_i,
  * computed with the D x D sums sum_j [v_j, 1]_m k_j k_j^T (forwards) and
  * sum_i [g_i, h_i]_m q_i q_i^T (backwards), one per column m.  out and d are
- * recomputed (the polynomial forward runs first, into the workspace).
+ * recomputed from the same forwards sums (so that the terms of the gradient,
+ * which cancel, cancel to the sums' precision); out is not an argument.
  * q, k, dq, dk: [B][H][N][D]; v, dout, dv: [B][H][N][M]; dq, dk, dv are
  * outputs, fully written.  D, M in {32, 64}; bf16 or fp32, fp32 sums.
- * Workspace: la_workspace_size(LA_OP_BWD_CAUSAL_POLY2, ...) bytes (the
- * forward's out and d, the weights [g, h], the segments' sums and one
- * partial dq / dk per block of columns m).  Results do not vary from run to
- * run.  A zero denominator (a query orthogonal to every earlier key) is not
- * guarded.  Errors as la_backward_causal.
+ * Workspace: la_workspace_size(LA_OP_BWD_CAUSAL_POLY2, ...) bytes (per token
+ * the weights [g, h] in fp32, the segments' sums and one partial dq / dk per
+ * block of columns m).  Results do not vary from run to run.  A zero
+ * denominator (a query orthogonal to every earlier key) is not guarded.
+ * Errors as la_backward_causal.
  */
 la_status_t la_backward_causal_poly2(const void *q, const void *k, const void *v, const void *dout,
                                      void *dq, void *dk, void *dv,
